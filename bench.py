@@ -1,0 +1,236 @@
+#!/usr/bin/env python3
+"""Forward-convolution benchmark on one MI355X.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 20] [--config resnet3x3] [--dtype f16]
+
+A step is one conv2d_fwd call: filter staging, then for every chunk of window
+rows the im2win pack and the window-GEMM, writing the fp32 output. Inputs are
+seeded synthetic tensors already resident in device memory. The timed region
+is `steps` back-to-back calls on one stream, bracketed by device syncs and
+HIP events; warm-up calls run first and caches stay warm (50 timed calls
+after 20 warm-up ones, the protocol of the fused-WTConv measurements).
+
+Prints ONE JSON line: TFLOPS (2 * multiply-adds / time, padded taps
+included) of the headline dtype, its fraction of the MI355X peak, the
+roofline of the dominant kernel (per-kernel HIP events around every launch
+in a second timed pass), the other dtype variants of the same layer, a
+parity check of the timed output against the CPU oracle on sampled points,
+and the CPU oracle's own throughput on the host cores as a baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "conv2d fwd TFLOPS and % of MFMA/fp32 peak per layer on 1 MI355X"
+# MI355X published peaks
+PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6, "f32": 157.3}   # dense MFMA / vector fp32
+HBM_GBPS = 8000.0
+TOL = {"f32": 1e-5, "f16": 2e-3, "bf16": 1e-2}
+
+
+def _say(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(cfg, dt, plan):
+    """Per-kernel algorithmic HBM bytes of one call (each tensor moved once).
+
+    pack   : reads x, writes the window tensor (N*Ho rows of Cin*W_win*KH)
+    gemm   : reads the window tensor and the staged filter, writes y (fp32)
+    stage  : reads w, writes the staged filter
+    """
+    es = 4 if dt == "f32" else 2
+    ho, wo = plan.Ho, plan.Wo
+    x = cfg.N * cfg.Cin * cfg.H * cfg.W * es
+    w = cfg.Cout * cfg.Cin * cfg.KH * cfg.KW * es
+    win = cfg.N * ho * cfg.Cin * plan.W_win * cfg.KH * es
+    y = cfg.N * cfg.Cout * ho * wo * 4
+    return {"pack": x + win, "gemm": win + w * plan.n_chunks + y,
+            "weight_stage": 2 * w if plan.wstage_bytes else 0}
+
+
+def time_variant(cfg, dt, steps, warmup, dev):
+    import torch
+
+    import cnn_convolution_amd as conv
+    import workloads
+
+    x, w = workloads.make_config_inputs(cfg, dt)
+    xd, wd = x.to(dev), w.to(dev)
+    d = conv.describe(tuple(x.shape), tuple(w.shape), cfg.stride, cfg.pad,
+                      {"f32": conv.F32, "f16": conv.F16, "bf16": conv.BF16}[dt])
+    plan = conv.plan(d)
+    y = torch.empty((cfg.N, cfg.Cout, plan.Ho, plan.Wo), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(plan.ws_bytes, 1), dtype=torch.uint8, device=dev)
+    wsarg = ws if plan.ws_bytes else None
+
+    for _ in range(warmup):
+        conv.conv2d_into(xd, wd, y, wsarg, cfg.stride, cfg.pad)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(steps):
+        conv.conv2d_into(xd, wd, y, wsarg, cfg.stride, cfg.pad)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / steps
+
+    # second timed pass: HIP events around every kernel launch (same stream)
+    conv.profile_read()
+    conv.profile_enable(True)
+    try:
+        for _ in range(steps):
+            conv.conv2d_into(xd, wd, y, wsarg, cfg.stride, cfg.pad)
+    finally:
+        conv.profile_enable(False)
+    prof = conv.profile_read()
+
+    # parity of the timed output on sampled points
+    import oracle
+    rng = np.random.default_rng(cfg.seed)
+    idx = rng.integers(0, y.numel(), 2000)
+    got = y.reshape(-1)[torch.from_numpy(idx).to(dev)].double().cpu().numpy()
+    ref = oracle.conv2d_points(x, w, cfg.stride, cfg.pad, idx)
+    rel = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+
+    flops = plan.flops
+    tflops = flops / (ms * 1e-3) / 1e12
+    ab = algorithmic_bytes(cfg, dt, plan)
+    kern = {}
+    for k in ("weight_stage", "pack", "gemm"):
+        n = prof[k]["launches"]
+        if n:
+            avg = prof[k]["total_ms"] / n
+            kern[k] = {"launches_per_step": n / steps, "avg_launch_us": avg * 1e3,
+                       "ms_per_step": prof[k]["total_ms"] / steps,
+                       "alg_bytes_per_launch": ab[k] / (n / steps)}
+    g = kern["gemm"]
+    gemm_s = g["avg_launch_us"] * 1e-6
+    gemm_flops = flops / g["launches_per_step"]
+    gemm_bytes = g["alg_bytes_per_launch"]
+    ai = gemm_flops / gemm_bytes
+    peak = PEAK_TFLOPS[dt]
+    ridge = peak * 1e12 / (HBM_GBPS * 1e9)
+    if ai < ridge:
+        roof = {"bound": "hbm", "achieved": gemm_bytes / gemm_s / 1e9, "peak": HBM_GBPS,
+                "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma" if dt != "f32" else "alu",
+                "achieved": gemm_flops / gemm_s / 1e12, "peak": peak, "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["kernel"] = "gemm_mfma" if dt != "f32" else "gemm_valu_f32"
+    roof["alg_bytes_per_launch"] = gemm_bytes
+    roof["flops_per_launch"] = gemm_flops
+    roof["avg_launch_us"] = g["avg_launch_us"]
+    return {
+        "dtype": dt, "value": tflops, "ms_per_step": ms, "wall_s": wall,
+        "pct_of_peak": 100.0 * tflops / peak, "peak_tflops": peak,
+        "rel_l2_sampled": rel, "parity_ok": rel <= TOL[dt],
+        "ws_bytes": plan.ws_bytes, "im2col_bytes": plan.im2col_bytes,
+        "ws_over_im2col": plan.ws_bytes / plan.im2col_bytes, "ws_target": 1.0 / cfg.KW,
+        "n_chunks": plan.n_chunks, "kernels": kern, "roofline": roof,
+    }
+
+
+def cpu_baseline(cfg, dt, min_seconds=10.0):
+    """The fp64 oracle on the host cores over a bounded sample of the layer:
+    whole images of the same batch, repeated until about min_seconds."""
+    import oracle
+    import workloads
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or min(16, os.cpu_count() or 1)
+    x, w = workloads.make_config_inputs(cfg, dt)
+    per_img = 2 * cfg.Cout * cfg.out_hw()[0] * cfg.out_hw()[1] * cfg.Cin * cfg.KH * cfg.KW
+    # size the sample from a one-image probe
+    t = time.perf_counter()
+    oracle.conv2d(x[:1], w, cfg.stride, cfg.pad, nthreads=threads)
+    probe = max(time.perf_counter() - t, 1e-4)
+    imgs = int(max(1, min(cfg.N, min_seconds / probe)))
+    reps = int(max(1, min(50, min_seconds / (probe * imgs))))
+    t = time.perf_counter()
+    for _ in range(reps):
+        oracle.conv2d(x[:imgs], w, cfg.stride, cfg.pad, nthreads=threads)
+    el = time.perf_counter() - t
+    return {"value": per_img * imgs * reps / el / 1e12, "unit": "TFLOPS", "cores": threads,
+            "kind": "oracle", "seconds": el,
+            "sample": f"{imgs} of {cfg.N} images of the {cfg.name} layer, {reps} pass(es), "
+                      f"fp64 direct sum, {dt} inputs"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="resnet3x3")
+    ap.add_argument("--dtype", default=None, help="headline dtype (default: the layer's "
+                    "half-precision variant if it has one)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--all-configs", action="store_true",
+                    help="one JSON line per layer and dtype (profiling / results table)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(json.dumps({"metric": METRIC, "value": None, "n_gpus": args.gpus,
+                          "error": "this build runs on one GPU only; a per-GPU share of a "
+                                   "sharded layer is the same kernel at N/G images"}))
+        _say("bench.py: only --gpus 1 is supported (single-GPU build)")
+        sys.exit(2)
+
+    import torch
+    import workloads
+    import cnn_convolution_amd  # noqa: F401  (fails loudly without the HIP library)
+
+    if not torch.cuda.is_available():
+        _say("bench.py: no GPU visible")
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    names = sorted(workloads.CONFIGS) if args.all_configs else [args.config]
+    for name in names:
+        cfg = workloads.get_config(name)
+        dts = list(cfg.dtypes)
+        head = args.dtype if args.dtype and args.dtype in dts else \
+            next((d for d in dts if d != "f32"), dts[0])
+        order = [head] + [d for d in dts if d != head]
+        results = {}
+        for dt in order:
+            _say(f"bench: {name} {dt} warmup={args.warmup} steps={args.steps}")
+            results[dt] = time_variant(cfg, dt, args.steps, args.warmup, dev)
+        h = results[head]
+        line = {
+            "metric": METRIC, "value": h["value"], "unit": "TFLOPS", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": h["ms_per_step"],
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": head, "data": "synthetic",
+            "config": {"workload": f"{name}: N={cfg.N} Cin={cfg.Cin} H=W={cfg.H} "
+                                   f"Cout={cfg.Cout} {cfg.KH}x{cfg.KW} s{cfg.stride} p{cfg.pad}",
+                       "N": cfg.N, "Cin": cfg.Cin, "H": cfg.H, "W": cfg.W, "Cout": cfg.Cout,
+                       "KH": cfg.KH, "KW": cfg.KW, "stride": cfg.stride, "pad": cfg.pad,
+                       "output": "fp32", "parallelism": "single GPU"},
+            "pct_of_peak": h["pct_of_peak"], "peak_tflops": h["peak_tflops"],
+            "roofline": h["roofline"], "kernels": h["kernels"],
+            "ws_bytes": h["ws_bytes"], "im2col_bytes": h["im2col_bytes"],
+            "ws_over_im2col": h["ws_over_im2col"], "ws_target": h["ws_target"],
+            "rel_l2_sampled": h["rel_l2_sampled"], "parity_ok": h["parity_ok"],
+            "variants": [{k: v for k, v in results[d].items()} for d in order[1:]],
+        }
+        if not args.no_cpu_baseline and name == names[0]:
+            _say("bench: cpu baseline (oracle)")
+            line["cpu_baseline"] = cpu_baseline(cfg, head)
+        print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

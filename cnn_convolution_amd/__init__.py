@@ -1,0 +1,118 @@
+"""im2win forward 2-D convolution for MI355X (gfx950).
+
+    y = cnn_convolution_amd.conv2d(x, w, stride=1, pad=0)
+
+x [N][Cin][H][W] and w [Cout][Cin][KH][KW] are contiguous CUDA (HIP) tensors
+of float32, float16 or bfloat16 (the same dtype); y is float32. PyTorch
+provides the device memory and the current stream; the convolution itself
+runs in libim2win_conv2d.so (see include/im2win_conv2d.h).
+"""
+from __future__ import annotations
+
+from . import _lib
+from ._lib import (Conv2dError, Desc, Plan, LAYOUT_CL, LAYOUT_ROW, F16, F32, BF16,  # noqa: F401
+                   make_desc, workspace_size, plan, profile_enable, profile_read, status_string)
+
+__all__ = ["conv2d", "conv2d_into", "pack", "weight_stage", "describe", "plan", "workspace_size",
+           "Conv2dError", "profile_enable", "profile_read"]
+
+
+def _dtype_code(t) -> int:
+    import torch
+    codes = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
+    if t.dtype not in codes:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return codes[t.dtype]
+
+
+def describe(x_shape, w_shape, stride=1, pad=0, dtype=F32) -> Desc:
+    N, Cin, H, W = x_shape
+    Cout, Cin2, KH, KW = w_shape
+    if Cin2 != Cin:
+        raise ValueError(f"channel mismatch: x has {Cin}, w has {Cin2}")
+    return make_desc(N, Cin, H, W, Cout, KH, KW, stride, pad, dtype)
+
+
+def _stream():
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _check(t, name):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def conv2d_into(x, w, y, ws, stride=1, pad=0) -> None:
+    """Enqueue y = conv2d(x, w) on the current stream using caller buffers."""
+    d = describe(tuple(x.shape), tuple(w.shape), stride, pad, _dtype_code(x))
+    if w.dtype != x.dtype:
+        raise TypeError("x and w must share a dtype")
+    st = _lib.fwd(d, x.data_ptr(), w.data_ptr(), y.data_ptr(),
+                  ws.data_ptr() if ws is not None and ws.numel() else None, _stream())
+    if st != 0:
+        raise Conv2dError(st, "conv2d_fwd")
+
+
+def conv2d(x, w, stride: int = 1, pad: int = 0):
+    import torch
+    _check(x, "x")
+    _check(w, "w")
+    d = describe(tuple(x.shape), tuple(w.shape), stride, pad, _dtype_code(x))
+    p = plan(d)
+    y = torch.empty((d.N, d.Cout, p.Ho, p.Wo), dtype=torch.float32, device=x.device)
+    ws = torch.empty(max(p.ws_bytes, 1), dtype=torch.uint8, device=x.device)
+    conv2d_into(x, w, y, ws if p.ws_bytes else None, stride, pad)
+    return y
+
+
+def pack(x, KH: int, KW: int, stride: int, pad: int, layout: int, row0: int = 0, rows=None):
+    """Rows [row0, row0+rows) of the im2win window tensor of x, as a flat tensor."""
+    import torch
+    _check(x, "x")
+    code = _dtype_code(x)
+    d = describe(tuple(x.shape), (1, x.shape[1], KH, KW), stride, pad, code)
+    p = plan(d)
+    if rows is None:
+        rows = p.rows_total - row0
+    geo = layout_geometry(d, layout)
+    out = torch.empty(max(rows, 0) * geo["row_elems"], dtype=x.dtype, device=x.device)
+    st = _lib.pack(d, layout, x.data_ptr(), out.data_ptr(), row0, rows, _stream())
+    if st != 0:
+        raise Conv2dError(st, "im2win_pack")
+    return out, geo
+
+
+def layout_geometry(d: Desc, layout: int) -> dict:
+    """Cin_pad, pos_pad and row_elems of a layout (as the planner computes them)."""
+    p = plan(d)
+    if layout == p.layout:
+        return {"Cin_pad": p.Cin_pad, "pos_pad": p.pos_pad, "row_elems": p.row_elems}
+    # the other layout: ask the planner for the dtype that uses it
+    other = make_desc(d.N, d.Cin, d.H, d.W, d.Cout, d.KH, d.KW, d.stride, d.pad,
+                      F16 if layout == LAYOUT_CL else F32)
+    q = plan(other)
+    return {"Cin_pad": q.Cin_pad, "pos_pad": q.pos_pad, "row_elems": q.row_elems}
+
+
+def weight_stage(w, stride: int, pad: int, x_hw, layout: int):
+    """The staged filter of w for `layout`, as a flat tensor (with its geometry)."""
+    import torch
+    _check(w, "w")
+    Cout, Cin, KH, KW = w.shape
+    code = _dtype_code(w)
+    d = describe((1, Cin, x_hw[0], x_hw[1]), tuple(w.shape), stride, pad, code)
+    p = plan(d)
+    if layout == LAYOUT_ROW:
+        rows, row_len = -(-Cout // 16) * 16, Cin * KH * KW
+    else:
+        rows, row_len = Cout, p.K_stage if p.layout == LAYOUT_CL else None
+        if row_len is None:
+            raise ValueError("channels-last staging is for fp16/bf16 filters")
+    out = torch.empty(rows * row_len, dtype=w.dtype, device=w.device)
+    st = _lib.weight_stage(d, layout, w.data_ptr(), out.data_ptr(), _stream())
+    if st != 0:
+        raise Conv2dError(st, "im2win_weight_stage")
+    return out, {"rows": rows, "row_len": row_len}

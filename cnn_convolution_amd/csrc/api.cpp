@@ -1,0 +1,302 @@
+// C ABI of the im2win forward convolution (declared in include/im2win_conv2d.h).
+//
+// conv2d_fwd: validate -> plan -> [stage filter] -> for each chunk of window
+// rows { pack the chunk (Eq. (2) of the im2win paper) ; window-GEMM the chunk
+// into y }. Everything is enqueued on the caller's stream; nothing is
+// allocated and nothing synchronises (except conv2d_profile_read).
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <algorithm>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include "im2win_conv2d.h"
+#include "launch.hpp"
+#include "plan.hpp"
+
+using namespace im2win;
+
+namespace {
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// ---- profiling hook: event pairs around each launch while enabled ----------
+struct Rec {
+    hipEvent_t a, b;
+    int kind;
+};
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<Rec> g_recs;        // recorded since the last read
+std::vector<hipEvent_t> g_pool;  // reusable events
+
+hipEvent_t pool_get()
+{
+    if (!g_pool.empty()) {
+        hipEvent_t e = g_pool.back();
+        g_pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+
+struct ProfScope {
+    hipStream_t s;
+    int kind;
+    hipEvent_t a = nullptr, b = nullptr;
+    ProfScope(hipStream_t s_, int kind_) : s(s_), kind(kind_)
+    {
+        if (!g_prof_on) return;
+        std::lock_guard<std::mutex> lk(g_prof_mu);
+        a = pool_get();
+        b = pool_get();
+        if (a && b) (void)hipEventRecord(a, s);
+    }
+    ~ProfScope()
+    {
+        if (!a || !b) return;
+        (void)hipEventRecord(b, s);
+        std::lock_guard<std::mutex> lk(g_prof_mu);
+        g_recs.push_back(Rec{a, b, kind});
+    }
+};
+
+PackArgs pack_args(const conv2d_desc_t &d, const conv2d_plan_t &p, int32_t layout,
+                   const LayoutGeom &g, const void *x, void *out, int64_t row0, int64_t rows)
+{
+    PackArgs a{};
+    a.x = x;
+    a.out = out;
+    a.N = int(d.N);
+    a.Cin = int(d.Cin);
+    a.H = int(d.H);
+    a.W = int(d.W);
+    a.KH = int(d.KH);
+    a.stride = int(d.stride);
+    a.pad = int(d.pad);
+    a.Ho = int(p.Ho);
+    a.Wwin = int(p.W_win);
+    a.Cin_pad = int(g.Cin_pad);
+    a.pos_pad = int(g.pos_pad);
+    a.row_elems = int(g.row_elems);
+    a.row0 = int(row0);
+    a.rows = int(rows);
+    a.esize = int(elem_size(d.dtype));
+    (void)layout;
+    return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t conv2d_workspace_size(const conv2d_desc_t *d)
+{
+    if (!d) return 0;
+    conv2d_plan_t p;
+    if (make_plan(*d, &p) != CONV2D_OK) return 0;
+    return size_t(p.ws_bytes);
+}
+
+conv2d_status_t conv2d_plan(const conv2d_desc_t *d, conv2d_plan_t *out)
+{
+    if (!d || !out) return CONV2D_ERR_NULL_POINTER;
+    return make_plan(*d, out);
+}
+
+const char *conv2d_status_string(conv2d_status_t s)
+{
+    switch (s) {
+    case CONV2D_OK: return "ok";
+    case CONV2D_ERR_INVALID_DESC: return "invalid descriptor";
+    case CONV2D_ERR_NULL_POINTER: return "null pointer";
+    case CONV2D_ERR_MISALIGNED: return "misaligned pointer";
+    case CONV2D_ERR_UNSUPPORTED: return "unsupported dtype or layout";
+    case CONV2D_ERR_WORKSPACE: return "workspace missing";
+    case CONV2D_ERR_HIP: return "HIP runtime error";
+    case CONV2D_ERR_RANGE: return "row range out of bounds";
+    }
+    return "unknown status";
+}
+
+conv2d_status_t conv2d_fwd(const conv2d_desc_t *d, const void *x, const void *w, float *y,
+                           void *ws, void *stream)
+{
+    if (!d) return CONV2D_ERR_NULL_POINTER;
+    conv2d_plan_t p;
+    const conv2d_status_t st = make_plan(*d, &p);
+    if (st != CONV2D_OK) return st;
+    if (!x || !w || !y) return CONV2D_ERR_NULL_POINTER;
+    if (p.ws_bytes > 0 && !ws) return CONV2D_ERR_WORKSPACE;
+    if (!aligned(x, 16) || !aligned(w, 16) || !aligned(y, 16)) return CONV2D_ERR_MISALIGNED;
+    if (ws && !aligned(ws, 256)) return CONV2D_ERR_MISALIGNED;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    char *wsb = static_cast<char *>(ws);
+    const LayoutGeom g = layout_geom(*d, p.layout);
+    const StageGeom sg = stage_geom(*d, p.layout, p.gemm_tile_m);
+    const int es = int(elem_size(d->dtype));
+    hipError_t e = hipSuccess;
+
+    // (a3) filter into the window's K order
+    const void *wst = w;
+    if (sg.needed) {
+        StageArgs sa{};
+        sa.w = w;
+        sa.out = wsb;
+        sa.Cout = int(d->Cout);
+        sa.Cin = int(d->Cin);
+        sa.KH = int(d->KH);
+        sa.KW = int(d->KW);
+        sa.Cin_pad = int(g.Cin_pad);
+        sa.rows = int(sg.rows);
+        sa.row_len = int(sg.row_len);
+        sa.esize = es;
+        ProfScope ps(s, CONV2D_KERNEL_WEIGHT_STAGE);
+        e = p.layout == IM2WIN_LAYOUT_ROW ? launch_stage_row(sa, s) : launch_stage_cl(sa, s);
+        if (e != hipSuccess) return CONV2D_ERR_HIP;
+        wst = wsb;
+    }
+    void *win = wsb + p.win_offset_bytes;
+
+    for (int64_t c = 0; c < p.n_chunks; ++c) {
+        const int64_t row0 = c * p.rows_per_chunk;
+        const int64_t rows = std::min<int64_t>(p.rows_per_chunk, p.rows_total - row0);
+        // (a2) window rows of this chunk
+        const PackArgs pa = pack_args(*d, p, p.layout, g, x, win, row0, rows);
+        {
+            ProfScope ps(s, CONV2D_KERNEL_PACK);
+            e = p.layout == IM2WIN_LAYOUT_ROW ? launch_pack_row(pa, s) : launch_pack_cl(pa, s);
+        }
+        if (e != hipSuccess) return CONV2D_ERR_HIP;
+        // (a4, a5) window-GEMM of the chunk, fp32 result written into y
+        ProfScope ps(s, CONV2D_KERNEL_GEMM);
+        if (p.path == 0) {
+            ValuGemmArgs ga{};
+            ga.win = static_cast<const float *>(win);
+            ga.wst = static_cast<const float *>(wst);
+            ga.y = y;
+            ga.rows = int(rows);
+            ga.row0 = int(row0);
+            ga.Cin = int(d->Cin);
+            ga.pos_pad = int(g.pos_pad);
+            ga.row_elems = int(g.row_elems);
+            ga.KH = int(d->KH);
+            ga.KW = int(d->KW);
+            ga.stride = int(d->stride);
+            ga.Ho = int(p.Ho);
+            ga.Wo = int(p.Wo);
+            ga.Cout = int(d->Cout);
+            ga.Cout_stage = int(p.Cout_stage);
+            e = launch_gemm_valu_f32(ga, s);
+        } else {
+            MfmaGemmArgs ga{};
+            ga.win = win;
+            ga.wst = wst;
+            ga.y = y;
+            ga.rows = int(rows);
+            ga.row0 = int(row0);
+            ga.row_elems = int(g.row_elems);
+            ga.col_step = int(d->stride * d->KH * g.Cin_pad);
+            ga.krun = int(d->KW * d->KH * g.Cin_pad);
+            ga.kstage = int(p.K_stage);
+            ga.Ho = int(p.Ho);
+            ga.Wo = int(p.Wo);
+            ga.Cout = int(d->Cout);
+            ga.tile_m = p.gemm_tile_m;
+            ga.tile_n = p.gemm_tile_n;
+            ga.bf16 = d->dtype == CONV2D_BF16 ? 1 : 0;
+            e = launch_gemm_mfma(ga, s);
+        }
+        if (e != hipSuccess) return CONV2D_ERR_HIP;
+    }
+    return CONV2D_OK;
+}
+
+conv2d_status_t im2win_pack(const conv2d_desc_t *d, int32_t layout, const void *x, void *out,
+                            int64_t row0, int64_t rows, void *stream)
+{
+    if (!d) return CONV2D_ERR_NULL_POINTER;
+    conv2d_plan_t p;
+    const conv2d_status_t st = make_plan(*d, &p);
+    if (st != CONV2D_OK) return st;
+    if (layout != IM2WIN_LAYOUT_ROW && layout != IM2WIN_LAYOUT_CL) return CONV2D_ERR_UNSUPPORTED;
+    if (layout == IM2WIN_LAYOUT_CL && d->dtype == CONV2D_F32) return CONV2D_ERR_UNSUPPORTED;
+    if (row0 < 0 || rows < 1 || row0 + rows > p.rows_total) return CONV2D_ERR_RANGE;
+    if (!x || !out) return CONV2D_ERR_NULL_POINTER;
+    if (!aligned(x, 16) || !aligned(out, 16)) return CONV2D_ERR_MISALIGNED;
+    const LayoutGeom g = layout_geom(*d, layout);
+    if (rows * g.row_elems > kMaxElems) return CONV2D_ERR_INVALID_DESC;
+    const PackArgs pa = pack_args(*d, p, layout, g, x, out, row0, rows);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const hipError_t e = layout == IM2WIN_LAYOUT_ROW ? launch_pack_row(pa, s) : launch_pack_cl(pa, s);
+    return e == hipSuccess ? CONV2D_OK : CONV2D_ERR_HIP;
+}
+
+conv2d_status_t im2win_weight_stage(const conv2d_desc_t *d, int32_t layout, const void *w,
+                                    void *out, void *stream)
+{
+    if (!d) return CONV2D_ERR_NULL_POINTER;
+    conv2d_plan_t p;
+    const conv2d_status_t st = make_plan(*d, &p);
+    if (st != CONV2D_OK) return st;
+    if (layout != IM2WIN_LAYOUT_ROW && layout != IM2WIN_LAYOUT_CL) return CONV2D_ERR_UNSUPPORTED;
+    if (!w || !out) return CONV2D_ERR_NULL_POINTER;
+    if (!aligned(w, 16) || !aligned(out, 16)) return CONV2D_ERR_MISALIGNED;
+    const LayoutGeom g = layout_geom(*d, layout);
+    const StageGeom sg = stage_geom(*d, layout, p.gemm_tile_m);
+    StageArgs sa{};
+    sa.w = w;
+    sa.out = out;
+    sa.Cout = int(d->Cout);
+    sa.Cin = int(d->Cin);
+    sa.KH = int(d->KH);
+    sa.KW = int(d->KW);
+    sa.Cin_pad = int(g.Cin_pad);
+    sa.rows = int(sg.rows);
+    sa.row_len = int(sg.row_len);
+    sa.esize = int(elem_size(d->dtype));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const hipError_t e = layout == IM2WIN_LAYOUT_ROW ? launch_stage_row(sa, s) : launch_stage_cl(sa, s);
+    return e == hipSuccess ? CONV2D_OK : CONV2D_ERR_HIP;
+}
+
+conv2d_status_t conv2d_profile_enable(int32_t on)
+{
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    g_prof_on = on != 0;
+    return CONV2D_OK;
+}
+
+conv2d_status_t conv2d_profile_read(conv2d_profile_t *out)
+{
+    if (!out) return CONV2D_ERR_NULL_POINTER;
+    std::memset(out, 0, sizeof(*out));
+    std::vector<Rec> recs;
+    {
+        std::lock_guard<std::mutex> lk(g_prof_mu);
+        recs.swap(g_recs);
+    }
+    conv2d_status_t st = CONV2D_OK;
+    for (const Rec &r : recs) {
+        float ms = 0.f;
+        if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess)
+            st = CONV2D_ERR_HIP;
+        else if (r.kind >= 0 && r.kind < CONV2D_KERNEL_KINDS) {
+            out->launches[r.kind] += 1;
+            out->total_ms[r.kind] += ms;
+        }
+    }
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    for (const Rec &r : recs) {
+        g_pool.push_back(r.a);
+        g_pool.push_back(r.b);
+    }
+    return st;
+}
+
+}  // extern "C"

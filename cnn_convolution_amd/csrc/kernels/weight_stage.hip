@@ -1,0 +1,102 @@
+// Filter staging: reorder w[Cout][Cin][KH][KW] into the K order in which the
+// window-GEMM walks a window. The im2win paper keeps the filter in a layout
+// whose taps follow the window's element order ("Enabling Memory-efficient
+// Im2win Convolution ...", Sec. III-C, end); here that order is:
+//   fp32 path (row-interleaved windows):
+//       out[cb][ci][kh][kw][j] = w[cb*16 + j][ci][kh][kw]      (j < 16)
+//     16 output channels innermost, so one scalar load brings the 16 filter
+//     values a wave multiplies against one window element;
+//   fp16/bf16 path (channels-last windows):
+//       out[co][(kw*KH + kh)*Cin_pad + ci] = w[co][ci][kh][kw]
+//     matching the contiguous window run (kw outer, kh, channels inner).
+// Cells with no filter value (padded channels, rows, K tail) are zero.
+// Pure copies of raw bits.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "../launch.hpp"
+
+namespace im2win {
+namespace {
+
+template <typename E>
+__global__ __launch_bounds__(256) void stage_row_kernel(const E *__restrict__ w, E *__restrict__ out,
+                                                        int Cout, int K, int rows)
+{
+    // out index = (cb*K + k)*16 + j ; co = cb*16 + j ; w index = co*K + k
+    const int64_t total = int64_t(rows) * K;
+    for (int64_t e = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; e < total;
+         e += int64_t(gridDim.x) * blockDim.x) {
+        const int j = int(e & 15);
+        const int64_t t = e >> 4;
+        const int k = int(t % K);
+        const int cb = int(t / K);
+        const int co = cb * 16 + j;
+        out[e] = co < Cout ? w[int64_t(co) * K + k] : E(0);
+    }
+}
+
+template <typename E>
+__global__ __launch_bounds__(256) void stage_cl_kernel(const E *__restrict__ w, E *__restrict__ out,
+                                                       int Cout, int Cin, int KH, int KW,
+                                                       int Cin_pad, int row_len)
+{
+    const int krun = KW * KH * Cin_pad;
+    const int64_t total = int64_t(Cout) * row_len;
+    for (int64_t e = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; e < total;
+         e += int64_t(gridDim.x) * blockDim.x) {
+        const int k = int(e % row_len);
+        const int co = int(e / row_len);
+        E v = E(0);
+        if (k < krun) {
+            const int ci = k % Cin_pad;
+            const int pos = k / Cin_pad;
+            const int kh = pos % KH;
+            const int kw = pos / KH;
+            if (ci < Cin) v = w[((int64_t(co) * Cin + ci) * KH + kh) * KW + kw];
+        }
+        out[e] = v;
+    }
+}
+
+unsigned grid_for(int64_t total)
+{
+    int64_t b = (total + 255) / 256;
+    if (b > 65536) b = 65536;
+    if (b < 1) b = 1;
+    return unsigned(b);
+}
+
+}  // namespace
+
+hipError_t launch_stage_row(const StageArgs &a, hipStream_t s)
+{
+    const int K = a.Cin * a.KH * a.KW;
+    const dim3 grid(grid_for(int64_t(a.rows) * K));
+    if (a.esize == 4)
+        hipLaunchKernelGGL(stage_row_kernel<uint32_t>, grid, dim3(256), 0, s,
+                           static_cast<const uint32_t *>(a.w), static_cast<uint32_t *>(a.out),
+                           a.Cout, K, a.rows);
+    else
+        hipLaunchKernelGGL(stage_row_kernel<uint16_t>, grid, dim3(256), 0, s,
+                           static_cast<const uint16_t *>(a.w), static_cast<uint16_t *>(a.out),
+                           a.Cout, K, a.rows);
+    return hipGetLastError();
+}
+
+hipError_t launch_stage_cl(const StageArgs &a, hipStream_t s)
+{
+    const dim3 grid(grid_for(int64_t(a.rows) * a.row_len));
+    if (a.esize == 4)
+        hipLaunchKernelGGL(stage_cl_kernel<uint32_t>, grid, dim3(256), 0, s,
+                           static_cast<const uint32_t *>(a.w), static_cast<uint32_t *>(a.out),
+                           a.Cout, a.Cin, a.KH, a.KW, a.Cin_pad, a.row_len);
+    else
+        hipLaunchKernelGGL(stage_cl_kernel<uint16_t>, grid, dim3(256), 0, s,
+                           static_cast<const uint16_t *>(a.w), static_cast<uint16_t *>(a.out),
+                           a.Cout, a.Cin, a.KH, a.KW, a.Cin_pad, a.row_len);
+    return hipGetLastError();
+}
+
+}  // namespace im2win

@@ -1,0 +1,57 @@
+// Host-side launchers of the HIP kernels (one per kernel family). Plain
+// pointers and sizes only; every launcher enqueues on `stream` and returns
+// hipGetLastError() of the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace im2win {
+
+struct PackArgs {
+    const void *x;          // NCHW input
+    void *out;              // window rows [rows][row_elems]
+    int N, Cin, H, W, KH, stride, pad, Ho, Wwin;
+    int Cin_pad, pos_pad, row_elems;
+    int row0, rows;         // window rows r in [row0, row0 + rows)
+    int esize;              // 2 or 4 bytes
+};
+hipError_t launch_pack_row(const PackArgs &a, hipStream_t s);
+hipError_t launch_pack_cl(const PackArgs &a, hipStream_t s);
+
+struct StageArgs {
+    const void *w;          // [Cout][Cin][KH][KW]
+    void *out;
+    int Cout, Cin, KH, KW;
+    int Cin_pad, rows, row_len;  // staged geometry
+    int esize;
+};
+hipError_t launch_stage_row(const StageArgs &a, hipStream_t s);
+hipError_t launch_stage_cl(const StageArgs &a, hipStream_t s);
+
+struct ValuGemmArgs {
+    const float *win;       // window chunk [rows][Cin][pos_pad]
+    const float *wst;       // staged filter [Cout_stage/16][Cin][KH][KW][16]
+    float *y;               // [N][Cout][Ho][Wo]
+    int rows, row0, Cin, pos_pad, row_elems;
+    int KH, KW, stride;
+    int Ho, Wo, Cout, Cout_stage;
+};
+hipError_t launch_gemm_valu_f32(const ValuGemmArgs &a, hipStream_t s);
+
+struct MfmaGemmArgs {
+    const void *win;        // window chunk [rows][row_elems] (channels-last)
+    const void *wst;        // staged filter [Cout][K_stage]
+    float *y;
+    int rows, row0, row_elems;
+    int col_step;           // stride*KH*Cin_pad: window start step between columns
+    int krun;               // KW*KH*Cin_pad: window length
+    int kstage;             // staged filter row length (multiple of the K slice)
+    int Ho, Wo, Cout;
+    int tile_m, tile_n;
+    int bf16;               // 0: fp16, 1: bf16
+};
+hipError_t launch_gemm_mfma(const MfmaGemmArgs &a, hipStream_t s);
+
+}  // namespace im2win

@@ -1,0 +1,123 @@
+// Host planner: see plan.hpp.
+#include "plan.hpp"
+
+#include <cstring>
+
+namespace im2win {
+
+conv2d_status_t check_desc(const conv2d_desc_t &d) {
+    if (d.dtype != CONV2D_F32 && d.dtype != CONV2D_F16 && d.dtype != CONV2D_BF16)
+        return CONV2D_ERR_UNSUPPORTED;
+    if (d.reserved != 0) return CONV2D_ERR_INVALID_DESC;
+    if (d.N < 1 || d.Cin < 1 || d.H < 1 || d.W < 1 || d.Cout < 1 || d.KH < 1 || d.KW < 1 ||
+        d.stride < 1 || d.pad < 0)
+        return CONV2D_ERR_INVALID_DESC;
+    // keep every product below well under int64 overflow before multiplying
+    const int64_t lim = int64_t(1) << 20;
+    if (d.N > lim || d.Cin > lim || d.H > lim || d.W > lim || d.Cout > lim || d.KH > lim ||
+        d.KW > lim || d.stride > lim || d.pad > lim)
+        return CONV2D_ERR_INVALID_DESC;
+    const int64_t Ho = out_extent(d.H, d.KH, d.stride, d.pad);
+    const int64_t Wo = out_extent(d.W, d.KW, d.stride, d.pad);
+    if (Ho < 1 || Wo < 1) return CONV2D_ERR_INVALID_DESC;
+    if (d.N * d.Cin * d.H * d.W > kMaxElems) return CONV2D_ERR_INVALID_DESC;
+    if (d.Cout * d.Cin * d.KH * d.KW > kMaxElems) return CONV2D_ERR_INVALID_DESC;
+    if (d.N * d.Cout * Ho * Wo > kMaxElems) return CONV2D_ERR_INVALID_DESC;
+    return CONV2D_OK;
+}
+
+LayoutGeom layout_geom(const conv2d_desc_t &d, int32_t layout) {
+    const int64_t Wo = out_extent(d.W, d.KW, d.stride, d.pad);
+    const int64_t Wwin = (Wo - 1) * d.stride + d.KW;
+    LayoutGeom g{};
+    if (layout == IM2WIN_LAYOUT_ROW) {
+        // each channel's run of W_win*KH positions, padded to 8 elements so
+        // every channel (and every row) starts 16-byte aligned
+        g.Cin_pad = d.Cin;
+        g.pos_pad = round_up(Wwin * d.KH, 8);
+        g.row_elems = d.Cin * g.pos_pad;
+    } else {
+        // channels innermost, padded so that every window start
+        // (wo*stride*KH*Cin_pad) and every 8-element group is 16-byte aligned
+        const bool four = d.Cin <= 4 && (d.stride * d.KH) % 2 == 0;
+        g.Cin_pad = four ? 4 : round_up(d.Cin, 8);
+        g.pos_pad = Wwin * d.KH;
+        g.row_elems = round_up(Wwin * d.KH * g.Cin_pad, 8);
+    }
+    return g;
+}
+
+StageGeom stage_geom(const conv2d_desc_t &d, int32_t layout, int tile_m) {
+    (void)tile_m;
+    StageGeom s{};
+    if (layout == IM2WIN_LAYOUT_ROW) {
+        s.rows = round_up(d.Cout, kValuMt);
+        s.row_len = d.Cin * d.KH * d.KW;
+        s.needed = true;
+    } else {
+        const LayoutGeom g = layout_geom(d, layout);
+        const int64_t krun = d.KW * d.KH * g.Cin_pad;
+        s.rows = d.Cout;
+        s.row_len = round_up(krun, kMfmaKB);
+        // a 1x1 filter whose channel count needs no padding already is [Cout][K]
+        s.needed = !(d.KH == 1 && d.KW == 1 && g.Cin_pad == d.Cin && s.row_len == d.Cin);
+    }
+    return s;
+}
+
+static void pick_mfma_tile(const conv2d_desc_t &d, int64_t cols_per_chunk, int32_t *tm, int32_t *tn) {
+    (void)cols_per_chunk;
+    *tm = d.Cout <= 64 ? 64 : 128;
+    *tn = 128;
+}
+
+conv2d_status_t make_plan(const conv2d_desc_t &d, conv2d_plan_t *p) {
+    const conv2d_status_t st = check_desc(d);
+    if (st != CONV2D_OK) return st;
+    std::memset(p, 0, sizeof(*p));
+    const int64_t es = elem_size(d.dtype);
+    p->Ho = out_extent(d.H, d.KH, d.stride, d.pad);
+    p->Wo = out_extent(d.W, d.KW, d.stride, d.pad);
+    p->W_win = (p->Wo - 1) * d.stride + d.KW;
+    p->path = d.dtype == CONV2D_F32 ? 0 : 1;
+    p->layout = d.dtype == CONV2D_F32 ? IM2WIN_LAYOUT_ROW : IM2WIN_LAYOUT_CL;
+    const LayoutGeom g = layout_geom(d, p->layout);
+    p->Cin_pad = g.Cin_pad;
+    p->pos_pad = g.pos_pad;
+    p->row_elems = g.row_elems;
+    p->rows_total = d.N * p->Ho;
+    p->K = d.Cin * d.KH * d.KW;
+    p->flops = 2 * d.N * d.Cout * p->Ho * p->Wo * p->K;
+
+    if (p->path == 1) {
+        pick_mfma_tile(d, 0, &p->gemm_tile_m, &p->gemm_tile_n);
+    } else {
+        p->gemm_tile_m = 4 * kValuMt;
+        p->gemm_tile_n = 64 * kValuNt;
+    }
+    const StageGeom sg = stage_geom(d, p->layout, p->gemm_tile_m);
+    p->Cout_stage = sg.rows;
+    p->K_stage = sg.row_len;
+    if (sg.rows * sg.row_len > kMaxElems) return CONV2D_ERR_INVALID_DESC;
+    p->wstage_bytes = sg.needed ? round_up(sg.rows * sg.row_len * es, 256) : 0;
+
+    p->im2col_bytes = p->rows_total * p->Wo * p->K * es;
+    p->ws_target_bytes = p->im2col_bytes / d.KW;
+    const int64_t row_bytes = p->row_elems * es;
+    int64_t rmax = (p->ws_target_bytes - p->wstage_bytes) / row_bytes;
+    if (rmax < 1) rmax = 1;                       // the 1/KW target is out of reach
+    if (rmax > p->rows_total) rmax = p->rows_total;
+    // never exceed the 2^31-element limit inside one window chunk
+    const int64_t rlim = kMaxElems / p->row_elems;
+    if (rlim < 1) return CONV2D_ERR_INVALID_DESC;
+    if (rmax > rlim) rmax = rlim;
+    p->n_chunks = ceil_div(p->rows_total, rmax);
+    p->rows_per_chunk = ceil_div(p->rows_total, p->n_chunks);
+    p->win_offset_bytes = p->wstage_bytes;
+    p->win_chunk_bytes = p->rows_per_chunk * row_bytes;
+    p->ws_bytes = p->wstage_bytes + p->win_chunk_bytes;
+    p->meets_ws_target = p->ws_bytes <= p->ws_target_bytes ? 1 : 0;
+    return CONV2D_OK;
+}
+
+}  // namespace im2win

@@ -1,0 +1,59 @@
+// Host planner for the im2win forward convolution (no HIP dependency).
+//
+// Decides, for a layer descriptor: the output extent, the window-tensor
+// layout and its padding, the chunking of window rows that keeps the
+// workspace within 1/KW of the im2col buffer, the staged filter, and the
+// GEMM tiling. Window rows are r = n*Ho + ho; a window row holds
+// W_win = (Wo-1)*stride + KW padded input columns times KH filter rows
+// ("Enabling Memory-efficient Im2win Convolution ...", Sec. III-B, Eq. (2)).
+#pragma once
+
+#include <cstdint>
+
+#include "im2win_conv2d.h"
+
+namespace im2win {
+
+constexpr int64_t kMaxElems = (int64_t(1) << 31) - 1;
+
+// fp32 vector-ALU window-GEMM: each lane computes kValuMt output channels
+// times kValuNt consecutive output columns of one window row.
+constexpr int kValuMt = 16;
+constexpr int kValuNt = 4;
+constexpr int kValuThreads = 256;
+
+// Matrix-core window-GEMM: K staged through LDS in slices of kMfmaKB.
+constexpr int kMfmaKB = 32;
+constexpr int kMfmaThreads = 256;
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
+
+inline int64_t elem_size(int32_t dtype) { return dtype == CONV2D_F32 ? 4 : 2; }
+
+inline int64_t out_extent(int64_t in, int64_t k, int64_t s, int64_t p) {
+    const int64_t span = in + 2 * p - k;
+    if (s < 1 || k < 1 || p < 0 || span < 0) return 0;
+    return span / s + 1;
+}
+
+// Validate the descriptor alone (shapes, dtype, element-count limits).
+conv2d_status_t check_desc(const conv2d_desc_t &d);
+
+// Geometry of one layout (no chunking): Cin_pad, pos_pad, row_elems.
+struct LayoutGeom {
+    int64_t Cin_pad, pos_pad, row_elems;
+};
+LayoutGeom layout_geom(const conv2d_desc_t &d, int32_t layout);
+
+// Staged-filter geometry for one layout: rows and row length (elements).
+struct StageGeom {
+    int64_t rows, row_len;
+    bool needed;   // false when w is already in the staged order
+};
+StageGeom stage_geom(const conv2d_desc_t &d, int32_t layout, int tile_m);
+
+// Full plan (fills the C struct). Returns CONV2D_OK or a validation error.
+conv2d_status_t make_plan(const conv2d_desc_t &d, conv2d_plan_t *p);
+
+}  // namespace im2win

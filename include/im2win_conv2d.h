@@ -1,0 +1,178 @@
+/*
+ * im2win forward 2-D convolution for AMD Instinct MI355X (gfx950) -- C ABI.
+ *
+ * The operation (every entry point below serves it):
+ *
+ *   Ho = floor((H + 2*pad - KH) / stride) + 1,  Wo = floor((W + 2*pad - KW) / stride) + 1
+ *   y[n][co][ho][wo] = sum_{ci, kh, kw} xp[n][ci][ho*stride + kh - pad][wo*stride + kw - pad]
+ *                                       * w[co][ci][kh][kw]
+ *
+ * with xp = x zero-padded by `pad` on all four sides: a cross-correlation (no
+ * kernel flip), one stride and one padding for both axes, no bias, dilation
+ * or groups. Sources: "Enabling Memory-efficient Im2win Convolution with
+ * Multi-precision Support on GPU CUDA and Tensor Cores", Sec. III-A Eq. (1)
+ * (the sum), Sec. III-B Eq. (2) (the window tensor), Sec. III-C Eq. (3) and
+ * Sec. III-D with Algorithm 1 (the window contraction as a GEMM with
+ * M = Cout, N = N*Ho*Wo, K = Cin*KH*KW); the padded output extent of
+ * "Unifying Convolutions and GEMM", Sec. 5.
+ *
+ * How it runs: the input is repacked, one chunk of window rows (n, ho) at a
+ * time, into the im2win window tensor held in the caller's workspace; the
+ * filter is restaged once per call into the window's K order; a window-GEMM
+ * kernel contracts each chunk into y. fp32 inputs run on the vector ALUs,
+ * fp16/bf16 inputs on the matrix cores with fp32 accumulation. The chunk size
+ * keeps the workspace at most 1/KW of the im2col buffer whenever one window
+ * row fits in that budget.
+ *
+ * Layouts: x, w, y are dense, contiguous NCHW: x [N][Cin][H][W] of `dtype`,
+ * w [Cout][Cin][KH][KW] of `dtype`, y [N][Cout][Ho][Wo] of float (fp32 for
+ * every input dtype).
+ *
+ * Pointers: x, w, y, ws and the pack/stage outputs are DEVICE pointers the
+ * caller allocates and owns. The library allocates no device memory and
+ * keeps no state between calls (apart from the optional profiling records
+ * below). `stream` is a hipStream_t passed as void*; NULL means the default
+ * stream. All GPU work is enqueued on `stream` and the calls return without
+ * synchronising; results are valid once the stream's work completes.
+ *
+ * Errors: every entry point validates its arguments before enqueueing any
+ * work; on an error nothing is launched and no output is touched. No entry
+ * point aborts or exits. Every buffer must hold fewer than 2^31 elements.
+ *
+ * Thread safety: all entry points are reentrant; calls that share a
+ * workspace must be ordered by the caller (same stream, or events).
+ */
+#ifndef IM2WIN_CONV2D_H
+#define IM2WIN_CONV2D_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Storage type of x and w (y is always fp32). */
+typedef enum {
+    CONV2D_F32 = 0,   /* IEEE binary32; runs on the vector ALUs               */
+    CONV2D_F16 = 1,   /* IEEE binary16; matrix cores, fp32 accumulation        */
+    CONV2D_BF16 = 2   /* bfloat16; matrix cores, fp32 accumulation             */
+} conv2d_dtype_t;
+
+/* The layer. All sizes in elements. */
+typedef struct {
+    int64_t N, Cin, H, W;     /* input batch, channels, height, width          */
+    int64_t Cout, KH, KW;     /* filters, filter height, filter width          */
+    int64_t stride, pad;      /* one stride and one zero padding for both axes */
+    int32_t dtype;            /* a conv2d_dtype_t                              */
+    int32_t reserved;         /* must be 0                                     */
+} conv2d_desc_t;
+
+typedef enum {
+    CONV2D_OK = 0,
+    CONV2D_ERR_INVALID_DESC = 1,  /* a size < 1 (pad < 0), no output, reserved != 0,
+                                     or a buffer of 2^31 elements or more            */
+    CONV2D_ERR_NULL_POINTER = 2,  /* a required pointer is NULL                     */
+    CONV2D_ERR_MISALIGNED = 3,    /* x, w, y or an output not 16-byte aligned;
+                                     ws not 256-byte aligned                        */
+    CONV2D_ERR_UNSUPPORTED = 4,   /* unknown dtype or layout for this call          */
+    CONV2D_ERR_WORKSPACE = 5,     /* ws NULL although a workspace is needed         */
+    CONV2D_ERR_HIP = 6,           /* the HIP runtime reported an error on launch    */
+    CONV2D_ERR_RANGE = 7          /* a row range outside [0, N*Ho)                  */
+} conv2d_status_t;
+
+/* Storage orders of the window tensor (Eq. (2) of the im2win paper, with r =
+ * n*Ho + ho a window row, pos = w*KH + kh, w < W_win = (Wo-1)*stride + KW a
+ * padded input column, and the value xp[n][ci][ho*stride + kh][w]):
+ *   ROW : T[r][ci][pos]   channel outermost, the paper's order; the window of
+ *         output column wo is the run pos in [wo*stride*KH, (wo*stride+KW)*KH)
+ *         of each channel. Used by the fp32 path.
+ *   CL  : T[r][pos][ci]   channels innermost; the window of column wo is ONE
+ *         contiguous run of KW*KH*Cin_pad elements. Used by the fp16/bf16
+ *         path. Cin is zero-padded to Cin_pad (see conv2d_plan_t). */
+typedef enum { IM2WIN_LAYOUT_ROW = 0, IM2WIN_LAYOUT_CL = 1 } im2win_layout_t;
+
+/* What conv2d_fwd will do for a descriptor (host-side only, no GPU needed). */
+typedef struct {
+    int64_t Ho, Wo, W_win;        /* output extent; padded columns per window row */
+    int32_t path;                 /* 0: fp32 vector ALU, 1: fp16/bf16 matrix core  */
+    int32_t layout;               /* an im2win_layout_t                           */
+    int64_t Cin_pad;              /* channels stored per position (CL) or Cin     */
+    int64_t pos_pad;              /* ROW: positions stored per channel (>= W_win*KH) */
+    int64_t row_elems;            /* elements of one window row in the workspace  */
+    int64_t rows_total;           /* N*Ho                                         */
+    int64_t rows_per_chunk;       /* window rows packed and contracted per chunk  */
+    int64_t n_chunks;
+    int64_t K;                    /* Cin*KH*KW                                    */
+    int64_t K_stage;              /* staged filter row length (K order, padded)   */
+    int64_t Cout_stage;           /* staged filter rows (Cout padded)             */
+    int64_t wstage_bytes;         /* staged filter, at the start of ws            */
+    int64_t win_offset_bytes;     /* where the window chunk starts in ws          */
+    int64_t win_chunk_bytes;      /* window chunk buffer                          */
+    int64_t ws_bytes;             /* total workspace = conv2d_workspace_size()     */
+    int64_t im2col_bytes;         /* N*Ho*Wo*Cin*KH*KW*sizeof(dtype)              */
+    int64_t ws_target_bytes;      /* im2col_bytes / KW                            */
+    int32_t meets_ws_target;      /* ws_bytes <= ws_target_bytes                  */
+    int32_t gemm_tile_m, gemm_tile_n;
+    int32_t reserved0;
+    int64_t flops;                /* 2*N*Cout*Ho*Wo*Cin*KH*KW (padded taps included) */
+} conv2d_plan_t;
+
+/* Bytes of workspace conv2d_fwd needs for *d (0 if d is invalid). */
+size_t conv2d_workspace_size(const conv2d_desc_t *d);
+
+/* Fill *out with the plan for *d. Host only; never touches a GPU. */
+conv2d_status_t conv2d_plan(const conv2d_desc_t *d, conv2d_plan_t *out);
+
+/* y = conv2d(x, w) as defined at the top of this file.
+ * ws: device buffer of at least conv2d_workspace_size(d) bytes, 256-byte
+ * aligned (NULL allowed only when that size is 0); its contents on return
+ * are unspecified. x, w, y: 16-byte aligned device pointers. */
+conv2d_status_t conv2d_fwd(const conv2d_desc_t *d, const void *x, const void *w, float *y,
+                           void *ws, void *stream);
+
+/* Row (a2) on its own: write window rows [row0, row0 + rows) of the window
+ * tensor of x (Eq. (2) of the im2win paper, zero padding included) in the
+ * given layout to `out`, with the row length, Cin_pad and pos_pad that
+ * conv2d_plan reports for that layout. A pure copy: every value is bit-equal
+ * to an element of x or zero. out must hold rows * row_elems elements of
+ * dtype and be 16-byte aligned. */
+conv2d_status_t im2win_pack(const conv2d_desc_t *d, int32_t layout, const void *x, void *out,
+                            int64_t row0, int64_t rows, void *stream);
+
+/* Row (a3) on its own: restage w into the K order of the window of `layout`:
+ *   ROW: out[cb][ci][kh][kw][j] = w[cb*16 + j][ci][kh][kw], j < 16, Cout padded
+ *        to a multiple of 16 with zeros (fp32 path);
+ *   CL : out[co][(kw*KH + kh)*Cin_pad + ci] = w[co][ci][kh][kw], rows padded to
+ *        Cout_stage and to K_stage with zeros.
+ * out holds Cout_stage * K_stage elements of dtype and is 16-byte aligned. */
+conv2d_status_t im2win_weight_stage(const conv2d_desc_t *d, int32_t layout, const void *w,
+                                    void *out, void *stream);
+
+const char *conv2d_status_string(conv2d_status_t s);
+
+/* ---- measurement hook --------------------------------------------------
+ * While enabled, conv2d_fwd records a HIP event pair around every kernel it
+ * launches (on the call's stream). conv2d_profile_read synchronises on the
+ * recorded events, returns per-kernel totals since the last read, and clears
+ * them. Not for concurrent use from several threads. */
+typedef enum {
+    CONV2D_KERNEL_WEIGHT_STAGE = 0,
+    CONV2D_KERNEL_PACK = 1,
+    CONV2D_KERNEL_GEMM = 2,
+    CONV2D_KERNEL_KINDS = 3
+} conv2d_kernel_kind_t;
+
+typedef struct {
+    int64_t launches[CONV2D_KERNEL_KINDS];
+    double total_ms[CONV2D_KERNEL_KINDS];
+} conv2d_profile_t;
+
+conv2d_status_t conv2d_profile_enable(int32_t on);
+conv2d_status_t conv2d_profile_read(conv2d_profile_t *out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* IM2WIN_CONV2D_H */

@@ -1,0 +1,301 @@
+"""GPU parity: the HIP path against the CPU oracle, through the C ABI.
+
+Tolerances (relative L2 over the compared outputs, oracle in float64 fed the
+same rounded inputs): fp32 <= 1e-5, fp16 <= 2e-3, bf16 <= 1e-2. Integer-valued
+inputs must match bit for bit (every product and partial sum is exact in the
+kernels' fp32 accumulators). The im2win pack and the filter staging are pure
+copies and must be bit-identical to their definitions.
+"""
+import ctypes
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import cnn_convolution_amd as conv
+from cnn_convolution_amd import _lib
+import oracle
+from oracle.im2win_model import im2win
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-5, "f16": 2e-3, "bf16": 1e-2}
+CODE = {"f32": conv.F32, "f16": conv.F16, "bf16": conv.BF16}
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    _lib.lib()   # the HIP library must load: no fallback
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def rel_l2(got, ref):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    den = np.linalg.norm(ref)
+    return float(np.linalg.norm(got - ref) / (den if den > 0 else 1.0))
+
+
+def run_conv(x, w, s, p):
+    y = conv.conv2d(x.to(DEV), w.to(DEV), stride=s, pad=p)
+    torch.cuda.synchronize()
+    return y.cpu()
+
+
+# ----------------------------------------------------------------- pack (a2)
+
+PACK_CASES = [
+    # N, C, H, W, KH, KW, s, p
+    (2, 3, 8, 9, 3, 3, 1, 1),
+    (1, 16, 14, 14, 3, 3, 1, 1),
+    (2, 8, 11, 13, 2, 3, 2, 1),
+    (1, 3, 23, 21, 7, 7, 2, 3),
+    (2, 72, 7, 7, 3, 3, 1, 1),       # two channel blocks, ragged
+    (1, 5, 9, 70, 5, 4, 1, 2),       # wide rows: several column blocks
+    (3, 64, 6, 6, 1, 1, 1, 0),
+    (1, 8, 12, 12, 9, 9, 1, 4),      # KH > 8: two filter-row passes
+]
+
+
+@pytest.mark.parametrize("case", PACK_CASES)
+@pytest.mark.parametrize("dt,layout", [("f32", conv.LAYOUT_ROW), ("f16", conv.LAYOUT_ROW),
+                                        ("f16", conv.LAYOUT_CL), ("bf16", conv.LAYOUT_CL)])
+def test_pack_bit_exact(case, dt, layout):
+    N, C, H, W, KH, KW, s, p = case
+    _say(f"pack {dt} layout={layout} {case}")
+    x = workloads.make_tensor((N, C, H, W), "normal", seed=5, dtype=dt)
+    xd = x.to(DEV)
+    d = conv.describe(tuple(x.shape), (1, C, KH, KW), s, p, CODE[dt])
+    total = conv.plan(d).rows_total
+    ref, Ho, Wo, Wwin = im2win(x.view(torch.int16 if dt != "f32" else torch.int32).numpy(),
+                               KH, KW, s, p, "row" if layout == conv.LAYOUT_ROW else "cl")
+    for row0, rows in [(0, total), (total // 3, max(1, total // 2)), (total - 1, 1)]:
+        out, geo = conv.pack(xd, KH, KW, s, p, layout, row0, rows)
+        torch.cuda.synchronize()
+        bits = out.cpu().view(torch.int16 if dt != "f32" else torch.int32).numpy()
+        bits = bits.reshape(rows, geo["row_elems"])
+        want = ref[row0:row0 + rows]
+        if layout == conv.LAYOUT_ROW:
+            body = bits[:, :C * geo["pos_pad"]].reshape(rows, C, geo["pos_pad"])
+            assert np.array_equal(body[:, :, :Wwin * KH], want)
+            assert np.all(body[:, :, Wwin * KH:] == 0)
+        else:
+            cp = geo["Cin_pad"]
+            body = bits[:, :Wwin * KH * cp].reshape(rows, Wwin * KH, cp)
+            assert np.array_equal(body[:, :, :C], want)
+            assert np.all(body[:, :, C:] == 0)
+            assert np.all(bits[:, Wwin * KH * cp:] == 0)
+
+
+# ----------------------------------------------------------------- filter staging (a3)
+
+@pytest.mark.parametrize("shape", [(16, 3, 3, 3), (20, 5, 2, 3), (64, 3, 7, 7), (40, 72, 3, 3),
+                                   (256, 64, 1, 1)])
+@pytest.mark.parametrize("dt,layout", [("f32", conv.LAYOUT_ROW), ("f16", conv.LAYOUT_CL),
+                                        ("bf16", conv.LAYOUT_CL)])
+def test_weight_stage_bit_exact(shape, dt, layout):
+    Cout, Cin, KH, KW = shape
+    _say(f"weight_stage {dt} layout={layout} {shape}")
+    w = workloads.make_tensor(shape, "normal", seed=6, dtype=dt)
+    out, geo = conv.weight_stage(w.to(DEV), 1, 1, (16, 16), layout)
+    torch.cuda.synchronize()
+    ity = torch.int32 if dt == "f32" else torch.int16
+    got = out.cpu().view(ity).numpy()
+    wb = w.view(ity).numpy()
+    if layout == conv.LAYOUT_ROW:
+        rows = geo["rows"]
+        want = np.zeros((rows, Cin, KH, KW), wb.dtype)
+        want[:Cout] = wb
+        # [cb][ci][kh][kw][16]: 16 output channels innermost
+        want = want.reshape(rows // 16, 16, Cin, KH, KW).transpose(0, 2, 3, 4, 1)
+        assert np.array_equal(got, want.reshape(-1))
+    else:
+        d = conv.describe((1, Cin, 16, 16), shape, 1, 1, CODE[dt])
+        cp = conv.plan(d).Cin_pad
+        want = np.zeros((Cout, KW, KH, cp), wb.dtype)
+        want[:, :, :, :Cin] = wb.transpose(0, 3, 2, 1)       # [co][kw][kh][ci]
+        want = want.reshape(Cout, -1)
+        full = np.zeros((Cout, geo["row_len"]), wb.dtype)
+        full[:, :want.shape[1]] = want
+        assert np.array_equal(got.reshape(Cout, -1), full)
+
+
+# ----------------------------------------------------------------- the convolution
+
+def _random_cases(seed, n):
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        KH, KW = int(rng.integers(1, 8)), int(rng.integers(1, 8))
+        s = int(rng.integers(1, 4))
+        p = int(rng.integers(0, max(KH, KW)))
+        H, W = int(rng.integers(1, 40)), int(rng.integers(1, 40))
+        if H + 2 * p < KH or W + 2 * p < KW:
+            continue
+        out.append((int(rng.integers(1, 4)), int(rng.integers(1, 40)), H, W,
+                    int(rng.integers(1, 150)), KH, KW, s, p))
+    return out
+
+
+FIXED = [
+    # N, Cin, H, W, Cout, KH, KW, s, p   -- several tiles plus ragged tails
+    (2, 3, 32, 32, 16, 3, 3, 1, 1),
+    (3, 64, 17, 19, 70, 3, 3, 1, 1),
+    (2, 24, 30, 29, 130, 3, 3, 2, 1),
+    (2, 3, 45, 47, 64, 7, 7, 2, 3),
+    (1, 40, 15, 15, 96, 5, 5, 1, 2),
+    (2, 128, 9, 7, 200, 3, 3, 1, 1),
+    (4, 64, 10, 10, 256, 1, 1, 1, 0),
+    (1, 5, 13, 11, 9, 2, 4, 3, 2),
+    (2, 6, 7, 9, 33, 7, 7, 1, 3),
+    (1, 1, 1, 1, 1, 1, 1, 1, 0),
+    (1, 2, 1, 1, 3, 3, 3, 1, 1),       # 1x1 image, 3x3 filter, pad 1: one output
+    (2, 3, 5, 4, 6, 5, 4, 1, 0),       # dense-as-conv: 1x1 output
+    (1, 4, 6, 6, 5, 3, 3, 4, 0),       # stride larger than the filter
+    (1, 3, 4, 4, 2, 3, 3, 1, 5),       # padding wider than the filter: zero border
+]
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("shape", FIXED + _random_cases(21, 16))
+def test_conv_matches_oracle(shape, dt):
+    N, Cin, H, W, Cout, KH, KW, s, p = shape
+    _say(f"conv {dt} {shape}")
+    x, w = workloads.make_inputs(N, Cin, H, W, Cout, KH, KW, seed=sum(shape), dtype=dt,
+                                 w_dist="normal")
+    y = run_conv(x, w, s, p)
+    ref = oracle.conv2d(x, w, s, p)
+    assert tuple(y.shape) == ref.shape
+    err = rel_l2(y.numpy(), ref)
+    assert err <= TOL[dt], f"rel L2 {err:.3e} > {TOL[dt]}"
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("shape", [(2, 3, 32, 32, 16, 3, 3, 1, 1), (2, 32, 15, 14, 72, 3, 3, 2, 1),
+                                   (1, 3, 30, 30, 64, 7, 7, 2, 3), (2, 64, 8, 8, 128, 1, 1, 1, 0),
+                                   (1, 16, 12, 12, 40, 5, 5, 1, 2)])
+def test_integer_inputs_bit_exact(shape, dt):
+    N, Cin, H, W, Cout, KH, KW, s, p = shape
+    _say(f"conv-int {dt} {shape}")
+    x, w = workloads.make_inputs(N, Cin, H, W, Cout, KH, KW, seed=3, dtype=dt,
+                                 x_dist="int3", w_dist="int3")
+    y = run_conv(x, w, s, p)
+    ref = oracle.conv2d(x, w, s, p)
+    assert np.array_equal(y.numpy().astype(np.float64), ref)
+
+
+def test_outputs_in_padding_are_exactly_zero():
+    x, w = workloads.make_inputs(1, 3, 4, 4, 2, 3, 3, seed=1, dtype="f16")
+    y = run_conv(x, w, 1, 5)
+    ref = oracle.conv2d(x, w, 1, 5)
+    assert np.array_equal(y.numpy() == 0, ref == 0)
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16"])
+def test_guard_bands_untouched(dt):
+    """y and the workspace sit inside larger buffers filled with a canary:
+    nothing outside the requested ranges may change."""
+    N, Cin, H, W, Cout, KH, KW, s, p = 2, 10, 13, 11, 21, 3, 3, 1, 1
+    x, w = workloads.make_inputs(N, Cin, H, W, Cout, KH, KW, seed=2, dtype=dt)
+    d = conv.describe(tuple(x.shape), tuple(w.shape), s, p, CODE[dt])
+    pl = conv.plan(d)
+    ny = N * Cout * pl.Ho * pl.Wo
+    guard = 4096
+    ybuf = torch.full((guard + ny + guard,), 12345.0, dtype=torch.float32, device=DEV)
+    wsbuf = torch.full((guard + pl.ws_bytes + guard,), 0xA5, dtype=torch.uint8, device=DEV)
+    y = ybuf[guard:guard + ny]
+    ws = wsbuf[guard:guard + pl.ws_bytes]
+    assert ws.data_ptr() % 256 == 0
+    xd, wd = x.to(DEV), w.to(DEV)
+    st = _lib.fwd(d, xd.data_ptr(), wd.data_ptr(), y.data_ptr(), ws.data_ptr(),
+                  torch.cuda.current_stream().cuda_stream)
+    assert st == 0
+    torch.cuda.synchronize()
+    yb = ybuf.cpu()
+    assert torch.all(yb[:guard] == 12345.0) and torch.all(yb[guard + ny:] == 12345.0)
+    wb = wsbuf.cpu()
+    assert torch.all(wb[:guard] == 0xA5) and torch.all(wb[guard + pl.ws_bytes:] == 0xA5)
+    ref = oracle.conv2d(x, w, s, p)
+    assert rel_l2(y.cpu().numpy().reshape(ref.shape), ref) <= TOL[dt]
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
+def test_repeatable_bits(dt):
+    x, w = workloads.make_inputs(4, 32, 20, 20, 48, 3, 3, seed=4, dtype=dt)
+    a = run_conv(x, w, 1, 1)
+    b = run_conv(x, w, 1, 1)
+    assert torch.equal(a, b)
+
+
+def test_profile_hook_counts_launches():
+    x, w = workloads.make_inputs(2, 16, 12, 12, 32, 3, 3, seed=1, dtype="f16")
+    xd, wd = x.to(DEV), w.to(DEV)
+    d = conv.describe(tuple(x.shape), tuple(w.shape), 1, 1, conv.F16)
+    pl = conv.plan(d)
+    conv.profile_read()
+    conv.profile_enable(True)
+    try:
+        conv.conv2d(xd, wd, 1, 1)
+        conv.conv2d(xd, wd, 1, 1)
+    finally:
+        conv.profile_enable(False)
+    prof = conv.profile_read()
+    assert prof["pack"]["launches"] == 2 * pl.n_chunks
+    assert prof["gemm"]["launches"] == 2 * pl.n_chunks
+    assert prof["weight_stage"]["launches"] == 2
+    assert all(v["total_ms"] >= 0 for v in prof.values())
+
+
+# ----------------------------------------------------------------- full-size layers
+
+def _sample_indices(N, Cout, Ho, Wo, rows_per_chunk, rng, count=3000):
+    idx = set(rng.integers(0, N * Cout * Ho * Wo, count).tolist())
+    rows = N * Ho
+    edge_rows = {0, rows - 1}
+    r = rows_per_chunk
+    while r < rows:
+        edge_rows.update({r - 1, r})
+        r += rows_per_chunk
+    cos = sorted({0, Cout - 1, Cout // 2} | set(rng.integers(0, Cout, 3).tolist()))
+    for rr in edge_rows:
+        n, ho = divmod(rr, Ho)
+        for co in cos:
+            for wo in {0, 1, Wo // 2, Wo - 2, Wo - 1}:
+                if 0 <= wo < Wo:
+                    idx.add(((n * Cout + co) * Ho + ho) * Wo + wo)
+    return np.array(sorted(idx), dtype=np.int64)
+
+
+FULL = [(name, dt) for name, cfg in sorted(workloads.CONFIGS.items()) for dt in cfg.dtypes]
+
+
+@pytest.mark.parametrize("name,dt", FULL)
+def test_full_size_layers_sampled(name, dt):
+    """At the measured sizes and in the launch configuration the benchmark
+    times: sampled outputs (random, plus borders and chunk boundaries)
+    against the oracle computed point by point."""
+    cfg = workloads.get_config(name)
+    _say(f"full-size {name} {dt} {cfg.desc()}")
+    x, w = workloads.make_config_inputs(cfg, dt)
+    d = conv.describe(tuple(x.shape), tuple(w.shape), cfg.stride, cfg.pad, CODE[dt])
+    pl = conv.plan(d)
+    assert pl.meets_ws_target == 1
+    y = run_conv(x, w, cfg.stride, cfg.pad)
+    ho, wo = cfg.out_hw()
+    assert tuple(y.shape) == (cfg.N, cfg.Cout, ho, wo)
+    yf = y.numpy().reshape(-1)
+    assert np.isfinite(yf).all()
+    rng = np.random.default_rng(cfg.seed)
+    idx = _sample_indices(cfg.N, cfg.Cout, ho, wo, pl.rows_per_chunk, rng)
+    ref = oracle.conv2d_points(x, w, cfg.stride, cfg.pad, idx)
+    err = rel_l2(yf[idx], ref)
+    assert err <= TOL[dt], f"{name} {dt}: rel L2 {err:.3e} > {TOL[dt]}"

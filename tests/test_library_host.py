@@ -1,0 +1,142 @@
+"""Host-side checks of the HIP library (no GPU needed): the shared library
+loads, exports every entry point the header declares, plans every layer,
+honours the workspace target, and rejects bad arguments before touching
+the GPU."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import cnn_convolution_amd as conv
+from cnn_convolution_amd import _lib
+import workloads
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "im2win_conv2d.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z0-9_]+)\s*\([^;{]*\)\s*;", text)))
+
+
+def test_header_declarations_match_binding():
+    assert _declared_functions() == sorted(_lib.EXPORTS)
+
+
+def test_library_exports_every_symbol():
+    L = _lib.lib()
+    for name in _lib.EXPORTS:
+        assert hasattr(L, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIBPATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for name in _lib.EXPORTS:
+        assert name in exported, name
+
+
+def test_device_code_is_gfx950_only():
+    data = open(_lib.LIBPATH, "rb").read()
+    targets = set(re.findall(rb"amdgcn-amd-amdhsa--(gfx[0-9a-z]+)", data))
+    assert targets == {b"gfx950"}
+
+
+def test_status_strings():
+    for code in range(8):
+        s = conv.status_string(code)
+        assert s and s != "unknown status"
+    assert conv.status_string(99) == "unknown status"
+
+
+@pytest.mark.parametrize("name", sorted(workloads.CONFIGS))
+def test_plans_of_the_measured_layers(name):
+    cfg = workloads.get_config(name)
+    for dt in cfg.dtypes:
+        code = {"f32": conv.F32, "f16": conv.F16, "bf16": conv.BF16}[dt]
+        d = conv.make_desc(*cfg.desc().values(), code)
+        p = conv.plan(d)
+        ho, wo = cfg.out_hw()
+        assert (p.Ho, p.Wo) == (ho, wo)
+        assert p.W_win == (wo - 1) * cfg.stride + cfg.KW
+        assert p.rows_total == cfg.N * ho
+        assert p.n_chunks * p.rows_per_chunk >= p.rows_total
+        assert (p.n_chunks - 1) * p.rows_per_chunk < p.rows_total
+        esz = 4 if dt == "f32" else 2
+        assert p.im2col_bytes == cfg.N * ho * wo * cfg.Cin * cfg.KH * cfg.KW * esz
+        assert p.ws_target_bytes == p.im2col_bytes // cfg.KW
+        # the workspace target: at most 1/KW of the im2col buffer
+        assert p.meets_ws_target == 1 and p.ws_bytes <= p.ws_target_bytes, (name, dt)
+        assert conv.workspace_size(d) == p.ws_bytes
+        assert p.flops == workloads.nominal_flops(**cfg.desc())
+        assert p.path == (0 if dt == "f32" else 1)
+        assert p.layout == (conv.LAYOUT_ROW if dt == "f32" else conv.LAYOUT_CL)
+        # window rows and chunk buffer stay 16-byte aligned
+        assert (p.row_elems * esz) % 16 == 0
+        assert p.win_offset_bytes % 256 == 0
+
+
+def test_plan_layout_geometry():
+    d = conv.make_desc(32, 3, 224, 224, 64, 7, 7, 2, 3, conv.F16)
+    p = conv.plan(d)
+    assert p.Cin_pad == 4               # 3 channels, stride*KH even: padded to 4
+    assert p.K_stage % 32 == 0 and p.K_stage >= 7 * 7 * 4
+    d = conv.make_desc(1, 3, 32, 32, 16, 3, 3, 1, 1, conv.F16)
+    assert conv.plan(d).Cin_pad == 8    # stride*KH odd: padded to 8
+    d = conv.make_desc(1, 3, 32, 32, 16, 3, 3, 1, 1, conv.F32)
+    p = conv.plan(d)
+    assert p.Cin_pad == 3 and p.pos_pad % 8 == 0 and p.pos_pad >= 34 * 3
+    d = conv.make_desc(64, 64, 56, 56, 256, 1, 1, 1, 0, conv.F16)
+    p = conv.plan(d)
+    assert p.wstage_bytes == 0          # 1x1 filter already in K order
+
+
+def test_unreachable_target_is_reported():
+    # dense-as-conv: one window row alone exceeds 1/KW of im2col
+    d = conv.make_desc(2, 3, 5, 4, 6, 5, 4, 1, 0, conv.F32)
+    p = conv.plan(d)
+    assert p.Ho == 1 and p.Wo == 1 and p.meets_ws_target == 0
+    assert p.rows_per_chunk == 1 and p.n_chunks == 2
+
+
+@pytest.mark.parametrize("bad", [
+    dict(N=0), dict(Cin=0), dict(H=0), dict(W=-1), dict(Cout=0), dict(KH=0), dict(KW=0),
+    dict(stride=0), dict(pad=-1), dict(H=2, KH=5), dict(reserved=1),
+    dict(N=1 << 21), dict(N=4096, Cin=4096, H=64, W=64),
+])
+def test_invalid_descriptors_rejected(bad):
+    f = dict(N=1, Cin=3, H=8, W=8, Cout=4, KH=3, KW=3, stride=1, pad=1, dtype=conv.F32,
+             reserved=0)
+    f.update(bad)
+    d = _lib.Desc(**f)
+    assert conv.workspace_size(d) == 0
+    p = _lib.Plan()
+    assert _lib.lib().conv2d_plan(ctypes.byref(d), ctypes.byref(p)) == 1
+    # conv2d_fwd validates before touching any pointer or the GPU
+    assert _lib.fwd(d, 16, 16, 16, 256, None) == 1
+
+
+def test_unknown_dtype_rejected():
+    d = _lib.Desc(1, 3, 8, 8, 4, 3, 3, 1, 1, 7, 0)
+    assert _lib.fwd(d, 16, 16, 16, 256, None) == 4
+
+
+def test_pointer_checks_before_launch():
+    d = conv.make_desc(1, 3, 8, 8, 4, 3, 3, 1, 1, conv.F32)
+    ws = conv.workspace_size(d)
+    assert ws > 0
+    assert _lib.fwd(d, None, 16, 16, 256, None) == 2
+    assert _lib.fwd(d, 16, None, 16, 256, None) == 2
+    assert _lib.fwd(d, 16, 16, None, 256, None) == 2
+    assert _lib.fwd(d, 16, 16, 16, None, None) == 5
+    assert _lib.fwd(d, 8, 16, 16, 256, None) == 3
+    assert _lib.fwd(d, 16, 16, 20, 256, None) == 3
+    assert _lib.fwd(d, 16, 16, 16, 16, None) == 3          # ws must be 256-byte aligned
+    assert _lib.pack(d, 0, 16, 16, 0, 0, None) == 7         # empty row range
+    assert _lib.pack(d, 0, 16, 16, 5, 4, None) == 7         # past N*Ho
+    assert _lib.pack(d, 1, 16, 16, 0, 1, None) == 4         # channels-last is half precision
+    assert _lib.pack(d, 2, 16, 16, 0, 1, None) == 4
+    assert _lib.weight_stage(d, 3, 16, 16, None) == 4
+    assert _lib.pack(d, 0, None, 16, 0, 1, None) == 2
