@@ -178,6 +178,7 @@ def main():
     ap.add_argument("--dtype", default=None, help="headline dtype (default: the layer's "
                     "half-precision variant if it has one)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--single", action="store_true", help="time the headline dtype only")
     ap.add_argument("--all-configs", action="store_true",
                     help="one JSON line per layer and dtype (profiling / results table)")
     args = ap.parse_args()
@@ -203,7 +204,7 @@ def main():
         dts = list(cfg.dtypes)
         head = args.dtype if args.dtype and args.dtype in dts else \
             next((d for d in dts if d != "f32"), dts[0])
-        order = [head] + [d for d in dts if d != head]
+        order = [head] + ([] if args.single else [d for d in dts if d != head])
         results = {}
         for dt in order:
             _say(f"bench: {name} {dt} warmup={args.warmup} steps={args.steps}")

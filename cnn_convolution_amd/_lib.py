@@ -45,7 +45,8 @@ _PLAN_FIELDS = [
     ("win_chunk_bytes", ctypes.c_int64), ("ws_bytes", ctypes.c_int64),
     ("im2col_bytes", ctypes.c_int64), ("ws_target_bytes", ctypes.c_int64),
     ("meets_ws_target", ctypes.c_int32), ("gemm_tile_m", ctypes.c_int32),
-    ("gemm_tile_n", ctypes.c_int32), ("reserved0", ctypes.c_int32),
+    ("gemm_tile_n", ctypes.c_int32), ("gemm_kslice", ctypes.c_int32),
+    ("gemm_ksplit", ctypes.c_int32), ("reserved0", ctypes.c_int32),
     ("flops", ctypes.c_int64),
 ]
 

@@ -192,6 +192,7 @@ conv2d_status_t conv2d_fwd(const conv2d_desc_t *d, const void *x, const void *w,
             ga.Wo = int(p.Wo);
             ga.Cout = int(d->Cout);
             ga.Cout_stage = int(p.Cout_stage);
+            ga.ksplit = p.gemm_ksplit;
             e = launch_gemm_valu_f32(ga, s);
         } else {
             MfmaGemmArgs ga{};
@@ -209,6 +210,8 @@ conv2d_status_t conv2d_fwd(const conv2d_desc_t *d, const void *x, const void *w,
             ga.Cout = int(d->Cout);
             ga.tile_m = p.gemm_tile_m;
             ga.tile_n = p.gemm_tile_n;
+            ga.kb = p.gemm_kslice;
+            ga.ks = p.gemm_ksplit;
             ga.bf16 = d->dtype == CONV2D_BF16 ? 1 : 0;
             e = launch_gemm_mfma(ga, s);
         }

@@ -10,13 +10,14 @@
 // K order (kw outer, kh, channel inner). Overlapping windows of neighbouring
 // columns are the same bytes of T, served by L1/L2.
 //
-// Tiles. A workgroup of 4 waves computes an MB x NB tile; K advances in
-// slices of 32 through two LDS buffers (ping-pong: the global loads of slice
-// k+1 are in flight while slice k is multiplied). Each wave multiplies
-// (MB/WM) x (NB/WN) with v_mfma_f32_16x16x32_{f16,bf16}: A and B fragments
-// are 8 consecutive K values per lane (one 16-byte LDS read), so any
-// consistent K order is valid. LDS rows are padded by 16 bytes so that the
-// fragment reads hit 32 distinct banks.
+// Tiles. A workgroup computes an MB x NB tile; K advances in stages of
+// KS*KB through two LDS buffers (ping-pong: the global loads of stage k+1 are
+// in flight while stage k is multiplied). KS groups of 4 waves split every
+// stage (intra-workgroup split-K) and are summed through LDS at the end.
+// Each wave multiplies (MB/WM) x (NB/WN) with v_mfma_f32_16x16x32_{f16,bf16}:
+// A and B fragments are 8 consecutive K values per lane (one 16-byte LDS
+// read), so any consistent K order is valid. LDS rows are padded by 16 bytes
+// so that the fragment reads hit 32 distinct banks.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -31,9 +32,6 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
-constexpr int KB = 32;           // K slice per LDS stage (one MFMA K step)
-constexpr int PITCH = KB + 8;    // halves per LDS row: 80 bytes
-
 template <bool BF16>
 __device__ __forceinline__ floatx4 mfma16(const uint4 &a, const uint4 &b, const floatx4 &c)
 {
@@ -46,19 +44,24 @@ __device__ __forceinline__ floatx4 mfma16(const uint4 &a, const uint4 &b, const 
     }
 }
 
-template <int MB, int NB, int WM, int WN, bool BF16>
-__global__ __launch_bounds__(256) void gemm_mfma_kernel(
+template <int MB, int NB, int KB, int KS, int WM, int WN, bool BF16>
+__global__ __launch_bounds__(256 * KS) void gemm_mfma_kernel(
     const uint16_t *__restrict__ win, const uint16_t *__restrict__ wst, float *__restrict__ y,
     int rows, int row0, int row_elems, int col_step, int krun, int kstage, int Ho, int Wo,
     int Cout, int tiles_m)
 {
+    constexpr int NTH = 256 * KS;
+    constexpr int KI = KB * KS;              // K per stage
+    constexpr int PITCH = KI + 8;            // halves per LDS row (16-byte pad: conflict-free)
+    constexpr int GPR = KI / 8;              // 16-byte granules per row
     constexpr int FM = MB / WM / 16;
     constexpr int FN = NB / WN / 16;
-    constexpr int AV = MB * KB / 8 / 256;   // 16-byte A vectors per thread per slice
-    constexpr int BV = NB * KB / 8 / 256;
-    static_assert(AV >= 1 && BV >= 1, "tile too small for 256 threads");
-    __shared__ __attribute__((aligned(16))) uint16_t As[2][MB * PITCH];
-    __shared__ __attribute__((aligned(16))) uint16_t Bs[2][NB * PITCH];
+    constexpr int AV = MB * GPR / NTH;       // 16-byte A vectors per thread per stage
+    constexpr int BV = NB * GPR / NTH;
+    static_assert(AV >= 1 && BV >= 1 && AV * NTH == MB * GPR && BV * NTH == NB * GPR, "tiling");
+    static_assert(WM * WN == 4, "4 waves per group");
+    static_assert(KS == 1 || MB * NB * 4 <= 2 * (MB + NB) * PITCH * 2, "reduction fits LDS");
+    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (MB + NB) * PITCH];
 
     int tm, tn;
     tile_coords(blockIdx.x, gridDim.x, tiles_m, tm, tn);
@@ -68,8 +71,10 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int wm = wave % WM;
-    const int wn = wave / WM;
+    const int grp = wave >> 2;               // K group
+    const int wig = wave & 3;
+    const int wm = wig % WM;
+    const int wn = wig / WM;
 
     // per-thread load descriptors (index precomputation: once per tile)
     const uint16_t *ap[AV];
@@ -78,50 +83,62 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(
     int bk[BV];       // window-relative K offset of this vector; -1: column outside the chunk
 #pragma unroll
     for (int i = 0; i < AV; ++i) {
-        const int v = tid + i * 256;
-        const int co = m0 + (v >> 2);
+        const int v = tid + i * NTH;
+        const int co = m0 + v / GPR;
         aok[i] = co < Cout;
-        ap[i] = wst + int64_t(aok[i] ? co : 0) * kstage + (v & 3) * 8;
+        ap[i] = wst + int64_t(aok[i] ? co : 0) * kstage + (v % GPR) * 8;
     }
 #pragma unroll
     for (int i = 0; i < BV; ++i) {
-        const int v = tid + i * 256;
-        const int n = n0 + (v >> 2);
+        const int v = tid + i * NTH;
+        const int n = n0 + v / GPR;
         const bool ok = n < ncols;
         const int rl = ok ? n / Wo : 0;
         const int wo = ok ? n - rl * Wo : 0;
-        bp[i] = win + int64_t(rl) * row_elems + int64_t(wo) * col_step + (v & 3) * 8;
-        bk[i] = ok ? (v & 3) * 8 : -1;
+        bp[i] = win + int64_t(rl) * row_elems + int64_t(wo) * col_step + (v % GPR) * 8;
+        bk[i] = ok ? (v % GPR) * 8 : -1;
     }
 
-    uint4 ra[AV], rb[BV];
-    auto gload = [&](int k0) {
+    // Two register sets of global loads. Loads are unconditional (clamped to
+    // a valid address); the masks that zero what lies outside the window are
+    // applied only when a set is written to LDS, so nothing waits for a load
+    // before its data is needed.
+    struct Set {
+        uint4 a[AV], b[BV];
+        bool blo[BV], bhi[BV];
+    };
+    Set s0, s1;
+    auto gload = [&](int k0, Set &st) {
 #pragma unroll
-        for (int i = 0; i < AV; ++i)
-            ra[i] = aok[i] ? *reinterpret_cast<const uint4 *>(ap[i] + k0) : make_uint4(0, 0, 0, 0);
+        for (int i = 0; i < AV; ++i) st.a[i] = *reinterpret_cast<const uint4 *>(ap[i] + k0);
 #pragma unroll
         for (int i = 0; i < BV; ++i) {
             const int left = krun - (k0 + bk[i]);   // window elements left from this vector
-            uint4 q = make_uint4(0, 0, 0, 0);
-            if (bk[i] >= 0 && left >= 8) {
-                q = *reinterpret_cast<const uint4 *>(bp[i] + k0);
-            } else if (bk[i] >= 0 && left >= 4) {
-                const uint2 h = *reinterpret_cast<const uint2 *>(bp[i] + k0);
-                q = make_uint4(h.x, h.y, 0, 0);
-            }
-            rb[i] = q;
+            const bool any = bk[i] >= 0 && left > 0;
+            st.blo[i] = any;
+            st.bhi[i] = any && left >= 8;           // else a 4-element tail (or nothing)
+            st.b[i] = *reinterpret_cast<const uint4 *>(bp[i] + (any ? k0 : 0));
         }
     };
-    auto sstore = [&](int buf) {
+    auto sstore = [&](int buf, const Set &st) {
+        uint16_t *As = smem + buf * (MB + NB) * PITCH;
+        uint16_t *Bs = As + MB * PITCH;
 #pragma unroll
         for (int i = 0; i < AV; ++i) {
-            const int v = tid + i * 256;
-            *reinterpret_cast<uint4 *>(&As[buf][(v >> 2) * PITCH + (v & 3) * 8]) = ra[i];
+            const int v = tid + i * NTH;
+            const uint32_t m = aok[i] ? 0xffffffffu : 0u;
+            const uint4 q = st.a[i];
+            *reinterpret_cast<uint4 *>(&As[(v / GPR) * PITCH + (v % GPR) * 8]) =
+                make_uint4(q.x & m, q.y & m, q.z & m, q.w & m);
         }
 #pragma unroll
         for (int i = 0; i < BV; ++i) {
-            const int v = tid + i * 256;
-            *reinterpret_cast<uint4 *>(&Bs[buf][(v >> 2) * PITCH + (v & 3) * 8]) = rb[i];
+            const int v = tid + i * NTH;
+            const uint32_t lo = st.blo[i] ? 0xffffffffu : 0u;
+            const uint32_t hi = st.bhi[i] ? 0xffffffffu : 0u;
+            const uint4 q = st.b[i];
+            *reinterpret_cast<uint4 *>(&Bs[(v / GPR) * PITCH + (v % GPR) * 8]) =
+                make_uint4(q.x & lo, q.y & lo, q.z & hi, q.w & hi);
         }
     };
 
@@ -131,29 +148,83 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(
 #pragma unroll
         for (int j = 0; j < FN; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    const int nk = kstage / KB;
-    gload(0);
-    sstore(0);
-    __syncthreads();
     const int arow = wm * (MB / WM) + (lane & 15);
     const int brow = wn * (NB / WN) + (lane & 15);
-    const int kofs = (lane >> 4) * 8;
-    for (int kt = 0; kt < nk; ++kt) {
-        const int buf = kt & 1;
-        if (kt + 1 < nk) gload((kt + 1) * KB);
-        uint4 af[FM], bf[FN];
+    const int kofs = grp * KB + (lane >> 4) * 8;
+    auto compute = [&](int buf) {
+        const uint16_t *As = smem + buf * (MB + NB) * PITCH;
+        const uint16_t *Bs = As + MB * PITCH;
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
-            af[i] = *reinterpret_cast<const uint4 *>(&As[buf][(arow + i * 16) * PITCH + kofs]);
+        for (int kk = 0; kk < KB; kk += 32) {
+            uint4 af[FM], bf[FN];
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
-            bf[j] = *reinterpret_cast<const uint4 *>(&Bs[buf][(brow + j * 16) * PITCH + kofs]);
+            for (int i = 0; i < FM; ++i)
+                af[i] = *reinterpret_cast<const uint4 *>(&As[(arow + i * 16) * PITCH + kofs + kk]);
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
+            for (int j = 0; j < FN; ++j)
+                bf[j] = *reinterpret_cast<const uint4 *>(&Bs[(brow + j * 16) * PITCH + kofs + kk]);
 #pragma unroll
-            for (int j = 0; j < FN; ++j) acc[i][j] = mfma16<BF16>(af[i], bf[j], acc[i][j]);
-        if (kt + 1 < nk) sstore(buf ^ 1);
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j) acc[i][j] = mfma16<BF16>(af[i], bf[j], acc[i][j]);
+        }
+    };
+
+    // Software pipeline, three stages deep: at step k the register set that
+    // holds stage k+1 is written to LDS and immediately reused for the loads
+    // of stage k+3, then stage k is multiplied from the other LDS buffer.
+    // Every load has two full steps to land, and the wait before a store
+    // only covers the older of the two sets in flight. The body has no
+    // data-dependent branches: loads past the end re-read the last stage.
+    const int nk = kstage / KI;
+    const int last = (nk - 1) * KI;
+    gload(0, s0);
+    gload(min(KI, last), s1);
+    sstore(0, s0);
+    gload(min(2 * KI, last), s0);
+    __syncthreads();
+    for (int kt = 0;; kt += 2) {
+        sstore(1, s1);                            // stage kt+1
+        gload(min((kt + 3) * KI, last), s1);
+        compute(0);                               // stage kt
         __syncthreads();
+        if (kt + 1 >= nk) break;
+        sstore(0, s0);                            // stage kt+2
+        gload(min((kt + 4) * KI, last), s0);
+        compute(1);                               // stage kt+1
+        __syncthreads();
+        if (kt + 2 >= nk) break;
+    }
+
+    if constexpr (KS > 1) {
+        // wave-level reduction of the K groups through LDS (the stage buffers
+        // are free after the last barrier): group g > 0 parks its partial
+        // tile, group 0 adds the partials in a fixed order.
+        float *red = reinterpret_cast<float *>(smem);
+        constexpr int PER = FM * FN * 4;     // floats per lane
+        for (int g = 1; g < KS; ++g) {
+            if (grp == g) {
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+#pragma unroll
+                    for (int j = 0; j < FN; ++j)
+#pragma unroll
+                        for (int v = 0; v < 4; ++v)
+                            red[((wig * PER) + (i * FN + j) * 4 + v) * 64 + lane] = acc[i][j][v];
+            }
+            __syncthreads();
+            if (grp == 0) {
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+#pragma unroll
+                    for (int j = 0; j < FN; ++j)
+#pragma unroll
+                        for (int v = 0; v < 4; ++v)
+                            acc[i][j][v] += red[((wig * PER) + (i * FN + j) * 4 + v) * 64 + lane];
+            }
+            __syncthreads();
+        }
+        if (grp != 0) return;
     }
 
     // epilogue: lane holds D[4*(lane/16) + v][lane%16] of every 16x16 block
@@ -179,9 +250,10 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(
     }
 }
 
-template <int MB, int NB, int WM, int WN>
+template <int MB, int NB, int KB, int KS, int WM, int WN>
 hipError_t launch_tile(const MfmaGemmArgs &a, hipStream_t s)
 {
+    if (a.kstage % (KB * KS) != 0) return hipErrorInvalidValue;
     const int tiles_m = (a.Cout + MB - 1) / MB;
     const int64_t ncols = int64_t(a.rows) * a.Wo;
     const int64_t tiles_n = (ncols + NB - 1) / NB;
@@ -189,13 +261,13 @@ hipError_t launch_tile(const MfmaGemmArgs &a, hipStream_t s)
     const auto *win = static_cast<const uint16_t *>(a.win);
     const auto *wst = static_cast<const uint16_t *>(a.wst);
     if (a.bf16)
-        hipLaunchKernelGGL((gemm_mfma_kernel<MB, NB, WM, WN, true>), grid, dim3(256), 0, s, win,
-                           wst, a.y, a.rows, a.row0, a.row_elems, a.col_step, a.krun, a.kstage,
-                           a.Ho, a.Wo, a.Cout, tiles_m);
+        hipLaunchKernelGGL((gemm_mfma_kernel<MB, NB, KB, KS, WM, WN, true>), grid, dim3(256 * KS),
+                           0, s, win, wst, a.y, a.rows, a.row0, a.row_elems, a.col_step, a.krun,
+                           a.kstage, a.Ho, a.Wo, a.Cout, tiles_m);
     else
-        hipLaunchKernelGGL((gemm_mfma_kernel<MB, NB, WM, WN, false>), grid, dim3(256), 0, s, win,
-                           wst, a.y, a.rows, a.row0, a.row_elems, a.col_step, a.krun, a.kstage,
-                           a.Ho, a.Wo, a.Cout, tiles_m);
+        hipLaunchKernelGGL((gemm_mfma_kernel<MB, NB, KB, KS, WM, WN, false>), grid, dim3(256 * KS),
+                           0, s, win, wst, a.y, a.rows, a.row0, a.row_elems, a.col_step, a.krun,
+                           a.kstage, a.Ho, a.Wo, a.Cout, tiles_m);
     return hipGetLastError();
 }
 
@@ -203,10 +275,23 @@ hipError_t launch_tile(const MfmaGemmArgs &a, hipStream_t s)
 
 hipError_t launch_gemm_mfma(const MfmaGemmArgs &a, hipStream_t s)
 {
-    if (a.kstage % KB != 0 || a.krun % 4 != 0 || a.col_step % 8 != 0 || a.row_elems % 8 != 0)
-        return hipErrorInvalidValue;
-    if (a.tile_m == 64 && a.tile_n == 128) return launch_tile<64, 128, 2, 2>(a, s);
-    if (a.tile_m == 128 && a.tile_n == 128) return launch_tile<128, 128, 2, 2>(a, s);
+    if (a.krun % 4 != 0 || a.col_step % 8 != 0 || a.row_elems % 8 != 0) return hipErrorInvalidValue;
+#define IM2WIN_TILE(M, N, KB, KS)                                                                \
+    if (a.tile_m == M && a.tile_n == N && a.kb == KB && a.ks == KS)                              \
+        return launch_tile<M, N, KB, KS, 2, 2>(a, s);
+    IM2WIN_TILE(64, 64, 64, 1)
+    IM2WIN_TILE(64, 64, 32, 1)
+    IM2WIN_TILE(64, 64, 32, 2)
+    IM2WIN_TILE(64, 128, 64, 1)
+    IM2WIN_TILE(64, 128, 32, 1)
+    IM2WIN_TILE(64, 128, 32, 2)
+    IM2WIN_TILE(128, 64, 64, 1)
+    IM2WIN_TILE(128, 64, 32, 1)
+    IM2WIN_TILE(128, 64, 32, 2)
+    IM2WIN_TILE(128, 128, 64, 1)
+    IM2WIN_TILE(128, 128, 32, 1)
+    IM2WIN_TILE(128, 128, 32, 2)
+#undef IM2WIN_TILE
     return hipErrorInvalidValue;
 }
 

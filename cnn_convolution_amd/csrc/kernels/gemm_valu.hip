@@ -45,74 +45,66 @@ __device__ __forceinline__ void store_cols(float *__restrict__ dst, const float 
         if (j < nvalid) dst[j] = a[j];
 }
 
-// Shapes known at compile time: KH, KW, S, NT.
-template <int KH, int KW, int S, int NT>
-__global__ __launch_bounds__(256) void gemm_valu_kernel(
-    const float *__restrict__ win, const float *__restrict__ wst, float *__restrict__ y, int rows,
-    int row0, int Cin, int pos_pad, int row_elems, int Ho, int Wo, int Cout, int slots,
-    int waves_m, int tiles_m)
+// Wave -> (channel split, channel block, column group). The 4 waves of a
+// workgroup form ks x waves_m x waves_n; waves that differ only in the split
+// index own the same outputs and sum their partials through LDS at the end.
+struct ValuMap {
+    int ksi, cb, g;
+    bool active;
+};
+
+__device__ __forceinline__ ValuMap valu_map(int wave, int lane, int ks, int waves_m, int tiles_m,
+                                            int Cout)
 {
-    constexpr int L = ((NT - 1) * S + KW) * KH;   // run length per channel
-    constexpr int LV = (L + 3) / 4;               // 16-byte vectors per run
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int lane = threadIdx.x & 63;
     int tm, tn;
     tile_coords(blockIdx.x, gridDim.x, tiles_m, tm, tn);
-    const int waves_n = 4 / waves_m;
-    const int wm = wave % waves_m, wn = wave / waves_m;
-    const int cb = tm * waves_m + wm;             // 16-channel block of this wave
-    if (cb * MT >= Cout) return;
-    const int g = (tn * waves_n + wn) * 64 + lane;
-    const int rl = g / slots;
-    const int slot = g - rl * slots;
-    const bool lane_ok = rl < rows;
-    const int wo0 = slot * NT;
-    const int nvalid = lane_ok ? min(NT, Wo - wo0) : 0;
-    const int lvalid = nvalid > 0 ? ((nvalid - 1) * S + KW) * KH : 0;
-    const float *run = win + int64_t(lane_ok ? rl : 0) * row_elems + wo0 * S * KH;
-    const float *wcb = wst + int64_t(cb) * Cin * (KH * KW * MT);
+    const int waves_n = 4 / (ks * waves_m);
+    const int ksi = wave % ks;
+    const int rest = wave / ks;
+    const int wm = rest % waves_m, wn = rest / waves_m;
+    ValuMap m;
+    m.ksi = ksi;
+    m.cb = tm * waves_m + wm;                  // 16-channel block of this wave
+    m.g = (tn * waves_n + wn) * 64 + lane;     // column group of this lane
+    m.active = m.cb * MT < Cout;
+    return m;
+}
 
-    float acc[MT][NT];
+// Sum the ks channel-split partials of acc into the split-0 wave (fixed order).
+template <int NT>
+__device__ __forceinline__ void valu_reduce(float (&acc)[MT][NT], float *red, int wave, int lane,
+                                            int ks)
+{
+    const int ksi = wave % ks;
 #pragma unroll
-    for (int m = 0; m < MT; ++m)
+    for (int h = 0; h < 2; ++h) {
+        if (ksi != 0) {
 #pragma unroll
-        for (int j = 0; j < NT; ++j) acc[m][j] = 0.f;
-
-    float v[LV * 4], vn[LV * 4];
+            for (int m = 0; m < MT / 2; ++m)
 #pragma unroll
-    for (int i = 0; i < LV; ++i) {
-        float4 q = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (4 * i < lvalid) q = *reinterpret_cast<const float4 *>(run + 4 * i);
-        v[4 * i] = q.x; v[4 * i + 1] = q.y; v[4 * i + 2] = q.z; v[4 * i + 3] = q.w;
-    }
-    for (int ci = 0; ci < Cin; ++ci) {
-        if (ci + 1 < Cin) {
-            const float *nrun = run + int64_t(ci + 1) * pos_pad;
+                for (int j = 0; j < NT; ++j)
+                    red[((wave * (MT / 2) + m) * NT + j) * 64 + lane] = acc[h * (MT / 2) + m][j];
+        }
+        __syncthreads();
+        if (ksi == 0) {
+            for (int k = 1; k < ks; ++k) {
 #pragma unroll
-            for (int i = 0; i < LV; ++i) {
-                float4 q = make_float4(0.f, 0.f, 0.f, 0.f);
-                if (4 * i < lvalid) q = *reinterpret_cast<const float4 *>(nrun + 4 * i);
-                vn[4 * i] = q.x; vn[4 * i + 1] = q.y; vn[4 * i + 2] = q.z; vn[4 * i + 3] = q.w;
+                for (int m = 0; m < MT / 2; ++m)
+#pragma unroll
+                    for (int j = 0; j < NT; ++j)
+                        acc[h * (MT / 2) + m][j] +=
+                            red[(((wave + k) * (MT / 2) + m) * NT + j) * 64 + lane];
             }
         }
-        const float *wc = wcb + ci * (KH * KW * MT);
-#pragma unroll
-        for (int kh = 0; kh < KH; ++kh) {
-#pragma unroll
-            for (int kw = 0; kw < KW; ++kw) {
-                const float *a = wc + (kh * KW + kw) * MT;   // wave-uniform: scalar loads
-#pragma unroll
-                for (int j = 0; j < NT; ++j) {
-                    const float x = v[(j * S + kw) * KH + kh];
-#pragma unroll
-                    for (int m = 0; m < MT; ++m) acc[m][j] = __builtin_fmaf(a[m], x, acc[m][j]);
-                }
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < LV * 4; ++i) v[i] = vn[i];
+        __syncthreads();
     }
-    if (nvalid <= 0) return;
+}
+
+template <int NT>
+__device__ __forceinline__ void valu_store(const float (&acc)[MT][NT], float *__restrict__ y, int cb,
+                                           int rl, int row0, int wo0, int nvalid, int Ho, int Wo,
+                                           int Cout)
+{
     const int r = row0 + rl;
     const int n = r / Ho;
     const int ho = r - n * Ho;
@@ -124,6 +116,77 @@ __global__ __launch_bounds__(256) void gemm_valu_kernel(
             store_cols<NT>(y + ((int64_t(n) * Cout + co) * Ho + ho) * Wo + wo0, acc[m], nvalid,
                            vec_ok);
     }
+}
+
+// Shapes known at compile time: KH, KW, S, NT.
+template <int KH, int KW, int S, int NT>
+__global__ __launch_bounds__(256) void gemm_valu_kernel(
+    const float *__restrict__ win, const float *__restrict__ wst, float *__restrict__ y, int rows,
+    int row0, int Cin, int pos_pad, int row_elems, int Ho, int Wo, int Cout, int slots,
+    int waves_m, int tiles_m, int ks)
+{
+    constexpr int L = ((NT - 1) * S + KW) * KH;   // run length per channel
+    constexpr int LV = (L + 3) / 4;               // 16-byte vectors per run
+    __shared__ float red[4 * (MT / 2) * NT * 64];
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const ValuMap mp = valu_map(wave, lane, ks, waves_m, tiles_m, Cout);
+    const int rl = mp.g / slots;
+    const int slot = mp.g - rl * slots;
+    const bool lane_ok = mp.active && rl < rows;
+    const int wo0 = slot * NT;
+    const int nvalid = lane_ok ? min(NT, Wo - wo0) : 0;
+    const int lvalid = nvalid > 0 ? ((nvalid - 1) * S + KW) * KH : 0;
+    const float *run = win + int64_t(lane_ok ? rl : 0) * row_elems + wo0 * S * KH;
+    const float *wcb = wst + int64_t(mp.active ? mp.cb : 0) * Cin * (KH * KW * MT);
+
+    float acc[MT][NT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int j = 0; j < NT; ++j) acc[m][j] = 0.f;
+
+    if (mp.active) {
+        float v[LV * 4], vn[LV * 4];
+        // Loads are unconditional: a vector past this lane's valid run reads
+        // the run start instead (a load under a branch would make the compiler
+        // wait for it at the join). Values past the valid run only ever meet
+        // the columns j >= nvalid, which are never stored, so no masking.
+        auto load_run = [&](const float *src, float (&dst)[LV * 4]) {
+#pragma unroll
+            for (int i = 0; i < LV; ++i) {
+                const float4 q = *reinterpret_cast<const float4 *>(src + (4 * i < lvalid ? 4 * i : 0));
+                dst[4 * i] = q.x;
+                dst[4 * i + 1] = q.y;
+                dst[4 * i + 2] = q.z;
+                dst[4 * i + 3] = q.w;
+            }
+        };
+        load_run(run + int64_t(mp.ksi < Cin ? mp.ksi : 0) * pos_pad, v);
+        for (int ci = mp.ksi; ci < Cin; ci += ks) {
+            // next channel of this split (the last iteration reloads its own run)
+            load_run(run + int64_t(ci + ks < Cin ? ci + ks : ci) * pos_pad, vn);
+            const float *wc = wcb + ci * (KH * KW * MT);
+#pragma unroll
+            for (int kh = 0; kh < KH; ++kh) {
+#pragma unroll
+                for (int kw = 0; kw < KW; ++kw) {
+                    const float *a = wc + (kh * KW + kw) * MT;   // wave-uniform: scalar loads
+#pragma unroll
+                    for (int j = 0; j < NT; ++j) {
+                        const float x = v[(j * S + kw) * KH + kh];
+#pragma unroll
+                        for (int m = 0; m < MT; ++m) acc[m][j] = __builtin_fmaf(a[m], x, acc[m][j]);
+                    }
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < LV * 4; ++i) v[i] = vn[i];
+        }
+    }
+    if (ks > 1) valu_reduce<NT>(acc, red, wave, lane, ks);
+    if (mp.ksi != 0 || nvalid <= 0) return;
+    valu_store<NT>(acc, y, mp.cb, rl, row0, wo0, nvalid, Ho, Wo, Cout);
 }
 
 // Any shape: taps loaded one element at a time (used for shapes without a
@@ -131,26 +194,21 @@ __global__ __launch_bounds__(256) void gemm_valu_kernel(
 __global__ __launch_bounds__(256) void gemm_valu_generic_kernel(
     const float *__restrict__ win, const float *__restrict__ wst, float *__restrict__ y, int rows,
     int row0, int Cin, int pos_pad, int row_elems, int KH, int KW, int S, int Ho, int Wo, int Cout,
-    int slots, int waves_m, int tiles_m)
+    int slots, int waves_m, int tiles_m, int ks)
 {
     constexpr int NT = 4;
+    __shared__ float red[4 * (MT / 2) * NT * 64];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
-    int tm, tn;
-    tile_coords(blockIdx.x, gridDim.x, tiles_m, tm, tn);
-    const int waves_n = 4 / waves_m;
-    const int wm = wave % waves_m, wn = wave / waves_m;
-    const int cb = tm * waves_m + wm;
-    if (cb * MT >= Cout) return;
-    const int g = (tn * waves_n + wn) * 64 + lane;
-    const int rl = g / slots;
-    const int slot = g - rl * slots;
-    const bool lane_ok = rl < rows;
+    const ValuMap mp = valu_map(wave, lane, ks, waves_m, tiles_m, Cout);
+    const int rl = mp.g / slots;
+    const int slot = mp.g - rl * slots;
+    const bool lane_ok = mp.active && rl < rows;
     const int wo0 = slot * NT;
     const int nvalid = lane_ok ? min(NT, Wo - wo0) : 0;
     const float *run = win + int64_t(lane_ok ? rl : 0) * row_elems + wo0 * S * KH;
     const int taps = KH * KW;
-    const float *wcb = wst + int64_t(cb) * Cin * taps * MT;
+    const float *wcb = wst + int64_t(mp.active ? mp.cb : 0) * Cin * taps * MT;
 
     float acc[MT][NT];
 #pragma unroll
@@ -158,66 +216,65 @@ __global__ __launch_bounds__(256) void gemm_valu_generic_kernel(
 #pragma unroll
         for (int j = 0; j < NT; ++j) acc[m][j] = 0.f;
 
-    for (int ci = 0; ci < Cin; ++ci) {
-        const float *rc = run + int64_t(ci) * pos_pad;
-        for (int kh = 0; kh < KH; ++kh) {
-            for (int kw = 0; kw < KW; ++kw) {
-                const float *a = wcb + (int64_t(ci) * taps + kh * KW + kw) * MT;
-                float x[NT];
+    if (mp.active) {
+        for (int ci = mp.ksi; ci < Cin; ci += ks) {
+            const float *rc = run + int64_t(ci) * pos_pad;
+            for (int kh = 0; kh < KH; ++kh) {
+                for (int kw = 0; kw < KW; ++kw) {
+                    const float *a = wcb + (int64_t(ci) * taps + kh * KW + kw) * MT;
+                    float x[NT];
 #pragma unroll
-                for (int j = 0; j < NT; ++j) x[j] = j < nvalid ? rc[(j * S + kw) * KH + kh] : 0.f;
+                    for (int j = 0; j < NT; ++j) x[j] = rc[j < nvalid ? (j * S + kw) * KH + kh : 0];
 #pragma unroll
-                for (int j = 0; j < NT; ++j)
+                    for (int j = 0; j < NT; ++j)
 #pragma unroll
-                    for (int m = 0; m < MT; ++m) acc[m][j] = __builtin_fmaf(a[m], x[j], acc[m][j]);
+                        for (int m = 0; m < MT; ++m) acc[m][j] = __builtin_fmaf(a[m], x[j], acc[m][j]);
+                }
             }
         }
     }
-    if (nvalid <= 0) return;
-    const int r = row0 + rl;
-    const int n = r / Ho;
-    const int ho = r - n * Ho;
-    const bool vec_ok = (Wo % 4) == 0;
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-        const int co = cb * MT + m;
-        if (co < Cout)
-            store_cols<NT>(y + ((int64_t(n) * Cout + co) * Ho + ho) * Wo + wo0, acc[m], nvalid,
-                           vec_ok);
-    }
+    if (ks > 1) valu_reduce<NT>(acc, red, wave, lane, ks);
+    if (mp.ksi != 0 || nvalid <= 0) return;
+    valu_store<NT>(acc, y, mp.cb, rl, row0, wo0, nvalid, Ho, Wo, Cout);
+}
+
+struct ValuGrid {
+    int slots, waves_m, tiles_m, ks;
+    unsigned blocks;
+};
+
+ValuGrid valu_grid(const ValuGemmArgs &a, int NT)
+{
+    ValuGrid g{};
+    g.ks = (a.ksplit == 2 || a.ksplit == 4) ? a.ksplit : 1;
+    g.slots = (a.Wo + NT - 1) / NT;
+    const int cblocks = a.Cout_stage / MT;
+    const int per = 4 / g.ks;                  // waves per split index
+    g.waves_m = cblocks >= per ? per : (cblocks >= 2 && per >= 2 ? 2 : 1);
+    const int waves_n = per / g.waves_m;
+    g.tiles_m = (cblocks + g.waves_m - 1) / g.waves_m;
+    const int64_t groups = int64_t(a.rows) * g.slots;
+    const int64_t tiles_n = (groups + 64 * waves_n - 1) / (64 * waves_n);
+    g.blocks = static_cast<unsigned>(g.tiles_m * tiles_n);
+    return g;
 }
 
 template <int KH, int KW, int S, int NT>
 hipError_t launch_spec(const ValuGemmArgs &a, hipStream_t s)
 {
-    const int slots = (a.Wo + NT - 1) / NT;
-    const int cblocks = a.Cout_stage / MT;
-    const int waves_m = cblocks >= 4 ? 4 : (cblocks >= 2 ? 2 : 1);
-    const int waves_n = 4 / waves_m;
-    const int tiles_m = (cblocks + waves_m - 1) / waves_m;
-    const int64_t groups = int64_t(a.rows) * slots;
-    const int64_t tiles_n = (groups + 64 * waves_n - 1) / (64 * waves_n);
-    const dim3 grid(static_cast<unsigned>(tiles_m * tiles_n));
-    hipLaunchKernelGGL((gemm_valu_kernel<KH, KW, S, NT>), grid, dim3(256), 0, s, a.win, a.wst, a.y,
-                       a.rows, a.row0, a.Cin, a.pos_pad, a.row_elems, a.Ho, a.Wo, a.Cout, slots,
-                       waves_m, tiles_m);
+    const ValuGrid g = valu_grid(a, NT);
+    hipLaunchKernelGGL((gemm_valu_kernel<KH, KW, S, NT>), dim3(g.blocks), dim3(256), 0, s, a.win,
+                       a.wst, a.y, a.rows, a.row0, a.Cin, a.pos_pad, a.row_elems, a.Ho, a.Wo, a.Cout,
+                       g.slots, g.waves_m, g.tiles_m, g.ks);
     return hipGetLastError();
 }
 
 hipError_t launch_generic(const ValuGemmArgs &a, hipStream_t s)
 {
-    constexpr int NT = 4;
-    const int slots = (a.Wo + NT - 1) / NT;
-    const int cblocks = a.Cout_stage / MT;
-    const int waves_m = cblocks >= 4 ? 4 : (cblocks >= 2 ? 2 : 1);
-    const int waves_n = 4 / waves_m;
-    const int tiles_m = (cblocks + waves_m - 1) / waves_m;
-    const int64_t groups = int64_t(a.rows) * slots;
-    const int64_t tiles_n = (groups + 64 * waves_n - 1) / (64 * waves_n);
-    const dim3 grid(static_cast<unsigned>(tiles_m * tiles_n));
-    hipLaunchKernelGGL(gemm_valu_generic_kernel, grid, dim3(256), 0, s, a.win, a.wst, a.y, a.rows,
-                       a.row0, a.Cin, a.pos_pad, a.row_elems, a.KH, a.KW, a.stride, a.Ho, a.Wo,
-                       a.Cout, slots, waves_m, tiles_m);
+    const ValuGrid g = valu_grid(a, 4);
+    hipLaunchKernelGGL(gemm_valu_generic_kernel, dim3(g.blocks), dim3(256), 0, s, a.win, a.wst, a.y,
+                       a.rows, a.row0, a.Cin, a.pos_pad, a.row_elems, a.KH, a.KW, a.stride, a.Ho,
+                       a.Wo, a.Cout, g.slots, g.waves_m, g.tiles_m, g.ks);
     return hipGetLastError();
 }
 

@@ -18,53 +18,78 @@ namespace im2win {
 namespace {
 
 // ---------------------------------------------------------------- row-interleaved
-// One wave per (window row, channel): the wave reads the KH input rows
-// coalesced along w and writes the channel's interleaved run of pos_pad
-// elements (tail past W_win*KH zero-filled). 4 waves per workgroup.
-template <typename E>
+// Workgroup = (window row r, block of RC channels); each wave takes RC/4
+// channels one after the other. A lane writes consecutive positions q of the
+// channel's run (coalesced stores), and reads the input element
+// (kh, w) = (q mod KH, q div KH) of the KH input rows, which a wave touches as
+// KH short contiguous segments (L1-resident). KH is a template parameter for
+// the common filter heights so that q div KH is a multiply-shift.
+constexpr int RC = 32;   // channels per workgroup (8 per wave)
+
+template <typename E, int KHT>
 __global__ __launch_bounds__(256) void pack_row_kernel(
-    const E *__restrict__ x, E *__restrict__ out, int Cin, int H, int W, int KH, int stride,
-    int pad, int Ho, int Wwin, int pos_pad, int row_elems, int row0, int rows)
+    const E *__restrict__ x, E *__restrict__ out, int Cin, int H, int W, int KH_rt, int stride,
+    int pad, int Ho, int Wwin, int pos_pad, int row_elems, int row0, int cblocks)
 {
+    const int KH = KHT > 0 ? KHT : KH_rt;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
-    const int64_t task = int64_t(blockIdx.x) * 4 + wave;      // (local row, channel)
-    if (task >= int64_t(rows) * Cin) return;
-    const int rl = int(task / Cin);
-    const int ci = int(task - int64_t(rl) * Cin);
+    const int cbk = blockIdx.x % cblocks;
+    const int rl = blockIdx.x / cblocks;
     const int r = row0 + rl;
     const int n = r / Ho;
     const int ho = r - n * Ho;
-    const E *xc = x + (int64_t(n) * Cin + ci) * H * W;
-    E *o = out + int64_t(rl) * row_elems + int64_t(ci) * pos_pad;
-    for (int kh = 0; kh < KH; ++kh) {
-        const int ih = ho * stride + kh - pad;
-        const bool row_ok = ih >= 0 && ih < H;
-        const E *xr = xc + int64_t(row_ok ? ih : 0) * W;
-        for (int w = lane; w < Wwin; w += 64) {
-            const int iw = w - pad;
-            E v = E(0);
-            if (row_ok && iw >= 0 && iw < W) v = xr[iw];
-            o[w * KH + kh] = v;
-        }
+    const int used = Wwin * KH;
+    const int ih0 = ho * stride - pad;
+    E *orow = out + int64_t(rl) * row_elems;
+    // each wave owns RC/4 channels and walks their runs together, so that
+    // RC/4 independent loads are in flight per lane
+    constexpr int CPW = RC / 4;
+    const E *xc[CPW];
+    E *o[CPW];
+    bool cok[CPW];
+#pragma unroll
+    for (int u = 0; u < CPW; ++u) {
+        const int ci = cbk * RC + wave * CPW + u;
+        cok[u] = ci < Cin;
+        xc[u] = x + (int64_t(n) * Cin + (cok[u] ? ci : 0)) * H * W;
+        o[u] = orow + int64_t(cok[u] ? ci : 0) * pos_pad;
     }
-    for (int q = Wwin * KH + lane; q < pos_pad; q += 64) o[q] = E(0);
+    for (int q = lane; q < pos_pad; q += 64) {
+        int src = -1;
+        if (q < used) {
+            const int w = q / KH;
+            const int kh = q - w * KH;
+            const int ih = ih0 + kh;
+            const int iw = w - pad;
+            if (ih >= 0 && ih < H && iw >= 0 && iw < W) src = ih * W + iw;
+        }
+        // unconditional loads from a valid address, masked after (no branch)
+        E v[CPW];
+#pragma unroll
+        for (int u = 0; u < CPW; ++u) {
+            const E t = xc[u][src >= 0 ? src : 0];
+            v[u] = (src >= 0 && cok[u]) ? t : E(0);
+        }
+#pragma unroll
+        for (int u = 0; u < CPW; ++u)
+            if (cok[u]) o[u][q] = v[u];
+    }
 }
 
 // ---------------------------------------------------------------- channels-last
-// Workgroup = (window row r, block of PW padded columns, block of CB channels).
-// Phase 1 stages T[ci][kh][w] in LDS with coalesced reads along w; phase 2
-// reads CG x 8 blocks (CG channels x 8 columns) as 16-byte LDS rows, transposes
-// them in registers and writes CG-channel vectors, so that global writes run
-// along ci, the innermost dimension of the window tensor.
-constexpr int PW = 32;           // padded columns per workgroup
-constexpr int CB = 64;           // channels per workgroup
+// Workgroup = (window row r, block of CB channels), looping over blocks of PW
+// padded columns and passes of up to KHB filter rows.
+// Phase 1 stages T[ci][kh][w] in LDS: one wave per (ci, kh) input row, lanes
+// along w (coalesced reads). Phase 2 reads CG x 8 blocks (CG channels x 8
+// columns) as 16-byte LDS rows, transposes them in registers and writes
+// CG-channel vectors, so global writes run along ci, the innermost dimension
+// of the window tensor (8 lanes cover one 128-byte run of 64 channels).
+constexpr int PW = 64;             // padded columns per pass (one per lane)
+constexpr int CB = 64;             // channels per workgroup
+constexpr int KHB = 4;             // filter rows per pass
 constexpr int LDS_PITCH = PW + 8;  // elements per (ci, kh) LDS row (16-byte multiple)
-
-template <int CG>
-struct Vec;
-template <> struct Vec<8> { using T = uint4; };
-template <> struct Vec<4> { using T = uint2; };
+constexpr int U1 = 16;             // input rows in flight per wave in phase 1
 
 // 16-bit lanes of a 32-bit word
 __device__ __forceinline__ uint32_t lo16(uint32_t v) { return v & 0xffffu; }
@@ -73,120 +98,140 @@ __device__ __forceinline__ uint32_t hi16(uint32_t v) { return v >> 16; }
 template <int CG>
 __global__ __launch_bounds__(256) void pack_cl_kernel(
     const uint16_t *__restrict__ x, uint16_t *__restrict__ out, int Cin, int H, int W, int KH,
-    int stride, int pad, int Ho, int Wwin, int Cin_pad, int row_elems, int row0, int wblocks,
-    int cblocks)
+    int stride, int pad, int Ho, int Wwin, int Cin_pad, int row_elems, int row0, int cblocks)
 {
-    __shared__ __attribute__((aligned(16))) uint16_t tile[CB * 8 * LDS_PITCH];  // KH <= 8 per pass
-    int b = blockIdx.x;
-    const int cbk = b % cblocks;
-    b /= cblocks;
-    const int wbk = b % wblocks;
-    const int rl = b / wblocks;
+    __shared__ __attribute__((aligned(16))) uint16_t tile[CB * KHB * LDS_PITCH];
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int cbk = blockIdx.x % cblocks;
+    const int rl = blockIdx.x / cblocks;
     const int r = row0 + rl;
     const int n = r / Ho;
     const int ho = r - n * Ho;
     const int c0 = cbk * CB;
-    const int w0 = wbk * PW;
-    const int cb = min(CB, Cin_pad - c0);                  // channels in this block (multiple of CG)
+    const int cb = min(CB, Cin_pad - c0);        // channels in this block (multiple of CG)
+    const int ih0 = ho * stride - pad;
+    const uint16_t *xn = x + int64_t(n) * Cin * H * W;
     uint16_t *orow = out + int64_t(rl) * row_elems;
+    const int cgroups = cb / CG;
 
-    for (int kh0 = 0; kh0 < KH; kh0 += 8) {
-        const int khn = min(8, KH - kh0);
-        // phase 1: tile[(ci*8 + kh)*LDS_PITCH + w] = xp value (0 outside / padded channel)
-        const int items1 = cb * khn * PW;
-        for (int i = threadIdx.x; i < items1; i += blockDim.x) {
-            const int wl = i % PW;
-            const int t = i / PW;
-            const int kh = t % khn;
-            const int ci = t / khn;
-            const int c = c0 + ci;
-            const int ih = ho * stride + kh0 + kh - pad;
-            const int iw = w0 + wl - pad;
-            uint16_t v = 0;
-            if (c < Cin && ih >= 0 && ih < H && iw >= 0 && iw < W)
-                v = x[((int64_t(n) * Cin + c) * H + ih) * W + iw];
-            tile[(ci * 8 + kh) * LDS_PITCH + wl] = v;
-        }
-        __syncthreads();
-        // phase 2: (kh, column group of 8, channel group of CG)
-        const int cgroups = cb / CG;
-        const int items2 = khn * (PW / 8) * cgroups;
-        for (int i = threadIdx.x; i < items2; i += blockDim.x) {
-            const int cg = i % cgroups;
-            const int t = i / cgroups;
-            const int wg = t % (PW / 8);
-            const int kh = t / (PW / 8);
-            uint32_t rowv[CG][4];
+    for (int w0 = 0; w0 < Wwin; w0 += PW) {
+        const int iw = w0 + lane - pad;
+        const bool col_ok = iw >= 0 && iw < W && w0 + lane < Wwin;
+        for (int kh0 = 0; kh0 < KH; kh0 += KHB) {
+            const int khn = min(KHB, KH - kh0);
+            // phase 1: tile[(ci*KHB + kh)*LDS_PITCH + lane]; each wave takes U rows
+            // at a time so that U independent loads are in flight per lane
+            const int nrows = cb * khn;
+            for (int rb = wave * U1; rb < nrows; rb += 4 * U1) {
+                uint16_t v[U1];
 #pragma unroll
-            for (int e = 0; e < CG; ++e) {
-                const uint4 q = *reinterpret_cast<const uint4 *>(
-                    &tile[((cg * CG + e) * 8 + kh) * LDS_PITCH + wg * 8]);
-                rowv[e][0] = q.x; rowv[e][1] = q.y; rowv[e][2] = q.z; rowv[e][3] = q.w;
-            }
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int w = w0 + wg * 8 + j;
-                if (w >= Wwin) break;
-                uint32_t o[CG / 2];
-#pragma unroll
-                for (int q = 0; q < CG / 2; ++q) {
-                    const uint32_t a = rowv[2 * q][j >> 1];
-                    const uint32_t c = rowv[2 * q + 1][j >> 1];
-                    o[q] = (j & 1) ? (hi16(a) | (c & 0xffff0000u)) : (lo16(a) | (c << 16));
+                for (int u = 0; u < U1; ++u) {
+                    const int row = rb + u;
+                    const int ci = row / khn;        // wave-uniform
+                    const int kh = row - ci * khn;
+                    const int c = c0 + ci;
+                    const int ih = ih0 + kh0 + kh;
+                    const bool ok = row < nrows && c < Cin && ih >= 0 && ih < H && col_ok;
+                    // unconditional load from a valid address, masked after (no branch)
+                    const uint16_t t = xn[ok ? (int64_t(c) * H + ih) * W + iw : 0];
+                    v[u] = ok ? t : uint16_t(0);
                 }
-                uint16_t *dst = orow + (int64_t(w) * KH + kh0 + kh) * Cin_pad + c0 + cg * CG;
-                if constexpr (CG == 8) {
-                    *reinterpret_cast<uint4 *>(dst) = make_uint4(o[0], o[1], o[2], o[3]);
-                } else {
-                    *reinterpret_cast<uint2 *>(dst) = make_uint2(o[0], o[1]);
+#pragma unroll
+                for (int u = 0; u < U1; ++u) {
+                    const int row = rb + u;
+                    const int ci = row / khn;
+                    const int kh = row - ci * khn;
+                    if (row < nrows) tile[(ci * KHB + kh) * LDS_PITCH + lane] = v[u];
                 }
             }
+            __syncthreads();
+            // phase 2: (kh, column group of 8, channel group of CG)
+            const int items = khn * (PW / 8) * cgroups;
+            for (int i = threadIdx.x; i < items; i += 256) {
+                const int cg = i % cgroups;
+                const int t = i / cgroups;
+                const int wg = t % (PW / 8);
+                const int kh = t / (PW / 8);
+                const int wbase = w0 + wg * 8;
+                if (wbase >= Wwin) continue;
+                uint32_t rowv[CG][4];
+#pragma unroll
+                for (int e = 0; e < CG; ++e) {
+                    const uint4 q = *reinterpret_cast<const uint4 *>(
+                        &tile[((cg * CG + e) * KHB + kh) * LDS_PITCH + wg * 8]);
+                    rowv[e][0] = q.x; rowv[e][1] = q.y; rowv[e][2] = q.z; rowv[e][3] = q.w;
+                }
+                uint16_t *dst = orow + (int64_t(wbase) * KH + kh0 + kh) * Cin_pad + c0 + cg * CG;
+                const int64_t wstep = int64_t(KH) * Cin_pad;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    if (wbase + j >= Wwin) break;
+                    uint32_t o[CG / 2];
+#pragma unroll
+                    for (int q = 0; q < CG / 2; ++q) {
+                        const uint32_t a = rowv[2 * q][j >> 1];
+                        const uint32_t c = rowv[2 * q + 1][j >> 1];
+                        o[q] = (j & 1) ? (hi16(a) | (c & 0xffff0000u)) : (lo16(a) | (c << 16));
+                    }
+                    if constexpr (CG == 8) {
+                        *reinterpret_cast<uint4 *>(dst + j * wstep) = make_uint4(o[0], o[1], o[2], o[3]);
+                    } else {
+                        *reinterpret_cast<uint2 *>(dst + j * wstep) = make_uint2(o[0], o[1]);
+                    }
+                }
+            }
+            __syncthreads();
         }
-        __syncthreads();
     }
     // zero the row tail past W_win*KH*Cin_pad (alignment padding), once per row
-    if (wbk == 0 && cbk == 0) {
+    if (cbk == 0) {
         const int used = Wwin * KH * Cin_pad;
-        for (int q = used + threadIdx.x; q < row_elems; q += blockDim.x) orow[q] = 0;
+        for (int q = used + threadIdx.x; q < row_elems; q += 256) orow[q] = 0;
     }
 }
 
 }  // namespace
 
+template <typename E>
+hipError_t launch_pack_row_t(const PackArgs &a, hipStream_t s)
+{
+    const int cblocks = (a.Cin + RC - 1) / RC;
+    const dim3 grid(static_cast<unsigned>(int64_t(a.rows) * cblocks));
+    const E *x = static_cast<const E *>(a.x);
+    E *out = static_cast<E *>(a.out);
+#define IM2WIN_PACK_ROW(K)                                                                       \
+    hipLaunchKernelGGL((pack_row_kernel<E, K>), grid, dim3(256), 0, s, x, out, a.Cin, a.H, a.W,   \
+                       a.KH, a.stride, a.pad, a.Ho, a.Wwin, a.pos_pad, a.row_elems, a.row0, cblocks)
+    switch (a.KH) {
+    case 1: IM2WIN_PACK_ROW(1); break;
+    case 3: IM2WIN_PACK_ROW(3); break;
+    case 5: IM2WIN_PACK_ROW(5); break;
+    case 7: IM2WIN_PACK_ROW(7); break;
+    default: IM2WIN_PACK_ROW(0); break;
+    }
+#undef IM2WIN_PACK_ROW
+    return hipGetLastError();
+}
+
 hipError_t launch_pack_row(const PackArgs &a, hipStream_t s)
 {
-    const int64_t tasks = int64_t(a.rows) * a.Cin;
-    const dim3 grid(static_cast<unsigned>((tasks + 3) / 4));
-    if (a.esize == 4)
-        hipLaunchKernelGGL(pack_row_kernel<uint32_t>, grid, dim3(256), 0, s,
-                           static_cast<const uint32_t *>(a.x), static_cast<uint32_t *>(a.out),
-                           a.Cin, a.H, a.W, a.KH, a.stride, a.pad, a.Ho, a.Wwin, a.pos_pad,
-                           a.row_elems, a.row0, a.rows);
-    else
-        hipLaunchKernelGGL(pack_row_kernel<uint16_t>, grid, dim3(256), 0, s,
-                           static_cast<const uint16_t *>(a.x), static_cast<uint16_t *>(a.out),
-                           a.Cin, a.H, a.W, a.KH, a.stride, a.pad, a.Ho, a.Wwin, a.pos_pad,
-                           a.row_elems, a.row0, a.rows);
-    return hipGetLastError();
+    return a.esize == 4 ? launch_pack_row_t<uint32_t>(a, s) : launch_pack_row_t<uint16_t>(a, s);
 }
 
 hipError_t launch_pack_cl(const PackArgs &a, hipStream_t s)
 {
     if (a.esize != 2) return hipErrorInvalidValue;
-    const int wblocks = (a.Wwin + PW - 1) / PW;
     const int cblocks = (a.Cin_pad + CB - 1) / CB;
-    const int64_t blocks = int64_t(a.rows) * wblocks * cblocks;
-    const dim3 grid(static_cast<unsigned>(blocks));
+    const dim3 grid(static_cast<unsigned>(int64_t(a.rows) * cblocks));
+    const auto *x = static_cast<const uint16_t *>(a.x);
+    auto *out = static_cast<uint16_t *>(a.out);
     if (a.Cin_pad % 8 == 0)
-        hipLaunchKernelGGL(pack_cl_kernel<8>, grid, dim3(256), 0, s,
-                           static_cast<const uint16_t *>(a.x), static_cast<uint16_t *>(a.out),
-                           a.Cin, a.H, a.W, a.KH, a.stride, a.pad, a.Ho, a.Wwin, a.Cin_pad,
-                           a.row_elems, a.row0, wblocks, cblocks);
+        hipLaunchKernelGGL(pack_cl_kernel<8>, grid, dim3(256), 0, s, x, out, a.Cin, a.H, a.W, a.KH,
+                           a.stride, a.pad, a.Ho, a.Wwin, a.Cin_pad, a.row_elems, a.row0, cblocks);
     else if (a.Cin_pad == 4)
-        hipLaunchKernelGGL(pack_cl_kernel<4>, grid, dim3(256), 0, s,
-                           static_cast<const uint16_t *>(a.x), static_cast<uint16_t *>(a.out),
-                           a.Cin, a.H, a.W, a.KH, a.stride, a.pad, a.Ho, a.Wwin, a.Cin_pad,
-                           a.row_elems, a.row0, wblocks, cblocks);
+        hipLaunchKernelGGL(pack_cl_kernel<4>, grid, dim3(256), 0, s, x, out, a.Cin, a.H, a.W, a.KH,
+                           a.stride, a.pad, a.Ho, a.Wwin, a.Cin_pad, a.row_elems, a.row0, cblocks);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();

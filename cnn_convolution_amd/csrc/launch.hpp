@@ -37,6 +37,7 @@ struct ValuGemmArgs {
     int rows, row0, Cin, pos_pad, row_elems;
     int KH, KW, stride;
     int Ho, Wo, Cout, Cout_stage;
+    int ksplit;             // waves of a workgroup splitting the channels (1, 2 or 4)
 };
 hipError_t launch_gemm_valu_f32(const ValuGemmArgs &a, hipStream_t s);
 
@@ -49,7 +50,8 @@ struct MfmaGemmArgs {
     int krun;               // KW*KH*Cin_pad: window length
     int kstage;             // staged filter row length (multiple of the K slice)
     int Ho, Wo, Cout;
-    int tile_m, tile_n;
+    int tile_m, tile_n;     // output tile
+    int kb, ks;             // K per wave group per LDS stage; wave groups splitting K
     int bf16;               // 0: fp16, 1: bf16
 };
 hipError_t launch_gemm_mfma(const MfmaGemmArgs &a, hipStream_t s);

@@ -1,6 +1,8 @@
 // Host planner: see plan.hpp.
 #include "plan.hpp"
 
+#include <cstdio>
+#include <cstdlib>
 #include <cstring>
 
 namespace im2win {
@@ -42,10 +44,15 @@ LayoutGeom layout_geom(const conv2d_desc_t &d, int32_t layout) {
         const bool four = d.Cin <= 4 && (d.stride * d.KH) % 2 == 0;
         g.Cin_pad = four ? 4 : round_up(d.Cin, 8);
         g.pos_pad = Wwin * d.KH;
-        g.row_elems = round_up(Wwin * d.KH * g.Cin_pad, 8);
+        // a window whose length is 4 mod 8 ends in a half vector: the kernel
+        // loads that vector whole, so the row keeps 4 spare elements after it
+        const int64_t krun = d.KW * d.KH * g.Cin_pad;
+        g.row_elems = round_up(Wwin * d.KH * g.Cin_pad + (krun % 8 ? 4 : 0), 8);
     }
     return g;
 }
+
+static int64_t mfma_kgran(int64_t krun);
 
 StageGeom stage_geom(const conv2d_desc_t &d, int32_t layout, int tile_m) {
     (void)tile_m;
@@ -58,17 +65,72 @@ StageGeom stage_geom(const conv2d_desc_t &d, int32_t layout, int tile_m) {
         const LayoutGeom g = layout_geom(d, layout);
         const int64_t krun = d.KW * d.KH * g.Cin_pad;
         s.rows = d.Cout;
-        s.row_len = round_up(krun, kMfmaKB);
+        s.row_len = round_up(krun, mfma_kgran(krun));
         // a 1x1 filter whose channel count needs no padding already is [Cout][K]
         s.needed = !(d.KH == 1 && d.KW == 1 && g.Cin_pad == d.Cin && s.row_len == d.Cin);
     }
     return s;
 }
 
-static void pick_mfma_tile(const conv2d_desc_t &d, int64_t cols_per_chunk, int32_t *tm, int32_t *tn) {
-    (void)cols_per_chunk;
-    *tm = d.Cout <= 64 ? 64 : 128;
-    *tn = 128;
+// Matrix-core tiles the kernel is compiled for: {MB, NB, KB, KS}.
+static const int kMfmaTiles[][4] = {
+    {64, 64, 64, 1},   {64, 64, 32, 1},   {64, 64, 32, 2},   {64, 128, 64, 1},
+    {64, 128, 32, 1},  {64, 128, 32, 2},  {128, 64, 64, 1},  {128, 64, 32, 1},
+    {128, 64, 32, 2},  {128, 128, 64, 1}, {128, 128, 32, 1}, {128, 128, 32, 2},
+};
+
+static bool mfma_tile_known(int m, int n, int kb, int ks) {
+    for (const auto &t : kMfmaTiles)
+        if (t[0] == m && t[1] == n && t[2] == kb && t[3] == ks) return true;
+    return false;
+}
+
+// K granularity of the staged filter: 64 unless that pads more than 32 would.
+static int64_t mfma_kgran(int64_t krun) { return round_up(krun, 64) == round_up(krun, 32) ? 64 : 32; }
+
+// Tile for one chunk of `cols` output columns: enough workgroups to cover the
+// 256 CUs a few times over, the largest tile that still does.
+static void pick_mfma_tile(const conv2d_desc_t &d, int64_t cols, int64_t kgran, conv2d_plan_t *p) {
+    const int m = d.Cout <= 64 ? 64 : 128;
+    const int64_t tm = ceil_div(d.Cout, m);
+    int n = 128, kb = kgran == 64 ? 64 : 32, ks = 1;
+    if (tm * ceil_div(cols, 128) < 1024) n = 64;
+    if (tm * ceil_div(cols, n) < 512 && kgran == 64) { kb = 32; ks = 2; }
+    // developer override for tile sweeps: IM2WIN_MFMA_TILE="MB,NB,KB,KS"
+    if (const char *e = std::getenv("IM2WIN_MFMA_TILE")) {
+        int a = 0, b = 0, c = 0, k = 0;
+        if (std::sscanf(e, "%d,%d,%d,%d", &a, &b, &c, &k) == 4 && mfma_tile_known(a, b, c, k) &&
+            p->K_stage % (c * k) == 0) {
+            p->gemm_tile_m = a; p->gemm_tile_n = b; p->gemm_kslice = c; p->gemm_ksplit = k;
+            return;
+        }
+    }
+    if (!mfma_tile_known(m, n, kb, ks) || p->K_stage % (kb * ks) != 0) {
+        n = 64; kb = 32; ks = 1;              // always compiled, K_stage is a multiple of 32
+    }
+    p->gemm_tile_m = m;
+    p->gemm_tile_n = n;
+    p->gemm_kslice = kb;
+    p->gemm_ksplit = ks;
+}
+
+int valu_cols_per_lane(const conv2d_desc_t &d) {
+    return (d.KH == 7 && d.KW == 7 && d.stride == 2) ? 2 : 4;
+}
+
+// Channel split across the 4 waves of a vector-ALU workgroup: used when the
+// output alone does not give every SIMD a couple of waves.
+static int pick_valu_ksplit(const conv2d_desc_t &d, int64_t rows, int64_t Wo, int64_t Cout_stage) {
+    if (const char *e = std::getenv("IM2WIN_VALU_KSPLIT")) {
+        const int k = std::atoi(e);
+        if (k == 1 || k == 2 || k == 4) return k;
+    }
+    const int64_t nt = valu_cols_per_lane(d);
+    const int64_t waves = (Cout_stage / kValuMt) * ceil_div(rows * ceil_div(Wo, nt), 64);
+    if (waves >= 2048) return 1;
+    if (d.Cin >= 4) return 4;
+    if (d.Cin >= 2) return 2;
+    return 1;
 }
 
 conv2d_status_t make_plan(const conv2d_desc_t &d, conv2d_plan_t *p) {
@@ -89,12 +151,6 @@ conv2d_status_t make_plan(const conv2d_desc_t &d, conv2d_plan_t *p) {
     p->K = d.Cin * d.KH * d.KW;
     p->flops = 2 * d.N * d.Cout * p->Ho * p->Wo * p->K;
 
-    if (p->path == 1) {
-        pick_mfma_tile(d, 0, &p->gemm_tile_m, &p->gemm_tile_n);
-    } else {
-        p->gemm_tile_m = 4 * kValuMt;
-        p->gemm_tile_n = 64 * kValuNt;
-    }
     const StageGeom sg = stage_geom(d, p->layout, p->gemm_tile_m);
     p->Cout_stage = sg.rows;
     p->K_stage = sg.row_len;
@@ -117,6 +173,14 @@ conv2d_status_t make_plan(const conv2d_desc_t &d, conv2d_plan_t *p) {
     p->win_chunk_bytes = p->rows_per_chunk * row_bytes;
     p->ws_bytes = p->wstage_bytes + p->win_chunk_bytes;
     p->meets_ws_target = p->ws_bytes <= p->ws_target_bytes ? 1 : 0;
+    if (p->path == 1) {
+        pick_mfma_tile(d, p->rows_per_chunk * p->Wo, mfma_kgran(d.KW * d.KH * g.Cin_pad), p);
+    } else {
+        p->gemm_tile_m = 4 * kValuMt;
+        p->gemm_tile_n = 64 * valu_cols_per_lane(d);
+        p->gemm_kslice = 0;
+        p->gemm_ksplit = pick_valu_ksplit(d, p->rows_per_chunk, p->Wo, p->Cout_stage);
+    }
     return CONV2D_OK;
 }
 

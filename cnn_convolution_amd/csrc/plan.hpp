@@ -22,9 +22,8 @@ constexpr int kValuMt = 16;
 constexpr int kValuNt = 4;
 constexpr int kValuThreads = 256;
 
-// Matrix-core window-GEMM: K staged through LDS in slices of kMfmaKB.
-constexpr int kMfmaKB = 32;
-constexpr int kMfmaThreads = 256;
+// fp32 vector-ALU kernel: output columns per lane for this filter shape.
+int valu_cols_per_lane(const conv2d_desc_t &d);
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
@@ -52,6 +51,7 @@ struct StageGeom {
     bool needed;   // false when w is already in the staged order
 };
 StageGeom stage_geom(const conv2d_desc_t &d, int32_t layout, int tile_m);
+
 
 // Full plan (fills the C struct). Returns CONV2D_OK or a validation error.
 conv2d_status_t make_plan(const conv2d_desc_t &d, conv2d_plan_t *p);

@@ -113,7 +113,9 @@ typedef struct {
     int64_t im2col_bytes;         /* N*Ho*Wo*Cin*KH*KW*sizeof(dtype)              */
     int64_t ws_target_bytes;      /* im2col_bytes / KW                            */
     int32_t meets_ws_target;      /* ws_bytes <= ws_target_bytes                  */
-    int32_t gemm_tile_m, gemm_tile_n;
+    int32_t gemm_tile_m, gemm_tile_n;  /* output tile of one workgroup (M x N)     */
+    int32_t gemm_kslice;          /* K per LDS stage per wave group (matrix path)  */
+    int32_t gemm_ksplit;          /* wave groups splitting K inside a workgroup    */
     int32_t reserved0;
     int64_t flops;                /* 2*N*Cout*Ho*Wo*Cin*KH*KW (padded taps included) */
 } conv2d_plan_t;

@@ -140,3 +140,22 @@ def test_pointer_checks_before_launch():
     assert _lib.pack(d, 2, 16, 16, 0, 1, None) == 4
     assert _lib.weight_stage(d, 3, 16, 16, None) == 4
     assert _lib.pack(d, 0, None, 16, 0, 1, None) == 2
+
+
+def test_planned_tiles_are_compiled():
+    """Every tile the planner can pick is one the matrix-core kernel is built for."""
+    import numpy as np
+    compiled = {(m, n, kb, ks) for m in (64, 128) for n in (64, 128)
+                for kb, ks in ((64, 1), (32, 1), (32, 2))}
+    rng = np.random.default_rng(0)
+    for _ in range(400):
+        KH, KW = int(rng.integers(1, 8)), int(rng.integers(1, 8))
+        s, p = int(rng.integers(1, 4)), int(rng.integers(0, 4))
+        H, W = int(rng.integers(KH, 80)), int(rng.integers(KW, 80))
+        d = conv.make_desc(int(rng.integers(1, 65)), int(rng.integers(1, 300)), H, W,
+                           int(rng.integers(1, 600)), KH, KW, s, p,
+                           [conv.F16, conv.BF16][int(rng.integers(0, 2))])
+        pl = conv.plan(d)
+        t = (pl.gemm_tile_m, pl.gemm_tile_n, pl.gemm_kslice, pl.gemm_ksplit)
+        assert t in compiled, t
+        assert pl.K_stage % (pl.gemm_kslice * pl.gemm_ksplit) == 0
