@@ -13,7 +13,8 @@ from . import _lib
 from ._lib import (Conv2dError, Desc, Plan, LAYOUT_CL, LAYOUT_ROW, F16, F32, BF16,  # noqa: F401
                    make_desc, workspace_size, plan, profile_enable, profile_read, status_string)
 
-__all__ = ["conv2d", "conv2d_into", "pack", "weight_stage", "describe", "plan", "workspace_size",
+__all__ = ["conv2d", "conv2d_into", "pack", "weight_stage", "window_gemm", "describe", "plan",
+           "workspace_size",
            "Conv2dError", "profile_enable", "profile_read"]
 
 
@@ -116,3 +117,14 @@ def weight_stage(w, stride: int, pad: int, x_hw, layout: int):
     if st != 0:
         raise Conv2dError(st, "im2win_weight_stage")
     return out, {"rows": rows, "row_len": row_len}
+
+
+def window_gemm(win, wst, y, desc: Desc, row0: int, rows: int) -> None:
+    """Enqueue the window-GEMM of window rows [row0, row0+rows) into y.
+
+    win: those rows of the window tensor in the plan's layout (flat device
+    tensor), wst: the staged filter of that layout, y: the full fp32 output."""
+    st = _lib.window_gemm(desc, win.data_ptr(), wst.data_ptr(), y.data_ptr(), row0, rows,
+                          _stream())
+    if st != 0:
+        raise Conv2dError(st, "im2win_window_gemm")

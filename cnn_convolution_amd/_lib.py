@@ -25,7 +25,7 @@ STATUS = {
 # every symbol the header declares
 EXPORTS = [
     "conv2d_workspace_size", "conv2d_plan", "conv2d_fwd", "im2win_pack", "im2win_weight_stage",
-    "conv2d_status_string", "conv2d_profile_enable", "conv2d_profile_read",
+    "im2win_window_gemm", "conv2d_status_string", "conv2d_profile_enable", "conv2d_profile_read",
 ]
 
 
@@ -92,6 +92,8 @@ def lib() -> ctypes.CDLL:
         L.im2win_pack.argtypes = [dp, i32, vp, vp, i64, i64, vp]
         L.im2win_weight_stage.restype = ctypes.c_int
         L.im2win_weight_stage.argtypes = [dp, i32, vp, vp, vp]
+        L.im2win_window_gemm.restype = ctypes.c_int
+        L.im2win_window_gemm.argtypes = [dp, vp, vp, vp, i64, i64, vp]
         L.conv2d_status_string.restype = ctypes.c_char_p
         L.conv2d_status_string.argtypes = [ctypes.c_int]
         L.conv2d_profile_enable.restype = ctypes.c_int
@@ -128,6 +130,10 @@ def pack(d: Desc, layout: int, x: int, out: int, row0: int, rows: int, stream: i
 
 def weight_stage(d: Desc, layout: int, w: int, out: int, stream: int) -> int:
     return lib().im2win_weight_stage(ctypes.byref(d), layout, w, out, stream)
+
+
+def window_gemm(d: Desc, win: int, wst: int, y: int, row0: int, rows: int, stream: int) -> int:
+    return lib().im2win_window_gemm(ctypes.byref(d), win, wst, y, row0, rows, stream)
 
 
 def status_string(st: int) -> str:

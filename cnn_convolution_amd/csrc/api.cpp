@@ -90,6 +90,51 @@ PackArgs pack_args(const conv2d_desc_t &d, const conv2d_plan_t &p, int32_t layou
     return a;
 }
 
+hipError_t launch_gemm(const conv2d_desc_t &d, const conv2d_plan_t &p, const LayoutGeom &g,
+                       const void *win, const void *wst, float *y, int64_t row0, int64_t rows,
+                       hipStream_t s)
+{
+    if (p.path == 0) {
+        ValuGemmArgs ga{};
+        ga.win = static_cast<const float *>(win);
+        ga.wst = static_cast<const float *>(wst);
+        ga.y = y;
+        ga.rows = int(rows);
+        ga.row0 = int(row0);
+        ga.Cin = int(d.Cin);
+        ga.pos_pad = int(g.pos_pad);
+        ga.row_elems = int(g.row_elems);
+        ga.KH = int(d.KH);
+        ga.KW = int(d.KW);
+        ga.stride = int(d.stride);
+        ga.Ho = int(p.Ho);
+        ga.Wo = int(p.Wo);
+        ga.Cout = int(d.Cout);
+        ga.Cout_stage = int(p.Cout_stage);
+        ga.ksplit = p.gemm_ksplit;
+        return launch_gemm_valu_f32(ga, s);
+    }
+    MfmaGemmArgs ga{};
+    ga.win = win;
+    ga.wst = wst;
+    ga.y = y;
+    ga.rows = int(rows);
+    ga.row0 = int(row0);
+    ga.row_elems = int(g.row_elems);
+    ga.col_step = int(d.stride * d.KH * g.Cin_pad);
+    ga.krun = int(d.KW * d.KH * g.Cin_pad);
+    ga.kstage = int(p.K_stage);
+    ga.Ho = int(p.Ho);
+    ga.Wo = int(p.Wo);
+    ga.Cout = int(d.Cout);
+    ga.tile_m = p.gemm_tile_m;
+    ga.tile_n = p.gemm_tile_n;
+    ga.kb = p.gemm_kslice;
+    ga.ks = p.gemm_ksplit;
+    ga.bf16 = d.dtype == CONV2D_BF16 ? 1 : 0;
+    return launch_gemm_mfma(ga, s);
+}
+
 }  // namespace
 
 extern "C" {
@@ -174,46 +219,9 @@ conv2d_status_t conv2d_fwd(const conv2d_desc_t *d, const void *x, const void *w,
         }
         if (e != hipSuccess) return CONV2D_ERR_HIP;
         // (a4, a5) window-GEMM of the chunk, fp32 result written into y
-        ProfScope ps(s, CONV2D_KERNEL_GEMM);
-        if (p.path == 0) {
-            ValuGemmArgs ga{};
-            ga.win = static_cast<const float *>(win);
-            ga.wst = static_cast<const float *>(wst);
-            ga.y = y;
-            ga.rows = int(rows);
-            ga.row0 = int(row0);
-            ga.Cin = int(d->Cin);
-            ga.pos_pad = int(g.pos_pad);
-            ga.row_elems = int(g.row_elems);
-            ga.KH = int(d->KH);
-            ga.KW = int(d->KW);
-            ga.stride = int(d->stride);
-            ga.Ho = int(p.Ho);
-            ga.Wo = int(p.Wo);
-            ga.Cout = int(d->Cout);
-            ga.Cout_stage = int(p.Cout_stage);
-            ga.ksplit = p.gemm_ksplit;
-            e = launch_gemm_valu_f32(ga, s);
-        } else {
-            MfmaGemmArgs ga{};
-            ga.win = win;
-            ga.wst = wst;
-            ga.y = y;
-            ga.rows = int(rows);
-            ga.row0 = int(row0);
-            ga.row_elems = int(g.row_elems);
-            ga.col_step = int(d->stride * d->KH * g.Cin_pad);
-            ga.krun = int(d->KW * d->KH * g.Cin_pad);
-            ga.kstage = int(p.K_stage);
-            ga.Ho = int(p.Ho);
-            ga.Wo = int(p.Wo);
-            ga.Cout = int(d->Cout);
-            ga.tile_m = p.gemm_tile_m;
-            ga.tile_n = p.gemm_tile_n;
-            ga.kb = p.gemm_kslice;
-            ga.ks = p.gemm_ksplit;
-            ga.bf16 = d->dtype == CONV2D_BF16 ? 1 : 0;
-            e = launch_gemm_mfma(ga, s);
+        {
+            ProfScope ps(s, CONV2D_KERNEL_GEMM);
+            e = launch_gemm(*d, p, g, win, wst, y, row0, rows, s);
         }
         if (e != hipSuccess) return CONV2D_ERR_HIP;
     }
@@ -265,6 +273,24 @@ conv2d_status_t im2win_weight_stage(const conv2d_desc_t *d, int32_t layout, cons
     sa.esize = int(elem_size(d->dtype));
     hipStream_t s = static_cast<hipStream_t>(stream);
     const hipError_t e = layout == IM2WIN_LAYOUT_ROW ? launch_stage_row(sa, s) : launch_stage_cl(sa, s);
+    return e == hipSuccess ? CONV2D_OK : CONV2D_ERR_HIP;
+}
+
+conv2d_status_t im2win_window_gemm(const conv2d_desc_t *d, const void *win, const void *wst,
+                                   float *y, int64_t row0, int64_t rows, void *stream)
+{
+    if (!d) return CONV2D_ERR_NULL_POINTER;
+    conv2d_plan_t p;
+    const conv2d_status_t st = make_plan(*d, &p);
+    if (st != CONV2D_OK) return st;
+    if (row0 < 0 || rows < 1 || row0 + rows > p.rows_total) return CONV2D_ERR_RANGE;
+    if (!win || !wst || !y) return CONV2D_ERR_NULL_POINTER;
+    if (!aligned(win, 16) || !aligned(wst, 16) || !aligned(y, 16)) return CONV2D_ERR_MISALIGNED;
+    const LayoutGeom g = layout_geom(*d, p.layout);
+    if (rows * g.row_elems > kMaxElems) return CONV2D_ERR_INVALID_DESC;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    ProfScope ps(s, CONV2D_KERNEL_GEMM);
+    const hipError_t e = launch_gemm(*d, p, g, win, wst, y, row0, rows, s);
     return e == hipSuccess ? CONV2D_OK : CONV2D_ERR_HIP;
 }
 

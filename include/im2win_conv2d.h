@@ -151,6 +151,18 @@ conv2d_status_t im2win_pack(const conv2d_desc_t *d, int32_t layout, const void *
 conv2d_status_t im2win_weight_stage(const conv2d_desc_t *d, int32_t layout, const void *w,
                                     void *out, void *stream);
 
+/* Rows (a4, a5) on their own: the window-GEMM of window rows
+ * [row0, row0 + rows), writing y[n][co][ho][wo] for those rows (r = n*Ho + ho)
+ * and leaving the rest of y untouched. `win` holds exactly those rows in the
+ * layout conv2d_plan reports for d (as im2win_pack writes them, row length
+ * row_elems); `wst` holds the staged filter of that layout (as
+ * im2win_weight_stage writes it; for a 1x1 filter whose plan has
+ * wstage_bytes == 0, w itself). fp32 accumulation, fp32 output.
+ * ("Enabling Memory-efficient Im2win Convolution ...", Sec. III-C Eq. (3),
+ * Sec. III-D Algorithm 1.) Device pointers, 16-byte aligned. */
+conv2d_status_t im2win_window_gemm(const conv2d_desc_t *d, const void *win, const void *wst,
+                                   float *y, int64_t row0, int64_t rows, void *stream);
+
 const char *conv2d_status_string(conv2d_status_t s);
 
 /* ---- measurement hook --------------------------------------------------

@@ -299,3 +299,69 @@ def test_full_size_layers_sampled(name, dt):
     ref = oracle.conv2d_points(x, w, cfg.stride, cfg.pad, idx)
     err = rel_l2(yf[idx], ref)
     assert err <= TOL[dt], f"{name} {dt}: rel L2 {err:.3e} > {TOL[dt]}"
+
+
+# ----------------------------------------------------------------- window-GEMM alone (a4, a5)
+
+def _host_window_rows(x, d, pl, row0, rows):
+    """The window rows in the plan's padded layout, built on the host from the
+    oracle's model of the transform (values copied as raw bits)."""
+    ity = torch.int32 if x.dtype == torch.float32 else torch.int16
+    bits = x.view(ity).numpy()
+    layout = "row" if pl.layout == conv.LAYOUT_ROW else "cl"
+    t, Ho, Wo, Wwin = im2win(bits, d.KH, d.KW, d.stride, d.pad, layout)
+    t = t[row0:row0 + rows]
+    out = np.zeros((rows, pl.row_elems), dtype=bits.dtype)
+    if layout == "row":
+        body = out[:, :d.Cin * pl.pos_pad].reshape(rows, d.Cin, pl.pos_pad)
+        body[:, :, :Wwin * d.KH] = t
+    else:
+        body = out[:, :Wwin * d.KH * pl.Cin_pad].reshape(rows, Wwin * d.KH, pl.Cin_pad)
+        body[:, :, :d.Cin] = t
+    return torch.from_numpy(out.reshape(-1)).view(x.dtype)
+
+
+def _host_staged_filter(w, d, pl):
+    ity = torch.int32 if w.dtype == torch.float32 else torch.int16
+    wb = w.view(ity).numpy()
+    Cout, Cin, KH, KW = wb.shape
+    if pl.layout == conv.LAYOUT_ROW:
+        rows = pl.Cout_stage
+        full = np.zeros((rows, Cin, KH, KW), wb.dtype)
+        full[:Cout] = wb
+        out = full.reshape(rows // 16, 16, Cin, KH, KW).transpose(0, 2, 3, 4, 1).reshape(-1)
+    else:
+        cw = np.zeros((Cout, KW, KH, pl.Cin_pad), wb.dtype)
+        cw[:, :, :, :Cin] = wb.transpose(0, 3, 2, 1)
+        out = np.zeros((Cout, pl.K_stage), wb.dtype)
+        out[:, :KW * KH * pl.Cin_pad] = cw.reshape(Cout, -1)
+        out = out.reshape(-1)
+    return torch.from_numpy(np.ascontiguousarray(out)).view(w.dtype)
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("shape", [(2, 16, 12, 13, 40, 3, 3, 1, 1), (1, 3, 23, 21, 64, 7, 7, 2, 3),
+                                   (2, 64, 9, 9, 130, 3, 3, 2, 1), (1, 24, 10, 10, 20, 5, 3, 1, 2)])
+def test_window_gemm_alone(shape, dt):
+    """The GEMM entry point on a window tensor packed on the host by the
+    oracle's model: the rows it is given are written, the others are not."""
+    N, Cin, H, W, Cout, KH, KW, s, p = shape
+    _say(f"window_gemm {dt} {shape}")
+    x, w = workloads.make_inputs(N, Cin, H, W, Cout, KH, KW, seed=7, dtype=dt, w_dist="normal")
+    d = conv.describe(tuple(x.shape), tuple(w.shape), s, p, CODE[dt])
+    pl = conv.plan(d)
+    ref = oracle.conv2d(x, w, s, p)
+    total = pl.rows_total
+    row0, rows = total // 3, max(1, total // 2)
+    win = _host_window_rows(x, d, pl, row0, rows).to(DEV)
+    wst = (_host_staged_filter(w, d, pl) if pl.wstage_bytes else w.reshape(-1)).to(DEV)
+    y = torch.full((N, Cout, pl.Ho, pl.Wo), 777.0, dtype=torch.float32, device=DEV)
+    conv.window_gemm(win, wst, y, d, row0, rows)
+    torch.cuda.synchronize()
+    got = y.cpu().numpy().transpose(0, 2, 1, 3).reshape(total, Cout, pl.Wo)
+    want = ref.transpose(0, 2, 1, 3).reshape(total, Cout, pl.Wo)
+    sel = slice(row0, row0 + rows)
+    assert rel_l2(got[sel], want[sel]) <= TOL[dt]
+    outside = np.ones(total, bool)
+    outside[sel] = False
+    assert np.all(got[outside] == 777.0)
