@@ -46,7 +46,8 @@ _PLAN_FIELDS = [
     ("im2col_bytes", ctypes.c_int64), ("ws_target_bytes", ctypes.c_int64),
     ("meets_ws_target", ctypes.c_int32), ("gemm_tile_m", ctypes.c_int32),
     ("gemm_tile_n", ctypes.c_int32), ("gemm_kslice", ctypes.c_int32),
-    ("gemm_ksplit", ctypes.c_int32), ("reserved0", ctypes.c_int32),
+    ("gemm_ksplit", ctypes.c_int32), ("gemm_kernel", ctypes.c_int32),
+    ("gemm_wave_m", ctypes.c_int32), ("reserved1", ctypes.c_int32),
     ("flops", ctypes.c_int64),
 ]
 
@@ -55,7 +56,7 @@ class Plan(ctypes.Structure):
     _fields_ = _PLAN_FIELDS
 
     def as_dict(self):
-        return {name: getattr(self, name) for name, _ in _PLAN_FIELDS if name != "reserved0"}
+        return {name: getattr(self, name) for name, _ in _PLAN_FIELDS if name != "reserved1"}
 
 
 class Profile(ctypes.Structure):

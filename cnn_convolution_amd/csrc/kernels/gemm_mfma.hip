@@ -21,6 +21,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <type_traits>
 
 #include "../launch.hpp"
 #include "tile_map.hpp"
@@ -99,15 +100,16 @@ __global__ __launch_bounds__(256 * KS) void gemm_mfma_kernel(
         bk[i] = ok ? (v % GPR) * 8 : -1;
     }
 
-    // Two register sets of global loads. Loads are unconditional (clamped to
-    // a valid address); the masks that zero what lies outside the window are
+    // NS register sets of global loads. Loads are unconditional (clamped to a
+    // valid address); the masks that zero what lies outside the window are
     // applied only when a set is written to LDS, so nothing waits for a load
     // before its data is needed.
+    constexpr int NS = (AV + BV <= 4) ? 4 : 2;   // pipeline depth: NS + 1 stages
     struct Set {
         uint4 a[AV], b[BV];
         bool blo[BV], bhi[BV];
     };
-    Set s0, s1;
+    Set sets[NS];
     auto gload = [&](int k0, Set &st) {
 #pragma unroll
         for (int i = 0; i < AV; ++i) st.a[i] = *reinterpret_cast<const uint4 *>(ap[i] + k0);
@@ -170,30 +172,41 @@ __global__ __launch_bounds__(256 * KS) void gemm_mfma_kernel(
         }
     };
 
-    // Software pipeline, three stages deep: at step k the register set that
+    // Software pipeline, NS + 1 stages deep: at step k the register set that
     // holds stage k+1 is written to LDS and immediately reused for the loads
-    // of stage k+3, then stage k is multiplied from the other LDS buffer.
-    // Every load has two full steps to land, and the wait before a store
-    // only covers the older of the two sets in flight. The body has no
-    // data-dependent branches: loads past the end re-read the last stage.
+    // of stage k+1+NS, then stage k is multiplied from the other LDS buffer.
+    // Every load has NS steps to land, and the wait before a store only
+    // covers the oldest set in flight. The body has no data-dependent
+    // branches: loads past the end re-read the last stage. The loop is
+    // unrolled NS times so that every register set is named statically.
     const int nk = kstage / KI;
     const int last = (nk - 1) * KI;
-    gload(0, s0);
-    gload(min(KI, last), s1);
-    sstore(0, s0);
-    gload(min(2 * KI, last), s0);
+#pragma unroll
+    for (int i = 0; i < NS; ++i) gload(min(i * KI, last), sets[i]);
+    sstore(0, sets[0]);
+    gload(min(NS * KI, last), sets[0]);
     __syncthreads();
-    for (int kt = 0;; kt += 2) {
-        sstore(1, s1);                            // stage kt+1
-        gload(min((kt + 3) * KI, last), s1);
-        compute(0);                               // stage kt
+    bool done = false;
+    auto step = [&](int k, auto J) {
+        constexpr int j = decltype(J)::value;        // k % NS
+        constexpr int nxt = (j + 1) % NS;
+        sstore((j + 1) & 1, sets[nxt]);              // stage k+1
+        gload(min((k + 1 + NS) * KI, last), sets[nxt]);
+        compute(j & 1);                              // stage k
         __syncthreads();
-        if (kt + 1 >= nk) break;
-        sstore(0, s0);                            // stage kt+2
-        gload(min((kt + 4) * KI, last), s0);
-        compute(1);                               // stage kt+1
-        __syncthreads();
-        if (kt + 2 >= nk) break;
+        done = k + 1 >= nk;
+    };
+    for (int kt = 0;; kt += NS) {
+        step(kt, std::integral_constant<int, 0>{});
+        if (done) break;
+        step(kt + 1, std::integral_constant<int, 1>{});
+        if (done) break;
+        if constexpr (NS == 4) {
+            step(kt + 2, std::integral_constant<int, 2>{});
+            if (done) break;
+            step(kt + 3, std::integral_constant<int, 3>{});
+            if (done) break;
+        }
     }
 
     if constexpr (KS > 1) {
@@ -276,21 +289,26 @@ hipError_t launch_tile(const MfmaGemmArgs &a, hipStream_t s)
 hipError_t launch_gemm_mfma(const MfmaGemmArgs &a, hipStream_t s)
 {
     if (a.krun % 4 != 0 || a.col_step % 8 != 0 || a.row_elems % 8 != 0) return hipErrorInvalidValue;
-#define IM2WIN_TILE(M, N, KB, KS)                                                                \
-    if (a.tile_m == M && a.tile_n == N && a.kb == KB && a.ks == KS)                              \
-        return launch_tile<M, N, KB, KS, 2, 2>(a, s);
-    IM2WIN_TILE(64, 64, 64, 1)
-    IM2WIN_TILE(64, 64, 32, 1)
-    IM2WIN_TILE(64, 64, 32, 2)
-    IM2WIN_TILE(64, 128, 64, 1)
-    IM2WIN_TILE(64, 128, 32, 1)
-    IM2WIN_TILE(64, 128, 32, 2)
-    IM2WIN_TILE(128, 64, 64, 1)
-    IM2WIN_TILE(128, 64, 32, 1)
-    IM2WIN_TILE(128, 64, 32, 2)
-    IM2WIN_TILE(128, 128, 64, 1)
-    IM2WIN_TILE(128, 128, 32, 1)
-    IM2WIN_TILE(128, 128, 32, 2)
+#define IM2WIN_TILE(M, N, KB, KS, WM)                                                            \
+    if (a.tile_m == M && a.tile_n == N && a.kb == KB && a.ks == KS && a.wm == WM)                 \
+        return launch_tile<M, N, KB, KS, WM, 4 / WM>(a, s);
+    IM2WIN_TILE(64, 64, 64, 1, 2)
+    IM2WIN_TILE(64, 64, 32, 1, 2)
+    IM2WIN_TILE(64, 64, 32, 2, 2)
+    IM2WIN_TILE(64, 128, 64, 1, 2)
+    IM2WIN_TILE(64, 128, 32, 1, 2)
+    IM2WIN_TILE(64, 128, 32, 2, 2)
+    IM2WIN_TILE(128, 64, 64, 1, 2)
+    IM2WIN_TILE(128, 64, 32, 1, 2)
+    IM2WIN_TILE(128, 64, 32, 2, 2)
+    IM2WIN_TILE(128, 128, 64, 1, 2)
+    IM2WIN_TILE(128, 128, 32, 1, 2)
+    IM2WIN_TILE(128, 128, 32, 2, 2)
+    IM2WIN_TILE(64, 128, 64, 1, 1)
+    IM2WIN_TILE(64, 256, 64, 1, 1)
+    IM2WIN_TILE(64, 256, 32, 1, 1)
+    IM2WIN_TILE(128, 256, 64, 1, 2)
+    IM2WIN_TILE(128, 128, 64, 1, 1)
 #undef IM2WIN_TILE
     return hipErrorInvalidValue;
 }

@@ -199,6 +199,146 @@ __global__ __launch_bounds__(256) void pack_cl_kernel(
     }
 }
 
+// ---------------------------------------------------------------- channels-last, row-staged
+// Workgroup = (window row r, block of cblk channels). Every channel of the
+// block needs the same KH input rows ih in [ho*stride - pad, ... + KH),
+// clipped to [0, H); in NCHW those rows are ONE contiguous run of len
+// elements per channel. Phase 1 copies each run into LDS as whole aligned
+// 16-byte chunks (a chunk may start up to 7 elements before the run, the
+// offset is kept per channel), issuing U chunk loads per wave before the
+// first wait. Phase 2 walks the output vectors of the row in storage order,
+// one per thread: CG channels at one position (w, kh) are gathered from the
+// LDS runs (zero outside the input or past Cin) and stored as one 16-byte
+// (CG = 8) or 8-byte (CG = 4) vector, so consecutive lanes write consecutive
+// bytes of the window row. One barrier per workgroup.
+constexpr int LU = 8;   // chunk loads in flight per lane in phase 1
+
+template <int CG>
+__global__ __launch_bounds__(256) void pack_cl_staged_kernel(
+    const uint16_t *__restrict__ x, uint16_t *__restrict__ out, int Cin, int H, int W, int KH,
+    int stride, int pad, int Ho, int Wwin, int Cin_pad, int row_elems, int row0, int cblocks,
+    int cblk, int cp, int nck, int x_elems, int x_chunks)
+{
+    extern __shared__ __attribute__((aligned(16))) uint16_t run[];   // [cblk][cp]
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int tid = threadIdx.x;
+    const int cbk = blockIdx.x % cblocks;
+    const int rl = blockIdx.x / cblocks;
+    const int r = row0 + rl;
+    const int n = r / Ho;
+    const int ho = r - n * Ho;
+    const int c0 = cbk * cblk;
+    const int cb = min(cblk, Cin_pad - c0);      // channels stored (multiple of CG)
+    const int cin_b = min(cb, Cin - c0);          // of which real (the rest are zero padding)
+    const int ih0 = ho * stride - pad;
+    const int ihA = max(ih0, 0);
+    const int ihB = min(ih0 + KH, H);
+    const int len = ihB > ihA ? (ihB - ihA) * W : 0;   // run length per channel
+    const int HW = H * W;
+    const int g0 = (n * Cin + c0) * HW + ihA * W;        // run start of channel c0 (elements)
+    const uint4 *x16 = reinterpret_cast<const uint4 *>(x);
+
+    // ---- phase 1: runs -> LDS, chunk k of channel c at run[c*cp + 8k]
+    const int lpc = nck < 64 ? nck : 64;          // lanes per channel
+    const int cpi = 64 / lpc;                     // channels per wave instruction
+    const int csub = lane / lpc;
+    const int k0 = lane - csub * lpc;
+    const int ksteps = (nck + lpc - 1) / lpc;
+    const int cgrp = (cin_b + 4 * cpi - 1) / (4 * cpi);
+    const int slots = len > 0 ? cgrp * ksteps : 0;
+    for (int s0 = 0; s0 < slots; s0 += LU) {
+        uint4 v[LU];
+        int dst[LU];
+#pragma unroll
+        for (int u = 0; u < LU; ++u) {
+            const int sl = s0 + u;
+            const int q = sl / ksteps;            // wave-uniform
+            const int ks = sl - q * ksteps;
+            const int c = (q * 4 + wave) * cpi + csub;
+            const int k = ks * lpc + k0;
+            const int g = g0 + c * HW;
+            const int a = (g >> 3) + k;           // chunk index in x
+            const bool ok = sl < slots && csub < cpi && c < cin_b &&
+                            a <= ((g + len - 1) >> 3) && a < x_chunks;
+            v[u] = x16[ok ? a : 0];               // unconditional, from a valid address
+            dst[u] = ok ? c * cp + k * 8 : -1;
+        }
+#pragma unroll
+        for (int u = 0; u < LU; ++u) {
+            if (dst[u] >= 0) {
+                uint32_t *d32 = reinterpret_cast<uint32_t *>(run + dst[u]);
+                d32[0] = v[u].x; d32[1] = v[u].y; d32[2] = v[u].z; d32[3] = v[u].w;
+            }
+        }
+    }
+    // the chunk holding the last elements of x when x_elems is not a multiple
+    // of 8: a 16-byte load would cross the end of x, copy it element-wise
+    if ((x_elems & 7) != 0 && len > 0) {
+        for (int c = tid; c < cin_b; c += 256) {
+            const int g = g0 + c * HW;
+            const int last = g + len - 1;
+            const int a = last >> 3;
+            if (a >= x_chunks) {
+                const int k = a - (g >> 3);
+                for (int j = max(g, a * 8); j <= last; ++j) run[c * cp + k * 8 + (j - a * 8)] = x[j];
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- phase 2: output vectors (cg, kh, w) of this block, cg fastest
+    const int cgroups = cb / CG;
+    const int total = Wwin * KH * cgroups;
+    int cg = tid % cgroups;
+    int t = tid / cgroups;
+    int kh = t % KH;
+    int w = t / KH;
+    const int dcg = 256 % cgroups;
+    const int dt = 256 / cgroups;
+    const int dkh = dt % KH;
+    const int dw = dt / KH;
+    const int sh_step = HW & 7;                   // run offset grows by HW per channel (mod 8)
+    uint16_t *orow = out + int64_t(rl) * row_elems + c0;
+    for (int vi = tid; vi < total; vi += 256) {
+        const int ih = ih0 + kh;
+        const int iw = w - pad;
+        const bool pos_ok = ih >= ihA && ih < ihB && iw >= 0 && iw < W;
+        const int inner = (ih - ihA) * W + iw;
+        uint16_t e16[CG];
+#pragma unroll
+        for (int e = 0; e < CG; ++e) {
+            const int c = cg * CG + e;
+            const bool ok = pos_ok && c < cin_b;
+            const int off = c * cp + ((g0 + c * sh_step) & 7) + inner;
+            const uint16_t val = run[ok ? off : 0];
+            e16[e] = ok ? val : uint16_t(0);
+        }
+        uint32_t o[CG / 2];
+#pragma unroll
+        for (int q = 0; q < CG / 2; ++q) o[q] = uint32_t(e16[2 * q]) | (uint32_t(e16[2 * q + 1]) << 16);
+        uint16_t *dst = orow + (w * KH + kh) * Cin_pad + cg * CG;
+        if constexpr (CG == 8)
+            *reinterpret_cast<uint4 *>(dst) = make_uint4(o[0], o[1], o[2], o[3]);
+        else
+            *reinterpret_cast<uint2 *>(dst) = make_uint2(o[0], o[1]);
+        // advance (cg, kh, w) by 256 vectors
+        cg += dcg;
+        int carry = cg >= cgroups;
+        cg -= carry ? cgroups : 0;
+        kh += dkh + carry;
+        carry = kh >= KH;
+        kh -= carry ? KH : 0;
+        w += dw + carry;
+    }
+    // zero the row tail past W_win*KH*Cin_pad (alignment padding), once per row
+    if (cbk == 0) {
+        const int used = Wwin * KH * Cin_pad;
+        uint16_t *orow0 = out + int64_t(rl) * row_elems;
+        for (int q = used + tid; q < row_elems; q += 256) orow0[q] = 0;
+    }
+}
+
 }  // namespace
 
 template <typename E>
@@ -229,21 +369,49 @@ hipError_t launch_pack_row(const PackArgs &a, hipStream_t s)
     return a.esize == 4 ? launch_pack_row_t<uint32_t>(a, s) : launch_pack_row_t<uint16_t>(a, s);
 }
 
+// LDS budget of the row-staged channels-last pack (per workgroup)
+constexpr int kStagedLdsBytes = 64 * 1024;
+
 hipError_t launch_pack_cl(const PackArgs &a, hipStream_t s)
 {
     if (a.esize != 2) return hipErrorInvalidValue;
-    const int cblocks = (a.Cin_pad + CB - 1) / CB;
-    const dim3 grid(static_cast<unsigned>(int64_t(a.rows) * cblocks));
     const auto *x = static_cast<const uint16_t *>(a.x);
     auto *out = static_cast<uint16_t *>(a.out);
-    if (a.Cin_pad % 8 == 0)
+    const int cg = a.Cin_pad % 8 == 0 ? 8 : (a.Cin_pad == 4 ? 4 : 0);
+    if (cg == 0) return hipErrorInvalidValue;
+    // row-staged form: one LDS run of KH input rows per channel
+    const int nck = (a.KH * a.W + 14) / 8;          // 16-byte chunks per run, worst alignment
+    int cp = 8 * nck + 2;                            // LDS pitch: odd number of 4-byte words
+    if ((cp / 2) % 2 == 0) cp += 2;
+    int cblk = (kStagedLdsBytes / (2 * cp)) / cg * cg;
+    const int x_elems = a.N * a.Cin * a.H * a.W;
+    if (cblk >= cg && x_elems >= 8) {
+        cblk = cblk < a.Cin_pad ? cblk : a.Cin_pad;
+        // keep at least ~2 workgroups per CU: split channels when rows are few
+        while (int64_t(a.rows) * ((a.Cin_pad + cblk - 1) / cblk) < 512 && cblk >= 128)
+            cblk = (cblk / 2) / cg * cg;
+        const int cblocks = (a.Cin_pad + cblk - 1) / cblk;
+        const dim3 grid(static_cast<unsigned>(int64_t(a.rows) * cblocks));
+        const size_t lds = size_t(cblk) * cp * 2;
+        if (cg == 8)
+            hipLaunchKernelGGL(pack_cl_staged_kernel<8>, grid, dim3(256), lds, s, x, out, a.Cin, a.H,
+                               a.W, a.KH, a.stride, a.pad, a.Ho, a.Wwin, a.Cin_pad, a.row_elems,
+                               a.row0, cblocks, cblk, cp, nck, x_elems, x_elems >> 3);
+        else
+            hipLaunchKernelGGL(pack_cl_staged_kernel<4>, grid, dim3(256), lds, s, x, out, a.Cin, a.H,
+                               a.W, a.KH, a.stride, a.pad, a.Ho, a.Wwin, a.Cin_pad, a.row_elems,
+                               a.row0, cblocks, cblk, cp, nck, x_elems, x_elems >> 3);
+        return hipGetLastError();
+    }
+    // very wide rows: tiled form (64 columns x 4 filter rows x 64 channels per pass)
+    const int cblocks = (a.Cin_pad + CB - 1) / CB;
+    const dim3 grid(static_cast<unsigned>(int64_t(a.rows) * cblocks));
+    if (cg == 8)
         hipLaunchKernelGGL(pack_cl_kernel<8>, grid, dim3(256), 0, s, x, out, a.Cin, a.H, a.W, a.KH,
                            a.stride, a.pad, a.Ho, a.Wwin, a.Cin_pad, a.row_elems, a.row0, cblocks);
-    else if (a.Cin_pad == 4)
+    else
         hipLaunchKernelGGL(pack_cl_kernel<4>, grid, dim3(256), 0, s, x, out, a.Cin, a.H, a.W, a.KH,
                            a.stride, a.pad, a.Ho, a.Wwin, a.Cin_pad, a.row_elems, a.row0, cblocks);
-    else
-        return hipErrorInvalidValue;
     return hipGetLastError();
 }
 

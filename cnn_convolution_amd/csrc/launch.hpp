@@ -52,8 +52,11 @@ struct MfmaGemmArgs {
     int Ho, Wo, Cout;
     int tile_m, tile_n;     // output tile
     int kb, ks;             // K per wave group per LDS stage; wave groups splitting K
+    int wm;                 // waves along M in a wave group (4 / wm along N)
     int bf16;               // 0: fp16, 1: bf16
 };
 hipError_t launch_gemm_mfma(const MfmaGemmArgs &a, hipStream_t s);
+// register-direct form: tile_m x tile_n is the tile of one wave
+hipError_t launch_gemm_mfma_direct(const MfmaGemmArgs &a, hipStream_t s);
 
 }  // namespace im2win

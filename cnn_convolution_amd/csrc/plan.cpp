@@ -73,15 +73,17 @@ StageGeom stage_geom(const conv2d_desc_t &d, int32_t layout, int tile_m) {
 }
 
 // Matrix-core tiles the kernel is compiled for: {MB, NB, KB, KS}.
-static const int kMfmaTiles[][4] = {
-    {64, 64, 64, 1},   {64, 64, 32, 1},   {64, 64, 32, 2},   {64, 128, 64, 1},
-    {64, 128, 32, 1},  {64, 128, 32, 2},  {128, 64, 64, 1},  {128, 64, 32, 1},
-    {128, 64, 32, 2},  {128, 128, 64, 1}, {128, 128, 32, 1}, {128, 128, 32, 2},
+static const int kMfmaTiles[][5] = {
+    {64, 64, 64, 1, 2},   {64, 64, 32, 1, 2},   {64, 64, 32, 2, 2},   {64, 128, 64, 1, 2},
+    {64, 128, 32, 1, 2},  {64, 128, 32, 2, 2},  {128, 64, 64, 1, 2},  {128, 64, 32, 1, 2},
+    {128, 64, 32, 2, 2},  {128, 128, 64, 1, 2}, {128, 128, 32, 1, 2}, {128, 128, 32, 2, 2},
+    {64, 128, 64, 1, 1},  {64, 256, 64, 1, 1},  {64, 256, 32, 1, 1},  {128, 256, 64, 1, 2},
+    {128, 128, 64, 1, 1},
 };
 
-static bool mfma_tile_known(int m, int n, int kb, int ks) {
+static bool mfma_tile_known(int m, int n, int kb, int ks, int wm) {
     for (const auto &t : kMfmaTiles)
-        if (t[0] == m && t[1] == n && t[2] == kb && t[3] == ks) return true;
+        if (t[0] == m && t[1] == n && t[2] == kb && t[3] == ks && t[4] == wm) return true;
     return false;
 }
 
@@ -91,27 +93,68 @@ static int64_t mfma_kgran(int64_t krun) { return round_up(krun, 64) == round_up(
 // Tile for one chunk of `cols` output columns: enough workgroups to cover the
 // 256 CUs a few times over, the largest tile that still does.
 static void pick_mfma_tile(const conv2d_desc_t &d, int64_t cols, int64_t kgran, conv2d_plan_t *p) {
-    const int m = d.Cout <= 64 ? 64 : 128;
-    const int64_t tm = ceil_div(d.Cout, m);
-    int n = 128, kb = kgran == 64 ? 64 : 32, ks = 1;
-    if (tm * ceil_div(cols, 128) < 1024) n = 64;
-    if (tm * ceil_div(cols, n) < 512 && kgran == 64) { kb = 32; ks = 2; }
-    // developer override for tile sweeps: IM2WIN_MFMA_TILE="MB,NB,KB,KS"
+    // Measured on MI355X over the layer sweep (ResNet-style 3x3, 7x7 stem,
+    // deep 3x3, 5x5, 3x3 stride 2, 512-channel 7x7, 1x1): the kernel is bound
+    // by the latency of its LDS and memory round trips, so the choice is about
+    // keeping enough independent waves per CU rather than about reuse.
+    const int64_t t64 = ceil_div(d.Cout, 64) * ceil_div(cols, 64);   // 64x64 output tiles
+    int m, n, kb, ks, wm;
+    if (d.Cout <= 64) {
+        // one M block; wide N tiles, all four waves along N
+        if (kgran == 64) { m = 64; n = 128; kb = 64; ks = 1; wm = 1; }
+        else             { m = 64; n = 64;  kb = 32; ks = 1; wm = 2; }
+    } else if (t64 >= 4096) {
+        m = 128; n = 128; kb = 64; ks = 1; wm = 2;    // plenty of tiles (large N*Ho*Wo)
+    } else if (t64 >= 700) {
+        m = 128; n = 128; kb = 64; ks = 1; wm = 1;
+    } else if (d.Cout >= 512 || t64 < 200) {
+        m = 64; n = 64; kb = 32; ks = 2; wm = 2;      // few tiles, deep K: split K in the workgroup
+    } else {
+        m = 128; n = 64; kb = 32; ks = 2; wm = 2;
+    }
+    // developer override for tile sweeps: IM2WIN_MFMA_TILE="MB,NB,KB,KS[,WM]"
     if (const char *e = std::getenv("IM2WIN_MFMA_TILE")) {
-        int a = 0, b = 0, c = 0, k = 0;
-        if (std::sscanf(e, "%d,%d,%d,%d", &a, &b, &c, &k) == 4 && mfma_tile_known(a, b, c, k) &&
-            p->K_stage % (c * k) == 0) {
+        int a = 0, b = 0, c = 0, k = 0, w = 2;
+        const int got = std::sscanf(e, "%d,%d,%d,%d,%d", &a, &b, &c, &k, &w);
+        if (got >= 4 && mfma_tile_known(a, b, c, k, w) && p->K_stage % (c * k) == 0) {
             p->gemm_tile_m = a; p->gemm_tile_n = b; p->gemm_kslice = c; p->gemm_ksplit = k;
+            p->gemm_wave_m = w;
             return;
         }
     }
-    if (!mfma_tile_known(m, n, kb, ks) || p->K_stage % (kb * ks) != 0) {
-        n = 64; kb = 32; ks = 1;              // always compiled, K_stage is a multiple of 32
+    if (!mfma_tile_known(m, n, kb, ks, wm) || p->K_stage % (kb * ks) != 0) {
+        m = 64; n = 64; kb = 32; ks = 1; wm = 2;   // always compiled, K_stage is a multiple of 32
     }
     p->gemm_tile_m = m;
     p->gemm_tile_n = n;
     p->gemm_kslice = kb;
     p->gemm_ksplit = ks;
+    p->gemm_wave_m = wm;
+}
+
+// Register-direct matrix-core form (opt-in: IM2WIN_MFMA_KERNEL=direct): one
+// wave per (16*FM) x (16*FN) tile, no LDS; IM2WIN_MFMA_WAVE_TILE="MW,NW".
+// Slower than the LDS tiles on every measured layer, kept for comparison.
+static void pick_mfma_direct(const conv2d_desc_t &d, int64_t cols, conv2d_plan_t *p) {
+    const char *k = std::getenv("IM2WIN_MFMA_KERNEL");
+    if (!k || std::strcmp(k, "direct") != 0) return;
+    int mw = d.Cout <= 32 ? 32 : 64;
+    int nw = 64;
+    const int64_t waves = ceil_div(d.Cout, mw) * ceil_div(cols, nw);
+    if (waves < 2048) nw = 32;
+    if (const char *e = std::getenv("IM2WIN_MFMA_WAVE_TILE")) {
+        int a = 0, b = 0;
+        if (std::sscanf(e, "%d,%d", &a, &b) == 2 && (a == 32 || a == 64) && (b == 32 || b == 64)) {
+            mw = a;
+            nw = b;
+        }
+    }
+    p->gemm_kernel = 2;
+    p->gemm_tile_m = mw;
+    p->gemm_tile_n = nw;
+    p->gemm_kslice = 32;
+    p->gemm_ksplit = 1;
+    p->gemm_wave_m = 0;
 }
 
 int valu_cols_per_lane(const conv2d_desc_t &d) {
@@ -175,7 +218,10 @@ conv2d_status_t make_plan(const conv2d_desc_t &d, conv2d_plan_t *p) {
     p->meets_ws_target = p->ws_bytes <= p->ws_target_bytes ? 1 : 0;
     if (p->path == 1) {
         pick_mfma_tile(d, p->rows_per_chunk * p->Wo, mfma_kgran(d.KW * d.KH * g.Cin_pad), p);
+        p->gemm_kernel = 1;
+        pick_mfma_direct(d, p->rows_per_chunk * p->Wo, p);
     } else {
+        p->gemm_kernel = 0;
         p->gemm_tile_m = 4 * kValuMt;
         p->gemm_tile_n = 64 * valu_cols_per_lane(d);
         p->gemm_kslice = 0;

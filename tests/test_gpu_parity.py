@@ -63,6 +63,10 @@ PACK_CASES = [
     (1, 5, 9, 70, 5, 4, 1, 2),       # wide rows: several column blocks
     (3, 64, 6, 6, 1, 1, 1, 0),
     (1, 8, 12, 12, 9, 9, 1, 4),      # KH > 8: two filter-row passes
+    (1, 130, 3, 3, 3, 3, 1, 1),      # few rows: channels split over workgroups, ragged last block
+    (1, 1, 2, 3, 1, 1, 1, 0),        # fewer than 8 input elements
+    (1, 12, 3, 1100, 3, 3, 1, 1),    # long input rows: 8-channel blocks to fit LDS
+    (1, 5, 3, 2400, 7, 3, 1, 3),     # rows too long to stage in LDS: tiled form
 ]
 
 

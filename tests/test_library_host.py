@@ -145,8 +145,10 @@ def test_pointer_checks_before_launch():
 def test_planned_tiles_are_compiled():
     """Every tile the planner can pick is one the matrix-core kernel is built for."""
     import numpy as np
-    compiled = {(m, n, kb, ks) for m in (64, 128) for n in (64, 128)
+    compiled = {(m, n, kb, ks, 2) for m in (64, 128) for n in (64, 128)
                 for kb, ks in ((64, 1), (32, 1), (32, 2))}
+    compiled |= {(64, 128, 64, 1, 1), (64, 256, 64, 1, 1), (64, 256, 32, 1, 1),
+                 (128, 256, 64, 1, 2), (128, 128, 64, 1, 1)}
     rng = np.random.default_rng(0)
     for _ in range(400):
         KH, KW = int(rng.integers(1, 8)), int(rng.integers(1, 8))
@@ -156,6 +158,10 @@ def test_planned_tiles_are_compiled():
                            int(rng.integers(1, 600)), KH, KW, s, p,
                            [conv.F16, conv.BF16][int(rng.integers(0, 2))])
         pl = conv.plan(d)
-        t = (pl.gemm_tile_m, pl.gemm_tile_n, pl.gemm_kslice, pl.gemm_ksplit)
+        t = (pl.gemm_tile_m, pl.gemm_tile_n, pl.gemm_kslice, pl.gemm_ksplit, pl.gemm_wave_m)
+        assert pl.gemm_kernel in (1, 2)
+        if pl.gemm_kernel == 2:
+            assert pl.gemm_tile_m in (32, 64) and pl.gemm_tile_n in (32, 64)
+            continue
         assert t in compiled, t
         assert pl.K_stage % (pl.gemm_kslice * pl.gemm_ksplit) == 0
