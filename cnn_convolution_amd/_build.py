@@ -28,7 +28,7 @@ SOURCES = [
     os.path.join(CSRC, "kernels", "weight_stage.hip"),
     os.path.join(CSRC, "kernels", "gemm_valu.hip"),
     os.path.join(CSRC, "kernels", "gemm_mfma.hip"),
-    os.path.join(CSRC, "kernels", "gemm_mfma_direct.hip"),
+    os.path.join(CSRC, "kernels", "gemm_mfma_resident.hip"),
 ]
 
 ARCH = "gfx950"

@@ -7,6 +7,8 @@
 
 #include <cstdint>
 
+#include "plan.hpp"
+
 namespace im2win {
 
 struct PackArgs {
@@ -56,7 +58,9 @@ struct MfmaGemmArgs {
     int bf16;               // 0: fp16, 1: bf16
 };
 hipError_t launch_gemm_mfma(const MfmaGemmArgs &a, hipStream_t s);
-// register-direct form: tile_m x tile_n is the tile of one wave
-hipError_t launch_gemm_mfma_direct(const MfmaGemmArgs &a, hipStream_t s);
+// filter-resident form: a 64-row filter block stays in LDS for the whole K,
+// window fragments go straight to registers; tile_n = columns per workgroup
+// (64, 128 or 256), tile_m = 64
+hipError_t launch_gemm_mfma_resident(const MfmaGemmArgs &a, hipStream_t s);
 
 }  // namespace im2win

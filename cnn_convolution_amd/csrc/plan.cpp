@@ -132,29 +132,37 @@ static void pick_mfma_tile(const conv2d_desc_t &d, int64_t cols, int64_t kgran, 
     p->gemm_wave_m = wm;
 }
 
-// Register-direct matrix-core form (opt-in: IM2WIN_MFMA_KERNEL=direct): one
-// wave per (16*FM) x (16*FN) tile, no LDS; IM2WIN_MFMA_WAVE_TILE="MW,NW".
-// Slower than the LDS tiles on every measured layer, kept for comparison.
-static void pick_mfma_direct(const conv2d_desc_t &d, int64_t cols, conv2d_plan_t *p) {
-    const char *k = std::getenv("IM2WIN_MFMA_KERNEL");
-    if (!k || std::strcmp(k, "direct") != 0) return;
-    int mw = d.Cout <= 32 ? 32 : 64;
-    int nw = 64;
-    const int64_t waves = ceil_div(d.Cout, mw) * ceil_div(cols, nw);
-    if (waves < 2048) nw = 32;
-    if (const char *e = std::getenv("IM2WIN_MFMA_WAVE_TILE")) {
-        int a = 0, b = 0;
-        if (std::sscanf(e, "%d,%d", &a, &b) == 2 && (a == 32 || a == 64) && (b == 32 || b == 64)) {
-            mw = a;
-            nw = b;
-        }
+// Filter-resident matrix-core form: a 64-row block of the staged filter
+// stays in LDS for the whole K and the window fragments go straight to
+// registers. Opt-in (the block must fit: short filter rows, small
+// Cin*KH*KW). IM2WIN_MFMA_KERNEL=tiled|resident, IM2WIN_MFMA_RESIDENT_N
+// (64, 128 or 256 columns per workgroup) and IM2WIN_MFMA_RESIDENT_PF (4, 8
+// or 16 K steps in flight) override the choice for sweeps.
+static void pick_mfma_resident(const conv2d_desc_t &d, int64_t cols, conv2d_plan_t *p) {
+    (void)d;
+    const bool fits = 64 * (p->K_stage + 8) * 2 <= kResidentMaxLdsBytes;
+    bool use = false;     // measured no faster than the tiled kernel on any layer of the sweep
+    if (const char *k = std::getenv("IM2WIN_MFMA_KERNEL")) {
+        if (std::strcmp(k, "tiled") == 0) use = false;
+        if (std::strcmp(k, "resident") == 0) use = fits;
+    }
+    if (!use) return;
+    int n = ceil_div(d.Cout, 64) * ceil_div(cols, 128) >= 512 ? 128 : 64;
+    if (const char *e = std::getenv("IM2WIN_MFMA_RESIDENT_N")) {
+        const int v = std::atoi(e);
+        if (v == 64 || v == 128 || v == 256) n = v;
+    }
+    int pf = 8;
+    if (const char *e = std::getenv("IM2WIN_MFMA_RESIDENT_PF")) {
+        const int v = std::atoi(e);
+        if (v == 4 || v == 8 || v == 16) pf = v;
     }
     p->gemm_kernel = 2;
-    p->gemm_tile_m = mw;
-    p->gemm_tile_n = nw;
-    p->gemm_kslice = 32;
+    p->gemm_tile_m = 64;
+    p->gemm_tile_n = n;
+    p->gemm_kslice = pf;      // this form: K steps of window fragments in flight per wave
     p->gemm_ksplit = 1;
-    p->gemm_wave_m = 0;
+    p->gemm_wave_m = 1;
 }
 
 int valu_cols_per_lane(const conv2d_desc_t &d) {
@@ -219,7 +227,7 @@ conv2d_status_t make_plan(const conv2d_desc_t &d, conv2d_plan_t *p) {
     if (p->path == 1) {
         pick_mfma_tile(d, p->rows_per_chunk * p->Wo, mfma_kgran(d.KW * d.KH * g.Cin_pad), p);
         p->gemm_kernel = 1;
-        pick_mfma_direct(d, p->rows_per_chunk * p->Wo, p);
+        pick_mfma_resident(d, p->rows_per_chunk * p->Wo, p);
     } else {
         p->gemm_kernel = 0;
         p->gemm_tile_m = 4 * kValuMt;

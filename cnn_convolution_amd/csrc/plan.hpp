@@ -22,6 +22,10 @@ constexpr int kValuMt = 16;
 constexpr int kValuNt = 4;
 constexpr int kValuThreads = 256;
 
+// filter-resident matrix-core window-GEMM: LDS bytes one workgroup may hold
+// for its 64 x (K_stage + 8) filter block (two workgroups still fit a CU)
+constexpr int64_t kResidentMaxLdsBytes = 80 * 1024;
+
 // fp32 vector-ALU kernel: output columns per lane for this filter shape.
 int valu_cols_per_lane(const conv2d_desc_t &d);
 

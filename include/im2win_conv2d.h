@@ -114,10 +114,12 @@ typedef struct {
     int64_t ws_target_bytes;      /* im2col_bytes / KW                            */
     int32_t meets_ws_target;      /* ws_bytes <= ws_target_bytes                  */
     int32_t gemm_tile_m, gemm_tile_n;  /* output tile of one workgroup (M x N)     */
-    int32_t gemm_kslice;          /* K per LDS stage per wave group (matrix path)  */
+    int32_t gemm_kslice;          /* kernel 1: K per LDS stage per wave group;
+                                     kernel 2: K steps of window fragments in flight */
     int32_t gemm_ksplit;          /* wave groups splitting K inside a workgroup    */
     int32_t gemm_kernel;          /* 0: vector ALU, 1: matrix core via LDS tiles,
-                                     2: matrix core, fragments straight to registers */
+                                     2: matrix core, filter block resident in LDS and
+                                        window fragments straight to registers      */
     int32_t gemm_wave_m;          /* waves along M in a wave group (matrix path)   */
     int32_t reserved1;
     int64_t flops;                /* 2*N*Cout*Ho*Wo*Cin*KH*KW (padded taps included) */

@@ -183,6 +183,43 @@ def test_conv_matches_oracle(shape, dt):
     assert err <= TOL[dt], f"rel L2 {err:.3e} > {TOL[dt]}"
 
 
+# Both matrix-core GEMM forms (and every workgroup width of the resident one)
+# on the same shapes: the planner picks one per layer, these force each.
+MFMA_FORMS = [
+    {"IM2WIN_MFMA_KERNEL": "tiled"},
+    {"IM2WIN_MFMA_KERNEL": "resident", "IM2WIN_MFMA_RESIDENT_N": "64", "IM2WIN_MFMA_RESIDENT_PF": "4"},
+    {"IM2WIN_MFMA_KERNEL": "resident", "IM2WIN_MFMA_RESIDENT_N": "128"},
+    {"IM2WIN_MFMA_KERNEL": "resident", "IM2WIN_MFMA_RESIDENT_N": "256", "IM2WIN_MFMA_RESIDENT_PF": "16"},
+]
+FORM_SHAPES = [
+    (2, 64, 17, 19, 70, 3, 3, 1, 1),    # Cout past one 64-row block, ragged columns
+    (2, 3, 45, 47, 64, 7, 7, 2, 3),     # 4 channels per position, 4-value window tail
+    (3, 64, 10, 10, 256, 1, 1, 1, 0),   # 1x1: the filter itself is the staged filter
+    (1, 5, 13, 11, 9, 2, 4, 3, 2),      # KH != KW, stride 3
+    (2, 32, 15, 14, 72, 3, 3, 2, 1),
+    (1, 24, 9, 9, 40, 5, 5, 1, 2),      # filter rows of 608 halves: close to the resident limit
+]
+
+
+@pytest.mark.parametrize("form", MFMA_FORMS, ids=lambda f: "-".join(f.values()))
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+@pytest.mark.parametrize("shape", FORM_SHAPES)
+def test_mfma_forms_match_oracle(shape, dt, form, monkeypatch):
+    for k, v in form.items():
+        monkeypatch.setenv(k, v)
+    N, Cin, H, W, Cout, KH, KW, s, p = shape
+    d = conv.describe((N, Cin, H, W), (Cout, Cin, KH, KW), s, p, CODE[dt])
+    want = 2 if form["IM2WIN_MFMA_KERNEL"] == "resident" else 1
+    assert conv.plan(d).gemm_kernel == want
+    _say(f"conv-form {form} {dt} {shape}")
+    x, w = workloads.make_inputs(N, Cin, H, W, Cout, KH, KW, seed=sum(shape) + 7, dtype=dt,
+                                 w_dist="normal")
+    y = run_conv(x, w, s, p)
+    ref = oracle.conv2d(x, w, s, p)
+    err = rel_l2(y.numpy(), ref)
+    assert err <= TOL[dt], f"rel L2 {err:.3e} > {TOL[dt]}"
+
+
 @pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
 @pytest.mark.parametrize("shape", [(2, 3, 32, 32, 16, 3, 3, 1, 1), (2, 32, 15, 14, 72, 3, 3, 2, 1),
                                    (1, 3, 30, 30, 64, 7, 7, 2, 3), (2, 64, 8, 8, 128, 1, 1, 1, 0),
