@@ -247,6 +247,7 @@ __global__ __launch_bounds__(256) void pack_cl_staged_kernel(
     const int ksteps = (nck + lpc - 1) / lpc;
     const int cgrp = (cin_b + 4 * cpi - 1) / (4 * cpi);
     const int slots = len > 0 ? cgrp * ksteps : 0;
+    const int spill = cblk * cp + lane * 8;       // per-lane 16-byte slot after the runs
     for (int s0 = 0; s0 < slots; s0 += LU) {
         uint4 v[LU];
         int dst[LU];
@@ -262,14 +263,12 @@ __global__ __launch_bounds__(256) void pack_cl_staged_kernel(
             const bool ok = sl < slots && csub < cpi && c < cin_b &&
                             a <= ((g + len - 1) >> 3) && a < x_chunks;
             v[u] = x16[ok ? a : 0];               // unconditional, from a valid address
-            dst[u] = ok ? c * cp + k * 8 : -1;
-        }
+            dst[u] = ok ? c * cp + k * 8 : spill;  // lanes with nothing to copy write their own
+        }                                         // slot past the runs (no branch)
 #pragma unroll
         for (int u = 0; u < LU; ++u) {
-            if (dst[u] >= 0) {
-                uint32_t *d32 = reinterpret_cast<uint32_t *>(run + dst[u]);
-                d32[0] = v[u].x; d32[1] = v[u].y; d32[2] = v[u].z; d32[3] = v[u].w;
-            }
+            uint32_t *d32 = reinterpret_cast<uint32_t *>(run + dst[u]);
+            d32[0] = v[u].x; d32[1] = v[u].y; d32[2] = v[u].z; d32[3] = v[u].w;
         }
     }
     // the chunk holding the last elements of x when x_elems is not a multiple
@@ -285,6 +284,9 @@ __global__ __launch_bounds__(256) void pack_cl_staged_kernel(
             }
         }
     }
+    // channels past Cin (zero padding of the last group): zero runs, so that
+    // phase 2 reads them like any other channel
+    for (int i = cin_b * cp + tid; i < cb * cp; i += 256) run[i] = 0;
     __syncthreads();
 
     // ---- phase 2: output vectors (cg, kh, w) of this block, cg fastest
@@ -298,38 +300,55 @@ __global__ __launch_bounds__(256) void pack_cl_staged_kernel(
     const int dt = 256 / cgroups;
     const int dkh = dt % KH;
     const int dw = dt / KH;
-    const int sh_step = HW & 7;                   // run offset grows by HW per channel (mod 8)
+    // element e of a vector (channel cg*CG + e) sits at run offset
+    // (cg*CG + e)*cp + shift + inner, where the run of channel c starts
+    // shift = (g0 + c*HW) mod 8 elements into its first chunk; cg*CG*HW is a
+    // multiple of 8 (CG = 8, or CG = 4 with one group), so e*cp + shift is the
+    // same for every vector: wave-uniform offsets
+    int eo[CG];
+#pragma unroll
+    for (int e = 0; e < CG; ++e) eo[e] = e * cp + ((g0 + e * HW) & 7);
     uint16_t *orow = out + int64_t(rl) * row_elems + c0;
-    for (int vi = tid; vi < total; vi += 256) {
-        const int ih = ih0 + kh;
-        const int iw = w - pad;
-        const bool pos_ok = ih >= ihA && ih < ihB && iw >= 0 && iw < W;
-        const int inner = (ih - ihA) * W + iw;
-        uint16_t e16[CG];
+    const int khn = max(ihB - ihA, 0);                     // staged rows (0: all padding)
+    auto advance = [&](int &cg_, int &kh_, int &w_) {      // by 256 vectors
+        cg_ += dcg;
+        int carry = cg_ >= cgroups;
+        cg_ -= carry ? cgroups : 0;
+        kh_ += dkh + carry;
+        carry = kh_ >= KH;
+        kh_ -= carry ? KH : 0;
+        w_ += dw + carry;
+    };
+    auto gather = [&](int cg_, int kh_, int w_, uint32_t (&o)[CG / 2]) {
+        const int ihr = ih0 + kh_ - ihA;                   // row inside the staged runs
+        const int iw = w_ - pad;
+        const bool ok = unsigned(ihr) < unsigned(khn) && unsigned(iw) < unsigned(W);
+        const int base = ok ? cg_ * CG * cp + ihr * W + iw : 0;
+        uint32_t e32[CG];
 #pragma unroll
-        for (int e = 0; e < CG; ++e) {
-            const int c = cg * CG + e;
-            const bool ok = pos_ok && c < cin_b;
-            const int off = c * cp + ((g0 + c * sh_step) & 7) + inner;
-            const uint16_t val = run[ok ? off : 0];
-            e16[e] = ok ? val : uint16_t(0);
-        }
-        uint32_t o[CG / 2];
+        for (int e = 0; e < CG; ++e) e32[e] = run[base + eo[e]];
+        const uint32_t m = ok ? 0xffffffffu : 0u;
 #pragma unroll
-        for (int q = 0; q < CG / 2; ++q) o[q] = uint32_t(e16[2 * q]) | (uint32_t(e16[2 * q + 1]) << 16);
-        uint16_t *dst = orow + (w * KH + kh) * Cin_pad + cg * CG;
+        for (int q = 0; q < CG / 2; ++q) o[q] = (e32[2 * q] | (e32[2 * q + 1] << 16)) & m;
+    };
+    auto put = [&](int cg_, int kh_, int w_, const uint32_t (&o)[CG / 2]) {
+        uint16_t *dst = orow + (w_ * KH + kh_) * Cin_pad + cg_ * CG;
         if constexpr (CG == 8)
             *reinterpret_cast<uint4 *>(dst) = make_uint4(o[0], o[1], o[2], o[3]);
         else
             *reinterpret_cast<uint2 *>(dst) = make_uint2(o[0], o[1]);
-        // advance (cg, kh, w) by 256 vectors
-        cg += dcg;
-        int carry = cg >= cgroups;
-        cg -= carry ? cgroups : 0;
-        kh += dkh + carry;
-        carry = kh >= KH;
-        kh -= carry ? KH : 0;
-        w += dw + carry;
+    };
+    // two vectors per trip: both gathers are issued before either store waits
+    for (int vi = tid; vi < total; vi += 512) {
+        int cg1 = cg, kh1 = kh, w1 = w;
+        advance(cg1, kh1, w1);
+        uint32_t o0[CG / 2], o1[CG / 2];
+        gather(cg, kh, w, o0);
+        gather(cg1, kh1, w1, o1);
+        put(cg, kh, w, o0);
+        if (vi + 256 < total) put(cg1, kh1, w1, o1);
+        cg = cg1; kh = kh1; w = w1;
+        advance(cg, kh, w);
     }
     // zero the row tail past W_win*KH*Cin_pad (alignment padding), once per row
     if (cbk == 0) {
@@ -370,7 +389,7 @@ hipError_t launch_pack_row(const PackArgs &a, hipStream_t s)
 }
 
 // LDS budget of the row-staged channels-last pack (per workgroup)
-constexpr int kStagedLdsBytes = 64 * 1024;
+constexpr int kStagedLdsBytes = 63 * 1024;   // plus 1 KB of spill slots: within 64 KB
 
 hipError_t launch_pack_cl(const PackArgs &a, hipStream_t s)
 {
@@ -392,7 +411,7 @@ hipError_t launch_pack_cl(const PackArgs &a, hipStream_t s)
             cblk = (cblk / 2) / cg * cg;
         const int cblocks = (a.Cin_pad + cblk - 1) / cblk;
         const dim3 grid(static_cast<unsigned>(int64_t(a.rows) * cblocks));
-        const size_t lds = size_t(cblk) * cp * 2;
+        const size_t lds = (size_t(cblk) * cp + 64 * 8) * 2;   // runs + per-lane spill slots
         if (cg == 8)
             hipLaunchKernelGGL(pack_cl_staged_kernel<8>, grid, dim3(256), lds, s, x, out, a.Cin, a.H,
                                a.W, a.KH, a.stride, a.pad, a.Ho, a.Wwin, a.Cin_pad, a.row_elems,

@@ -67,6 +67,8 @@ PACK_CASES = [
     (1, 1, 2, 3, 1, 1, 1, 0),        # fewer than 8 input elements
     (1, 12, 3, 1100, 3, 3, 1, 1),    # long input rows: 8-channel blocks to fit LDS
     (1, 5, 3, 2400, 7, 3, 1, 3),     # rows too long to stage in LDS: tiled form
+    (1, 3, 4, 4, 3, 3, 1, 5),        # padding wider than the filter: window rows all padding
+    (2, 16, 3, 5, 2, 2, 3, 4),       # stride 3, pad 4: rows and columns all padding
 ]
 
 
