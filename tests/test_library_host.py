@@ -142,13 +142,22 @@ def test_pointer_checks_before_launch():
     assert _lib.pack(d, 0, None, 16, 0, 1, None) == 2
 
 
+def _compiled_mfma_tiles():
+    """The (MB, NB, KB, KS, WM) tiles the tiled matrix-core kernel is instantiated for,
+    read from its dispatch list."""
+    import re
+    with open(os.path.join(ROOT, "cnn_convolution_amd", "csrc", "kernels", "gemm_mfma.hip")) as f:
+        src = f.read()
+    return {tuple(int(v) for v in m.groups())
+            for m in re.finditer(r"^\s*IM2WIN_TILE\((\d+), (\d+), (\d+), (\d+), (\d+)\)",
+                                 src, re.M)}
+
+
 def test_planned_tiles_are_compiled():
-    """Every tile the planner can pick is one the matrix-core kernel is built for."""
+    """Every tile the planner can pick is one the matrix-core kernels are built for."""
     import numpy as np
-    compiled = {(m, n, kb, ks, 2) for m in (64, 128) for n in (64, 128)
-                for kb, ks in ((64, 1), (32, 1), (32, 2))}
-    compiled |= {(64, 128, 64, 1, 1), (64, 256, 64, 1, 1), (64, 256, 32, 1, 1),
-                 (128, 256, 64, 1, 2), (128, 128, 64, 1, 1)}
+    compiled = _compiled_mfma_tiles()
+    assert len(compiled) >= 15
     rng = np.random.default_rng(0)
     for _ in range(400):
         KH, KW = int(rng.integers(1, 8)), int(rng.integers(1, 8))
@@ -161,7 +170,22 @@ def test_planned_tiles_are_compiled():
         t = (pl.gemm_tile_m, pl.gemm_tile_n, pl.gemm_kslice, pl.gemm_ksplit, pl.gemm_wave_m)
         assert pl.gemm_kernel in (1, 2)
         if pl.gemm_kernel == 2:
-            assert pl.gemm_tile_m in (32, 64) and pl.gemm_tile_n in (32, 64)
+            assert pl.gemm_tile_m == 64 and pl.gemm_tile_n in (64, 128, 256)
+            assert pl.gemm_kslice in (4, 8, 16)
             continue
         assert t in compiled, t
         assert pl.K_stage % (pl.gemm_kslice * pl.gemm_ksplit) == 0
+
+
+def test_tile_override_accepts_only_compiled_tiles(monkeypatch):
+    """IM2WIN_MFMA_TILE selects a compiled tile and is ignored for anything else."""
+    d = conv.make_desc(2, 64, 20, 20, 128, 3, 3, 1, 1, conv.F16)
+    for t in sorted(_compiled_mfma_tiles()):
+        monkeypatch.setenv("IM2WIN_MFMA_TILE", ",".join(str(v) for v in t))
+        pl = conv.plan(d)
+        got = (pl.gemm_tile_m, pl.gemm_tile_n, pl.gemm_kslice, pl.gemm_ksplit, pl.gemm_wave_m)
+        assert got == t
+    monkeypatch.setenv("IM2WIN_MFMA_TILE", "96,96,64,1,2")
+    pl = conv.plan(d)
+    got = (pl.gemm_tile_m, pl.gemm_tile_n, pl.gemm_kslice, pl.gemm_ksplit, pl.gemm_wave_m)
+    assert got in _compiled_mfma_tiles()
