@@ -188,10 +188,12 @@ conv2d_status_t conv2d_fwd(const conv2d_desc_t *d, const void *x, const void *w,
     const int es = int(elem_size(d->dtype));
     hipError_t e = hipSuccess;
 
-    // (a3) filter into the window's K order
+    // (a3) filter into the window's K order: carried by the first pack
+    // launch when its form allows, else a launch of its own before the
+    // first GEMM
     const void *wst = w;
+    StageArgs sa{};
     if (sg.needed) {
-        StageArgs sa{};
         sa.w = w;
         sa.out = wsb;
         sa.Cout = int(d->Cout);
@@ -202,9 +204,6 @@ conv2d_status_t conv2d_fwd(const conv2d_desc_t *d, const void *x, const void *w,
         sa.rows = int(sg.rows);
         sa.row_len = int(sg.row_len);
         sa.esize = es;
-        ProfScope ps(s, CONV2D_KERNEL_WEIGHT_STAGE);
-        e = p.layout == IM2WIN_LAYOUT_ROW ? launch_stage_row(sa, s) : launch_stage_cl(sa, s);
-        if (e != hipSuccess) return CONV2D_ERR_HIP;
         wst = wsb;
     }
     void *win = wsb + p.win_offset_bytes;
@@ -214,11 +213,19 @@ conv2d_status_t conv2d_fwd(const conv2d_desc_t *d, const void *x, const void *w,
         const int64_t rows = std::min<int64_t>(p.rows_per_chunk, p.rows_total - row0);
         // (a2) window rows of this chunk
         const PackArgs pa = pack_args(*d, p, p.layout, g, x, win, row0, rows);
+        const StageArgs *fold = (c == 0 && sg.needed) ? &sa : nullptr;
+        bool folded = false;
         {
             ProfScope ps(s, CONV2D_KERNEL_PACK);
-            e = p.layout == IM2WIN_LAYOUT_ROW ? launch_pack_row(pa, s) : launch_pack_cl(pa, s);
+            e = p.layout == IM2WIN_LAYOUT_ROW ? launch_pack_row(pa, s, fold, &folded)
+                                              : launch_pack_cl(pa, s, fold, &folded);
         }
         if (e != hipSuccess) return CONV2D_ERR_HIP;
+        if (fold && !folded) {
+            ProfScope ps(s, CONV2D_KERNEL_WEIGHT_STAGE);
+            e = p.layout == IM2WIN_LAYOUT_ROW ? launch_stage_row(sa, s) : launch_stage_cl(sa, s);
+            if (e != hipSuccess) return CONV2D_ERR_HIP;
+        }
         // (a4, a5) window-GEMM of the chunk, fp32 result written into y
         {
             ProfScope ps(s, CONV2D_KERNEL_GEMM);

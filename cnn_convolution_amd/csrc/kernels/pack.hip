@@ -13,6 +13,7 @@
 #include <cstdint>
 
 #include "../launch.hpp"
+#include "stage_body.hpp"
 
 namespace im2win {
 namespace {
@@ -31,12 +32,19 @@ constexpr int QU = 4;     // positions per lane per step
 template <typename E, int KHT>
 __global__ __launch_bounds__(256) void pack_row_kernel(
     const E *__restrict__ x, E *__restrict__ out, int Cin, int H, int W, int KH_rt, int stride,
-    int pad, int Ho, int Wwin, int pos_pad, int row_elems, int row0, int rows, int cgroups)
+    int pad, int Ho, int Wwin, int pos_pad, int row_elems, int row0, int rows, int cgroups,
+    StageFold fs)
 {
+    if (int(blockIdx.x) < fs.blocks) {            // filter staging carried by this launch
+        stage_row_elems(static_cast<const E *>(fs.w), static_cast<E *>(fs.out), fs.Cout,
+                        fs.Cin * fs.KH * fs.KW, fs.rows, blockIdx.x * 256u + threadIdx.x,
+                        unsigned(fs.blocks) * 256u);
+        return;
+    }
     const int KH = KHT > 0 ? KHT : KH_rt;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
-    const int task = blockIdx.x * 4 + wave;
+    const int task = (int(blockIdx.x) - fs.blocks) * 4 + wave;
     if (task >= rows * cgroups) return;            // no barriers in this kernel
     const int rl = task / cgroups;
     const int c0 = (task - rl * cgroups) * CPW;
@@ -217,14 +225,21 @@ template <int CG>
 __global__ __launch_bounds__(256) void pack_cl_staged_kernel(
     const uint16_t *__restrict__ x, uint16_t *__restrict__ out, int Cin, int H, int W, int KH,
     int stride, int pad, int Ho, int Wwin, int Cin_pad, int row_elems, int row0, int cblocks,
-    int cblk, int cp, int nck, int x_elems, int x_chunks)
+    int cblk, int cp, int nck, int x_elems, int x_chunks, StageFold fs)
 {
     extern __shared__ __attribute__((aligned(16))) uint16_t run[];   // [cblk][cp]
+    if (int(blockIdx.x) < fs.blocks) {            // filter staging carried by this launch
+        stage_cl_elems(static_cast<const uint16_t *>(fs.w), static_cast<uint16_t *>(fs.out), fs.Cout,
+                       fs.Cin, fs.KH, fs.KW, fs.Cin_pad, fs.row_len,
+                       blockIdx.x * 256u + threadIdx.x, unsigned(fs.blocks) * 256u);
+        return;
+    }
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int tid = threadIdx.x;
-    const int cbk = blockIdx.x % cblocks;
-    const int rl = blockIdx.x / cblocks;
+    const int bid = int(blockIdx.x) - fs.blocks;
+    const int cbk = bid % cblocks;
+    const int rl = bid / cblocks;
     const int r = row0 + rl;
     const int n = r / Ho;
     const int ho = r - n * Ho;
@@ -360,18 +375,38 @@ __global__ __launch_bounds__(256) void pack_cl_staged_kernel(
 
 }  // namespace
 
+// staging workgroups a pack launch carries: about 4 filter elements per
+// thread
+static StageFold make_fold(const StageArgs *f, int64_t elems)
+{
+    StageFold fs{};
+    if (!f) return fs;
+    fs.w = f->w;
+    fs.out = f->out;
+    fs.Cout = f->Cout;
+    fs.Cin = f->Cin;
+    fs.KH = f->KH;
+    fs.KW = f->KW;
+    fs.Cin_pad = f->Cin_pad;
+    fs.rows = f->rows;
+    fs.row_len = f->row_len;
+    const int64_t b = (elems + 1023) / 1024;
+    fs.blocks = int(b < 2048 ? (b > 0 ? b : 1) : 2048);
+    return fs;
+}
+
 template <typename E>
-hipError_t launch_pack_row_t(const PackArgs &a, hipStream_t s)
+hipError_t launch_pack_row_t(const PackArgs &a, hipStream_t s, const StageFold &fs)
 {
     const int cgroups = (a.Cin + CPW - 1) / CPW;
     const int64_t tasks = int64_t(a.rows) * cgroups;
-    const dim3 grid(static_cast<unsigned>((tasks + 3) / 4));
+    const dim3 grid(static_cast<unsigned>((tasks + 3) / 4 + fs.blocks));
     const E *x = static_cast<const E *>(a.x);
     E *out = static_cast<E *>(a.out);
 #define IM2WIN_PACK_ROW(K)                                                                       \
     hipLaunchKernelGGL((pack_row_kernel<E, K>), grid, dim3(256), 0, s, x, out, a.Cin, a.H, a.W,   \
                        a.KH, a.stride, a.pad, a.Ho, a.Wwin, a.pos_pad, a.row_elems, a.row0,       \
-                       a.rows, cgroups)
+                       a.rows, cgroups, fs)
     switch (a.KH) {
     case 1: IM2WIN_PACK_ROW(1); break;
     case 3: IM2WIN_PACK_ROW(3); break;
@@ -383,16 +418,19 @@ hipError_t launch_pack_row_t(const PackArgs &a, hipStream_t s)
     return hipGetLastError();
 }
 
-hipError_t launch_pack_row(const PackArgs &a, hipStream_t s)
+hipError_t launch_pack_row(const PackArgs &a, hipStream_t s, const StageArgs *fold, bool *folded)
 {
-    return a.esize == 4 ? launch_pack_row_t<uint32_t>(a, s) : launch_pack_row_t<uint16_t>(a, s);
+    const StageFold fs = make_fold(fold, fold ? int64_t(fold->rows) * fold->Cin * fold->KH * fold->KW : 0);
+    if (folded) *folded = fold != nullptr;
+    return a.esize == 4 ? launch_pack_row_t<uint32_t>(a, s, fs) : launch_pack_row_t<uint16_t>(a, s, fs);
 }
 
 // LDS budget of the row-staged channels-last pack (per workgroup)
 constexpr int kStagedLdsBytes = 63 * 1024;   // plus 1 KB of spill slots: within 64 KB
 
-hipError_t launch_pack_cl(const PackArgs &a, hipStream_t s)
+hipError_t launch_pack_cl(const PackArgs &a, hipStream_t s, const StageArgs *fold, bool *folded)
 {
+    if (folded) *folded = false;
     if (a.esize != 2) return hipErrorInvalidValue;
     const auto *x = static_cast<const uint16_t *>(a.x);
     auto *out = static_cast<uint16_t *>(a.out);
@@ -410,16 +448,18 @@ hipError_t launch_pack_cl(const PackArgs &a, hipStream_t s)
         while (int64_t(a.rows) * ((a.Cin_pad + cblk - 1) / cblk) < 512 && cblk >= 128)
             cblk = (cblk / 2) / cg * cg;
         const int cblocks = (a.Cin_pad + cblk - 1) / cblk;
-        const dim3 grid(static_cast<unsigned>(int64_t(a.rows) * cblocks));
         const size_t lds = (size_t(cblk) * cp + 64 * 8) * 2;   // runs + per-lane spill slots
+        const StageFold fs = make_fold(fold, fold ? int64_t(fold->rows) * fold->row_len : 0);
+        if (folded) *folded = fold != nullptr;
+        const dim3 grid2(static_cast<unsigned>(int64_t(a.rows) * cblocks + fs.blocks));
         if (cg == 8)
-            hipLaunchKernelGGL(pack_cl_staged_kernel<8>, grid, dim3(256), lds, s, x, out, a.Cin, a.H,
-                               a.W, a.KH, a.stride, a.pad, a.Ho, a.Wwin, a.Cin_pad, a.row_elems,
-                               a.row0, cblocks, cblk, cp, nck, x_elems, x_elems >> 3);
+            hipLaunchKernelGGL(pack_cl_staged_kernel<8>, grid2, dim3(256), lds, s, x, out, a.Cin,
+                               a.H, a.W, a.KH, a.stride, a.pad, a.Ho, a.Wwin, a.Cin_pad,
+                               a.row_elems, a.row0, cblocks, cblk, cp, nck, x_elems, x_elems >> 3, fs);
         else
-            hipLaunchKernelGGL(pack_cl_staged_kernel<4>, grid, dim3(256), lds, s, x, out, a.Cin, a.H,
-                               a.W, a.KH, a.stride, a.pad, a.Ho, a.Wwin, a.Cin_pad, a.row_elems,
-                               a.row0, cblocks, cblk, cp, nck, x_elems, x_elems >> 3);
+            hipLaunchKernelGGL(pack_cl_staged_kernel<4>, grid2, dim3(256), lds, s, x, out, a.Cin,
+                               a.H, a.W, a.KH, a.stride, a.pad, a.Ho, a.Wwin, a.Cin_pad,
+                               a.row_elems, a.row0, cblocks, cblk, cp, nck, x_elems, x_elems >> 3, fs);
         return hipGetLastError();
     }
     // very wide rows: tiled form (64 columns x 4 filter rows x 64 channels per pass)

@@ -10,12 +10,14 @@
 //       out[co][(kw*KH + kh)*Cin_pad + ci] = w[co][ci][kh][kw]
 //     matching the contiguous window run (kw outer, kh, channels inner).
 // Cells with no filter value (padded channels, rows, K tail) are zero.
-// Pure copies of raw bits.
+// Pure copies of raw bits (element bodies in stage_body.hpp; the forward
+// call usually runs them inside the first pack launch instead).
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
 
 #include "../launch.hpp"
+#include "stage_body.hpp"
 
 namespace im2win {
 namespace {
@@ -24,17 +26,8 @@ template <typename E>
 __global__ __launch_bounds__(256) void stage_row_kernel(const E *__restrict__ w, E *__restrict__ out,
                                                         int Cout, int K, int rows)
 {
-    // out index = (cb*K + k)*16 + j ; co = cb*16 + j ; w index = co*K + k
-    const int64_t total = int64_t(rows) * K;
-    for (int64_t e = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; e < total;
-         e += int64_t(gridDim.x) * blockDim.x) {
-        const int j = int(e & 15);
-        const int64_t t = e >> 4;
-        const int k = int(t % K);
-        const int cb = int(t / K);
-        const int co = cb * 16 + j;
-        out[e] = co < Cout ? w[int64_t(co) * K + k] : E(0);
-    }
+    stage_row_elems(w, out, Cout, K, rows, blockIdx.x * blockDim.x + threadIdx.x,
+                    gridDim.x * blockDim.x);
 }
 
 template <typename E>
@@ -42,22 +35,8 @@ __global__ __launch_bounds__(256) void stage_cl_kernel(const E *__restrict__ w, 
                                                        int Cout, int Cin, int KH, int KW,
                                                        int Cin_pad, int row_len)
 {
-    const int krun = KW * KH * Cin_pad;
-    const int64_t total = int64_t(Cout) * row_len;
-    for (int64_t e = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; e < total;
-         e += int64_t(gridDim.x) * blockDim.x) {
-        const int k = int(e % row_len);
-        const int co = int(e / row_len);
-        E v = E(0);
-        if (k < krun) {
-            const int ci = k % Cin_pad;
-            const int pos = k / Cin_pad;
-            const int kh = pos % KH;
-            const int kw = pos / KH;
-            if (ci < Cin) v = w[((int64_t(co) * Cin + ci) * KH + kh) * KW + kw];
-        }
-        out[e] = v;
-    }
+    stage_cl_elems(w, out, Cout, Cin, KH, KW, Cin_pad, row_len,
+                   blockIdx.x * blockDim.x + threadIdx.x, gridDim.x * blockDim.x);
 }
 
 unsigned grid_for(int64_t total)

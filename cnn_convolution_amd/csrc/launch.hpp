@@ -19,8 +19,14 @@ struct PackArgs {
     int row0, rows;         // window rows r in [row0, row0 + rows)
     int esize;              // 2 or 4 bytes
 };
-hipError_t launch_pack_row(const PackArgs &a, hipStream_t s);
-hipError_t launch_pack_cl(const PackArgs &a, hipStream_t s);
+struct StageArgs;
+// A pack launch can carry the filter staging along, as extra workgroups
+// ahead of the pack's own: pass `fold`; *folded tells whether it was taken
+// (the tiled channels-last form, for rows too long to stage, does not).
+hipError_t launch_pack_row(const PackArgs &a, hipStream_t s, const StageArgs *fold = nullptr,
+                           bool *folded = nullptr);
+hipError_t launch_pack_cl(const PackArgs &a, hipStream_t s, const StageArgs *fold = nullptr,
+                          bool *folded = nullptr);
 
 struct StageArgs {
     const void *w;          // [Cout][Cin][KH][KW]

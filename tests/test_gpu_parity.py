@@ -168,6 +168,7 @@ FIXED = [
     (2, 3, 5, 4, 6, 5, 4, 1, 0),       # dense-as-conv: 1x1 output
     (1, 4, 6, 6, 5, 3, 3, 4, 0),       # stride larger than the filter
     (1, 3, 4, 4, 2, 3, 3, 1, 5),       # padding wider than the filter: zero border
+    (1, 5, 3, 2400, 8, 7, 3, 1, 3),    # input rows too long to stage: tiled pack, own staging launch
 ]
 
 
@@ -294,7 +295,8 @@ def test_profile_hook_counts_launches():
     prof = conv.profile_read()
     assert prof["pack"]["launches"] == 2 * pl.n_chunks
     assert prof["gemm"]["launches"] == 2 * pl.n_chunks
-    assert prof["weight_stage"]["launches"] == 2
+    # the filter staging rides in the first pack launch of each call
+    assert prof["weight_stage"]["launches"] == 0
     assert all(v["total_ms"] >= 0 for v in prof.values())
 
 
