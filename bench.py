@@ -42,6 +42,49 @@ def _say(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+# sources that decide what the dominant (window-GEMM) kernel does, per path
+GEMM_SOURCES = {
+    "mfma": ["cnn_convolution_amd/csrc/kernels/gemm_mfma.hip",
+             "cnn_convolution_amd/csrc/kernels/tile_map.hpp",
+             "cnn_convolution_amd/csrc/launch.hpp"],
+    "valu": ["cnn_convolution_amd/csrc/kernels/gemm_valu.hip",
+             "cnn_convolution_amd/csrc/launch.hpp"],
+}
+COPY_BYTES = 256 << 20     # calibration copy for the HBM byte counters
+
+
+def gemm_source_sha(path_kind):
+    import hashlib
+    h = hashlib.sha256()
+    for rel in GEMM_SOURCES[path_kind]:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def gemm_tile_key(plan):
+    return (f"k{plan.gemm_kernel}:{plan.gemm_tile_m}x{plan.gemm_tile_n}/{plan.gemm_kslice}"
+            f"/{plan.gemm_ksplit}/{plan.gemm_wave_m}")
+
+
+def recorded_traffic(name, dt, plan, rows):
+    """HBM bytes per launch of the window-GEMM from the committed counter summary
+    (profiles/<layer>_<dtype>_gemm_counters.md), or None when there is none or the
+    kernel sources, tile or launch size differ from what the counters measured."""
+    path = os.path.join(ROOT, "profiles", f"{name}_{dt}_gemm_counters.md")
+    if not os.path.exists(path):
+        return None
+    kind = "valu" if dt == "f32" else "mfma"
+    want = {"sha": gemm_source_sha(kind), "tile": gemm_tile_key(plan), "rows": str(rows)}
+    with open(path) as f:
+        for line in f:
+            if line.startswith("traffic-record:"):
+                rec = dict(kv.split("=", 1) for kv in line.split()[1:])
+                if all(rec.get(k) == v for k, v in want.items()):
+                    return float(rec["bytes_per_launch"])
+    return None
+
+
 def algorithmic_bytes(cfg, dt, plan):
     """Per-kernel algorithmic HBM bytes of one call (each tensor moved once).
 
@@ -153,8 +196,11 @@ def time_variant(cfg, dt, steps, warmup, dev):
         roof = {"bound": "mfma" if dt != "f32" else "alu",
                 "achieved": gemm_flops / gemm_s / 1e12, "peak": peak, "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    # HBM bytes per launch from FETCH_SIZE + WRITE_SIZE counters scaled by a copy
+    # of known size (committed summary); null once the kernel has changed
+    roof["traffic"] = recorded_traffic(cfg.name, dt, plan, rows)
     roof["kernel"] = "gemm_mfma" if dt != "f32" else "gemm_valu_f32"
+    roof["tile"] = gemm_tile_key(plan)
     roof["alg_bytes_per_launch"] = gemm_bytes
     roof["flops_per_launch"] = gemm_flops
     roof["avg_launch_us"] = gemm_us
@@ -194,6 +240,42 @@ def cpu_baseline(cfg, dt, min_seconds=10.0):
                       f"fp64 direct sum, {dt} inputs"}
 
 
+def probe(args, dev):
+    """Kernel launches for the counter passes, nothing else timed or printed on stdout."""
+    import torch
+
+    import cnn_convolution_amd as conv
+    import workloads
+    if args.probe == "copy":
+        a = torch.ones(COPY_BYTES, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(args.steps):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        _say(f"probe copy: {args.steps} copies of {COPY_BYTES} bytes")
+        return
+    cfg = workloads.get_config(args.config)
+    dt = args.dtype or next((d for d in cfg.dtypes if d != "f32"), cfg.dtypes[0])
+    x, w = workloads.make_config_inputs(cfg, dt)
+    xd, wd = x.to(dev), w.to(dev)
+    d = conv.describe(tuple(x.shape), tuple(w.shape), cfg.stride, cfg.pad,
+                      {"f32": conv.F32, "f16": conv.F16, "bf16": conv.BF16}[dt])
+    plan = conv.plan(d)
+    y = torch.empty((cfg.N, cfg.Cout, plan.Ho, plan.Wo), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(plan.ws_bytes, 1), dtype=torch.uint8, device=dev)
+    conv.conv2d_into(xd, wd, y, ws if plan.ws_bytes else None, cfg.stride, cfg.pad)
+    row0 = (plan.n_chunks - 1) * plan.rows_per_chunk
+    rows = plan.rows_total - row0
+    es = 4 if dt == "f32" else 2
+    win = ws[plan.win_offset_bytes:plan.win_offset_bytes + rows * plan.row_elems * es]
+    wst = ws if plan.wstage_bytes else wd
+    for _ in range(args.steps):
+        conv.window_gemm(win, wst, y, d, row0, rows)
+    torch.cuda.synchronize()
+    _say(f"probe gemm: {cfg.name} {dt} rows={rows} tile={gemm_tile_key(plan)} "
+         f"sha={gemm_source_sha('valu' if dt == 'f32' else 'mfma')} launches={args.steps}")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -206,6 +288,9 @@ def main():
     ap.add_argument("--single", action="store_true", help="time the headline dtype only")
     ap.add_argument("--all-configs", action="store_true",
                     help="one JSON line per layer and dtype (profiling / results table)")
+    ap.add_argument("--probe", choices=["gemm", "copy"], default=None,
+                    help="for hardware counters: launch only the dominant kernel of the "
+                         "layer (last chunk, --steps times) or a device copy of a known size")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -223,6 +308,9 @@ def main():
         _say("bench.py: no GPU visible")
         sys.exit(1)
     dev = torch.device("cuda:0")
+    if args.probe:
+        probe(args, dev)
+        return
     names = sorted(workloads.CONFIGS) if args.all_configs else [args.config]
     for name in names:
         cfg = workloads.get_config(name)
