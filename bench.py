@@ -130,6 +130,17 @@ def time_variant(cfg, dt, steps, warmup, dev):
     wall = time.perf_counter() - t0
     ms = e0.elapsed_time(e1) / steps
 
+    # each call on its own between two events: median and best call
+    per_call = []
+    for _ in range(steps):
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record()
+        conv.conv2d_into(xd, wd, y, wsarg, cfg.stride, cfg.pad)
+        c1.record()
+        per_call.append((c0, c1))
+    torch.cuda.synchronize()
+    call_ms = sorted(a.elapsed_time(b) for a, b in per_call)
+
     # second timed pass: HIP events around every kernel launch (same stream);
     # the event pairs add a few microseconds to each short kernel, so this pass
     # gives the split between kernels, not the roofline figure
@@ -148,6 +159,10 @@ def time_variant(cfg, dt, steps, warmup, dev):
     row0 = (plan.n_chunks - 1) * plan.rows_per_chunk
     rows = plan.rows_total - row0
     es = 4 if dt == "f32" else 2
+    # the back-to-back launches below read (GEMM) and rewrite (pack) the window
+    # chunk inside ws: check on the host that it is all there
+    if plan.ws_bytes < plan.win_offset_bytes + rows * plan.row_elems * es:
+        raise RuntimeError(f"{cfg.name} {dt}: workspace holds no whole window chunk")
     win = ws[plan.win_offset_bytes:plan.win_offset_bytes + rows * plan.row_elems * es]
     wst = ws if plan.wstage_bytes else wd
     torch.cuda.synchronize()
@@ -158,6 +173,16 @@ def time_variant(cfg, dt, steps, warmup, dev):
     g1.record()
     torch.cuda.synchronize()
     gemm_us = g0.elapsed_time(g1) / steps * 1e3
+    # the pack of the same chunk, back to back as well (rewrites the same rows)
+    from cnn_convolution_amd import _lib
+    sptr = torch.cuda.current_stream().cuda_stream
+    p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    p0.record()
+    for _ in range(steps):
+        _lib.pack(d, plan.layout, xd.data_ptr(), win.data_ptr(), row0, rows, sptr)
+    p1.record()
+    torch.cuda.synchronize()
+    pack_us = p0.elapsed_time(p1) / steps * 1e3
     conv.conv2d_into(xd, wd, y, wsarg, cfg.stride, cfg.pad)   # y whole again for the parity check
     torch.cuda.synchronize()
 
@@ -208,6 +233,8 @@ def time_variant(cfg, dt, steps, warmup, dev):
     roof["tflops_in_kernel"] = gemm_flops / gemm_s / 1e12
     return {
         "dtype": dt, "value": tflops, "ms_per_step": ms, "wall_s": wall,
+        "ms_per_call_median": call_ms[len(call_ms) // 2], "ms_per_call_best": call_ms[0],
+        "chunk_pack_us": pack_us, "chunk_gemm_us": gemm_us, "chunk_rows": rows,
         "pct_of_peak": 100.0 * tflops / peak, "peak_tflops": peak,
         "rel_l2_sampled": rel, "parity_ok": rel <= TOL[dt],
         "ws_bytes": plan.ws_bytes, "im2col_bytes": plan.im2col_bytes,
@@ -267,6 +294,8 @@ def probe(args, dev):
     row0 = (plan.n_chunks - 1) * plan.rows_per_chunk
     rows = plan.rows_total - row0
     es = 4 if dt == "f32" else 2
+    if plan.ws_bytes < plan.win_offset_bytes + rows * plan.row_elems * es:
+        raise RuntimeError(f"{cfg.name} {dt}: workspace holds no whole window chunk")
     win = ws[plan.win_offset_bytes:plan.win_offset_bytes + rows * plan.row_elems * es]
     wst = ws if plan.wstage_bytes else wd
     for _ in range(args.steps):
@@ -285,6 +314,8 @@ def main():
     ap.add_argument("--dtype", default=None, help="headline dtype (default: the layer's "
                     "half-precision variant if it has one)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-baseline-all", action="store_true",
+                    help="with --all-configs: time the oracle on every layer, not only the first")
     ap.add_argument("--single", action="store_true", help="time the headline dtype only")
     ap.add_argument("--all-configs", action="store_true",
                     help="one JSON line per layer and dtype (profiling / results table)")
@@ -338,9 +369,12 @@ def main():
             "ws_bytes": h["ws_bytes"], "im2col_bytes": h["im2col_bytes"],
             "ws_over_im2col": h["ws_over_im2col"], "ws_target": h["ws_target"],
             "rel_l2_sampled": h["rel_l2_sampled"], "parity_ok": h["parity_ok"],
+            "ms_per_call_median": h["ms_per_call_median"], "ms_per_call_best": h["ms_per_call_best"],
+            "chunk_pack_us": h["chunk_pack_us"], "chunk_gemm_us": h["chunk_gemm_us"],
+            "chunk_rows": h["chunk_rows"], "n_chunks": h["n_chunks"],
             "variants": [{k: v for k, v in results[d].items()} for d in order[1:]],
         }
-        if not args.no_cpu_baseline and name == names[0]:
+        if not args.no_cpu_baseline and (name == names[0] or args.cpu_baseline_all):
             _say("bench: cpu baseline (oracle)")
             line["cpu_baseline"] = cpu_baseline(cfg, head)
         print(json.dumps(line), flush=True)
