@@ -193,6 +193,7 @@ MFMA_FORMS = [
     {"IM2WIN_MFMA_KERNEL": "resident", "IM2WIN_MFMA_RESIDENT_N": "64", "IM2WIN_MFMA_RESIDENT_PF": "4"},
     {"IM2WIN_MFMA_KERNEL": "resident", "IM2WIN_MFMA_RESIDENT_N": "128"},
     {"IM2WIN_MFMA_KERNEL": "resident", "IM2WIN_MFMA_RESIDENT_N": "256", "IM2WIN_MFMA_RESIDENT_PF": "16"},
+    {"IM2WIN_MFMA_KERNEL": "tiled", "IM2WIN_MFMA_TILE": "128,64,32,2,2"},
 ]
 FORM_SHAPES = [
     (2, 64, 17, 19, 70, 3, 3, 1, 1),    # Cout past one 64-row block, ragged columns
@@ -204,7 +205,7 @@ FORM_SHAPES = [
 ]
 
 
-@pytest.mark.parametrize("form", MFMA_FORMS, ids=lambda f: "-".join(f.values()))
+@pytest.mark.parametrize("form", MFMA_FORMS, ids=lambda f: "-".join(f.values()).replace(",", "."))
 @pytest.mark.parametrize("dt", ["f16", "bf16"])
 @pytest.mark.parametrize("shape", FORM_SHAPES)
 def test_mfma_forms_match_oracle(shape, dt, form, monkeypatch):
@@ -213,7 +214,13 @@ def test_mfma_forms_match_oracle(shape, dt, form, monkeypatch):
     N, Cin, H, W, Cout, KH, KW, s, p = shape
     d = conv.describe((N, Cin, H, W), (Cout, Cin, KH, KW), s, p, CODE[dt])
     want = 2 if form["IM2WIN_MFMA_KERNEL"] == "resident" else 1
-    assert conv.plan(d).gemm_kernel == want
+    pl = conv.plan(d)
+    assert pl.gemm_kernel == want
+    if "IM2WIN_MFMA_TILE" in form:          # applies when K_stage is a multiple of its K stage
+        tile = tuple(int(v) for v in form["IM2WIN_MFMA_TILE"].split(","))
+        if pl.K_stage % (tile[2] * tile[3]) == 0:
+            assert (pl.gemm_tile_m, pl.gemm_tile_n, pl.gemm_kslice, pl.gemm_ksplit,
+                    pl.gemm_wave_m) == tile
     _say(f"conv-form {form} {dt} {shape}")
     x, w = workloads.make_inputs(N, Cin, H, W, Cout, KH, KW, seed=sum(shape) + 7, dtype=dt,
                                  w_dist="normal")
