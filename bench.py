@@ -102,13 +102,33 @@ def algorithmic_bytes(cfg, dt, plan):
             "weight_stage": 2 * w if plan.wstage_bytes else 0}
 
 
+_INPUTS = {}
+
+
+def layer_inputs(cfg, dt):
+    """Seeded inputs of a layer in dtype dt. The half-precision tensors are the
+    float32 draws rounded once to nearest-even, so one draw serves every dtype
+    (the same bits the generator gives for each dtype on its own)."""
+    import torch
+
+    import workloads
+    if cfg.name not in _INPUTS:
+        _INPUTS.clear()
+        _INPUTS[cfg.name] = workloads.make_config_inputs(cfg, "f32")
+    x32, w32 = _INPUTS[cfg.name]
+    if dt == "f32":
+        return x32, w32
+    t = workloads.TORCH_DTYPES[dt]
+    return x32.to(t).contiguous(), w32.to(t).contiguous()
+
+
 def time_variant(cfg, dt, steps, warmup, dev):
     import torch
 
     import cnn_convolution_amd as conv
     import workloads
 
-    x, w = workloads.make_config_inputs(cfg, dt)
+    x, w = layer_inputs(cfg, dt)
     xd, wd = x.to(dev), w.to(dev)
     d = conv.describe(tuple(x.shape), tuple(w.shape), cfg.stride, cfg.pad,
                       {"f32": conv.F32, "f16": conv.F16, "bf16": conv.BF16}[dt])
@@ -249,7 +269,7 @@ def cpu_baseline(cfg, dt, min_seconds=10.0):
     import oracle
     import workloads
     threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or min(16, os.cpu_count() or 1)
-    x, w = workloads.make_config_inputs(cfg, dt)
+    x, w = layer_inputs(cfg, dt)
     per_img = 2 * cfg.Cout * cfg.out_hw()[0] * cfg.out_hw()[1] * cfg.Cin * cfg.KH * cfg.KW
     # size the sample from a one-image probe
     t = time.perf_counter()
@@ -319,6 +339,9 @@ def main():
     ap.add_argument("--single", action="store_true", help="time the headline dtype only")
     ap.add_argument("--all-configs", action="store_true",
                     help="one JSON line per layer and dtype (profiling / results table)")
+    ap.add_argument("--table1", action="store_true",
+                    help="one JSON line per layer of the im2win paper's Table I (N=256, "
+                         "no padding), fp16 headline with the fp32 variant")
     ap.add_argument("--probe", choices=["gemm", "copy"], default=None,
                     help="for hardware counters: launch only the dominant kernel of the "
                          "layer (last chunk, --steps times) or a device copy of a known size")
@@ -342,7 +365,8 @@ def main():
     if args.probe:
         probe(args, dev)
         return
-    names = sorted(workloads.CONFIGS) if args.all_configs else [args.config]
+    names = (list(workloads.TABLE1) if args.table1 else
+             sorted(workloads.CONFIGS) if args.all_configs else [args.config])
     for name in names:
         cfg = workloads.get_config(name)
         dts = list(cfg.dtypes)

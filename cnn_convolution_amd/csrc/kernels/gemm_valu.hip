@@ -288,6 +288,7 @@ hipError_t launch_gemm_valu_f32(const ValuGemmArgs &a, hipStream_t s)
     if (a.KH == 7 && a.KW == 7 && a.stride == 2) return launch_spec<7, 7, 2, 2>(a, s);
     if (a.KH == 5 && a.KW == 5 && a.stride == 1) return launch_spec<5, 5, 1, 4>(a, s);
     if (a.KH == 1 && a.KW == 1 && a.stride == 1) return launch_spec<1, 1, 1, 4>(a, s);
+    if (a.KH == 11 && a.KW == 11 && a.stride == 4) return launch_spec<11, 11, 4, 1>(a, s);
     return launch_generic(a, s);
 }
 

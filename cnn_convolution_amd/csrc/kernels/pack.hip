@@ -11,6 +11,8 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <cstdlib>
+#include <cstring>
 
 #include "../launch.hpp"
 #include "stage_body.hpp"
@@ -442,7 +444,16 @@ hipError_t launch_pack_cl(const PackArgs &a, hipStream_t s, const StageArgs *fol
     if ((cp / 2) % 2 == 0) cp += 2;
     int cblk = (kStagedLdsBytes / (2 * cp)) / cg * cg;
     const int x_elems = a.N * a.Cin * a.H * a.W;
-    if (cblk >= cg && x_elems >= 8) {
+    // A block must hold the channels of at least one whole 128-byte line per
+    // position (64 channels, or all of them): narrower blocks leave every
+    // line of the row to be written piecewise by several workgroups, which
+    // the tiled form avoids. IM2WIN_PACK_FORM=staged|tiled overrides (sweeps).
+    bool staged = cblk >= (a.Cin_pad < 64 ? a.Cin_pad : 64);
+    if (const char *e = std::getenv("IM2WIN_PACK_FORM")) {
+        if (std::strcmp(e, "staged") == 0) staged = true;
+        if (std::strcmp(e, "tiled") == 0) staged = false;
+    }
+    if (staged && cblk >= cg && x_elems >= 8) {
         cblk = cblk < a.Cin_pad ? cblk : a.Cin_pad;
         // keep at least ~2 workgroups per CU: split channels when rows are few
         while (int64_t(a.rows) * ((a.Cin_pad + cblk - 1) / cblk) < 512 && cblk >= 128)

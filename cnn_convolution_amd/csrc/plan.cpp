@@ -34,9 +34,11 @@ LayoutGeom layout_geom(const conv2d_desc_t &d, int32_t layout) {
     LayoutGeom g{};
     if (layout == IM2WIN_LAYOUT_ROW) {
         // each channel's run of W_win*KH positions, padded to 8 elements so
-        // every channel (and every row) starts 16-byte aligned
+        // every channel (and every row) starts 16-byte aligned, with at least
+        // 3 spare elements: the fp32 kernel loads a lane's window run in whole
+        // 16-byte vectors, and the last one may reach 3 elements past it
         g.Cin_pad = d.Cin;
-        g.pos_pad = round_up(Wwin * d.KH, 8);
+        g.pos_pad = round_up(Wwin * d.KH + 3, 8);
         g.row_elems = d.Cin * g.pos_pad;
     } else {
         // channels innermost, padded so that every window start
@@ -166,7 +168,9 @@ static void pick_mfma_resident(const conv2d_desc_t &d, int64_t cols, conv2d_plan
 }
 
 int valu_cols_per_lane(const conv2d_desc_t &d) {
-    return (d.KH == 7 && d.KW == 7 && d.stride == 2) ? 2 : 4;
+    if (d.KH == 7 && d.KW == 7 && d.stride == 2) return 2;
+    if (d.KH == 11 && d.KW == 11 && d.stride == 4) return 1;
+    return 4;
 }
 
 // Channel split across the 4 waves of a vector-ALU workgroup: used when the

@@ -98,7 +98,8 @@ typedef struct {
     int32_t path;                 /* 0: fp32 vector ALU, 1: fp16/bf16 matrix core  */
     int32_t layout;               /* an im2win_layout_t                           */
     int64_t Cin_pad;              /* channels stored per position (CL) or Cin     */
-    int64_t pos_pad;              /* ROW: positions stored per channel (>= W_win*KH) */
+    int64_t pos_pad;              /* ROW: positions stored per channel: a multiple of 8,
+                                     at least W_win*KH + 3 (spare, zero)          */
     int64_t row_elems;            /* elements of one window row in the workspace  */
     int64_t rows_total;           /* N*Ho                                         */
     int64_t rows_per_chunk;       /* window rows packed and contracted per chunk  */

@@ -353,6 +353,47 @@ def test_full_size_layers_sampled(name, dt):
     assert err <= TOL[dt], f"{name} {dt}: rel L2 {err:.3e} > {TOL[dt]}"
 
 
+# ----------------------------------------------------------------- Table I layers of the im2win paper
+
+@pytest.mark.parametrize("dt", ["f16", "f32"])
+@pytest.mark.parametrize("name", list(workloads.TABLE1))
+def test_table1_layers_small_batch(name, dt):
+    """Every Table I layer (its shape, stride and no padding) at N=2, element by
+    element against the oracle."""
+    cfg = workloads.TABLE1[name]
+    _say(f"table1 {name} {dt} N=2")
+    x, w = workloads.make_inputs(2, cfg.Cin, cfg.H, cfg.W, cfg.Cout, cfg.KH, cfg.KW,
+                                 seed=cfg.seed, dtype=dt, x_dist=cfg.x_dist, w_dist=cfg.w_dist)
+    y = run_conv(x, w, cfg.stride, cfg.pad)
+    ref = oracle.conv2d(x, w, cfg.stride, cfg.pad)
+    assert tuple(y.shape) == ref.shape
+    err = rel_l2(y.numpy(), ref)
+    assert err <= TOL[dt], f"{name} {dt}: rel L2 {err:.3e} > {TOL[dt]}"
+
+
+@pytest.mark.parametrize("name,dt", [("cv4", "f16"), ("cv1", "f32")])
+def test_table1_full_batch_sampled(name, dt):
+    """Table I layers at the paper's batch (N=256): a multi-GB window tensor in
+    several chunks (cv4), and stride 4 with an 11x11 filter in five chunks
+    (cv1); sampled outputs, chunk boundaries included, against the oracle."""
+    cfg = workloads.TABLE1[name]
+    _say(f"table1 full batch {name} {dt} {cfg.desc()}")
+    x, w = workloads.make_config_inputs(cfg, dt)
+    d = conv.describe(tuple(x.shape), tuple(w.shape), cfg.stride, cfg.pad, CODE[dt])
+    pl = conv.plan(d)
+    assert pl.meets_ws_target == 1 and pl.n_chunks >= 3
+    y = run_conv(x, w, cfg.stride, cfg.pad)
+    ho, wo = cfg.out_hw()
+    assert tuple(y.shape) == (cfg.N, cfg.Cout, ho, wo)
+    yf = y.numpy().reshape(-1)
+    rng = np.random.default_rng(cfg.seed)
+    idx = _sample_indices(cfg.N, cfg.Cout, ho, wo, pl.rows_per_chunk, rng)
+    assert np.isfinite(yf[idx]).all()
+    ref = oracle.conv2d_points(x, w, cfg.stride, cfg.pad, idx)
+    err = rel_l2(yf[idx], ref)
+    assert err <= TOL[dt], f"{name} {dt}: rel L2 {err:.3e} > {TOL[dt]}"
+
+
 # ----------------------------------------------------------------- window-GEMM alone (a4, a5)
 
 def _host_window_rows(x, d, pl, row0, rows):

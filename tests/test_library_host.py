@@ -189,3 +189,20 @@ def test_tile_override_accepts_only_compiled_tiles(monkeypatch):
     pl = conv.plan(d)
     got = (pl.gemm_tile_m, pl.gemm_tile_n, pl.gemm_kslice, pl.gemm_ksplit, pl.gemm_wave_m)
     assert got in _compiled_mfma_tiles()
+
+
+def test_row_layout_keeps_slack_after_every_run():
+    """The fp32 GEMM reads a lane's window run in whole 16-byte vectors (up to 3
+    elements past it), so every channel run of the row-interleaved layout keeps at
+    least 3 spare elements and the last read of a chunk stays inside it."""
+    import numpy as np
+    rng = np.random.default_rng(7)
+    for _ in range(300):
+        KH, KW = int(rng.integers(1, 12)), int(rng.integers(1, 12))
+        s, p = int(rng.integers(1, 5)), int(rng.integers(0, 4))
+        H, W = int(rng.integers(KH, 90)), int(rng.integers(KW, 90))
+        d = conv.make_desc(int(rng.integers(1, 5)), int(rng.integers(1, 70)), H, W, 16, KH, KW,
+                           s, p, conv.F32)
+        pl = conv.plan(d)
+        assert pl.pos_pad % 8 == 0 and pl.pos_pad >= pl.W_win * KH + 3
+        assert pl.row_elems == d.Cin * pl.pos_pad

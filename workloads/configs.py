@@ -78,5 +78,32 @@ CONFIGS: Dict[str, LayerConfig] = {c.name: c for c in [
 ]}
 
 
+# The twelve layers of Table I of "Enabling Memory-efficient Im2win Convolution
+# with Multi-precision Support on GPU CUDA and Tensor Cores" (Sec. IV-B), at the
+# batch the paper measures them with (N = 256) and with no padding, as printed.
+# Each runs in fp32 (vector ALU) and fp16 (matrix cores); inputs N(0,1), filters
+# He-initialised, one seed per layer.
+_TABLE1_SHAPES = [
+    # name, Cin, Hi, Wi, Cout, KH, KW, stride
+    ("cv1", 3, 227, 227, 96, 11, 11, 4),
+    ("cv2", 3, 231, 231, 96, 11, 11, 4),
+    ("cv3", 3, 227, 227, 64, 7, 7, 2),
+    ("cv4", 64, 224, 224, 64, 7, 7, 2),
+    ("cv5", 96, 24, 24, 256, 5, 5, 1),
+    ("cv6", 256, 12, 12, 512, 3, 3, 1),
+    ("cv7", 3, 224, 224, 64, 3, 3, 1),
+    ("cv8", 64, 112, 112, 128, 3, 3, 1),
+    ("cv9", 64, 56, 56, 64, 3, 3, 1),
+    ("cv10", 128, 28, 28, 128, 3, 3, 1),
+    ("cv11", 256, 14, 14, 256, 3, 3, 1),
+    ("cv12", 512, 7, 7, 512, 3, 3, 1),
+]
+TABLE1: Dict[str, LayerConfig] = {
+    name: LayerConfig(name, 256, ci, h, w, co, kh, kw, s, 0, ("f16", "f32"), 100 + i,
+                      "normal", "he", "Table I layer of the im2win paper, N=256, no padding")
+    for i, (name, ci, h, w, co, kh, kw, s) in enumerate(_TABLE1_SHAPES, start=1)
+}
+
+
 def get_config(name: str) -> LayerConfig:
-    return CONFIGS[name]
+    return CONFIGS[name] if name in CONFIGS else TABLE1[name]
