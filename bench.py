@@ -42,21 +42,27 @@ def _say(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-# sources that decide what the dominant (window-GEMM) kernel does, per path
+# sources that decide what the dominant (window-GEMM) kernel does, per GEMM
+# kernel of the plan (0: fp32 vector ALU, 1: tiled matrix core, 2: filter-resident
+# matrix core, 3: direct-to-LDS matrix core)
 GEMM_SOURCES = {
-    "mfma": ["cnn_convolution_amd/csrc/kernels/gemm_mfma.hip",
-             "cnn_convolution_amd/csrc/kernels/tile_map.hpp",
-             "cnn_convolution_amd/csrc/launch.hpp"],
-    "valu": ["cnn_convolution_amd/csrc/kernels/gemm_valu.hip",
-             "cnn_convolution_amd/csrc/launch.hpp"],
+    0: ["cnn_convolution_amd/csrc/kernels/gemm_valu.hip"],
+    1: ["cnn_convolution_amd/csrc/kernels/gemm_mfma.hip",
+        "cnn_convolution_amd/csrc/kernels/tile_map.hpp"],
+    2: ["cnn_convolution_amd/csrc/kernels/gemm_mfma_resident.hip",
+        "cnn_convolution_amd/csrc/kernels/tile_map.hpp"],
+    3: ["cnn_convolution_amd/csrc/kernels/gemm_mfma_dma.hip",
+        "cnn_convolution_amd/csrc/kernels/tile_map.hpp"],
 }
+GEMM_KERNEL_NAMES = {0: "gemm_valu_f32", 1: "gemm_mfma", 2: "gemm_mfma_resident",
+                     3: "gemm_mfma_dma"}
 COPY_BYTES = 256 << 20     # calibration copy for the HBM byte counters
 
 
-def gemm_source_sha(path_kind):
+def gemm_source_sha(kernel):
     import hashlib
     h = hashlib.sha256()
-    for rel in GEMM_SOURCES[path_kind]:
+    for rel in GEMM_SOURCES[kernel] + ["cnn_convolution_amd/csrc/launch.hpp"]:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -74,8 +80,8 @@ def recorded_traffic(name, dt, plan, rows):
     path = os.path.join(ROOT, "profiles", f"{name}_{dt}_gemm_counters.md")
     if not os.path.exists(path):
         return None
-    kind = "valu" if dt == "f32" else "mfma"
-    want = {"sha": gemm_source_sha(kind), "tile": gemm_tile_key(plan), "rows": str(rows)}
+    want = {"sha": gemm_source_sha(plan.gemm_kernel), "tile": gemm_tile_key(plan),
+            "rows": str(rows)}
     with open(path) as f:
         for line in f:
             if line.startswith("traffic-record:"):
@@ -244,7 +250,7 @@ def time_variant(cfg, dt, steps, warmup, dev):
     # HBM bytes per launch from FETCH_SIZE + WRITE_SIZE counters scaled by a copy
     # of known size (committed summary); null once the kernel has changed
     roof["traffic"] = recorded_traffic(cfg.name, dt, plan, rows)
-    roof["kernel"] = "gemm_mfma" if dt != "f32" else "gemm_valu_f32"
+    roof["kernel"] = GEMM_KERNEL_NAMES[plan.gemm_kernel]
     roof["tile"] = gemm_tile_key(plan)
     roof["alg_bytes_per_launch"] = gemm_bytes
     roof["flops_per_launch"] = gemm_flops
@@ -322,7 +328,8 @@ def probe(args, dev):
         conv.window_gemm(win, wst, y, d, row0, rows)
     torch.cuda.synchronize()
     _say(f"probe gemm: {cfg.name} {dt} rows={rows} tile={gemm_tile_key(plan)} "
-         f"sha={gemm_source_sha('valu' if dt == 'f32' else 'mfma')} launches={args.steps}")
+         f"kernel={GEMM_KERNEL_NAMES[plan.gemm_kernel]} sha={gemm_source_sha(plan.gemm_kernel)} "
+         f"launches={args.steps}")
 
 
 def main():

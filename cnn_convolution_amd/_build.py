@@ -29,6 +29,7 @@ SOURCES = [
     os.path.join(CSRC, "kernels", "gemm_valu.hip"),
     os.path.join(CSRC, "kernels", "gemm_mfma.hip"),
     os.path.join(CSRC, "kernels", "gemm_mfma_resident.hip"),
+    os.path.join(CSRC, "kernels", "gemm_mfma_dma.hip"),
 ]
 
 ARCH = "gfx950"

@@ -1,0 +1,266 @@
+// fp16 / bf16 window-GEMM on the CDNA4 matrix cores, direct-to-LDS form.
+//
+// Same contraction as gemm_mfma.hip (M = Cout, N = window columns n = (r, wo),
+// K = KW*KH*Cin_pad; the window of column n is one contiguous run of K
+// elements of the channels-last window tensor at base(n) = r*row_elems +
+// wo*stride*KH*Cin_pad; "Enabling Memory-efficient Im2win Convolution ...",
+// Sec. III-C Eq. (3), Sec. III-D), for windows whose length is a multiple of
+// the 64-element K stage (no K tail to mask).
+//
+// The filter and window tiles of a K stage go from memory straight into LDS
+// with global_load_lds_dwordx4 (gfx950): a wave instruction fills one 1 KB
+// block, lane l writing bytes [16l, 16l+16). A block holds 8 rows of 128 bytes
+// (64 halves); lane l fetches granule g = (l & 7) ^ (l >> 3) of row l >> 3,
+// so granule g of a row r sits in slot g ^ (r & 7): the fragment reads of 8
+// consecutive rows hit 8 different 16-byte bank groups. There is no register
+// staging and no LDS store instruction. Three stage buffers: while stage k is
+// multiplied, stages k+1 and k+2 are in flight; each wave waits only for its
+// own oldest stage (s_waitcnt vmcnt) and the workgroup barrier then makes all
+// waves' copies visible. The barrier is the raw s_barrier, fenced for the
+// compiler only: a workgroup memory fence would make every wave wait for all
+// its copies in flight.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <type_traits>
+
+#include "../launch.hpp"
+#include "tile_map.hpp"
+
+namespace im2win {
+namespace {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+template <bool BF16>
+__device__ __forceinline__ floatx4 mfma16(const uint4 &a, const uint4 &b, const floatx4 &c)
+{
+    if constexpr (BF16) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    } else {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, a),
+                                                      __builtin_bit_cast(half8, b), c, 0, 0, 0);
+    }
+}
+
+// s_waitcnt with only the vector-memory count constrained (gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void wait_vm()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Workgroup barrier between K stages: this wave's LDS reads are complete
+// (lgkmcnt(0)) before it signals, so no wave copies into a buffer another
+// wave may still be reading; the compiler may move no LDS access across it.
+__device__ __forceinline__ void stage_barrier()
+{
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));   // lgkmcnt(0) only
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// One wave copy of 16 bytes per lane from global memory into the LDS block at
+// byte address lds (wave-uniform): lane l lands at lds + 16*l. Written as
+// inline assembly so that the compiler adds no wait of its own before later
+// LDS reads (its alias tracking of these copies is conservative across the
+// stage loop and would drain every copy in flight); the waits of the stage
+// loop (wait_vm, stage_barrier) and the final wait_vm<0> order them instead.
+__device__ __forceinline__ void copy_to_lds(const void *src, uint32_t lds)
+{
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(src), "s"(lds)
+                 : "memory", "m0");
+}
+
+typedef const __attribute__((address_space(3))) uint16_t *lds_u16_ptr;
+
+__device__ __forceinline__ uint32_t lds_addr(const uint16_t *p)
+{
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_u16_ptr)p));   // LDS byte offset
+}
+
+constexpr int KI = 64;   // halves per stage row: 128 bytes, 8 granules of 16 bytes
+
+template <int MB, int NB, int WM, bool BF16>
+__global__ __launch_bounds__(256) void gemm_mfma_dma_kernel(
+    const uint16_t *__restrict__ win, const uint16_t *__restrict__ wst, float *__restrict__ y,
+    int rows, int row0, int row_elems, int col_step, int kstage, int Ho, int Wo, int Cout,
+    int tiles_m)
+{
+    constexpr int WN = 4 / WM;
+    constexpr int FM = MB / WM / 16;
+    constexpr int FN = NB / WN / 16;
+    constexpr int AI = MB / 32;            // 1 KB filter blocks per wave per stage
+    constexpr int BI = NB / 32;            // 1 KB window blocks per wave per stage
+    constexpr int D = AI + BI;             // copies per wave per stage
+    static_assert(AI >= 1 && BI >= 1 && AI * 32 == MB && BI * 32 == NB, "tiling");
+    static_assert(FM >= 1 && FN >= 1 && WM * WN == 4, "wave layout");
+    __shared__ __attribute__((aligned(16))) uint16_t sa0[MB * KI], sb0[NB * KI];
+    __shared__ __attribute__((aligned(16))) uint16_t sa1[MB * KI], sb1[NB * KI];
+    __shared__ __attribute__((aligned(16))) uint16_t sa2[MB * KI], sb2[NB * KI];
+
+    int tm, tn;
+    tile_coords(blockIdx.x, gridDim.x, tiles_m, tm, tn);
+    const int m0 = tm * MB;
+    const int n0 = tn * NB;
+    const int ncols = rows * Wo;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int wm = wave % WM;
+    const int wn = wave / WM;
+    const int nk = kstage / KI;
+
+    // copy sources: row (or column) blk*8 + (lane >> 3) of the tile, granule g.
+    // Filter rows past Cout read row Cout-1 and columns past the chunk read
+    // column 0: they only feed outputs the epilogue never stores.
+    const int rib = lane >> 3;
+    const int g8 = ((lane & 7) ^ rib) * 8;
+    const uint16_t *asrc[AI];
+#pragma unroll
+    for (int i = 0; i < AI; ++i) {
+        const int r = (wave + 4 * i) * 8 + rib;
+        asrc[i] = wst + int64_t(min(m0 + r, Cout - 1)) * kstage + g8;
+    }
+    const uint16_t *bsrc[BI];
+#pragma unroll
+    for (int i = 0; i < BI; ++i) {
+        const int n = n0 + (wave + 4 * i) * 8 + rib;
+        const bool ok = n < ncols;
+        const int rl = ok ? n / Wo : 0;
+        const int wo = ok ? n - rl * Wo : 0;
+        bsrc[i] = win + int64_t(rl) * row_elems + int64_t(wo) * col_step + g8;
+    }
+    auto issue = [&](int stage, uint16_t *sa, uint16_t *sb) {
+        const int k0 = stage * KI;
+#pragma unroll
+        for (int i = 0; i < AI; ++i)
+            copy_to_lds(asrc[i] + k0, __builtin_amdgcn_readfirstlane(lds_addr(sa + (wave + 4 * i) * 512)));
+#pragma unroll
+        for (int i = 0; i < BI; ++i)
+            copy_to_lds(bsrc[i] + k0, __builtin_amdgcn_readfirstlane(lds_addr(sb + (wave + 4 * i) * 512)));
+    };
+
+    floatx4 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    const int arow = wm * (MB / WM) + (lane & 15);
+    const int bcol = wn * (NB / WN) + (lane & 15);
+    auto compute = [&](const uint16_t *sa, const uint16_t *sb) {
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            const int gr = kk * 4 + (lane >> 4);        // granule of this lane's 8 K values
+            uint4 af[FM], bf[FN];
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                const int r = arow + i * 16;
+                af[i] = *reinterpret_cast<const uint4 *>(sa + r * KI + ((gr ^ (r & 7)) * 8));
+            }
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const int c = bcol + j * 16;
+                bf[j] = *reinterpret_cast<const uint4 *>(sb + c * KI + ((gr ^ (c & 7)) * 8));
+            }
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j) acc[i][j] = mfma16<BF16>(af[i], bf[j], acc[i][j]);
+        }
+    };
+
+    // three-buffer pipeline, unrolled by three so that every buffer is named
+    // statically (the compiler then tracks the copies into each one apart).
+    // Every step issues one stage group (the stage index clamped to the last
+    // one, so the final two steps re-copy it into buffers already read), so
+    // each wave always has exactly two groups in flight at the top of a step
+    // and waits for the older one: no data-dependent branch in the loop.
+    issue(0, sa0, sb0);
+    issue(min(1, nk - 1), sa1, sb1);
+    auto step = [&](int k, uint16_t *ca, uint16_t *cb, uint16_t *na, uint16_t *nb) {
+        wait_vm<D>();                      // own copies of stage k landed (k+1 may fly)
+        stage_barrier();                   // everyone's copies of stage k landed; stage k-1 read
+        issue(min(k + 2, nk - 1), na, nb); // into the buffer stage k-1 used
+        compute(ca, cb);
+        __builtin_amdgcn_sched_barrier(0); // keep each step's work inside its step
+    };
+    // the loop may leave after any step (uniform test): the accumulators then
+    // stay in the same registers from one step to the next
+    for (int k = 0;; k += 3) {
+        step(k, sa0, sb0, sa2, sb2);
+        if (k + 1 >= nk) break;
+        step(k + 1, sa1, sb1, sa0, sb0);
+        if (k + 2 >= nk) break;
+        step(k + 2, sa2, sb2, sa1, sb1);
+        if (k + 3 >= nk) break;
+    }
+    wait_vm<0>();                          // no copy may still be writing LDS at the end
+
+    // epilogue: lane holds D[4*(lane/16) + v][lane%16] of every 16x16 block
+    const int64_t plane = int64_t(Ho) * Wo;
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+        const int n = n0 + bcol + j * 16;
+        if (n >= ncols) continue;
+        const int rl = n / Wo;
+        const int wo = n - rl * Wo;
+        const int r = row0 + rl;
+        const int img = r / Ho;
+        const int ho = r - img * Ho;
+        float *yb = y + int64_t(img) * Cout * plane + int64_t(ho) * Wo + wo;
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int co = m0 + wm * (MB / WM) + i * 16 + (lane >> 4) * 4 + v;
+                if (co < Cout) yb[int64_t(co) * plane] = acc[i][j][v];
+            }
+        }
+    }
+}
+
+template <int MB, int NB, int WM>
+hipError_t launch_dma_tile(const MfmaGemmArgs &a, hipStream_t s)
+{
+    const int tiles_m = (a.Cout + MB - 1) / MB;
+    const int64_t ncols = int64_t(a.rows) * a.Wo;
+    const int64_t tiles_n = (ncols + NB - 1) / NB;
+    const dim3 grid(static_cast<unsigned>(tiles_m * tiles_n));
+    const auto *win = static_cast<const uint16_t *>(a.win);
+    const auto *wst = static_cast<const uint16_t *>(a.wst);
+    if (a.bf16)
+        hipLaunchKernelGGL((gemm_mfma_dma_kernel<MB, NB, WM, true>), grid, dim3(256), 0, s, win, wst,
+                           a.y, a.rows, a.row0, a.row_elems, a.col_step, a.kstage, a.Ho, a.Wo,
+                           a.Cout, tiles_m);
+    else
+        hipLaunchKernelGGL((gemm_mfma_dma_kernel<MB, NB, WM, false>), grid, dim3(256), 0, s, win,
+                           wst, a.y, a.rows, a.row0, a.row_elems, a.col_step, a.kstage, a.Ho, a.Wo,
+                           a.Cout, tiles_m);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemm_mfma_dma(const MfmaGemmArgs &a, hipStream_t s)
+{
+    // whole K stages only: the window length is the staged filter row length
+    if (a.krun != a.kstage || a.kstage % KI != 0 || a.col_step % 8 != 0 || a.row_elems % 8 != 0)
+        return hipErrorInvalidValue;
+    if (a.tile_m == 64 && a.tile_n == 128 && a.wm == 1) return launch_dma_tile<64, 128, 1>(a, s);
+    if (a.tile_m == 64 && a.tile_n == 64 && a.wm == 2) return launch_dma_tile<64, 64, 2>(a, s);
+    if (a.tile_m == 128 && a.tile_n == 64 && a.wm == 2) return launch_dma_tile<128, 64, 2>(a, s);
+    if (a.tile_m == 128 && a.tile_n == 128 && a.wm == 2) return launch_dma_tile<128, 128, 2>(a, s);
+    if (a.tile_m == 128 && a.tile_n == 128 && a.wm == 1) return launch_dma_tile<128, 128, 1>(a, s);
+    if (a.tile_m == 64 && a.tile_n == 256 && a.wm == 1) return launch_dma_tile<64, 256, 1>(a, s);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace im2win

@@ -68,5 +68,8 @@ hipError_t launch_gemm_mfma(const MfmaGemmArgs &a, hipStream_t s);
 // window fragments go straight to registers; tile_n = columns per workgroup
 // (64, 128 or 256), tile_m = 64
 hipError_t launch_gemm_mfma_resident(const MfmaGemmArgs &a, hipStream_t s);
+// direct-to-LDS form: tile_m x tile_n with wm waves along M, K stages of 64;
+// only for windows whose length krun equals kstage, a multiple of 64
+hipError_t launch_gemm_mfma_dma(const MfmaGemmArgs &a, hipStream_t s);
 
 }  // namespace im2win

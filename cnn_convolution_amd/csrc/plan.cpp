@@ -167,6 +167,50 @@ static void pick_mfma_resident(const conv2d_desc_t &d, int64_t cols, conv2d_plan
     p->gemm_wave_m = 1;
 }
 
+// Direct-to-LDS matrix-core form: whole 64-element K stages (the window
+// length equals the staged filter row, a multiple of 64). Taken wherever it
+// applies: it measured faster than the tiled kernel on the layers of the
+// sweep. Tile rule from the same sweep: one 64-row block when Cout <= 64 (128
+// columns, or 64 when that leaves fewer tiles than CUs); 64 x 64 for Cout >=
+// 256 with a deep K; else 128 x 64. IM2WIN_MFMA_KERNEL=tiled|resident turns
+// it off; IM2WIN_MFMA_DMA_TILE="MB,NB,WM" overrides the tile for sweeps.
+static const int kDmaTiles[][3] = {
+    {64, 128, 1}, {64, 64, 2}, {128, 64, 2}, {128, 128, 2}, {128, 128, 1}, {64, 256, 1},
+};
+
+static bool dma_tile_known(int m, int n, int wm) {
+    for (const auto &t : kDmaTiles)
+        if (t[0] == m && t[1] == n && t[2] == wm) return true;
+    return false;
+}
+
+static void pick_mfma_dma(const conv2d_desc_t &d, int64_t krun, int64_t cols, conv2d_plan_t *p) {
+    if (krun != p->K_stage || p->K_stage % 64 != 0) return;
+    if (const char *k = std::getenv("IM2WIN_MFMA_KERNEL"))
+        if (std::strcmp(k, "tiled") == 0 || std::strcmp(k, "resident") == 0) return;
+    int m, n, wm;
+    if (d.Cout <= 64) {
+        m = 64; wm = 1; n = 128;
+        if (ceil_div(cols, 128) < 256) { n = 64; wm = 2; }
+    } else if (d.Cout >= 256 && p->K_stage >= 256) {
+        m = 64; n = 64; wm = 2;
+    } else {
+        m = 128; n = 64; wm = 2;
+    }
+    if (const char *e = std::getenv("IM2WIN_MFMA_DMA_TILE")) {
+        int a = 0, b = 0, w = 0;
+        if (std::sscanf(e, "%d,%d,%d", &a, &b, &w) == 3 && dma_tile_known(a, b, w)) {
+            m = a; n = b; wm = w;
+        }
+    }
+    p->gemm_kernel = 3;
+    p->gemm_tile_m = m;
+    p->gemm_tile_n = n;
+    p->gemm_kslice = 64;
+    p->gemm_ksplit = 1;
+    p->gemm_wave_m = wm;
+}
+
 int valu_cols_per_lane(const conv2d_desc_t &d) {
     if (d.KH == 7 && d.KW == 7 && d.stride == 2) return 2;
     if (d.KH == 11 && d.KW == 11 && d.stride == 4) return 1;
@@ -232,6 +276,7 @@ conv2d_status_t make_plan(const conv2d_desc_t &d, conv2d_plan_t *p) {
         pick_mfma_tile(d, p->rows_per_chunk * p->Wo, mfma_kgran(d.KW * d.KH * g.Cin_pad), p);
         p->gemm_kernel = 1;
         pick_mfma_resident(d, p->rows_per_chunk * p->Wo, p);
+        pick_mfma_dma(d, d.KW * d.KH * g.Cin_pad, p->rows_per_chunk * p->Wo, p);
     } else {
         p->gemm_kernel = 0;
         p->gemm_tile_m = 4 * kValuMt;

@@ -120,7 +120,9 @@ typedef struct {
     int32_t gemm_ksplit;          /* wave groups splitting K inside a workgroup    */
     int32_t gemm_kernel;          /* 0: vector ALU, 1: matrix core via LDS tiles,
                                      2: matrix core, filter block resident in LDS and
-                                        window fragments straight to registers      */
+                                        window fragments straight to registers,
+                                     3: matrix core, tiles copied memory -> LDS
+                                        directly (whole 64-element K stages)         */
     int32_t gemm_wave_m;          /* waves along M in a wave group (matrix path)   */
     int32_t reserved1;
     int64_t flops;                /* 2*N*Cout*Ho*Wo*Cin*KH*KW (padded taps included) */

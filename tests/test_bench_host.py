@@ -48,14 +48,14 @@ def test_traffic_records_are_consistent(dt):
 
 def test_traffic_is_null_once_the_kernel_changes(monkeypatch):
     p, rows = _plan("resnet3x3", "f16")
-    monkeypatch.setattr(bench, "gemm_source_sha", lambda kind: "0" * 16)
+    monkeypatch.setattr(bench, "gemm_source_sha", lambda kernel: "0" * 16)
     assert bench.recorded_traffic("resnet3x3", "f16", p, rows) is None
 
 
 def test_traffic_is_null_for_another_launch_size_or_tile(monkeypatch):
     p, rows = _plan("resnet3x3", "f16")
     assert bench.recorded_traffic("resnet3x3", "f16", p, rows - 1) is None
-    monkeypatch.setenv("IM2WIN_MFMA_TILE", "64,64,32,1,2")
+    monkeypatch.setenv("IM2WIN_MFMA_DMA_TILE", "128,128,1")
     q, rows_q = _plan("resnet3x3", "f16")
     assert bench.recorded_traffic("resnet3x3", "f16", q, rows_q) is None
 

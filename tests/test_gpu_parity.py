@@ -230,6 +230,38 @@ def test_mfma_forms_match_oracle(shape, dt, form, monkeypatch):
     assert err <= TOL[dt], f"rel L2 {err:.3e} > {TOL[dt]}"
 
 
+# Direct-to-LDS form: windows of whole 64-element K stages. The K-stage counts
+# 1, 2, 4, 9 and 18 leave the three-buffer loop after each of its three steps.
+DMA_TILES = ["64,128,1", "64,64,2", "128,64,2", "128,128,2", "128,128,1", "64,256,1"]
+DMA_SHAPES = [
+    (2, 64, 17, 19, 70, 3, 3, 1, 1),    # 9 stages, Cout past one block, ragged columns
+    (1, 5, 13, 11, 9, 2, 4, 3, 2),      # 8 padded channels x 8 taps: 1 stage
+    (2, 128, 8, 9, 96, 1, 1, 1, 0),     # 1x1, filter used as staged: 2 stages
+    (1, 256, 6, 7, 136, 1, 1, 1, 0),    # 4 stages
+    (2, 128, 9, 10, 200, 3, 3, 1, 1),   # 18 stages
+    (3, 64, 11, 12, 64, 3, 3, 2, 0),    # stride 2
+]
+
+
+@pytest.mark.parametrize("tile", DMA_TILES)
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+@pytest.mark.parametrize("shape", DMA_SHAPES)
+def test_dma_form_matches_oracle(shape, dt, tile, monkeypatch):
+    monkeypatch.setenv("IM2WIN_MFMA_DMA_TILE", tile)
+    N, Cin, H, W, Cout, KH, KW, s, p = shape
+    d = conv.describe((N, Cin, H, W), (Cout, Cin, KH, KW), s, p, CODE[dt])
+    pl = conv.plan(d)
+    assert pl.gemm_kernel == 3
+    assert (pl.gemm_tile_m, pl.gemm_tile_n, pl.gemm_wave_m) == tuple(int(v) for v in tile.split(","))
+    _say(f"conv-dma {tile} {dt} {shape}")
+    x, w = workloads.make_inputs(N, Cin, H, W, Cout, KH, KW, seed=sum(shape) + 11, dtype=dt,
+                                 w_dist="normal")
+    y = run_conv(x, w, s, p)
+    ref = oracle.conv2d(x, w, s, p)
+    err = rel_l2(y.numpy(), ref)
+    assert err <= TOL[dt], f"rel L2 {err:.3e} > {TOL[dt]}"
+
+
 @pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
 @pytest.mark.parametrize("shape", [(2, 3, 32, 32, 16, 3, 3, 1, 1), (2, 32, 15, 14, 72, 3, 3, 2, 1),
                                    (1, 3, 30, 30, 64, 7, 7, 2, 3), (2, 64, 8, 8, 128, 1, 1, 1, 0),

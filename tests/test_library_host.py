@@ -168,7 +168,11 @@ def test_planned_tiles_are_compiled():
                            [conv.F16, conv.BF16][int(rng.integers(0, 2))])
         pl = conv.plan(d)
         t = (pl.gemm_tile_m, pl.gemm_tile_n, pl.gemm_kslice, pl.gemm_ksplit, pl.gemm_wave_m)
-        assert pl.gemm_kernel in (1, 2)
+        assert pl.gemm_kernel in (1, 2, 3)
+        if pl.gemm_kernel == 3:
+            assert (pl.gemm_tile_m, pl.gemm_tile_n, pl.gemm_wave_m) in _compiled_dma_tiles()
+            assert pl.K_stage % 64 == 0 and pl.gemm_kslice == 64 and pl.gemm_ksplit == 1
+            continue
         if pl.gemm_kernel == 2:
             assert pl.gemm_tile_m == 64 and pl.gemm_tile_n in (64, 128, 256)
             assert pl.gemm_kslice in (4, 8, 16)
@@ -180,6 +184,7 @@ def test_planned_tiles_are_compiled():
 def test_tile_override_accepts_only_compiled_tiles(monkeypatch):
     """IM2WIN_MFMA_TILE selects a compiled tile and is ignored for anything else."""
     d = conv.make_desc(2, 64, 20, 20, 128, 3, 3, 1, 1, conv.F16)
+    monkeypatch.setenv("IM2WIN_MFMA_KERNEL", "tiled")
     for t in sorted(_compiled_mfma_tiles()):
         monkeypatch.setenv("IM2WIN_MFMA_TILE", ",".join(str(v) for v in t))
         pl = conv.plan(d)
@@ -189,6 +194,51 @@ def test_tile_override_accepts_only_compiled_tiles(monkeypatch):
     pl = conv.plan(d)
     got = (pl.gemm_tile_m, pl.gemm_tile_n, pl.gemm_kslice, pl.gemm_ksplit, pl.gemm_wave_m)
     assert got in _compiled_mfma_tiles()
+
+
+def _compiled_dma_tiles():
+    path = os.path.join(ROOT, "cnn_convolution_amd", "csrc", "kernels", "gemm_mfma_dma.hip")
+    with open(path) as f:
+        src = f.read()
+    return {tuple(int(v) for v in m.groups())
+            for m in re.finditer(r"launch_dma_tile<(\d+), (\d+), (\d+)>\(a, s\)", src)}
+
+
+def test_dma_form_only_for_whole_k_stages(monkeypatch):
+    """The direct-to-LDS form is planned wherever the window is a whole number of
+    64-element K stages, and only there, with a tile it is built for."""
+    import numpy as np
+    compiled = _compiled_dma_tiles()
+    assert len(compiled) == 6
+    rng = np.random.default_rng(3)
+    seen = 0
+    for _ in range(300):
+        KH, KW = int(rng.integers(1, 6)), int(rng.integers(1, 6))
+        Cin = int(rng.choice([3, 5, 8, 16, 24, 64, 96, 128, 256]))
+        s, p = int(rng.integers(1, 3)), int(rng.integers(0, 3))
+        H, W = int(rng.integers(KH, 40)), int(rng.integers(KW, 40))
+        d = conv.make_desc(int(rng.integers(1, 9)), Cin, H, W, int(rng.integers(1, 300)),
+                           KH, KW, s, p, conv.F16)
+        monkeypatch.setenv("IM2WIN_MFMA_DMA_TILE", ",".join(map(str, sorted(compiled)[seen % 6])))
+        pl = conv.plan(d)
+        whole = pl.K_stage == KH * KW * pl.Cin_pad and pl.K_stage % 64 == 0
+        assert (pl.gemm_kernel == 3) == whole
+        if whole:
+            seen += 1
+            assert (pl.gemm_tile_m, pl.gemm_tile_n, pl.gemm_wave_m) in compiled
+            assert pl.gemm_kslice == 64 and pl.gemm_ksplit == 1
+    assert seen > 20
+    d = conv.make_desc(2, 64, 20, 20, 128, 3, 3, 1, 1, conv.F16)
+    monkeypatch.delenv("IM2WIN_MFMA_DMA_TILE")
+    default = conv.plan(d)
+    monkeypatch.setenv("IM2WIN_MFMA_DMA_TILE", "96,96,2")     # not built: the planned tile
+    pl = conv.plan(d)
+    assert pl.gemm_kernel == 3
+    assert (pl.gemm_tile_m, pl.gemm_tile_n, pl.gemm_wave_m) == \
+        (default.gemm_tile_m, default.gemm_tile_n, default.gemm_wave_m)
+    for form in ("tiled", "resident"):                          # the other forms, forced
+        monkeypatch.setenv("IM2WIN_MFMA_KERNEL", form)
+        assert conv.plan(d).gemm_kernel == (1 if form == "tiled" else 2)
 
 
 def test_row_layout_keeps_slack_after_every_run():
