@@ -3,9 +3,13 @@
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 20] [--config resnet3x3] [--dtype f16]
 
-A step is one conv2d_fwd call: filter staging, then for every chunk of window
-rows the im2win pack and the window-GEMM, writing the fp32 output. Inputs are
-seeded synthetic tensors already resident in device memory. The timed region
+A step is one conv2d_fwd call in the form the library plans for the layer:
+either the window tensor (filter staging, then for every chunk of window rows
+the im2win pack and the window-GEMM) or the implicit form (filter staging,
+then one kernel that builds the window rows in LDS and contracts them), each
+writing the fp32 output. Where a layer has both forms the other one is timed
+too and reported under "other_form". Inputs are seeded synthetic tensors
+already resident in device memory. The timed region
 is `steps` back-to-back calls on one stream, bracketed by device syncs and
 HIP events; warm-up calls run first and caches stay warm (50 timed calls
 after 20 warm-up ones, the protocol of the fused-WTConv measurements).
@@ -42,9 +46,10 @@ def _say(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-# sources that decide what the dominant (window-GEMM) kernel does, per GEMM
-# kernel of the plan (0: fp32 vector ALU, 1: tiled matrix core, 2: filter-resident
-# matrix core, 3: direct-to-LDS matrix core)
+# sources that decide what the dominant kernel of a call does, per kernel id
+# (0: fp32 vector-ALU window-GEMM, 1: tiled matrix-core window-GEMM,
+# 2: filter-resident matrix-core window-GEMM, 3: direct-to-LDS matrix-core
+# window-GEMM, 4: implicit convolution, window rows built in LDS)
 GEMM_SOURCES = {
     0: ["cnn_convolution_amd/csrc/kernels/gemm_valu.hip"],
     1: ["cnn_convolution_amd/csrc/kernels/gemm_mfma.hip",
@@ -52,10 +57,14 @@ GEMM_SOURCES = {
     2: ["cnn_convolution_amd/csrc/kernels/gemm_mfma_resident.hip",
         "cnn_convolution_amd/csrc/kernels/tile_map.hpp"],
     3: ["cnn_convolution_amd/csrc/kernels/gemm_mfma_dma.hip",
+        "cnn_convolution_amd/csrc/kernels/lds_dma.hpp",
+        "cnn_convolution_amd/csrc/kernels/tile_map.hpp"],
+    4: ["cnn_convolution_amd/csrc/kernels/conv_implicit.hip",
+        "cnn_convolution_amd/csrc/kernels/lds_dma.hpp",
         "cnn_convolution_amd/csrc/kernels/tile_map.hpp"],
 }
 GEMM_KERNEL_NAMES = {0: "gemm_valu_f32", 1: "gemm_mfma", 2: "gemm_mfma_resident",
-                     3: "gemm_mfma_dma"}
+                     3: "gemm_mfma_dma", 4: "conv_implicit"}
 COPY_BYTES = 256 << 20     # calibration copy for the HBM byte counters
 
 
@@ -68,19 +77,30 @@ def gemm_source_sha(kernel):
     return h.hexdigest()[:16]
 
 
-def gemm_tile_key(plan):
-    return (f"k{plan.gemm_kernel}:{plan.gemm_tile_m}x{plan.gemm_tile_n}/{plan.gemm_kslice}"
-            f"/{plan.gemm_ksplit}/{plan.gemm_wave_m}")
+def dominant_key(d, plan):
+    """(kernel id, tile key, rows per launch) of the dominant kernel of a call:
+    the implicit kernel (all N*Ho window rows in one launch) or the window-GEMM
+    (timed on the last chunk of window rows)."""
+    import cnn_convolution_amd as conv
+    if plan.algo == 1:
+        ip = conv.implicit_plan(d)
+        return (4, f"i:{ip.tile_m}x{ip.tile_n}/{ip.wave_m}/r{ip.rows_per_tile}/c{ip.cols_per_tile}",
+                plan.rows_total)
+    rows = plan.rows_total - (plan.n_chunks - 1) * plan.rows_per_chunk
+    return (plan.gemm_kernel, f"k{plan.gemm_kernel}:{plan.gemm_tile_m}x{plan.gemm_tile_n}/"
+            f"{plan.gemm_kslice}/{plan.gemm_ksplit}/{plan.gemm_wave_m}", rows)
 
 
-def recorded_traffic(name, dt, plan, rows):
-    """HBM bytes per launch of the window-GEMM from the committed counter summary
-    (profiles/<layer>_<dtype>_gemm_counters.md), or None when there is none or the
-    kernel sources, tile or launch size differ from what the counters measured."""
+def recorded_traffic(name, dt, d, plan):
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary (profiles/<layer>_<dtype>_gemm_counters.md), or None when there is
+    none or the kernel sources, tile or launch size differ from what the
+    counters measured."""
     path = os.path.join(ROOT, "profiles", f"{name}_{dt}_gemm_counters.md")
     if not os.path.exists(path):
         return None
-    want = {"sha": gemm_source_sha(plan.gemm_kernel), "tile": gemm_tile_key(plan),
+    kid, tile, rows = dominant_key(d, plan)
+    want = {"kernel": GEMM_KERNEL_NAMES[kid], "sha": gemm_source_sha(kid), "tile": tile,
             "rows": str(rows)}
     with open(path) as f:
         for line in f:
@@ -94,9 +114,10 @@ def recorded_traffic(name, dt, plan, rows):
 def algorithmic_bytes(cfg, dt, plan):
     """Per-kernel algorithmic HBM bytes of one call (each tensor moved once).
 
-    pack   : reads x, writes the window tensor (N*Ho rows of Cin*W_win*KH)
-    gemm   : reads the window tensor and the staged filter, writes y (fp32)
-    stage  : reads w, writes the staged filter
+    pack     : reads x, writes the window tensor (N*Ho rows of Cin*W_win*KH)
+    gemm     : reads the window tensor and the staged filter, writes y (fp32)
+    stage    : reads w, writes the staged filter
+    implicit : reads x and the staged filter, writes y (no window tensor)
     """
     es = 4 if dt == "f32" else 2
     ho, wo = plan.Ho, plan.Wo
@@ -104,8 +125,10 @@ def algorithmic_bytes(cfg, dt, plan):
     w = cfg.Cout * cfg.Cin * cfg.KH * cfg.KW * es
     win = cfg.N * ho * cfg.Cin * plan.W_win * cfg.KH * es
     y = cfg.N * cfg.Cout * ho * wo * 4
+    staged = not (cfg.KH == 1 and cfg.KW == 1)
     return {"pack": x + win, "gemm": win + w * plan.n_chunks + y,
-            "weight_stage": 2 * w if plan.wstage_bytes else 0}
+            "weight_stage": 2 * w if (plan.wstage_bytes if plan.algo == 0 else staged) else 0,
+            "implicit": x + w + y}
 
 
 _INPUTS = {}
@@ -128,11 +151,33 @@ def layer_inputs(cfg, dt):
     return x32.to(t).contiguous(), w32.to(t).contiguous()
 
 
-def time_variant(cfg, dt, steps, warmup, dev):
+def time_variant(cfg, dt, steps, warmup, dev, algo=None):
+    """Time conv2d_fwd on one layer and dtype, in the form the planner picks
+    (or the one `algo` forces: "window" or "implicit"), and its dominant kernel
+    alone; check the timed output against the oracle on sampled points."""
     import torch
 
     import cnn_convolution_amd as conv
-    import workloads
+
+    saved = os.environ.get("IM2WIN_ALGO")
+    if algo:
+        os.environ["IM2WIN_ALGO"] = algo
+    else:
+        os.environ.pop("IM2WIN_ALGO", None)
+    try:
+        return _time_variant(cfg, dt, steps, warmup, dev)
+    finally:
+        if saved is None:
+            os.environ.pop("IM2WIN_ALGO", None)
+        else:
+            os.environ["IM2WIN_ALGO"] = saved
+
+
+def _time_variant(cfg, dt, steps, warmup, dev):
+    import torch
+
+    import cnn_convolution_amd as conv
+    from cnn_convolution_amd import _lib
 
     x, w = layer_inputs(cfg, dt)
     xd, wd = x.to(dev), w.to(dev)
@@ -179,36 +224,55 @@ def time_variant(cfg, dt, steps, warmup, dev):
         conv.profile_enable(False)
     prof = conv.profile_read()
 
-    # dominant kernel alone: after a call the workspace holds the staged filter
-    # and the last chunk of window rows; launch the window-GEMM on them back to
-    # back between two events on the same stream
-    row0 = (plan.n_chunks - 1) * plan.rows_per_chunk
-    rows = plan.rows_total - row0
+    # dominant kernel alone, back to back between two events on the same
+    # stream: after a call the workspace holds the staged filter (and, for the
+    # window form, the last chunk of window rows)
     es = 4 if dt == "f32" else 2
-    # the back-to-back launches below read (GEMM) and rewrite (pack) the window
-    # chunk inside ws: check on the host that it is all there
-    if plan.ws_bytes < plan.win_offset_bytes + rows * plan.row_elems * es:
-        raise RuntimeError(f"{cfg.name} {dt}: workspace holds no whole window chunk")
-    win = ws[plan.win_offset_bytes:plan.win_offset_bytes + rows * plan.row_elems * es]
-    wst = ws if plan.wstage_bytes else wd
-    torch.cuda.synchronize()
-    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    g0.record()
-    for _ in range(steps):
-        conv.window_gemm(win, wst, y, d, row0, rows)
-    g1.record()
-    torch.cuda.synchronize()
-    gemm_us = g0.elapsed_time(g1) / steps * 1e3
-    # the pack of the same chunk, back to back as well (rewrites the same rows)
-    from cnn_convolution_amd import _lib
+    kid, tile, rows = dominant_key(d, plan)
     sptr = torch.cuda.current_stream().cuda_stream
-    p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    p0.record()
-    for _ in range(steps):
-        _lib.pack(d, plan.layout, xd.data_ptr(), win.data_ptr(), row0, rows, sptr)
-    p1.record()
-    torch.cuda.synchronize()
-    pack_us = p0.elapsed_time(p1) / steps * 1e3
+    pack_us = None
+    if plan.algo == 1:
+        ip = conv.implicit_plan(d)
+        wst = ws if ip.ws_bytes else wd
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record()
+        for _ in range(steps):
+            conv.implicit_gemm(xd, wst, y, d)
+        g1.record()
+        torch.cuda.synchronize()
+        kern_us = g0.elapsed_time(g1) / steps * 1e3
+        dom_flops = plan.flops
+        dom_bytes = algorithmic_bytes(cfg, dt, plan)["implicit"]
+        n_chunks = 1
+    else:
+        row0 = (plan.n_chunks - 1) * plan.rows_per_chunk
+        # the back-to-back launches below read (GEMM) and rewrite (pack) the
+        # window chunk inside ws: check on the host that it is all there
+        if plan.ws_bytes < plan.win_offset_bytes + rows * plan.row_elems * es:
+            raise RuntimeError(f"{cfg.name} {dt}: workspace holds no whole window chunk")
+        win = ws[plan.win_offset_bytes:plan.win_offset_bytes + rows * plan.row_elems * es]
+        wst = ws if plan.wstage_bytes else wd
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record()
+        for _ in range(steps):
+            conv.window_gemm(win, wst, y, d, row0, rows)
+        g1.record()
+        torch.cuda.synchronize()
+        kern_us = g0.elapsed_time(g1) / steps * 1e3
+        # the pack of the same chunk, back to back as well (rewrites the same rows)
+        p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        p0.record()
+        for _ in range(steps):
+            _lib.pack(d, plan.layout, xd.data_ptr(), win.data_ptr(), row0, rows, sptr)
+        p1.record()
+        torch.cuda.synchronize()
+        pack_us = p0.elapsed_time(p1) / steps * 1e3
+        dom_flops = 2 * rows * plan.Wo * cfg.Cout * cfg.Cin * cfg.KH * cfg.KW
+        dom_bytes = (rows * cfg.Cin * plan.W_win * cfg.KH * es
+                     + cfg.Cout * cfg.Cin * cfg.KH * cfg.KW * es + rows * plan.Wo * cfg.Cout * 4)
+        n_chunks = plan.n_chunks
     conv.conv2d_into(xd, wd, y, wsarg, cfg.stride, cfg.pad)   # y whole again for the parity check
     torch.cuda.synchronize()
 
@@ -224,48 +288,47 @@ def time_variant(cfg, dt, steps, warmup, dev):
     tflops = flops / (ms * 1e-3) / 1e12
     ab = algorithmic_bytes(cfg, dt, plan)
     kern = {}
-    for k in ("weight_stage", "pack", "gemm"):
+    for k in ("weight_stage", "pack", "gemm", "implicit"):
         n = prof[k]["launches"]
         if n:
             avg = prof[k]["total_ms"] / n
             kern[k] = {"launches_per_step": n / steps, "avg_launch_us": avg * 1e3,
                        "ms_per_step": prof[k]["total_ms"] / steps,
                        "alg_bytes_per_launch": ab[k] / (n / steps)}
-    # algorithmic work of that GEMM launch (each tensor moved once)
-    ho, wo = plan.Ho, plan.Wo
-    gemm_flops = 2 * rows * wo * cfg.Cout * cfg.Cin * cfg.KH * cfg.KW
-    gemm_bytes = (rows * cfg.Cin * plan.W_win * cfg.KH * es
-                  + cfg.Cout * cfg.Cin * cfg.KH * cfg.KW * es + rows * wo * cfg.Cout * 4)
-    gemm_s = gemm_us * 1e-6
-    ai = gemm_flops / gemm_bytes
+    # roofline of the dominant kernel: algorithmic work of one launch (each
+    # tensor moved once) over its back-to-back launch time
+    kern_s = kern_us * 1e-6
+    ai = dom_flops / dom_bytes
     peak = PEAK_TFLOPS[dt]
     ridge = peak * 1e12 / (HBM_GBPS * 1e9)
     if ai < ridge:
-        roof = {"bound": "hbm", "achieved": gemm_bytes / gemm_s / 1e9, "peak": HBM_GBPS,
+        roof = {"bound": "hbm", "achieved": dom_bytes / kern_s / 1e9, "peak": HBM_GBPS,
                 "unit": "GB/s"}
     else:
         roof = {"bound": "mfma" if dt != "f32" else "alu",
-                "achieved": gemm_flops / gemm_s / 1e12, "peak": peak, "unit": "TFLOP/s"}
+                "achieved": dom_flops / kern_s / 1e12, "peak": peak, "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     # HBM bytes per launch from FETCH_SIZE + WRITE_SIZE counters scaled by a copy
     # of known size (committed summary); null once the kernel has changed
-    roof["traffic"] = recorded_traffic(cfg.name, dt, plan, rows)
-    roof["kernel"] = GEMM_KERNEL_NAMES[plan.gemm_kernel]
-    roof["tile"] = gemm_tile_key(plan)
-    roof["alg_bytes_per_launch"] = gemm_bytes
-    roof["flops_per_launch"] = gemm_flops
-    roof["avg_launch_us"] = gemm_us
+    roof["traffic"] = recorded_traffic(cfg.name, dt, d, plan)
+    roof["kernel"] = GEMM_KERNEL_NAMES[kid]
+    roof["tile"] = tile
+    roof["alg_bytes_per_launch"] = dom_bytes
+    roof["flops_per_launch"] = dom_flops
+    roof["avg_launch_us"] = kern_us
     roof["rows_per_launch"] = rows
-    roof["tflops_in_kernel"] = gemm_flops / gemm_s / 1e12
+    roof["tflops_in_kernel"] = dom_flops / kern_s / 1e12
     return {
-        "dtype": dt, "value": tflops, "ms_per_step": ms, "wall_s": wall,
+        "dtype": dt, "form": "implicit" if plan.algo == 1 else "window",
+        "value": tflops, "ms_per_step": ms, "wall_s": wall,
         "ms_per_call_median": call_ms[len(call_ms) // 2], "ms_per_call_best": call_ms[0],
-        "chunk_pack_us": pack_us, "chunk_gemm_us": gemm_us, "chunk_rows": rows,
+        "chunk_pack_us": pack_us, "chunk_gemm_us": kern_us if plan.algo == 0 else None,
+        "kernel_us": kern_us, "chunk_rows": rows,
         "pct_of_peak": 100.0 * tflops / peak, "peak_tflops": peak,
         "rel_l2_sampled": rel, "parity_ok": rel <= TOL[dt],
         "ws_bytes": plan.ws_bytes, "im2col_bytes": plan.im2col_bytes,
         "ws_over_im2col": plan.ws_bytes / plan.im2col_bytes, "ws_target": 1.0 / cfg.KW,
-        "n_chunks": plan.n_chunks, "kernels": kern, "roofline": roof,
+        "n_chunks": n_chunks, "kernels": kern, "roofline": roof,
     }
 
 
@@ -293,6 +356,14 @@ def cpu_baseline(cfg, dt, min_seconds=10.0):
                       f"fp64 direct sum, {dt} inputs"}
 
 
+def implicit_applies(cfg, dt):
+    import cnn_convolution_amd as conv
+    from cnn_convolution_amd import _lib
+    d = conv.make_desc(cfg.N, cfg.Cin, cfg.H, cfg.W, cfg.Cout, cfg.KH, cfg.KW, cfg.stride,
+                       cfg.pad, {"f16": conv.F16, "bf16": conv.BF16}[dt])
+    return _lib.implicit_plan_status(d) == 0
+
+
 def probe(args, dev):
     """Kernel launches for the counter passes, nothing else timed or printed on stdout."""
     import torch
@@ -317,19 +388,24 @@ def probe(args, dev):
     y = torch.empty((cfg.N, cfg.Cout, plan.Ho, plan.Wo), dtype=torch.float32, device=dev)
     ws = torch.empty(max(plan.ws_bytes, 1), dtype=torch.uint8, device=dev)
     conv.conv2d_into(xd, wd, y, ws if plan.ws_bytes else None, cfg.stride, cfg.pad)
-    row0 = (plan.n_chunks - 1) * plan.rows_per_chunk
-    rows = plan.rows_total - row0
-    es = 4 if dt == "f32" else 2
-    if plan.ws_bytes < plan.win_offset_bytes + rows * plan.row_elems * es:
-        raise RuntimeError(f"{cfg.name} {dt}: workspace holds no whole window chunk")
-    win = ws[plan.win_offset_bytes:plan.win_offset_bytes + rows * plan.row_elems * es]
-    wst = ws if plan.wstage_bytes else wd
-    for _ in range(args.steps):
-        conv.window_gemm(win, wst, y, d, row0, rows)
+    kid, tile, rows = dominant_key(d, plan)
+    if plan.algo == 1:
+        ip = conv.implicit_plan(d)
+        wst = ws if ip.ws_bytes else wd
+        for _ in range(args.steps):
+            conv.implicit_gemm(xd, wst, y, d)
+    else:
+        row0 = (plan.n_chunks - 1) * plan.rows_per_chunk
+        es = 4 if dt == "f32" else 2
+        if plan.ws_bytes < plan.win_offset_bytes + rows * plan.row_elems * es:
+            raise RuntimeError(f"{cfg.name} {dt}: workspace holds no whole window chunk")
+        win = ws[plan.win_offset_bytes:plan.win_offset_bytes + rows * plan.row_elems * es]
+        wst = ws if plan.wstage_bytes else wd
+        for _ in range(args.steps):
+            conv.window_gemm(win, wst, y, d, row0, rows)
     torch.cuda.synchronize()
-    _say(f"probe gemm: {cfg.name} {dt} rows={rows} tile={gemm_tile_key(plan)} "
-         f"kernel={GEMM_KERNEL_NAMES[plan.gemm_kernel]} sha={gemm_source_sha(plan.gemm_kernel)} "
-         f"launches={args.steps}")
+    _say(f"probe gemm: {cfg.name} {dt} rows={rows} tile={tile} "
+         f"kernel={GEMM_KERNEL_NAMES[kid]} sha={gemm_source_sha(kid)} launches={args.steps}")
 
 
 def main():
@@ -385,6 +461,12 @@ def main():
             _say(f"bench: {name} {dt} warmup={args.warmup} steps={args.steps}")
             results[dt] = time_variant(cfg, dt, args.steps, args.warmup, dev)
         h = results[head]
+        # the other form of the headline dtype, where the layer has both
+        other = None
+        if head != "f32" and implicit_applies(cfg, head):
+            alt = "window" if h["form"] == "implicit" else "implicit"
+            _say(f"bench: {name} {head} other form ({alt})")
+            other = time_variant(cfg, head, args.steps, args.warmup, dev, algo=alt)
         line = {
             "metric": METRIC, "value": h["value"], "unit": "TFLOPS", "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": h["ms_per_step"],
@@ -401,9 +483,11 @@ def main():
             "ws_over_im2col": h["ws_over_im2col"], "ws_target": h["ws_target"],
             "rel_l2_sampled": h["rel_l2_sampled"], "parity_ok": h["parity_ok"],
             "ms_per_call_median": h["ms_per_call_median"], "ms_per_call_best": h["ms_per_call_best"],
+            "form": h["form"], "kernel_us": h["kernel_us"],
             "chunk_pack_us": h["chunk_pack_us"], "chunk_gemm_us": h["chunk_gemm_us"],
             "chunk_rows": h["chunk_rows"], "n_chunks": h["n_chunks"],
             "variants": [{k: v for k, v in results[d].items()} for d in order[1:]],
+            "other_form": other,
         }
         if not args.no_cpu_baseline and (name == names[0] or args.cpu_baseline_all):
             _say("bench: cpu baseline (oracle)")

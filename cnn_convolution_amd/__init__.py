@@ -10,11 +10,13 @@ runs in libim2win_conv2d.so (see include/im2win_conv2d.h).
 from __future__ import annotations
 
 from . import _lib
-from ._lib import (Conv2dError, Desc, Plan, LAYOUT_CL, LAYOUT_ROW, F16, F32, BF16,  # noqa: F401
-                   make_desc, workspace_size, plan, profile_enable, profile_read, status_string)
+from ._lib import (Conv2dError, Desc, Plan, ImplicitPlan, LAYOUT_CL, LAYOUT_ROW,  # noqa: F401
+                   F16, F32, BF16, make_desc, workspace_size, plan, implicit_plan,
+                   implicit_workspace_size, profile_enable, profile_read, status_string)
 
-__all__ = ["conv2d", "conv2d_into", "pack", "weight_stage", "window_gemm", "describe", "plan",
-           "workspace_size",
+__all__ = ["conv2d", "conv2d_into", "conv2d_implicit", "conv2d_implicit_into", "pack",
+           "weight_stage", "window_gemm", "describe", "plan", "implicit_plan", "workspace_size",
+           "implicit_workspace_size", "implicit_gemm",
            "Conv2dError", "profile_enable", "profile_read"]
 
 
@@ -67,6 +69,39 @@ def conv2d(x, w, stride: int = 1, pad: int = 0):
     ws = torch.empty(max(p.ws_bytes, 1), dtype=torch.uint8, device=x.device)
     conv2d_into(x, w, y, ws if p.ws_bytes else None, stride, pad)
     return y
+
+
+def conv2d_implicit_into(x, w, y, ws, stride=1, pad=0) -> None:
+    """Enqueue y = conv2d(x, w) by the implicit form (window rows built in LDS,
+    no window tensor) on the current stream, using caller buffers."""
+    d = describe(tuple(x.shape), tuple(w.shape), stride, pad, _dtype_code(x))
+    if w.dtype != x.dtype:
+        raise TypeError("x and w must share a dtype")
+    st = _lib.fwd_implicit(d, x.data_ptr(), w.data_ptr(), y.data_ptr(),
+                           ws.data_ptr() if ws is not None and ws.numel() else None, _stream())
+    if st != 0:
+        raise Conv2dError(st, "conv2d_fwd_implicit")
+
+
+def conv2d_implicit(x, w, stride: int = 1, pad: int = 0):
+    """y = conv2d(x, w) by the implicit form (fp16/bf16, Cin a multiple of 64)."""
+    import torch
+    _check(x, "x")
+    _check(w, "w")
+    d = describe(tuple(x.shape), tuple(w.shape), stride, pad, _dtype_code(x))
+    p = implicit_plan(d)
+    y = torch.empty((d.N, d.Cout, p.Ho, p.Wo), dtype=torch.float32, device=x.device)
+    ws = torch.empty(max(p.ws_bytes, 1), dtype=torch.uint8, device=x.device)
+    conv2d_implicit_into(x, w, y, ws if p.ws_bytes else None, stride, pad)
+    return y
+
+
+def implicit_gemm(x, wst, y, desc: Desc) -> None:
+    """Enqueue the implicit kernel alone: y from x and a filter already staged
+    in the channels-last K order (w itself for a 1x1 filter)."""
+    st = _lib.implicit_gemm(desc, x.data_ptr(), wst.data_ptr(), y.data_ptr(), _stream())
+    if st != 0:
+        raise Conv2dError(st, "im2win_implicit_gemm")
 
 
 def pack(x, KH: int, KW: int, stride: int, pad: int, layout: int, row0: int = 0, rows=None):

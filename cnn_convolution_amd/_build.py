@@ -30,6 +30,7 @@ SOURCES = [
     os.path.join(CSRC, "kernels", "gemm_mfma.hip"),
     os.path.join(CSRC, "kernels", "gemm_mfma_resident.hip"),
     os.path.join(CSRC, "kernels", "gemm_mfma_dma.hip"),
+    os.path.join(CSRC, "kernels", "conv_implicit.hip"),
 ]
 
 ARCH = "gfx950"

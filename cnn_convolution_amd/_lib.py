@@ -14,7 +14,7 @@ LIBPATH = os.path.join(PKG, "lib", "libim2win_conv2d.so")
 
 F32, F16, BF16 = 0, 1, 2
 LAYOUT_ROW, LAYOUT_CL = 0, 1
-KERNEL_WEIGHT_STAGE, KERNEL_PACK, KERNEL_GEMM, KERNEL_KINDS = 0, 1, 2, 3
+KERNEL_WEIGHT_STAGE, KERNEL_PACK, KERNEL_GEMM, KERNEL_IMPLICIT, KERNEL_KINDS = 0, 1, 2, 3, 4
 
 STATUS = {
     0: "CONV2D_OK", 1: "CONV2D_ERR_INVALID_DESC", 2: "CONV2D_ERR_NULL_POINTER",
@@ -26,6 +26,8 @@ STATUS = {
 EXPORTS = [
     "conv2d_workspace_size", "conv2d_plan", "conv2d_fwd", "im2win_pack", "im2win_weight_stage",
     "im2win_window_gemm", "conv2d_status_string", "conv2d_profile_enable", "conv2d_profile_read",
+    "conv2d_implicit_plan", "conv2d_implicit_workspace_size", "conv2d_fwd_implicit",
+    "im2win_implicit_gemm",
 ]
 
 
@@ -47,7 +49,7 @@ _PLAN_FIELDS = [
     ("meets_ws_target", ctypes.c_int32), ("gemm_tile_m", ctypes.c_int32),
     ("gemm_tile_n", ctypes.c_int32), ("gemm_kslice", ctypes.c_int32),
     ("gemm_ksplit", ctypes.c_int32), ("gemm_kernel", ctypes.c_int32),
-    ("gemm_wave_m", ctypes.c_int32), ("reserved1", ctypes.c_int32),
+    ("gemm_wave_m", ctypes.c_int32), ("algo", ctypes.c_int32),
     ("flops", ctypes.c_int64),
 ]
 
@@ -56,7 +58,24 @@ class Plan(ctypes.Structure):
     _fields_ = _PLAN_FIELDS
 
     def as_dict(self):
-        return {name: getattr(self, name) for name, _ in _PLAN_FIELDS if name != "reserved1"}
+        return {name: getattr(self, name) for name, _ in _PLAN_FIELDS}
+
+
+_IMPLICIT_PLAN_FIELDS = [
+    ("tile_m", ctypes.c_int32), ("tile_n", ctypes.c_int32), ("wave_m", ctypes.c_int32),
+    ("rows_per_tile", ctypes.c_int32), ("cols_per_tile", ctypes.c_int32),
+    ("patch_rows", ctypes.c_int32), ("patch_cols", ctypes.c_int32), ("reserved", ctypes.c_int32),
+    ("lds_bytes", ctypes.c_int64), ("tiles", ctypes.c_int64), ("Ho", ctypes.c_int64),
+    ("Wo", ctypes.c_int64), ("K_stage", ctypes.c_int64), ("ws_bytes", ctypes.c_int64),
+    ("flops", ctypes.c_int64),
+]
+
+
+class ImplicitPlan(ctypes.Structure):
+    _fields_ = _IMPLICIT_PLAN_FIELDS
+
+    def as_dict(self):
+        return {name: getattr(self, name) for name, _ in _IMPLICIT_PLAN_FIELDS if name != "reserved"}
 
 
 class Profile(ctypes.Structure):
@@ -97,6 +116,14 @@ def lib() -> ctypes.CDLL:
         L.im2win_window_gemm.argtypes = [dp, vp, vp, vp, i64, i64, vp]
         L.conv2d_status_string.restype = ctypes.c_char_p
         L.conv2d_status_string.argtypes = [ctypes.c_int]
+        L.conv2d_implicit_plan.restype = ctypes.c_int
+        L.conv2d_implicit_plan.argtypes = [dp, ctypes.POINTER(ImplicitPlan)]
+        L.conv2d_implicit_workspace_size.restype = ctypes.c_size_t
+        L.conv2d_implicit_workspace_size.argtypes = [dp]
+        L.conv2d_fwd_implicit.restype = ctypes.c_int
+        L.conv2d_fwd_implicit.argtypes = [dp, vp, vp, vp, vp, vp]
+        L.im2win_implicit_gemm.restype = ctypes.c_int
+        L.im2win_implicit_gemm.argtypes = [dp, vp, vp, vp, vp]
         L.conv2d_profile_enable.restype = ctypes.c_int
         L.conv2d_profile_enable.argtypes = [i32]
         L.conv2d_profile_read.restype = ctypes.c_int
@@ -125,6 +152,31 @@ def fwd(d: Desc, x: int, w: int, y: int, ws: int, stream: int) -> int:
     return lib().conv2d_fwd(ctypes.byref(d), x, w, y, ws, stream)
 
 
+def implicit_plan(d: Desc) -> ImplicitPlan:
+    p = ImplicitPlan()
+    st = lib().conv2d_implicit_plan(ctypes.byref(d), ctypes.byref(p))
+    if st != 0:
+        raise Conv2dError(st, "conv2d_implicit_plan")
+    return p
+
+
+def implicit_plan_status(d: Desc) -> int:
+    p = ImplicitPlan()
+    return int(lib().conv2d_implicit_plan(ctypes.byref(d), ctypes.byref(p)))
+
+
+def implicit_workspace_size(d: Desc) -> int:
+    return int(lib().conv2d_implicit_workspace_size(ctypes.byref(d)))
+
+
+def fwd_implicit(d: Desc, x: int, w: int, y: int, ws: int, stream: int) -> int:
+    return lib().conv2d_fwd_implicit(ctypes.byref(d), x, w, y, ws, stream)
+
+
+def implicit_gemm(d: Desc, x: int, wst: int, y: int, stream: int) -> int:
+    return lib().im2win_implicit_gemm(ctypes.byref(d), x, wst, y, stream)
+
+
 def pack(d: Desc, layout: int, x: int, out: int, row0: int, rows: int, stream: int) -> int:
     return lib().im2win_pack(ctypes.byref(d), layout, x, out, row0, rows, stream)
 
@@ -150,6 +202,6 @@ def profile_read() -> dict:
     st = lib().conv2d_profile_read(ctypes.byref(p))
     if st != 0:
         raise Conv2dError(st, "conv2d_profile_read")
-    names = ("weight_stage", "pack", "gemm")
+    names = ("weight_stage", "pack", "gemm", "implicit")
     return {names[k]: {"launches": int(p.launches[k]), "total_ms": float(p.total_ms[k])}
             for k in range(KERNEL_KINDS)}

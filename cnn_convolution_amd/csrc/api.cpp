@@ -137,6 +137,66 @@ hipError_t launch_gemm(const conv2d_desc_t &d, const conv2d_plan_t &p, const Lay
     return p.gemm_kernel == 2 ? launch_gemm_mfma_resident(ga, s) : launch_gemm_mfma(ga, s);
 }
 
+ImplicitArgs implicit_args(const conv2d_desc_t &d, const conv2d_implicit_plan_t &p, const void *x,
+                           const void *wst, float *y)
+{
+    ImplicitArgs a{};
+    a.x = x;
+    a.wst = wst;
+    a.y = y;
+    a.N = int(d.N);
+    a.Cin = int(d.Cin);
+    a.H = int(d.H);
+    a.W = int(d.W);
+    a.Cout = int(d.Cout);
+    a.KH = int(d.KH);
+    a.KW = int(d.KW);
+    a.stride = int(d.stride);
+    a.pad = int(d.pad);
+    a.Ho = int(p.Ho);
+    a.Wo = int(p.Wo);
+    a.kstage = int(p.K_stage);
+    a.R = p.rows_per_tile;
+    a.WB = p.cols_per_tile;
+    a.IR = p.patch_rows;
+    a.IW = p.patch_cols;
+    a.tile_m = p.tile_m;
+    a.tile_n = p.tile_n;
+    a.wm = p.wave_m;
+    a.bf16 = d.dtype == CONV2D_BF16 ? 1 : 0;
+    return a;
+}
+
+// implicit form: (a3) the filter into the window's K order (kw, kh, ci)
+// unless a 1x1 filter already is, then (a2, a4, a5) in one kernel: window
+// rows built in LDS, contracted, fp32 y written. Arguments checked by the caller.
+conv2d_status_t run_implicit(const conv2d_desc_t &d, const conv2d_implicit_plan_t &p, const void *x,
+                             const void *w, float *y, void *ws, hipStream_t s)
+{
+    const void *wst = w;
+    if (p.ws_bytes > 0) {
+        const LayoutGeom g = layout_geom(d, IM2WIN_LAYOUT_CL);
+        const StageGeom sg = stage_geom(d, IM2WIN_LAYOUT_CL, p.tile_m);
+        StageArgs sa{};
+        sa.w = w;
+        sa.out = ws;
+        sa.Cout = int(d.Cout);
+        sa.Cin = int(d.Cin);
+        sa.KH = int(d.KH);
+        sa.KW = int(d.KW);
+        sa.Cin_pad = int(g.Cin_pad);
+        sa.rows = int(sg.rows);
+        sa.row_len = int(sg.row_len);
+        sa.esize = int(elem_size(d.dtype));
+        ProfScope ps(s, CONV2D_KERNEL_WEIGHT_STAGE);
+        if (launch_stage_cl(sa, s) != hipSuccess) return CONV2D_ERR_HIP;
+        wst = ws;
+    }
+    ProfScope ps(s, CONV2D_KERNEL_IMPLICIT);
+    return launch_conv_implicit(implicit_args(d, p, x, wst, y), s) == hipSuccess ? CONV2D_OK
+                                                                                 : CONV2D_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -183,6 +243,11 @@ conv2d_status_t conv2d_fwd(const conv2d_desc_t *d, const void *x, const void *w,
     if (ws && !aligned(ws, 256)) return CONV2D_ERR_MISALIGNED;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if (p.algo == 1) {
+        conv2d_implicit_plan_t ip;
+        if (make_implicit_plan(*d, &ip) != CONV2D_OK) return CONV2D_ERR_UNSUPPORTED;
+        return run_implicit(*d, ip, x, w, y, ws, s);
+    }
     char *wsb = static_cast<char *>(ws);
     const LayoutGeom g = layout_geom(*d, p.layout);
     const StageGeom sg = stage_geom(*d, p.layout, p.gemm_tile_m);
@@ -301,6 +366,49 @@ conv2d_status_t im2win_window_gemm(const conv2d_desc_t *d, const void *win, cons
     ProfScope ps(s, CONV2D_KERNEL_GEMM);
     const hipError_t e = launch_gemm(*d, p, g, win, wst, y, row0, rows, s);
     return e == hipSuccess ? CONV2D_OK : CONV2D_ERR_HIP;
+}
+
+conv2d_status_t conv2d_implicit_plan(const conv2d_desc_t *d, conv2d_implicit_plan_t *out)
+{
+    if (!d || !out) return CONV2D_ERR_NULL_POINTER;
+    return make_implicit_plan(*d, out);
+}
+
+size_t conv2d_implicit_workspace_size(const conv2d_desc_t *d)
+{
+    if (!d) return 0;
+    conv2d_implicit_plan_t p;
+    if (make_implicit_plan(*d, &p) != CONV2D_OK) return 0;
+    return size_t(p.ws_bytes);
+}
+
+conv2d_status_t conv2d_fwd_implicit(const conv2d_desc_t *d, const void *x, const void *w,
+                                    float *y, void *ws, void *stream)
+{
+    if (!d) return CONV2D_ERR_NULL_POINTER;
+    conv2d_implicit_plan_t p;
+    const conv2d_status_t st = make_implicit_plan(*d, &p);
+    if (st != CONV2D_OK) return st;
+    if (!x || !w || !y) return CONV2D_ERR_NULL_POINTER;
+    if (p.ws_bytes > 0 && !ws) return CONV2D_ERR_WORKSPACE;
+    if (!aligned(x, 16) || !aligned(w, 16) || !aligned(y, 16)) return CONV2D_ERR_MISALIGNED;
+    if (ws && !aligned(ws, 256)) return CONV2D_ERR_MISALIGNED;
+    return run_implicit(*d, p, x, w, y, ws, static_cast<hipStream_t>(stream));
+}
+
+conv2d_status_t im2win_implicit_gemm(const conv2d_desc_t *d, const void *x, const void *wst,
+                                     float *y, void *stream)
+{
+    if (!d) return CONV2D_ERR_NULL_POINTER;
+    conv2d_implicit_plan_t p;
+    const conv2d_status_t st = make_implicit_plan(*d, &p);
+    if (st != CONV2D_OK) return st;
+    if (!x || !wst || !y) return CONV2D_ERR_NULL_POINTER;
+    if (!aligned(x, 16) || !aligned(wst, 16) || !aligned(y, 16)) return CONV2D_ERR_MISALIGNED;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    ProfScope ps(s, CONV2D_KERNEL_IMPLICIT);
+    return launch_conv_implicit(implicit_args(*d, p, x, wst, y), s) == hipSuccess ? CONV2D_OK
+                                                                                   : CONV2D_ERR_HIP;
 }
 
 conv2d_status_t conv2d_profile_enable(int32_t on)

@@ -22,71 +22,15 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
-#include <type_traits>
 
 #include "../launch.hpp"
+#include "lds_dma.hpp"
 #include "tile_map.hpp"
 
 namespace im2win {
 namespace {
 
-typedef _Float16 half8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float floatx4 __attribute__((ext_vector_type(4)));
-
-template <bool BF16>
-__device__ __forceinline__ floatx4 mfma16(const uint4 &a, const uint4 &b, const floatx4 &c)
-{
-    if constexpr (BF16) {
-        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-    } else {
-        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, a),
-                                                      __builtin_bit_cast(half8, b), c, 0, 0, 0);
-    }
-}
-
-// s_waitcnt with only the vector-memory count constrained (gfx9 encoding)
-template <int N>
-__device__ __forceinline__ void wait_vm()
-{
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-
-// Workgroup barrier between K stages: this wave's LDS reads are complete
-// (lgkmcnt(0)) before it signals, so no wave copies into a buffer another
-// wave may still be reading; the compiler may move no LDS access across it.
-__device__ __forceinline__ void stage_barrier()
-{
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));   // lgkmcnt(0) only
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
-
-// One wave copy of 16 bytes per lane from global memory into the LDS block at
-// byte address lds (wave-uniform): lane l lands at lds + 16*l. Written as
-// inline assembly so that the compiler adds no wait of its own before later
-// LDS reads (its alias tracking of these copies is conservative across the
-// stage loop and would drain every copy in flight); the waits of the stage
-// loop (wait_vm, stage_barrier) and the final wait_vm<0> order them instead.
-__device__ __forceinline__ void copy_to_lds(const void *src, uint32_t lds)
-{
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-                 :
-                 : "v"(src), "s"(lds)
-                 : "memory", "m0");
-}
-
-typedef const __attribute__((address_space(3))) uint16_t *lds_u16_ptr;
-
-__device__ __forceinline__ uint32_t lds_addr(const uint16_t *p)
-{
-    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_u16_ptr)p));   // LDS byte offset
-}
-
-constexpr int KI = 64;   // halves per stage row: 128 bytes, 8 granules of 16 bytes
+constexpr int KI = kStageK;
 
 template <int MB, int NB, int WM, bool BF16>
 __global__ __launch_bounds__(256) void gemm_mfma_dma_kernel(
@@ -147,11 +91,11 @@ __global__ __launch_bounds__(256) void gemm_mfma_dma_kernel(
             copy_to_lds(bsrc[i] + k0, __builtin_amdgcn_readfirstlane(lds_addr(sb + (wave + 4 * i) * 512)));
     };
 
-    floatx4 acc[FM][FN];
+    floatx4_t acc[FM][FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < FN; ++j) acc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
     const int arow = wm * (MB / WM) + (lane & 15);
     const int bcol = wn * (NB / WN) + (lane & 15);
@@ -173,7 +117,7 @@ __global__ __launch_bounds__(256) void gemm_mfma_dma_kernel(
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
-                for (int j = 0; j < FN; ++j) acc[i][j] = mfma16<BF16>(af[i], bf[j], acc[i][j]);
+                for (int j = 0; j < FN; ++j) acc[i][j] = mfma16x16x32<BF16>(af[i], bf[j], acc[i][j]);
         }
     };
 

@@ -72,4 +72,19 @@ hipError_t launch_gemm_mfma_resident(const MfmaGemmArgs &a, hipStream_t s);
 // only for windows whose length krun equals kstage, a multiple of 64
 hipError_t launch_gemm_mfma_dma(const MfmaGemmArgs &a, hipStream_t s);
 
+// implicit form: window rows built in LDS straight from NCHW x (no window
+// tensor); tile_m x tile_n output tile over R window rows x WB columns of
+// one image, a patch of IR x IW input positions per 64-channel block
+struct ImplicitArgs {
+    const void *x;          // NCHW input
+    const void *wst;        // staged filter [Cout][kstage], K order (kw, kh, ci)
+    float *y;
+    int N, Cin, H, W, Cout, KH, KW, stride, pad, Ho, Wo;
+    int kstage;             // KW*KH*Cin
+    int R, WB, IR, IW;
+    int tile_m, tile_n, wm;
+    int bf16;
+};
+hipError_t launch_conv_implicit(const ImplicitArgs &a, hipStream_t s);
+
 }  // namespace im2win

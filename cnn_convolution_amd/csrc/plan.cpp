@@ -1,6 +1,7 @@
 // Host planner: see plan.hpp.
 #include "plan.hpp"
 
+#include <algorithm>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -211,6 +212,29 @@ static void pick_mfma_dma(const conv2d_desc_t &d, int64_t krun, int64_t cols, co
     p->gemm_wave_m = wm;
 }
 
+// What conv2d_fwd runs for a matrix-core layer. The implicit form (window
+// rows built in LDS, no window tensor) measured faster for 3x3-class filters
+// (2 to 9 taps) with one or two 64-channel blocks: it skips the window
+// tensor's HBM round trip, and with few blocks its per-block patch load is
+// rarely exposed. With more channel blocks, one tap or larger filters the
+// window tensor path was faster on the measured layers.
+// IM2WIN_ALGO=window|implicit overrides (implicit only where it applies).
+static void pick_algo(const conv2d_desc_t &d, conv2d_plan_t *p) {
+    conv2d_implicit_plan_t ip;
+    const bool can = make_implicit_plan(d, &ip) == CONV2D_OK;
+    const int64_t taps = d.KH * d.KW;
+    bool use = can && d.Cin <= 128 && taps >= 2 && taps <= 9;
+    if (const char *e = std::getenv("IM2WIN_ALGO")) {
+        if (std::strcmp(e, "window") == 0) use = false;
+        if (std::strcmp(e, "implicit") == 0) use = can;
+    }
+    p->algo = use ? 1 : 0;
+    if (use) {
+        p->ws_bytes = ip.ws_bytes;
+        p->meets_ws_target = p->ws_bytes <= p->ws_target_bytes ? 1 : 0;
+    }
+}
+
 int valu_cols_per_lane(const conv2d_desc_t &d) {
     if (d.KH == 7 && d.KW == 7 && d.stride == 2) return 2;
     if (d.KH == 11 && d.KW == 11 && d.stride == 4) return 1;
@@ -277,6 +301,7 @@ conv2d_status_t make_plan(const conv2d_desc_t &d, conv2d_plan_t *p) {
         p->gemm_kernel = 1;
         pick_mfma_resident(d, p->rows_per_chunk * p->Wo, p);
         pick_mfma_dma(d, d.KW * d.KH * g.Cin_pad, p->rows_per_chunk * p->Wo, p);
+        pick_algo(d, p);
     } else {
         p->gemm_kernel = 0;
         p->gemm_tile_m = 4 * kValuMt;
@@ -284,6 +309,81 @@ conv2d_status_t make_plan(const conv2d_desc_t &d, conv2d_plan_t *p) {
         p->gemm_kslice = 0;
         p->gemm_ksplit = pick_valu_ksplit(d, p->rows_per_chunk, p->Wo, p->Cout_stage);
     }
+    return CONV2D_OK;
+}
+
+// Implicit form. A tile covers R window rows x WB output columns of one
+// image (R*WB <= NB GEMM columns); its patch holds IR = (R-1)*s + KH input
+// rows x IW = (WB-1)*s + KW input columns of one 64-channel block. Candidates
+// are scored by the share of the NB columns that are real outputs, with a
+// penalty when the LDS of a workgroup leaves room for only one per CU.
+// IM2WIN_IMPLICIT_TILE="MB,NB,WM,R,WB" overrides the choice (for sweeps).
+static const int kImplicitTiles[][3] = {{64, 64, 1}, {64, 128, 1}, {128, 64, 2}, {128, 128, 2}};
+
+conv2d_status_t make_implicit_plan(const conv2d_desc_t &d, conv2d_implicit_plan_t *p) {
+    const conv2d_status_t st = check_desc(d);
+    if (st != CONV2D_OK) return st;
+    std::memset(p, 0, sizeof(*p));
+    if (d.dtype == CONV2D_F32 || d.Cin % 64 != 0) return CONV2D_ERR_UNSUPPORTED;
+    const int64_t Ho = out_extent(d.H, d.KH, d.stride, d.pad);
+    const int64_t Wo = out_extent(d.W, d.KW, d.stride, d.pad);
+    p->Ho = Ho;
+    p->Wo = Wo;
+    p->K_stage = d.KW * d.KH * d.Cin;
+    p->flops = 2 * d.N * d.Cout * Ho * Wo * d.Cin * d.KH * d.KW;
+    const StageGeom sg = stage_geom(d, IM2WIN_LAYOUT_CL, 64);
+    if (sg.row_len != p->K_stage) return CONV2D_ERR_UNSUPPORTED;
+    p->ws_bytes = sg.needed ? round_up(sg.rows * sg.row_len * elem_size(d.dtype), 256) : 0;
+
+    struct Cand { int64_t mb, nb, wm, r, wb; double score; };
+    Cand best{0, 0, 0, 0, 0, -1.0};
+    auto consider = [&](int64_t mb, int64_t nb, int64_t wm, int64_t r, int64_t wb) {
+        if (r < 1 || wb < 1 || r * wb > nb) return;
+        const int64_t ir = (r - 1) * d.stride + d.KH, iw = (wb - 1) * d.stride + d.KW;
+        const int64_t lds = implicit_lds_bytes(mb, ir, iw);
+        if (lds > kImplicitMaxLdsBytes) return;
+        const double cols = double(Ho * Wo) / double(ceil_div(Ho, r) * ceil_div(Wo, wb) * nb);
+        const double rowsm = double(d.Cout) / double(ceil_div(d.Cout, mb) * mb);
+        double score = cols * rowsm;
+        if (lds > kImplicitPairLdsBytes) score *= 0.8;
+        if (mb == 128) score *= 1.05;          // fewer filter re-reads per output
+        if (nb == 128) score *= 1.05;
+        if (score > best.score) best = Cand{mb, nb, wm, r, wb, score};
+    };
+    for (const auto &t : kImplicitTiles) {
+        const int64_t mb = t[0], nb = t[1], wm = t[2];
+        if (mb == 128 && d.Cout <= 64) continue;
+        if (Wo >= nb) {
+            consider(mb, nb, wm, 1, nb);
+        } else {
+            // balanced rows: as many tiles as the widest R needs, rows spread evenly
+            const int64_t rmax = std::min<int64_t>(Ho, nb / Wo);
+            for (int64_t r = 1; r <= rmax; ++r) consider(mb, nb, wm, ceil_div(Ho, ceil_div(Ho, r)), Wo);
+        }
+        for (int64_t wb = std::min<int64_t>(Wo, nb); wb >= 8; wb /= 2) consider(mb, nb, wm, 1, wb);
+    }
+    if (const char *e = std::getenv("IM2WIN_IMPLICIT_TILE")) {
+        int m = 0, n = 0, w = 0, r = 0, b = 0;
+        if (std::sscanf(e, "%d,%d,%d,%d,%d", &m, &n, &w, &r, &b) == 5) {
+            bool known = false;
+            for (const auto &t : kImplicitTiles) known = known || (t[0] == m && t[1] == n && t[2] == w);
+            const int64_t ir = (r - 1) * d.stride + d.KH, iw = (int64_t(b) - 1) * d.stride + d.KW;
+            if (known && r >= 1 && b >= 1 && int64_t(r) * b <= n &&
+                implicit_lds_bytes(m, ir, iw) <= kImplicitMaxLdsBytes)
+                best = Cand{m, n, w, r, b, 1.0};
+        }
+    }
+    if (best.score < 0) return CONV2D_ERR_UNSUPPORTED;
+    p->tile_m = int32_t(best.mb);
+    p->tile_n = int32_t(best.nb);
+    p->wave_m = int32_t(best.wm);
+    p->rows_per_tile = int32_t(best.r);
+    p->cols_per_tile = int32_t(best.wb);
+    p->patch_rows = int32_t((best.r - 1) * d.stride + d.KH);
+    p->patch_cols = int32_t((best.wb - 1) * d.stride + d.KW);
+    p->lds_bytes = implicit_lds_bytes(best.mb, p->patch_rows, p->patch_cols);
+    p->tiles = ceil_div(d.Cout, best.mb) * d.N * ceil_div(Ho, best.r) * ceil_div(Wo, best.wb);
+    if (p->tiles > 0x7fffffff) return CONV2D_ERR_INVALID_DESC;
     return CONV2D_OK;
 }
 

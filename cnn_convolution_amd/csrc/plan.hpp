@@ -26,6 +26,12 @@ constexpr int kValuThreads = 256;
 // for its 64 x (K_stage + 8) filter block (two workgroups still fit a CU)
 constexpr int64_t kResidentMaxLdsBytes = 80 * 1024;
 
+// implicit matrix-core convolution: LDS of one workgroup = three filter stage
+// buffers of mb rows x 128 bytes + a patch of ir x iw positions x 128 bytes
+inline int64_t implicit_lds_bytes(int64_t mb, int64_t ir, int64_t iw) { return (3 * mb + ir * iw) * 128; }
+constexpr int64_t kImplicitMaxLdsBytes = 160 * 1024;   // one workgroup per CU
+constexpr int64_t kImplicitPairLdsBytes = 80 * 1024;   // two workgroups per CU
+
 // fp32 vector-ALU kernel: output columns per lane for this filter shape.
 int valu_cols_per_lane(const conv2d_desc_t &d);
 
@@ -59,5 +65,9 @@ StageGeom stage_geom(const conv2d_desc_t &d, int32_t layout, int tile_m);
 
 // Full plan (fills the C struct). Returns CONV2D_OK or a validation error.
 conv2d_status_t make_plan(const conv2d_desc_t &d, conv2d_plan_t *p);
+
+// Plan of the implicit form; CONV2D_ERR_UNSUPPORTED when the layer does not
+// qualify (fp32, Cin not a multiple of 64, or no tile whose patch fits LDS).
+conv2d_status_t make_implicit_plan(const conv2d_desc_t &d, conv2d_implicit_plan_t *p);
 
 }  // namespace im2win

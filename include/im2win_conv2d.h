@@ -110,7 +110,9 @@ typedef struct {
     int64_t wstage_bytes;         /* staged filter, at the start of ws            */
     int64_t win_offset_bytes;     /* where the window chunk starts in ws          */
     int64_t win_chunk_bytes;      /* window chunk buffer                          */
-    int64_t ws_bytes;             /* total workspace = conv2d_workspace_size()     */
+    int64_t ws_bytes;             /* workspace of conv2d_fwd = conv2d_workspace_size():
+                                     staged filter + window chunk (algo 0), or what
+                                     conv2d_implicit_workspace_size reports (algo 1) */
     int64_t im2col_bytes;         /* N*Ho*Wo*Cin*KH*KW*sizeof(dtype)              */
     int64_t ws_target_bytes;      /* im2col_bytes / KW                            */
     int32_t meets_ws_target;      /* ws_bytes <= ws_target_bytes                  */
@@ -124,7 +126,9 @@ typedef struct {
                                      3: matrix core, tiles copied memory -> LDS
                                         directly (whole 64-element K stages)         */
     int32_t gemm_wave_m;          /* waves along M in a wave group (matrix path)   */
-    int32_t reserved1;
+    int32_t algo;                 /* what conv2d_fwd runs: 0 the window tensor in ws
+                                     (pack + window-GEMM per chunk), 1 the implicit
+                                     form (conv2d_fwd_implicit)                     */
     int64_t flops;                /* 2*N*Cout*Ho*Wo*Cin*KH*KW (padded taps included) */
 } conv2d_plan_t;
 
@@ -134,7 +138,9 @@ size_t conv2d_workspace_size(const conv2d_desc_t *d);
 /* Fill *out with the plan for *d. Host only; never touches a GPU. */
 conv2d_status_t conv2d_plan(const conv2d_desc_t *d, conv2d_plan_t *out);
 
-/* y = conv2d(x, w) as defined at the top of this file.
+/* y = conv2d(x, w) as defined at the top of this file, by the form the plan
+ * names (conv2d_plan_t.algo): the window tensor in ws, or the implicit form
+ * below where it measured faster for that layer class.
  * ws: device buffer of at least conv2d_workspace_size(d) bytes, 256-byte
  * aligned (NULL allowed only when that size is 0); its contents on return
  * are unspecified. x, w, y: 16-byte aligned device pointers. */
@@ -173,16 +179,67 @@ conv2d_status_t im2win_window_gemm(const conv2d_desc_t *d, const void *win, cons
 
 const char *conv2d_status_string(conv2d_status_t s);
 
+/* ---- implicit (fused) form ---------------------------------------------
+ * The same y = conv2d(x, w), with the window rows built in LDS straight
+ * from x instead of going through a window tensor in the workspace: each
+ * output tile (tile_m output channels x cols_per_tile columns of
+ * rows_per_tile window rows (n, ho) of one image) holds, per block of 64
+ * input channels, the input rows its window rows interleave (Eq. (2) of the
+ * im2win paper: window row ho = input rows ho*stride - pad .. + KH - 1) as a
+ * channels-innermost patch, and contracts it against the staged filter in
+ * the window's K order (Sec. III-C Eq. (3), Sec. III-D). fp16/bf16 only,
+ * Cin a multiple of 64; matrix cores with fp32 accumulation, fp32 y. The
+ * workspace holds only the staged filter (none for a 1x1 filter). */
+typedef struct {
+    int32_t tile_m, tile_n;       /* output channels x GEMM columns per workgroup  */
+    int32_t wave_m;               /* waves along M                                 */
+    int32_t rows_per_tile;        /* window rows (n, ho) of one image per tile      */
+    int32_t cols_per_tile;        /* output columns wo per tile                     */
+    int32_t patch_rows;           /* input rows held per tile: (rows-1)*stride + KH */
+    int32_t patch_cols;           /* input columns held: (cols-1)*stride + KW       */
+    int32_t reserved;
+    int64_t lds_bytes;            /* LDS per workgroup                              */
+    int64_t tiles;                /* workgroups of the launch                       */
+    int64_t Ho, Wo;
+    int64_t K_stage;              /* staged filter row: KW*KH*Cin                   */
+    int64_t ws_bytes;             /* the staged filter; 0 for a 1x1 filter           */
+    int64_t flops;                /* 2*N*Cout*Ho*Wo*Cin*KH*KW                        */
+} conv2d_implicit_plan_t;
+
+/* Fill *out for *d. CONV2D_ERR_UNSUPPORTED when the implicit form does not
+ * take the layer (fp32, Cin not a multiple of 64, or no tile whose patch
+ * fits in LDS); other errors as conv2d_plan. Host only. */
+conv2d_status_t conv2d_implicit_plan(const conv2d_desc_t *d, conv2d_implicit_plan_t *out);
+
+/* Bytes of workspace conv2d_fwd_implicit needs (0 if d is invalid or not
+ * supported, or for a 1x1 filter). */
+size_t conv2d_implicit_workspace_size(const conv2d_desc_t *d);
+
+/* y = conv2d(x, w) by the implicit form. Arguments, alignment, ownership and
+ * asynchrony as conv2d_fwd; ws of at least conv2d_implicit_workspace_size(d)
+ * bytes (NULL allowed when that is 0). Returns CONV2D_ERR_UNSUPPORTED, and
+ * launches nothing, for a layer conv2d_implicit_plan does not take. */
+conv2d_status_t conv2d_fwd_implicit(const conv2d_desc_t *d, const void *x, const void *w,
+                                    float *y, void *ws, void *stream);
+
+/* Rows (a2, a4, a5) of the implicit form on their own: the implicit kernel
+ * with a filter already staged in the window's K order (as
+ * im2win_weight_stage writes it for IM2WIN_LAYOUT_CL; for a 1x1 filter w
+ * itself), writing all of y. Device pointers, 16-byte aligned. */
+conv2d_status_t im2win_implicit_gemm(const conv2d_desc_t *d, const void *x, const void *wst,
+                                     float *y, void *stream);
+
 /* ---- measurement hook --------------------------------------------------
- * While enabled, conv2d_fwd records a HIP event pair around every kernel it
- * launches (on the call's stream). conv2d_profile_read synchronises on the
- * recorded events, returns per-kernel totals since the last read, and clears
- * them. Not for concurrent use from several threads. */
+ * While enabled, conv2d_fwd and conv2d_fwd_implicit record a HIP event pair
+ * around every kernel they launch (on the call's stream). conv2d_profile_read
+ * synchronises on the recorded events, returns per-kernel totals since the
+ * last read, and clears them. Not for concurrent use from several threads. */
 typedef enum {
     CONV2D_KERNEL_WEIGHT_STAGE = 0,
     CONV2D_KERNEL_PACK = 1,
     CONV2D_KERNEL_GEMM = 2,
-    CONV2D_KERNEL_KINDS = 3
+    CONV2D_KERNEL_IMPLICIT = 3,   /* the implicit form's convolution kernel        */
+    CONV2D_KERNEL_KINDS = 4
 } conv2d_kernel_kind_t;
 
 typedef struct {

@@ -18,8 +18,7 @@ def _plan(name, dt):
     cfg = workloads.get_config(name)
     code = {"f32": conv.F32, "f16": conv.F16, "bf16": conv.BF16}[dt]
     d = conv.describe(cfg.x_shape, cfg.w_shape, cfg.stride, cfg.pad, code)
-    p = conv.plan(d)
-    return p, p.rows_total - (p.n_chunks - 1) * p.rows_per_chunk
+    return d, conv.plan(d)
 
 
 def test_more_than_one_gpu_exits_with_a_message():
@@ -47,19 +46,39 @@ def test_traffic_records_are_consistent(dt):
 
 
 def test_traffic_is_null_once_the_kernel_changes(monkeypatch):
-    p, rows = _plan("resnet3x3", "f16")
+    d, p = _plan("resnet3x3", "f16")
     monkeypatch.setattr(bench, "gemm_source_sha", lambda kernel: "0" * 16)
-    assert bench.recorded_traffic("resnet3x3", "f16", p, rows) is None
+    assert bench.recorded_traffic("resnet3x3", "f16", d, p) is None
 
 
-def test_traffic_is_null_for_another_launch_size_or_tile(monkeypatch):
-    p, rows = _plan("resnet3x3", "f16")
-    assert bench.recorded_traffic("resnet3x3", "f16", p, rows - 1) is None
+def test_traffic_is_null_for_another_form_or_tile(monkeypatch):
+    d, p = _plan("resnet3x3", "f16")
+    base = bench.dominant_key(d, p)
+    monkeypatch.setenv("IM2WIN_ALGO", "window" if p.algo == 1 else "implicit")
+    d2, q = _plan("resnet3x3", "f16")
+    assert bench.dominant_key(d2, q) != base
+    if bench.recorded_traffic("resnet3x3", "f16", d, p) is not None:
+        assert bench.recorded_traffic("resnet3x3", "f16", d2, q) is None
+    monkeypatch.delenv("IM2WIN_ALGO")
+    monkeypatch.setenv("IM2WIN_IMPLICIT_TILE", "64,64,1,1,56")
     monkeypatch.setenv("IM2WIN_MFMA_DMA_TILE", "128,128,1")
-    q, rows_q = _plan("resnet3x3", "f16")
-    assert bench.recorded_traffic("resnet3x3", "f16", q, rows_q) is None
+    d3, r = _plan("resnet3x3", "f16")
+    assert bench.dominant_key(d3, r) != base
+    assert bench.recorded_traffic("resnet3x3", "f16", d3, r) is None
+
+
+def test_dominant_kernel_follows_the_plan(monkeypatch):
+    d, p = _plan("resnet3x3", "f16")
+    kid, tile, rows = bench.dominant_key(d, p)
+    if p.algo == 1:
+        assert kid == 4 and rows == p.rows_total and tile.startswith("i:")
+    monkeypatch.setenv("IM2WIN_ALGO", "window")
+    d, p = _plan("resnet3x3", "f16")
+    kid, tile, rows = bench.dominant_key(d, p)
+    assert p.algo == 0 and kid == p.gemm_kernel
+    assert rows == p.rows_total - (p.n_chunks - 1) * p.rows_per_chunk
 
 
 def test_traffic_is_null_without_a_summary():
-    p, rows = _plan("mix512", "f16")
-    assert bench.recorded_traffic("mix512", "f16", p, rows) is None
+    d, p = _plan("mix512", "f16")
+    assert bench.recorded_traffic("mix512", "f16", d, p) is None

@@ -1,0 +1,236 @@
+"""GPU parity of the implicit form (conv2d_fwd_implicit: window rows built in
+LDS straight from x, no window tensor) against the CPU oracle, through the C
+ABI. Same tolerances as the two-kernel path: relative L2 over the compared
+outputs <= 2e-3 (fp16) and <= 1e-2 (bf16), oracle in float64 on the same
+rounded inputs; integer-valued inputs bit for bit."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import cnn_convolution_amd as conv
+from cnn_convolution_amd import _lib
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f16": 2e-3, "bf16": 1e-2}
+CODE = {"f16": conv.F16, "bf16": conv.BF16}
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    _lib.lib()   # the HIP library must load: no fallback
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def rel_l2(got, ref):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    den = np.linalg.norm(ref)
+    return float(np.linalg.norm(got - ref) / (den if den > 0 else 1.0))
+
+
+def run_implicit(x, w, s, p):
+    y = conv.conv2d_implicit(x.to(DEV), w.to(DEV), stride=s, pad=p)
+    torch.cuda.synchronize()
+    return y.cpu()
+
+
+# N, Cin, H, W, Cout, KH, KW, s, p: several tiles, ragged rows/columns/channels
+SHAPES = [
+    (2, 64, 9, 10, 70, 3, 3, 1, 1),      # Cout past one 64-row block
+    (1, 128, 6, 7, 40, 1, 1, 1, 0),      # 1x1: the filter is used as staged; two channel blocks
+    (2, 64, 11, 12, 130, 3, 3, 2, 0),    # stride 2, three M blocks
+    (1, 64, 9, 9, 20, 5, 5, 1, 2),       # 5x5
+    (1, 64, 5, 40, 8, 3, 3, 1, 1),       # one image row of tiles
+    (1, 64, 3, 3, 3, 3, 3, 1, 5),        # padding wider than the filter: zero border
+    (2, 192, 8, 8, 96, 3, 3, 1, 1),      # three channel blocks: the patch is rebuilt twice
+    (1, 64, 12, 140, 16, 3, 3, 1, 1),    # output rows wider than one tile: column tiles
+    (1, 64, 16, 16, 64, 7, 7, 2, 3),     # 7x7 stride 2
+    (1, 64, 8, 11, 24, 2, 4, 3, 2),      # KH != KW, stride 3
+]
+TILES = [None, "64,64,1,1,16", "128,128,2,3,8", "128,64,2,2,5", "64,128,1,4,9"]
+
+
+@pytest.mark.parametrize("tile", TILES, ids=lambda t: "planned" if t is None else t.replace(",", "."))
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+@pytest.mark.parametrize("shape", SHAPES)
+def test_implicit_matches_oracle(shape, dt, tile, monkeypatch):
+    if tile is not None:
+        monkeypatch.setenv("IM2WIN_IMPLICIT_TILE", tile)
+    N, Cin, H, W, Cout, KH, KW, s, p = shape
+    d = conv.describe((N, Cin, H, W), (Cout, Cin, KH, KW), s, p, CODE[dt])
+    pl = conv.implicit_plan(d)
+    if tile is not None:
+        want = tuple(int(v) for v in tile.split(","))
+        got = (pl.tile_m, pl.tile_n, pl.wave_m, pl.rows_per_tile, pl.cols_per_tile)
+        assert got == want
+    _say(f"implicit {tile} {dt} {shape} tiles={pl.tiles} lds={pl.lds_bytes}")
+    x, w = workloads.make_inputs(N, Cin, H, W, Cout, KH, KW, seed=sum(shape) + 5, dtype=dt,
+                                 w_dist="normal")
+    y = run_implicit(x, w, s, p)
+    ref = oracle.conv2d(x, w, s, p)
+    assert tuple(y.shape) == ref.shape
+    err = rel_l2(y.numpy(), ref)
+    assert err <= TOL[dt], f"rel L2 {err:.3e} > {TOL[dt]}"
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+@pytest.mark.parametrize("shape", [(2, 64, 9, 10, 70, 3, 3, 1, 1), (2, 128, 7, 6, 33, 3, 3, 2, 1),
+                                   (1, 64, 12, 12, 64, 1, 1, 1, 0)])
+def test_implicit_integer_inputs_bit_exact(shape, dt):
+    N, Cin, H, W, Cout, KH, KW, s, p = shape
+    _say(f"implicit-int {dt} {shape}")
+    x, w = workloads.make_inputs(N, Cin, H, W, Cout, KH, KW, seed=4, dtype=dt,
+                                 x_dist="int3", w_dist="int3")
+    y = run_implicit(x, w, s, p)
+    ref = oracle.conv2d(x, w, s, p)
+    assert np.array_equal(y.numpy().astype(np.float64), ref)
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_implicit_agrees_with_two_kernel_path(dt, monkeypatch):
+    """Same inputs through both forms: each against the oracle, and close to each other."""
+    shape = (2, 128, 10, 9, 80, 3, 3, 1, 1)
+    N, Cin, H, W, Cout, KH, KW, s, p = shape
+    x, w = workloads.make_inputs(N, Cin, H, W, Cout, KH, KW, seed=9, dtype=dt, w_dist="normal")
+    xd, wd = x.to(DEV), w.to(DEV)
+    a = conv.conv2d_implicit(xd, wd, s, p)
+    monkeypatch.setenv("IM2WIN_ALGO", "window")
+    assert conv.plan(conv.describe(tuple(x.shape), tuple(w.shape), s, p, CODE[dt])).algo == 0
+    b = conv.conv2d(xd, wd, s, p)
+    torch.cuda.synchronize()
+    ref = oracle.conv2d(x, w, s, p)
+    assert rel_l2(a.cpu().numpy(), ref) <= TOL[dt]
+    assert rel_l2(b.cpu().numpy(), ref) <= TOL[dt]
+    assert rel_l2(a.cpu().numpy(), b.cpu().numpy()) <= TOL[dt]
+
+
+def test_implicit_leaves_memory_past_y_untouched():
+    """The kernel stores exactly the N*Cout*Ho*Wo outputs: a guard band after y
+    keeps its sentinel."""
+    N, Cin, H, W, Cout, KH, KW, s, p = 2, 64, 9, 10, 70, 3, 3, 1, 1
+    x, w = workloads.make_inputs(N, Cin, H, W, Cout, KH, KW, seed=2, dtype="f16")
+    d = conv.describe(tuple(x.shape), tuple(w.shape), s, p, conv.F16)
+    pl = conv.implicit_plan(d)
+    n_out = N * Cout * pl.Ho * pl.Wo
+    buf = torch.full((n_out + 4096,), 12345.0, dtype=torch.float32, device=DEV)
+    ws = torch.empty(max(pl.ws_bytes, 1), dtype=torch.uint8, device=DEV)
+    conv.conv2d_implicit_into(x.to(DEV), w.to(DEV), buf, ws, s, p)
+    torch.cuda.synchronize()
+    host = buf.cpu().numpy()
+    assert (host[n_out:] == 12345.0).all()
+    ref = oracle.conv2d(x, w, s, p).reshape(-1)
+    assert rel_l2(host[:n_out], ref) <= TOL["f16"]
+
+
+def test_implicit_profile_hook_counts_launches():
+    x, w = workloads.make_inputs(2, 64, 8, 8, 32, 3, 3, seed=1, dtype="f16")
+    xd, wd = x.to(DEV), w.to(DEV)
+    conv.conv2d_implicit(xd, wd, 1, 1)
+    torch.cuda.synchronize()
+    conv.profile_read()
+    conv.profile_enable(True)
+    try:
+        conv.conv2d_implicit(xd, wd, 1, 1)
+        conv.conv2d_implicit(xd, wd, 1, 1)
+    finally:
+        conv.profile_enable(False)
+    prof = conv.profile_read()
+    assert prof["implicit"]["launches"] == 2
+    assert prof["weight_stage"]["launches"] == 2
+    assert prof["pack"]["launches"] == 0 and prof["gemm"]["launches"] == 0
+
+
+def _sample_indices(N, Cout, Ho, Wo, rng, count=3000):
+    idx = set(rng.integers(0, N * Cout * Ho * Wo, count).tolist())
+    cos = sorted({0, Cout - 1, Cout // 2} | set(rng.integers(0, Cout, 3).tolist()))
+    for n in {0, N - 1}:
+        for ho in {0, 1, Ho // 2, Ho - 1}:
+            for co in cos:
+                for wo in {0, 1, Wo // 2, Wo - 2, Wo - 1}:
+                    if 0 <= wo < Wo and 0 <= ho < Ho:
+                        idx.add(((n * Cout + co) * Ho + ho) * Wo + wo)
+    return np.array(sorted(idx), dtype=np.int64)
+
+
+def _eligible_configs():
+    out = []
+    for name, cfg in sorted(workloads.CONFIGS.items()):
+        for dt in cfg.dtypes:
+            if dt != "f32" and cfg.Cin % 64 == 0:
+                out.append((name, dt))
+    for name in ("cv4", "cv8", "cv12"):
+        out.append((name, "f16"))
+    return out
+
+
+def test_conv2d_fwd_runs_the_planned_form(monkeypatch):
+    """conv2d_fwd follows the plan's algo: the implicit form's kernel for a layer
+    it is planned for, pack + window-GEMM when the window form is forced."""
+    x, w = workloads.make_inputs(2, 64, 10, 10, 32, 3, 3, seed=6, dtype="f16")
+    xd, wd = x.to(DEV), w.to(DEV)
+    d = conv.describe(tuple(x.shape), tuple(w.shape), 1, 1, conv.F16)
+    ref = oracle.conv2d(x, w, 1, 1)
+    for algo, kind in (("implicit", "implicit"), ("window", "gemm")):
+        monkeypatch.setenv("IM2WIN_ALGO", algo)
+        pl = conv.plan(d)
+        assert pl.algo == (1 if algo == "implicit" else 0)
+        conv.conv2d(xd, wd, 1, 1)
+        torch.cuda.synchronize()
+        conv.profile_read()
+        conv.profile_enable(True)
+        try:
+            y = conv.conv2d(xd, wd, 1, 1)
+        finally:
+            conv.profile_enable(False)
+        prof = conv.profile_read()
+        assert prof[kind]["launches"] >= 1
+        other = "gemm" if kind == "implicit" else "implicit"
+        assert prof[other]["launches"] == 0
+        assert rel_l2(y.cpu().numpy(), ref) <= TOL["f16"]
+
+
+def test_implicit_kernel_alone_with_staged_filter():
+    """im2win_implicit_gemm on a filter staged by im2win_weight_stage."""
+    N, Cin, H, W, Cout, KH, KW, s, p = 2, 128, 9, 8, 40, 3, 3, 1, 1
+    x, w = workloads.make_inputs(N, Cin, H, W, Cout, KH, KW, seed=8, dtype="bf16")
+    xd, wd = x.to(DEV), w.to(DEV)
+    wst, _ = conv.weight_stage(wd, s, p, (H, W), conv.LAYOUT_CL)
+    d = conv.describe(tuple(x.shape), tuple(w.shape), s, p, conv.BF16)
+    pl = conv.implicit_plan(d)
+    y = torch.empty((N, Cout, pl.Ho, pl.Wo), dtype=torch.float32, device=DEV)
+    conv.implicit_gemm(xd, wst, y, d)
+    torch.cuda.synchronize()
+    ref = oracle.conv2d(x, w, s, p)
+    assert rel_l2(y.cpu().numpy(), ref) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("name,dt", _eligible_configs())
+def test_implicit_full_size_sampled(name, dt):
+    """At the measured sizes, with the launch configuration the benchmark times:
+    sampled outputs (random, borders, first and last image) against the oracle
+    point by point."""
+    cfg = workloads.get_config(name)
+    _say(f"implicit full-size {name} {dt} {cfg.desc()}")
+    x, w = workloads.make_config_inputs(cfg, dt)
+    y = run_implicit(x, w, cfg.stride, cfg.pad)
+    ho, wo = cfg.out_hw()
+    assert tuple(y.shape) == (cfg.N, cfg.Cout, ho, wo)
+    yf = y.numpy().reshape(-1)
+    rng = np.random.default_rng(cfg.seed + 1)
+    idx = _sample_indices(cfg.N, cfg.Cout, ho, wo, rng)
+    assert np.isfinite(yf[idx]).all()
+    ref = oracle.conv2d_points(x, w, cfg.stride, cfg.pad, idx)
+    err = rel_l2(yf[idx], ref)
+    assert err <= TOL[dt], f"{name} {dt}: rel L2 {err:.3e} > {TOL[dt]}"

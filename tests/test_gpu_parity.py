@@ -209,6 +209,7 @@ FORM_SHAPES = [
 @pytest.mark.parametrize("dt", ["f16", "bf16"])
 @pytest.mark.parametrize("shape", FORM_SHAPES)
 def test_mfma_forms_match_oracle(shape, dt, form, monkeypatch):
+    monkeypatch.setenv("IM2WIN_ALGO", "window")    # the window tensor path, not the implicit form
     for k, v in form.items():
         monkeypatch.setenv(k, v)
     N, Cin, H, W, Cout, KH, KW, s, p = shape
@@ -247,6 +248,7 @@ DMA_SHAPES = [
 @pytest.mark.parametrize("dt", ["f16", "bf16"])
 @pytest.mark.parametrize("shape", DMA_SHAPES)
 def test_dma_form_matches_oracle(shape, dt, tile, monkeypatch):
+    monkeypatch.setenv("IM2WIN_ALGO", "window")    # the window tensor path, not the implicit form
     monkeypatch.setenv("IM2WIN_MFMA_DMA_TILE", tile)
     N, Cin, H, W, Cout, KH, KW, s, p = shape
     d = conv.describe((N, Cin, H, W), (Cout, Cin, KH, KW), s, p, CODE[dt])
@@ -363,16 +365,17 @@ FULL = [(name, dt) for name, cfg in sorted(workloads.CONFIGS.items()) for dt in 
 
 
 @pytest.mark.parametrize("name,dt", FULL)
-def test_full_size_layers_sampled(name, dt):
-    """At the measured sizes and in the launch configuration the benchmark
-    times: sampled outputs (random, plus borders and chunk boundaries)
-    against the oracle computed point by point."""
+def test_full_size_layers_sampled(name, dt, monkeypatch):
+    """At the measured sizes, through the window tensor path (the implicit form
+    has its own full-size test): sampled outputs (random, plus borders and
+    chunk boundaries) against the oracle computed point by point."""
+    monkeypatch.setenv("IM2WIN_ALGO", "window")
     cfg = workloads.get_config(name)
     _say(f"full-size {name} {dt} {cfg.desc()}")
     x, w = workloads.make_config_inputs(cfg, dt)
     d = conv.describe(tuple(x.shape), tuple(w.shape), cfg.stride, cfg.pad, CODE[dt])
     pl = conv.plan(d)
-    assert pl.meets_ws_target == 1
+    assert pl.meets_ws_target == 1 and pl.algo == 0
     y = run_conv(x, w, cfg.stride, cfg.pad)
     ho, wo = cfg.out_hw()
     assert tuple(y.shape) == (cfg.N, cfg.Cout, ho, wo)

@@ -256,3 +256,64 @@ def test_row_layout_keeps_slack_after_every_run():
         pl = conv.plan(d)
         assert pl.pos_pad % 8 == 0 and pl.pos_pad >= pl.W_win * KH + 3
         assert pl.row_elems == d.Cin * pl.pos_pad
+
+
+def test_implicit_plan_takes_only_its_layers():
+    """The implicit form takes fp16/bf16 layers with Cin a multiple of 64 and
+    reports UNSUPPORTED (status 4) for the rest, before touching any pointer."""
+    assert conv._lib.implicit_plan_status(conv.make_desc(2, 64, 9, 9, 8, 3, 3, 1, 1, conv.F32)) == 4
+    assert conv._lib.implicit_plan_status(conv.make_desc(2, 96, 9, 9, 8, 3, 3, 1, 1, conv.F16)) == 4
+    assert conv._lib.implicit_plan_status(conv.make_desc(2, 3, 9, 9, 8, 3, 3, 1, 1, conv.BF16)) == 4
+    assert conv._lib.implicit_plan_status(conv.make_desc(0, 64, 9, 9, 8, 3, 3, 1, 1, conv.F16)) == 1
+    d = conv.make_desc(2, 96, 9, 9, 8, 3, 3, 1, 1, conv.F16)
+    assert conv.implicit_workspace_size(d) == 0
+    assert _lib.fwd_implicit(d, 16, 16, 16, 256, None) == 4
+    d = conv.make_desc(2, 64, 9, 9, 8, 3, 3, 1, 1, conv.F16)
+    assert _lib.fwd_implicit(d, None, 16, 16, 256, None) == 2
+    assert _lib.fwd_implicit(d, 16, 16, 16, None, None) == 5
+    assert _lib.fwd_implicit(d, 8, 16, 16, 256, None) == 3
+    assert _lib.fwd_implicit(d, 16, 16, 16, 16, None) == 3
+
+
+def test_implicit_plan_geometry():
+    """Every implicit plan: the patch holds the tile's windows, the tile's columns
+    fit its GEMM columns, LDS fits one CU, and the grid covers every output once."""
+    import numpy as np
+    rng = np.random.default_rng(11)
+    for _ in range(400):
+        KH, KW = int(rng.integers(1, 8)), int(rng.integers(1, 8))
+        s, p = int(rng.integers(1, 4)), int(rng.integers(0, 4))
+        H, W = int(rng.integers(KH, 120)), int(rng.integers(KW, 240))
+        Cin = 64 * int(rng.integers(1, 6))
+        N, Cout = int(rng.integers(1, 9)), int(rng.integers(1, 600))
+        d = conv.make_desc(N, Cin, H, W, Cout, KH, KW, s, p, [conv.F16, conv.BF16][int(rng.integers(0, 2))])
+        pl = conv.implicit_plan(d)
+        assert (pl.tile_m, pl.tile_n, pl.wave_m) in {(64, 64, 1), (64, 128, 1), (128, 64, 2), (128, 128, 2)}
+        assert pl.rows_per_tile * pl.cols_per_tile <= pl.tile_n
+        assert pl.patch_rows == (pl.rows_per_tile - 1) * s + KH
+        assert pl.patch_cols == (pl.cols_per_tile - 1) * s + KW
+        assert pl.lds_bytes == (3 * pl.tile_m + pl.patch_rows * pl.patch_cols) * 128 <= 160 * 1024
+        tiles = (-(-Cout // pl.tile_m)) * N * (-(-pl.Ho // pl.rows_per_tile)) * (-(-pl.Wo // pl.cols_per_tile))
+        assert pl.tiles == tiles
+        assert pl.K_stage == KW * KH * Cin
+        staged = not (KH == 1 and KW == 1)
+        assert (pl.ws_bytes > 0) == staged
+        if staged:
+            assert pl.ws_bytes >= Cout * pl.K_stage * 2
+
+
+def test_conv2d_plan_names_the_form_conv2d_fwd_runs(monkeypatch):
+    """algo 1 (implicit) only where the implicit form applies; its workspace is
+    then the implicit one; IM2WIN_ALGO forces either form where it applies."""
+    d = conv.make_desc(32, 64, 56, 56, 64, 3, 3, 1, 1, conv.F16)
+    p = conv.plan(d)
+    assert p.algo == 1
+    assert p.ws_bytes == conv.implicit_workspace_size(d) == conv.workspace_size(d)
+    monkeypatch.setenv("IM2WIN_ALGO", "window")
+    q = conv.plan(d)
+    assert q.algo == 0 and q.ws_bytes == q.wstage_bytes + q.win_chunk_bytes
+    monkeypatch.setenv("IM2WIN_ALGO", "implicit")
+    for args in [(2, 3, 20, 20, 16, 3, 3, 1, 1, conv.F16), (2, 64, 20, 20, 16, 3, 3, 1, 1, conv.F32),
+                 (2, 96, 20, 20, 16, 3, 3, 1, 1, conv.BF16)]:
+        assert conv.plan(conv.make_desc(*args)).algo == 0     # not applicable: stays on the window form
+    assert conv.plan(conv.make_desc(2, 256, 14, 14, 16, 3, 3, 1, 1, conv.BF16)).algo == 1
