@@ -49,7 +49,8 @@ def _say(msg):
 # sources that decide what the dominant kernel of a call does, per kernel id
 # (0: fp32 vector-ALU window-GEMM, 1: tiled matrix-core window-GEMM,
 # 2: filter-resident matrix-core window-GEMM, 3: direct-to-LDS matrix-core
-# window-GEMM, 4: implicit convolution, window rows built in LDS)
+# window-GEMM, 4: implicit convolution, window rows built in LDS, 5: the same
+# with the filter held in registers)
 GEMM_SOURCES = {
     0: ["cnn_convolution_amd/csrc/kernels/gemm_valu.hip"],
     1: ["cnn_convolution_amd/csrc/kernels/gemm_mfma.hip",
@@ -62,9 +63,11 @@ GEMM_SOURCES = {
     4: ["cnn_convolution_amd/csrc/kernels/conv_implicit.hip",
         "cnn_convolution_amd/csrc/kernels/lds_dma.hpp",
         "cnn_convolution_amd/csrc/kernels/tile_map.hpp"],
+    5: ["cnn_convolution_amd/csrc/kernels/conv_implicit_fs.hip",
+        "cnn_convolution_amd/csrc/kernels/lds_dma.hpp"],
 }
 GEMM_KERNEL_NAMES = {0: "gemm_valu_f32", 1: "gemm_mfma", 2: "gemm_mfma_resident",
-                     3: "gemm_mfma_dma", 4: "conv_implicit"}
+                     3: "gemm_mfma_dma", 4: "conv_implicit", 5: "conv_implicit_fs"}
 COPY_BYTES = 256 << 20     # calibration copy for the HBM byte counters
 
 
@@ -84,8 +87,9 @@ def dominant_key(d, plan):
     import cnn_convolution_amd as conv
     if plan.algo == 1:
         ip = conv.implicit_plan(d)
-        return (4, f"i:{ip.tile_m}x{ip.tile_n}/{ip.wave_m}/r{ip.rows_per_tile}/c{ip.cols_per_tile}",
-                plan.rows_total)
+        kid = 5 if ip.kernel == 1 else 4
+        return (kid, f"i{ip.kernel}:{ip.tile_m}x{ip.tile_n}/{ip.wave_m}/r{ip.rows_per_tile}/"
+                f"c{ip.cols_per_tile}/g{ip.tiles}", plan.rows_total)
     rows = plan.rows_total - (plan.n_chunks - 1) * plan.rows_per_chunk
     return (plan.gemm_kernel, f"k{plan.gemm_kernel}:{plan.gemm_tile_m}x{plan.gemm_tile_n}/"
             f"{plan.gemm_kslice}/{plan.gemm_ksplit}/{plan.gemm_wave_m}", rows)

@@ -31,6 +31,7 @@ SOURCES = [
     os.path.join(CSRC, "kernels", "gemm_mfma_resident.hip"),
     os.path.join(CSRC, "kernels", "gemm_mfma_dma.hip"),
     os.path.join(CSRC, "kernels", "conv_implicit.hip"),
+    os.path.join(CSRC, "kernels", "conv_implicit_fs.hip"),
 ]
 
 ARCH = "gfx950"

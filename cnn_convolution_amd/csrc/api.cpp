@@ -164,7 +164,13 @@ ImplicitArgs implicit_args(const conv2d_desc_t &d, const conv2d_implicit_plan_t 
     a.tile_n = p.tile_n;
     a.wm = p.wave_m;
     a.bf16 = d.dtype == CONV2D_BF16 ? 1 : 0;
+    a.fs_groups = int(p.tiles / ((d.Cout + 63) / 64));
     return a;
+}
+
+hipError_t launch_implicit(const conv2d_implicit_plan_t &p, const ImplicitArgs &a, hipStream_t s)
+{
+    return p.kernel == 1 ? launch_conv_implicit_fs(a, s) : launch_conv_implicit(a, s);
 }
 
 // implicit form: (a3) the filter into the window's K order (kw, kh, ci)
@@ -193,8 +199,8 @@ conv2d_status_t run_implicit(const conv2d_desc_t &d, const conv2d_implicit_plan_
         wst = ws;
     }
     ProfScope ps(s, CONV2D_KERNEL_IMPLICIT);
-    return launch_conv_implicit(implicit_args(d, p, x, wst, y), s) == hipSuccess ? CONV2D_OK
-                                                                                 : CONV2D_ERR_HIP;
+    return launch_implicit(p, implicit_args(d, p, x, wst, y), s) == hipSuccess ? CONV2D_OK
+                                                                               : CONV2D_ERR_HIP;
 }
 
 }  // namespace
@@ -407,8 +413,8 @@ conv2d_status_t im2win_implicit_gemm(const conv2d_desc_t *d, const void *x, cons
     if (!aligned(x, 16) || !aligned(wst, 16) || !aligned(y, 16)) return CONV2D_ERR_MISALIGNED;
     hipStream_t s = static_cast<hipStream_t>(stream);
     ProfScope ps(s, CONV2D_KERNEL_IMPLICIT);
-    return launch_conv_implicit(implicit_args(*d, p, x, wst, y), s) == hipSuccess ? CONV2D_OK
-                                                                                   : CONV2D_ERR_HIP;
+    return launch_implicit(p, implicit_args(*d, p, x, wst, y), s) == hipSuccess ? CONV2D_OK
+                                                                                : CONV2D_ERR_HIP;
 }
 
 conv2d_status_t conv2d_profile_enable(int32_t on)

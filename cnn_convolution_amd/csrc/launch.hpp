@@ -84,7 +84,11 @@ struct ImplicitArgs {
     int R, WB, IR, IW;
     int tile_m, tile_n, wm;
     int bf16;
+    int fs_groups;          // filter-stationary form: workgroups per 64-row filter block
 };
 hipError_t launch_conv_implicit(const ImplicitArgs &a, hipStream_t s);
+// filter-stationary form (K = KW*KH*Cin of 64, 128, 256 or 576): a 64-row
+// filter block in registers, persistent workgroups over contiguous tiles
+hipError_t launch_conv_implicit_fs(const ImplicitArgs &a, hipStream_t s);
 
 }  // namespace im2win

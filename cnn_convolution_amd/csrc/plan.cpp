@@ -320,6 +320,52 @@ conv2d_status_t make_plan(const conv2d_desc_t &d, conv2d_plan_t *p) {
 // IM2WIN_IMPLICIT_TILE="MB,NB,WM,R,WB" overrides the choice (for sweeps).
 static const int kImplicitTiles[][3] = {{64, 64, 1}, {64, 128, 1}, {128, 64, 2}, {128, 128, 2}};
 
+// Filter-stationary implicit kernel: K = KW*KH*Cin of 64, 128, 256 or 576
+// (its compiled forms); 64 GEMM columns per tile for K = 576 (the filter
+// block takes 144 registers per lane), 128 otherwise; the loads of the next
+// tile's patch are held in registers (512 row chunks of 8 channels x 8
+// columns when W is a multiple of 8, else 1536 gathered 16-byte vectors); one
+// workgroup per CU,
+// each walking a contiguous range of tiles of one 64-row filter block.
+// Opt-in (IM2WIN_IMPLICIT_KERNEL=stationary): on the measured layers it was
+// no faster than the streamed kernel (with one wave per SIMD, the per-tile
+// address arithmetic and patch packing are not hidden behind other waves).
+static void pick_implicit_fs(const conv2d_desc_t &d, int64_t Ho, int64_t Wo, conv2d_implicit_plan_t *p) {
+    const int64_t K = d.KW * d.KH * d.Cin;
+    if (K != 64 && K != 128 && K != 256 && K != 576) return;
+    const char *e = std::getenv("IM2WIN_IMPLICIT_KERNEL");
+    if (!e || std::strcmp(e, "stationary") != 0) return;
+    const int64_t nb = K == 576 ? 64 : 128;
+    const int64_t nblk = d.Cin / 64;
+    int64_t r, wb;
+    if (Wo >= nb) { r = 1; wb = nb; }
+    else { const int64_t rmax = std::min<int64_t>(Ho, nb / Wo); r = ceil_div(Ho, ceil_div(Ho, rmax)); wb = Wo; }
+    auto fits = [&](int64_t rr, int64_t ww) {
+        const int64_t ir = (rr - 1) * d.stride + d.KH, iw = (ww - 1) * d.stride + d.KW;
+        // held in registers: 16-byte row chunks of 8 channels (W a multiple of
+        // 8), or gathered patch vectors
+        const bool held = d.W % 8 == 0 ? nblk * 8 * ir * ((iw + 7) / 8 + 1) <= 512
+                                       : nblk * ir * iw * 8 <= 1536;
+        return held && implicit_fs_lds_bytes(d.Cin, ir, iw) <= kImplicitMaxLdsBytes;
+    };
+    while (!fits(r, wb) && r > 1) --r;
+    while (!fits(r, wb) && wb > 8) wb = (wb + 1) / 2;
+    if (!fits(r, wb)) return;
+    const int64_t tiles_m = ceil_div(d.Cout, 64);
+    const int64_t col_tiles = d.N * ceil_div(Ho, r) * ceil_div(Wo, wb);
+    const int64_t groups = std::min<int64_t>(col_tiles, std::max<int64_t>(1, 256 / tiles_m));
+    p->kernel = 1;
+    p->tile_m = 64;
+    p->tile_n = int32_t(nb);
+    p->wave_m = 1;
+    p->rows_per_tile = int32_t(r);
+    p->cols_per_tile = int32_t(wb);
+    p->patch_rows = int32_t((r - 1) * d.stride + d.KH);
+    p->patch_cols = int32_t((wb - 1) * d.stride + d.KW);
+    p->lds_bytes = implicit_fs_lds_bytes(d.Cin, p->patch_rows, p->patch_cols);
+    p->tiles = groups * tiles_m;
+}
+
 conv2d_status_t make_implicit_plan(const conv2d_desc_t &d, conv2d_implicit_plan_t *p) {
     const conv2d_status_t st = check_desc(d);
     if (st != CONV2D_OK) return st;
@@ -374,6 +420,7 @@ conv2d_status_t make_implicit_plan(const conv2d_desc_t &d, conv2d_implicit_plan_
         }
     }
     if (best.score < 0) return CONV2D_ERR_UNSUPPORTED;
+    p->kernel = 0;
     p->tile_m = int32_t(best.mb);
     p->tile_n = int32_t(best.nb);
     p->wave_m = int32_t(best.wm);
@@ -384,6 +431,7 @@ conv2d_status_t make_implicit_plan(const conv2d_desc_t &d, conv2d_implicit_plan_
     p->lds_bytes = implicit_lds_bytes(best.mb, p->patch_rows, p->patch_cols);
     p->tiles = ceil_div(d.Cout, best.mb) * d.N * ceil_div(Ho, best.r) * ceil_div(Wo, best.wb);
     if (p->tiles > 0x7fffffff) return CONV2D_ERR_INVALID_DESC;
+    pick_implicit_fs(d, Ho, Wo, p);
     return CONV2D_OK;
 }
 

@@ -197,7 +197,11 @@ typedef struct {
     int32_t cols_per_tile;        /* output columns wo per tile                     */
     int32_t patch_rows;           /* input rows held per tile: (rows-1)*stride + KH */
     int32_t patch_cols;           /* input columns held: (cols-1)*stride + KW       */
-    int32_t reserved;
+    int32_t kernel;               /* 0: the filter streamed through LDS per K stage,
+                                     one workgroup per tile; 1 (opt-in): filter-
+                                     stationary, KW*KH*Cin of 64, 128, 256 or 576:
+                                     a 64-row filter block in registers, workgroups
+                                     that each walk a contiguous range of tiles    */
     int64_t lds_bytes;            /* LDS per workgroup                              */
     int64_t tiles;                /* workgroups of the launch                       */
     int64_t Ho, Wo;

@@ -85,9 +85,48 @@ def test_implicit_matches_oracle(shape, dt, tile, monkeypatch):
     assert err <= TOL[dt], f"rel L2 {err:.3e} > {TOL[dt]}"
 
 
+# filter-stationary kernel (K = KW*KH*Cin of 64, 128, 256 or 576)
+FS_SHAPES = [
+    (2, 64, 9, 10, 70, 3, 3, 1, 1),      # two 64-row filter blocks
+    (4, 64, 66, 20, 256, 3, 3, 1, 1),    # more tiles than workgroups: several tiles per workgroup
+    (8, 64, 56, 56, 64, 3, 3, 1, 1),     # the ResNet layer's shape at N=8
+    (3, 256, 20, 9, 130, 1, 1, 1, 0),    # 1x1, four channel blocks, ragged Cout
+    (2, 128, 5, 9, 20, 1, 1, 1, 0),      # 1x1, two channel blocks
+    (3, 64, 4, 4, 200, 1, 1, 2, 1),      # 1x1 with stride and padding: zero border outputs
+    (1, 64, 5, 70, 8, 3, 3, 1, 1),       # column tiles along wo
+    (2, 64, 11, 12, 30, 3, 3, 2, 0),     # stride 2
+    (1, 64, 3, 3, 3, 3, 3, 1, 5),        # padding wider than the filter
+    # input rows a multiple of 8 long: the patch loaded as 16-byte row chunks
+    (2, 64, 9, 16, 70, 3, 3, 1, 1),
+    (1, 64, 5, 72, 8, 3, 3, 1, 1),       # column tiles along wo
+    (1, 64, 3, 8, 3, 3, 3, 1, 5),        # padding wider than the image: zero columns on both sides
+    (3, 64, 4, 8, 200, 1, 1, 2, 1),
+    (1, 256, 4, 16, 65, 1, 1, 1, 0),
+    (2, 64, 40, 24, 256, 3, 3, 1, 1),
+]
+
+
+@pytest.mark.parametrize("kernel", ["stationary", "streamed"])
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+@pytest.mark.parametrize("shape", FS_SHAPES)
+def test_filter_stationary_kernel_matches_oracle(shape, dt, kernel, monkeypatch):
+    monkeypatch.setenv("IM2WIN_IMPLICIT_KERNEL", kernel)
+    N, Cin, H, W, Cout, KH, KW, s, p = shape
+    d = conv.describe((N, Cin, H, W), (Cout, Cin, KH, KW), s, p, CODE[dt])
+    pl = conv.implicit_plan(d)
+    assert pl.kernel == (1 if kernel == "stationary" else 0)
+    _say(f"implicit-{kernel} {dt} {shape} workgroups={pl.tiles} lds={pl.lds_bytes}")
+    x, w = workloads.make_inputs(N, Cin, H, W, Cout, KH, KW, seed=sum(shape) + 13, dtype=dt,
+                                 w_dist="normal")
+    y = run_implicit(x, w, s, p)
+    ref = oracle.conv2d(x, w, s, p)
+    err = rel_l2(y.numpy(), ref)
+    assert err <= TOL[dt], f"rel L2 {err:.3e} > {TOL[dt]}"
+
+
 @pytest.mark.parametrize("dt", ["f16", "bf16"])
 @pytest.mark.parametrize("shape", [(2, 64, 9, 10, 70, 3, 3, 1, 1), (2, 128, 7, 6, 33, 3, 3, 2, 1),
-                                   (1, 64, 12, 12, 64, 1, 1, 1, 0)])
+                                   (1, 64, 12, 12, 64, 1, 1, 1, 0), (4, 64, 66, 20, 256, 3, 3, 1, 1)])
 def test_implicit_integer_inputs_bit_exact(shape, dt):
     N, Cin, H, W, Cout, KH, KW, s, p = shape
     _say(f"implicit-int {dt} {shape}")

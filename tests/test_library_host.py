@@ -275,26 +275,44 @@ def test_implicit_plan_takes_only_its_layers():
     assert _lib.fwd_implicit(d, 16, 16, 16, 16, None) == 3
 
 
-def test_implicit_plan_geometry():
+def test_implicit_plan_geometry(monkeypatch):
     """Every implicit plan: the patch holds the tile's windows, the tile's columns
     fit its GEMM columns, LDS fits one CU, and the grid covers every output once."""
     import numpy as np
     rng = np.random.default_rng(11)
+    monkeypatch.setenv("IM2WIN_IMPLICIT_KERNEL", "stationary")
     for _ in range(400):
         KH, KW = int(rng.integers(1, 8)), int(rng.integers(1, 8))
         s, p = int(rng.integers(1, 4)), int(rng.integers(0, 4))
         H, W = int(rng.integers(KH, 120)), int(rng.integers(KW, 240))
         Cin = 64 * int(rng.integers(1, 6))
+        if rng.integers(0, 3) == 0:       # short K: the filter-stationary kernel (opt-in)
+            KH, KW = [(3, 3), (1, 1), (1, 1)][int(rng.integers(0, 3))]
+            Cin = 64 if KH == 3 else int(rng.choice([64, 128, 256]))
+            H, W = max(H, KH), max(W, KW)
         N, Cout = int(rng.integers(1, 9)), int(rng.integers(1, 600))
         d = conv.make_desc(N, Cin, H, W, Cout, KH, KW, s, p, [conv.F16, conv.BF16][int(rng.integers(0, 2))])
         pl = conv.implicit_plan(d)
-        assert (pl.tile_m, pl.tile_n, pl.wave_m) in {(64, 64, 1), (64, 128, 1), (128, 64, 2), (128, 128, 2)}
         assert pl.rows_per_tile * pl.cols_per_tile <= pl.tile_n
         assert pl.patch_rows == (pl.rows_per_tile - 1) * s + KH
         assert pl.patch_cols == (pl.cols_per_tile - 1) * s + KW
-        assert pl.lds_bytes == (3 * pl.tile_m + pl.patch_rows * pl.patch_cols) * 128 <= 160 * 1024
-        tiles = (-(-Cout // pl.tile_m)) * N * (-(-pl.Ho // pl.rows_per_tile)) * (-(-pl.Wo // pl.cols_per_tile))
-        assert pl.tiles == tiles
+        col_tiles = N * (-(-pl.Ho // pl.rows_per_tile)) * (-(-pl.Wo // pl.cols_per_tile))
+        K = KH * KW * Cin
+        if pl.kernel == 1:
+            # filter-stationary: compiled K, 64-row blocks, patch in registers, 1 workgroup per CU
+            assert K in (64, 128, 256, 576) and pl.tile_m == 64
+            assert pl.tile_n == (64 if K == 576 else 128)
+            if W % 8 == 0:
+                assert (Cin // 64) * 8 * pl.patch_rows * ((pl.patch_cols + 7) // 8 + 1) <= 512
+            else:
+                assert (Cin // 64) * pl.patch_rows * pl.patch_cols * 8 <= 1536
+            assert pl.lds_bytes == 2 * (Cin // 64) * pl.patch_rows * pl.patch_cols * 128 <= 160 * 1024
+            tiles_m = -(-Cout // 64)
+            assert pl.tiles == tiles_m * min(col_tiles, max(1, 256 // tiles_m))
+        else:
+            assert (pl.tile_m, pl.tile_n, pl.wave_m) in {(64, 64, 1), (64, 128, 1), (128, 64, 2), (128, 128, 2)}
+            assert pl.lds_bytes == (3 * pl.tile_m + pl.patch_rows * pl.patch_cols) * 128 <= 160 * 1024
+            assert pl.tiles == (-(-Cout // pl.tile_m)) * col_tiles
         assert pl.K_stage == KW * KH * Cin
         staged = not (KH == 1 and KW == 1)
         assert (pl.ws_bytes > 0) == staged
