@@ -163,6 +163,7 @@ ImplicitArgs implicit_args(const conv2d_desc_t &d, const conv2d_implicit_plan_t 
     a.tile_m = p.tile_m;
     a.tile_n = p.tile_n;
     a.wm = p.wave_m;
+    a.stages = p.stages;
     a.bf16 = d.dtype == CONV2D_BF16 ? 1 : 0;
     a.fs_groups = int(p.tiles / ((d.Cout + 63) / 64));
     return a;

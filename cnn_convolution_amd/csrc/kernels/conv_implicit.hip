@@ -51,7 +51,7 @@ struct ImplicitKArgs {
     int tiles_ho, tiles_wo, tiles_m;
 };
 
-template <int MB, int NB, int WM, bool BF16>
+template <int MB, int NB, int WM, int NS, bool BF16>
 __global__ __launch_bounds__(256) void conv_implicit_kernel(const ImplicitKArgs a)
 {
     constexpr int WN = 4 / WM;
@@ -61,11 +61,10 @@ __global__ __launch_bounds__(256) void conv_implicit_kernel(const ImplicitKArgs 
     constexpr int D = AI;                  // copies per wave per stage
     static_assert(AI >= 1 && AI * 32 == MB, "tiling");
     static_assert(FM >= 1 && FN >= 1 && WM * WN == 4, "wave layout");
+    static_assert(NS >= 3 && (NS - 2) * D < 64, "stage buffers");
     extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
-    uint16_t *const sa0 = lds;
-    uint16_t *const sa1 = lds + MB * KI;
-    uint16_t *const sa2 = lds + 2 * MB * KI;
-    uint16_t *const patch = lds + 3 * MB * KI;
+    auto sbuf = [&](int b) { return lds + b * MB * KI; };   // filter stage buffer b < NS
+    uint16_t *const patch = lds + NS * MB * KI;
 
     int tm, tn;
     tile_coords(blockIdx.x, gridDim.x, a.tiles_m, tm, tn);
@@ -197,31 +196,33 @@ __global__ __launch_bounds__(256) void conv_implicit_kernel(const ImplicitKArgs 
         }
     };
 
-    // the same three-buffer filter pipeline as the direct-to-LDS window-GEMM;
-    // at the first tap of a channel block (after the barrier that ends every
-    // wave's reads of the previous block) the patch is rebuilt and published
-    // by a second barrier
+    // the filter pipeline of the direct-to-LDS window-GEMM with NS stage
+    // buffers: NS-1 stages in flight, each wave waiting only for its own
+    // oldest one (every step issues one group, the stage index clamped to the
+    // last, so the count in flight is the same at every step); at the first
+    // tap of a channel block (after the barrier that ends every wave's reads
+    // of the previous block) the patch is rebuilt and published by a second
+    // barrier
     build_patch(0);
-    issue(0, sa0);
-    issue(min(1, nk - 1), sa1);
-    auto step = [&](int k, uint16_t *ca, uint16_t *na) {
-        wait_vm<D>();
+#pragma unroll
+    for (int b = 0; b < NS - 1; ++b) issue(min(b, nk - 1), sbuf(b));
+    auto step = [&](int k, int b) {
+        wait_vm<(NS - 2) * D>();
         stage_barrier();
         if (k > 0 && k % taps == 0) {
             build_patch(k / taps);
             stage_barrier();
         }
-        issue(min(k + 2, nk - 1), na);
-        compute(k, ca);
+        issue(min(k + NS - 1, nk - 1), sbuf((b + NS - 1) % NS));   // the buffer stage k-1 used
+        compute(k, sbuf(b));
         __builtin_amdgcn_sched_barrier(0);
     };
-    for (int k = 0;; k += 3) {
-        step(k, sa0, sa2);
-        if (k + 1 >= nk) break;
-        step(k + 1, sa1, sa0);
-        if (k + 2 >= nk) break;
-        step(k + 2, sa2, sa1);
-        if (k + 3 >= nk) break;
+    // unrolled by NS so that every buffer is named statically; the exit test
+    // is uniform and the accumulators stay in the same registers
+    for (int k = 0; k < nk; k += NS) {
+#pragma unroll
+        for (int b = 0; b < NS; ++b)
+            if (k + b < nk) step(k + b, b);
     }
     wait_vm<0>();
 
@@ -246,7 +247,7 @@ __global__ __launch_bounds__(256) void conv_implicit_kernel(const ImplicitKArgs 
     }
 }
 
-template <int MB, int NB, int WM>
+template <int MB, int NB, int WM, int NS>
 hipError_t launch_implicit_tile(const ImplicitArgs &h, hipStream_t s)
 {
     ImplicitKArgs a{};
@@ -273,8 +274,8 @@ hipError_t launch_implicit_tile(const ImplicitArgs &h, hipStream_t s)
     a.tiles_m = (h.Cout + MB - 1) / MB;
     const int64_t tiles = int64_t(a.tiles_m) * h.N * a.tiles_ho * a.tiles_wo;
     if (tiles < 1 || tiles > 0x7fffffff) return hipErrorInvalidValue;
-    const size_t lds = implicit_lds_bytes(MB, h.IR, h.IW);
-    auto kern = h.bf16 ? conv_implicit_kernel<MB, NB, WM, true> : conv_implicit_kernel<MB, NB, WM, false>;
+    const size_t lds = implicit_lds_bytes(MB, h.IR, h.IW, NS);
+    auto kern = h.bf16 ? conv_implicit_kernel<MB, NB, WM, NS, true> : conv_implicit_kernel<MB, NB, WM, NS, false>;
     if (lds > 64 * 1024) {
         const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                                  hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -292,12 +293,20 @@ hipError_t launch_conv_implicit(const ImplicitArgs &h, hipStream_t s)
     // channel blocks of 64, a patch that holds every window of the tile
     if (h.Cin % KI != 0 || h.R < 1 || h.WB < 1 || h.IR < (h.R - 1) * h.stride + h.KH ||
         h.IW < (h.WB - 1) * h.stride + h.KW || h.kstage != h.KW * h.KH * h.Cin ||
-        h.tile_n < h.R * h.WB || implicit_lds_bytes(h.tile_m, h.IR, h.IW) > kImplicitMaxLdsBytes)
+        h.tile_n < h.R * h.WB || h.stages < 3 || h.stages > 5 ||
+        implicit_lds_bytes(h.tile_m, h.IR, h.IW, h.stages) > kImplicitMaxLdsBytes)
         return hipErrorInvalidValue;
-    if (h.tile_m == 64 && h.tile_n == 64 && h.wm == 1) return launch_implicit_tile<64, 64, 1>(h, s);
-    if (h.tile_m == 64 && h.tile_n == 128 && h.wm == 1) return launch_implicit_tile<64, 128, 1>(h, s);
-    if (h.tile_m == 128 && h.tile_n == 64 && h.wm == 2) return launch_implicit_tile<128, 64, 2>(h, s);
-    if (h.tile_m == 128 && h.tile_n == 128 && h.wm == 2) return launch_implicit_tile<128, 128, 2>(h, s);
+#define IM2WIN_IMPLICIT_TILE(M, N, W)                                                              \
+    if (h.tile_m == M && h.tile_n == N && h.wm == W) {                                            \
+        if (h.stages == 5) return launch_implicit_tile<M, N, W, 5>(h, s);                          \
+        if (h.stages == 4) return launch_implicit_tile<M, N, W, 4>(h, s);                          \
+        return launch_implicit_tile<M, N, W, 3>(h, s);                                             \
+    }
+    IM2WIN_IMPLICIT_TILE(64, 64, 1)
+    IM2WIN_IMPLICIT_TILE(64, 128, 1)
+    IM2WIN_IMPLICIT_TILE(128, 64, 2)
+    IM2WIN_IMPLICIT_TILE(128, 128, 2)
+#undef IM2WIN_IMPLICIT_TILE
     return hipErrorInvalidValue;
 }
 

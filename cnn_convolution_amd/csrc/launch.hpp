@@ -83,6 +83,7 @@ struct ImplicitArgs {
     int kstage;             // KW*KH*Cin
     int R, WB, IR, IW;
     int tile_m, tile_n, wm;
+    int stages;             // filter stage buffers (3, 4 or 5)
     int bf16;
     int fs_groups;          // filter-stationary form: workgroups per 64-row filter block
 };

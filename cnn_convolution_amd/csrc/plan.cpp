@@ -213,17 +213,23 @@ static void pick_mfma_dma(const conv2d_desc_t &d, int64_t krun, int64_t cols, co
 }
 
 // What conv2d_fwd runs for a matrix-core layer. The implicit form (window
-// rows built in LDS, no window tensor) measured faster for 3x3-class filters
-// (2 to 9 taps) with one or two 64-channel blocks: it skips the window
-// tensor's HBM round trip, and with few blocks its per-block patch load is
-// rarely exposed. With more channel blocks, one tap or larger filters the
-// window tensor path was faster on the measured layers.
+// rows built in LDS, no window tensor) skips the window tensor's HBM round
+// trip and measured faster on the stride-1 layers of the sweep (3x3, 5x5,
+// 1x1, 512-channel 7x7, the Table I 3x3 layers) where its tiles fill at
+// least 70 % of their GEMM columns; it lost where they do not (5x5 outputs),
+// with stride 2 (a patch of 2R+1 input rows per R window rows) and for a 7x7
+// filter (a patch that leaves one workgroup per CU).
 // IM2WIN_ALGO=window|implicit overrides (implicit only where it applies).
 static void pick_algo(const conv2d_desc_t &d, conv2d_plan_t *p) {
     conv2d_implicit_plan_t ip;
     const bool can = make_implicit_plan(d, &ip) == CONV2D_OK;
     const int64_t taps = d.KH * d.KW;
-    bool use = can && d.Cin <= 128 && taps >= 2 && taps <= 9;
+    bool use = false;
+    if (can && ip.kernel == 0 && d.stride == 1 && taps <= 25) {
+        const double fill = double(p->Ho * p->Wo) /
+            double(ceil_div(p->Ho, ip.rows_per_tile) * ceil_div(p->Wo, ip.cols_per_tile) * ip.tile_n);
+        use = fill >= 0.7;
+    }
     if (const char *e = std::getenv("IM2WIN_ALGO")) {
         if (std::strcmp(e, "window") == 0) use = false;
         if (std::strcmp(e, "implicit") == 0) use = can;
@@ -386,7 +392,7 @@ conv2d_status_t make_implicit_plan(const conv2d_desc_t &d, conv2d_implicit_plan_
     auto consider = [&](int64_t mb, int64_t nb, int64_t wm, int64_t r, int64_t wb) {
         if (r < 1 || wb < 1 || r * wb > nb) return;
         const int64_t ir = (r - 1) * d.stride + d.KH, iw = (wb - 1) * d.stride + d.KW;
-        const int64_t lds = implicit_lds_bytes(mb, ir, iw);
+        const int64_t lds = implicit_lds_bytes(mb, ir, iw, 3);
         if (lds > kImplicitMaxLdsBytes) return;
         const double cols = double(Ho * Wo) / double(ceil_div(Ho, r) * ceil_div(Wo, wb) * nb);
         const double rowsm = double(d.Cout) / double(ceil_div(d.Cout, mb) * mb);
@@ -415,7 +421,7 @@ conv2d_status_t make_implicit_plan(const conv2d_desc_t &d, conv2d_implicit_plan_
             for (const auto &t : kImplicitTiles) known = known || (t[0] == m && t[1] == n && t[2] == w);
             const int64_t ir = (r - 1) * d.stride + d.KH, iw = (int64_t(b) - 1) * d.stride + d.KW;
             if (known && r >= 1 && b >= 1 && int64_t(r) * b <= n &&
-                implicit_lds_bytes(m, ir, iw) <= kImplicitMaxLdsBytes)
+                implicit_lds_bytes(m, ir, iw, 3) <= kImplicitMaxLdsBytes)
                 best = Cand{m, n, w, r, b, 1.0};
         }
     }
@@ -428,7 +434,19 @@ conv2d_status_t make_implicit_plan(const conv2d_desc_t &d, conv2d_implicit_plan_
     p->cols_per_tile = int32_t(best.wb);
     p->patch_rows = int32_t((best.r - 1) * d.stride + d.KH);
     p->patch_cols = int32_t((best.wb - 1) * d.stride + d.KW);
-    p->lds_bytes = implicit_lds_bytes(best.mb, p->patch_rows, p->patch_cols);
+    // filter stage buffers: three (two stages in flight); four for 128-row
+    // tiles when two workgroups still fit a CU (measured 2-3 % faster there,
+    // no gain for 64-row tiles); IM2WIN_IMPLICIT_STAGES=3|4|5 overrides
+    int ns = 3;
+    if (best.mb == 128 && implicit_lds_bytes(best.mb, p->patch_rows, p->patch_cols, 4) <= kImplicitPairLdsBytes)
+        ns = 4;
+    if (const char *e = std::getenv("IM2WIN_IMPLICIT_STAGES")) {
+        const int v = std::atoi(e);
+        if (v >= 3 && v <= 5 && implicit_lds_bytes(best.mb, p->patch_rows, p->patch_cols, v) <= kImplicitMaxLdsBytes)
+            ns = v;
+    }
+    p->stages = ns;
+    p->lds_bytes = implicit_lds_bytes(best.mb, p->patch_rows, p->patch_cols, ns);
     p->tiles = ceil_div(d.Cout, best.mb) * d.N * ceil_div(Ho, best.r) * ceil_div(Wo, best.wb);
     if (p->tiles > 0x7fffffff) return CONV2D_ERR_INVALID_DESC;
     pick_implicit_fs(d, Ho, Wo, p);

@@ -202,6 +202,9 @@ typedef struct {
                                      stationary, KW*KH*Cin of 64, 128, 256 or 576:
                                      a 64-row filter block in registers, workgroups
                                      that each walk a contiguous range of tiles    */
+    int32_t stages;               /* kernel 0: filter K stages in flight + 1 (LDS
+                                     stage buffers)                                 */
+    int32_t reserved;
     int64_t lds_bytes;            /* LDS per workgroup                              */
     int64_t tiles;                /* workgroups of the launch                       */
     int64_t Ho, Wo;

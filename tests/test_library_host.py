@@ -311,7 +311,10 @@ def test_implicit_plan_geometry(monkeypatch):
             assert pl.tiles == tiles_m * min(col_tiles, max(1, 256 // tiles_m))
         else:
             assert (pl.tile_m, pl.tile_n, pl.wave_m) in {(64, 64, 1), (64, 128, 1), (128, 64, 2), (128, 128, 2)}
-            assert pl.lds_bytes == (3 * pl.tile_m + pl.patch_rows * pl.patch_cols) * 128 <= 160 * 1024
+            assert 3 <= pl.stages <= 5
+            assert pl.lds_bytes == (pl.stages * pl.tile_m + pl.patch_rows * pl.patch_cols) * 128 <= 160 * 1024
+            if pl.stages > 3:
+                assert pl.lds_bytes <= 80 * 1024
             assert pl.tiles == (-(-Cout // pl.tile_m)) * col_tiles
         assert pl.K_stage == KW * KH * Cin
         staged = not (KH == 1 and KW == 1)
