@@ -2,6 +2,7 @@
 #include "plan.hpp"
 
 #include <algorithm>
+#include <cmath>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -321,8 +322,9 @@ conv2d_status_t make_plan(const conv2d_desc_t &d, conv2d_plan_t *p) {
 // Implicit form. A tile covers R window rows x WB output columns of one
 // image (R*WB <= NB GEMM columns); its patch holds IR = (R-1)*s + KH input
 // rows x IW = (WB-1)*s + KW input columns of one 64-channel block. Candidates
-// are scored by the share of the NB columns that are real outputs, with a
-// penalty when the LDS of a workgroup leaves room for only one per CU.
+// are scored by the share of the tile that is real outputs, the tile size,
+// the number of tiles per CU, and a penalty when the LDS of a workgroup
+// leaves room for only one per CU.
 // IM2WIN_IMPLICIT_TILE="MB,NB,WM,R,WB" overrides the choice (for sweeps).
 static const int kImplicitTiles[][3] = {{64, 64, 1}, {64, 128, 1}, {128, 64, 2}, {128, 128, 2}};
 
@@ -396,11 +398,16 @@ conv2d_status_t make_implicit_plan(const conv2d_desc_t &d, conv2d_implicit_plan_
         if (lds > kImplicitMaxLdsBytes) return;
         const double cols = double(Ho * Wo) / double(ceil_div(Ho, r) * ceil_div(Wo, wb) * nb);
         const double rowsm = double(d.Cout) / double(ceil_div(d.Cout, mb) * mb);
-        double score = cols * rowsm;
+        const double tiles = double(ceil_div(d.Cout, mb) * d.N * ceil_div(Ho, r) * ceil_div(Wo, wb));
+        // share of real outputs, a mild preference for larger tiles (less
+        // per-tile set-up per output), and a penalty below ~1.5 tiles per CU;
+        // fitted to a sweep of every tile on the measured layers
+        double score = cols * rowsm * std::pow(double(mb * nb) / 8192.0, 0.2) *
+                       std::sqrt(std::min(1.0, tiles / 384.0));
         if (lds > kImplicitPairLdsBytes) score *= 0.8;
-        if (mb == 128) score *= 1.05;          // fewer filter re-reads per output
-        if (nb == 128) score *= 1.05;
-        if (score > best.score) best = Cand{mb, nb, wm, r, wb, score};
+        // ties go to the taller tile (each filter row read by fewer tiles)
+        const bool tie = std::fabs(score - best.score) <= 1e-9 * best.score;
+        if ((score > best.score && !tie) || (tie && mb > best.mb)) best = Cand{mb, nb, wm, r, wb, score};
     };
     for (const auto &t : kImplicitTiles) {
         const int64_t mb = t[0], nb = t[1], wm = t[2];
