@@ -231,9 +231,14 @@ __global__ __launch_bounds__(256) void pack_cl_staged_kernel(
 {
     extern __shared__ __attribute__((aligned(16))) uint16_t run[];   // [cblk][cp]
     if (int(blockIdx.x) < fs.blocks) {            // filter staging carried by this launch
-        stage_cl_elems(static_cast<const uint16_t *>(fs.w), static_cast<uint16_t *>(fs.out), fs.Cout,
-                       fs.Cin, fs.KH, fs.KW, fs.Cin_pad, fs.row_len,
-                       blockIdx.x * 256u + threadIdx.x, unsigned(fs.blocks) * 256u);
+        if (fs.Cin_pad % 8 == 0 && fs.row_len % 8 == 0)
+            stage_cl_vec8(static_cast<const uint16_t *>(fs.w), static_cast<uint16_t *>(fs.out), fs.Cout,
+                          fs.Cin, fs.KH, fs.KW, fs.Cin_pad, fs.row_len,
+                          blockIdx.x * 256u + threadIdx.x, unsigned(fs.blocks) * 256u);
+        else
+            stage_cl_elems(static_cast<const uint16_t *>(fs.w), static_cast<uint16_t *>(fs.out), fs.Cout,
+                           fs.Cin, fs.KH, fs.KW, fs.Cin_pad, fs.row_len,
+                           blockIdx.x * 256u + threadIdx.x, unsigned(fs.blocks) * 256u);
         return;
     }
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);

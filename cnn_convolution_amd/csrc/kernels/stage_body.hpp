@@ -63,4 +63,36 @@ __device__ __forceinline__ void stage_cl_elems(const E *__restrict__ w, E *__res
     }
 }
 
+// Channels-last order, 16 bytes at a time: one 8-channel group of one
+// filter position per step, gathered from w with the channel stride KH*KW
+// and stored as one 16-byte vector. For 16-bit elements with Cin_pad and
+// row_len multiples of 8 (out rows 16-byte aligned); the caller checks.
+__device__ __forceinline__ void stage_cl_vec8(const uint16_t *__restrict__ w, uint16_t *__restrict__ out,
+                                              int Cout, int Cin, int KH, int KW, int Cin_pad, int row_len,
+                                              unsigned first, unsigned step)
+{
+    const int krun = KW * KH * Cin_pad;
+    const int gpr = row_len >> 3;                 // 8-element groups per row
+    const unsigned total = unsigned(Cout) * unsigned(gpr);
+    const int taps = KH * KW;
+    for (unsigned gi = first; gi < total; gi += step) {
+        const int co = int(gi / unsigned(gpr));
+        const int k = (int(gi) - co * gpr) * 8;
+        uint32_t v[4] = {0u, 0u, 0u, 0u};
+        if (k < krun) {
+            const int pos = k / Cin_pad;
+            const int ci0 = k - pos * Cin_pad;
+            const int kw = pos / KH;
+            const int kh = pos - kw * KH;
+            const uint16_t *src = w + (co * Cin + ci0) * taps + kh * KW + kw;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t h = ci0 + e < Cin ? uint32_t(src[e * taps]) : 0u;
+                v[e >> 1] |= h << (16 * (e & 1));
+            }
+        }
+        *reinterpret_cast<uint4 *>(out + size_t(co) * row_len + k) = uint4{v[0], v[1], v[2], v[3]};
+    }
+}
+
 }  // namespace im2win

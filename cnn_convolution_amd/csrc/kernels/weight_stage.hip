@@ -39,6 +39,14 @@ __global__ __launch_bounds__(256) void stage_cl_kernel(const E *__restrict__ w, 
                    blockIdx.x * blockDim.x + threadIdx.x, gridDim.x * blockDim.x);
 }
 
+__global__ __launch_bounds__(256) void stage_cl_vec8_kernel(const uint16_t *__restrict__ w,
+                                                            uint16_t *__restrict__ out, int Cout, int Cin,
+                                                            int KH, int KW, int Cin_pad, int row_len)
+{
+    stage_cl_vec8(w, out, Cout, Cin, KH, KW, Cin_pad, row_len, blockIdx.x * blockDim.x + threadIdx.x,
+                  gridDim.x * blockDim.x);
+}
+
 unsigned grid_for(int64_t total)
 {
     int64_t b = (total + 255) / 256;
@@ -66,6 +74,13 @@ hipError_t launch_stage_row(const StageArgs &a, hipStream_t s)
 
 hipError_t launch_stage_cl(const StageArgs &a, hipStream_t s)
 {
+    if (a.esize == 2 && a.Cin_pad % 8 == 0 && a.row_len % 8 == 0) {
+        // one 16-byte output vector per thread
+        hipLaunchKernelGGL(stage_cl_vec8_kernel, dim3(grid_for(int64_t(a.Cout) * (a.row_len / 8))), dim3(256),
+                           0, s, static_cast<const uint16_t *>(a.w), static_cast<uint16_t *>(a.out),
+                           a.Cout, a.Cin, a.KH, a.KW, a.Cin_pad, a.row_len);
+        return hipGetLastError();
+    }
     const dim3 grid(grid_for(int64_t(a.rows) * a.row_len));
     if (a.esize == 4)
         hipLaunchKernelGGL(stage_cl_kernel<uint32_t>, grid, dim3(256), 0, s,
