@@ -50,7 +50,8 @@ def _say(msg):
 # (0: fp32 vector-ALU window-GEMM, 1: tiled matrix-core window-GEMM,
 # 2: filter-resident matrix-core window-GEMM, 3: direct-to-LDS matrix-core
 # window-GEMM, 4: implicit convolution, window rows built in LDS, 5: the same
-# with the filter held in registers)
+# with the filter held in registers, 6: the row-block implicit kernel, filter
+# and input rows resident in LDS)
 GEMM_SOURCES = {
     0: ["cnn_convolution_amd/csrc/kernels/gemm_valu.hip"],
     1: ["cnn_convolution_amd/csrc/kernels/gemm_mfma.hip",
@@ -65,9 +66,13 @@ GEMM_SOURCES = {
         "cnn_convolution_amd/csrc/kernels/tile_map.hpp"],
     5: ["cnn_convolution_amd/csrc/kernels/conv_implicit_fs.hip",
         "cnn_convolution_amd/csrc/kernels/lds_dma.hpp"],
+    6: ["cnn_convolution_amd/csrc/kernels/conv_implicit_rows.hip",
+        "cnn_convolution_amd/csrc/kernels/lds_dma.hpp",
+        "cnn_convolution_amd/csrc/kernels/tile_map.hpp"],
 }
 GEMM_KERNEL_NAMES = {0: "gemm_valu_f32", 1: "gemm_mfma", 2: "gemm_mfma_resident",
-                     3: "gemm_mfma_dma", 4: "conv_implicit", 5: "conv_implicit_fs"}
+                     3: "gemm_mfma_dma", 4: "conv_implicit", 5: "conv_implicit_fs",
+                     6: "conv_implicit_rows"}
 COPY_BYTES = 256 << 20     # calibration copy for the HBM byte counters
 
 
@@ -87,7 +92,7 @@ def dominant_key(d, plan):
     import cnn_convolution_amd as conv
     if plan.algo == 1:
         ip = conv.implicit_plan(d)
-        kid = 5 if ip.kernel == 1 else 4
+        kid = {0: 4, 1: 5, 2: 6}[ip.kernel]
         return (kid, f"i{ip.kernel}:{ip.tile_m}x{ip.tile_n}/{ip.wave_m}/r{ip.rows_per_tile}/"
                 f"c{ip.cols_per_tile}/g{ip.tiles}", plan.rows_total)
     rows = plan.rows_total - (plan.n_chunks - 1) * plan.rows_per_chunk

@@ -32,6 +32,7 @@ SOURCES = [
     os.path.join(CSRC, "kernels", "gemm_mfma_dma.hip"),
     os.path.join(CSRC, "kernels", "conv_implicit.hip"),
     os.path.join(CSRC, "kernels", "conv_implicit_fs.hip"),
+    os.path.join(CSRC, "kernels", "conv_implicit_rows.hip"),
 ]
 
 ARCH = "gfx950"

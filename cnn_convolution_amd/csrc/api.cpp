@@ -171,6 +171,7 @@ ImplicitArgs implicit_args(const conv2d_desc_t &d, const conv2d_implicit_plan_t 
 
 hipError_t launch_implicit(const conv2d_implicit_plan_t &p, const ImplicitArgs &a, hipStream_t s)
 {
+    if (p.kernel == 2) return launch_conv_implicit_rows(a, s);
     return p.kernel == 1 ? launch_conv_implicit_fs(a, s) : launch_conv_implicit(a, s);
 }
 

@@ -1,0 +1,286 @@
+// fp16 / bf16 implicit im2win convolution, row-block form, for layers with
+// 64 input channels, stride 1, input rows a multiple of 8 long and output
+// rows of at most 64 columns (the ResNet-style 3x3 and 1x1 layers).
+//
+// A workgroup of eight waves owns a block of RW consecutive output rows
+// (n, ho0 .. ho0+RW-1) of one image and a block of 64 output channels. The
+// window rows of those output rows (Eq. (2) of "Enabling Memory-efficient
+// Im2win Convolution with Multi-precision Support on GPU CUDA and Tensor
+// Cores", Sec. III-B: window row ho interleaves input rows ho - pad .. ho -
+// pad + KH - 1) share all but their first and last input rows, so the block
+// holds the union once: SL = RW + KH - 1 input rows of IW = W + 2*pad
+// positions (zero padding included), channels innermost, one 128-byte LDS
+// row per position (8-channel granule g of position q in slot g ^ (q & 7),
+// so reads of consecutive positions hit different bank groups). The window
+// of output column wo of row i at filter tap (kh, kw) is position
+// (i + kh, wo + kw).
+//
+// The filter block stays in LDS for the whole contraction: w[co][ci][kh][kw]
+// is read as it is stored (8 channels x all taps of one output channel per
+// thread, 16-byte loads), reordered in registers into one 64-channel run per
+// tap (the window's K order of Sec. III-D: taps outer, channels inner), and
+// written once. Nothing is staged in device memory.
+//
+// Every load of the block is issued before the first wait (the filter and
+// the input rows, 16-byte loads of 8 consecutive columns of one channel,
+// transposed 8 x 8 in registers with byte permutes into 8 channels of one
+// position), then one barrier; after it wave i contracts output row i on its
+// own (no further barrier): the product is formed transposed, D[column][co],
+// so that a lane holds 4 consecutive output columns of one channel and
+// stores them as one 16-byte vector.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "../launch.hpp"
+#include "lds_dma.hpp"
+#include "tile_map.hpp"
+
+namespace im2win {
+namespace {
+
+constexpr int kRowsThreads = 512;   // eight waves: one output row each
+
+struct RowsKArgs {
+    const uint16_t *x;
+    const uint16_t *w;
+    float *y;
+    int H, W, Cout, pad, Ho, Wo;
+    int RW;                 // output rows per workgroup
+    int row_groups;         // ceil(Ho / RW)
+    int co_blocks;          // ceil(Cout / 64)
+    int IW;                 // W + 2*pad
+};
+
+// 16-bit element e (0..7) of a 16-byte vector, as the low half of a dword
+__device__ __forceinline__ uint32_t dword_of(const uint4 &v, int d)
+{
+    return d == 0 ? v.x : d == 1 ? v.y : d == 2 ? v.z : v.w;
+}
+
+template <int KH, int KW, bool BF16>
+__global__ __launch_bounds__(kRowsThreads) void conv_implicit_rows_kernel(const RowsKArgs a)
+{
+    constexpr int TAPS = KH * KW;
+    constexpr int CIN = 64;
+    extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
+    uint16_t *const fl = lds;                        // [TAPS][64 co][64 ci], 8 KB per tap
+    uint16_t *const patch = lds + TAPS * 64 * CIN;   // [SL][IW][64 ci]
+
+    int cb, tn;
+    tile_coords(blockIdx.x, gridDim.x, a.co_blocks, cb, tn);
+    const int rg = tn % a.row_groups;
+    const int n = tn / a.row_groups;
+    const int ho0 = rg * a.RW;
+    const int rw = min(a.RW, a.Ho - ho0);            // rows of this block
+    const int SL = rw + KH - 1;                      // input rows held
+    const int ih0 = ho0 - a.pad;
+    const int tid = threadIdx.x;
+    const int HW = a.H * a.W;
+    const uint16_t *const ximg = a.x + int64_t(n) * CIN * HW;
+
+    // ---- issue every load of the block -------------------------------------
+    // filter: thread = (output channel co_l, 8-channel group cg); its 8 x TAPS
+    // halves w[co][cg*8 .. cg*8+7][taps] are contiguous (16*TAPS bytes)
+    const int co_l = tid >> 3;
+    const int cg = tid & 7;
+    const int co_src = min(cb * 64 + co_l, a.Cout - 1);  // rows past Cout: never stored
+    uint4 wraw[TAPS];
+    {
+        const uint4 *src = reinterpret_cast<const uint4 *>(a.w + (int64_t(co_src) * CIN + cg * 8) * TAPS);
+#pragma unroll
+        for (int i = 0; i < TAPS; ++i) wraw[i] = src[i];
+    }
+    // input rows: units of (input row i, chunk k of 8 columns, 8-channel group
+    // g), g fastest so that the 8 lanes writing one position hit 8 different
+    // bank groups; a wave's load of channel g*8+e covers 8 consecutive chunks
+    const int CW = a.W >> 3;
+    const int units = SL * CW * 8;
+    auto unit_src = [&](int u, int &i, int &k, int &g, bool &in) {
+        g = u & 7;
+        const int r = u >> 3;
+        i = r / CW;
+        k = r - i * CW;
+        in = unsigned(ih0 + i) < unsigned(a.H);
+    };
+    uint4 xraw[8];
+    int ui, uk, ug;
+    bool uin;
+    {
+        const int u = min(tid, units - 1);
+        unit_src(u, ui, uk, ug, uin);
+        const uint4 *src = reinterpret_cast<const uint4 *>(
+            ximg + int64_t(ug * 8) * HW + int64_t(uin ? ih0 + ui : 0) * a.W + uk * 8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) xraw[e] = src[int64_t(e) * (HW >> 3)];
+    }
+
+    // ---- filter: one 16-byte vector per tap, 8 channels of co_l -------------
+    // (element e of tap t is half e*TAPS + t of the 8*TAPS run)
+#pragma unroll
+    for (int t = 0; t < TAPS; ++t) {
+        uint32_t o[4];
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            const int p0 = (2 * d) * TAPS + t, p1 = (2 * d + 1) * TAPS + t;
+            const uint32_t s0 = dword_of(wraw[p0 >> 3], (p0 & 7) >> 1);
+            const uint32_t s1 = dword_of(wraw[p1 >> 3], (p1 & 7) >> 1);
+            const uint32_t sel = ((p0 & 1) ? 0x0302u : 0x0100u) | ((p1 & 1) ? 0x07060000u : 0x05040000u);
+            o[d] = __builtin_amdgcn_perm(s1, s0, sel);
+        }
+        *reinterpret_cast<uint4 *>(fl + t * 64 * CIN + co_l * CIN + ((cg ^ (co_l & 7)) << 3)) =
+            uint4{o[0], o[1], o[2], o[3]};
+    }
+
+    // ---- input rows: 8 x 8 transpose into 8 positions of one granule ---------
+    auto put_unit = [&](int i, int k, int g, bool in, const uint4 *raw) {
+        const int qrow = i * a.IW + a.pad + k * 8;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+            uint4 o;
+            o.x = in ? __builtin_amdgcn_perm(dword_of(raw[1], j >> 1), dword_of(raw[0], j >> 1), sel) : 0u;
+            o.y = in ? __builtin_amdgcn_perm(dword_of(raw[3], j >> 1), dword_of(raw[2], j >> 1), sel) : 0u;
+            o.z = in ? __builtin_amdgcn_perm(dword_of(raw[5], j >> 1), dword_of(raw[4], j >> 1), sel) : 0u;
+            o.w = in ? __builtin_amdgcn_perm(dword_of(raw[7], j >> 1), dword_of(raw[6], j >> 1), sel) : 0u;
+            const int q = qrow + j;
+            *reinterpret_cast<uint4 *>(patch + q * CIN + ((g ^ (q & 7)) << 3)) = o;
+        }
+    };
+    if (tid < units) put_unit(ui, uk, ug, uin, xraw);
+    for (int u = tid + kRowsThreads; u < units; u += kRowsThreads) {
+        int i, k, g;
+        bool in;
+        unit_src(u, i, k, g, in);
+        const uint4 *src = reinterpret_cast<const uint4 *>(
+            ximg + int64_t(g * 8) * HW + int64_t(in ? ih0 + i : 0) * a.W + k * 8);
+        uint4 raw[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) raw[e] = src[int64_t(e) * (HW >> 3)];
+        put_unit(i, k, g, in, raw);
+    }
+    // zero padding columns (positions < pad and >= pad + W) of every row
+    const int pads = SL * 2 * a.pad * 8;
+    for (int v = tid; v < pads; v += kRowsThreads) {
+        const int g = v & 7;
+        const int r = v >> 3;
+        const int i = r / (2 * a.pad);
+        const int c = r - i * 2 * a.pad;
+        const int q = i * a.IW + (c < a.pad ? c : a.W + c);
+        *reinterpret_cast<uint4 *>(patch + q * CIN + ((g ^ (q & 7)) << 3)) = uint4{0u, 0u, 0u, 0u};
+    }
+    __syncthreads();
+
+    // ---- wave i: output row ho0 + i, 64 columns x 64 channels ----------------
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    if (wave >= rw) return;
+    floatx4_t acc[4][4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[s][c] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    // this lane's A row (output column) of each 16-column block, at tap (0, 0);
+    // columns past Wo read column Wo-1 and are never stored
+    int qa[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) qa[s] = wave * a.IW + min(s * 16 + (lane & 15), a.Wo - 1);
+    const int rb = lane & 15;                        // this lane's B column (co) in a block
+#pragma unroll
+    for (int kh = 0; kh < KH; ++kh) {
+#pragma unroll
+        for (int kw = 0; kw < KW; ++kw) {
+            const uint16_t *ft = fl + (kh * KW + kw) * 64 * CIN;
+            const int dq = kh * a.IW + kw;
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                const int gr = kk * 4 + (lane >> 4);
+                uint4 af[4], bf[4];
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    const int q = qa[s] + dq;
+                    af[s] = *reinterpret_cast<const uint4 *>(patch + q * CIN + ((gr ^ (q & 7)) << 3));
+                }
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const int r = c * 16 + rb;
+                    bf[c] = *reinterpret_cast<const uint4 *>(ft + r * CIN + ((gr ^ (r & 7)) << 3));
+                }
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) acc[s][c] = mfma16x16x32<BF16>(af[s], bf[c], acc[s][c]);
+            }
+        }
+    }
+
+    // ---- store: lane holds D[4*(lane/16) + v][lane % 16] of each block -------
+    const int ho = ho0 + wave;
+    const int64_t plane = int64_t(a.Ho) * a.Wo;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const int co = cb * 64 + c * 16 + rb;
+        if (co >= a.Cout) continue;
+        float *yrow = a.y + (int64_t(n) * a.Cout + co) * plane + int64_t(ho) * a.Wo;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const int m = s * 16 + (lane >> 4) * 4;
+            if ((a.Wo & 3) == 0) {
+                if (m < a.Wo) *reinterpret_cast<floatx4_t *>(yrow + m) = acc[s][c];
+            } else {
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    if (m + v < a.Wo) yrow[m + v] = acc[s][c][v];
+            }
+        }
+    }
+}
+
+template <int KH, int KW>
+hipError_t launch_rows(const ImplicitArgs &h, hipStream_t s)
+{
+    RowsKArgs a{};
+    a.x = static_cast<const uint16_t *>(h.x);
+    a.w = static_cast<const uint16_t *>(h.wst);
+    a.y = h.y;
+    a.H = h.H;
+    a.W = h.W;
+    a.Cout = h.Cout;
+    a.pad = h.pad;
+    a.Ho = h.Ho;
+    a.Wo = h.Wo;
+    a.RW = h.R;
+    a.row_groups = (h.Ho + h.R - 1) / h.R;
+    a.co_blocks = (h.Cout + 63) / 64;
+    a.IW = h.W + 2 * h.pad;
+    const int64_t blocks = int64_t(a.co_blocks) * h.N * a.row_groups;
+    if (blocks < 1 || blocks > 0x7fffffff) return hipErrorInvalidValue;
+    const size_t lds = implicit_rows_lds_bytes(KH * KW, h.R + KH - 1, a.IW);
+    auto kern = h.bf16 ? conv_implicit_rows_kernel<KH, KW, true> : conv_implicit_rows_kernel<KH, KW, false>;
+    if (lds > 64 * 1024) {
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(kern, dim3(unsigned(blocks)), dim3(kRowsThreads), lds, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_conv_implicit_rows(const ImplicitArgs &h, hipStream_t s)
+{
+    // the kernel's assumptions, checked again here (the planner only picks it
+    // for such layers): 64 input channels, stride 1, whole rows of W % 8 == 0
+    // elements, at most 64 output columns, one output row per wave
+    if (h.Cin != 64 || h.stride != 1 || h.W % 8 != 0 || h.W < 8 || h.Wo < 1 || h.Wo > 64 ||
+        h.Wo != h.W + 2 * h.pad - h.KW + 1 || h.R < 1 || h.R > kRowsThreads / 64 ||
+        h.Ho != h.H + 2 * h.pad - h.KH + 1 ||
+        implicit_rows_lds_bytes(h.KH * h.KW, h.R + h.KH - 1, h.W + 2 * h.pad) > kImplicitMaxLdsBytes)
+        return hipErrorInvalidValue;
+    if (h.KH == 3 && h.KW == 3) return launch_rows<3, 3>(h, s);
+    if (h.KH == 1 && h.KW == 1) return launch_rows<1, 1>(h, s);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace im2win

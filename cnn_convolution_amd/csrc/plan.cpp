@@ -226,6 +226,7 @@ static void pick_algo(const conv2d_desc_t &d, conv2d_plan_t *p) {
     const bool can = make_implicit_plan(d, &ip) == CONV2D_OK;
     const int64_t taps = d.KH * d.KW;
     bool use = false;
+    if (can && ip.kernel == 2) use = true;
     if (can && ip.kernel == 0 && d.stride == 1 && taps <= 25) {
         const double fill = double(p->Ho * p->Wo) /
             double(ceil_div(p->Ho, ip.rows_per_tile) * ceil_div(p->Wo, ip.cols_per_tile) * ip.tile_n);
@@ -374,6 +375,56 @@ static void pick_implicit_fs(const conv2d_desc_t &d, int64_t Ho, int64_t Wo, con
     p->tiles = groups * tiles_m;
 }
 
+// Row-block implicit kernel: 64 input channels, stride 1, input rows a
+// multiple of 8 long, output rows of at most 64 columns, a 1x1 or 3x3
+// filter. A workgroup of eight waves takes RW <= 8 whole output rows of one
+// image (one per wave) and 64 output channels, with the raw filter and the
+// RW + KH - 1 input rows in LDS; no staged filter. RW is the one that needs
+// the fewest rounds of workgroups over the CUs, each round costing about its
+// rows plus a fixed set-up (the block's loads and barrier) of three rows.
+// Default where it applies; IM2WIN_IMPLICIT_KERNEL=streamed|stationary (or a
+// tile in IM2WIN_IMPLICIT_TILE) selects the other kernels; IM2WIN_IMPLICIT_ROWS
+// sets RW.
+static void pick_implicit_rows(const conv2d_desc_t &d, int64_t Ho, int64_t Wo, conv2d_implicit_plan_t *p) {
+    const int64_t taps = d.KH * d.KW;
+    if (d.Cin != 64 || d.stride != 1 || d.W % 8 != 0 || Wo > 64 ||
+        !((d.KH == 3 && d.KW == 3) || (d.KH == 1 && d.KW == 1)))
+        return;
+    if (const char *e = std::getenv("IM2WIN_IMPLICIT_KERNEL"))
+        if (std::strcmp(e, "rows") != 0) return;
+    if (std::getenv("IM2WIN_IMPLICIT_TILE")) return;   // a streamed-kernel tile was asked for
+    const int64_t iw = d.W + 2 * d.pad;
+    const int64_t co_blocks = ceil_div(d.Cout, 64);
+    int64_t best_rw = 0;
+    double best_cost = 0.0;
+    for (int64_t rw = 1; rw <= 8 && rw <= Ho; ++rw) {
+        const int64_t lds = implicit_rows_lds_bytes(taps, rw + d.KH - 1, iw);
+        if (lds > kImplicitMaxLdsBytes) break;
+        const int64_t per_cu = std::min<int64_t>(2, kImplicitMaxLdsBytes / lds);
+        const int64_t blocks = co_blocks * d.N * ceil_div(Ho, rw);
+        const double cost = double(ceil_div(blocks, 256 * per_cu)) * double(rw + 3);
+        if (best_rw == 0 || cost <= best_cost) { best_rw = rw; best_cost = cost; }
+    }
+    if (best_rw == 0) return;
+    if (const char *e = std::getenv("IM2WIN_IMPLICIT_ROWS")) {
+        const int64_t v = std::min<int64_t>(std::atoi(e), Ho);
+        if (v >= 1 && v <= 8 && implicit_rows_lds_bytes(taps, v + d.KH - 1, iw) <= kImplicitMaxLdsBytes)
+            best_rw = v;
+    }
+    p->kernel = 2;
+    p->tile_m = 64;
+    p->tile_n = 64;
+    p->wave_m = 1;
+    p->rows_per_tile = int32_t(best_rw);
+    p->cols_per_tile = int32_t(Wo);
+    p->patch_rows = int32_t(best_rw + d.KH - 1);
+    p->patch_cols = int32_t(iw);
+    p->stages = 0;
+    p->lds_bytes = implicit_rows_lds_bytes(taps, p->patch_rows, iw);
+    p->tiles = co_blocks * d.N * ceil_div(Ho, best_rw);
+    p->ws_bytes = 0;    // the kernel reads w as it is stored
+}
+
 conv2d_status_t make_implicit_plan(const conv2d_desc_t &d, conv2d_implicit_plan_t *p) {
     const conv2d_status_t st = check_desc(d);
     if (st != CONV2D_OK) return st;
@@ -457,6 +508,7 @@ conv2d_status_t make_implicit_plan(const conv2d_desc_t &d, conv2d_implicit_plan_
     p->tiles = ceil_div(d.Cout, best.mb) * d.N * ceil_div(Ho, best.r) * ceil_div(Wo, best.wb);
     if (p->tiles > 0x7fffffff) return CONV2D_ERR_INVALID_DESC;
     pick_implicit_fs(d, Ho, Wo, p);
+    pick_implicit_rows(d, Ho, Wo, p);
     return CONV2D_OK;
 }
 

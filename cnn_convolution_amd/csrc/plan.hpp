@@ -35,6 +35,9 @@ constexpr int64_t kImplicitMaxLdsBytes = 160 * 1024;   // one workgroup per CU
 // filter-stationary implicit form: two patch buffers, all channel blocks
 inline int64_t implicit_fs_lds_bytes(int64_t cin, int64_t ir, int64_t iw) { return 2 * (cin / 64) * ir * iw * 128; }
 constexpr int64_t kImplicitPairLdsBytes = 80 * 1024;   // two workgroups per CU
+// row-block implicit form: the filter block (8 KB per tap) + sl input rows of
+// iw positions x 128 bytes
+inline int64_t implicit_rows_lds_bytes(int64_t taps, int64_t sl, int64_t iw) { return taps * 8192 + sl * iw * 128; }
 
 // fp32 vector-ALU kernel: output columns per lane for this filter shape.
 int valu_cols_per_lane(const conv2d_desc_t &d);

@@ -338,3 +338,48 @@ def test_conv2d_plan_names_the_form_conv2d_fwd_runs(monkeypatch):
                  (2, 96, 20, 20, 16, 3, 3, 1, 1, conv.BF16)]:
         assert conv.plan(conv.make_desc(*args)).algo == 0     # not applicable: stays on the window form
     assert conv.plan(conv.make_desc(2, 256, 14, 14, 16, 3, 3, 1, 1, conv.BF16)).algo == 1
+
+
+def test_row_block_plan_geometry(monkeypatch):
+    """The row-block implicit kernel is planned exactly for its layers (64 input
+    channels, stride 1, W % 8 == 0, Wo <= 64, a 3x3 or 1x1 filter, fp16/bf16):
+    whole output rows per workgroup, the block's input rows and the filter in LDS,
+    no workspace, one workgroup per (64-channel block, row block, image)."""
+    import numpy as np
+    rng = np.random.default_rng(12)
+    taken = 0
+    for _ in range(600):
+        KH, KW = [(3, 3), (1, 1), (5, 5), (3, 1)][int(rng.integers(0, 4))]
+        s = int(rng.choice([1, 1, 1, 2]))
+        p = int(rng.integers(0, 4))
+        Cin = int(rng.choice([64, 64, 64, 128]))
+        W = int(rng.choice([8, 16, 24, 56, 60, 64, 72]))
+        H = int(rng.integers(max(KH, 1), 40))
+        N, Cout = int(rng.integers(1, 9)), int(rng.integers(1, 300))
+        dt = [conv.F16, conv.BF16][int(rng.integers(0, 2))]
+        d = conv.make_desc(N, Cin, H, W, Cout, KH, KW, s, p, dt)
+        if conv._lib.implicit_plan_status(d) != 0:
+            continue
+        pl = conv.implicit_plan(d)
+        eligible = (Cin == 64 and s == 1 and W % 8 == 0 and pl.Wo <= 64 and (KH, KW) in ((3, 3), (1, 1)))
+        assert (pl.kernel == 2) == eligible, (N, Cin, H, W, Cout, KH, KW, s, p)
+        if not eligible:
+            continue
+        taken += 1
+        R = pl.rows_per_tile
+        assert 1 <= R <= min(8, pl.Ho)
+        assert pl.patch_rows == R + KH - 1 and pl.patch_cols == W + 2 * p
+        assert pl.cols_per_tile == pl.Wo and pl.tile_m == 64 and pl.tile_n == 64
+        assert pl.lds_bytes == KH * KW * 8192 + pl.patch_rows * pl.patch_cols * 128 <= 160 * 1024
+        assert pl.tiles == -(-Cout // 64) * N * -(-pl.Ho // R)
+        assert pl.ws_bytes == 0 == conv.implicit_workspace_size(d)
+        assert conv.plan(d).algo == 1 and conv.workspace_size(d) == 0
+    assert taken > 50
+    # the other kernels stay reachable
+    d = conv.make_desc(32, 64, 56, 56, 64, 3, 3, 1, 1, conv.F16)
+    assert conv.implicit_plan(d).kernel == 2 and conv.implicit_plan(d).rows_per_tile == 7
+    monkeypatch.setenv("IM2WIN_IMPLICIT_KERNEL", "streamed")
+    assert conv.implicit_plan(d).kernel == 0 and conv.implicit_plan(d).ws_bytes > 0
+    monkeypatch.setenv("IM2WIN_IMPLICIT_KERNEL", "rows")
+    monkeypatch.setenv("IM2WIN_IMPLICIT_ROWS", "3")
+    assert conv.implicit_plan(d).kernel == 2 and conv.implicit_plan(d).rows_per_tile == 3
