@@ -201,7 +201,13 @@ typedef struct {
                                      one workgroup per tile; 1 (opt-in): filter-
                                      stationary, KW*KH*Cin of 64, 128, 256 or 576:
                                      a 64-row filter block in registers, workgroups
-                                     that each walk a contiguous range of tiles    */
+                                     that each walk a contiguous range of tiles;
+                                     2 (default where it applies: Cin = 64,
+                                     stride 1, W % 8 == 0, Wo <= 64, 3x3 or 1x1):
+                                     row-block, rows_per_tile whole output rows
+                                     of one image per workgroup with w as stored
+                                     and the input rows resident in LDS, no
+                                     staged filter (ws_bytes 0)                   */
     int32_t stages;               /* kernel 0: filter K stages in flight + 1 (LDS
                                      stage buffers)                                 */
     int32_t reserved;
@@ -209,7 +215,8 @@ typedef struct {
     int64_t tiles;                /* workgroups of the launch                       */
     int64_t Ho, Wo;
     int64_t K_stage;              /* staged filter row: KW*KH*Cin                   */
-    int64_t ws_bytes;             /* the staged filter; 0 for a 1x1 filter           */
+    int64_t ws_bytes;             /* the staged filter; 0 for a 1x1 filter and for
+                                     kernel 2                                       */
     int64_t flops;                /* 2*N*Cout*Ho*Wo*Cin*KH*KW                        */
 } conv2d_implicit_plan_t;
 
@@ -231,8 +238,10 @@ conv2d_status_t conv2d_fwd_implicit(const conv2d_desc_t *d, const void *x, const
 
 /* Rows (a2, a4, a5) of the implicit form on their own: the implicit kernel
  * with a filter already staged in the window's K order (as
- * im2win_weight_stage writes it for IM2WIN_LAYOUT_CL; for a 1x1 filter w
- * itself), writing all of y. Device pointers, 16-byte aligned. */
+ * im2win_weight_stage writes it for IM2WIN_LAYOUT_CL), or w itself where the
+ * plan keeps no staged filter (conv2d_implicit_workspace_size(d) == 0: a 1x1
+ * filter, or the row-block kernel, which reorders w in LDS on its own),
+ * writing all of y. Device pointers, 16-byte aligned. */
 conv2d_status_t im2win_implicit_gemm(const conv2d_desc_t *d, const void *x, const void *wst,
                                      float *y, void *stream);
 
