@@ -165,6 +165,7 @@ ImplicitArgs implicit_args(const conv2d_desc_t &d, const conv2d_implicit_plan_t 
     a.wm = p.wave_m;
     a.stages = p.stages;
     a.bf16 = d.dtype == CONV2D_BF16 ? 1 : 0;
+    a.f32 = d.dtype == CONV2D_F32 ? 1 : 0;
     a.fs_groups = int(p.tiles / ((d.Cout + 63) / 64));
     return a;
 }

@@ -236,6 +236,217 @@ __global__ __launch_bounds__(kRowsThreads) void conv_implicit_rows_kernel(const 
     }
 }
 
+// fp32 form of the same row block on the matrix cores' fp32 multiply
+// (v_mfma_f32_16x16x4_f32: fp32 products, fp32 accumulation): the input
+// channels are taken in blocks of 32 (128 bytes per position, the LDS
+// geometry of the half-precision form), each block's filter slice (64
+// output channels x all taps x 32 channels) and its input rows loaded,
+// contracted, and replaced by the next block's after a barrier. Units of the
+// input rows are 4 channels x 4 columns (16-byte loads of 4 columns of one
+// channel), transposed by register moves. K of one MFMA step is 4 channels:
+// lane group g = lane / 16 holds channels 4g .. 4g + 3 of a 16-channel slice
+// as one 16-byte vector and feeds element j to step j, for the window rows
+// and the filter alike.
+struct RowsF32KArgs {
+    const float *x;
+    const float *w;
+    float *y;
+    int Cin, H, W, Cout, pad, Ho, Wo;
+    int RW, row_groups, co_blocks, IW;
+};
+
+template <int KH, int KW>
+__global__ __launch_bounds__(kRowsThreads) void conv_implicit_rows_f32_kernel(const RowsF32KArgs a)
+{
+    constexpr int TAPS = KH * KW;
+    constexpr int CB = 32;                           // channels per block: 128 bytes per position
+    extern __shared__ __attribute__((aligned(16))) float ldsf[];
+    float *const fl = ldsf;                          // [TAPS][64 co][32 ci], 8 KB per tap
+    float *const patch = ldsf + TAPS * 64 * CB;      // [SL][IW][32 ci]
+
+    int cb, tn;
+    tile_coords(blockIdx.x, gridDim.x, a.co_blocks, cb, tn);
+    const int rg = tn % a.row_groups;
+    const int n = tn / a.row_groups;
+    const int ho0 = rg * a.RW;
+    const int rw = min(a.RW, a.Ho - ho0);
+    const int SL = rw + KH - 1;
+    const int ih0 = ho0 - a.pad;
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int HW = a.H * a.W;
+    const float *const ximg = a.x + int64_t(n) * a.Cin * HW;
+    const int nblk = a.Cin / CB;
+    const int CW = a.W >> 2;                         // chunks of 4 columns
+    const int units = SL * CW * 8;                   // (input row, chunk, 4-channel group)
+    const int co_l = tid >> 3;
+    const int cg = tid & 7;                          // 4-channel group of the block
+    const int co_src = min(cb * 64 + co_l, a.Cout - 1);
+
+    // zero padding columns of every row held (the same positions for every block)
+    const int pads = SL * 2 * a.pad * 8;
+    for (int v = tid; v < pads; v += kRowsThreads) {
+        const int g = v & 7;
+        const int r = v >> 3;
+        const int i = r / (2 * a.pad);
+        const int c = r - i * 2 * a.pad;
+        const int q = i * a.IW + (c < a.pad ? c : a.W + c);
+        *reinterpret_cast<float4 *>(patch + q * CB + ((g ^ (q & 7)) << 2)) = float4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    floatx4_t acc[4][4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[s][c] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    int qa[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) qa[s] = wave * a.IW + min(s * 16 + (lane & 15), a.Wo - 1);
+    const int rbl = lane & 15;
+
+    for (int blk = 0; blk < nblk; ++blk) {
+        if (blk > 0) __syncthreads();                // every wave is done with the previous block
+        // filter slice: thread (co_l, cg) reads w[co][blk*32 + cg*4 .. +3][taps]
+        // (4*TAPS contiguous floats) and writes one 4-channel vector per tap
+        float4 wraw[TAPS];
+        {
+            const float4 *src = reinterpret_cast<const float4 *>(
+                a.w + (int64_t(co_src) * a.Cin + blk * CB + cg * 4) * TAPS);
+#pragma unroll
+            for (int i = 0; i < TAPS; ++i) wraw[i] = src[i];
+        }
+        auto load_unit = [&](int u, float4 *raw, int &q0, int &g, bool &in) {
+            g = u & 7;
+            const int r = u >> 3;
+            const int i = r / CW;
+            const int k = r - i * CW;
+            in = unsigned(ih0 + i) < unsigned(a.H);
+            q0 = i * a.IW + a.pad + k * 4;
+            const float4 *src = reinterpret_cast<const float4 *>(
+                ximg + int64_t(blk * CB + g * 4) * HW + int64_t(in ? ih0 + i : 0) * a.W + k * 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) raw[e] = src[int64_t(e) * (HW >> 2)];
+        };
+        auto put_unit = [&](int q0, int g, bool in, const float4 *raw) {
+            const float4 z{0.f, 0.f, 0.f, 0.f};
+            const float4 o0 = in ? float4{raw[0].x, raw[1].x, raw[2].x, raw[3].x} : z;
+            const float4 o1 = in ? float4{raw[0].y, raw[1].y, raw[2].y, raw[3].y} : z;
+            const float4 o2 = in ? float4{raw[0].z, raw[1].z, raw[2].z, raw[3].z} : z;
+            const float4 o3 = in ? float4{raw[0].w, raw[1].w, raw[2].w, raw[3].w} : z;
+            *reinterpret_cast<float4 *>(patch + q0 * CB + ((g ^ (q0 & 7)) << 2)) = o0;
+            *reinterpret_cast<float4 *>(patch + (q0 + 1) * CB + ((g ^ ((q0 + 1) & 7)) << 2)) = o1;
+            *reinterpret_cast<float4 *>(patch + (q0 + 2) * CB + ((g ^ ((q0 + 2) & 7)) << 2)) = o2;
+            *reinterpret_cast<float4 *>(patch + (q0 + 3) * CB + ((g ^ ((q0 + 3) & 7)) << 2)) = o3;
+        };
+        // the first two units of this thread are in flight with the filter slice
+        float4 r0[4], r1[4];
+        int q0a, g0a, q0b, g0b;
+        bool i0a, i0b;
+        load_unit(min(tid, units - 1), r0, q0a, g0a, i0a);
+        load_unit(min(tid + kRowsThreads, units - 1), r1, q0b, g0b, i0b);
+#pragma unroll
+        for (int t = 0; t < TAPS; ++t) {
+            // element e of tap t is float e*TAPS + t of the 4*TAPS run
+            const float *f = reinterpret_cast<const float *>(wraw);
+            *reinterpret_cast<float4 *>(fl + t * 64 * CB + co_l * CB + ((cg ^ (co_l & 7)) << 2)) =
+                float4{f[t], f[TAPS + t], f[2 * TAPS + t], f[3 * TAPS + t]};
+        }
+        if (tid < units) put_unit(q0a, g0a, i0a, r0);
+        if (tid + kRowsThreads < units) put_unit(q0b, g0b, i0b, r1);
+        for (int u = tid + 2 * kRowsThreads; u < units; u += kRowsThreads) {
+            float4 raw[4];
+            int q0, g;
+            bool in;
+            load_unit(u, raw, q0, g, in);
+            put_unit(q0, g, in, raw);
+        }
+        __syncthreads();
+
+        if (wave < rw) {
+#pragma unroll
+            for (int t = 0; t < TAPS; ++t) {
+                const float *ft = fl + t * 64 * CB;
+                const int dq = (t / KW) * a.IW + (t % KW);
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int gr = h * 4 + (lane >> 4);
+                    floatx4_t af[4], bf[4];
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) {
+                        const int q = qa[s] + dq;
+                        af[s] = *reinterpret_cast<const floatx4_t *>(patch + q * CB + ((gr ^ (q & 7)) << 2));
+                    }
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        const int r = c * 16 + rbl;
+                        bf[c] = *reinterpret_cast<const floatx4_t *>(ft + r * CB + ((gr ^ (r & 7)) << 2));
+                    }
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+#pragma unroll
+                        for (int s = 0; s < 4; ++s)
+#pragma unroll
+                            for (int c = 0; c < 4; ++c)
+                                acc[s][c] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[s][j], bf[c][j], acc[s][c], 0, 0, 0);
+                }
+            }
+        }
+    }
+    if (wave >= rw) return;
+
+    const int ho = ho0 + wave;
+    const int64_t plane = int64_t(a.Ho) * a.Wo;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const int co = cb * 64 + c * 16 + rbl;
+        if (co >= a.Cout) continue;
+        float *yrow = a.y + (int64_t(n) * a.Cout + co) * plane + int64_t(ho) * a.Wo;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const int m = s * 16 + (lane >> 4) * 4;
+            if ((a.Wo & 3) == 0) {
+                if (m < a.Wo) *reinterpret_cast<floatx4_t *>(yrow + m) = acc[s][c];
+            } else {
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    if (m + v < a.Wo) yrow[m + v] = acc[s][c][v];
+            }
+        }
+    }
+}
+
+template <int KH, int KW>
+hipError_t launch_rows_f32(const ImplicitArgs &h, hipStream_t s)
+{
+    RowsF32KArgs a{};
+    a.x = static_cast<const float *>(h.x);
+    a.w = static_cast<const float *>(h.wst);
+    a.y = h.y;
+    a.Cin = h.Cin;
+    a.H = h.H;
+    a.W = h.W;
+    a.Cout = h.Cout;
+    a.pad = h.pad;
+    a.Ho = h.Ho;
+    a.Wo = h.Wo;
+    a.RW = h.R;
+    a.row_groups = (h.Ho + h.R - 1) / h.R;
+    a.co_blocks = (h.Cout + 63) / 64;
+    a.IW = h.W + 2 * h.pad;
+    const int64_t blocks = int64_t(a.co_blocks) * h.N * a.row_groups;
+    if (blocks < 1 || blocks > 0x7fffffff) return hipErrorInvalidValue;
+    const size_t lds = implicit_rows_lds_bytes(KH * KW, h.R + KH - 1, a.IW);
+    auto kern = conv_implicit_rows_f32_kernel<KH, KW>;
+    if (lds > 64 * 1024) {
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(kern, dim3(unsigned(blocks)), dim3(kRowsThreads), lds, s, a);
+    return hipGetLastError();
+}
+
 template <int KH, int KW>
 hipError_t launch_rows(const ImplicitArgs &h, hipStream_t s)
 {
@@ -273,6 +484,17 @@ hipError_t launch_conv_implicit_rows(const ImplicitArgs &h, hipStream_t s)
     // the kernel's assumptions, checked again here (the planner only picks it
     // for such layers): 64 input channels, stride 1, whole rows of W % 8 == 0
     // elements, at most 64 output columns, one output row per wave
+    if (h.f32) {
+        // fp32: channel blocks of 32, whole rows of W % 4 == 0 elements
+        if (h.Cin % 32 != 0 || h.Cin < 32 || h.stride != 1 || h.W % 4 != 0 || h.W < 4 || h.Wo < 1 ||
+            h.Wo > 64 || h.Wo != h.W + 2 * h.pad - h.KW + 1 || h.R < 1 || h.R > kRowsThreads / 64 ||
+            h.Ho != h.H + 2 * h.pad - h.KH + 1 ||
+            implicit_rows_lds_bytes(h.KH * h.KW, h.R + h.KH - 1, h.W + 2 * h.pad) > kImplicitMaxLdsBytes)
+            return hipErrorInvalidValue;
+        if (h.KH == 3 && h.KW == 3) return launch_rows_f32<3, 3>(h, s);
+        if (h.KH == 1 && h.KW == 1) return launch_rows_f32<1, 1>(h, s);
+        return hipErrorInvalidValue;
+    }
     if (h.Cin != 64 || h.stride != 1 || h.W % 8 != 0 || h.W < 8 || h.Wo < 1 || h.Wo > 64 ||
         h.Wo != h.W + 2 * h.pad - h.KW + 1 || h.R < 1 || h.R > kRowsThreads / 64 ||
         h.Ho != h.H + 2 * h.pad - h.KH + 1 ||

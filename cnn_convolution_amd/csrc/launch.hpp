@@ -85,15 +85,17 @@ struct ImplicitArgs {
     int tile_m, tile_n, wm;
     int stages;             // filter stage buffers (3, 4 or 5)
     int bf16;
+    int f32;                // fp32 x, w (the row-block kernel only)
     int fs_groups;          // filter-stationary form: workgroups per 64-row filter block
 };
 hipError_t launch_conv_implicit(const ImplicitArgs &a, hipStream_t s);
 // filter-stationary form (K = KW*KH*Cin of 64, 128, 256 or 576): a 64-row
 // filter block in registers, persistent workgroups over contiguous tiles
 hipError_t launch_conv_implicit_fs(const ImplicitArgs &a, hipStream_t s);
-// row-block form (Cin = 64, stride 1, W % 8 == 0, Wo <= 64, 1x1 or 3x3):
-// R whole output rows of one image per workgroup, raw filter and input rows
-// resident in LDS; wst is w itself
+// row-block form (fp16/bf16: Cin = 64, W % 8 == 0; fp32: Cin % 32 == 0,
+// W % 4 == 0; stride 1, Wo <= 64, 1x1 or 3x3): R whole output rows of one
+// image per workgroup, raw filter and input rows resident in LDS; wst is w
+// itself
 hipError_t launch_conv_implicit_rows(const ImplicitArgs &a, hipStream_t s);
 
 }  // namespace im2win

@@ -316,6 +316,7 @@ conv2d_status_t make_plan(const conv2d_desc_t &d, conv2d_plan_t *p) {
         p->gemm_tile_n = 64 * valu_cols_per_lane(d);
         p->gemm_kslice = 0;
         p->gemm_ksplit = pick_valu_ksplit(d, p->rows_per_chunk, p->Wo, p->Cout_stage);
+        pick_algo(d, p);
     }
     return CONV2D_OK;
 }
@@ -387,7 +388,9 @@ static void pick_implicit_fs(const conv2d_desc_t &d, int64_t Ho, int64_t Wo, con
 // sets RW.
 static void pick_implicit_rows(const conv2d_desc_t &d, int64_t Ho, int64_t Wo, conv2d_implicit_plan_t *p) {
     const int64_t taps = d.KH * d.KW;
-    if (d.Cin != 64 || d.stride != 1 || d.W % 8 != 0 || Wo > 64 ||
+    const bool f32 = d.dtype == CONV2D_F32;
+    const bool chans = f32 ? (d.Cin % 32 == 0) : (d.Cin == 64);
+    if (!chans || d.stride != 1 || d.W % (f32 ? 4 : 8) != 0 || Wo > 64 ||
         !((d.KH == 3 && d.KW == 3) || (d.KH == 1 && d.KW == 1)))
         return;
     if (const char *e = std::getenv("IM2WIN_IMPLICIT_KERNEL"))
@@ -429,13 +432,18 @@ conv2d_status_t make_implicit_plan(const conv2d_desc_t &d, conv2d_implicit_plan_
     const conv2d_status_t st = check_desc(d);
     if (st != CONV2D_OK) return st;
     std::memset(p, 0, sizeof(*p));
-    if (d.dtype == CONV2D_F32 || d.Cin % 64 != 0) return CONV2D_ERR_UNSUPPORTED;
     const int64_t Ho = out_extent(d.H, d.KH, d.stride, d.pad);
     const int64_t Wo = out_extent(d.W, d.KW, d.stride, d.pad);
     p->Ho = Ho;
     p->Wo = Wo;
     p->K_stage = d.KW * d.KH * d.Cin;
     p->flops = 2 * d.N * d.Cout * Ho * Wo * d.Cin * d.KH * d.KW;
+    if (d.dtype == CONV2D_F32) {
+        // fp32: only the row-block kernel (fp32 matrix-core products)
+        pick_implicit_rows(d, Ho, Wo, p);
+        return p->kernel == 2 ? CONV2D_OK : CONV2D_ERR_UNSUPPORTED;
+    }
+    if (d.Cin % 64 != 0) return CONV2D_ERR_UNSUPPORTED;
     const StageGeom sg = stage_geom(d, IM2WIN_LAYOUT_CL, 64);
     if (sg.row_len != p->K_stage) return CONV2D_ERR_UNSUPPORTED;
     p->ws_bytes = sg.needed ? round_up(sg.rows * sg.row_len * elem_size(d.dtype), 256) : 0;

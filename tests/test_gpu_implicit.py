@@ -16,8 +16,8 @@ import workloads
 
 pytestmark = pytest.mark.gpu
 
-TOL = {"f16": 2e-3, "bf16": 1e-2}
-CODE = {"f16": conv.F16, "bf16": conv.BF16}
+TOL = {"f32": 1e-5, "f16": 2e-3, "bf16": 1e-2}
+CODE = {"f32": conv.F32, "f16": conv.F16, "bf16": conv.BF16}
 DEV = "cuda:0"
 
 
@@ -209,7 +209,7 @@ def _eligible_configs():
     out = []
     for name, cfg in sorted(workloads.CONFIGS.items()):
         for dt in cfg.dtypes:
-            if dt != "f32" and cfg.Cin % 64 == 0:
+            if (dt != "f32" and cfg.Cin % 64 == 0) or (name, dt) == ("resnet3x3", "f32"):
                 out.append((name, dt))
     for name in ("cv4", "cv8", "cv12"):
         out.append((name, "f16"))
@@ -291,10 +291,22 @@ ROWS_SHAPES = [
 ]
 
 
-@pytest.mark.parametrize("shape", ROWS_SHAPES, ids=[str(s) for s in ROWS_SHAPES])
+# fp32 (channel blocks of 32, W % 4 == 0): more channel blocks, rows of 4k columns
+ROWS_SHAPES_F32 = [
+    (2, 32, 9, 12, 40, 3, 3, 1, 1),      # one 32-channel block, W = 12
+    (1, 96, 7, 20, 70, 3, 3, 1, 0),      # three blocks, Wo = 18
+    (2, 128, 6, 28, 64, 1, 1, 1, 0),     # 1x1, four blocks
+    (1, 64, 5, 4, 16, 3, 3, 1, 2),       # W = 4: one chunk per row, padding 2
+]
+
+
+ROWS_CASES = [(s, dt) for dt in ("f32", "f16", "bf16") for s in ROWS_SHAPES] + \
+             [(s, "f32") for s in ROWS_SHAPES_F32]
+
+
+@pytest.mark.parametrize("shape,dt", ROWS_CASES, ids=[f"{dt}-{s}" for s, dt in ROWS_CASES])
 @pytest.mark.parametrize("rw", [None, 1, 3, 8])
-@pytest.mark.parametrize("dt", ["f16", "bf16"])
-def test_row_block_kernel_matches_oracle(shape, rw, dt, monkeypatch):
+def test_row_block_kernel_matches_oracle(shape, dt, rw, monkeypatch):
     N, Cin, H, W, Cout, KH, KW, s, p = shape
     if rw is not None:
         monkeypatch.setenv("IM2WIN_IMPLICIT_ROWS", str(rw))
@@ -311,22 +323,24 @@ def test_row_block_kernel_matches_oracle(shape, rw, dt, monkeypatch):
 
 
 @pytest.mark.parametrize("shape", ROWS_SHAPES[:4] + ROWS_SHAPES[6:7], ids=[str(s) for s in ROWS_SHAPES[:4] + ROWS_SHAPES[6:7]])
-def test_row_block_kernel_integer_inputs_exact(shape):
+@pytest.mark.parametrize("dt", ["f32", "f16"])
+def test_row_block_kernel_integer_inputs_exact(shape, dt):
     """Integer-valued inputs: every product and partial sum is exact in fp32,
     so the row-block kernel matches the oracle bit for bit."""
     N, Cin, H, W, Cout, KH, KW, s, p = shape
-    x, w = workloads.make_inputs(N, Cin, H, W, Cout, KH, KW, seed=22, dtype="f16",
+    x, w = workloads.make_inputs(N, Cin, H, W, Cout, KH, KW, seed=22, dtype=dt,
                                  x_dist="int3", w_dist="int3")
-    assert conv.implicit_plan(conv.make_desc(*shape, conv.F16)).kernel == 2
+    assert conv.implicit_plan(conv.make_desc(*shape, CODE[dt])).kernel == 2
     got = run_implicit(x, w, s, p)
     ref = oracle.conv2d(x, w, s, p)
     assert np.array_equal(got.numpy().astype(np.float64), ref)
 
 
-def test_row_block_kernel_leaves_memory_past_y_untouched():
+@pytest.mark.parametrize("dt", ["f32", "f16"])
+def test_row_block_kernel_leaves_memory_past_y_untouched(dt):
     N, Cin, H, W, Cout, KH, KW, s, p = 2, 64, 9, 16, 70, 3, 3, 1, 0
-    x, w = workloads.make_inputs(N, Cin, H, W, Cout, KH, KW, seed=23, dtype="f16")
-    d = conv.describe(tuple(x.shape), tuple(w.shape), s, p, conv.F16)
+    x, w = workloads.make_inputs(N, Cin, H, W, Cout, KH, KW, seed=23, dtype=dt)
+    d = conv.describe(tuple(x.shape), tuple(w.shape), s, p, CODE[dt])
     pl = conv.implicit_plan(d)
     assert pl.kernel == 2
     n_out = N * Cout * pl.Ho * pl.Wo
@@ -335,7 +349,7 @@ def test_row_block_kernel_leaves_memory_past_y_untouched():
     torch.cuda.synchronize()
     host = buf.cpu().numpy()
     assert (host[n_out:] == 12345.0).all()
-    assert rel_l2(host[:n_out], oracle.conv2d(x, w, s, p).reshape(-1)) <= TOL["f16"]
+    assert rel_l2(host[:n_out], oracle.conv2d(x, w, s, p).reshape(-1)) <= TOL[dt]
 
 
 def test_row_block_kernel_agrees_with_streamed_kernel(monkeypatch):

@@ -334,7 +334,7 @@ def test_conv2d_plan_names_the_form_conv2d_fwd_runs(monkeypatch):
     q = conv.plan(d)
     assert q.algo == 0 and q.ws_bytes == q.wstage_bytes + q.win_chunk_bytes
     monkeypatch.setenv("IM2WIN_ALGO", "implicit")
-    for args in [(2, 3, 20, 20, 16, 3, 3, 1, 1, conv.F16), (2, 64, 20, 20, 16, 3, 3, 1, 1, conv.F32),
+    for args in [(2, 3, 20, 20, 16, 3, 3, 1, 1, conv.F16), (2, 48, 20, 20, 16, 3, 3, 1, 1, conv.F32),
                  (2, 96, 20, 20, 16, 3, 3, 1, 1, conv.BF16)]:
         assert conv.plan(conv.make_desc(*args)).algo == 0     # not applicable: stays on the window form
     assert conv.plan(conv.make_desc(2, 256, 14, 14, 16, 3, 3, 1, 1, conv.BF16)).algo == 1
@@ -383,3 +383,38 @@ def test_row_block_plan_geometry(monkeypatch):
     monkeypatch.setenv("IM2WIN_IMPLICIT_KERNEL", "rows")
     monkeypatch.setenv("IM2WIN_IMPLICIT_ROWS", "3")
     assert conv.implicit_plan(d).kernel == 2 and conv.implicit_plan(d).rows_per_tile == 3
+
+
+def test_row_block_plan_fp32():
+    """fp32 layers go to the implicit form only through the row-block kernel
+    (fp32 matrix-core products): Cin a multiple of 32, stride 1, W % 4 == 0,
+    Wo <= 64, a 3x3 or 1x1 filter; every other fp32 layer stays on the
+    vector-ALU window form."""
+    import numpy as np
+    rng = np.random.default_rng(13)
+    seen = {True: 0, False: 0}
+    for _ in range(500):
+        KH, KW = [(3, 3), (1, 1), (5, 5), (1, 3)][int(rng.integers(0, 4))]
+        s = int(rng.choice([1, 1, 2]))
+        p = int(rng.integers(0, 3))
+        Cin = int(rng.choice([3, 32, 48, 64, 96, 128]))
+        W = int(rng.choice([6, 8, 12, 14, 28, 56, 60, 64, 70]))
+        H = int(rng.integers(KH, 30))
+        N, Cout = int(rng.integers(1, 5)), int(rng.integers(1, 200))
+        d = conv.make_desc(N, Cin, H, W, Cout, KH, KW, s, p, conv.F32)
+        Wo = (W + 2 * p - KW) // s + 1
+        if Wo < 1 or (H + 2 * p - KH) // s + 1 < 1:
+            continue
+        eligible = (Cin % 32 == 0 and s == 1 and W % 4 == 0 and Wo <= 64 and (KH, KW) in ((3, 3), (1, 1)))
+        seen[eligible] += 1
+        st = conv._lib.implicit_plan_status(d)
+        assert (st == 0) == eligible, (N, Cin, H, W, Cout, KH, KW, s, p)
+        pl = conv.plan(d)
+        assert pl.algo == (1 if eligible else 0)
+        if eligible:
+            ip = conv.implicit_plan(d)
+            assert ip.kernel == 2 and ip.ws_bytes == 0 and pl.ws_bytes == 0
+            assert ip.lds_bytes == KH * KW * 8192 + ip.patch_rows * ip.patch_cols * 128 <= 160 * 1024
+        else:
+            assert pl.ws_bytes == pl.wstage_bytes + pl.win_chunk_bytes
+    assert seen[True] > 30 and seen[False] > 30
