@@ -58,6 +58,57 @@ __device__ __forceinline__ uint32_t dword_of(const uint4 &v, int d)
     return d == 0 ? v.x : d == 1 ? v.y : d == 2 ? v.z : v.w;
 }
 
+// The rw x Wo outputs of a workgroup, flattened (i * Wo + wo, which is also
+// their order inside each output plane), are cut into MFMA blocks of 16 and
+// shared out over the eight waves in contiguous ranges of at most 4 blocks.
+// Lane l of a block works on output m = 16 * block + l % 16 (clamped to the
+// last output: such lanes read a valid window and store nothing); its window
+// at tap (0, 0) starts at patch position i * IW + wo.
+__device__ __forceinline__ void wave_blocks(int wave, int outs, int &b0, int &nb)
+{
+    const int total = (outs + 15) >> 4;
+    b0 = wave * total / 8;
+    nb = (wave + 1) * total / 8 - b0;
+}
+
+__device__ __forceinline__ void block_bases(int *qa, int b0, int lane, int outs, int Wo, int IW)
+{
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        const int m = min((b0 + s) * 16 + (lane & 15), outs - 1);
+        const int i = m / Wo;
+        qa[s] = i * IW + (m - i * Wo);
+    }
+}
+
+// Lane l holds D[4*(l/16) + v][l % 16] of each 16 x 16 block: 4 consecutive
+// outputs m of output channel co = block column l % 16, which are 4
+// consecutive floats of the plane (one 16-byte store when Wo % 4 == 0).
+__device__ __forceinline__ void store_blocks(const floatx4_t (*acc)[4], int nb, int b0, int lane,
+                                             float *y, int n, int Cout, int cb, int Ho, int Wo,
+                                             int ho0, int outs)
+{
+    const int64_t plane = int64_t(Ho) * Wo;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const int co = cb * 64 + c * 16 + (lane & 15);
+        if (co >= Cout) continue;
+        float *yb = y + (int64_t(n) * Cout + co) * plane + int64_t(ho0) * Wo;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            if (s >= nb) break;
+            const int m = (b0 + s) * 16 + (lane >> 4) * 4;
+            if ((Wo & 3) == 0) {
+                if (m < outs) *reinterpret_cast<floatx4_t *>(yb + m) = acc[s][c];
+            } else {
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    if (m + v < outs) yb[m + v] = acc[s][c][v];
+            }
+        }
+    }
+}
+
 template <int KH, int KW, bool BF16>
 __global__ __launch_bounds__(kRowsThreads) void conv_implicit_rows_kernel(const RowsKArgs a)
 {
@@ -171,69 +222,58 @@ __global__ __launch_bounds__(kRowsThreads) void conv_implicit_rows_kernel(const 
     }
     __syncthreads();
 
-    // ---- wave i: output row ho0 + i, 64 columns x 64 channels ----------------
+    // ---- this wave's output blocks: up to 64 outputs x 64 channels -----------
     const int wave = tid >> 6;
     const int lane = tid & 63;
-    if (wave >= rw) return;
+    const int outs = rw * a.Wo;
+    int b0, nb;
+    wave_blocks(wave, outs, b0, nb);
+    if (nb == 0) return;
     floatx4_t acc[4][4];
 #pragma unroll
     for (int s = 0; s < 4; ++s)
 #pragma unroll
         for (int c = 0; c < 4; ++c) acc[s][c] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-    // this lane's A row (output column) of each 16-column block, at tap (0, 0);
-    // columns past Wo read column Wo-1 and are never stored
     int qa[4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) qa[s] = wave * a.IW + min(s * 16 + (lane & 15), a.Wo - 1);
+    block_bases(qa, b0, lane, outs, a.Wo, a.IW);
     const int rb = lane & 15;                        // this lane's B column (co) in a block
+    // one compiled contraction per block count, so the unrolled K loop holds
+    // no run-time test
+    auto contract = [&](auto nbc) {
+        constexpr int NBW = decltype(nbc)::value;
 #pragma unroll
-    for (int kh = 0; kh < KH; ++kh) {
+        for (int kh = 0; kh < KH; ++kh) {
 #pragma unroll
-        for (int kw = 0; kw < KW; ++kw) {
-            const uint16_t *ft = fl + (kh * KW + kw) * 64 * CIN;
-            const int dq = kh * a.IW + kw;
+            for (int kw = 0; kw < KW; ++kw) {
+                const uint16_t *ft = fl + (kh * KW + kw) * 64 * CIN;
+                const int dq = kh * a.IW + kw;
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                const int gr = kk * 4 + (lane >> 4);
-                uint4 af[4], bf[4];
+                for (int kk = 0; kk < 2; ++kk) {
+                    const int gr = kk * 4 + (lane >> 4);
+                    uint4 af[NBW], bf[4];
 #pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    const int q = qa[s] + dq;
-                    af[s] = *reinterpret_cast<const uint4 *>(patch + q * CIN + ((gr ^ (q & 7)) << 3));
+                    for (int s = 0; s < NBW; ++s) {
+                        const int q = qa[s] + dq;
+                        af[s] = *reinterpret_cast<const uint4 *>(patch + q * CIN + ((gr ^ (q & 7)) << 3));
+                    }
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        const int r = c * 16 + rb;
+                        bf[c] = *reinterpret_cast<const uint4 *>(ft + r * CIN + ((gr ^ (r & 7)) << 3));
+                    }
+#pragma unroll
+                    for (int s = 0; s < NBW; ++s)
+#pragma unroll
+                        for (int c = 0; c < 4; ++c) acc[s][c] = mfma16x16x32<BF16>(af[s], bf[c], acc[s][c]);
                 }
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    const int r = c * 16 + rb;
-                    bf[c] = *reinterpret_cast<const uint4 *>(ft + r * CIN + ((gr ^ (r & 7)) << 3));
-                }
-#pragma unroll
-                for (int s = 0; s < 4; ++s)
-#pragma unroll
-                    for (int c = 0; c < 4; ++c) acc[s][c] = mfma16x16x32<BF16>(af[s], bf[c], acc[s][c]);
             }
         }
-    }
-
-    // ---- store: lane holds D[4*(lane/16) + v][lane % 16] of each block -------
-    const int ho = ho0 + wave;
-    const int64_t plane = int64_t(a.Ho) * a.Wo;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        const int co = cb * 64 + c * 16 + rb;
-        if (co >= a.Cout) continue;
-        float *yrow = a.y + (int64_t(n) * a.Cout + co) * plane + int64_t(ho) * a.Wo;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const int m = s * 16 + (lane >> 4) * 4;
-            if ((a.Wo & 3) == 0) {
-                if (m < a.Wo) *reinterpret_cast<floatx4_t *>(yrow + m) = acc[s][c];
-            } else {
-#pragma unroll
-                for (int v = 0; v < 4; ++v)
-                    if (m + v < a.Wo) yrow[m + v] = acc[s][c][v];
-            }
-        }
-    }
+    };
+    if (nb >= 4) contract(std::integral_constant<int, 4>{});
+    else if (nb == 3) contract(std::integral_constant<int, 3>{});
+    else if (nb == 2) contract(std::integral_constant<int, 2>{});
+    else contract(std::integral_constant<int, 1>{});
+    store_blocks(acc, nb, b0, lane, a.y, n, a.Cout, cb, a.Ho, a.Wo, ho0, outs);
 }
 
 // fp32 form of the same row block on the matrix cores' fp32 multiply
@@ -300,9 +340,11 @@ __global__ __launch_bounds__(kRowsThreads) void conv_implicit_rows_f32_kernel(co
     for (int s = 0; s < 4; ++s)
 #pragma unroll
         for (int c = 0; c < 4; ++c) acc[s][c] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    const int outs = rw * a.Wo;
+    int b0, nb;
+    wave_blocks(wave, outs, b0, nb);
     int qa[4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) qa[s] = wave * a.IW + min(s * 16 + (lane & 15), a.Wo - 1);
+    block_bases(qa, b0, lane, outs, a.Wo, a.IW);
     const int rbl = lane & 15;
 
     for (int blk = 0; blk < nblk; ++blk) {
@@ -363,7 +405,9 @@ __global__ __launch_bounds__(kRowsThreads) void conv_implicit_rows_f32_kernel(co
         }
         __syncthreads();
 
-        if (wave < rw) {
+        // (fp32 MFMAs are long enough that the run-time block tests cost
+        // nothing; specialising per block count spills registers here)
+        if (nb > 0) {
 #pragma unroll
             for (int t = 0; t < TAPS; ++t) {
                 const float *ft = fl + t * 64 * CB;
@@ -375,7 +419,7 @@ __global__ __launch_bounds__(kRowsThreads) void conv_implicit_rows_f32_kernel(co
 #pragma unroll
                     for (int s = 0; s < 4; ++s) {
                         const int q = qa[s] + dq;
-                        af[s] = *reinterpret_cast<const floatx4_t *>(patch + q * CB + ((gr ^ (q & 7)) << 2));
+                        if (s < nb) af[s] = *reinterpret_cast<const floatx4_t *>(patch + q * CB + ((gr ^ (q & 7)) << 2));
                     }
 #pragma unroll
                     for (int c = 0; c < 4; ++c) {
@@ -385,35 +429,18 @@ __global__ __launch_bounds__(kRowsThreads) void conv_implicit_rows_f32_kernel(co
 #pragma unroll
                     for (int j = 0; j < 4; ++j)
 #pragma unroll
-                        for (int s = 0; s < 4; ++s)
+                        for (int s = 0; s < 4; ++s) {
+                            if (s >= nb) break;
 #pragma unroll
                             for (int c = 0; c < 4; ++c)
                                 acc[s][c] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[s][j], bf[c][j], acc[s][c], 0, 0, 0);
+                        }
                 }
             }
         }
     }
-    if (wave >= rw) return;
-
-    const int ho = ho0 + wave;
-    const int64_t plane = int64_t(a.Ho) * a.Wo;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        const int co = cb * 64 + c * 16 + rbl;
-        if (co >= a.Cout) continue;
-        float *yrow = a.y + (int64_t(n) * a.Cout + co) * plane + int64_t(ho) * a.Wo;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const int m = s * 16 + (lane >> 4) * 4;
-            if ((a.Wo & 3) == 0) {
-                if (m < a.Wo) *reinterpret_cast<floatx4_t *>(yrow + m) = acc[s][c];
-            } else {
-#pragma unroll
-                for (int v = 0; v < 4; ++v)
-                    if (m + v < a.Wo) yrow[m + v] = acc[s][c][v];
-            }
-        }
-    }
+    if (nb == 0) return;
+    store_blocks(acc, nb, b0, lane, a.y, n, a.Cout, cb, a.Ho, a.Wo, ho0, outs);
 }
 
 template <int KH, int KW>
@@ -487,7 +514,7 @@ hipError_t launch_conv_implicit_rows(const ImplicitArgs &h, hipStream_t s)
     if (h.f32) {
         // fp32: channel blocks of 32, whole rows of W % 4 == 0 elements
         if (h.Cin % 32 != 0 || h.Cin < 32 || h.stride != 1 || h.W % 4 != 0 || h.W < 4 || h.Wo < 1 ||
-            h.Wo > 64 || h.Wo != h.W + 2 * h.pad - h.KW + 1 || h.R < 1 || h.R > kRowsThreads / 64 ||
+            h.Wo > 64 || h.Wo != h.W + 2 * h.pad - h.KW + 1 || h.R < 1 || int64_t(h.R) * h.Wo > 512 ||
             h.Ho != h.H + 2 * h.pad - h.KH + 1 ||
             implicit_rows_lds_bytes(h.KH * h.KW, h.R + h.KH - 1, h.W + 2 * h.pad) > kImplicitMaxLdsBytes)
             return hipErrorInvalidValue;
@@ -496,7 +523,7 @@ hipError_t launch_conv_implicit_rows(const ImplicitArgs &h, hipStream_t s)
         return hipErrorInvalidValue;
     }
     if (h.Cin != 64 || h.stride != 1 || h.W % 8 != 0 || h.W < 8 || h.Wo < 1 || h.Wo > 64 ||
-        h.Wo != h.W + 2 * h.pad - h.KW + 1 || h.R < 1 || h.R > kRowsThreads / 64 ||
+        h.Wo != h.W + 2 * h.pad - h.KW + 1 || h.R < 1 || int64_t(h.R) * h.Wo > 512 ||
         h.Ho != h.H + 2 * h.pad - h.KH + 1 ||
         implicit_rows_lds_bytes(h.KH * h.KW, h.R + h.KH - 1, h.W + 2 * h.pad) > kImplicitMaxLdsBytes)
         return hipErrorInvalidValue;

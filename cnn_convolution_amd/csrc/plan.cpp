@@ -378,11 +378,11 @@ static void pick_implicit_fs(const conv2d_desc_t &d, int64_t Ho, int64_t Wo, con
 
 // Row-block implicit kernel: 64 input channels, stride 1, input rows a
 // multiple of 8 long, output rows of at most 64 columns, a 1x1 or 3x3
-// filter. A workgroup of eight waves takes RW <= 8 whole output rows of one
-// image (one per wave) and 64 output channels, with the raw filter and the
-// RW + KH - 1 input rows in LDS; no staged filter. RW is the one that needs
-// the fewest rounds of workgroups over the CUs, each round costing about its
-// rows plus a fixed set-up (the block's loads and barrier) of three rows.
+// filter. A workgroup of eight waves takes RW whole output rows of one image
+// (RW * Wo <= 512 outputs, 16-output blocks shared over the waves) and 64
+// output channels, with the raw filter and the RW + KH - 1 input rows in LDS;
+// no staged filter. RW minimises the rounds of workgroups over the CUs times
+// the busiest SIMD's blocks plus a fixed set-up.
 // Default where it applies; IM2WIN_IMPLICIT_KERNEL=streamed|stationary (or a
 // tile in IM2WIN_IMPLICIT_TILE) selects the other kernels; IM2WIN_IMPLICIT_ROWS
 // sets RW.
@@ -398,20 +398,34 @@ static void pick_implicit_rows(const conv2d_desc_t &d, int64_t Ho, int64_t Wo, c
     if (std::getenv("IM2WIN_IMPLICIT_TILE")) return;   // a streamed-kernel tile was asked for
     const int64_t iw = d.W + 2 * d.pad;
     const int64_t co_blocks = ceil_div(d.Cout, 64);
+    // the busiest SIMD's MFMA blocks: 16-output blocks shared over 8 waves in
+    // contiguous ranges, waves w and w + 4 on one SIMD
+    auto simd_blocks = [](int64_t outs) {
+        const int64_t total = ceil_div(outs, 16);
+        int64_t worst = 0;
+        for (int64_t sm = 0; sm < 4; ++sm) {
+            int64_t b = 0;
+            for (int64_t w = sm; w < 8; w += 4) b += (w + 1) * total / 8 - w * total / 8;
+            worst = std::max(worst, b);
+        }
+        return worst;
+    };
     int64_t best_rw = 0;
     double best_cost = 0.0;
-    for (int64_t rw = 1; rw <= 8 && rw <= Ho; ++rw) {
+    for (int64_t rw = 1; rw <= Ho && rw * Wo <= 512; ++rw) {
         const int64_t lds = implicit_rows_lds_bytes(taps, rw + d.KH - 1, iw);
         if (lds > kImplicitMaxLdsBytes) break;
         const int64_t per_cu = std::min<int64_t>(2, kImplicitMaxLdsBytes / lds);
         const int64_t blocks = co_blocks * d.N * ceil_div(Ho, rw);
-        const double cost = double(ceil_div(blocks, 256 * per_cu)) * double(rw + 3);
-        if (best_rw == 0 || cost <= best_cost) { best_rw = rw; best_cost = cost; }
+        // rounds of workgroups over the CUs, each costing its busiest SIMD's
+        // blocks plus a fixed set-up (the block's loads and barrier) worth 12
+        const double cost = double(ceil_div(blocks, 256 * per_cu)) * double(simd_blocks(rw * Wo) + 12);
+        if (best_rw == 0 || cost < best_cost) { best_rw = rw; best_cost = cost; }
     }
     if (best_rw == 0) return;
     if (const char *e = std::getenv("IM2WIN_IMPLICIT_ROWS")) {
         const int64_t v = std::min<int64_t>(std::atoi(e), Ho);
-        if (v >= 1 && v <= 8 && implicit_rows_lds_bytes(taps, v + d.KH - 1, iw) <= kImplicitMaxLdsBytes)
+        if (v >= 1 && v * Wo <= 512 && implicit_rows_lds_bytes(taps, v + d.KH - 1, iw) <= kImplicitMaxLdsBytes)
             best_rw = v;
     }
     p->kernel = 2;

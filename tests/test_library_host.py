@@ -367,7 +367,7 @@ def test_row_block_plan_geometry(monkeypatch):
             continue
         taken += 1
         R = pl.rows_per_tile
-        assert 1 <= R <= min(8, pl.Ho)
+        assert 1 <= R <= pl.Ho and R * pl.Wo <= 512
         assert pl.patch_rows == R + KH - 1 and pl.patch_cols == W + 2 * p
         assert pl.cols_per_tile == pl.Wo and pl.tile_m == 64 and pl.tile_n == 64
         assert pl.lds_bytes == KH * KW * 8192 + pl.patch_rows * pl.patch_cols * 128 <= 160 * 1024
