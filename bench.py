@@ -314,7 +314,8 @@ def _time_variant(cfg, dt, steps, warmup, dev):
         roof = {"bound": "hbm", "achieved": dom_bytes / kern_s / 1e9, "peak": HBM_GBPS,
                 "unit": "GB/s"}
     else:
-        roof = {"bound": "mfma" if dt != "f32" else "alu",
+        # fp32 runs on the matrix cores in the implicit form, on the vector ALUs otherwise
+        roof = {"bound": "mfma" if (dt != "f32" or plan.algo == 1) else "alu",
                 "achieved": dom_flops / kern_s / 1e12, "peak": peak, "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     # HBM bytes per launch from FETCH_SIZE + WRITE_SIZE counters scaled by a copy
@@ -369,7 +370,7 @@ def implicit_applies(cfg, dt):
     import cnn_convolution_amd as conv
     from cnn_convolution_amd import _lib
     d = conv.make_desc(cfg.N, cfg.Cin, cfg.H, cfg.W, cfg.Cout, cfg.KH, cfg.KW, cfg.stride,
-                       cfg.pad, {"f16": conv.F16, "bf16": conv.BF16}[dt])
+                       cfg.pad, {"f32": conv.F32, "f16": conv.F16, "bf16": conv.BF16}[dt])
     return _lib.implicit_plan_status(d) == 0
 
 
@@ -470,12 +471,18 @@ def main():
             _say(f"bench: {name} {dt} warmup={args.warmup} steps={args.steps}")
             results[dt] = time_variant(cfg, dt, args.steps, args.warmup, dev)
         h = results[head]
-        # the other form of the headline dtype, where the layer has both
-        other = None
-        if head != "f32" and implicit_applies(cfg, head):
-            alt = "window" if h["form"] == "implicit" else "implicit"
-            _say(f"bench: {name} {head} other form ({alt})")
-            other = time_variant(cfg, head, args.steps, args.warmup, dev, algo=alt)
+        # the other form of each dtype, where the layer has both (for fp32 the
+        # other form is the vector-ALU window form, or the matrix-core implicit one)
+        others = {}
+        for dt in order:
+            if implicit_applies(cfg, dt):
+                alt = "window" if results[dt]["form"] == "implicit" else "implicit"
+                _say(f"bench: {name} {dt} other form ({alt})")
+                others[dt] = time_variant(cfg, dt, args.steps, args.warmup, dev, algo=alt)
+        other = others.get(head)
+        for dt in order[1:]:
+            if dt in others:
+                results[dt]["other_form"] = others[dt]
         line = {
             "metric": METRIC, "value": h["value"], "unit": "TFLOPS", "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": h["ms_per_step"],
