@@ -33,6 +33,7 @@ SOURCES = [
     os.path.join(CSRC, "kernels", "conv_implicit.hip"),
     os.path.join(CSRC, "kernels", "conv_implicit_fs.hip"),
     os.path.join(CSRC, "kernels", "conv_implicit_rows.hip"),
+    os.path.join(CSRC, "kernels", "conv_implicit_narrow.hip"),
 ]
 
 ARCH = "gfx950"

@@ -166,6 +166,7 @@ ImplicitArgs implicit_args(const conv2d_desc_t &d, const conv2d_implicit_plan_t 
     a.stages = p.stages;
     a.bf16 = d.dtype == CONV2D_BF16 ? 1 : 0;
     a.f32 = d.dtype == CONV2D_F32 ? 1 : 0;
+    a.narrow_cp = p.kernel == 3 ? p.stages : 0;
     a.fs_groups = int(p.tiles / ((d.Cout + 63) / 64));
     return a;
 }
@@ -173,6 +174,7 @@ ImplicitArgs implicit_args(const conv2d_desc_t &d, const conv2d_implicit_plan_t 
 hipError_t launch_implicit(const conv2d_implicit_plan_t &p, const ImplicitArgs &a, hipStream_t s)
 {
     if (p.kernel == 2) return launch_conv_implicit_rows(a, s);
+    if (p.kernel == 3) return launch_conv_implicit_narrow(a, s);
     return p.kernel == 1 ? launch_conv_implicit_fs(a, s) : launch_conv_implicit(a, s);
 }
 
@@ -193,9 +195,10 @@ conv2d_status_t run_implicit(const conv2d_desc_t &d, const conv2d_implicit_plan_
         sa.Cin = int(d.Cin);
         sa.KH = int(d.KH);
         sa.KW = int(d.KW);
-        sa.Cin_pad = int(g.Cin_pad);
+        // the narrow-channel kernel: CP channels per position, rows of Kp
+        sa.Cin_pad = p.kernel == 3 ? p.stages : int(g.Cin_pad);
         sa.rows = int(sg.rows);
-        sa.row_len = int(sg.row_len);
+        sa.row_len = p.kernel == 3 ? int(p.K_stage) : int(sg.row_len);
         sa.esize = int(elem_size(d.dtype));
         ProfScope ps(s, CONV2D_KERNEL_WEIGHT_STAGE);
         if (launch_stage_cl(sa, s) != hipSuccess) return CONV2D_ERR_HIP;

@@ -1,0 +1,496 @@
+// Implicit im2win convolution for layers with few input channels (Cin <= 8:
+// the RGB stem and its kind), fp16 / bf16 and fp32, on the matrix cores.
+//
+// With a handful of channels the window rows of Eq. (2) of "Enabling
+// Memory-efficient Im2win Convolution with Multi-precision Support on GPU
+// CUDA and Tensor Cores" (Sec. III-B) are short in channels and long in
+// positions, so they are built in LDS in the channels-last order of the
+// window tensor: window row ho holds, for every column w < W_win =
+// (Wo - 1) * s + KW and filter row kh, the CP (4 or 8, zero-padded) channels
+// of input position (ho * s - pad + kh, w - pad). The window of output
+// column wo is then ONE contiguous run of K = KW * KH * CP elements starting
+// at wo * s * KH * CP, contracted against the filter staged in the same K
+// order (kw, kh, ci) (Sec. III-C Eq. (3), Sec. III-D) — the contraction of the
+// window form with the window rows in LDS instead of HBM.
+//
+// A workgroup of eight waves owns a block of 64 output channels and walks a
+// contiguous range of row blocks (R output rows of one image, R * Wo <= 512).
+// It stages its filter block into LDS once (64 rows of Kp elements, Kp = K
+// rounded up to the MFMA K step, zero past K, as the channels-last filter
+// staging writes it into the workspace; each LDS row 16 bytes longer than Kp
+// so that the 16 rows a fragment read touches fall in different bank groups).
+// Per row block it builds the R window rows (zero outside the image; the
+// gathers of the next row block are in flight while this one is contracted
+// and stored), and after a barrier each wave contracts its 16-output blocks
+// of the flattened R x Wo outputs. The elements past K
+// in a run are the next columns' window elements (or zeroed slack at the end
+// of a row) and meet zero filter taps. The product is formed transposed,
+// D[output][co], and stored as 16-byte vectors, or through an LDS transpose
+// where output rows are not a multiple of 4 long (out_blocks.hpp).
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <type_traits>
+
+#include "../launch.hpp"
+#include "lds_dma.hpp"
+#include "out_blocks.hpp"
+#include "tile_map.hpp"
+
+namespace im2win {
+namespace {
+
+constexpr int kNarrowThreads = 512;
+
+struct NarrowKArgs {
+    const void *x;
+    const void *w;
+    float *y;
+    int Cin, H, W, Cout, KH, KW, stride, pad, Ho, Wo;
+    int K, Kp;              // window run KW*KH*CP and its padded length
+    int Wwin;               // (Wo - 1) * stride + KW
+    int L, Lp;              // window row elements W_win*KH*CP, and per row in LDS (with slack)
+    int R, row_groups, co_blocks;
+    int groups;             // workgroups per 64-channel block (gridDim.x / co_blocks)
+};
+
+// The filter block: the staged rows [Cout][Kp] (16-byte vectors; rows past
+// Cout read row Cout-1, never stored) into LDS rows of FS elements, FB
+// vectors per thread in flight at a time.
+template <int FB, typename T>
+__device__ __forceinline__ void load_filter(const NarrowKArgs &a, const T *wst, T *fl, int FS, int cb, int tid)
+{
+    constexpr int V = 16 / sizeof(T);
+    const int fv_row = a.Kp / V;
+    const int fvec = 64 * fv_row;
+    for (int f0 = 0; f0 < fvec; f0 += FB * kNarrowThreads) {
+        uint4 fv[FB];
+#pragma unroll
+        for (int j = 0; j < FB; ++j) {
+            const int v = min(f0 + tid + j * kNarrowThreads, fvec - 1);
+            const int r = v / fv_row;
+            const int row = min(cb * 64 + r, a.Cout - 1);
+            fv[j] = *reinterpret_cast<const uint4 *>(wst + int64_t(row) * a.Kp + (v - r * fv_row) * V);
+        }
+#pragma unroll
+        for (int j = 0; j < FB; ++j) {
+            const int v = f0 + tid + j * kNarrowThreads;
+            if (v < fvec) {
+                const int r = v / fv_row;
+                *reinterpret_cast<uint4 *>(fl + r * FS + (v - r * fv_row) * V) = fv[j];
+            }
+        }
+    }
+}
+
+// The rw window rows of output rows ho0 .. ho0+rw-1: units (row i, filter row
+// kh, window column wc), consecutive lanes on consecutive input columns so
+// that each load instruction reads one contiguous stretch of an input row; a
+// unit writes the CP channels of position (wc, kh) as one vector. A thread
+// holds UB units per round: fetch_window issues a round's loads into
+// registers, put_window writes them (and, on the last round, zeroes the slack
+// after each row), so that the next row block's loads can be in flight while
+// the current one is contracted.
+template <int CP, int UB, typename T>
+struct WinRegs {
+    T v[UB][CP];
+    bool in[UB];
+};
+
+template <int CP, int UB, typename T>
+__device__ __forceinline__ void fetch_window(const NarrowKArgs &a, const T *ximg, int ho0, int rw, int u0,
+                                             int tid, WinRegs<CP, UB, T> &r)
+{
+    const int upr = a.KH * a.Wwin;
+    const int units = rw * upr;
+    const int HW = a.H * a.W;
+#pragma unroll
+    for (int j = 0; j < UB; ++j) {
+        const int u = min(u0 + tid + j * kNarrowThreads, units - 1);
+        const int i = u / upr;
+        const int q = u - i * upr;
+        const int kh = q / a.Wwin;
+        const int wc = q - kh * a.Wwin;
+        const int ih = (ho0 + i) * a.stride - a.pad + kh;
+        const int iw = wc - a.pad;
+        r.in[j] = unsigned(ih) < unsigned(a.H) && unsigned(iw) < unsigned(a.W);
+        const int src = r.in[j] ? ih * a.W + iw : 0;
+#pragma unroll
+        for (int c = 0; c < CP; ++c) r.v[j][c] = ximg[min(c, a.Cin - 1) * HW + src];
+    }
+}
+
+template <int CP, int UB, typename T>
+__device__ __forceinline__ void put_window(const NarrowKArgs &a, T *win, int rw, int u0, int tid,
+                                           const WinRegs<CP, UB, T> &r)
+{
+    constexpr int V = 16 / sizeof(T);
+    const int upr = a.KH * a.Wwin;
+    const int units = rw * upr;
+#pragma unroll
+    for (int j = 0; j < UB; ++j) {
+        const int u = u0 + tid + j * kNarrowThreads;
+        if (u >= units) break;
+        const int i = u / upr;
+        const int q = u - i * upr;
+        const int kh = q / a.Wwin;
+        const int wc = q - kh * a.Wwin;
+        T o[CP];
+#pragma unroll
+        for (int c = 0; c < CP; ++c) o[c] = (r.in[j] && c < a.Cin) ? r.v[j][c] : T(0);
+        T *dst = win + i * a.Lp + (wc * a.KH + kh) * CP;
+        if constexpr (CP * sizeof(T) == 8) {
+            uint2 q2;
+            __builtin_memcpy(&q2, o, 8);
+            *reinterpret_cast<uint2 *>(dst) = q2;
+        } else {
+#pragma unroll
+            for (int c = 0; c < CP; c += V) {
+                uint4 q4;
+                __builtin_memcpy(&q4, o + c, 16);
+                *reinterpret_cast<uint4 *>(dst + c) = q4;
+            }
+        }
+    }
+    if (u0 + UB * kNarrowThreads >= units) {
+        const int slack = a.Lp - a.L;
+        for (int v = tid; v < rw * slack; v += kNarrowThreads) {
+            const int i = v / slack;
+            win[i * a.Lp + a.L + (v - i * slack)] = T(0);
+        }
+    }
+}
+
+// One row block per workgroup: the filter block's vectors (FB per thread) and
+// the window units (UB per thread) of a round all in flight together, then
+// written; normally a single round.
+template <int CP, int FB, int UB, typename T>
+__device__ __forceinline__ void load_block(const NarrowKArgs &a, const T *ximg, const T *wst, T *fl, T *win,
+                                           int FS, int cb, int ho0, int rw, int tid)
+{
+    constexpr int V = 16 / sizeof(T);
+    const int fv_row = a.Kp / V;
+    const int fvec = 64 * fv_row;
+    const int units = rw * a.KH * a.Wwin;
+    for (int f0 = 0, u0 = 0; f0 < fvec || u0 < units; f0 += FB * kNarrowThreads, u0 += UB * kNarrowThreads) {
+        uint4 fv[FB];
+#pragma unroll
+        for (int j = 0; j < FB; ++j) {
+            const int v = min(f0 + tid + j * kNarrowThreads, fvec - 1);
+            const int r = v / fv_row;
+            const int row = min(cb * 64 + r, a.Cout - 1);
+            fv[j] = *reinterpret_cast<const uint4 *>(wst + int64_t(row) * a.Kp + (v - r * fv_row) * V);
+        }
+        WinRegs<CP, UB, T> wr;
+        if (u0 < units) fetch_window(a, ximg, ho0, rw, u0, tid, wr);
+#pragma unroll
+        for (int j = 0; j < FB; ++j) {
+            const int v = f0 + tid + j * kNarrowThreads;
+            if (v < fvec) {
+                const int r = v / fv_row;
+                *reinterpret_cast<uint4 *>(fl + r * FS + (v - r * fv_row) * V) = fv[j];
+            }
+        }
+        if (u0 < units) put_window(a, win, rw, u0, tid, wr);
+    }
+}
+
+// this workgroup's row blocks [t_begin, t_end): image and first output row
+__device__ __forceinline__ void task_rows(const NarrowKArgs &a, int t, int &n, int &ho0, int &rw)
+{
+    n = t / a.row_groups;
+    ho0 = (t - n * a.row_groups) * a.R;
+    rw = min(a.R, a.Ho - ho0);
+}
+
+// ---- fp16 / bf16 -------------------------------------------------------------
+template <int CP, bool BF16, bool PIPE>
+__global__ __launch_bounds__(kNarrowThreads) void conv_implicit_narrow_kernel(const NarrowKArgs a, int ntasks)
+{
+    extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
+    const int FS = a.Kp + 8;                         // filter row stride in LDS (elements)
+    uint16_t *const fl = lds;                        // [64][FS]
+    uint16_t *const win = lds + 64 * FS;             // [R][Lp], then the store scratch
+
+    const int cb = blockIdx.x % a.co_blocks;
+    const int g = blockIdx.x / a.co_blocks;
+    const int t_begin = int(int64_t(ntasks) * g / a.groups);
+    const int t_end = int(int64_t(ntasks) * (g + 1) / a.groups);
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const uint16_t *const wst = static_cast<const uint16_t *>(a.w);   // staged [Cout][Kp]
+    constexpr int UB = CP == 4 ? 16 : 8;
+    constexpr int UBR = UB * kNarrowThreads;         // window units per round
+    const uint16_t *const x = static_cast<const uint16_t *>(a.x);
+    const int64_t img = int64_t(a.Cin) * a.H * a.W;
+    // contraction and stores of one row block, after its window rows are in LDS
+    auto run_block = [&](int n, int ho0, int rw) {
+        const int outs = rw * a.Wo;
+        int b0, nb;
+        wave_blocks(wave, outs, b0, nb);
+        // this lane's window run (A row) of each block and filter row (B column)
+        int abase[4];
+        const int step = a.stride * a.KH * CP;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const int m = min((b0 + s) * 16 + (lane & 15), outs - 1);
+            const int i = m / a.Wo;
+            abase[s] = i * a.Lp + (m - i * a.Wo) * step + 8 * (lane >> 4);
+        }
+        const int bbase = (lane & 15) * FS + 8 * (lane >> 4);
+        floatx4_t acc[4][4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) acc[s][c] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+        const int nk = a.Kp >> 5;
+        auto contract = [&](auto nbc) {
+            constexpr int NBW = decltype(nbc)::value;
+#pragma unroll 2
+            for (int kk = 0; kk < nk; ++kk) {
+                uint4 af[NBW], bf[4];
+#pragma unroll
+                for (int s = 0; s < NBW; ++s) af[s] = *reinterpret_cast<const uint4 *>(win + abase[s] + kk * 32);
+#pragma unroll
+                for (int c = 0; c < 4; ++c) bf[c] = *reinterpret_cast<const uint4 *>(fl + bbase + c * 16 * FS + kk * 32);
+#pragma unroll
+                for (int s = 0; s < NBW; ++s)
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) acc[s][c] = mfma16x16x32<BF16>(af[s], bf[c], acc[s][c]);
+            }
+        };
+        if (nb >= 4) contract(std::integral_constant<int, 4>{});
+        else if (nb == 3) contract(std::integral_constant<int, 3>{});
+        else if (nb == 2) contract(std::integral_constant<int, 2>{});
+        else if (nb == 1) contract(std::integral_constant<int, 1>{});
+        if ((a.Wo & 3) == 0) {
+            if (nb > 0) store_blocks(acc, nb, b0, lane, a.y, n, a.Cout, cb, a.Ho, a.Wo, ho0, outs);
+        } else {
+            __syncthreads();                         // the window rows are dead: their LDS is store scratch
+            if (nb > 0)
+                store_blocks_lds(acc, nb, b0, lane, reinterpret_cast<float *>(win) + wave * kStoreScratchFloats,
+                                 a.y, n, a.Cout, cb, a.Ho, a.Wo, ho0, outs);
+        }
+    };
+    if constexpr (!PIPE) {
+        // one row block: filter and window loads in one round trip
+        int n, ho0, rw;
+        task_rows(a, t_begin, n, ho0, rw);
+        load_block<CP, 4, UB>(a, x + n * img, wst, fl, win, FS, cb, ho0, rw, tid);
+        __syncthreads();
+        run_block(n, ho0, rw);
+    } else {
+        // persistent: the filter once; the first round of each row block's
+        // gathers in flight during the previous block's contraction (the
+        // first block's together with the filter loads)
+        WinRegs<CP, UB, uint16_t> nxt;
+        {
+            int n, ho0, rw;
+            task_rows(a, t_begin, n, ho0, rw);
+            fetch_window(a, x + n * img, ho0, rw, 0, tid, nxt);
+        }
+        load_filter<4>(a, wst, fl, FS, cb, tid);
+        for (int t = t_begin; t < t_end; ++t) {
+            int n, ho0, rw;
+            task_rows(a, t, n, ho0, rw);
+            if (t != t_begin) __syncthreads();       // the previous block's window rows (scratch) are dead
+            put_window(a, win, rw, 0, tid, nxt);
+            for (int u0 = UBR; u0 < rw * a.KH * a.Wwin; u0 += UBR) {
+                WinRegs<CP, UB, uint16_t> more;
+                fetch_window(a, x + n * img, ho0, rw, u0, tid, more);
+                put_window(a, win, rw, u0, tid, more);
+            }
+            if (t + 1 < t_end) {
+                int n1, h1, r1;
+                task_rows(a, t + 1, n1, h1, r1);
+                fetch_window(a, x + n1 * img, h1, r1, 0, tid, nxt);
+            }
+            __syncthreads();
+            run_block(n, ho0, rw);
+        }
+    }
+}
+
+// ---- fp32: v_mfma_f32_16x16x4_f32; K in slices of 16 elements, lane group
+// g = lane / 16 holding elements 4g .. 4g + 3 of a slice as one vector and
+// feeding element j to K step j (window runs and filter alike) -------------
+template <int CP, bool PIPE>
+__global__ __launch_bounds__(kNarrowThreads) void conv_implicit_narrow_f32_kernel(const NarrowKArgs a, int ntasks)
+{
+    extern __shared__ __attribute__((aligned(16))) float ldsf[];
+    const int FS = a.Kp + 4;
+    float *const fl = ldsf;                          // [64][FS]
+    float *const win = ldsf + 64 * FS;               // [R][Lp], then the store scratch
+
+    const int cb = blockIdx.x % a.co_blocks;
+    const int g = blockIdx.x / a.co_blocks;
+    const int t_begin = int(int64_t(ntasks) * g / a.groups);
+    const int t_end = int(int64_t(ntasks) * (g + 1) / a.groups);
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const float *const wst = static_cast<const float *>(a.w);         // staged [Cout][Kp]
+    constexpr int UB = CP == 4 ? 16 : 8;
+    constexpr int UBR = UB * kNarrowThreads;         // window units per round
+    const float *const x = static_cast<const float *>(a.x);
+    const int64_t img = int64_t(a.Cin) * a.H * a.W;
+    // contraction and stores of one row block, after its window rows are in LDS
+    auto run_block = [&](int n, int ho0, int rw) {
+        const int outs = rw * a.Wo;
+        int b0, nb;
+        wave_blocks(wave, outs, b0, nb);
+        int abase[4];
+        const int step = a.stride * a.KH * CP;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const int m = min((b0 + s) * 16 + (lane & 15), outs - 1);
+            const int i = m / a.Wo;
+            abase[s] = i * a.Lp + (m - i * a.Wo) * step + 4 * (lane >> 4);
+        }
+        const int bbase = (lane & 15) * FS + 4 * (lane >> 4);
+        floatx4_t acc[4][4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) acc[s][c] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+        const int nsl = nb > 0 ? a.Kp >> 4 : 0;
+        for (int sl = 0; sl < nsl; ++sl) {
+            floatx4_t af[4], bf[4];
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                if (s < nb) af[s] = *reinterpret_cast<const floatx4_t *>(win + abase[s] + sl * 16);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) bf[c] = *reinterpret_cast<const floatx4_t *>(fl + bbase + c * 16 * FS + sl * 16);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    if (s >= nb) break;
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+                        acc[s][c] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[s][j], bf[c][j], acc[s][c], 0, 0, 0);
+                }
+        }
+        if ((a.Wo & 3) == 0) {
+            if (nb > 0) store_blocks(acc, nb, b0, lane, a.y, n, a.Cout, cb, a.Ho, a.Wo, ho0, outs);
+        } else {
+            __syncthreads();
+            if (nb > 0)
+                store_blocks_lds(acc, nb, b0, lane, win + wave * kStoreScratchFloats, a.y, n, a.Cout, cb, a.Ho,
+                                 a.Wo, ho0, outs);
+        }
+    };
+    if constexpr (!PIPE) {
+        // one row block: filter and window loads in one round trip
+        int n, ho0, rw;
+        task_rows(a, t_begin, n, ho0, rw);
+        load_block<CP, 4, UB>(a, x + n * img, wst, fl, win, FS, cb, ho0, rw, tid);
+        __syncthreads();
+        run_block(n, ho0, rw);
+    } else {
+        // persistent: the filter once; the first round of each row block's
+        // gathers in flight during the previous block's contraction (the
+        // first block's together with the filter loads)
+        WinRegs<CP, UB, float> nxt;
+        {
+            int n, ho0, rw;
+            task_rows(a, t_begin, n, ho0, rw);
+            fetch_window(a, x + n * img, ho0, rw, 0, tid, nxt);
+        }
+        load_filter<4>(a, wst, fl, FS, cb, tid);
+        for (int t = t_begin; t < t_end; ++t) {
+            int n, ho0, rw;
+            task_rows(a, t, n, ho0, rw);
+            if (t != t_begin) __syncthreads();       // the previous block's window rows (scratch) are dead
+            put_window(a, win, rw, 0, tid, nxt);
+            for (int u0 = UBR; u0 < rw * a.KH * a.Wwin; u0 += UBR) {
+                WinRegs<CP, UB, float> more;
+                fetch_window(a, x + n * img, ho0, rw, u0, tid, more);
+                put_window(a, win, rw, u0, tid, more);
+            }
+            if (t + 1 < t_end) {
+                int n1, h1, r1;
+                task_rows(a, t + 1, n1, h1, r1);
+                fetch_window(a, x + n1 * img, h1, r1, 0, tid, nxt);
+            }
+            __syncthreads();
+            run_block(n, ho0, rw);
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_conv_implicit_narrow(const ImplicitArgs &h, hipStream_t s)
+{
+    const int cp = h.narrow_cp;
+    const int kstep = h.f32 ? 16 : 32;
+    NarrowKArgs a{};
+    a.x = h.x;
+    a.w = h.wst;
+    a.y = h.y;
+    a.Cin = h.Cin;
+    a.H = h.H;
+    a.W = h.W;
+    a.Cout = h.Cout;
+    a.KH = h.KH;
+    a.KW = h.KW;
+    a.stride = h.stride;
+    a.pad = h.pad;
+    a.Ho = h.Ho;
+    a.Wo = h.Wo;
+    a.K = h.KW * h.KH * cp;
+    a.Kp = (a.K + kstep - 1) / kstep * kstep;
+    a.Wwin = (h.Wo - 1) * h.stride + h.KW;
+    a.L = a.Wwin * h.KH * cp;
+    const int vec = h.f32 ? 4 : 8;
+    a.Lp = (a.L + a.Kp - a.K + vec - 1) / vec * vec;
+    a.R = h.R;
+    a.row_groups = (h.Ho + h.R - 1) / h.R;
+    a.co_blocks = (h.Cout + 63) / 64;
+    // the kernel's assumptions: CP channels hold Cin, every window start is a
+    // whole 16-byte vector, the outputs of a block fit 32 MFMA blocks, and
+    // element offsets of the image fit 32 bits
+    const int es = h.f32 ? 4 : 2;
+    if ((cp != 4 && cp != 8) || h.Cin < 1 || h.Cin > cp || (h.stride * h.KH * cp * es) % 16 != 0 ||
+        h.kstage != a.Kp || h.R < 1 || int64_t(h.R) * h.Wo > 512 || h.Wo < 1 || h.Ho < 1 ||
+        int64_t(h.Cin) * h.H * h.W >= (int64_t(1) << 31) ||
+        int64_t(h.Cout) * h.Cin * h.KH * h.KW >= (int64_t(1) << 31) ||
+        implicit_narrow_lds_bytes(es, a.Kp, a.Lp, h.R) > kImplicitMaxLdsBytes)
+        return hipErrorInvalidValue;
+    // workgroups: co_blocks x groups, each group walking a contiguous range of
+    // the N * row_groups row blocks with its filter block staged once
+    a.groups = h.fs_groups;
+    int ntasks = h.N * a.row_groups;
+    const int64_t blocks = int64_t(a.co_blocks) * a.groups;
+    if (a.groups < 1 || a.groups > ntasks || blocks > 0x7fffffff) return hipErrorInvalidValue;
+    const size_t lds = size_t(implicit_narrow_lds_bytes(es, a.Kp, a.Lp, h.R));
+    // one row block per workgroup, or persistent workgroups that prefetch the
+    // next row block's gathers (more registers: one workgroup per CU)
+    const bool pipe = a.groups < ntasks;
+    const void *kern;
+#define IM2WIN_NARROW_PICK(P)                                                                                      \
+    if (h.f32) kern = cp == 4 ? reinterpret_cast<const void *>(conv_implicit_narrow_f32_kernel<4, P>)              \
+                              : reinterpret_cast<const void *>(conv_implicit_narrow_f32_kernel<8, P>);             \
+    else if (h.bf16) kern = cp == 4 ? reinterpret_cast<const void *>(conv_implicit_narrow_kernel<4, true, P>)      \
+                                    : reinterpret_cast<const void *>(conv_implicit_narrow_kernel<8, true, P>);     \
+    else kern = cp == 4 ? reinterpret_cast<const void *>(conv_implicit_narrow_kernel<4, false, P>)                 \
+                        : reinterpret_cast<const void *>(conv_implicit_narrow_kernel<8, false, P>);
+    if (pipe) {
+        IM2WIN_NARROW_PICK(true)
+    } else {
+        IM2WIN_NARROW_PICK(false)
+    }
+#undef IM2WIN_NARROW_PICK
+    if (lds > 64 * 1024) {
+        const hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+        if (e != hipSuccess) return e;
+    }
+    void *args[] = {&a, &ntasks};
+    const hipError_t e = hipLaunchKernel(kern, dim3(unsigned(blocks)), dim3(kNarrowThreads), args, lds, s);
+    if (e != hipSuccess) return e;
+    return hipGetLastError();
+}
+
+}  // namespace im2win

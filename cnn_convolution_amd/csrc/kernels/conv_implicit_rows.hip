@@ -34,6 +34,7 @@
 
 #include "../launch.hpp"
 #include "lds_dma.hpp"
+#include "out_blocks.hpp"
 #include "tile_map.hpp"
 
 namespace im2win {
@@ -58,19 +59,8 @@ __device__ __forceinline__ uint32_t dword_of(const uint4 &v, int d)
     return d == 0 ? v.x : d == 1 ? v.y : d == 2 ? v.z : v.w;
 }
 
-// The rw x Wo outputs of a workgroup, flattened (i * Wo + wo, which is also
-// their order inside each output plane), are cut into MFMA blocks of 16 and
-// shared out over the eight waves in contiguous ranges of at most 4 blocks.
-// Lane l of a block works on output m = 16 * block + l % 16 (clamped to the
-// last output: such lanes read a valid window and store nothing); its window
-// at tap (0, 0) starts at patch position i * IW + wo.
-__device__ __forceinline__ void wave_blocks(int wave, int outs, int &b0, int &nb)
-{
-    const int total = (outs + 15) >> 4;
-    b0 = wave * total / 8;
-    nb = (wave + 1) * total / 8 - b0;
-}
-
+// Patch position of the window at tap (0, 0) of each of a lane's output
+// blocks (output m = i * Wo + wo: input row i, column wo of the patch).
 __device__ __forceinline__ void block_bases(int *qa, int b0, int lane, int outs, int Wo, int IW)
 {
 #pragma unroll
@@ -78,34 +68,6 @@ __device__ __forceinline__ void block_bases(int *qa, int b0, int lane, int outs,
         const int m = min((b0 + s) * 16 + (lane & 15), outs - 1);
         const int i = m / Wo;
         qa[s] = i * IW + (m - i * Wo);
-    }
-}
-
-// Lane l holds D[4*(l/16) + v][l % 16] of each 16 x 16 block: 4 consecutive
-// outputs m of output channel co = block column l % 16, which are 4
-// consecutive floats of the plane (one 16-byte store when Wo % 4 == 0).
-__device__ __forceinline__ void store_blocks(const floatx4_t (*acc)[4], int nb, int b0, int lane,
-                                             float *y, int n, int Cout, int cb, int Ho, int Wo,
-                                             int ho0, int outs)
-{
-    const int64_t plane = int64_t(Ho) * Wo;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        const int co = cb * 64 + c * 16 + (lane & 15);
-        if (co >= Cout) continue;
-        float *yb = y + (int64_t(n) * Cout + co) * plane + int64_t(ho0) * Wo;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            if (s >= nb) break;
-            const int m = (b0 + s) * 16 + (lane >> 4) * 4;
-            if ((Wo & 3) == 0) {
-                if (m < outs) *reinterpret_cast<floatx4_t *>(yb + m) = acc[s][c];
-            } else {
-#pragma unroll
-                for (int v = 0; v < 4; ++v)
-                    if (m + v < outs) yb[m + v] = acc[s][c][v];
-            }
-        }
     }
 }
 
@@ -228,7 +190,6 @@ __global__ __launch_bounds__(kRowsThreads) void conv_implicit_rows_kernel(const 
     const int outs = rw * a.Wo;
     int b0, nb;
     wave_blocks(wave, outs, b0, nb);
-    if (nb == 0) return;
     floatx4_t acc[4][4];
 #pragma unroll
     for (int s = 0; s < 4; ++s)
@@ -272,8 +233,15 @@ __global__ __launch_bounds__(kRowsThreads) void conv_implicit_rows_kernel(const 
     if (nb >= 4) contract(std::integral_constant<int, 4>{});
     else if (nb == 3) contract(std::integral_constant<int, 3>{});
     else if (nb == 2) contract(std::integral_constant<int, 2>{});
-    else contract(std::integral_constant<int, 1>{});
-    store_blocks(acc, nb, b0, lane, a.y, n, a.Cout, cb, a.Ho, a.Wo, ho0, outs);
+    else if (nb == 1) contract(std::integral_constant<int, 1>{});
+    if ((a.Wo & 3) == 0) {
+        if (nb > 0) store_blocks(acc, nb, b0, lane, a.y, n, a.Cout, cb, a.Ho, a.Wo, ho0, outs);
+    } else {
+        __syncthreads();                             // patch and filter are dead: LDS is store scratch
+        if (nb > 0)
+            store_blocks_lds(acc, nb, b0, lane, reinterpret_cast<float *>(lds) + wave * kStoreScratchFloats,
+                             a.y, n, a.Cout, cb, a.Ho, a.Wo, ho0, outs);
+    }
 }
 
 // fp32 form of the same row block on the matrix cores' fp32 multiply
@@ -439,8 +407,14 @@ __global__ __launch_bounds__(kRowsThreads) void conv_implicit_rows_f32_kernel(co
             }
         }
     }
-    if (nb == 0) return;
-    store_blocks(acc, nb, b0, lane, a.y, n, a.Cout, cb, a.Ho, a.Wo, ho0, outs);
+    if ((a.Wo & 3) == 0) {
+        if (nb > 0) store_blocks(acc, nb, b0, lane, a.y, n, a.Cout, cb, a.Ho, a.Wo, ho0, outs);
+    } else {
+        __syncthreads();                             // patch and filter are dead: LDS is store scratch
+        if (nb > 0)
+            store_blocks_lds(acc, nb, b0, lane, ldsf + wave * kStoreScratchFloats, a.y, n, a.Cout, cb, a.Ho,
+                             a.Wo, ho0, outs);
+    }
 }
 
 template <int KH, int KW>

@@ -1,0 +1,92 @@
+// Output blocks of the implicit kernels that take whole output rows per
+// workgroup (row-block and narrow-channel forms): the workgroup's outputs,
+// flattened row-major, are cut into 16-output MFMA blocks shared over eight
+// waves, and a block's results are stored as 16-byte vectors of 4
+// consecutive outputs of one output channel.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "lds_dma.hpp"
+
+namespace im2win {
+
+// The rw x Wo outputs of a workgroup, flattened (i * Wo + wo, which is also
+// their order inside each output plane), are cut into MFMA blocks of 16 and
+// shared out over the eight waves in contiguous ranges of at most 4 blocks.
+// Lane l of a block works on output m = 16 * block + l % 16 (clamped to the
+// last output: such lanes read a valid window and store nothing).
+__device__ __forceinline__ void wave_blocks(int wave, int outs, int &b0, int &nb)
+{
+    const int total = (outs + 15) >> 4;
+    b0 = wave * total / 8;
+    nb = (wave + 1) * total / 8 - b0;
+}
+
+// Lane l holds D[4*(l/16) + v][l % 16] of each 16 x 16 block: 4 consecutive
+// outputs m of output channel co = block column l % 16, which are 4
+// consecutive floats of the plane (one 16-byte store when Wo % 4 == 0).
+__device__ __forceinline__ void store_blocks(const floatx4_t (*acc)[4], int nb, int b0, int lane,
+                                             float *y, int n, int Cout, int cb, int Ho, int Wo,
+                                             int ho0, int outs)
+{
+    const int64_t plane = int64_t(Ho) * Wo;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const int co = cb * 64 + c * 16 + (lane & 15);
+        if (co >= Cout) continue;
+        float *yb = y + (int64_t(n) * Cout + co) * plane + int64_t(ho0) * Wo;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            if (s >= nb) break;
+            const int m = (b0 + s) * 16 + (lane >> 4) * 4;
+            if ((Wo & 3) == 0) {
+                if (m < outs) *reinterpret_cast<floatx4_t *>(yb + m) = acc[s][c];
+            } else {
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    if (m + v < outs) yb[m + v] = acc[s][c][v];
+            }
+        }
+    }
+}
+
+// Per-wave LDS scratch of store_blocks_lds: 16 rows (output channels) of 64
+// outputs, each row 4 floats longer so that the 16 rows fall in different
+// bank groups.
+constexpr int kStoreRow = 68;
+constexpr int kStoreScratchFloats = 16 * kStoreRow;
+
+// The same stores for any Wo, through a per-wave LDS scratch of
+// kStoreScratchFloats floats: one 16-channel block at a time, a lane's 4
+// outputs are written to the scratch row of its channel, then read back one
+// channel row per instruction, so that each store instruction writes up to 64
+// consecutive floats of one output plane (the wave's outputs are consecutive
+// in every plane). For rows whose length is not a multiple of 4, where the
+// 16-byte stores of store_blocks do not apply. LDS operations of one wave
+// complete in order, so no barrier is needed between the 4 blocks.
+__device__ __forceinline__ void store_blocks_lds(const floatx4_t (*acc)[4], int nb, int b0, int lane,
+                                                 float *scratch, float *y, int n, int Cout, int cb,
+                                                 int Ho, int Wo, int ho0, int outs)
+{
+    const int64_t plane = int64_t(Ho) * Wo;
+    const int nout = min(nb * 16, outs - b0 * 16);   // this wave's outputs
+    float *const yb = y + (int64_t(n) * Cout + cb * 64) * plane + int64_t(ho0) * Wo + b0 * 16;
+    float *const srow = scratch + (lane & 15) * kStoreRow + 4 * (lane >> 4);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+            if (s < nb) *reinterpret_cast<floatx4_t *>(srow + s * 16) = acc[s][c];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int co = cb * 64 + c * 16 + r;
+            const float v = scratch[r * kStoreRow + lane];
+            if (co < Cout && lane < nout) yb[int64_t(c * 16 + r) * plane + lane] = v;
+        }
+    }
+}
+
+}  // namespace im2win

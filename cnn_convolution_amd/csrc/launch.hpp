@@ -85,7 +85,8 @@ struct ImplicitArgs {
     int tile_m, tile_n, wm;
     int stages;             // filter stage buffers (3, 4 or 5)
     int bf16;
-    int f32;                // fp32 x, w (the row-block kernel only)
+    int f32;                // fp32 x, w (row-block and narrow kernels)
+    int narrow_cp;          // narrow kernel: channels per window position (4 or 8)
     int fs_groups;          // filter-stationary form: workgroups per 64-row filter block
 };
 hipError_t launch_conv_implicit(const ImplicitArgs &a, hipStream_t s);
@@ -97,5 +98,9 @@ hipError_t launch_conv_implicit_fs(const ImplicitArgs &a, hipStream_t s);
 // image per workgroup, raw filter and input rows resident in LDS; wst is w
 // itself
 hipError_t launch_conv_implicit_rows(const ImplicitArgs &a, hipStream_t s);
+// narrow-channel form (Cin <= 8, any filter and stride, Wo <= 512): R output
+// rows of one image per workgroup, their channels-last window rows and the
+// filter in LDS; wst is w itself
+hipError_t launch_conv_implicit_narrow(const ImplicitArgs &a, hipStream_t s);
 
 }  // namespace im2win

@@ -226,7 +226,7 @@ static void pick_algo(const conv2d_desc_t &d, conv2d_plan_t *p) {
     const bool can = make_implicit_plan(d, &ip) == CONV2D_OK;
     const int64_t taps = d.KH * d.KW;
     bool use = false;
-    if (can && ip.kernel == 2) use = true;
+    if (can && (ip.kernel == 2 || ip.kernel == 3)) use = true;
     if (can && ip.kernel == 0 && d.stride == 1 && taps <= 25) {
         const double fill = double(p->Ho * p->Wo) /
             double(ceil_div(p->Ho, ip.rows_per_tile) * ceil_div(p->Wo, ip.cols_per_tile) * ip.tile_n);
@@ -442,6 +442,71 @@ static void pick_implicit_rows(const conv2d_desc_t &d, int64_t Ho, int64_t Wo, c
     p->ws_bytes = 0;    // the kernel reads w as it is stored
 }
 
+// Narrow-channel implicit kernel: Cin <= 8 (the RGB stem and its kind), any
+// filter and stride, Wo <= 512, fp16/bf16/fp32. A workgroup of eight waves
+// takes R output rows of one image (R * Wo <= 512) and 64 output channels,
+// with its R channels-last window rows (CP = 4 channels per position, or 8
+// where 4 would leave a window start off a 16-byte boundary) and the filter in
+// the window's K order in LDS, read from the filter staged in the workspace.
+// Default where it applies; IM2WIN_IMPLICIT_KERNEL names another kernel to
+// leave it; IM2WIN_IMPLICIT_ROWS sets R. The plan's `stages` field carries CP
+// and `K_stage` the staged row length Kp.
+static void pick_implicit_narrow(const conv2d_desc_t &d, int64_t Ho, int64_t Wo, conv2d_implicit_plan_t *p) {
+    if (d.Cin > 8 || Wo > 512 || Wo < 1 || Ho < 1) return;
+    if (const char *e = std::getenv("IM2WIN_IMPLICIT_KERNEL"))
+        if (std::strcmp(e, "narrow") != 0) return;
+    if (d.Cin * d.H * d.W >= (int64_t(1) << 31) || d.Cout * d.Cin * d.KH * d.KW >= (int64_t(1) << 31)) return;
+    const bool f32 = d.dtype == CONV2D_F32;
+    const int64_t es = f32 ? 4 : 2;
+    const int64_t cp = (d.Cin <= 4 && (d.stride * d.KH * 4 * es) % 16 == 0) ? 4 : 8;
+    const int64_t K = d.KW * d.KH * cp;
+    const int64_t kstep = f32 ? 16 : 32;
+    const int64_t Kp = round_up(K, kstep);
+    const int64_t L = ((Wo - 1) * d.stride + d.KW) * d.KH * cp;
+    const int64_t Lp = round_up(L + Kp - K, f32 ? 4 : 8);
+    const int64_t co_blocks = ceil_div(d.Cout, 64);
+    // R: the largest that fits LDS and 512 outputs (measured best: the
+    // block's set-up, its load round trip and barrier, is paid once per R
+    // rows), made smaller only while the grid would leave CUs idle
+    int64_t best_r = 0;
+    for (int64_t r = 1; r <= Ho && r * Wo <= 512; ++r) {
+        if (implicit_narrow_lds_bytes(es, Kp, Lp, r) > kImplicitMaxLdsBytes) break;
+        best_r = r;
+    }
+    while (best_r > 1 && co_blocks * d.N * ceil_div(Ho, best_r) < 256) --best_r;
+    if (best_r == 0) return;
+    if (const char *e = std::getenv("IM2WIN_IMPLICIT_ROWS")) {
+        const int64_t v = std::min<int64_t>(std::atoi(e), Ho);
+        if (v >= 1 && v * Wo <= 512 && implicit_narrow_lds_bytes(es, Kp, Lp, v) <= kImplicitMaxLdsBytes)
+            best_r = v;
+    }
+    p->kernel = 3;
+    p->tile_m = 64;
+    p->tile_n = int32_t(best_r * Wo);
+    p->wave_m = 1;
+    p->rows_per_tile = int32_t(best_r);
+    p->cols_per_tile = int32_t(Wo);
+    p->patch_rows = int32_t(best_r);               // window rows held
+    p->patch_cols = int32_t(Lp);                   // elements per window row in LDS
+    p->stages = int32_t(cp);
+    p->lds_bytes = implicit_narrow_lds_bytes(es, Kp, Lp, best_r);
+    // One row block per workgroup, or (fp32, and filter blocks over 48 KB)
+    // persistent workgroups, one per CU, each walking a contiguous range of
+    // the N * ceil(Ho / R) row blocks with its filter block staged once and
+    // the next block's gathers in flight during the contraction: measured
+    // faster there (stem fp32 159 -> 139 us, cv3 fp32 1164 -> 953 us, cv1
+    // fp16 591 -> 528 us), slower for fp16 with small filters (stem 49 -> 61).
+    const int64_t row_blocks = d.N * ceil_div(Ho, best_r);
+    const bool persistent = f32 || 64 * Kp * es > 48 * 1024;
+    const int64_t groups = persistent ? std::min(row_blocks, std::max<int64_t>(1, 256 / co_blocks)) : row_blocks;
+    p->tiles = co_blocks * groups;
+    // the filter staged into the workspace by the channels-last staging:
+    // [Cout][Kp], CP channels per position (the half-precision layout's
+    // Cin_pad and row length)
+    p->K_stage = Kp;
+    p->ws_bytes = round_up(d.Cout * Kp * es, 256);
+}
+
 conv2d_status_t make_implicit_plan(const conv2d_desc_t &d, conv2d_implicit_plan_t *p) {
     const conv2d_status_t st = check_desc(d);
     if (st != CONV2D_OK) return st;
@@ -452,6 +517,11 @@ conv2d_status_t make_implicit_plan(const conv2d_desc_t &d, conv2d_implicit_plan_
     p->Wo = Wo;
     p->K_stage = d.KW * d.KH * d.Cin;
     p->flops = 2 * d.N * d.Cout * Ho * Wo * d.Cin * d.KH * d.KW;
+    if (d.Cin <= 8) {
+        // few input channels: the narrow-channel kernel, any dtype
+        pick_implicit_narrow(d, Ho, Wo, p);
+        return p->kernel == 3 ? CONV2D_OK : CONV2D_ERR_UNSUPPORTED;
+    }
     if (d.dtype == CONV2D_F32) {
         // fp32: only the row-block kernel (fp32 matrix-core products)
         pick_implicit_rows(d, Ho, Wo, p);

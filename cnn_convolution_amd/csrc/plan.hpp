@@ -8,6 +8,7 @@
 // ("Enabling Memory-efficient Im2win Convolution ...", Sec. III-B, Eq. (2)).
 #pragma once
 
+#include <algorithm>
 #include <cstdint>
 
 #include "im2win_conv2d.h"
@@ -37,7 +38,17 @@ inline int64_t implicit_fs_lds_bytes(int64_t cin, int64_t ir, int64_t iw) { retu
 constexpr int64_t kImplicitPairLdsBytes = 80 * 1024;   // two workgroups per CU
 // row-block implicit form: the filter block (8 KB per tap) + sl input rows of
 // iw positions x 128 bytes
-inline int64_t implicit_rows_lds_bytes(int64_t taps, int64_t sl, int64_t iw) { return taps * 8192 + sl * iw * 128; }
+// (at least the per-wave store scratch: 8 waves x 16 x 68 floats)
+constexpr int64_t kImplicitStoreScratchBytes = 8 * 16 * 68 * 4;
+inline int64_t implicit_rows_lds_bytes(int64_t taps, int64_t sl, int64_t iw) {
+    return std::max<int64_t>(taps * 8192 + sl * iw * 128, kImplicitStoreScratchBytes);
+}
+// narrow-channel implicit form: the filter block (64 rows of kp elements + 16
+// bytes) + r window rows of lp elements, es bytes per element (the window rows'
+// space holds at least the store scratch)
+inline int64_t implicit_narrow_lds_bytes(int64_t es, int64_t kp, int64_t lp, int64_t r) {
+    return 64 * (kp + 16 / es) * es + std::max<int64_t>(r * lp * es, kImplicitStoreScratchBytes);
+}
 
 // fp32 vector-ALU kernel: output columns per lane for this filter shape.
 int valu_cols_per_lane(const conv2d_desc_t &d);

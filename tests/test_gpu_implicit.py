@@ -362,3 +362,91 @@ def test_row_block_kernel_agrees_with_streamed_kernel(monkeypatch):
     b = conv.conv2d_implicit(xd, wd, 1, 1)
     torch.cuda.synchronize()
     assert rel_l2(a.cpu().numpy(), b.cpu().numpy()) <= 1e-6
+
+
+# narrow-channel kernel (Cin <= 8, any filter and stride): window rows built in
+# LDS channels-last, CP = 4 (or 8) channels per position
+NARROW_SHAPES = [
+    (2, 3, 30, 30, 64, 7, 7, 2, 3),      # the stem's geometry, small image
+    (1, 3, 35, 35, 96, 11, 11, 4, 0),    # 11x11 stride 4, two channel blocks of Cout (ragged)
+    (2, 3, 20, 22, 16, 3, 3, 1, 1),      # stride 1, KH odd: CP = 8 in half precision
+    (1, 1, 9, 13, 8, 5, 3, 2, 2),        # one channel, KH != KW
+    (2, 8, 11, 10, 70, 3, 3, 1, 1),      # eight channels: CP = 8
+    (1, 5, 7, 9, 20, 2, 4, 3, 1),        # five channels, stride 3
+    (1, 3, 4, 4, 2, 3, 3, 1, 5),         # padding wider than the filter: zero border
+    (2, 2, 5, 4, 6, 5, 4, 1, 0),         # dense-as-conv: one output per image
+    (1, 3, 6, 600, 12, 3, 3, 2, 1),      # 300 outputs per row: one row per workgroup
+]
+
+
+@pytest.mark.parametrize("shape", NARROW_SHAPES, ids=[str(s) for s in NARROW_SHAPES])
+@pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("rows", [None, 1, 3])
+def test_narrow_kernel_matches_oracle(shape, dt, rows, monkeypatch):
+    N, Cin, H, W, Cout, KH, KW, s, p = shape
+    if rows is not None:
+        monkeypatch.setenv("IM2WIN_IMPLICIT_ROWS", str(rows))
+    d = conv.make_desc(*shape, CODE[dt])
+    pl = conv.implicit_plan(d)
+    assert pl.kernel == 3 and pl.ws_bytes > 0 and conv.plan(d).algo == 1
+    _say(f"implicit-narrow {dt} {shape} rows/block={pl.rows_per_tile} cp={pl.stages} workgroups={pl.tiles}")
+    x, w = workloads.make_inputs(N, Cin, H, W, Cout, KH, KW, seed=31, dtype=dt, w_dist="normal")
+    got = run_implicit(x, w, s, p)
+    ref = oracle.conv2d(x, w, s, p)
+    assert tuple(got.shape) == ref.shape
+    assert rel_l2(got.numpy(), ref) <= TOL[dt]
+
+
+@pytest.mark.parametrize("shape", NARROW_SHAPES[:5], ids=[str(s) for s in NARROW_SHAPES[:5]])
+@pytest.mark.parametrize("dt", ["f32", "f16"])
+def test_narrow_kernel_integer_inputs_exact(shape, dt):
+    N, Cin, H, W, Cout, KH, KW, s, p = shape
+    x, w = workloads.make_inputs(N, Cin, H, W, Cout, KH, KW, seed=32, dtype=dt,
+                                 x_dist="int3", w_dist="int3")
+    got = run_implicit(x, w, s, p)
+    assert np.array_equal(got.numpy().astype(np.float64), oracle.conv2d(x, w, s, p))
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16"])
+def test_narrow_kernel_leaves_memory_past_y_untouched(dt):
+    N, Cin, H, W, Cout, KH, KW, s, p = 2, 3, 17, 19, 70, 7, 7, 2, 3
+    x, w = workloads.make_inputs(N, Cin, H, W, Cout, KH, KW, seed=33, dtype=dt)
+    d = conv.describe(tuple(x.shape), tuple(w.shape), s, p, CODE[dt])
+    pl = conv.implicit_plan(d)
+    assert pl.kernel == 3
+    n_out = N * Cout * pl.Ho * pl.Wo
+    buf = torch.full((n_out + 4096,), 12345.0, dtype=torch.float32, device=DEV)
+    ws = torch.empty(pl.ws_bytes, dtype=torch.uint8, device=DEV)
+    conv.conv2d_implicit_into(x.to(DEV), w.to(DEV), buf, ws, s, p)
+    torch.cuda.synchronize()
+    host = buf.cpu().numpy()
+    assert (host[n_out:] == 12345.0).all()
+    assert rel_l2(host[:n_out], oracle.conv2d(x, w, s, p).reshape(-1)) <= TOL[dt]
+
+
+# the narrow kernel's two launch forms and its multi-round window loads:
+# persistent workgroups (fp32, or filter blocks over 48 KB) walking several
+# row blocks with the next block's gathers prefetched, and window rows whose
+# gathers take more than one round per thread
+NARROW_PERSISTENT = [
+    ((64, 3, 16, 16, 16, 3, 3, 1, 1), "f32", 1),       # 1024 row blocks, one per output row
+    ((32, 3, 47, 47, 96, 11, 11, 4, 0), "f16", 1),     # 11x11: a 64 KB filter block, two channel blocks
+    ((32, 3, 47, 47, 96, 11, 11, 4, 0), "bf16", 2),
+    ((1, 3, 9, 1000, 8, 9, 9, 2, 0), "f16", None),     # 9 x 999 window positions: two gather rounds
+    ((1, 6, 9, 600, 8, 7, 7, 3, 1), "bf16", None),     # 8 channels per position: two rounds of 8 units
+]
+
+
+@pytest.mark.parametrize("shape,dt,rows", NARROW_PERSISTENT, ids=[f"{d}-{s}-r{r}" for s, d, r in NARROW_PERSISTENT])
+def test_narrow_kernel_persistent_and_multiround(shape, dt, rows, monkeypatch):
+    N, Cin, H, W, Cout, KH, KW, s, p = shape
+    if rows is not None:
+        monkeypatch.setenv("IM2WIN_IMPLICIT_ROWS", str(rows))
+    pl = conv.implicit_plan(conv.make_desc(*shape, CODE[dt]))
+    assert pl.kernel == 3
+    row_blocks = N * -(-pl.Ho // pl.rows_per_tile)
+    _say(f"implicit-narrow {dt} {shape} workgroups={pl.tiles} row blocks={row_blocks}")
+    x, w = workloads.make_inputs(N, Cin, H, W, Cout, KH, KW, seed=34, dtype=dt, w_dist="normal")
+    got = run_implicit(x, w, s, p)
+    ref = oracle.conv2d(x, w, s, p)
+    assert rel_l2(got.numpy(), ref) <= TOL[dt]

@@ -174,6 +174,23 @@ FIXED = [
 
 @pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
 @pytest.mark.parametrize("shape", FIXED + _random_cases(21, 16))
+def test_window_form_matches_oracle(shape, dt, monkeypatch):
+    """The window form (pack + window-GEMM) on every shape, also where the
+    planner would take the implicit form."""
+    monkeypatch.setenv("IM2WIN_ALGO", "window")
+    N, Cin, H, W, Cout, KH, KW, s, p = shape
+    _say(f"conv-window {dt} {shape}")
+    x, w = workloads.make_inputs(N, Cin, H, W, Cout, KH, KW, seed=sum(shape), dtype=dt,
+                                 w_dist="normal")
+    assert conv.plan(conv.describe(tuple(x.shape), tuple(w.shape), s, p, CODE[dt])).algo == 0
+    y = run_conv(x, w, s, p)
+    ref = oracle.conv2d(x, w, s, p)
+    err = rel_l2(y.numpy(), ref)
+    assert err <= TOL[dt], f"rel L2 {err:.3e} > {TOL[dt]}"
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("shape", FIXED + _random_cases(21, 16))
 def test_conv_matches_oracle(shape, dt):
     N, Cin, H, W, Cout, KH, KW, s, p = shape
     _say(f"conv {dt} {shape}")

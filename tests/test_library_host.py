@@ -17,6 +17,10 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "im2win_conv2d.h")
 
 
+# LDS of the row-block and narrow kernels is at least their per-wave store
+# scratch (8 waves x 16 x 68 floats)
+STORE_SCRATCH = 8 * 16 * 68 * 4
+
 def _declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
@@ -93,8 +97,9 @@ def test_plan_layout_geometry():
     assert p.wstage_bytes == 0          # 1x1 filter already in K order
 
 
-def test_unreachable_target_is_reported():
-    # dense-as-conv: one window row alone exceeds 1/KW of im2col
+def test_unreachable_target_is_reported(monkeypatch):
+    # dense-as-conv: one window row alone exceeds 1/KW of im2col (window form)
+    monkeypatch.setenv("IM2WIN_ALGO", "window")
     d = conv.make_desc(2, 3, 5, 4, 6, 5, 4, 1, 0, conv.F32)
     p = conv.plan(d)
     assert p.Ho == 1 and p.Wo == 1 and p.meets_ws_target == 0
@@ -123,7 +128,8 @@ def test_unknown_dtype_rejected():
     assert _lib.fwd(d, 16, 16, 16, 256, None) == 4
 
 
-def test_pointer_checks_before_launch():
+def test_pointer_checks_before_launch(monkeypatch):
+    monkeypatch.setenv("IM2WIN_ALGO", "window")     # a form with a workspace
     d = conv.make_desc(1, 3, 8, 8, 4, 3, 3, 1, 1, conv.F32)
     ws = conv.workspace_size(d)
     assert ws > 0
@@ -263,7 +269,10 @@ def test_implicit_plan_takes_only_its_layers():
     reports UNSUPPORTED (status 4) for the rest, before touching any pointer."""
     assert conv._lib.implicit_plan_status(conv.make_desc(2, 64, 9, 9, 8, 3, 3, 1, 1, conv.F32)) == 4
     assert conv._lib.implicit_plan_status(conv.make_desc(2, 96, 9, 9, 8, 3, 3, 1, 1, conv.F16)) == 4
-    assert conv._lib.implicit_plan_status(conv.make_desc(2, 3, 9, 9, 8, 3, 3, 1, 1, conv.BF16)) == 4
+    assert conv._lib.implicit_plan_status(conv.make_desc(2, 12, 9, 9, 8, 3, 3, 1, 1, conv.BF16)) == 4
+    # up to 8 input channels: the narrow-channel kernel, any dtype
+    for dt in (conv.F32, conv.F16, conv.BF16):
+        assert conv.implicit_plan(conv.make_desc(2, 3, 9, 9, 8, 3, 3, 1, 1, dt)).kernel == 3
     assert conv._lib.implicit_plan_status(conv.make_desc(0, 64, 9, 9, 8, 3, 3, 1, 1, conv.F16)) == 1
     d = conv.make_desc(2, 96, 9, 9, 8, 3, 3, 1, 1, conv.F16)
     assert conv.implicit_workspace_size(d) == 0
@@ -334,7 +343,7 @@ def test_conv2d_plan_names_the_form_conv2d_fwd_runs(monkeypatch):
     q = conv.plan(d)
     assert q.algo == 0 and q.ws_bytes == q.wstage_bytes + q.win_chunk_bytes
     monkeypatch.setenv("IM2WIN_ALGO", "implicit")
-    for args in [(2, 3, 20, 20, 16, 3, 3, 1, 1, conv.F16), (2, 48, 20, 20, 16, 3, 3, 1, 1, conv.F32),
+    for args in [(2, 16, 20, 20, 16, 3, 3, 1, 1, conv.F16), (2, 48, 20, 20, 16, 3, 3, 1, 1, conv.F32),
                  (2, 96, 20, 20, 16, 3, 3, 1, 1, conv.BF16)]:
         assert conv.plan(conv.make_desc(*args)).algo == 0     # not applicable: stays on the window form
     assert conv.plan(conv.make_desc(2, 256, 14, 14, 16, 3, 3, 1, 1, conv.BF16)).algo == 1
@@ -370,7 +379,7 @@ def test_row_block_plan_geometry(monkeypatch):
         assert 1 <= R <= pl.Ho and R * pl.Wo <= 512
         assert pl.patch_rows == R + KH - 1 and pl.patch_cols == W + 2 * p
         assert pl.cols_per_tile == pl.Wo and pl.tile_m == 64 and pl.tile_n == 64
-        assert pl.lds_bytes == KH * KW * 8192 + pl.patch_rows * pl.patch_cols * 128 <= 160 * 1024
+        assert pl.lds_bytes == max(KH * KW * 8192 + pl.patch_rows * pl.patch_cols * 128, STORE_SCRATCH) <= 160 * 1024
         assert pl.tiles == -(-Cout // 64) * N * -(-pl.Ho // R)
         assert pl.ws_bytes == 0 == conv.implicit_workspace_size(d)
         assert conv.plan(d).algo == 1 and conv.workspace_size(d) == 0
@@ -406,15 +415,76 @@ def test_row_block_plan_fp32():
         if Wo < 1 or (H + 2 * p - KH) // s + 1 < 1:
             continue
         eligible = (Cin % 32 == 0 and s == 1 and W % 4 == 0 and Wo <= 64 and (KH, KW) in ((3, 3), (1, 1)))
+        narrow = Cin <= 8 and Wo <= 512
         seen[eligible] += 1
         st = conv._lib.implicit_plan_status(d)
-        assert (st == 0) == eligible, (N, Cin, H, W, Cout, KH, KW, s, p)
+        assert (st == 0) == (eligible or narrow), (N, Cin, H, W, Cout, KH, KW, s, p)
         pl = conv.plan(d)
-        assert pl.algo == (1 if eligible else 0)
-        if eligible:
+        assert pl.algo == (1 if eligible or narrow else 0)
+        if eligible or narrow:
             ip = conv.implicit_plan(d)
-            assert ip.kernel == 2 and ip.ws_bytes == 0 and pl.ws_bytes == 0
-            assert ip.lds_bytes == KH * KW * 8192 + ip.patch_rows * ip.patch_cols * 128 <= 160 * 1024
+            assert ip.kernel == (2 if eligible else 3) and pl.ws_bytes == ip.ws_bytes
+            assert (ip.ws_bytes == 0) == eligible   # the narrow kernel reads a staged filter
+            if eligible:
+                assert ip.lds_bytes == max(KH * KW * 8192 + ip.patch_rows * ip.patch_cols * 128, STORE_SCRATCH) <= 160 * 1024
         else:
             assert pl.ws_bytes == pl.wstage_bytes + pl.win_chunk_bytes
     assert seen[True] > 30 and seen[False] > 30
+
+
+def test_narrow_plan_geometry():
+    """Layers with up to 8 input channels take the narrow-channel implicit kernel
+    in every dtype: CP = 4 channels per window position (8 where a window start
+    would leave a 16-byte boundary, or for 5..8 channels), R * Wo <= 512 outputs
+    per workgroup, the filter block and R window rows (with slack for the padded
+    K of the last window) in LDS, no workspace."""
+    import numpy as np
+    rng = np.random.default_rng(14)
+    taken = 0
+    for _ in range(600):
+        KH, KW = int(rng.integers(1, 12)), int(rng.integers(1, 12))
+        s, p = int(rng.integers(1, 5)), int(rng.integers(0, 4))
+        Cin = int(rng.integers(1, 9))
+        H, W = int(rng.integers(KH, 240)), int(rng.integers(KW, 240))
+        N, Cout = int(rng.integers(1, 9)), int(rng.integers(1, 200))
+        dt = [conv.F32, conv.F16, conv.BF16][int(rng.integers(0, 3))]
+        d = conv.make_desc(N, Cin, H, W, Cout, KH, KW, s, p, dt)
+        es = 4 if dt == conv.F32 else 2
+        if conv._lib.implicit_plan_status(d) != 0:
+            # not taken: output rows too long, or the filter block and one
+            # window row do not fit LDS
+            Wo = (W + 2 * p - KW) // s + 1
+            cp = 4 if (Cin <= 4 and (s * KH * 4 * es) % 16 == 0) else 8
+            K = KW * KH * cp
+            Kp = -(-K // (16 if dt == conv.F32 else 32)) * (16 if dt == conv.F32 else 32)
+            L = ((Wo - 1) * s + KW) * KH * cp
+            Lp = -(-(L + Kp - K) // (16 // es)) * (16 // es)
+            assert Wo > 512 or 64 * (Kp + 16 // es) * es + max(Lp * es, STORE_SCRATCH) > 160 * 1024
+            continue
+        pl = conv.implicit_plan(d)
+        assert pl.kernel == 3
+        taken += 1
+        cp = pl.stages
+        assert cp in (4, 8) and Cin <= cp
+        assert (s * KH * cp * es) % 16 == 0
+        if cp == 8 and Cin <= 4:
+            assert (s * KH * 4 * es) % 16 != 0
+        K = KW * KH * cp
+        kstep = 16 if dt == conv.F32 else 32
+        Kp = -(-K // kstep) * kstep
+        L = ((pl.Wo - 1) * s + KW) * KH * cp
+        vec = 16 // es
+        Lp = -(-(L + Kp - K) // vec) * vec
+        R = pl.rows_per_tile
+        assert pl.patch_cols == Lp and pl.patch_rows == R and 1 <= R <= pl.Ho and R * pl.Wo <= 512
+        assert pl.lds_bytes == 64 * (Kp + 16 // es) * es + max(R * Lp * es, STORE_SCRATCH) <= 160 * 1024
+        # one row block per workgroup, or (fp32, filter blocks over 48 KB)
+        # persistent workgroups, one per CU
+        cob = -(-Cout // 64)
+        rb = N * -(-pl.Ho // R)
+        persistent = dt == conv.F32 or 64 * Kp * es > 48 * 1024
+        assert pl.tiles == cob * (min(rb, max(1, 256 // cob)) if persistent else rb)
+        # staged filter [Cout][Kp] in the workspace
+        assert pl.K_stage == Kp and pl.ws_bytes == -(-(Cout * Kp * es) // 256) * 256
+        assert conv.implicit_workspace_size(d) == pl.ws_bytes
+    assert taken > 300
