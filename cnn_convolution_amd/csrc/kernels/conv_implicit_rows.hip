@@ -46,7 +46,7 @@ struct RowsKArgs {
     const uint16_t *x;
     const uint16_t *w;
     float *y;
-    int H, W, Cout, pad, Ho, Wo;
+    int Cin, H, W, Cout, pad, Ho, Wo;
     int RW;                 // output rows per workgroup
     int row_groups;         // ceil(Ho / RW)
     int co_blocks;          // ceil(Cout / 64)
@@ -234,6 +234,252 @@ __global__ __launch_bounds__(kRowsThreads) void conv_implicit_rows_kernel(const 
     else if (nb == 3) contract(std::integral_constant<int, 3>{});
     else if (nb == 2) contract(std::integral_constant<int, 2>{});
     else if (nb == 1) contract(std::integral_constant<int, 1>{});
+    if ((a.Wo & 3) == 0) {
+        if (nb > 0) store_blocks(acc, nb, b0, lane, a.y, n, a.Cout, cb, a.Ho, a.Wo, ho0, outs);
+    } else {
+        __syncthreads();                             // patch and filter are dead: LDS is store scratch
+        if (nb > 0)
+            store_blocks_lds(acc, nb, b0, lane, reinterpret_cast<float *>(lds) + wave * kStoreScratchFloats,
+                             a.y, n, a.Cout, cb, a.Ho, a.Wo, ho0, outs);
+    }
+}
+
+// The half-precision row block over several 64-channel blocks and for any
+// row width (the deep 3x3 layers: 128 - 512 channels on small images): the
+// block's accumulators stay in registers while the channel blocks pass
+// through LDS one at a time, each block's filter chunk (64 output channels x
+// all taps x 64 channels, reordered from w as stored) and patch rows replacing
+// the previous block's after a barrier. The next block's loads are issued
+// before the current block is contracted and written after it, so they are
+// in flight during the contraction. Rows whose width is a multiple of 8 are
+// loaded as 16-byte row chunks and transposed in registers (as in the
+// one-block kernel); other widths are gathered 2 bytes at a time, 8 channels
+// of one position per unit with consecutive lanes on consecutive columns.
+template <int KH, int KW, bool BF16, bool VEC8>
+__global__ __launch_bounds__(kRowsThreads) void conv_implicit_rows_multi_kernel(const RowsKArgs a)
+{
+    constexpr int TAPS = KH * KW;
+    constexpr int CIN = 64;                          // channels per block
+    constexpr int UG = 4;                            // gathered units per thread held per block
+    extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
+    uint16_t *const fl = lds;                        // [TAPS][64 co][64 ci]
+    uint16_t *const patch = lds + TAPS * 64 * CIN;   // [SL][IW][64 ci]
+
+    int cb, tn;
+    tile_coords(blockIdx.x, gridDim.x, a.co_blocks, cb, tn);
+    const int rg = tn % a.row_groups;
+    const int n = tn / a.row_groups;
+    const int ho0 = rg * a.RW;
+    const int rw = min(a.RW, a.Ho - ho0);
+    const int SL = rw + KH - 1;
+    const int ih0 = ho0 - a.pad;
+    const int tid = threadIdx.x;
+    const int HW = a.H * a.W;
+    const int nblk = a.Cin / CIN;
+    const uint16_t *const ximg = a.x + int64_t(n) * a.Cin * HW;
+    const int co_l = tid >> 3;
+    const int cg = tid & 7;
+    const int co_src = min(cb * 64 + co_l, a.Cout - 1);
+    // patch units of one block: VEC8: (row i, 8-column chunk k, group g), g
+    // fastest; gather: (row i, group g, column c), c fastest
+    const int units = VEC8 ? SL * (a.W >> 3) * 8 : SL * 8 * a.W;
+
+    // ---- registers of one block's loads ------------------------------------
+    uint4 wraw[TAPS];
+    uint4 vraw[8];                                   // VEC8: the first unit
+    uint32_t graw[UG][8];                            // gather: the first UG units
+    // the patch units are prefetched; the filter chunk (from L2: w is small
+    // and read by every workgroup of its 64-channel block) is loaded when the
+    // block is written, which keeps the registers held across the contraction
+    // to the patch units
+    auto issue = [&](int blk) {
+        const uint16_t *xb = ximg + int64_t(blk * CIN) * HW;
+        if constexpr (VEC8) {
+            const int CW = a.W >> 3;
+            const int u = min(tid, units - 1);
+            const int g = u & 7, r = u >> 3, i = r / CW, k = r - i * CW;
+            const bool in = unsigned(ih0 + i) < unsigned(a.H);
+            const uint4 *vs = reinterpret_cast<const uint4 *>(xb + int64_t(g * 8) * HW +
+                                                              int64_t(in ? ih0 + i : 0) * a.W + k * 8);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) vraw[e] = vs[int64_t(e) * (HW >> 3)];
+        } else {
+#pragma unroll
+            for (int j = 0; j < UG; ++j) {
+                const int u = min(tid + j * kRowsThreads, units - 1);
+                const int c = u % a.W, r = u / a.W, g = r & 7, i = r >> 3;
+                const bool in = unsigned(ih0 + i) < unsigned(a.H);
+                const uint16_t *gs = xb + int64_t(g * 8) * HW + (in ? (ih0 + i) * a.W + c : 0);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) graw[j][e] = gs[int64_t(e) * HW];
+            }
+        }
+    };
+    // 8 x 8 transpose of a VEC8 unit into 8 positions of one granule
+    auto put_vec8 = [&](int i, int k, int g, bool in, const uint4 *raw) {
+        const int qrow = i * a.IW + a.pad + k * 8;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+            uint4 o;
+            o.x = in ? __builtin_amdgcn_perm(dword_of(raw[1], j >> 1), dword_of(raw[0], j >> 1), sel) : 0u;
+            o.y = in ? __builtin_amdgcn_perm(dword_of(raw[3], j >> 1), dword_of(raw[2], j >> 1), sel) : 0u;
+            o.z = in ? __builtin_amdgcn_perm(dword_of(raw[5], j >> 1), dword_of(raw[4], j >> 1), sel) : 0u;
+            o.w = in ? __builtin_amdgcn_perm(dword_of(raw[7], j >> 1), dword_of(raw[6], j >> 1), sel) : 0u;
+            const int q = qrow + j;
+            *reinterpret_cast<uint4 *>(patch + q * CIN + ((g ^ (q & 7)) << 3)) = o;
+        }
+    };
+    auto put_gather = [&](int u, const uint32_t *h) {
+        const int c = u % a.W, r = u / a.W, g = r & 7, i = r >> 3;
+        const bool in = unsigned(ih0 + i) < unsigned(a.H);
+        const int q = i * a.IW + a.pad + c;
+        *reinterpret_cast<uint4 *>(patch + q * CIN + ((g ^ (q & 7)) << 3)) =
+            in ? uint4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)}
+               : uint4{0u, 0u, 0u, 0u};
+    };
+    // write one block: the filter chunk from wraw, the patch from the held
+    // units, the remaining units loaded and written here
+    auto commit = [&](int blk) {
+        {
+            const uint4 *src = reinterpret_cast<const uint4 *>(
+                a.w + (int64_t(co_src) * a.Cin + blk * CIN + cg * 8) * TAPS);
+#pragma unroll
+            for (int i = 0; i < TAPS; ++i) wraw[i] = src[i];
+        }
+#pragma unroll
+        for (int t = 0; t < TAPS; ++t) {
+            uint32_t o[4];
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                const int p0 = (2 * d) * TAPS + t, p1 = (2 * d + 1) * TAPS + t;
+                const uint32_t s0 = dword_of(wraw[p0 >> 3], (p0 & 7) >> 1);
+                const uint32_t s1 = dword_of(wraw[p1 >> 3], (p1 & 7) >> 1);
+                const uint32_t sel = ((p0 & 1) ? 0x0302u : 0x0100u) | ((p1 & 1) ? 0x07060000u : 0x05040000u);
+                o[d] = __builtin_amdgcn_perm(s1, s0, sel);
+            }
+            *reinterpret_cast<uint4 *>(fl + t * 64 * CIN + co_l * CIN + ((cg ^ (co_l & 7)) << 3)) =
+                uint4{o[0], o[1], o[2], o[3]};
+        }
+        const uint16_t *xb = ximg + int64_t(blk * CIN) * HW;
+        if constexpr (VEC8) {
+            const int CW = a.W >> 3;
+            auto unit = [&](int u, int &i, int &k, int &g, bool &in) {
+                g = u & 7;
+                const int r = u >> 3;
+                i = r / CW;
+                k = r - i * CW;
+                in = unsigned(ih0 + i) < unsigned(a.H);
+            };
+            if (tid < units) {
+                int i, k, g;
+                bool in;
+                unit(tid, i, k, g, in);
+                put_vec8(i, k, g, in, vraw);
+            }
+            for (int u = tid + kRowsThreads; u < units; u += kRowsThreads) {
+                int i, k, g;
+                bool in;
+                unit(u, i, k, g, in);
+                const uint4 *vs = reinterpret_cast<const uint4 *>(xb + int64_t(g * 8) * HW +
+                                                                  int64_t(in ? ih0 + i : 0) * a.W + k * 8);
+                uint4 raw[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) raw[e] = vs[int64_t(e) * (HW >> 3)];
+                put_vec8(i, k, g, in, raw);
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < UG; ++j)
+                if (tid + j * kRowsThreads < units) put_gather(tid + j * kRowsThreads, graw[j]);
+            for (int u = tid + UG * kRowsThreads; u < units; u += kRowsThreads) {
+                const int c = u % a.W, r = u / a.W, g = r & 7, i = r >> 3;
+                const bool in = unsigned(ih0 + i) < unsigned(a.H);
+                const uint16_t *gs = xb + int64_t(g * 8) * HW + (in ? (ih0 + i) * a.W + c : 0);
+                uint32_t h[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) h[e] = gs[int64_t(e) * HW];
+                put_gather(u, h);
+            }
+        }
+    };
+
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int outs = rw * a.Wo;
+    int b0, nb;
+    wave_blocks(wave, outs, b0, nb);
+    floatx4_t acc[4][4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[s][c] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    int qa[4];
+    block_bases(qa, b0, lane, outs, a.Wo, a.IW);
+    const int rb = lane & 15;
+    auto contract = [&](auto nbc) {
+        constexpr int NBW = decltype(nbc)::value;
+        // the per-lane bases pass through an empty asm once per block, so the
+        // compiler recomputes each step's LDS addresses instead of holding all
+        // of them in registers across the channel-block loop
+        int q0[NBW];
+#pragma unroll
+        for (int s = 0; s < NBW; ++s) {
+            q0[s] = qa[s];
+            asm volatile("" : "+v"(q0[s]));
+        }
+        int rbv = rb;
+        asm volatile("" : "+v"(rbv));
+#pragma unroll
+        for (int kh = 0; kh < KH; ++kh) {
+#pragma unroll
+            for (int kw = 0; kw < KW; ++kw) {
+                const uint16_t *ft = fl + (kh * KW + kw) * 64 * CIN;
+                const int dq = kh * a.IW + kw;
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) {
+                    const int gr = kk * 4 + (lane >> 4);
+                    uint4 af[NBW], bf[4];
+#pragma unroll
+                    for (int s = 0; s < NBW; ++s) {
+                        const int q = q0[s] + dq;
+                        af[s] = *reinterpret_cast<const uint4 *>(patch + q * CIN + ((gr ^ (q & 7)) << 3));
+                    }
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        const int r = c * 16 + rbv;
+                        bf[c] = *reinterpret_cast<const uint4 *>(ft + r * CIN + ((gr ^ (r & 7)) << 3));
+                    }
+#pragma unroll
+                    for (int s = 0; s < NBW; ++s)
+#pragma unroll
+                        for (int c = 0; c < 4; ++c) acc[s][c] = mfma16x16x32<BF16>(af[s], bf[c], acc[s][c]);
+                }
+            }
+        }
+    };
+
+    // zero padding columns of every row held (the same positions in every block)
+    const int pads = SL * 2 * a.pad * 8;
+    for (int v = tid; v < pads; v += kRowsThreads) {
+        const int g = v & 7;
+        const int r = v >> 3;
+        const int i = r / (2 * a.pad);
+        const int c = r - i * 2 * a.pad;
+        const int q = i * a.IW + (c < a.pad ? c : a.W + c);
+        *reinterpret_cast<uint4 *>(patch + q * CIN + ((g ^ (q & 7)) << 3)) = uint4{0u, 0u, 0u, 0u};
+    }
+    issue(0);
+    for (int blk = 0; blk < nblk; ++blk) {
+        if (blk > 0) __syncthreads();                // every wave is done with the previous block
+        commit(blk);
+        __syncthreads();
+        if (blk + 1 < nblk) issue(blk + 1);          // in flight during this block's contraction
+        if (nb >= 4) contract(std::integral_constant<int, 4>{});
+        else if (nb == 3) contract(std::integral_constant<int, 3>{});
+        else if (nb == 2) contract(std::integral_constant<int, 2>{});
+        else if (nb == 1) contract(std::integral_constant<int, 1>{});
+    }
     if ((a.Wo & 3) == 0) {
         if (nb > 0) store_blocks(acc, nb, b0, lane, a.y, n, a.Cout, cb, a.Ho, a.Wo, ho0, outs);
     } else {
@@ -455,6 +701,7 @@ hipError_t launch_rows(const ImplicitArgs &h, hipStream_t s)
     a.x = static_cast<const uint16_t *>(h.x);
     a.w = static_cast<const uint16_t *>(h.wst);
     a.y = h.y;
+    a.Cin = h.Cin;
     a.H = h.H;
     a.W = h.W;
     a.Cout = h.Cout;
@@ -468,7 +715,15 @@ hipError_t launch_rows(const ImplicitArgs &h, hipStream_t s)
     const int64_t blocks = int64_t(a.co_blocks) * h.N * a.row_groups;
     if (blocks < 1 || blocks > 0x7fffffff) return hipErrorInvalidValue;
     const size_t lds = implicit_rows_lds_bytes(KH * KW, h.R + KH - 1, a.IW);
-    auto kern = h.bf16 ? conv_implicit_rows_kernel<KH, KW, true> : conv_implicit_rows_kernel<KH, KW, false>;
+    // one 64-channel block with 8-column rows: the one-block kernel; else the
+    // channel-block loop (16-byte row chunks or 2-byte gathers)
+    const bool one = h.Cin == 64 && h.W % 8 == 0;
+    auto kern = one ? (h.bf16 ? conv_implicit_rows_kernel<KH, KW, true> : conv_implicit_rows_kernel<KH, KW, false>)
+          : h.W % 8 == 0
+              ? (h.bf16 ? conv_implicit_rows_multi_kernel<KH, KW, true, true>
+                        : conv_implicit_rows_multi_kernel<KH, KW, false, true>)
+              : (h.bf16 ? conv_implicit_rows_multi_kernel<KH, KW, true, false>
+                        : conv_implicit_rows_multi_kernel<KH, KW, false, false>);
     if (lds > 64 * 1024) {
         const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                                  hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
@@ -496,7 +751,8 @@ hipError_t launch_conv_implicit_rows(const ImplicitArgs &h, hipStream_t s)
         if (h.KH == 1 && h.KW == 1) return launch_rows_f32<1, 1>(h, s);
         return hipErrorInvalidValue;
     }
-    if (h.Cin != 64 || h.stride != 1 || h.W % 8 != 0 || h.W < 8 || h.Wo < 1 || h.Wo > 64 ||
+    if (h.Cin % 64 != 0 || h.Cin < 64 || h.stride != 1 || h.W < 1 || h.Wo < 1 || h.Wo > 64 ||
+        int64_t(h.Cin) * h.H * h.W >= (int64_t(1) << 31) ||
         h.Wo != h.W + 2 * h.pad - h.KW + 1 || h.R < 1 || int64_t(h.R) * h.Wo > 512 ||
         h.Ho != h.H + 2 * h.pad - h.KH + 1 ||
         implicit_rows_lds_bytes(h.KH * h.KW, h.R + h.KH - 1, h.W + 2 * h.pad) > kImplicitMaxLdsBytes)

@@ -376,9 +376,10 @@ static void pick_implicit_fs(const conv2d_desc_t &d, int64_t Ho, int64_t Wo, con
     p->tiles = groups * tiles_m;
 }
 
-// Row-block implicit kernel: 64 input channels, stride 1, input rows a
-// multiple of 8 long, output rows of at most 64 columns, a 1x1 or 3x3
-// filter. A workgroup of eight waves takes RW whole output rows of one image
+// Row-block implicit kernel: stride 1, output rows of at most 64 columns, a
+// 1x1 or 3x3 filter; fp16/bf16 with 64 input channels on rows of 8k elements,
+// or any multiple of 64 channels where an image has at least 128 outputs;
+// fp32 with a multiple of 32 channels on rows of 4k elements. A workgroup of eight waves takes RW whole output rows of one image
 // (RW * Wo <= 512 outputs, 16-output blocks shared over the waves) and 64
 // output channels, with the raw filter and the RW + KH - 1 input rows in LDS;
 // no staged filter. RW minimises the rounds of workgroups over the CUs times
@@ -389,10 +390,15 @@ static void pick_implicit_fs(const conv2d_desc_t &d, int64_t Ho, int64_t Wo, con
 static void pick_implicit_rows(const conv2d_desc_t &d, int64_t Ho, int64_t Wo, conv2d_implicit_plan_t *p) {
     const int64_t taps = d.KH * d.KW;
     const bool f32 = d.dtype == CONV2D_F32;
-    const bool chans = f32 ? (d.Cin % 32 == 0) : (d.Cin == 64);
-    if (!chans || d.stride != 1 || d.W % (f32 ? 4 : 8) != 0 || Wo > 64 ||
-        !((d.KH == 3 && d.KW == 3) || (d.KH == 1 && d.KW == 1)))
+    // fp16/bf16: one 64-channel block on rows of 8k elements (the one-block
+    // kernel), or several blocks / any width (the channel-block loop) where an
+    // image has at least 128 outputs (8 MFMA blocks: every wave busy); smaller
+    // images stay on the streamed kernel
+    const bool chans = f32 ? (d.Cin % 32 == 0 && d.W % 4 == 0)
+                           : (d.Cin % 64 == 0 && ((d.Cin == 64 && d.W % 8 == 0) || Ho * Wo >= 128));
+    if (!chans || d.stride != 1 || Wo > 64 || !((d.KH == 3 && d.KW == 3) || (d.KH == 1 && d.KW == 1)))
         return;
+    if (d.Cin * d.H * d.W >= (int64_t(1) << 31)) return;
     if (const char *e = std::getenv("IM2WIN_IMPLICIT_KERNEL"))
         if (std::strcmp(e, "rows") != 0) return;
     if (std::getenv("IM2WIN_IMPLICIT_TILE")) return;   // a streamed-kernel tile was asked for
@@ -419,7 +425,8 @@ static void pick_implicit_rows(const conv2d_desc_t &d, int64_t Ho, int64_t Wo, c
         const int64_t blocks = co_blocks * d.N * ceil_div(Ho, rw);
         // rounds of workgroups over the CUs, each costing its busiest SIMD's
         // blocks plus a fixed set-up (the block's loads and barrier) worth 12
-        const double cost = double(ceil_div(blocks, 256 * per_cu)) * double(simd_blocks(rw * Wo) + 12);
+        const int64_t nblk = f32 ? d.Cin / 32 : d.Cin / 64;
+        const double cost = double(ceil_div(blocks, 256 * per_cu)) * double(simd_blocks(rw * Wo) * nblk + 12);
         if (best_rw == 0 || cost < best_cost) { best_rw = rw; best_cost = cost; }
     }
     if (best_rw == 0) return;

@@ -300,8 +300,19 @@ ROWS_SHAPES_F32 = [
 ]
 
 
+# half precision over several 64-channel blocks, and rows of any width (the
+# deep 3x3 layers); images of at least 128 outputs
+ROWS_SHAPES_MULTI = [
+    (2, 256, 14, 14, 72, 3, 3, 1, 1),    # the deep layer's image: 4 channel blocks, 14-wide rows (gathered)
+    (1, 128, 16, 14, 130, 3, 3, 1, 0),   # two blocks, 14x12 outputs, three channel blocks of Cout
+    (2, 192, 12, 16, 64, 3, 3, 1, 1),    # three blocks, 16-wide rows (16-byte chunks)
+    (1, 128, 14, 18, 40, 1, 1, 1, 0),    # 1x1 over two blocks, 18-wide rows
+    (2, 64, 12, 12, 16, 3, 3, 1, 1),     # one block, 12-wide rows: the gathering loader
+]
+
 ROWS_CASES = [(s, dt) for dt in ("f32", "f16", "bf16") for s in ROWS_SHAPES] + \
-             [(s, "f32") for s in ROWS_SHAPES_F32]
+             [(s, "f32") for s in ROWS_SHAPES_F32] + \
+             [(s, dt) for dt in ("f16", "bf16") for s in ROWS_SHAPES_MULTI]
 
 
 @pytest.mark.parametrize("shape,dt", ROWS_CASES, ids=[f"{dt}-{s}" for s, dt in ROWS_CASES])
@@ -450,3 +461,13 @@ def test_narrow_kernel_persistent_and_multiround(shape, dt, rows, monkeypatch):
     got = run_implicit(x, w, s, p)
     ref = oracle.conv2d(x, w, s, p)
     assert rel_l2(got.numpy(), ref) <= TOL[dt]
+
+
+@pytest.mark.parametrize("shape", ROWS_SHAPES_MULTI, ids=[str(s) for s in ROWS_SHAPES_MULTI])
+def test_row_block_multi_integer_inputs_exact(shape):
+    N, Cin, H, W, Cout, KH, KW, s, p = shape
+    assert conv.implicit_plan(conv.make_desc(*shape, conv.F16)).kernel == 2
+    x, w = workloads.make_inputs(N, Cin, H, W, Cout, KH, KW, seed=24, dtype="f16",
+                                 x_dist="int3", w_dist="int3")
+    got = run_implicit(x, w, s, p)
+    assert np.array_equal(got.numpy().astype(np.float64), oracle.conv2d(x, w, s, p))

@@ -350,10 +350,12 @@ def test_conv2d_plan_names_the_form_conv2d_fwd_runs(monkeypatch):
 
 
 def test_row_block_plan_geometry(monkeypatch):
-    """The row-block implicit kernel is planned exactly for its layers (64 input
-    channels, stride 1, W % 8 == 0, Wo <= 64, a 3x3 or 1x1 filter, fp16/bf16):
-    whole output rows per workgroup, the block's input rows and the filter in LDS,
-    no workspace, one workgroup per (64-channel block, row block, image)."""
+    """The row-block implicit kernel is planned exactly for its layers (fp16/bf16,
+    stride 1, Wo <= 64, a 3x3 or 1x1 filter; 64 input channels on rows of 8k
+    elements, or any multiple of 64 channels where an image has at least 128
+    outputs): whole output rows per workgroup, the block's input rows and the
+    filter in LDS, no workspace, one workgroup per (64-channel block, row
+    block, image)."""
     import numpy as np
     rng = np.random.default_rng(12)
     taken = 0
@@ -361,8 +363,8 @@ def test_row_block_plan_geometry(monkeypatch):
         KH, KW = [(3, 3), (1, 1), (5, 5), (3, 1)][int(rng.integers(0, 4))]
         s = int(rng.choice([1, 1, 1, 2]))
         p = int(rng.integers(0, 4))
-        Cin = int(rng.choice([64, 64, 64, 128]))
-        W = int(rng.choice([8, 16, 24, 56, 60, 64, 72]))
+        Cin = int(rng.choice([64, 64, 64, 128, 256]))
+        W = int(rng.choice([8, 12, 14, 16, 24, 56, 60, 64, 72]))
         H = int(rng.integers(max(KH, 1), 40))
         N, Cout = int(rng.integers(1, 9)), int(rng.integers(1, 300))
         dt = [conv.F16, conv.BF16][int(rng.integers(0, 2))]
@@ -370,7 +372,8 @@ def test_row_block_plan_geometry(monkeypatch):
         if conv._lib.implicit_plan_status(d) != 0:
             continue
         pl = conv.implicit_plan(d)
-        eligible = (Cin == 64 and s == 1 and W % 8 == 0 and pl.Wo <= 64 and (KH, KW) in ((3, 3), (1, 1)))
+        eligible = (s == 1 and pl.Wo <= 64 and (KH, KW) in ((3, 3), (1, 1)) and
+                    ((Cin == 64 and W % 8 == 0) or pl.Ho * pl.Wo >= 128))
         assert (pl.kernel == 2) == eligible, (N, Cin, H, W, Cout, KH, KW, s, p)
         if not eligible:
             continue
