@@ -51,7 +51,8 @@ def _say(msg):
 # 2: filter-resident matrix-core window-GEMM, 3: direct-to-LDS matrix-core
 # window-GEMM, 4: implicit convolution, window rows built in LDS, 5: the same
 # with the filter held in registers, 6: the row-block implicit kernel, filter
-# and input rows resident in LDS, 7: the narrow-channel implicit kernel)
+# and input rows resident in LDS, 7: the narrow-channel implicit kernel, 8: the
+# pipelined row-block kernel, 32-channel K chunks double-buffered by loader waves)
 GEMM_SOURCES = {
     0: ["cnn_convolution_amd/csrc/kernels/gemm_valu.hip"],
     1: ["cnn_convolution_amd/csrc/kernels/gemm_mfma.hip",
@@ -74,10 +75,13 @@ GEMM_SOURCES = {
         "cnn_convolution_amd/csrc/kernels/out_blocks.hpp",
         "cnn_convolution_amd/csrc/kernels/lds_dma.hpp",
         "cnn_convolution_amd/csrc/kernels/tile_map.hpp"],
+    8: ["cnn_convolution_amd/csrc/kernels/conv_implicit_pipe.hip",
+        "cnn_convolution_amd/csrc/kernels/out_blocks.hpp",
+        "cnn_convolution_amd/csrc/kernels/lds_dma.hpp"],
 }
 GEMM_KERNEL_NAMES = {0: "gemm_valu_f32", 1: "gemm_mfma", 2: "gemm_mfma_resident",
                      3: "gemm_mfma_dma", 4: "conv_implicit", 5: "conv_implicit_fs",
-                     6: "conv_implicit_rows", 7: "conv_implicit_narrow"}
+                     6: "conv_implicit_rows", 7: "conv_implicit_narrow", 8: "conv_implicit_pipe"}
 COPY_BYTES = 256 << 20     # calibration copy for the HBM byte counters
 
 
@@ -97,7 +101,7 @@ def dominant_key(d, plan):
     import cnn_convolution_amd as conv
     if plan.algo == 1:
         ip = conv.implicit_plan(d)
-        kid = {0: 4, 1: 5, 2: 6, 3: 7}[ip.kernel]
+        kid = {0: 4, 1: 5, 2: 6, 3: 7, 4: 8}[ip.kernel]
         return (kid, f"i{ip.kernel}:{ip.tile_m}x{ip.tile_n}/{ip.wave_m}/r{ip.rows_per_tile}/"
                 f"c{ip.cols_per_tile}/g{ip.tiles}", plan.rows_total)
     rows = plan.rows_total - (plan.n_chunks - 1) * plan.rows_per_chunk

@@ -167,7 +167,9 @@ ImplicitArgs implicit_args(const conv2d_desc_t &d, const conv2d_implicit_plan_t 
     a.bf16 = d.dtype == CONV2D_BF16 ? 1 : 0;
     a.f32 = d.dtype == CONV2D_F32 ? 1 : 0;
     a.narrow_cp = p.kernel == 3 ? p.stages : 0;
-    a.fs_groups = int(p.tiles / ((d.Cout + 63) / 64));
+    // filter-stationary form: workgroups per 64-row filter block; pipelined
+    // row-block form: the persistent workgroups
+    a.fs_groups = p.kernel == 4 ? int(p.tiles) : int(p.tiles / ((d.Cout + 63) / 64));
     return a;
 }
 
@@ -175,6 +177,7 @@ hipError_t launch_implicit(const conv2d_implicit_plan_t &p, const ImplicitArgs &
 {
     if (p.kernel == 2) return launch_conv_implicit_rows(a, s);
     if (p.kernel == 3) return launch_conv_implicit_narrow(a, s);
+    if (p.kernel == 4) return launch_conv_implicit_pipe(a, s);
     return p.kernel == 1 ? launch_conv_implicit_fs(a, s) : launch_conv_implicit(a, s);
 }
 

@@ -59,18 +59,6 @@ __device__ __forceinline__ uint32_t dword_of(const uint4 &v, int d)
     return d == 0 ? v.x : d == 1 ? v.y : d == 2 ? v.z : v.w;
 }
 
-// Patch position of the window at tap (0, 0) of each of a lane's output
-// blocks (output m = i * Wo + wo: input row i, column wo of the patch).
-__device__ __forceinline__ void block_bases(int *qa, int b0, int lane, int outs, int Wo, int IW)
-{
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-        const int m = min((b0 + s) * 16 + (lane & 15), outs - 1);
-        const int i = m / Wo;
-        qa[s] = i * IW + (m - i * Wo);
-    }
-}
-
 template <int KH, int KW, bool BF16>
 __global__ __launch_bounds__(kRowsThreads) void conv_implicit_rows_kernel(const RowsKArgs a)
 {

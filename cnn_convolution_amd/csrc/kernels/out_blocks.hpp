@@ -15,19 +15,40 @@ namespace im2win {
 
 // The rw x Wo outputs of a workgroup, flattened (i * Wo + wo, which is also
 // their order inside each output plane), are cut into MFMA blocks of 16 and
-// shared out over the eight waves in contiguous ranges of at most 4 blocks.
+// shared out over the workgroup's computing waves (eight, or four in the
+// pipelined kernel) in contiguous ranges of at most 4 blocks.
 // Lane l of a block works on output m = 16 * block + l % 16 (clamped to the
 // last output: such lanes read a valid window and store nothing).
-__device__ __forceinline__ void wave_blocks(int wave, int outs, int &b0, int &nb)
+__device__ __forceinline__ void wave_blocks_of(int wave, int waves, int outs, int &b0, int &nb)
 {
     const int total = (outs + 15) >> 4;
-    b0 = wave * total / 8;
-    nb = (wave + 1) * total / 8 - b0;
+    b0 = wave * total / waves;
+    nb = (wave + 1) * total / waves - b0;
+}
+
+__device__ __forceinline__ void wave_blocks(int wave, int outs, int &b0, int &nb)
+{
+    wave_blocks_of(wave, 8, outs, b0, nb);
+}
+
+// Patch position of the window at tap (0, 0) of each of a lane's output
+// blocks (output m = i * Wo + wo: input row i, column wo of a patch of rows
+// IW positions long; stride 1).
+__device__ __forceinline__ void block_bases(int *qa, int b0, int lane, int outs, int Wo, int IW)
+{
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        const int m = min((b0 + s) * 16 + (lane & 15), outs - 1);
+        const int i = m / Wo;
+        qa[s] = i * IW + (m - i * Wo);
+    }
 }
 
 // Lane l holds D[4*(l/16) + v][l % 16] of each 16 x 16 block: 4 consecutive
 // outputs m of output channel co = block column l % 16, which are 4
 // consecutive floats of the plane (one 16-byte store when Wo % 4 == 0).
+// acc holds MAXB blocks, nb <= MAXB of them in use.
+template <int MAXB = 4>
 __device__ __forceinline__ void store_blocks(const floatx4_t (*acc)[4], int nb, int b0, int lane,
                                              float *y, int n, int Cout, int cb, int Ho, int Wo,
                                              int ho0, int outs)
@@ -39,7 +60,7 @@ __device__ __forceinline__ void store_blocks(const floatx4_t (*acc)[4], int nb, 
         if (co >= Cout) continue;
         float *yb = y + (int64_t(n) * Cout + co) * plane + int64_t(ho0) * Wo;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
+        for (int s = 0; s < MAXB; ++s) {
             if (s >= nb) break;
             const int m = (b0 + s) * 16 + (lane >> 4) * 4;
             if ((Wo & 3) == 0) {
@@ -67,6 +88,7 @@ constexpr int kStoreScratchFloats = 16 * kStoreRow;
 // in every plane). For rows whose length is not a multiple of 4, where the
 // 16-byte stores of store_blocks do not apply. LDS operations of one wave
 // complete in order, so no barrier is needed between the 4 blocks.
+template <int MAXB = 4>
 __device__ __forceinline__ void store_blocks_lds(const floatx4_t (*acc)[4], int nb, int b0, int lane,
                                                  float *scratch, float *y, int n, int Cout, int cb,
                                                  int Ho, int Wo, int ho0, int outs)
@@ -78,7 +100,7 @@ __device__ __forceinline__ void store_blocks_lds(const floatx4_t (*acc)[4], int 
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
+        for (int s = 0; s < MAXB; ++s)
             if (s < nb) *reinterpret_cast<floatx4_t *>(srow + s * 16) = acc[s][c];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {

@@ -102,5 +102,10 @@ hipError_t launch_conv_implicit_rows(const ImplicitArgs &a, hipStream_t s);
 // rows of one image per workgroup, their channels-last window rows and the
 // filter in LDS; wst is w itself
 hipError_t launch_conv_implicit_narrow(const ImplicitArgs &a, hipStream_t s);
+// pipelined row-block form (fp16/bf16, Cin % 32 == 0, stride 1, R * Wo <=
+// 256, 1x1 or 3x3): fs_groups persistent workgroups over tasks of R whole
+// output rows x 64 output channels, 32-channel K chunks double-buffered in
+// LDS by four loader waves while four waves contract; wst is w itself
+hipError_t launch_conv_implicit_pipe(const ImplicitArgs &a, hipStream_t s);
 
 }  // namespace im2win

@@ -226,7 +226,7 @@ static void pick_algo(const conv2d_desc_t &d, conv2d_plan_t *p) {
     const bool can = make_implicit_plan(d, &ip) == CONV2D_OK;
     const int64_t taps = d.KH * d.KW;
     bool use = false;
-    if (can && (ip.kernel == 2 || ip.kernel == 3)) use = true;
+    if (can && ip.kernel >= 2) use = true;
     if (can && ip.kernel == 0 && d.stride == 1 && taps <= 25) {
         const double fill = double(p->Ho * p->Wo) /
             double(ceil_div(p->Ho, ip.rows_per_tile) * ceil_div(p->Wo, ip.cols_per_tile) * ip.tile_n);
@@ -449,6 +449,142 @@ static void pick_implicit_rows(const conv2d_desc_t &d, int64_t Ho, int64_t Wo, c
     p->ws_bytes = 0;    // the kernel reads w as it is stored
 }
 
+// Pipelined row-block implicit kernel: fp16/bf16, Cin % 32 == 0, stride 1,
+// 3x3 or 1x1, Wo <= 256. Tasks of RW whole output rows x 64 output channels
+// (RW * Wo <= 256: four computing waves of at most four 16-output blocks),
+// walked by at most 256 persistent workgroups in 32-channel K chunks that
+// four loader waves double-buffer in LDS. RW minimises an estimate of the
+// busiest workgroup's cycles: per chunk the larger of the busiest computing
+// wave's MFMA cycles and its LDS reads (128 bytes per clock per CU), against
+// the chunk's loads and the task's stores at a CU's share of HBM bandwidth
+// (13 bytes per clock). Taken when `dflt` (the caller's rule) or when
+// IM2WIN_IMPLICIT_KERNEL=pipe; IM2WIN_IMPLICIT_ROWS sets RW.
+static void pick_implicit_pipe(const conv2d_desc_t &d, int64_t Ho, int64_t Wo, conv2d_implicit_plan_t *p,
+                               bool dflt) {
+    if (d.dtype == CONV2D_F32 || d.Cin % 32 != 0 || d.stride != 1 || Wo > 256 || Wo < 1 || Ho < 1) return;
+    if (!((d.KH == 3 && d.KW == 3) || (d.KH == 1 && d.KW == 1))) return;
+    if (d.Cin * d.H * d.W >= (int64_t(1) << 31)) return;
+    if (const char *e = std::getenv("IM2WIN_IMPLICIT_KERNEL")) {
+        if (std::strcmp(e, "pipe") != 0) return;
+    } else if (!dflt || std::getenv("IM2WIN_IMPLICIT_TILE")) {
+        return;
+    }
+    const int64_t taps = d.KH * d.KW;
+    const int64_t iw = d.W + 2 * d.pad;
+    const int64_t co_blocks = ceil_div(d.Cout, 64);
+    const int64_t nch = d.Cin / 32;
+    constexpr double kHbmBytesPerClk = 13.0;
+    int64_t best_rw = 0, best_groups = 0;
+    double best_cost = 0.0;
+    for (int64_t rw = 1; rw <= Ho && rw * Wo <= 256; ++rw) {
+        const int64_t sl = rw + d.KH - 1;
+        if (pipe_lds_bytes(taps, sl, iw) > kImplicitMaxLdsBytes) break;
+        const int64_t tasks = co_blocks * d.N * ceil_div(Ho, rw);
+        const int64_t groups = std::min<int64_t>(tasks, 256);
+        const int64_t rounds = ceil_div(tasks, groups);
+        const int64_t bw = ceil_div(ceil_div(rw * Wo, 16), 4);
+        const double chunk = double(std::max(taps * bw * 64, taps * 32 * (bw + 4)));
+        const double load = double(sl * d.W * 64 + taps * 4096) / kHbmBytesPerClk;
+        const double store = double(rw * Wo * 64 * 4) / kHbmBytesPerClk;
+        const double cost = double(rounds) * std::max(double(nch) * chunk, double(nch) * load + store);
+        if (best_rw == 0 || cost < best_cost) { best_rw = rw; best_groups = groups; best_cost = cost; }
+    }
+    if (best_rw == 0) return;
+    if (const char *e = std::getenv("IM2WIN_IMPLICIT_ROWS")) {
+        const int64_t v = std::min<int64_t>(std::atoi(e), Ho);
+        if (v >= 1 && v * Wo <= 256 && pipe_lds_bytes(taps, v + d.KH - 1, iw) <= kImplicitMaxLdsBytes) {
+            best_rw = v;
+            best_groups = std::min<int64_t>(co_blocks * d.N * ceil_div(Ho, v), 256);
+        }
+    }
+    p->kernel = 4;
+    p->tile_m = 64;
+    p->tile_n = 64;
+    p->wave_m = 1;
+    p->rows_per_tile = int32_t(best_rw);
+    p->cols_per_tile = int32_t(Wo);
+    p->patch_rows = int32_t(best_rw + d.KH - 1);
+    p->patch_cols = int32_t(iw);
+    p->stages = 2;
+    p->lds_bytes = pipe_lds_bytes(taps, p->patch_rows, iw);
+    p->tiles = best_groups;
+    p->ws_bytes = 0;    // the kernel reads w as it is stored
+}
+
+// Paired row-block implicit kernel (the same kernel file, `stages` 1):
+// fp16/bf16, Cin % 32 == 0, stride 1, 3x3 or 1x1, one task of RW whole
+// output rows x 64 output channels per workgroup (RW * Wo <= 256), a single
+// 32-channel chunk slot in LDS of at most 80 KB, so that two workgroups
+// share a CU. Taken when `dflt` or when IM2WIN_IMPLICIT_KERNEL=pair;
+// IM2WIN_IMPLICIT_ROWS sets RW.
+static void pick_implicit_pair(const conv2d_desc_t &d, int64_t Ho, int64_t Wo, conv2d_implicit_plan_t *p,
+                               bool dflt) {
+    if (d.dtype == CONV2D_F32 || d.Cin % 32 != 0 || d.stride != 1 || Wo > 256 || Wo < 1 || Ho < 1) return;
+    if (!((d.KH == 3 && d.KW == 3) || (d.KH == 1 && d.KW == 1))) return;
+    if (d.Cin * d.H * d.W >= (int64_t(1) << 31)) return;
+    if (const char *e = std::getenv("IM2WIN_IMPLICIT_KERNEL")) {
+        if (std::strcmp(e, "pair") != 0) return;
+    } else if (!dflt || std::getenv("IM2WIN_IMPLICIT_TILE")) {
+        return;
+    }
+    const int64_t taps = d.KH * d.KW;
+    const int64_t iw = d.W + 2 * d.pad;
+    const int64_t co_blocks = ceil_div(d.Cout, 64);
+    // the most rows per task (the most MFMA blocks per wave) that still leaves
+    // 512 tasks, two per CU; the most rows that fit where none does
+    int64_t best_rw = 0, fit_rw = 0;
+    for (int64_t rw = 1; rw <= Ho && rw * Wo <= 256; ++rw) {
+        if (pair_lds_bytes(taps, rw + d.KH - 1, iw) > kImplicitPairLdsBytes) break;
+        fit_rw = rw;
+        if (co_blocks * d.N * ceil_div(Ho, rw) >= 512) best_rw = rw;
+    }
+    if (best_rw == 0) best_rw = fit_rw;
+    if (best_rw == 0) return;
+    if (const char *e = std::getenv("IM2WIN_IMPLICIT_ROWS")) {
+        const int64_t v = std::min<int64_t>(std::atoi(e), Ho);
+        if (v >= 1 && v * Wo <= 256 && pair_lds_bytes(taps, v + d.KH - 1, iw) <= kImplicitMaxLdsBytes)
+            best_rw = v;
+    }
+    p->kernel = 4;
+    p->tile_m = 64;
+    p->tile_n = 64;
+    p->wave_m = 1;
+    p->rows_per_tile = int32_t(best_rw);
+    p->cols_per_tile = int32_t(Wo);
+    p->patch_rows = int32_t(best_rw + d.KH - 1);
+    p->patch_cols = int32_t(iw);
+    p->stages = 1;
+    p->lds_bytes = pair_lds_bytes(taps, p->patch_rows, iw);
+    p->tiles = co_blocks * d.N * ceil_div(Ho, best_rw);
+    p->ws_bytes = 0;
+}
+
+// The pipelined row-block kernels where they apply by default: the paired
+// form where its tasks of the most rows give at least two per CU or output
+// rows are wider than 64 (the one-slot form keeps its workgroups busy),
+// else the persistent form (its four computing waves take up to four
+// blocks each of a task of up to 256 outputs). Measured on the Table I 3x3
+// layers and the deep 3x3 layer against the row-block kernel over several
+// channel blocks: paired 1.04-1.6x faster on cv8, cv10 and cv11, persistent
+// 1.13x on the 14x14 deep layer (one task per CU).
+static void pick_implicit_pipelined(const conv2d_desc_t &d, int64_t Ho, int64_t Wo, conv2d_implicit_plan_t *p,
+                                    bool dflt) {
+    if (!dflt) {
+        pick_implicit_pipe(d, Ho, Wo, p, false);
+        pick_implicit_pair(d, Ho, Wo, p, false);
+        return;
+    }
+    const int64_t rmax = std::min<int64_t>(Ho, std::max<int64_t>(1, 256 / Wo));
+    const int64_t tasks = ceil_div(d.Cout, 64) * d.N * ceil_div(Ho, rmax);
+    if (Wo > 64 || tasks >= 512) {
+        pick_implicit_pair(d, Ho, Wo, p, true);
+        pick_implicit_pipe(d, Ho, Wo, p, false);
+    } else {
+        pick_implicit_pipe(d, Ho, Wo, p, true);
+        pick_implicit_pair(d, Ho, Wo, p, false);
+    }
+}
+
 // Narrow-channel implicit kernel: Cin <= 8 (the RGB stem and its kind), any
 // filter and stride, Wo <= 512, fp16/bf16/fp32. A workgroup of eight waves
 // takes R output rows of one image (R * Wo <= 512) and 64 output channels,
@@ -534,7 +670,11 @@ conv2d_status_t make_implicit_plan(const conv2d_desc_t &d, conv2d_implicit_plan_
         pick_implicit_rows(d, Ho, Wo, p);
         return p->kernel == 2 ? CONV2D_OK : CONV2D_ERR_UNSUPPORTED;
     }
-    if (d.Cin % 64 != 0) return CONV2D_ERR_UNSUPPORTED;
+    if (d.Cin % 64 != 0) {
+        // 32-channel multiples: only the pipelined row-block kernel
+        pick_implicit_pipelined(d, Ho, Wo, p, true);
+        return p->kernel == 4 ? CONV2D_OK : CONV2D_ERR_UNSUPPORTED;
+    }
     const StageGeom sg = stage_geom(d, IM2WIN_LAYOUT_CL, 64);
     if (sg.row_len != p->K_stage) return CONV2D_ERR_UNSUPPORTED;
     p->ws_bytes = sg.needed ? round_up(sg.rows * sg.row_len * elem_size(d.dtype), 256) : 0;
@@ -608,6 +748,12 @@ conv2d_status_t make_implicit_plan(const conv2d_desc_t &d, conv2d_implicit_plan_
     if (p->tiles > 0x7fffffff) return CONV2D_ERR_INVALID_DESC;
     pick_implicit_fs(d, Ho, Wo, p);
     pick_implicit_rows(d, Ho, Wo, p);
+    // the one-block row kernel stays where it applies (64 channels on rows of
+    // 8k elements, measured faster than both pipelined forms); elsewhere the
+    // pipelined forms take the stride-1 3x3 and 1x1 layers of at least 128
+    // outputs per image
+    const bool one_block = p->kernel == 2 && d.Cin == 64 && d.W % 8 == 0;
+    pick_implicit_pipelined(d, Ho, Wo, p, !one_block && Ho * Wo >= 128);
     return CONV2D_OK;
 }
 

@@ -43,6 +43,17 @@ constexpr int64_t kImplicitStoreScratchBytes = 8 * 16 * 68 * 4;
 inline int64_t implicit_rows_lds_bytes(int64_t taps, int64_t sl, int64_t iw) {
     return std::max<int64_t>(taps * 8192 + sl * iw * 128, kImplicitStoreScratchBytes);
 }
+// pipelined row-block implicit form: two slots, each a 32-channel filter
+// block (4 KB per tap) + sl input rows of iw positions x 64 bytes, and the
+// store scratch of its four computing waves (16 x 68 floats each)
+inline int64_t pipe_lds_bytes(int64_t taps, int64_t sl, int64_t iw) {
+    return 2 * (taps * 4096 + sl * iw * 64) + 4 * 16 * 68 * 4;
+}
+// paired row-block implicit form: one such slot, which after the last chunk
+// holds the store scratch of its eight waves
+inline int64_t pair_lds_bytes(int64_t taps, int64_t sl, int64_t iw) {
+    return std::max<int64_t>(taps * 4096 + sl * iw * 64, kImplicitStoreScratchBytes);
+}
 // narrow-channel implicit form: the filter block (64 rows of kp elements + 16
 // bytes) + r window rows of lp elements, es bytes per element (the window rows'
 // space holds at least the store scratch)

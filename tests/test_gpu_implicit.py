@@ -211,7 +211,7 @@ def _eligible_configs():
         for dt in cfg.dtypes:
             if (dt != "f32" and cfg.Cin % 64 == 0) or (name, dt) == ("resnet3x3", "f32"):
                 out.append((name, dt))
-    for name in ("cv4", "cv8", "cv12"):
+    for name in ("cv4", "cv8", "cv10", "cv11", "cv12"):
         out.append((name, "f16"))
     return out
 
@@ -319,6 +319,7 @@ ROWS_CASES = [(s, dt) for dt in ("f32", "f16", "bf16") for s in ROWS_SHAPES] + \
 @pytest.mark.parametrize("rw", [None, 1, 3, 8])
 def test_row_block_kernel_matches_oracle(shape, dt, rw, monkeypatch):
     N, Cin, H, W, Cout, KH, KW, s, p = shape
+    monkeypatch.setenv("IM2WIN_IMPLICIT_KERNEL", "rows")
     if rw is not None:
         monkeypatch.setenv("IM2WIN_IMPLICIT_ROWS", str(rw))
     d = conv.make_desc(*shape, CODE[dt])
@@ -335,10 +336,11 @@ def test_row_block_kernel_matches_oracle(shape, dt, rw, monkeypatch):
 
 @pytest.mark.parametrize("shape", ROWS_SHAPES[:4] + ROWS_SHAPES[6:7], ids=[str(s) for s in ROWS_SHAPES[:4] + ROWS_SHAPES[6:7]])
 @pytest.mark.parametrize("dt", ["f32", "f16"])
-def test_row_block_kernel_integer_inputs_exact(shape, dt):
+def test_row_block_kernel_integer_inputs_exact(shape, dt, monkeypatch):
     """Integer-valued inputs: every product and partial sum is exact in fp32,
     so the row-block kernel matches the oracle bit for bit."""
     N, Cin, H, W, Cout, KH, KW, s, p = shape
+    monkeypatch.setenv("IM2WIN_IMPLICIT_KERNEL", "rows")
     x, w = workloads.make_inputs(N, Cin, H, W, Cout, KH, KW, seed=22, dtype=dt,
                                  x_dist="int3", w_dist="int3")
     assert conv.implicit_plan(conv.make_desc(*shape, CODE[dt])).kernel == 2
@@ -348,8 +350,9 @@ def test_row_block_kernel_integer_inputs_exact(shape, dt):
 
 
 @pytest.mark.parametrize("dt", ["f32", "f16"])
-def test_row_block_kernel_leaves_memory_past_y_untouched(dt):
+def test_row_block_kernel_leaves_memory_past_y_untouched(dt, monkeypatch):
     N, Cin, H, W, Cout, KH, KW, s, p = 2, 64, 9, 16, 70, 3, 3, 1, 0
+    monkeypatch.setenv("IM2WIN_IMPLICIT_KERNEL", "rows")
     x, w = workloads.make_inputs(N, Cin, H, W, Cout, KH, KW, seed=23, dtype=dt)
     d = conv.describe(tuple(x.shape), tuple(w.shape), s, p, CODE[dt])
     pl = conv.implicit_plan(d)
@@ -464,10 +467,92 @@ def test_narrow_kernel_persistent_and_multiround(shape, dt, rows, monkeypatch):
 
 
 @pytest.mark.parametrize("shape", ROWS_SHAPES_MULTI, ids=[str(s) for s in ROWS_SHAPES_MULTI])
-def test_row_block_multi_integer_inputs_exact(shape):
+def test_row_block_multi_integer_inputs_exact(shape, monkeypatch):
     N, Cin, H, W, Cout, KH, KW, s, p = shape
+    monkeypatch.setenv("IM2WIN_IMPLICIT_KERNEL", "rows")
     assert conv.implicit_plan(conv.make_desc(*shape, conv.F16)).kernel == 2
     x, w = workloads.make_inputs(N, Cin, H, W, Cout, KH, KW, seed=24, dtype="f16",
                                  x_dist="int3", w_dist="int3")
     got = run_implicit(x, w, s, p)
     assert np.array_equal(got.numpy().astype(np.float64), oracle.conv2d(x, w, s, p))
+
+
+# pipelined row-block kernels (fp16/bf16, Cin % 32 == 0, stride 1, 3x3 or 1x1,
+# Wo <= 256) over 32-channel K chunks: "pipe", persistent workgroups whose
+# four loader waves fill one of two LDS slots while four waves contract the
+# other; "pair", one task and one slot per workgroup, two workgroups per CU
+PIPE_SHAPES = [
+    (2, 32, 10, 16, 40, 3, 3, 1, 1),     # one chunk; planes of 8k positions (16-byte loads)
+    (2, 64, 14, 14, 72, 3, 3, 1, 1),     # planes of 4k positions (8-byte loads), Cout past one block
+    (1, 96, 9, 13, 64, 3, 3, 1, 0),      # odd planes (2-byte loads), three chunks, Wo = 11
+    (3, 128, 12, 20, 130, 1, 1, 1, 0),   # 1x1, three blocks of Cout
+    (1, 64, 6, 8, 8, 3, 3, 1, 2),        # padding 2: zero rows and columns
+    (1, 64, 5, 56, 72, 3, 3, 1, 3),      # padding wider than the filter: tasks with no input row
+    (2, 256, 14, 14, 256, 3, 3, 1, 1),   # the deep 3x3 layer's image, eight chunks
+    (1, 32, 5, 160, 16, 3, 3, 1, 1),     # 160-column output rows (10 blocks per row)
+    (1, 64, 9, 24, 64, 1, 1, 1, 1),      # 1x1 with padding: zero border outputs
+]
+PIPE_CASES = [(s, dt, k) for k in ("pipe", "pair") for dt in ("f16", "bf16") for s in PIPE_SHAPES]
+
+
+@pytest.mark.parametrize("shape,dt,form", PIPE_CASES, ids=[f"{k}-{dt}-{s}" for s, dt, k in PIPE_CASES])
+@pytest.mark.parametrize("rw", [None, 1, 3])
+def test_pipelined_kernel_matches_oracle(shape, dt, form, rw, monkeypatch):
+    N, Cin, H, W, Cout, KH, KW, s, p = shape
+    monkeypatch.setenv("IM2WIN_IMPLICIT_KERNEL", form)
+    if rw is not None:
+        monkeypatch.setenv("IM2WIN_IMPLICIT_ROWS", str(rw))
+    pl = conv.implicit_plan(conv.make_desc(*shape, CODE[dt]))
+    assert pl.kernel == 4 and pl.ws_bytes == 0 and pl.stages == (2 if form == "pipe" else 1)
+    if rw is not None and rw * pl.Wo <= 256:     # else the override is ignored
+        assert pl.rows_per_tile == min(rw, pl.Ho)
+    _say(f"implicit-{form} {dt} {shape} rows/task={pl.rows_per_tile} workgroups={pl.tiles} lds={pl.lds_bytes}")
+    x, w = workloads.make_inputs(N, Cin, H, W, Cout, KH, KW, seed=25, dtype=dt)
+    got = run_implicit(x, w, s, p)
+    assert rel_l2(got.numpy(), oracle.conv2d(x, w, s, p)) <= TOL[dt]
+
+
+@pytest.mark.parametrize("form", ["pipe", "pair"])
+@pytest.mark.parametrize("shape", PIPE_SHAPES[:6], ids=[str(s) for s in PIPE_SHAPES[:6]])
+def test_pipelined_kernel_integer_inputs_exact(shape, form, monkeypatch):
+    N, Cin, H, W, Cout, KH, KW, s, p = shape
+    monkeypatch.setenv("IM2WIN_IMPLICIT_KERNEL", form)
+    assert conv.implicit_plan(conv.make_desc(*shape, conv.F16)).kernel == 4
+    x, w = workloads.make_inputs(N, Cin, H, W, Cout, KH, KW, seed=26, dtype="f16",
+                                 x_dist="int3", w_dist="int3")
+    got = run_implicit(x, w, s, p)
+    assert np.array_equal(got.numpy().astype(np.float64), oracle.conv2d(x, w, s, p))
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_pipelined_kernel_several_tasks_per_workgroup(dt, monkeypatch):
+    """More tasks than workgroups (one output row per task): each persistent
+    workgroup carries its chunk pipeline across task boundaries."""
+    shape = (4, 64, 30, 30, 256, 3, 3, 1, 1)
+    N, Cin, H, W, Cout, KH, KW, s, p = shape
+    monkeypatch.setenv("IM2WIN_IMPLICIT_KERNEL", "pipe")
+    monkeypatch.setenv("IM2WIN_IMPLICIT_ROWS", "1")
+    pl = conv.implicit_plan(conv.make_desc(*shape, CODE[dt]))
+    tasks = 4 * N * pl.Ho
+    assert pl.kernel == 4 and pl.tiles == 256 and tasks > pl.tiles
+    _say(f"implicit-pipe {dt} {shape} tasks={tasks} workgroups={pl.tiles}")
+    x, w = workloads.make_inputs(N, Cin, H, W, Cout, KH, KW, seed=27, dtype=dt)
+    got = run_implicit(x, w, s, p)
+    assert rel_l2(got.numpy(), oracle.conv2d(x, w, s, p)) <= TOL[dt]
+
+
+@pytest.mark.parametrize("form", ["pipe", "pair"])
+def test_pipelined_kernel_leaves_memory_past_y_untouched(form, monkeypatch):
+    N, Cin, H, W, Cout, KH, KW, s, p = 2, 64, 9, 13, 70, 3, 3, 1, 0
+    monkeypatch.setenv("IM2WIN_IMPLICIT_KERNEL", form)
+    x, w = workloads.make_inputs(N, Cin, H, W, Cout, KH, KW, seed=28, dtype="f16")
+    d = conv.describe(tuple(x.shape), tuple(w.shape), s, p, conv.F16)
+    pl = conv.implicit_plan(d)
+    assert pl.kernel == 4
+    n_out = N * Cout * pl.Ho * pl.Wo
+    buf = torch.full((n_out + 4096,), 12345.0, dtype=torch.float32, device=DEV)
+    conv.conv2d_implicit_into(x.to(DEV), w.to(DEV), buf, None, s, p)
+    torch.cuda.synchronize()
+    host = buf.cpu().numpy()
+    assert (host[n_out:] == 12345.0).all()
+    assert rel_l2(host[:n_out], oracle.conv2d(x, w, s, p).reshape(-1)) <= TOL["f16"]

@@ -265,16 +265,19 @@ def test_row_layout_keeps_slack_after_every_run():
 
 
 def test_implicit_plan_takes_only_its_layers():
-    """The implicit form takes fp16/bf16 layers with Cin a multiple of 64 and
-    reports UNSUPPORTED (status 4) for the rest, before touching any pointer."""
+    """The implicit form takes fp16/bf16 layers with Cin a multiple of 64 (and
+    stride-1 3x3 / 1x1 ones with Cin a multiple of 32) and reports UNSUPPORTED
+    (status 4) for the rest, before touching any pointer."""
     assert conv._lib.implicit_plan_status(conv.make_desc(2, 64, 9, 9, 8, 3, 3, 1, 1, conv.F32)) == 4
-    assert conv._lib.implicit_plan_status(conv.make_desc(2, 96, 9, 9, 8, 3, 3, 1, 1, conv.F16)) == 4
+    assert conv._lib.implicit_plan_status(conv.make_desc(2, 80, 9, 9, 8, 3, 3, 1, 1, conv.F16)) == 4
+    assert conv._lib.implicit_plan_status(conv.make_desc(2, 96, 9, 9, 8, 3, 3, 2, 1, conv.F16)) == 4
+    assert conv.implicit_plan(conv.make_desc(2, 96, 9, 9, 8, 3, 3, 1, 1, conv.F16)).kernel == 4
     assert conv._lib.implicit_plan_status(conv.make_desc(2, 12, 9, 9, 8, 3, 3, 1, 1, conv.BF16)) == 4
     # up to 8 input channels: the narrow-channel kernel, any dtype
     for dt in (conv.F32, conv.F16, conv.BF16):
         assert conv.implicit_plan(conv.make_desc(2, 3, 9, 9, 8, 3, 3, 1, 1, dt)).kernel == 3
     assert conv._lib.implicit_plan_status(conv.make_desc(0, 64, 9, 9, 8, 3, 3, 1, 1, conv.F16)) == 1
-    d = conv.make_desc(2, 96, 9, 9, 8, 3, 3, 1, 1, conv.F16)
+    d = conv.make_desc(2, 80, 9, 9, 8, 3, 3, 1, 1, conv.F16)
     assert conv.implicit_workspace_size(d) == 0
     assert _lib.fwd_implicit(d, 16, 16, 16, 256, None) == 4
     d = conv.make_desc(2, 64, 9, 9, 8, 3, 3, 1, 1, conv.F16)
@@ -344,19 +347,20 @@ def test_conv2d_plan_names_the_form_conv2d_fwd_runs(monkeypatch):
     assert q.algo == 0 and q.ws_bytes == q.wstage_bytes + q.win_chunk_bytes
     monkeypatch.setenv("IM2WIN_ALGO", "implicit")
     for args in [(2, 16, 20, 20, 16, 3, 3, 1, 1, conv.F16), (2, 48, 20, 20, 16, 3, 3, 1, 1, conv.F32),
-                 (2, 96, 20, 20, 16, 3, 3, 1, 1, conv.BF16)]:
+                 (2, 80, 20, 20, 16, 3, 3, 1, 1, conv.BF16)]:
         assert conv.plan(conv.make_desc(*args)).algo == 0     # not applicable: stays on the window form
     assert conv.plan(conv.make_desc(2, 256, 14, 14, 16, 3, 3, 1, 1, conv.BF16)).algo == 1
 
 
 def test_row_block_plan_geometry(monkeypatch):
-    """The row-block implicit kernel is planned exactly for its layers (fp16/bf16,
-    stride 1, Wo <= 64, a 3x3 or 1x1 filter; 64 input channels on rows of 8k
-    elements, or any multiple of 64 channels where an image has at least 128
-    outputs): whole output rows per workgroup, the block's input rows and the
-    filter in LDS, no workspace, one workgroup per (64-channel block, row
-    block, image)."""
+    """The row-block implicit kernel (asked for by name) is planned exactly for
+    its layers (fp16/bf16, stride 1, Wo <= 64, a 3x3 or 1x1 filter; 64 input
+    channels on rows of 8k elements, or any multiple of 64 channels where an
+    image has at least 128 outputs): whole output rows per workgroup, the
+    block's input rows and the filter in LDS, no workspace, one workgroup per
+    (64-channel block, row block, image)."""
     import numpy as np
+    monkeypatch.setenv("IM2WIN_IMPLICIT_KERNEL", "rows")
     rng = np.random.default_rng(12)
     taken = 0
     for _ in range(600):
@@ -388,6 +392,7 @@ def test_row_block_plan_geometry(monkeypatch):
         assert conv.plan(d).algo == 1 and conv.workspace_size(d) == 0
     assert taken > 50
     # the other kernels stay reachable
+    monkeypatch.delenv("IM2WIN_IMPLICIT_KERNEL")
     d = conv.make_desc(32, 64, 56, 56, 64, 3, 3, 1, 1, conv.F16)
     assert conv.implicit_plan(d).kernel == 2 and conv.implicit_plan(d).rows_per_tile == 7
     monkeypatch.setenv("IM2WIN_IMPLICIT_KERNEL", "streamed")
@@ -395,6 +400,64 @@ def test_row_block_plan_geometry(monkeypatch):
     monkeypatch.setenv("IM2WIN_IMPLICIT_KERNEL", "rows")
     monkeypatch.setenv("IM2WIN_IMPLICIT_ROWS", "3")
     assert conv.implicit_plan(d).kernel == 2 and conv.implicit_plan(d).rows_per_tile == 3
+
+
+def test_pipelined_plan_geometry():
+    """By default the one-block row kernel keeps its layers (64 channels on rows
+    of 8k elements, Wo <= 64) and the pipelined row-block kernels take the other
+    stride-1 3x3 and 1x1 fp16/bf16 layers with Cin a multiple of 32 and at least
+    128 outputs per image (any size where Cin is not a multiple of 64): tasks of
+    R whole output rows x 64 output channels, R * Wo <= 256, 32-channel chunks
+    in LDS (two slots and persistent workgroups, or one slot of at most 80 KB,
+    one task per workgroup), no workspace."""
+    import numpy as np
+    rng = np.random.default_rng(14)
+    seen = {1: 0, 2: 0}
+    for _ in range(800):
+        KH, KW = [(3, 3), (1, 1), (5, 5)][int(rng.integers(0, 3))]
+        s = int(rng.choice([1, 1, 1, 2]))
+        p = int(rng.integers(0, 3))
+        Cin = int(rng.choice([32, 64, 96, 128, 256]))
+        W = int(rng.choice([8, 12, 14, 16, 28, 56, 60, 112, 150]))
+        H = int(rng.integers(max(KH, 1), 40))
+        N, Cout = int(rng.integers(1, 9)), int(rng.integers(1, 300))
+        d = conv.make_desc(N, Cin, H, W, Cout, KH, KW, s, p, [conv.F16, conv.BF16][int(rng.integers(0, 2))])
+        if conv._lib.implicit_plan_status(d) != 0:
+            continue
+        pl = conv.implicit_plan(d)
+        one_block = Cin == 64 and W % 8 == 0 and s == 1 and pl.Wo <= 64 and (KH, KW) in ((3, 3), (1, 1))
+        if one_block:
+            assert pl.kernel == 2, (N, Cin, H, W, Cout, KH, KW, s, p)
+            continue
+        if pl.kernel != 4:
+            # only where a pipelined form does not apply (or a small image)
+            assert s != 1 or (KH, KW) not in ((3, 3), (1, 1)) or pl.Wo > 256 or \
+                (Cin % 64 == 0 and pl.Ho * pl.Wo < 128) or Cin % 32 != 0, (N, Cin, H, W, Cout, KH, KW, s, p)
+            continue
+        assert s == 1 and (KH, KW) in ((3, 3), (1, 1)) and Cin % 32 == 0
+        seen[pl.stages] += 1
+        R = pl.rows_per_tile
+        assert 1 <= R <= pl.Ho and R * pl.Wo <= 256
+        assert pl.patch_rows == R + KH - 1 and pl.patch_cols == W + 2 * p and pl.cols_per_tile == pl.Wo
+        tasks = -(-Cout // 64) * N * -(-pl.Ho // R)
+        taps = KH * KW
+        if pl.stages == 2:
+            assert pl.lds_bytes == 2 * (taps * 4096 + pl.patch_rows * pl.patch_cols * 64) + 4 * 16 * 68 * 4
+            assert pl.tiles == min(tasks, 256)
+        else:
+            assert pl.lds_bytes == max(taps * 4096 + pl.patch_rows * pl.patch_cols * 64, STORE_SCRATCH)
+            assert pl.lds_bytes <= 80 * 1024 and pl.tiles == tasks
+        assert pl.lds_bytes <= 160 * 1024
+        assert pl.ws_bytes == 0 == conv.implicit_workspace_size(d)
+        assert conv.plan(d).algo == 1
+    assert seen[1] > 20 and seen[2] > 20, seen
+    # the layers measured: the deep 14x14 layer on the persistent form, the
+    # Table I 28x28 and 14x14 layers on the paired one
+    for name, stages in [("deep3x3", 2), ("cv10", 1), ("cv11", 1), ("cv8", 1)]:
+        cfg = workloads.get_config(name)
+        dt = conv.BF16 if name == "deep3x3" else conv.F16
+        pl = conv.implicit_plan(conv.make_desc(*cfg.desc().values(), dt))
+        assert pl.kernel == 4 and pl.stages == stages, name
 
 
 def test_row_block_plan_fp32():
