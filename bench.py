@@ -102,8 +102,10 @@ def dominant_key(d, plan):
     if plan.algo == 1:
         ip = conv.implicit_plan(d)
         kid = {0: 4, 1: 5, 2: 6, 3: 7, 4: 8}[ip.kernel]
+        # the pipelined row-block kernel: stages 2 = persistent, 1 = paired form
+        form = f"/s{ip.stages}" if ip.kernel == 4 else ""
         return (kid, f"i{ip.kernel}:{ip.tile_m}x{ip.tile_n}/{ip.wave_m}/r{ip.rows_per_tile}/"
-                f"c{ip.cols_per_tile}/g{ip.tiles}", plan.rows_total)
+                f"c{ip.cols_per_tile}/g{ip.tiles}{form}", plan.rows_total)
     rows = plan.rows_total - (plan.n_chunks - 1) * plan.rows_per_chunk
     return (plan.gemm_kernel, f"k{plan.gemm_kernel}:{plan.gemm_tile_m}x{plan.gemm_tile_n}/"
             f"{plan.gemm_kslice}/{plan.gemm_ksplit}/{plan.gemm_wave_m}", rows)

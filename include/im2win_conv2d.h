@@ -187,9 +187,11 @@ const char *conv2d_status_string(conv2d_status_t s);
  * input channels, the input rows its window rows interleave (Eq. (2) of the
  * im2win paper: window row ho = input rows ho*stride - pad .. + KH - 1) as a
  * channels-innermost patch, and contracts it against the staged filter in
- * the window's K order (Sec. III-C Eq. (3), Sec. III-D). fp16/bf16 only,
- * Cin a multiple of 64; matrix cores with fp32 accumulation, fp32 y. The
- * workspace holds only the staged filter (none for a 1x1 filter). */
+ * the window's K order (Sec. III-C Eq. (3), Sec. III-D). Matrix cores with
+ * fp32 accumulation, fp32 y: fp16/bf16 with Cin a multiple of 64 (or of 32
+ * for stride-1 3x3 and 1x1 filters), up to 8 input channels in any dtype,
+ * fp32 on the row-block kernel's layers. The workspace holds only the staged
+ * filter (none for a 1x1 filter or for the row-block kernels). */
 typedef struct {
     int32_t tile_m, tile_n;       /* output channels x GEMM columns per workgroup  */
     int32_t wave_m;               /* waves along M                                 */
@@ -207,22 +209,34 @@ typedef struct {
                                      row-block, rows_per_tile whole output rows
                                      of one image per workgroup with w as stored
                                      and the input rows resident in LDS, no
-                                     staged filter (ws_bytes 0)                   */
+                                     staged filter (ws_bytes 0); 3: narrow-channel
+                                     (Cin <= 8); 4 (default for the other stride-1
+                                     3x3 and 1x1 layers with Cin % 32 == 0, Wo <=
+                                     256 and at least 128 outputs per image):
+                                     pipelined row-block, tasks of rows_per_tile
+                                     whole output rows x 64 output channels over
+                                     32-channel K chunks double-buffered in LDS,
+                                     w as stored (ws_bytes 0)                       */
     int32_t stages;               /* kernel 0: filter K stages in flight + 1 (LDS
-                                     stage buffers)                                 */
+                                     stage buffers); kernel 3: channels per window
+                                     position; kernel 4: 2 = persistent workgroups
+                                     (tiles of them) with loading and computing
+                                     waves, 1 = one task per workgroup (tiles
+                                     tasks), two workgroups per CU                 */
     int32_t reserved;
     int64_t lds_bytes;            /* LDS per workgroup                              */
     int64_t tiles;                /* workgroups of the launch                       */
     int64_t Ho, Wo;
     int64_t K_stage;              /* staged filter row: KW*KH*Cin                   */
     int64_t ws_bytes;             /* the staged filter; 0 for a 1x1 filter and for
-                                     kernel 2                                       */
+                                     kernels 2 and 4                                */
     int64_t flops;                /* 2*N*Cout*Ho*Wo*Cin*KH*KW                        */
 } conv2d_implicit_plan_t;
 
 /* Fill *out for *d. CONV2D_ERR_UNSUPPORTED when the implicit form does not
- * take the layer (fp32, Cin not a multiple of 64, or no tile whose patch
- * fits in LDS); other errors as conv2d_plan. Host only. */
+ * take the layer (fp32 outside the row-block kernel's layers, Cin past 8 and
+ * not a multiple of 64 outside the pipelined row-block kernel's layers, or no
+ * tile whose patch fits in LDS); other errors as conv2d_plan. Host only. */
 conv2d_status_t conv2d_implicit_plan(const conv2d_desc_t *d, conv2d_implicit_plan_t *out);
 
 /* Bytes of workspace conv2d_fwd_implicit needs (0 if d is invalid or not
@@ -240,7 +254,7 @@ conv2d_status_t conv2d_fwd_implicit(const conv2d_desc_t *d, const void *x, const
  * with a filter already staged in the window's K order (as
  * im2win_weight_stage writes it for IM2WIN_LAYOUT_CL), or w itself where the
  * plan keeps no staged filter (conv2d_implicit_workspace_size(d) == 0: a 1x1
- * filter, or the row-block kernel, which reorders w in LDS on its own),
+ * filter, or the row-block kernels, which reorder w in LDS on their own),
  * writing all of y. Device pointers, 16-byte aligned. */
 conv2d_status_t im2win_implicit_gemm(const conv2d_desc_t *d, const void *x, const void *wst,
                                      float *y, void *stream);
