@@ -429,6 +429,75 @@ def probe(args, dev):
          f"kernel={GEMM_KERNEL_NAMES[kid]} sha={gemm_source_sha(kid)} launches={args.steps}")
 
 
+ABLATIONS = [("none", ""), ("serpentine", "serpentine"), ("dma", "dma"), ("buffers", "buffers"),
+             ("all", "serpentine,dma,buffers")]
+ABLATION_LAYERS = [("resnet3x3", "f16"), ("deep3x3", "bf16"), ("mix5x5", "f16"), ("mix512", "f16"),
+                   ("mix3x3s2", "f16"), ("mix1x1", "f16"), ("cv9", "f16"), ("cv10", "f16"),
+                   ("cv11", "f16"), ("cv12", "f16")]
+
+
+def ablation(args, dev):
+    """The page's optimisations turned off one at a time in the direct-to-LDS
+    window-GEMM (IM2WIN_ABLATE): the window form is forced, the window rows of
+    the last chunk are packed once, and the GEMM alone on them is timed with
+    events over back-to-back launches for each variant, whose output is also
+    checked against the planned kernel's. One JSON line per layer."""
+    import torch
+
+    import cnn_convolution_amd as conv
+    import workloads
+    os.environ["IM2WIN_ALGO"] = "window"
+    for name, dt in ABLATION_LAYERS:
+        cfg = workloads.get_config(name)
+        x, w = layer_inputs(cfg, dt)
+        xd, wd = x.to(dev), w.to(dev)
+        d = conv.describe(tuple(x.shape), tuple(w.shape), cfg.stride, cfg.pad,
+                          {"f16": conv.F16, "bf16": conv.BF16}[dt])
+        plan = conv.plan(d)
+        if plan.gemm_kernel != 3:
+            _say(f"ablation: {name} {dt}: the window-GEMM is not the direct-to-LDS kernel, skipped")
+            continue
+        y = torch.zeros((cfg.N, cfg.Cout, plan.Ho, plan.Wo), dtype=torch.float32, device=dev)
+        ws = torch.empty(max(plan.ws_bytes, 1), dtype=torch.uint8, device=dev)
+        conv.conv2d_into(xd, wd, y, ws, cfg.stride, cfg.pad)
+        row0 = (plan.n_chunks - 1) * plan.rows_per_chunk
+        rows = plan.rows_total - row0
+        win = ws[plan.win_offset_bytes:plan.win_offset_bytes + rows * plan.row_elems * 2]
+        wst = ws if plan.wstage_bytes else wd
+        flops = 2 * cfg.Cout * rows * plan.Wo * cfg.Cin * cfg.KH * cfg.KW
+        ref = None
+        out = {}
+        for label, env in ABLATIONS:
+            if env:
+                os.environ["IM2WIN_ABLATE"] = env
+            else:
+                os.environ.pop("IM2WIN_ABLATE", None)
+            assert conv.plan(d).gemm_ablate == sum(b for k, b in (("serpentine", 1), ("dma", 2), ("buffers", 4))
+                                                   if k in env)
+            y.zero_()
+            for _ in range(args.warmup):
+                conv.window_gemm(win, wst, y, d, row0, rows)
+            torch.cuda.synchronize()
+            got = y.clone()
+            if ref is None:
+                ref = got
+            same = bool(torch.equal(got, ref))
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(args.steps):
+                conv.window_gemm(win, wst, y, d, row0, rows)
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) / args.steps * 1e3
+            out[label] = {"us": round(us, 2), "tflops": round(flops / us / 1e6, 1), "same_output": same}
+            _say(f"ablation: {name} {dt} {label}: {us:.2f} us")
+        os.environ.pop("IM2WIN_ABLATE", None)
+        print(json.dumps({"workload": name, "dtype": dt, "kernel": "gemm_mfma_dma",
+                          "tile": f"{plan.gemm_tile_m}x{plan.gemm_tile_n}/{plan.gemm_wave_m}",
+                          "rows_per_launch": rows, "variants": out}), flush=True)
+    os.environ.pop("IM2WIN_ALGO", None)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -446,6 +515,9 @@ def main():
     ap.add_argument("--table1", action="store_true",
                     help="one JSON line per layer of the im2win paper's Table I (N=256, "
                          "no padding), fp16 headline with the fp32 variant")
+    ap.add_argument("--ablation", action="store_true",
+                    help="the window-GEMM with each of the page's optimisations turned off, "
+                         "one JSON line per layer (not the benchmark line)")
     ap.add_argument("--probe", choices=["gemm", "copy"], default=None,
                     help="for hardware counters: launch only the dominant kernel of the "
                          "layer (last chunk, --steps times) or a device copy of a known size")
@@ -468,6 +540,9 @@ def main():
     dev = torch.device("cuda:0")
     if args.probe:
         probe(args, dev)
+        return
+    if args.ablation:
+        ablation(args, dev)
         return
     names = (list(workloads.TABLE1) if args.table1 else
              sorted(workloads.CONFIGS) if args.all_configs else [args.config])

@@ -50,6 +50,7 @@ _PLAN_FIELDS = [
     ("gemm_tile_n", ctypes.c_int32), ("gemm_kslice", ctypes.c_int32),
     ("gemm_ksplit", ctypes.c_int32), ("gemm_kernel", ctypes.c_int32),
     ("gemm_wave_m", ctypes.c_int32), ("algo", ctypes.c_int32),
+    ("gemm_ablate", ctypes.c_int32), ("reserved2", ctypes.c_int32),
     ("flops", ctypes.c_int64),
 ]
 

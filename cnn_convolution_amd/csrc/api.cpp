@@ -133,6 +133,7 @@ hipError_t launch_gemm(const conv2d_desc_t &d, const conv2d_plan_t &p, const Lay
     ga.ks = p.gemm_ksplit;
     ga.wm = p.gemm_wave_m;
     ga.bf16 = d.dtype == CONV2D_BF16 ? 1 : 0;
+    ga.ablate = p.gemm_ablate;
     if (p.gemm_kernel == 3) return launch_gemm_mfma_dma(ga, s);
     return p.gemm_kernel == 2 ? launch_gemm_mfma_resident(ga, s) : launch_gemm_mfma(ga, s);
 }

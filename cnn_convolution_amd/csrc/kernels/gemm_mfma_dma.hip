@@ -32,12 +32,26 @@ namespace {
 
 constexpr int KI = kStageK;
 
-template <int MB, int NB, int WM, bool BF16>
+// Ablation switches (ABL, a bit mask; 0 is the kernel as planned), for
+// measuring what each of the page's three optimisations gives on MI355X
+// ("Enabling Memory-efficient Im2win Convolution ...", Sec. III-E; the
+// ablation of Sec. IV-E, Fig. 4): no serpentine tile order (plain row-major tiles), no
+// direct-to-LDS copies (global loads into registers, then LDS stores), one
+// stage buffer instead of three (each stage loaded, waited for, then
+// multiplied).
+constexpr int kAblateSerpentine = 1;
+constexpr int kAblateDma = 2;
+constexpr int kAblateBuffers = 4;
+
+template <int MB, int NB, int WM, bool BF16, int ABL>
 __global__ __launch_bounds__(256) void gemm_mfma_dma_kernel(
     const uint16_t *__restrict__ win, const uint16_t *__restrict__ wst, float *__restrict__ y,
     int rows, int row0, int row_elems, int col_step, int kstage, int Ho, int Wo, int Cout,
     int tiles_m)
 {
+    constexpr bool SERP = !(ABL & kAblateSerpentine);
+    constexpr bool DMA = !(ABL & kAblateDma);
+    constexpr int NBUF = (ABL & kAblateBuffers) ? 1 : 3;
     constexpr int WN = 4 / WM;
     constexpr int FM = MB / WM / 16;
     constexpr int FN = NB / WN / 16;
@@ -47,11 +61,16 @@ __global__ __launch_bounds__(256) void gemm_mfma_dma_kernel(
     static_assert(AI >= 1 && BI >= 1 && AI * 32 == MB && BI * 32 == NB, "tiling");
     static_assert(FM >= 1 && FN >= 1 && WM * WN == 4, "wave layout");
     __shared__ __attribute__((aligned(16))) uint16_t sa0[MB * KI], sb0[NB * KI];
-    __shared__ __attribute__((aligned(16))) uint16_t sa1[MB * KI], sb1[NB * KI];
-    __shared__ __attribute__((aligned(16))) uint16_t sa2[MB * KI], sb2[NB * KI];
+    __shared__ __attribute__((aligned(16))) uint16_t sa1[NBUF > 1 ? MB * KI : 8], sb1[NBUF > 1 ? NB * KI : 8];
+    __shared__ __attribute__((aligned(16))) uint16_t sa2[NBUF > 1 ? MB * KI : 8], sb2[NBUF > 1 ? NB * KI : 8];
 
     int tm, tn;
-    tile_coords(blockIdx.x, gridDim.x, tiles_m, tm, tn);
+    if constexpr (SERP) {
+        tile_coords(blockIdx.x, gridDim.x, tiles_m, tm, tn);
+    } else {
+        tm = blockIdx.x % tiles_m;
+        tn = blockIdx.x / tiles_m;
+    }
     const int m0 = tm * MB;
     const int n0 = tn * NB;
     const int ncols = rows * Wo;
@@ -90,6 +109,22 @@ __global__ __launch_bounds__(256) void gemm_mfma_dma_kernel(
         for (int i = 0; i < BI; ++i)
             copy_to_lds(bsrc[i] + k0, __builtin_amdgcn_readfirstlane(lds_addr(sb + (wave + 4 * i) * 512)));
     };
+    // the same copies through registers (ablation): lane l's 16 bytes land
+    // at bytes [16l, 16l+16) of the same 1 KB block
+    uint4 stg[D];
+    auto load_regs = [&](int stage) {
+        const int k0 = stage * KI;
+#pragma unroll
+        for (int i = 0; i < AI; ++i) stg[i] = *reinterpret_cast<const uint4 *>(asrc[i] + k0);
+#pragma unroll
+        for (int i = 0; i < BI; ++i) stg[AI + i] = *reinterpret_cast<const uint4 *>(bsrc[i] + k0);
+    };
+    auto store_regs = [&](uint16_t *sa, uint16_t *sb) {
+#pragma unroll
+        for (int i = 0; i < AI; ++i) *reinterpret_cast<uint4 *>(sa + (wave + 4 * i) * 512 + lane * 8) = stg[i];
+#pragma unroll
+        for (int i = 0; i < BI; ++i) *reinterpret_cast<uint4 *>(sb + (wave + 4 * i) * 512 + lane * 8) = stg[AI + i];
+    };
 
     floatx4_t acc[FM][FN];
 #pragma unroll
@@ -127,24 +162,64 @@ __global__ __launch_bounds__(256) void gemm_mfma_dma_kernel(
     // one, so the final two steps re-copy it into buffers already read), so
     // each wave always has exactly two groups in flight at the top of a step
     // and waits for the older one: no data-dependent branch in the loop.
-    issue(0, sa0, sb0);
-    issue(min(1, nk - 1), sa1, sb1);
-    auto step = [&](int k, uint16_t *ca, uint16_t *cb, uint16_t *na, uint16_t *nb) {
-        wait_vm<D>();                      // own copies of stage k landed (k+1 may fly)
-        stage_barrier();                   // everyone's copies of stage k landed; stage k-1 read
-        issue(min(k + 2, nk - 1), na, nb); // into the buffer stage k-1 used
-        compute(ca, cb);
-        __builtin_amdgcn_sched_barrier(0); // keep each step's work inside its step
-    };
-    // the loop may leave after any step (uniform test): the accumulators then
-    // stay in the same registers from one step to the next
-    for (int k = 0;; k += 3) {
-        step(k, sa0, sb0, sa2, sb2);
-        if (k + 1 >= nk) break;
-        step(k + 1, sa1, sb1, sa0, sb0);
-        if (k + 2 >= nk) break;
-        step(k + 2, sa2, sb2, sa1, sb1);
-        if (k + 3 >= nk) break;
+    if constexpr (NBUF == 1) {
+        // ablation: one buffer, each stage loaded and waited for before it is
+        // multiplied, and multiplied by every wave before the next is loaded
+        for (int k = 0; k < nk; ++k) {
+            if (k > 0) stage_barrier();
+            if constexpr (DMA) {
+                issue(k, sa0, sb0);
+                wait_vm<0>();
+            } else {
+                load_regs(k);
+                store_regs(sa0, sb0);
+            }
+            stage_barrier();
+            compute(sa0, sb0);
+        }
+    } else if constexpr (!DMA) {
+        // ablation: the three-buffer pipeline with register-staged copies:
+        // stage k+2 is loaded while stage k is multiplied and stored after it,
+        // into the buffer stage k-1 used (read by every wave before this
+        // step's barrier)
+        load_regs(0);
+        store_regs(sa0, sb0);
+        load_regs(min(1, nk - 1));
+        store_regs(sa1, sb1);
+        auto rstep = [&](int k, uint16_t *ca, uint16_t *cb, uint16_t *na, uint16_t *nb) {
+            stage_barrier();
+            load_regs(min(k + 2, nk - 1));
+            compute(ca, cb);
+            store_regs(na, nb);
+        };
+        for (int k = 0;; k += 3) {
+            rstep(k, sa0, sb0, sa2, sb2);
+            if (k + 1 >= nk) break;
+            rstep(k + 1, sa1, sb1, sa0, sb0);
+            if (k + 2 >= nk) break;
+            rstep(k + 2, sa2, sb2, sa1, sb1);
+            if (k + 3 >= nk) break;
+        }
+    } else {
+        issue(0, sa0, sb0);
+        issue(min(1, nk - 1), sa1, sb1);
+        auto step = [&](int k, uint16_t *ca, uint16_t *cb, uint16_t *na, uint16_t *nb) {
+            wait_vm<D>();                      // own copies of stage k landed (k+1 may fly)
+            stage_barrier();                   // everyone's copies of stage k landed; stage k-1 read
+            issue(min(k + 2, nk - 1), na, nb); // into the buffer stage k-1 used
+            compute(ca, cb);
+            __builtin_amdgcn_sched_barrier(0); // keep each step's work inside its step
+        };
+        // the loop may leave after any step (uniform test): the accumulators then
+        // stay in the same registers from one step to the next
+        for (int k = 0;; k += 3) {
+            step(k, sa0, sb0, sa2, sb2);
+            if (k + 1 >= nk) break;
+            step(k + 1, sa1, sb1, sa0, sb0);
+            if (k + 2 >= nk) break;
+            step(k + 2, sa2, sb2, sa1, sb1);
+            if (k + 3 >= nk) break;
+        }
     }
     wait_vm<0>();                          // no copy may still be writing LDS at the end
 
@@ -171,8 +246,8 @@ __global__ __launch_bounds__(256) void gemm_mfma_dma_kernel(
     }
 }
 
-template <int MB, int NB, int WM>
-hipError_t launch_dma_tile(const MfmaGemmArgs &a, hipStream_t s)
+template <int MB, int NB, int WM, int ABL>
+hipError_t launch_dma_variant(const MfmaGemmArgs &a, hipStream_t s)
 {
     const int tiles_m = (a.Cout + MB - 1) / MB;
     const int64_t ncols = int64_t(a.rows) * a.Wo;
@@ -181,14 +256,30 @@ hipError_t launch_dma_tile(const MfmaGemmArgs &a, hipStream_t s)
     const auto *win = static_cast<const uint16_t *>(a.win);
     const auto *wst = static_cast<const uint16_t *>(a.wst);
     if (a.bf16)
-        hipLaunchKernelGGL((gemm_mfma_dma_kernel<MB, NB, WM, true>), grid, dim3(256), 0, s, win, wst,
+        hipLaunchKernelGGL((gemm_mfma_dma_kernel<MB, NB, WM, true, ABL>), grid, dim3(256), 0, s, win, wst,
                            a.y, a.rows, a.row0, a.row_elems, a.col_step, a.kstage, a.Ho, a.Wo,
                            a.Cout, tiles_m);
     else
-        hipLaunchKernelGGL((gemm_mfma_dma_kernel<MB, NB, WM, false>), grid, dim3(256), 0, s, win,
+        hipLaunchKernelGGL((gemm_mfma_dma_kernel<MB, NB, WM, false, ABL>), grid, dim3(256), 0, s, win,
                            wst, a.y, a.rows, a.row0, a.row_elems, a.col_step, a.kstage, a.Ho, a.Wo,
                            a.Cout, tiles_m);
     return hipGetLastError();
+}
+
+template <int MB, int NB, int WM>
+hipError_t launch_dma_tile(const MfmaGemmArgs &a, hipStream_t s)
+{
+    switch (a.ablate) {
+    case 0: return launch_dma_variant<MB, NB, WM, 0>(a, s);
+    case 1: return launch_dma_variant<MB, NB, WM, 1>(a, s);
+    case 2: return launch_dma_variant<MB, NB, WM, 2>(a, s);
+    case 3: return launch_dma_variant<MB, NB, WM, 3>(a, s);
+    case 4: return launch_dma_variant<MB, NB, WM, 4>(a, s);
+    case 5: return launch_dma_variant<MB, NB, WM, 5>(a, s);
+    case 6: return launch_dma_variant<MB, NB, WM, 6>(a, s);
+    case 7: return launch_dma_variant<MB, NB, WM, 7>(a, s);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace

@@ -62,6 +62,7 @@ struct MfmaGemmArgs {
     int kb, ks;             // K per wave group per LDS stage; wave groups splitting K
     int wm;                 // waves along M in a wave group (4 / wm along N)
     int bf16;               // 0: fp16, 1: bf16
+    int ablate;             // direct-to-LDS kernel: ablation bits (0: as planned)
 };
 hipError_t launch_gemm_mfma(const MfmaGemmArgs &a, hipStream_t s);
 // filter-resident form: a 64-row filter block stays in LDS for the whole K,

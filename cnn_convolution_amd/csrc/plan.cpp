@@ -211,6 +211,18 @@ static void pick_mfma_dma(const conv2d_desc_t &d, int64_t krun, int64_t cols, co
     p->gemm_kslice = 64;
     p->gemm_ksplit = 1;
     p->gemm_wave_m = wm;
+    // IM2WIN_ABLATE: a comma list of "serpentine", "dma", "buffers", each
+    // turning one of the page's optimisations off in this kernel (the
+    // ablation of "Enabling Memory-efficient Im2win Convolution ...",
+    // Sec. IV-E, Fig. 4, of the optimisations of Sec. III-E); for
+    // measurements only
+    if (const char *e = std::getenv("IM2WIN_ABLATE")) {
+        int bits = 0;
+        if (std::strstr(e, "serpentine")) bits |= 1;
+        if (std::strstr(e, "dma")) bits |= 2;
+        if (std::strstr(e, "buffers")) bits |= 4;
+        p->gemm_ablate = bits;
+    }
 }
 
 // What conv2d_fwd runs for a matrix-core layer. The implicit form (window

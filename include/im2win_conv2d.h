@@ -129,6 +129,13 @@ typedef struct {
     int32_t algo;                 /* what conv2d_fwd runs: 0 the window tensor in ws
                                      (pack + window-GEMM per chunk), 1 the implicit
                                      form (conv2d_fwd_implicit)                     */
+    int32_t gemm_ablate;          /* gemm_kernel 3 only, for measuring the page's
+                                     optimisations one by one (0 as planned; set
+                                     from IM2WIN_ABLATE): bit 0 no serpentine tile
+                                     order, bit 1 no direct-to-LDS copies (through
+                                     registers), bit 2 one stage buffer instead of
+                                     three                                          */
+    int32_t reserved2;            /* 0                                              */
     int64_t flops;                /* 2*N*Cout*Ho*Wo*Cin*KH*KW (padded taps included) */
 } conv2d_plan_t;
 

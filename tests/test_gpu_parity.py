@@ -281,6 +281,34 @@ def test_dma_form_matches_oracle(shape, dt, tile, monkeypatch):
     assert err <= TOL[dt], f"rel L2 {err:.3e} > {TOL[dt]}"
 
 
+ABLATE = ["serpentine", "dma", "buffers", "serpentine,dma", "dma,buffers", "serpentine,dma,buffers"]
+
+
+@pytest.mark.parametrize("ablate", ABLATE)
+@pytest.mark.parametrize("tile", ["64,128,1", "128,64,2"])
+@pytest.mark.parametrize("shape", [DMA_SHAPES[0], DMA_SHAPES[2], DMA_SHAPES[4], DMA_SHAPES[5]])
+def test_dma_form_ablations_match_oracle(shape, tile, ablate, monkeypatch):
+    """The direct-to-LDS window-GEMM with the page's optimisations turned off
+    (plain tile order, copies through registers, one stage buffer) computes
+    the same sums in the same order: bit-equal to the planned kernel, and
+    within tolerance of the oracle."""
+    monkeypatch.setenv("IM2WIN_ALGO", "window")
+    monkeypatch.setenv("IM2WIN_MFMA_DMA_TILE", tile)
+    N, Cin, H, W, Cout, KH, KW, s, p = shape
+    d = conv.describe((N, Cin, H, W), (Cout, Cin, KH, KW), s, p, conv.F16)
+    x, w = workloads.make_inputs(N, Cin, H, W, Cout, KH, KW, seed=sum(shape) + 12, dtype="f16",
+                                 w_dist="normal")
+    assert conv.plan(d).gemm_kernel == 3 and conv.plan(d).gemm_ablate == 0
+    base = run_conv(x, w, s, p)
+    monkeypatch.setenv("IM2WIN_ABLATE", ablate)
+    bits = sum(b for k, b in (("serpentine", 1), ("dma", 2), ("buffers", 4)) if k in ablate)
+    assert conv.plan(d).gemm_ablate == bits
+    _say(f"conv-dma-ablate {ablate} {tile} {shape}")
+    y = run_conv(x, w, s, p)
+    assert torch.equal(y, base)
+    assert rel_l2(y.numpy(), oracle.conv2d(x, w, s, p)) <= TOL["f16"]
+
+
 @pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
 @pytest.mark.parametrize("shape", [(2, 3, 32, 32, 16, 3, 3, 1, 1), (2, 32, 15, 14, 72, 3, 3, 2, 1),
                                    (1, 3, 30, 30, 64, 7, 7, 2, 3), (2, 64, 8, 8, 128, 1, 1, 1, 0),
