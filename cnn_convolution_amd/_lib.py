@@ -66,7 +66,7 @@ _IMPLICIT_PLAN_FIELDS = [
     ("tile_m", ctypes.c_int32), ("tile_n", ctypes.c_int32), ("wave_m", ctypes.c_int32),
     ("rows_per_tile", ctypes.c_int32), ("cols_per_tile", ctypes.c_int32),
     ("patch_rows", ctypes.c_int32), ("patch_cols", ctypes.c_int32), ("kernel", ctypes.c_int32),
-    ("stages", ctypes.c_int32), ("reserved", ctypes.c_int32),
+    ("stages", ctypes.c_int32), ("images", ctypes.c_int32),
     ("lds_bytes", ctypes.c_int64), ("tiles", ctypes.c_int64), ("Ho", ctypes.c_int64),
     ("Wo", ctypes.c_int64), ("K_stage", ctypes.c_int64), ("ws_bytes", ctypes.c_int64),
     ("flops", ctypes.c_int64),
@@ -77,7 +77,7 @@ class ImplicitPlan(ctypes.Structure):
     _fields_ = _IMPLICIT_PLAN_FIELDS
 
     def as_dict(self):
-        return {name: getattr(self, name) for name, _ in _IMPLICIT_PLAN_FIELDS if name != "reserved"}
+        return {name: getattr(self, name) for name, _ in _IMPLICIT_PLAN_FIELDS}
 
 
 class Profile(ctypes.Structure):

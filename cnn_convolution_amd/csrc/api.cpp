@@ -171,6 +171,7 @@ ImplicitArgs implicit_args(const conv2d_desc_t &d, const conv2d_implicit_plan_t 
     // filter-stationary form: workgroups per 64-row filter block; pipelined
     // row-block form: the persistent workgroups
     a.fs_groups = p.kernel == 4 ? int(p.tiles) : int(p.tiles / ((d.Cout + 63) / 64));
+    a.images = p.kernel == 4 ? p.images : 0;
     return a;
 }
 

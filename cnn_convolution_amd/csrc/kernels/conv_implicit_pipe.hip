@@ -57,9 +57,12 @@ struct PipeKArgs {
     int row_groups;     // ceil(Ho / RW)
     int co_blocks;      // ceil(Cout / 64)
     int IW;             // W + 2*pad
-    int ntasks;         // co_blocks * N * row_groups
-    int SLmax;          // RW + KH - 1
+    int ntasks;         // co_blocks * N * row_groups, or co_blocks * ceil(N / IMG)
+    int SLmax;          // patch rows: RW + KH - 1, or IMG * (Ho + KH - 1)
     int slot_halves;    // one LDS slot: filter block + SLmax * IW * 32
+    int N;
+    int IMG;            // 1: tasks of RW output rows of one image; > 1: tasks of
+                        // IMG whole images (RW = Ho), their patches stacked
 };
 
 // LDS slot of 16-byte granule g (0..3) of 64-byte row q. A 16-byte LDS read
@@ -111,20 +114,33 @@ __device__ __forceinline__ uint4 position_of(const PlaneVec<V> *raw, int j)
     }
 }
 
+// A task: 64 output channels (block cb) of rw output rows from ho0 of nimg
+// consecutive images from n (nimg > 1 only for whole images); image j's
+// patch is rows j*SL .. j*SL + SL - 1 of the task's patch.
 struct PipeTask {
-    int cb, n, ho0, rw, ih0, SL;
+    int cb, n, nimg, ho0, rw, ih0, SL;
 };
 
-template <int KH>
+// MI: the launch takes tasks of several whole images (a.IMG > 1); the
+// kernels are compiled apart for it, so that row tasks pay nothing for it
+template <int KH, bool MI>
 __device__ __forceinline__ PipeTask pipe_task(const PipeKArgs &a, int t)
 {
     PipeTask k;
     k.cb = t % a.co_blocks;
     const int r = t / a.co_blocks;
-    const int rg = r % a.row_groups;
-    k.n = r / a.row_groups;
-    k.ho0 = rg * a.RW;
-    k.rw = min(a.RW, a.Ho - k.ho0);
+    if constexpr (MI) {
+        k.n = r * a.IMG;
+        k.nimg = min(a.IMG, a.N - k.n);
+        k.ho0 = 0;
+        k.rw = a.Ho;
+    } else {
+        const int rg = r % a.row_groups;
+        k.n = r / a.row_groups;
+        k.nimg = 1;
+        k.ho0 = rg * a.RW;
+        k.rw = min(a.RW, a.Ho - k.ho0);
+    }
     k.ih0 = k.ho0 - a.pad;
     k.SL = k.rw + KH - 1;
     return k;
@@ -132,12 +148,13 @@ __device__ __forceinline__ PipeTask pipe_task(const PipeKArgs &a, int t)
 
 // Patch loads of one K chunk of a task: the task's input rows that lie in
 // the image are a contiguous run [p_lo, p_hi) of every channel plane; unit u
-// is (8-channel granule u & 3, V positions from flat index (j_lo + u/4) * V).
+// is (image u / units1 of the task, then 8-channel granule u1 & 3 and V
+// positions from flat index (j_lo + u1/4) * V, u1 = u mod units1).
 struct ChunkGeom {
-    int p_lo, p_hi, j_lo, units;
+    int p_lo, p_hi, j_lo, units1, units;
 };
 
-template <int V>
+template <int V, bool MI>
 __device__ __forceinline__ ChunkGeom chunk_geom(const PipeKArgs &a, const PipeTask &tk)
 {
     ChunkGeom g;
@@ -145,35 +162,40 @@ __device__ __forceinline__ ChunkGeom chunk_geom(const PipeKArgs &a, const PipeTa
     g.p_lo = r_lo * a.W;
     g.p_hi = max(r_hi, r_lo) * a.W;
     g.j_lo = g.p_lo / V;
-    g.units = 4 * ((g.p_hi + V - 1) / V - g.j_lo);
+    g.units1 = 4 * ((g.p_hi + V - 1) / V - g.j_lo);
+    g.units = MI ? g.units1 * tk.nimg : g.units1;
     return g;
 }
 
-template <int V>
+template <int V, bool MI>
 __device__ __forceinline__ void load_patch_unit(const PipeKArgs &a, const PipeTask &tk, int blk,
                                                 const ChunkGeom &cg, int u, PlaneVec<V> *raw)
 {
     const int HW = a.H * a.W;
-    const int g = u & 3, j = cg.j_lo + (u >> 2);
-    const uint16_t *src = a.x + (int64_t(tk.n) * a.Cin + blk * kChunkC + g * 8) * HW + int64_t(j) * V;
+    const int im = MI ? u / cg.units1 : 0, u1 = u - im * cg.units1;
+    const int g = u1 & 3, j = cg.j_lo + (u1 >> 2);
+    const uint16_t *src =
+        a.x + (int64_t(tk.n + im) * a.Cin + blk * kChunkC + g * 8) * HW + int64_t(j) * V;
 #pragma unroll
     for (int e = 0; e < 8; ++e) raw[e].load(src + int64_t(e) * HW);
 }
 
 // the unit's positions inside [p_lo, p_hi), 8 channels each, into the patch
-template <int V>
+template <int V, bool MI>
 __device__ __forceinline__ void put_patch_unit(uint16_t *patch, const PipeKArgs &a, const PipeTask &tk,
                                                const ChunkGeom &cg, int u, const PlaneVec<V> *raw)
 {
-    const int g = u & 3;
-    const int p0 = (cg.j_lo + (u >> 2)) * V;
+    const int im = MI ? u / cg.units1 : 0, u1 = u - im * cg.units1;
+    const int g = u1 & 3;
+    const int p0 = (cg.j_lo + (u1 >> 2)) * V;
+    const int row0 = im * tk.SL - tk.ih0;            // patch row of input row 0 of this image
     int r = p0 / a.W;
     int col = p0 - r * a.W;
 #pragma unroll
     for (int v = 0; v < V; ++v) {
         const int p = p0 + v;
         if (p >= cg.p_lo && p < cg.p_hi) {
-            const int q = (r - tk.ih0) * a.IW + a.pad + col;
+            const int q = (row0 + r) * a.IW + a.pad + col;
             *reinterpret_cast<uint4 *>(patch + q * kChunkC + (gslot(g, q) << 3)) = position_of<V>(raw, v);
         }
         if (++col == a.W) { col = 0; ++r; }
@@ -213,18 +235,64 @@ __device__ __forceinline__ void put_filter_unit(uint16_t *fl, int co_l, int fg, 
     }
 }
 
-// rows of the task outside the image: zeros (thread t0 of nt)
+// rows of the task outside the image: zeros, in every image's patch (thread
+// t0 of nt)
+template <bool MI>
 __device__ __forceinline__ void zero_rows(uint16_t *patch, const PipeKArgs &a, const PipeTask &tk, int t0, int nt)
 {
     const int top = min(max(-tk.ih0, 0), tk.SL);
     const int bot0 = max(min(a.H - tk.ih0, tk.SL), top);
     const int zrows = top + (tk.SL - bot0);
-    for (int v = t0; v < zrows * a.IW * 4; v += nt) {
-        const int g = v & 3, e = v >> 2;
+    const int per = zrows * a.IW * 4;
+    for (int v = t0; v < (MI ? per * tk.nimg : per); v += nt) {
+        const int im = MI ? v / per : 0, w = v - im * per;
+        const int g = w & 3, e = w >> 2;
         const int zr = e / a.IW, col = e - zr * a.IW;
         const int i = zr < top ? zr : bot0 + (zr - top);
-        const int q = i * a.IW + col;
+        const int q = (im * tk.SL + i) * a.IW + col;
         *reinterpret_cast<uint4 *>(patch + q * kChunkC + (gslot(g, q) << 3)) = uint4{0u, 0u, 0u, 0u};
+    }
+}
+
+// Patch position of the window at tap (0, 0) of each of a lane's output
+// blocks: output m of the task is image m / opi, row and column of the rest
+// (opi = rw * Wo outputs per image), at patch row im * SL + i.
+template <bool MI>
+__device__ __forceinline__ void task_bases(int *qa, int b0, int lane, int outs, int Wo, int IW, int opi, int SL)
+{
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        const int m = min((b0 + s) * 16 + (lane & 15), outs - 1);
+        const int im = MI ? m / opi : 0, rem = m - im * opi;
+        const int i = rem / Wo;
+        qa[s] = (im * SL + i) * IW + (rem - i * Wo);
+    }
+}
+
+// Stores of a task of several whole images through the wave's LDS scratch
+// (as store_blocks_lds): lane l stores output m = 16*b0 + l of each channel
+// row, at its image's plane.
+template <int MAXB>
+__device__ __forceinline__ void store_blocks_images(const floatx4_t (*acc)[4], int nb, int b0, int lane,
+                                                   float *scratch, float *y, int n, int Cout, int cb,
+                                                   int plane, int outs)
+{
+    const int nout = min(nb * 16, outs - b0 * 16);
+    const int m = b0 * 16 + lane;
+    const int im = m / plane;
+    float *const yb = y + (int64_t(n + im) * Cout + cb * 64) * plane + (m - im * plane);
+    float *const srow = scratch + (lane & 15) * kStoreRow + 4 * (lane >> 4);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+#pragma unroll
+        for (int s = 0; s < MAXB; ++s)
+            if (s < nb) *reinterpret_cast<floatx4_t *>(srow + s * 16) = acc[s][c];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int co = cb * 64 + c * 16 + r;
+            const float v = scratch[r * kStoreRow + lane];
+            if (co < Cout && lane < nout) yb[int64_t(c * 16 + r) * plane] = v;
+        }
     }
 }
 
@@ -331,7 +399,7 @@ __device__ __forceinline__ int xcd_logical(int b, int G)
     return x * per + min(x, rem) + (b >> 3);
 }
 
-template <int KH, int KW, bool BF16, int V>
+template <int KH, int KW, bool BF16, int V, bool MI>
 __global__ __launch_bounds__(kPipeThreads) void conv_implicit_pipe_kernel(const PipeKArgs a)
 {
     constexpr int TAPS = KH * KW;
@@ -359,34 +427,34 @@ __global__ __launch_bounds__(kPipeThreads) void conv_implicit_pipe_kernel(const 
         uint4 wraw[TAPS];
         PlaneVec<V> praw[kUnitsHeld][8];
         auto fetch = [&](int c) {
-            const PipeTask tk = pipe_task<KH>(a, L + (c / nch) * G);
+            const PipeTask tk = pipe_task<KH, MI>(a, L + (c / nch) * G);
             const int blk = c - (c / nch) * nch;
-            const ChunkGeom cg = chunk_geom<V>(a, tk);
+            const ChunkGeom cg = chunk_geom<V, MI>(a, tk);
             load_filter_unit<TAPS>(a, tk, blk, co_l, fg, wraw);
 #pragma unroll
             for (int k = 0; k < kUnitsHeld; ++k) {
                 const int u = lt + k * kLoaderThreads;
-                if (u < cg.units) load_patch_unit<V>(a, tk, blk, cg, u, praw[k]);
+                if (u < cg.units) load_patch_unit<V, MI>(a, tk, blk, cg, u, praw[k]);
             }
         };
         auto put = [&](int c) {
-            const PipeTask tk = pipe_task<KH>(a, L + (c / nch) * G);
+            const PipeTask tk = pipe_task<KH, MI>(a, L + (c / nch) * G);
             const int blk = c - (c / nch) * nch;
-            const ChunkGeom cg = chunk_geom<V>(a, tk);
+            const ChunkGeom cg = chunk_geom<V, MI>(a, tk);
             uint16_t *const fl = lds + (c & 1) * a.slot_halves;
             uint16_t *const patch = fl + FILT;
             put_filter_unit<TAPS>(fl, co_l, fg, wraw);
 #pragma unroll
             for (int k = 0; k < kUnitsHeld; ++k) {
                 const int u = lt + k * kLoaderThreads;
-                if (u < cg.units) put_patch_unit<V>(patch, a, tk, cg, u, praw[k]);
+                if (u < cg.units) put_patch_unit<V, MI>(patch, a, tk, cg, u, praw[k]);
             }
             for (int u = lt + kUnitsHeld * kLoaderThreads; u < cg.units; u += kLoaderThreads) {
                 PlaneVec<V> raw[8];
-                load_patch_unit<V>(a, tk, blk, cg, u, raw);
-                put_patch_unit<V>(patch, a, tk, cg, u, raw);
+                load_patch_unit<V, MI>(a, tk, blk, cg, u, raw);
+                put_patch_unit<V, MI>(patch, a, tk, cg, u, raw);
             }
-            zero_rows(patch, a, tk, lt, kLoaderThreads);
+            zero_rows<MI>(patch, a, tk, lt, kLoaderThreads);
         };
         if (total > 0) {
             fetch(0);
@@ -415,15 +483,18 @@ __global__ __launch_bounds__(kPipeThreads) void conv_implicit_pipe_kernel(const 
         for (int c = 0; c < total; ++c) {
             const int blk = c - (c / nch) * nch;
             if (blk == 0) {
-                tk = pipe_task<KH>(a, L + (c / nch) * G);
-                outs = tk.rw * a.Wo;
+                tk = pipe_task<KH, MI>(a, L + (c / nch) * G);
+                outs = tk.nimg * tk.rw * a.Wo;
                 wave_blocks_of(wave, kComputeWaves, outs, b0, nb);
-                block_bases(qa, b0, lane, outs, a.Wo, a.IW);
+                task_bases<MI>(qa, b0, lane, outs, a.Wo, a.IW, tk.rw * a.Wo, tk.SL);
             }
             contract_blocks<KH, KW, BF16, true>(acc, nb, qa, lds + (c & 1) * a.slot_halves, a.IW, lane);
             if (blk == nch - 1) {
                 if (nb > 0) {
-                    if ((a.Wo & 3) == 0)
+                    if (MI)
+                        store_blocks_images<4>(acc, nb, b0, lane, scratch + wave * kStoreScratchFloats, a.y,
+                                               tk.n, a.Cout, tk.cb, a.Ho * a.Wo, outs);
+                    else if ((a.Wo & 3) == 0)
                         store_blocks(acc, nb, b0, lane, a.y, tk.n, a.Cout, tk.cb, a.Ho, a.Wo, tk.ho0, outs);
                     else
                         store_blocks_lds(acc, nb, b0, lane, scratch + wave * kStoreScratchFloats, a.y, tk.n,
@@ -444,7 +515,7 @@ __global__ __launch_bounds__(kPipeThreads) void conv_implicit_pipe_kernel(const 
 // and stores overlap the other's contraction. All eight waves load a chunk
 // (filter block by the first four, patch units by all), then all eight
 // contract it (up to two 16-output blocks each, R * Wo <= 256).
-template <int KH, int KW, bool BF16, int V>
+template <int KH, int KW, bool BF16, int V, bool MI>
 __global__ __launch_bounds__(kPipeThreads) __attribute__((amdgpu_waves_per_eu(4))) void conv_implicit_pair_kernel(const PipeKArgs a)
 {
     constexpr int TAPS = KH * KW;
@@ -454,18 +525,18 @@ __global__ __launch_bounds__(kPipeThreads) __attribute__((amdgpu_waves_per_eu(4)
     uint16_t *const patch = lds + FILT;
 
     const int tid = threadIdx.x;
-    const PipeTask tk = pipe_task<KH>(a, xcd_logical(blockIdx.x, gridDim.x));
+    const PipeTask tk = pipe_task<KH, MI>(a, xcd_logical(blockIdx.x, gridDim.x));
     const int nch = a.Cin / kChunkC;
-    const ChunkGeom cg = chunk_geom<V>(a, tk);
-    zero_pad_columns(patch, a, tk.SL, tid, kPipeThreads);
+    const ChunkGeom cg = chunk_geom<V, MI>(a, tk);
+    zero_pad_columns(patch, a, tk.SL * tk.nimg, tid, kPipeThreads);
 
     const int wave = tid >> 6;
     const int lane = tid & 63;
-    const int outs = tk.rw * a.Wo;
+    const int outs = tk.nimg * tk.rw * a.Wo;
     int b0, nb;
     wave_blocks(wave, outs, b0, nb);
     int qa[4];
-    block_bases(qa, b0, lane, outs, a.Wo, a.IW);
+    task_bases<MI>(qa, b0, lane, outs, a.Wo, a.IW, tk.rw * a.Wo, tk.SL);
     constexpr int MAXB = 2;                          // R * Wo <= 256: at most 2 blocks per wave
     floatx4_t acc[MAXB][4];
 #pragma unroll
@@ -484,15 +555,20 @@ __global__ __launch_bounds__(kPipeThreads) __attribute__((amdgpu_waves_per_eu(4)
         asm volatile("" ::: "memory");
         for (int u = tid; u < cg.units; u += kPipeThreads) {
             PlaneVec<V> raw[8];
-            load_patch_unit<V>(a, tk, blk, cg, u, raw);
-            put_patch_unit<V>(patch, a, tk, cg, u, raw);
+            load_patch_unit<V, MI>(a, tk, blk, cg, u, raw);
+            put_patch_unit<V, MI>(patch, a, tk, cg, u, raw);
         }
-        zero_rows(patch, a, tk, tid, kPipeThreads);
+        zero_rows<MI>(patch, a, tk, tid, kPipeThreads);
         __syncthreads();
         contract_blocks<KH, KW, BF16, false, MAXB>(acc, nb, qa, fl, a.IW, lane);
     }
-    if ((a.Wo & 3) == 0) {
+    if ((a.Wo & 3) == 0 && !MI) {
         if (nb > 0) store_blocks<MAXB>(acc, nb, b0, lane, a.y, tk.n, a.Cout, tk.cb, a.Ho, a.Wo, tk.ho0, outs);
+    } else if (MI) {
+        __syncthreads();                             // the chunk is dead: LDS is store scratch
+        if (nb > 0)
+            store_blocks_images<MAXB>(acc, nb, b0, lane, reinterpret_cast<float *>(lds) + wave * kStoreScratchFloats,
+                                      a.y, tk.n, a.Cout, tk.cb, a.Ho * a.Wo, outs);
     } else {
         __syncthreads();                             // the chunk is dead: LDS is store scratch
         if (nb > 0)
@@ -508,9 +584,11 @@ hipError_t launch_conv_implicit_pipe(const ImplicitArgs &h, hipStream_t s)
     // stages: 2 for the pipelined form (two LDS slots, persistent workgroups),
     // 1 for the paired form (one slot, one task per workgroup)
     const bool pair = h.stages == 1;
+    const int img = std::max(h.images, 1);
     if (h.f32 || h.Cin % kChunkC != 0 || h.stride != 1 || h.W < 1 || h.H < 1 || h.Wo < 1 || h.Ho < 1 ||
-        h.R < 1 || int64_t(h.R) * h.Wo > 256 || h.IW != h.W + 2 * h.pad ||
-        h.IR != h.R + h.KH - 1 || int64_t(h.Cin) * h.H * h.W >= (int64_t(1) << 31) ||
+        h.R < 1 || int64_t(img) * h.R * h.Wo > 256 || h.IW != h.W + 2 * h.pad ||
+        h.IR != img * (h.R + h.KH - 1) || (img > 1 && h.R != h.Ho) ||
+        int64_t(h.Cin) * h.H * h.W >= (int64_t(1) << 31) ||
         (!pair && h.fs_groups < 1) || (h.stages != 1 && h.stages != 2) ||
         !((h.KH == 3 && h.KW == 3) || (h.KH == 1 && h.KW == 1)))
         return hipErrorInvalidValue;
@@ -529,7 +607,10 @@ hipError_t launch_conv_implicit_pipe(const ImplicitArgs &h, hipStream_t s)
     a.row_groups = (h.Ho + h.R - 1) / h.R;
     a.co_blocks = (h.Cout + 63) / 64;
     a.IW = h.IW;
-    const int64_t ntasks = int64_t(a.co_blocks) * h.N * a.row_groups;
+    a.N = h.N;
+    a.IMG = img;
+    const int64_t ntasks = img > 1 ? int64_t(a.co_blocks) * ((h.N + img - 1) / img)
+                                   : int64_t(a.co_blocks) * h.N * a.row_groups;
     if (ntasks > 0x7fffffff) return hipErrorInvalidValue;
     a.ntasks = int(ntasks);
     a.SLmax = h.IR;
@@ -541,18 +622,18 @@ hipError_t launch_conv_implicit_pipe(const ImplicitArgs &h, hipStream_t s)
     const int hw = h.H * h.W;
     void *args[] = {&a};
     const bool k3 = h.KH == 3;
-#define IM2WIN_PIPE_PICK(K, V)                                                                               \
-    (k3 ? (h.bf16 ? reinterpret_cast<const void *>(K<3, 3, true, V>)                                         \
-                  : reinterpret_cast<const void *>(K<3, 3, false, V>))                                       \
-        : (h.bf16 ? reinterpret_cast<const void *>(K<1, 1, true, V>)                                         \
-                  : reinterpret_cast<const void *>(K<1, 1, false, V>)))
-    const void *kern =
-        pair ? (hw % 8 == 0   ? IM2WIN_PIPE_PICK(conv_implicit_pair_kernel, 8)
-                : hw % 4 == 0 ? IM2WIN_PIPE_PICK(conv_implicit_pair_kernel, 4)
-                              : IM2WIN_PIPE_PICK(conv_implicit_pair_kernel, 1))
-             : (hw % 8 == 0   ? IM2WIN_PIPE_PICK(conv_implicit_pipe_kernel, 8)
-                : hw % 4 == 0 ? IM2WIN_PIPE_PICK(conv_implicit_pipe_kernel, 4)
-                              : IM2WIN_PIPE_PICK(conv_implicit_pipe_kernel, 1));
+#define IM2WIN_PIPE_PICK(K, V, M)                                                                            \
+    (k3 ? (h.bf16 ? reinterpret_cast<const void *>(K<3, 3, true, V, M>)                                      \
+                  : reinterpret_cast<const void *>(K<3, 3, false, V, M>))                                    \
+        : (h.bf16 ? reinterpret_cast<const void *>(K<1, 1, true, V, M>)                                      \
+                  : reinterpret_cast<const void *>(K<1, 1, false, V, M>)))
+#define IM2WIN_PIPE_FORM(K, M)                                                                               \
+    (hw % 8 == 0 ? IM2WIN_PIPE_PICK(K, 8, M) : hw % 4 == 0 ? IM2WIN_PIPE_PICK(K, 4, M) : IM2WIN_PIPE_PICK(K, 1, M))
+    const void *kern = pair ? (img > 1 ? IM2WIN_PIPE_FORM(conv_implicit_pair_kernel, true)
+                                       : IM2WIN_PIPE_FORM(conv_implicit_pair_kernel, false))
+                            : (img > 1 ? IM2WIN_PIPE_FORM(conv_implicit_pipe_kernel, true)
+                                       : IM2WIN_PIPE_FORM(conv_implicit_pipe_kernel, false));
+#undef IM2WIN_PIPE_FORM
 #undef IM2WIN_PIPE_PICK
     return hipLaunchKernel(kern, dim3(groups), dim3(kPipeThreads), args, lds, s);
 }

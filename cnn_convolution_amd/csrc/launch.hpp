@@ -89,6 +89,7 @@ struct ImplicitArgs {
     int f32;                // fp32 x, w (row-block and narrow kernels)
     int narrow_cp;          // narrow kernel: channels per window position (4 or 8)
     int fs_groups;          // filter-stationary form: workgroups per 64-row filter block
+    int images;             // pipelined row-block form: whole images per task (0 or 1: row tasks)
 };
 hipError_t launch_conv_implicit(const ImplicitArgs &a, hipStream_t s);
 // filter-stationary form (K = KW*KH*Cin of 64, 128, 256 or 576): a 64-row

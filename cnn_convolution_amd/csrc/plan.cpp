@@ -1,11 +1,16 @@
 // Host planner: see plan.hpp.
 #include "plan.hpp"
 
+#include <unistd.h>
+
 #include <algorithm>
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
+#include <string>
+#include <unordered_map>
 
 namespace im2win {
 
@@ -276,7 +281,7 @@ static int pick_valu_ksplit(const conv2d_desc_t &d, int64_t rows, int64_t Wo, in
     return 1;
 }
 
-conv2d_status_t make_plan(const conv2d_desc_t &d, conv2d_plan_t *p) {
+static conv2d_status_t compute_plan(const conv2d_desc_t &d, conv2d_plan_t *p) {
     const conv2d_status_t st = check_desc(d);
     if (st != CONV2D_OK) return st;
     std::memset(p, 0, sizeof(*p));
@@ -461,6 +466,29 @@ static void pick_implicit_rows(const conv2d_desc_t &d, int64_t Ho, int64_t Wo, c
     p->ws_bytes = 0;    // the kernel reads w as it is stored
 }
 
+// Whole images per task for the pipelined row-block kernels where images are
+// small (fewer than 128 outputs, so a task of one image would leave waves
+// idle): the most images (at most 256 outputs, the patches within the LDS
+// limit) that still leave min_tasks tasks; 1 where even two do not.
+// IM2WIN_IMPLICIT_IMAGES sets it.
+static int64_t pick_images(const conv2d_desc_t &d, int64_t Ho, int64_t Wo, int64_t min_tasks, bool pair) {
+    const int64_t taps = d.KH * d.KW, iw = d.W + 2 * d.pad, sl = Ho + d.KH - 1;
+    const int64_t co_blocks = ceil_div(d.Cout, 64);
+    auto fits = [&](int64_t img) {
+        const int64_t lds = pair ? pair_lds_bytes(taps, img * sl, iw) : pipe_lds_bytes(taps, img * sl, iw);
+        return img * Ho * Wo <= 256 && img <= d.N && lds <= (pair ? kImplicitPairLdsBytes : kImplicitMaxLdsBytes);
+    };
+    int64_t best = 1;
+    if (Ho * Wo < 128)
+        for (int64_t img = 2; fits(img); ++img)
+            if (co_blocks * ceil_div(d.N, img) >= min_tasks) best = img;
+    if (const char *e = std::getenv("IM2WIN_IMPLICIT_IMAGES")) {
+        const int64_t v = std::atoi(e);
+        if (v >= 1 && (v == 1 || fits(v))) best = v;
+    }
+    return best;
+}
+
 // Pipelined row-block implicit kernel: fp16/bf16, Cin % 32 == 0, stride 1,
 // 3x3 or 1x1, Wo <= 256. Tasks of RW whole output rows x 64 output channels
 // (RW * Wo <= 256: four computing waves of at most four 16-output blocks),
@@ -509,15 +537,21 @@ static void pick_implicit_pipe(const conv2d_desc_t &d, int64_t Ho, int64_t Wo, c
             best_groups = std::min<int64_t>(co_blocks * d.N * ceil_div(Ho, v), 256);
         }
     }
+    const int64_t img = pick_images(d, Ho, Wo, 256, false);
+    if (img > 1) {
+        best_rw = Ho;
+        best_groups = std::min<int64_t>(co_blocks * ceil_div(d.N, img), 256);
+    }
     p->kernel = 4;
     p->tile_m = 64;
     p->tile_n = 64;
     p->wave_m = 1;
     p->rows_per_tile = int32_t(best_rw);
     p->cols_per_tile = int32_t(Wo);
-    p->patch_rows = int32_t(best_rw + d.KH - 1);
+    p->patch_rows = int32_t(img * (best_rw + d.KH - 1));
     p->patch_cols = int32_t(iw);
     p->stages = 2;
+    p->images = int32_t(img);
     p->lds_bytes = pipe_lds_bytes(taps, p->patch_rows, iw);
     p->tiles = best_groups;
     p->ws_bytes = 0;    // the kernel reads w as it is stored
@@ -552,33 +586,38 @@ static void pick_implicit_pair(const conv2d_desc_t &d, int64_t Ho, int64_t Wo, c
     }
     if (best_rw == 0) best_rw = fit_rw;
     if (best_rw == 0) return;
+    best_rw = ceil_div(Ho, ceil_div(Ho, best_rw));   // the same number of tasks, rows spread evenly
     if (const char *e = std::getenv("IM2WIN_IMPLICIT_ROWS")) {
         const int64_t v = std::min<int64_t>(std::atoi(e), Ho);
         if (v >= 1 && v * Wo <= 256 && pair_lds_bytes(taps, v + d.KH - 1, iw) <= kImplicitMaxLdsBytes)
             best_rw = v;
     }
+    const int64_t img = pick_images(d, Ho, Wo, 512, true);
+    if (img > 1) best_rw = Ho;
     p->kernel = 4;
     p->tile_m = 64;
     p->tile_n = 64;
     p->wave_m = 1;
     p->rows_per_tile = int32_t(best_rw);
     p->cols_per_tile = int32_t(Wo);
-    p->patch_rows = int32_t(best_rw + d.KH - 1);
+    p->patch_rows = int32_t(img * (best_rw + d.KH - 1));
     p->patch_cols = int32_t(iw);
     p->stages = 1;
+    p->images = int32_t(img);
     p->lds_bytes = pair_lds_bytes(taps, p->patch_rows, iw);
-    p->tiles = co_blocks * d.N * ceil_div(Ho, best_rw);
+    p->tiles = img > 1 ? co_blocks * ceil_div(d.N, img) : co_blocks * d.N * ceil_div(Ho, best_rw);
     p->ws_bytes = 0;
 }
 
 // The pipelined row-block kernels where they apply by default: the paired
-// form where its tasks of the most rows give at least two per CU or output
-// rows are wider than 64 (the one-slot form keeps its workgroups busy),
-// else the persistent form (its four computing waves take up to four
-// blocks each of a task of up to 256 outputs). Measured on the Table I 3x3
-// layers and the deep 3x3 layer against the row-block kernel over several
-// channel blocks: paired 1.04-1.6x faster on cv8, cv10 and cv11, persistent
-// 1.13x on the 14x14 deep layer (one task per CU).
+// form where its tasks hold at least 128 outputs (every one of its eight
+// waves busy) and number at least 512 (two per CU), else the persistent form
+// (its four computing waves take up to four blocks each of a task of up to
+// 256 outputs, small images several to a task). Measured against the
+// row-block kernel over several channel blocks and the streamed kernel: paired
+// 1.04-1.6x faster on cv6, cv8, cv10 and cv11, persistent 1.13x on the 14x14
+// deep layer (paired tasks of 98 outputs), 1.36x on the 512-channel 7x7 layer
+// and 1.9x on cv12 (several images per task).
 static void pick_implicit_pipelined(const conv2d_desc_t &d, int64_t Ho, int64_t Wo, conv2d_implicit_plan_t *p,
                                     bool dflt) {
     if (!dflt) {
@@ -586,15 +625,19 @@ static void pick_implicit_pipelined(const conv2d_desc_t &d, int64_t Ho, int64_t 
         pick_implicit_pair(d, Ho, Wo, p, false);
         return;
     }
-    const int64_t rmax = std::min<int64_t>(Ho, std::max<int64_t>(1, 256 / Wo));
-    const int64_t tasks = ceil_div(d.Cout, 64) * d.N * ceil_div(Ho, rmax);
-    if (Wo > 64 || tasks >= 512) {
-        pick_implicit_pair(d, Ho, Wo, p, true);
+    if (std::getenv("IM2WIN_IMPLICIT_KERNEL")) {   // a kernel asked for by name
         pick_implicit_pipe(d, Ho, Wo, p, false);
-    } else {
-        pick_implicit_pipe(d, Ho, Wo, p, true);
         pick_implicit_pair(d, Ho, Wo, p, false);
+        return;
     }
+    conv2d_implicit_plan_t pair = *p;
+    pick_implicit_pair(d, Ho, Wo, &pair, true);
+    if (pair.kernel == 4 && pair.tiles >= 512 &&
+        int64_t(pair.images) * pair.rows_per_tile * Wo >= 128) {
+        *p = pair;
+        return;
+    }
+    pick_implicit_pipe(d, Ho, Wo, p, true);
 }
 
 // Narrow-channel implicit kernel: Cin <= 8 (the RGB stem and its kind), any
@@ -662,7 +705,7 @@ static void pick_implicit_narrow(const conv2d_desc_t &d, int64_t Ho, int64_t Wo,
     p->ws_bytes = round_up(d.Cout * Kp * es, 256);
 }
 
-conv2d_status_t make_implicit_plan(const conv2d_desc_t &d, conv2d_implicit_plan_t *p) {
+static conv2d_status_t compute_implicit_plan(const conv2d_desc_t &d, conv2d_implicit_plan_t *p) {
     const conv2d_status_t st = check_desc(d);
     if (st != CONV2D_OK) return st;
     std::memset(p, 0, sizeof(*p));
@@ -762,11 +805,87 @@ conv2d_status_t make_implicit_plan(const conv2d_desc_t &d, conv2d_implicit_plan_
     pick_implicit_rows(d, Ho, Wo, p);
     // the one-block row kernel stays where it applies (64 channels on rows of
     // 8k elements, measured faster than both pipelined forms); elsewhere the
-    // pipelined forms take the stride-1 3x3 and 1x1 layers of at least 128
-    // outputs per image
+    // pipelined forms take the stride-1 3x3 and 1x1 layers
     const bool one_block = p->kernel == 2 && d.Cin == 64 && d.W % 8 == 0;
-    pick_implicit_pipelined(d, Ho, Wo, p, !one_block && Ho * Wo >= 128);
+    pick_implicit_pipelined(d, Ho, Wo, p, !one_block);
     return CONV2D_OK;
+}
+
+// Plans are cached per descriptor and per set of IM2WIN_* overrides in the
+// environment (read on every call, so that a changed override takes effect):
+// planning searches tiles and kernels for tens of microseconds, as long as a
+// small layer's kernel. The cache is bounded and guarded by a mutex, so calls
+// stay reentrant.
+namespace {
+
+std::string plan_key(const conv2d_desc_t &d) {
+    std::string k(reinterpret_cast<const char *>(&d), sizeof(d));
+    for (char **e = environ; e && *e; ++e)
+        if (std::strncmp(*e, "IM2WIN_", 7) == 0) {
+            k += '\n';
+            k += *e;
+        }
+    return k;
+}
+
+struct CachedPlans {
+    bool have_plan = false, have_implicit = false;
+    conv2d_status_t plan_st = CONV2D_OK, implicit_st = CONV2D_OK;
+    conv2d_plan_t plan{};
+    conv2d_implicit_plan_t implicit{};
+};
+
+std::mutex g_plan_mutex;
+std::unordered_map<std::string, CachedPlans> g_plans;
+constexpr size_t kMaxCachedPlans = 1024;
+
+CachedPlans &cached(const std::string &key) {
+    if (g_plans.size() >= kMaxCachedPlans && g_plans.find(key) == g_plans.end()) g_plans.clear();
+    return g_plans[key];
+}
+
+}  // namespace
+
+conv2d_status_t make_plan(const conv2d_desc_t &d, conv2d_plan_t *p) {
+    const std::string key = plan_key(d);
+    {
+        std::lock_guard<std::mutex> lock(g_plan_mutex);
+        const CachedPlans &c = cached(key);
+        if (c.have_plan) {
+            *p = c.plan;
+            return c.plan_st;
+        }
+    }
+    conv2d_plan_t q;
+    const conv2d_status_t st = compute_plan(d, &q);
+    std::lock_guard<std::mutex> lock(g_plan_mutex);
+    CachedPlans &c = cached(key);
+    c.have_plan = true;
+    c.plan_st = st;
+    c.plan = q;
+    *p = q;
+    return st;
+}
+
+conv2d_status_t make_implicit_plan(const conv2d_desc_t &d, conv2d_implicit_plan_t *p) {
+    const std::string key = plan_key(d);
+    {
+        std::lock_guard<std::mutex> lock(g_plan_mutex);
+        const CachedPlans &c = cached(key);
+        if (c.have_implicit) {
+            *p = c.implicit;
+            return c.implicit_st;
+        }
+    }
+    conv2d_implicit_plan_t q;
+    const conv2d_status_t st = compute_implicit_plan(d, &q);
+    std::lock_guard<std::mutex> lock(g_plan_mutex);
+    CachedPlans &c = cached(key);
+    c.have_implicit = true;
+    c.implicit_st = st;
+    c.implicit = q;
+    *p = q;
+    return st;
 }
 
 }  // namespace im2win

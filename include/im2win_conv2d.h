@@ -218,19 +218,22 @@ typedef struct {
                                      and the input rows resident in LDS, no
                                      staged filter (ws_bytes 0); 3: narrow-channel
                                      (Cin <= 8); 4 (default for the other stride-1
-                                     3x3 and 1x1 layers with Cin % 32 == 0, Wo <=
-                                     256 and at least 128 outputs per image):
-                                     pipelined row-block, tasks of rows_per_tile
-                                     whole output rows x 64 output channels over
-                                     32-channel K chunks double-buffered in LDS,
-                                     w as stored (ws_bytes 0)                       */
+                                     3x3 and 1x1 layers with Cin % 32 == 0 and Wo
+                                     <= 256): pipelined row-block, tasks of
+                                     rows_per_tile whole output rows (or of
+                                     `images` whole images) x 64 output channels
+                                     over 32-channel K chunks double-buffered in
+                                     LDS, w as stored (ws_bytes 0)                  */
     int32_t stages;               /* kernel 0: filter K stages in flight + 1 (LDS
                                      stage buffers); kernel 3: channels per window
                                      position; kernel 4: 2 = persistent workgroups
                                      (tiles of them) with loading and computing
                                      waves, 1 = one task per workgroup (tiles
                                      tasks), two workgroups per CU                 */
-    int32_t reserved;
+    int32_t images;               /* kernel 4: whole images per task when > 1 (then
+                                     rows_per_tile = Ho and patch_rows = images *
+                                     (Ho + KH - 1)); 1 otherwise, 0 for the other
+                                     kernels                                        */
     int64_t lds_bytes;            /* LDS per workgroup                              */
     int64_t tiles;                /* workgroups of the launch                       */
     int64_t Ho, Wo;

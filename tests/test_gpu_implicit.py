@@ -211,7 +211,7 @@ def _eligible_configs():
         for dt in cfg.dtypes:
             if (dt != "f32" and cfg.Cin % 64 == 0) or (name, dt) == ("resnet3x3", "f32"):
                 out.append((name, dt))
-    for name in ("cv4", "cv8", "cv10", "cv11", "cv12"):
+    for name in ("cv4", "cv6", "cv8", "cv10", "cv11", "cv12"):
         out.append((name, "f16"))
     return out
 
@@ -242,14 +242,17 @@ def test_conv2d_fwd_runs_the_planned_form(monkeypatch):
         assert rel_l2(y.cpu().numpy(), ref) <= TOL["f16"]
 
 
-def test_implicit_kernel_alone_with_staged_filter():
-    """im2win_implicit_gemm on a filter staged by im2win_weight_stage."""
+def test_implicit_kernel_alone_with_staged_filter(monkeypatch):
+    """im2win_implicit_gemm on a filter staged by im2win_weight_stage (the
+    streamed kernel, whose plan keeps a staged filter)."""
+    monkeypatch.setenv("IM2WIN_IMPLICIT_KERNEL", "streamed")
     N, Cin, H, W, Cout, KH, KW, s, p = 2, 128, 9, 8, 40, 3, 3, 1, 1
     x, w = workloads.make_inputs(N, Cin, H, W, Cout, KH, KW, seed=8, dtype="bf16")
     xd, wd = x.to(DEV), w.to(DEV)
     wst, _ = conv.weight_stage(wd, s, p, (H, W), conv.LAYOUT_CL)
     d = conv.describe(tuple(x.shape), tuple(w.shape), s, p, conv.BF16)
     pl = conv.implicit_plan(d)
+    assert pl.kernel == 0 and conv.implicit_workspace_size(d) > 0
     y = torch.empty((N, Cout, pl.Ho, pl.Wo), dtype=torch.float32, device=DEV)
     conv.implicit_gemm(xd, wst, y, d)
     torch.cuda.synchronize()
@@ -556,3 +559,48 @@ def test_pipelined_kernel_leaves_memory_past_y_untouched(form, monkeypatch):
     host = buf.cpu().numpy()
     assert (host[n_out:] == 12345.0).all()
     assert rel_l2(host[:n_out], oracle.conv2d(x, w, s, p).reshape(-1)) <= TOL["f16"]
+
+
+# tasks of several whole images (small images: fewer than 128 outputs each),
+# their patches stacked in LDS; the last task of a layer may hold fewer images
+PIPE_IMAGE_SHAPES = [
+    (6, 64, 7, 7, 72, 3, 3, 1, 1),       # 49 outputs per image, Cout past one block
+    (9, 96, 5, 6, 40, 3, 3, 1, 0),       # 3x4 outputs, odd planes (2-byte loads), Wo = 4
+    (5, 32, 4, 4, 130, 1, 1, 1, 0),      # 1x1, 16 outputs, three blocks of Cout
+    (4, 64, 12, 12, 64, 3, 3, 1, 0),     # 10x10 outputs
+    (7, 128, 7, 7, 512, 3, 3, 1, 1),     # the 512-channel 7x7 layer's shape with 128 channels
+]
+PIPE_IMAGE_CASES = [(s, dt, k, im) for k in ("pipe", "pair") for dt in ("f16", "bf16")
+                    for s in PIPE_IMAGE_SHAPES for im in (2, 3, 5)]
+
+
+@pytest.mark.parametrize("shape,dt,form,images", PIPE_IMAGE_CASES,
+                         ids=[f"{k}-{dt}-{s}-i{im}" for s, dt, k, im in PIPE_IMAGE_CASES])
+def test_pipelined_kernel_whole_image_tasks(shape, dt, form, images, monkeypatch):
+    N, Cin, H, W, Cout, KH, KW, s, p = shape
+    monkeypatch.setenv("IM2WIN_IMPLICIT_KERNEL", form)
+    monkeypatch.setenv("IM2WIN_IMPLICIT_IMAGES", str(images))
+    pl = conv.implicit_plan(conv.make_desc(*shape, CODE[dt]))
+    assert pl.kernel == 4
+    if images * pl.Ho * pl.Wo <= 256 and images <= N:
+        assert pl.images == images and pl.rows_per_tile == pl.Ho
+        assert pl.patch_rows == images * (pl.Ho + KH - 1)
+    else:
+        assert pl.images == 1
+    _say(f"implicit-{form} {dt} {shape} images/task={pl.images} workgroups={pl.tiles} lds={pl.lds_bytes}")
+    x, w = workloads.make_inputs(N, Cin, H, W, Cout, KH, KW, seed=29, dtype=dt)
+    got = run_implicit(x, w, s, p)
+    assert rel_l2(got.numpy(), oracle.conv2d(x, w, s, p)) <= TOL[dt]
+
+
+@pytest.mark.parametrize("form", ["pipe", "pair"])
+def test_pipelined_kernel_whole_image_tasks_exact(form, monkeypatch):
+    shape = (5, 64, 7, 7, 72, 3, 3, 1, 1)
+    N, Cin, H, W, Cout, KH, KW, s, p = shape
+    monkeypatch.setenv("IM2WIN_IMPLICIT_KERNEL", form)
+    monkeypatch.setenv("IM2WIN_IMPLICIT_IMAGES", "3")
+    assert conv.implicit_plan(conv.make_desc(*shape, conv.F16)).images == 3
+    x, w = workloads.make_inputs(N, Cin, H, W, Cout, KH, KW, seed=30, dtype="f16",
+                                 x_dist="int3", w_dist="int3")
+    got = run_implicit(x, w, s, p)
+    assert np.array_equal(got.numpy().astype(np.float64), oracle.conv2d(x, w, s, p))

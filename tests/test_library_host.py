@@ -280,7 +280,8 @@ def test_implicit_plan_takes_only_its_layers():
     d = conv.make_desc(2, 80, 9, 9, 8, 3, 3, 1, 1, conv.F16)
     assert conv.implicit_workspace_size(d) == 0
     assert _lib.fwd_implicit(d, 16, 16, 16, 256, None) == 4
-    d = conv.make_desc(2, 64, 9, 9, 8, 3, 3, 1, 1, conv.F16)
+    d = conv.make_desc(2, 64, 9, 9, 8, 3, 3, 2, 1, conv.F16)     # the streamed kernel: a staged filter
+    assert conv.implicit_workspace_size(d) > 0
     assert _lib.fwd_implicit(d, None, 16, 16, 256, None) == 2
     assert _lib.fwd_implicit(d, 16, 16, 16, None, None) == 5
     assert _lib.fwd_implicit(d, 8, 16, 16, 256, None) == 3
@@ -402,62 +403,78 @@ def test_row_block_plan_geometry(monkeypatch):
     assert conv.implicit_plan(d).kernel == 2 and conv.implicit_plan(d).rows_per_tile == 3
 
 
-def test_pipelined_plan_geometry():
+def test_pipelined_plan_geometry(monkeypatch):
     """By default the one-block row kernel keeps its layers (64 channels on rows
     of 8k elements, Wo <= 64) and the pipelined row-block kernels take the other
-    stride-1 3x3 and 1x1 fp16/bf16 layers with Cin a multiple of 32 and at least
-    128 outputs per image (any size where Cin is not a multiple of 64): tasks of
-    R whole output rows x 64 output channels, R * Wo <= 256, 32-channel chunks
-    in LDS (two slots and persistent workgroups, or one slot of at most 80 KB,
-    one task per workgroup), no workspace."""
+    stride-1 3x3 and 1x1 fp16/bf16 layers with Cin a multiple of 32 and Wo <=
+    256: tasks of R whole output rows x 64 output channels, or of several whole
+    small images, at most 256 outputs, 32-channel chunks in LDS (two slots and
+    persistent workgroups, or one slot of at most 80 KB, one task per
+    workgroup), no workspace."""
     import numpy as np
-    rng = np.random.default_rng(14)
-    seen = {1: 0, 2: 0}
-    for _ in range(800):
-        KH, KW = [(3, 3), (1, 1), (5, 5)][int(rng.integers(0, 3))]
-        s = int(rng.choice([1, 1, 1, 2]))
-        p = int(rng.integers(0, 3))
-        Cin = int(rng.choice([32, 64, 96, 128, 256]))
-        W = int(rng.choice([8, 12, 14, 16, 28, 56, 60, 112, 150]))
-        H = int(rng.integers(max(KH, 1), 40))
-        N, Cout = int(rng.integers(1, 9)), int(rng.integers(1, 300))
-        d = conv.make_desc(N, Cin, H, W, Cout, KH, KW, s, p, [conv.F16, conv.BF16][int(rng.integers(0, 2))])
-        if conv._lib.implicit_plan_status(d) != 0:
-            continue
-        pl = conv.implicit_plan(d)
-        one_block = Cin == 64 and W % 8 == 0 and s == 1 and pl.Wo <= 64 and (KH, KW) in ((3, 3), (1, 1))
-        if one_block:
-            assert pl.kernel == 2, (N, Cin, H, W, Cout, KH, KW, s, p)
-            continue
-        if pl.kernel != 4:
-            # only where a pipelined form does not apply (or a small image)
-            assert s != 1 or (KH, KW) not in ((3, 3), (1, 1)) or pl.Wo > 256 or \
-                (Cin % 64 == 0 and pl.Ho * pl.Wo < 128) or Cin % 32 != 0, (N, Cin, H, W, Cout, KH, KW, s, p)
-            continue
-        assert s == 1 and (KH, KW) in ((3, 3), (1, 1)) and Cin % 32 == 0
-        seen[pl.stages] += 1
-        R = pl.rows_per_tile
-        assert 1 <= R <= pl.Ho and R * pl.Wo <= 256
-        assert pl.patch_rows == R + KH - 1 and pl.patch_cols == W + 2 * p and pl.cols_per_tile == pl.Wo
-        tasks = -(-Cout // 64) * N * -(-pl.Ho // R)
-        taps = KH * KW
-        if pl.stages == 2:
-            assert pl.lds_bytes == 2 * (taps * 4096 + pl.patch_rows * pl.patch_cols * 64) + 4 * 16 * 68 * 4
-            assert pl.tiles == min(tasks, 256)
-        else:
-            assert pl.lds_bytes == max(taps * 4096 + pl.patch_rows * pl.patch_cols * 64, STORE_SCRATCH)
-            assert pl.lds_bytes <= 80 * 1024 and pl.tiles == tasks
-        assert pl.lds_bytes <= 160 * 1024
-        assert pl.ws_bytes == 0 == conv.implicit_workspace_size(d)
-        assert conv.plan(d).algo == 1
-    assert seen[1] > 20 and seen[2] > 20, seen
-    # the layers measured: the deep 14x14 layer on the persistent form, the
-    # Table I 28x28 and 14x14 layers on the paired one
-    for name, stages in [("deep3x3", 2), ("cv10", 1), ("cv11", 1), ("cv8", 1)]:
+    seen = {1: 0, 2: 0, "images": 0}
+    for form, images in ((None, None), ("pair", None), ("pipe", "3"), ("pair", "2")):
+        if form:
+            monkeypatch.setenv("IM2WIN_IMPLICIT_KERNEL", form)
+        if images:
+            monkeypatch.setenv("IM2WIN_IMPLICIT_IMAGES", images)
+        rng = np.random.default_rng(14)
+        for _ in range(800):
+            KH, KW = [(3, 3), (1, 1), (5, 5)][int(rng.integers(0, 3))]
+            s = int(rng.choice([1, 1, 1, 2]))
+            p = int(rng.integers(0, 3))
+            Cin = int(rng.choice([32, 64, 96, 128, 256]))
+            W = int(rng.choice([4, 7, 8, 12, 14, 16, 28, 56, 60, 112, 150]))
+            H = int(rng.integers(max(KH, 1), 40))
+            N, Cout = int(rng.integers(1, 9)), int(rng.integers(1, 300))
+            d = conv.make_desc(N, Cin, H, W, Cout, KH, KW, s, p, [conv.F16, conv.BF16][int(rng.integers(0, 2))])
+            if conv._lib.implicit_plan_status(d) != 0:
+                continue
+            pl = conv.implicit_plan(d)
+            pipelined = s == 1 and (KH, KW) in ((3, 3), (1, 1)) and Cin % 32 == 0 and pl.Wo <= 256
+            one_block = Cin == 64 and W % 8 == 0 and s == 1 and pl.Wo <= 64 and (KH, KW) in ((3, 3), (1, 1))
+            if form is None and one_block:
+                assert pl.kernel == 2, (N, Cin, H, W, Cout, KH, KW, s, p)
+                continue
+            if pl.kernel != 4:
+                # only where a pipelined form does not apply, or its LDS does not fit
+                assert not pipelined or pl.lds_bytes == 0 or form, (N, Cin, H, W, Cout, KH, KW, s, p)
+                continue
+            assert pipelined
+            seen[pl.stages] += 1
+            R, img = pl.rows_per_tile, pl.images
+            assert img >= 1 and 1 <= R <= pl.Ho and img * R * pl.Wo <= 256
+            if img > 1:
+                seen["images"] += 1
+                assert R == pl.Ho and img <= N and (images or pl.Ho * pl.Wo < 128)
+            assert pl.patch_rows == img * (R + KH - 1) and pl.patch_cols == W + 2 * p
+            assert pl.cols_per_tile == pl.Wo
+            cob = -(-Cout // 64)
+            tasks = cob * -(-N // img) if img > 1 else cob * N * -(-pl.Ho // R)
+            taps = KH * KW
+            if pl.stages == 2:
+                assert pl.lds_bytes == 2 * (taps * 4096 + pl.patch_rows * pl.patch_cols * 64) + 4 * 16 * 68 * 4
+                assert pl.tiles == min(tasks, 256)
+            else:
+                assert pl.lds_bytes == max(taps * 4096 + pl.patch_rows * pl.patch_cols * 64, STORE_SCRATCH)
+                assert pl.lds_bytes <= 80 * 1024 and pl.tiles == tasks
+                if form is None:
+                    assert tasks >= 512 and img * R * pl.Wo >= 128
+            assert pl.lds_bytes <= 160 * 1024
+            assert pl.ws_bytes == 0 == conv.implicit_workspace_size(d)
+            assert conv.plan(d).algo == 1
+    assert seen[1] > 20 and seen[2] > 20 and seen["images"] > 10, seen
+    # the layers measured: the persistent form for the deep 14x14 layer and the
+    # small-image 512-channel layers, the paired one for the Table I 28x28,
+    # 14x14, 12x12 and 112x112 3x3 layers
+    monkeypatch.delenv("IM2WIN_IMPLICIT_KERNEL")
+    monkeypatch.delenv("IM2WIN_IMPLICIT_IMAGES")
+    for name, stages, img in [("deep3x3", 2, 1), ("mix512", 2, 2), ("cv12", 2, 8), ("cv6", 1, 2),
+                              ("cv8", 1, 1), ("cv10", 1, 1), ("cv11", 1, 1)]:
         cfg = workloads.get_config(name)
         dt = conv.BF16 if name == "deep3x3" else conv.F16
         pl = conv.implicit_plan(conv.make_desc(*cfg.desc().values(), dt))
-        assert pl.kernel == 4 and pl.stages == stages, name
+        assert (pl.kernel, pl.stages, pl.images) == (4, stages, img), name
 
 
 def test_row_block_plan_fp32():
