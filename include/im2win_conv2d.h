@@ -40,7 +40,9 @@
  * point aborts or exits. Every buffer must hold fewer than 2^31 elements.
  *
  * Thread safety: all entry points are reentrant; calls that share a
- * workspace must be ordered by the caller (same stream, or events).
+ * workspace must be ordered by the caller (same stream, or events). Plans
+ * are cached per descriptor and per set of IM2WIN_* environment overrides
+ * (a bounded cache behind a mutex), so repeated calls skip the planner.
  */
 #ifndef IM2WIN_CONV2D_H
 #define IM2WIN_CONV2D_H
