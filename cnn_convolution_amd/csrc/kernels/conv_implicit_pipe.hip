@@ -1,14 +1,15 @@
 // fp16 / bf16 implicit im2win convolution, pipelined row-block form, for
-// stride-1 3x3 and 1x1 layers with a multiple of 32 input channels and output
-// rows of at most 256 columns.
+// 3x3 and 1x1 layers with a multiple of 32 input channels and output rows of
+// at most 256 columns.
 //
 // A task is a block of RW whole output rows (n, ho0 .. ho0+RW-1) of one image
 // and 64 output channels, as in the row-block kernel: the window rows of those
 // output rows (Eq. (2) of "Enabling Memory-efficient Im2win Convolution with
 // Multi-precision Support on GPU CUDA and Tensor Cores", Sec. III-B) share all
 // but their first and last input rows, so a task holds the union once, SL =
-// RW + KH - 1 input rows of IW = W + 2*pad positions, channels innermost; the
-// window of output (i, wo) at tap (kh, kw) is position (i + kh, wo + kw).
+// (RW - 1) * s + KH input rows of IW = W + 2*pad positions, channels
+// innermost; the window of output (i, wo) at tap (kh, kw) is position
+// (i * s + kh, wo * s + kw) for stride s.
 //
 // The contraction runs over K chunks of 32 input channels x all taps (the
 // window's K order of Sec. III-D, taps outer and channels inner within a
@@ -63,6 +64,7 @@ struct PipeKArgs {
     int N;
     int IMG;            // 1: tasks of RW output rows of one image; > 1: tasks of
                         // IMG whole images (RW = Ho), their patches stacked
+    int stride;
 };
 
 // LDS slot of 16-byte granule g (0..3) of 64-byte row q. A 16-byte LDS read
@@ -141,8 +143,8 @@ __device__ __forceinline__ PipeTask pipe_task(const PipeKArgs &a, int t)
         k.ho0 = rg * a.RW;
         k.rw = min(a.RW, a.Ho - k.ho0);
     }
-    k.ih0 = k.ho0 - a.pad;
-    k.SL = k.rw + KH - 1;
+    k.ih0 = k.ho0 * a.stride - a.pad;
+    k.SL = (k.rw - 1) * a.stride + KH;
     return k;
 }
 
@@ -255,17 +257,19 @@ __device__ __forceinline__ void zero_rows(uint16_t *patch, const PipeKArgs &a, c
 }
 
 // Patch position of the window at tap (0, 0) of each of a lane's output
-// blocks: output m of the task is image m / opi, row and column of the rest
-// (opi = rw * Wo outputs per image), at patch row im * SL + i.
+// blocks: output m of the task is image m / opi, row i and column wo of the
+// rest (opi = rw * Wo outputs per image), at patch row im * SL + i * st and
+// column wo * st.
 template <bool MI>
-__device__ __forceinline__ void task_bases(int *qa, int b0, int lane, int outs, int Wo, int IW, int opi, int SL)
+__device__ __forceinline__ void task_bases(int *qa, int b0, int lane, int outs, int Wo, int IW, int opi, int SL,
+                                           int st)
 {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
         const int m = min((b0 + s) * 16 + (lane & 15), outs - 1);
         const int im = MI ? m / opi : 0, rem = m - im * opi;
         const int i = rem / Wo;
-        qa[s] = (im * SL + i) * IW + (rem - i * Wo);
+        qa[s] = (im * SL + i * st) * IW + (rem - i * Wo) * st;
     }
 }
 
@@ -486,7 +490,7 @@ __global__ __launch_bounds__(kPipeThreads) void conv_implicit_pipe_kernel(const 
                 tk = pipe_task<KH, MI>(a, L + (c / nch) * G);
                 outs = tk.nimg * tk.rw * a.Wo;
                 wave_blocks_of(wave, kComputeWaves, outs, b0, nb);
-                task_bases<MI>(qa, b0, lane, outs, a.Wo, a.IW, tk.rw * a.Wo, tk.SL);
+                task_bases<MI>(qa, b0, lane, outs, a.Wo, a.IW, tk.rw * a.Wo, tk.SL, a.stride);
             }
             contract_blocks<KH, KW, BF16, true>(acc, nb, qa, lds + (c & 1) * a.slot_halves, a.IW, lane);
             if (blk == nch - 1) {
@@ -536,7 +540,7 @@ __global__ __launch_bounds__(kPipeThreads) __attribute__((amdgpu_waves_per_eu(4)
     int b0, nb;
     wave_blocks(wave, outs, b0, nb);
     int qa[4];
-    task_bases<MI>(qa, b0, lane, outs, a.Wo, a.IW, tk.rw * a.Wo, tk.SL);
+    task_bases<MI>(qa, b0, lane, outs, a.Wo, a.IW, tk.rw * a.Wo, tk.SL, a.stride);
     constexpr int MAXB = 2;                          // R * Wo <= 256: at most 2 blocks per wave
     floatx4_t acc[MAXB][4];
 #pragma unroll
@@ -585,9 +589,10 @@ hipError_t launch_conv_implicit_pipe(const ImplicitArgs &h, hipStream_t s)
     // 1 for the paired form (one slot, one task per workgroup)
     const bool pair = h.stages == 1;
     const int img = std::max(h.images, 1);
-    if (h.f32 || h.Cin % kChunkC != 0 || h.stride != 1 || h.W < 1 || h.H < 1 || h.Wo < 1 || h.Ho < 1 ||
+    if (h.f32 || h.Cin % kChunkC != 0 || h.stride < 1 || h.W < 1 || h.H < 1 || h.Wo < 1 || h.Ho < 1 ||
         h.R < 1 || int64_t(img) * h.R * h.Wo > 256 || h.IW != h.W + 2 * h.pad ||
-        h.IR != img * (h.R + h.KH - 1) || (img > 1 && h.R != h.Ho) ||
+        (h.Wo - 1) * h.stride + h.KW > h.IW || h.IR != img * ((h.R - 1) * h.stride + h.KH) ||
+        (img > 1 && h.R != h.Ho) ||
         int64_t(h.Cin) * h.H * h.W >= (int64_t(1) << 31) ||
         (!pair && h.fs_groups < 1) || (h.stages != 1 && h.stages != 2) ||
         !((h.KH == 3 && h.KW == 3) || (h.KH == 1 && h.KW == 1)))
@@ -609,6 +614,7 @@ hipError_t launch_conv_implicit_pipe(const ImplicitArgs &h, hipStream_t s)
     a.IW = h.IW;
     a.N = h.N;
     a.IMG = img;
+    a.stride = h.stride;
     const int64_t ntasks = img > 1 ? int64_t(a.co_blocks) * ((h.N + img - 1) / img)
                                    : int64_t(a.co_blocks) * h.N * a.row_groups;
     if (ntasks > 0x7fffffff) return hipErrorInvalidValue;

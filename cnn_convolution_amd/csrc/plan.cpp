@@ -472,7 +472,7 @@ static void pick_implicit_rows(const conv2d_desc_t &d, int64_t Ho, int64_t Wo, c
 // limit) that still leave min_tasks tasks; 1 where even two do not.
 // IM2WIN_IMPLICIT_IMAGES sets it.
 static int64_t pick_images(const conv2d_desc_t &d, int64_t Ho, int64_t Wo, int64_t min_tasks, bool pair) {
-    const int64_t taps = d.KH * d.KW, iw = d.W + 2 * d.pad, sl = Ho + d.KH - 1;
+    const int64_t taps = d.KH * d.KW, iw = d.W + 2 * d.pad, sl = (Ho - 1) * d.stride + d.KH;
     const int64_t co_blocks = ceil_div(d.Cout, 64);
     auto fits = [&](int64_t img) {
         const int64_t lds = pair ? pair_lds_bytes(taps, img * sl, iw) : pipe_lds_bytes(taps, img * sl, iw);
@@ -501,7 +501,7 @@ static int64_t pick_images(const conv2d_desc_t &d, int64_t Ho, int64_t Wo, int64
 // IM2WIN_IMPLICIT_KERNEL=pipe; IM2WIN_IMPLICIT_ROWS sets RW.
 static void pick_implicit_pipe(const conv2d_desc_t &d, int64_t Ho, int64_t Wo, conv2d_implicit_plan_t *p,
                                bool dflt) {
-    if (d.dtype == CONV2D_F32 || d.Cin % 32 != 0 || d.stride != 1 || Wo > 256 || Wo < 1 || Ho < 1) return;
+    if (d.dtype == CONV2D_F32 || d.Cin % 32 != 0 || d.stride > 2 || Wo > 256 || Wo < 1 || Ho < 1) return;
     if (!((d.KH == 3 && d.KW == 3) || (d.KH == 1 && d.KW == 1))) return;
     if (d.Cin * d.H * d.W >= (int64_t(1) << 31)) return;
     if (const char *e = std::getenv("IM2WIN_IMPLICIT_KERNEL")) {
@@ -509,6 +509,7 @@ static void pick_implicit_pipe(const conv2d_desc_t &d, int64_t Ho, int64_t Wo, c
     } else if (!dflt || std::getenv("IM2WIN_IMPLICIT_TILE")) {
         return;
     }
+    const int64_t s = d.stride;
     const int64_t taps = d.KH * d.KW;
     const int64_t iw = d.W + 2 * d.pad;
     const int64_t co_blocks = ceil_div(d.Cout, 64);
@@ -517,7 +518,7 @@ static void pick_implicit_pipe(const conv2d_desc_t &d, int64_t Ho, int64_t Wo, c
     int64_t best_rw = 0, best_groups = 0;
     double best_cost = 0.0;
     for (int64_t rw = 1; rw <= Ho && rw * Wo <= 256; ++rw) {
-        const int64_t sl = rw + d.KH - 1;
+        const int64_t sl = (rw - 1) * s + d.KH;
         if (pipe_lds_bytes(taps, sl, iw) > kImplicitMaxLdsBytes) break;
         const int64_t tasks = co_blocks * d.N * ceil_div(Ho, rw);
         const int64_t groups = std::min<int64_t>(tasks, 256);
@@ -532,7 +533,7 @@ static void pick_implicit_pipe(const conv2d_desc_t &d, int64_t Ho, int64_t Wo, c
     if (best_rw == 0) return;
     if (const char *e = std::getenv("IM2WIN_IMPLICIT_ROWS")) {
         const int64_t v = std::min<int64_t>(std::atoi(e), Ho);
-        if (v >= 1 && v * Wo <= 256 && pipe_lds_bytes(taps, v + d.KH - 1, iw) <= kImplicitMaxLdsBytes) {
+        if (v >= 1 && v * Wo <= 256 && pipe_lds_bytes(taps, (v - 1) * s + d.KH, iw) <= kImplicitMaxLdsBytes) {
             best_rw = v;
             best_groups = std::min<int64_t>(co_blocks * d.N * ceil_div(Ho, v), 256);
         }
@@ -548,7 +549,7 @@ static void pick_implicit_pipe(const conv2d_desc_t &d, int64_t Ho, int64_t Wo, c
     p->wave_m = 1;
     p->rows_per_tile = int32_t(best_rw);
     p->cols_per_tile = int32_t(Wo);
-    p->patch_rows = int32_t(img * (best_rw + d.KH - 1));
+    p->patch_rows = int32_t(img * ((best_rw - 1) * s + d.KH));
     p->patch_cols = int32_t(iw);
     p->stages = 2;
     p->images = int32_t(img);
@@ -565,7 +566,7 @@ static void pick_implicit_pipe(const conv2d_desc_t &d, int64_t Ho, int64_t Wo, c
 // IM2WIN_IMPLICIT_ROWS sets RW.
 static void pick_implicit_pair(const conv2d_desc_t &d, int64_t Ho, int64_t Wo, conv2d_implicit_plan_t *p,
                                bool dflt) {
-    if (d.dtype == CONV2D_F32 || d.Cin % 32 != 0 || d.stride != 1 || Wo > 256 || Wo < 1 || Ho < 1) return;
+    if (d.dtype == CONV2D_F32 || d.Cin % 32 != 0 || d.stride > 2 || Wo > 256 || Wo < 1 || Ho < 1) return;
     if (!((d.KH == 3 && d.KW == 3) || (d.KH == 1 && d.KW == 1))) return;
     if (d.Cin * d.H * d.W >= (int64_t(1) << 31)) return;
     if (const char *e = std::getenv("IM2WIN_IMPLICIT_KERNEL")) {
@@ -573,6 +574,7 @@ static void pick_implicit_pair(const conv2d_desc_t &d, int64_t Ho, int64_t Wo, c
     } else if (!dflt || std::getenv("IM2WIN_IMPLICIT_TILE")) {
         return;
     }
+    const int64_t s = d.stride;
     const int64_t taps = d.KH * d.KW;
     const int64_t iw = d.W + 2 * d.pad;
     const int64_t co_blocks = ceil_div(d.Cout, 64);
@@ -580,7 +582,7 @@ static void pick_implicit_pair(const conv2d_desc_t &d, int64_t Ho, int64_t Wo, c
     // 512 tasks, two per CU; the most rows that fit where none does
     int64_t best_rw = 0, fit_rw = 0;
     for (int64_t rw = 1; rw <= Ho && rw * Wo <= 256; ++rw) {
-        if (pair_lds_bytes(taps, rw + d.KH - 1, iw) > kImplicitPairLdsBytes) break;
+        if (pair_lds_bytes(taps, (rw - 1) * s + d.KH, iw) > kImplicitPairLdsBytes) break;
         fit_rw = rw;
         if (co_blocks * d.N * ceil_div(Ho, rw) >= 512) best_rw = rw;
     }
@@ -589,7 +591,7 @@ static void pick_implicit_pair(const conv2d_desc_t &d, int64_t Ho, int64_t Wo, c
     best_rw = ceil_div(Ho, ceil_div(Ho, best_rw));   // the same number of tasks, rows spread evenly
     if (const char *e = std::getenv("IM2WIN_IMPLICIT_ROWS")) {
         const int64_t v = std::min<int64_t>(std::atoi(e), Ho);
-        if (v >= 1 && v * Wo <= 256 && pair_lds_bytes(taps, v + d.KH - 1, iw) <= kImplicitMaxLdsBytes)
+        if (v >= 1 && v * Wo <= 256 && pair_lds_bytes(taps, (v - 1) * s + d.KH, iw) <= kImplicitMaxLdsBytes)
             best_rw = v;
     }
     const int64_t img = pick_images(d, Ho, Wo, 512, true);
@@ -600,7 +602,7 @@ static void pick_implicit_pair(const conv2d_desc_t &d, int64_t Ho, int64_t Wo, c
     p->wave_m = 1;
     p->rows_per_tile = int32_t(best_rw);
     p->cols_per_tile = int32_t(Wo);
-    p->patch_rows = int32_t(img * (best_rw + d.KH - 1));
+    p->patch_rows = int32_t(img * ((best_rw - 1) * s + d.KH));
     p->patch_cols = int32_t(iw);
     p->stages = 1;
     p->images = int32_t(img);
@@ -610,14 +612,16 @@ static void pick_implicit_pair(const conv2d_desc_t &d, int64_t Ho, int64_t Wo, c
 }
 
 // The pipelined row-block kernels where they apply by default: the paired
-// form where its tasks hold at least 128 outputs (every one of its eight
-// waves busy) and number at least 512 (two per CU), else the persistent form
+// form where its tasks number at least 512 (two per CU) and either hold at
+// least 128 outputs (every one of its eight waves busy) or number at least
+// 1024, else the persistent form
 // (its four computing waves take up to four blocks each of a task of up to
 // 256 outputs, small images several to a task). Measured against the
 // row-block kernel over several channel blocks and the streamed kernel: paired
 // 1.04-1.6x faster on cv6, cv8, cv10 and cv11, persistent 1.13x on the 14x14
 // deep layer (paired tasks of 98 outputs), 1.36x on the 512-channel 7x7 layer
-// and 1.9x on cv12 (several images per task).
+// and 1.9x on cv12 (several images per task); stride 2: paired 1.2x over the
+// streamed kernel and the window form on the 28x28 -> 14x14 layer.
 static void pick_implicit_pipelined(const conv2d_desc_t &d, int64_t Ho, int64_t Wo, conv2d_implicit_plan_t *p,
                                     bool dflt) {
     if (!dflt) {
@@ -633,7 +637,7 @@ static void pick_implicit_pipelined(const conv2d_desc_t &d, int64_t Ho, int64_t 
     conv2d_implicit_plan_t pair = *p;
     pick_implicit_pair(d, Ho, Wo, &pair, true);
     if (pair.kernel == 4 && pair.tiles >= 512 &&
-        int64_t(pair.images) * pair.rows_per_tile * Wo >= 128) {
+        (int64_t(pair.images) * pair.rows_per_tile * Wo >= 128 || pair.tiles >= 1024)) {
         *p = pair;
         return;
     }
@@ -805,7 +809,7 @@ static conv2d_status_t compute_implicit_plan(const conv2d_desc_t &d, conv2d_impl
     pick_implicit_rows(d, Ho, Wo, p);
     // the one-block row kernel stays where it applies (64 channels on rows of
     // 8k elements, measured faster than both pipelined forms); elsewhere the
-    // pipelined forms take the stride-1 3x3 and 1x1 layers
+    // pipelined forms take the 3x3 and 1x1 layers of stride 1 or 2
     const bool one_block = p->kernel == 2 && d.Cin == 64 && d.W % 8 == 0;
     pick_implicit_pipelined(d, Ho, Wo, p, !one_block);
     return CONV2D_OK;

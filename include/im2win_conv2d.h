@@ -198,7 +198,7 @@ const char *conv2d_status_string(conv2d_status_t s);
  * channels-innermost patch, and contracts it against the staged filter in
  * the window's K order (Sec. III-C Eq. (3), Sec. III-D). Matrix cores with
  * fp32 accumulation, fp32 y: fp16/bf16 with Cin a multiple of 64 (or of 32
- * for stride-1 3x3 and 1x1 filters), up to 8 input channels in any dtype,
+ * for 3x3 and 1x1 filters of stride 1 or 2), up to 8 input channels in any dtype,
  * fp32 on the row-block kernel's layers. The workspace holds only the staged
  * filter (none for a 1x1 filter or for the row-block kernels). */
 typedef struct {
@@ -219,9 +219,9 @@ typedef struct {
                                      of one image per workgroup with w as stored
                                      and the input rows resident in LDS, no
                                      staged filter (ws_bytes 0); 3: narrow-channel
-                                     (Cin <= 8); 4 (default for the other stride-1
-                                     3x3 and 1x1 layers with Cin % 32 == 0 and Wo
-                                     <= 256): pipelined row-block, tasks of
+                                     (Cin <= 8); 4 (default for the other 3x3 and
+                                     1x1 layers of stride 1 or 2 with Cin % 32 ==
+                                     0 and Wo <= 256): pipelined row-block, tasks of
                                      rows_per_tile whole output rows (or of
                                      `images` whole images) x 64 output channels
                                      over 32-channel K chunks double-buffered in

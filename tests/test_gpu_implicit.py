@@ -604,3 +604,36 @@ def test_pipelined_kernel_whole_image_tasks_exact(form, monkeypatch):
                                  x_dist="int3", w_dist="int3")
     got = run_implicit(x, w, s, p)
     assert np.array_equal(got.numpy().astype(np.float64), oracle.conv2d(x, w, s, p))
+
+
+# stride 2 (asked for by name): patches of (R - 1) * 2 + KH input rows, the
+# windows of consecutive outputs two positions apart
+PIPE_STRIDE_SHAPES = [
+    (2, 64, 14, 14, 72, 3, 3, 2, 1),     # 7x7 outputs, Cout past one block
+    (1, 96, 17, 23, 64, 3, 3, 2, 0),     # odd planes, 8x11 outputs
+    (3, 128, 12, 16, 130, 1, 1, 2, 0),   # 1x1 stride 2 (a downsampling shortcut)
+    (2, 32, 28, 28, 40, 3, 3, 2, 1),     # 14x14 outputs
+]
+PIPE_STRIDE_CASES = [(s, dt, k, im) for k in ("pipe", "pair") for dt in ("f16", "bf16")
+                     for s in PIPE_STRIDE_SHAPES for im in (None, 1, 2)]
+
+
+@pytest.mark.parametrize("shape,dt,form,images", PIPE_STRIDE_CASES,
+                         ids=[f"{k}-{dt}-{s}-i{im}" for s, dt, k, im in PIPE_STRIDE_CASES])
+def test_pipelined_kernel_stride_two(shape, dt, form, images, monkeypatch):
+    N, Cin, H, W, Cout, KH, KW, s, p = shape
+    monkeypatch.setenv("IM2WIN_IMPLICIT_KERNEL", form)
+    if images is not None:
+        monkeypatch.setenv("IM2WIN_IMPLICIT_IMAGES", str(images))
+    pl = conv.implicit_plan(conv.make_desc(*shape, CODE[dt]))
+    assert pl.kernel == 4
+    assert pl.patch_rows == pl.images * ((pl.rows_per_tile - 1) * s + KH)
+    _say(f"implicit-{form} {dt} {shape} rows/task={pl.rows_per_tile} images={pl.images}")
+    x, w = workloads.make_inputs(N, Cin, H, W, Cout, KH, KW, seed=31, dtype=dt)
+    got = run_implicit(x, w, s, p)
+    assert rel_l2(got.numpy(), oracle.conv2d(x, w, s, p)) <= TOL[dt]
+    if dt == "f16" and images is None:
+        xi, wi = workloads.make_inputs(N, Cin, H, W, Cout, KH, KW, seed=32, dtype="f16",
+                                       x_dist="int3", w_dist="int3")
+        got = run_implicit(xi, wi, s, p)
+        assert np.array_equal(got.numpy().astype(np.float64), oracle.conv2d(xi, wi, s, p))

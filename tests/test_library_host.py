@@ -266,11 +266,12 @@ def test_row_layout_keeps_slack_after_every_run():
 
 def test_implicit_plan_takes_only_its_layers():
     """The implicit form takes fp16/bf16 layers with Cin a multiple of 64 (and
-    stride-1 3x3 / 1x1 ones with Cin a multiple of 32) and reports UNSUPPORTED
+    3x3 / 1x1 ones of stride 1 or 2 with Cin a multiple of 32) and reports UNSUPPORTED
     (status 4) for the rest, before touching any pointer."""
     assert conv._lib.implicit_plan_status(conv.make_desc(2, 64, 9, 9, 8, 3, 3, 1, 1, conv.F32)) == 4
     assert conv._lib.implicit_plan_status(conv.make_desc(2, 80, 9, 9, 8, 3, 3, 1, 1, conv.F16)) == 4
-    assert conv._lib.implicit_plan_status(conv.make_desc(2, 96, 9, 9, 8, 3, 3, 2, 1, conv.F16)) == 4
+    assert conv._lib.implicit_plan_status(conv.make_desc(2, 96, 9, 9, 8, 3, 3, 3, 1, conv.F16)) == 4
+    assert conv._lib.implicit_plan_status(conv.make_desc(2, 96, 9, 9, 8, 5, 5, 1, 1, conv.F16)) == 4
     assert conv.implicit_plan(conv.make_desc(2, 96, 9, 9, 8, 3, 3, 1, 1, conv.F16)).kernel == 4
     assert conv._lib.implicit_plan_status(conv.make_desc(2, 12, 9, 9, 8, 3, 3, 1, 1, conv.BF16)) == 4
     # up to 8 input channels: the narrow-channel kernel, any dtype
@@ -280,7 +281,7 @@ def test_implicit_plan_takes_only_its_layers():
     d = conv.make_desc(2, 80, 9, 9, 8, 3, 3, 1, 1, conv.F16)
     assert conv.implicit_workspace_size(d) == 0
     assert _lib.fwd_implicit(d, 16, 16, 16, 256, None) == 4
-    d = conv.make_desc(2, 64, 9, 9, 8, 3, 3, 2, 1, conv.F16)     # the streamed kernel: a staged filter
+    d = conv.make_desc(2, 64, 9, 9, 8, 5, 5, 1, 2, conv.F16)     # the streamed kernel: a staged filter
     assert conv.implicit_workspace_size(d) > 0
     assert _lib.fwd_implicit(d, None, 16, 16, 256, None) == 2
     assert _lib.fwd_implicit(d, 16, 16, 16, None, None) == 5
@@ -406,8 +407,8 @@ def test_row_block_plan_geometry(monkeypatch):
 def test_pipelined_plan_geometry(monkeypatch):
     """By default the one-block row kernel keeps its layers (64 channels on rows
     of 8k elements, Wo <= 64) and the pipelined row-block kernels take the other
-    stride-1 3x3 and 1x1 fp16/bf16 layers with Cin a multiple of 32 and Wo <=
-    256: tasks of R whole output rows x 64 output channels, or of several whole
+    3x3 and 1x1 fp16/bf16 layers of stride 1 or 2 with Cin a multiple of 32 and
+    Wo <= 256: tasks of R whole output rows x 64 output channels, or of several whole
     small images, at most 256 outputs, 32-channel chunks in LDS (two slots and
     persistent workgroups, or one slot of at most 80 KB, one task per
     workgroup), no workspace."""
@@ -431,7 +432,7 @@ def test_pipelined_plan_geometry(monkeypatch):
             if conv._lib.implicit_plan_status(d) != 0:
                 continue
             pl = conv.implicit_plan(d)
-            pipelined = s == 1 and (KH, KW) in ((3, 3), (1, 1)) and Cin % 32 == 0 and pl.Wo <= 256
+            pipelined = s <= 2 and (KH, KW) in ((3, 3), (1, 1)) and Cin % 32 == 0 and pl.Wo <= 256
             one_block = Cin == 64 and W % 8 == 0 and s == 1 and pl.Wo <= 64 and (KH, KW) in ((3, 3), (1, 1))
             if form is None and one_block:
                 assert pl.kernel == 2, (N, Cin, H, W, Cout, KH, KW, s, p)
@@ -447,7 +448,7 @@ def test_pipelined_plan_geometry(monkeypatch):
             if img > 1:
                 seen["images"] += 1
                 assert R == pl.Ho and img <= N and (images or pl.Ho * pl.Wo < 128)
-            assert pl.patch_rows == img * (R + KH - 1) and pl.patch_cols == W + 2 * p
+            assert pl.patch_rows == img * ((R - 1) * s + KH) and pl.patch_cols == W + 2 * p
             assert pl.cols_per_tile == pl.Wo
             cob = -(-Cout // 64)
             tasks = cob * -(-N // img) if img > 1 else cob * N * -(-pl.Ho // R)
@@ -459,7 +460,7 @@ def test_pipelined_plan_geometry(monkeypatch):
                 assert pl.lds_bytes == max(taps * 4096 + pl.patch_rows * pl.patch_cols * 64, STORE_SCRATCH)
                 assert pl.lds_bytes <= 80 * 1024 and pl.tiles == tasks
                 if form is None:
-                    assert tasks >= 512 and img * R * pl.Wo >= 128
+                    assert tasks >= 512 and (img * R * pl.Wo >= 128 or tasks >= 1024)
             assert pl.lds_bytes <= 160 * 1024
             assert pl.ws_bytes == 0 == conv.implicit_workspace_size(d)
             assert conv.plan(d).algo == 1
