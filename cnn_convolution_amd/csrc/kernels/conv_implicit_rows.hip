@@ -497,7 +497,12 @@ struct RowsF32KArgs {
     int RW, row_groups, co_blocks, IW;
 };
 
-template <int KH, int KW>
+// VEC4: rows of 4k floats, loaded as 16-byte row chunks of one channel and
+// transposed in registers; otherwise (any row width) each unit gathers the 4
+// channels of one position with 4-byte loads, consecutive lanes on
+// consecutive positions of the block's input rows (one contiguous run of
+// every channel plane), and the rows outside the image are zeroed once.
+template <int KH, int KW, bool VEC4>
 __global__ __launch_bounds__(kRowsThreads) void conv_implicit_rows_f32_kernel(const RowsF32KArgs a)
 {
     constexpr int TAPS = KH * KW;
@@ -521,7 +526,11 @@ __global__ __launch_bounds__(kRowsThreads) void conv_implicit_rows_f32_kernel(co
     const float *const ximg = a.x + int64_t(n) * a.Cin * HW;
     const int nblk = a.Cin / CB;
     const int CW = a.W >> 2;                         // chunks of 4 columns
-    const int units = SL * CW * 8;                   // (input row, chunk, 4-channel group)
+    // VEC4: (input row, chunk, 4-channel group); else (4-channel group,
+    // position of the block's rows in the image), position fastest
+    const int r_lo = max(ih0, 0), r_hi = max(min(ih0 + SL, a.H), r_lo);
+    const int npos = (r_hi - r_lo) * a.W;
+    const int units = VEC4 ? SL * CW * 8 : 8 * npos;
     const int co_l = tid >> 3;
     const int cg = tid & 7;                          // 4-channel group of the block
     const int co_src = min(cb * 64 + co_l, a.Cout - 1);
@@ -535,6 +544,18 @@ __global__ __launch_bounds__(kRowsThreads) void conv_implicit_rows_f32_kernel(co
         const int c = r - i * 2 * a.pad;
         const int q = i * a.IW + (c < a.pad ? c : a.W + c);
         *reinterpret_cast<float4 *>(patch + q * CB + ((g ^ (q & 7)) << 2)) = float4{0.f, 0.f, 0.f, 0.f};
+    }
+    if constexpr (!VEC4) {
+        // rows of the block outside the image (the same in every channel block)
+        const int top = r_lo - ih0;                  // rows 0 .. top-1
+        const int bot = SL - (r_hi - ih0);           // the last bot rows
+        for (int v = tid; v < (top + bot) * a.IW * 8; v += kRowsThreads) {
+            const int g = v & 7, e = v >> 3;
+            const int zr = e / a.IW, c = e - zr * a.IW;
+            const int i = zr < top ? zr : (r_hi - ih0) + (zr - top);
+            const int q = i * a.IW + c;
+            *reinterpret_cast<float4 *>(patch + q * CB + ((g ^ (q & 7)) << 2)) = float4{0.f, 0.f, 0.f, 0.f};
+        }
     }
 
     floatx4_t acc[4][4];
@@ -585,10 +606,12 @@ __global__ __launch_bounds__(kRowsThreads) void conv_implicit_rows_f32_kernel(co
         };
         // the first two units of this thread are in flight with the filter slice
         float4 r0[4], r1[4];
-        int q0a, g0a, q0b, g0b;
-        bool i0a, i0b;
-        load_unit(min(tid, units - 1), r0, q0a, g0a, i0a);
-        load_unit(min(tid + kRowsThreads, units - 1), r1, q0b, g0b, i0b);
+        int q0a = 0, g0a = 0, q0b = 0, g0b = 0;
+        bool i0a = false, i0b = false;
+        if constexpr (VEC4) {
+            load_unit(min(tid, units - 1), r0, q0a, g0a, i0a);
+            load_unit(min(tid + kRowsThreads, units - 1), r1, q0b, g0b, i0b);
+        }
 #pragma unroll
         for (int t = 0; t < TAPS; ++t) {
             // element e of tap t is float e*TAPS + t of the 4*TAPS run
@@ -596,14 +619,26 @@ __global__ __launch_bounds__(kRowsThreads) void conv_implicit_rows_f32_kernel(co
             *reinterpret_cast<float4 *>(fl + t * 64 * CB + co_l * CB + ((cg ^ (co_l & 7)) << 2)) =
                 float4{f[t], f[TAPS + t], f[2 * TAPS + t], f[3 * TAPS + t]};
         }
-        if (tid < units) put_unit(q0a, g0a, i0a, r0);
-        if (tid + kRowsThreads < units) put_unit(q0b, g0b, i0b, r1);
-        for (int u = tid + 2 * kRowsThreads; u < units; u += kRowsThreads) {
-            float4 raw[4];
-            int q0, g;
-            bool in;
-            load_unit(u, raw, q0, g, in);
-            put_unit(q0, g, in, raw);
+        if constexpr (VEC4) {
+            if (tid < units) put_unit(q0a, g0a, i0a, r0);
+            if (tid + kRowsThreads < units) put_unit(q0b, g0b, i0b, r1);
+            for (int u = tid + 2 * kRowsThreads; u < units; u += kRowsThreads) {
+                float4 raw[4];
+                int q0, g;
+                bool in;
+                load_unit(u, raw, q0, g, in);
+                put_unit(q0, g, in, raw);
+            }
+        } else {
+            const float *xb = ximg + int64_t(blk * CB) * HW + int64_t(r_lo) * a.W;
+            for (int u = tid; u < units; u += kRowsThreads) {
+                const int g = u / npos, p = u - g * npos;
+                const float *src = xb + int64_t(g * 4) * HW + p;
+                const float v0 = src[0], v1 = src[HW], v2 = src[2 * HW], v3 = src[3 * HW];
+                const int r = p / a.W;
+                const int q = (r_lo - ih0 + r) * a.IW + a.pad + (p - r * a.W);
+                *reinterpret_cast<float4 *>(patch + q * CB + ((g ^ (q & 7)) << 2)) = float4{v0, v1, v2, v3};
+            }
         }
         __syncthreads();
 
@@ -672,7 +707,7 @@ hipError_t launch_rows_f32(const ImplicitArgs &h, hipStream_t s)
     const int64_t blocks = int64_t(a.co_blocks) * h.N * a.row_groups;
     if (blocks < 1 || blocks > 0x7fffffff) return hipErrorInvalidValue;
     const size_t lds = implicit_rows_lds_bytes(KH * KW, h.R + KH - 1, a.IW);
-    auto kern = conv_implicit_rows_f32_kernel<KH, KW>;
+    auto kern = h.W % 4 == 0 ? conv_implicit_rows_f32_kernel<KH, KW, true> : conv_implicit_rows_f32_kernel<KH, KW, false>;
     if (lds > 64 * 1024) {
         const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                                  hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
@@ -729,8 +764,8 @@ hipError_t launch_conv_implicit_rows(const ImplicitArgs &h, hipStream_t s)
     // for such layers): 64 input channels, stride 1, whole rows of W % 8 == 0
     // elements, at most 64 output columns, one output row per wave
     if (h.f32) {
-        // fp32: channel blocks of 32, whole rows of W % 4 == 0 elements
-        if (h.Cin % 32 != 0 || h.Cin < 32 || h.stride != 1 || h.W % 4 != 0 || h.W < 4 || h.Wo < 1 ||
+        // fp32: channel blocks of 32, rows of any width (row chunks where W % 4 == 0)
+        if (h.Cin % 32 != 0 || h.Cin < 32 || h.stride != 1 || h.W < 1 || h.Wo < 1 ||
             h.Wo > 64 || h.Wo != h.W + 2 * h.pad - h.KW + 1 || h.R < 1 || int64_t(h.R) * h.Wo > 512 ||
             h.Ho != h.H + 2 * h.pad - h.KH + 1 ||
             implicit_rows_lds_bytes(h.KH * h.KW, h.R + h.KH - 1, h.W + 2 * h.pad) > kImplicitMaxLdsBytes)

@@ -411,7 +411,7 @@ static void pick_implicit_rows(const conv2d_desc_t &d, int64_t Ho, int64_t Wo, c
     // kernel), or several blocks / any width (the channel-block loop) where an
     // image has at least 128 outputs (8 MFMA blocks: every wave busy); smaller
     // images stay on the streamed kernel
-    const bool chans = f32 ? (d.Cin % 32 == 0 && d.W % 4 == 0)
+    const bool chans = f32 ? (d.Cin % 32 == 0 && (d.W % 4 == 0 || Ho * Wo >= 128))
                            : (d.Cin % 64 == 0 && ((d.Cin == 64 && d.W % 8 == 0) || Ho * Wo >= 128));
     if (!chans || d.stride != 1 || Wo > 64 || !((d.KH == 3 && d.KW == 3) || (d.KH == 1 && d.KW == 1)))
         return;

@@ -300,6 +300,11 @@ ROWS_SHAPES_F32 = [
     (1, 96, 7, 20, 70, 3, 3, 1, 0),      # three blocks, Wo = 18
     (2, 128, 6, 28, 64, 1, 1, 1, 0),     # 1x1, four blocks
     (1, 64, 5, 4, 16, 3, 3, 1, 2),       # W = 4: one chunk per row, padding 2
+    # rows of any width (gathered 4 channels of one position at a time)
+    (2, 64, 14, 14, 72, 3, 3, 1, 1),     # the deep layer's 14x14 image
+    (1, 96, 13, 15, 40, 3, 3, 1, 0),     # 11x13 outputs
+    (2, 32, 18, 18, 16, 1, 1, 1, 0),     # 1x1
+    (1, 32, 17, 9, 24, 3, 3, 1, 2),      # padding 2: rows outside the image, 19x11 outputs
 ]
 
 

@@ -480,7 +480,8 @@ def test_pipelined_plan_geometry(monkeypatch):
 
 def test_row_block_plan_fp32():
     """fp32 layers go to the implicit form only through the row-block kernel
-    (fp32 matrix-core products): Cin a multiple of 32, stride 1, W % 4 == 0,
+    (fp32 matrix-core products): Cin a multiple of 32, stride 1, W % 4 == 0
+    (or any width where an image has at least 128 outputs),
     Wo <= 64, a 3x3 or 1x1 filter; every other fp32 layer stays on the
     vector-ALU window form."""
     import numpy as np
@@ -496,9 +497,11 @@ def test_row_block_plan_fp32():
         N, Cout = int(rng.integers(1, 5)), int(rng.integers(1, 200))
         d = conv.make_desc(N, Cin, H, W, Cout, KH, KW, s, p, conv.F32)
         Wo = (W + 2 * p - KW) // s + 1
-        if Wo < 1 or (H + 2 * p - KH) // s + 1 < 1:
+        Ho = (H + 2 * p - KH) // s + 1
+        if Wo < 1 or Ho < 1:
             continue
-        eligible = (Cin % 32 == 0 and s == 1 and W % 4 == 0 and Wo <= 64 and (KH, KW) in ((3, 3), (1, 1)))
+        eligible = (Cin % 32 == 0 and s == 1 and (W % 4 == 0 or Ho * Wo >= 128) and Wo <= 64 and
+                    (KH, KW) in ((3, 3), (1, 1)))
         narrow = Cin <= 8 and Wo <= 512
         seen[eligible] += 1
         st = conv._lib.implicit_plan_status(d)
