@@ -575,3 +575,31 @@ def test_narrow_plan_geometry():
         assert pl.K_stage == Kp and pl.ws_bytes == -(-(Cout * Kp * es) // 256) * 256
         assert conv.implicit_workspace_size(d) == pl.ws_bytes
     assert taken > 300
+
+
+def test_plans_are_cached_per_descriptor_and_override(monkeypatch):
+    """Repeated plans of one descriptor are the same; an IM2WIN_* override in
+    the environment is part of the cache key, so changing it changes the plan,
+    and removing it brings the first plan back."""
+    for k in [k for k in os.environ if k.startswith("IM2WIN_")]:
+        monkeypatch.delenv(k)
+    d = conv.make_desc(2, 128, 14, 14, 72, 3, 3, 1, 1, conv.F16)
+    first = conv.implicit_plan(d).as_dict()
+    assert conv.implicit_plan(d).as_dict() == first and first["kernel"] == 4
+    monkeypatch.setenv("IM2WIN_IMPLICIT_KERNEL", "streamed")
+    assert conv.implicit_plan(d).kernel == 0
+    monkeypatch.setenv("IM2WIN_IMPLICIT_KERNEL", "rows")
+    assert conv.implicit_plan(d).kernel == 2
+    monkeypatch.delenv("IM2WIN_IMPLICIT_KERNEL")
+    assert conv.implicit_plan(d).as_dict() == first
+    # the window-form plan follows the same rule
+    p0 = conv.plan(d).as_dict()
+    monkeypatch.setenv("IM2WIN_ALGO", "window")
+    assert conv.plan(d).algo == 0 and p0["algo"] == 1
+    monkeypatch.delenv("IM2WIN_ALGO")
+    assert conv.plan(d).as_dict() == p0
+    # more descriptors than the cache holds: plans stay right
+    for n in range(1, 1200):
+        q = conv.plan(conv.make_desc(n, 16, 8, 8, 8, 3, 3, 1, 1, conv.F32))
+        assert q.rows_total == n * 8
+    assert conv.implicit_plan(d).as_dict() == first
