@@ -517,8 +517,8 @@ __global__ __launch_bounds__(kPipeThreads) void conv_implicit_pipe_kernel(const 
 // The paired form: one task per workgroup and a single LDS slot, small
 // enough (at most 80 KB) that two workgroups share a CU, so that one's loads
 // and stores overlap the other's contraction. All eight waves load a chunk
-// (filter block by the first four, patch units by all), then all eight
-// contract it (up to two 16-output blocks each, R * Wo <= 256).
+// (filter block by the first four, patch units by all), then the fewest
+// waves that hold two 16-output blocks each contract it (R * Wo <= 256).
 template <int KH, int KW, bool BF16, int V, bool MI>
 __global__ __launch_bounds__(kPipeThreads) __attribute__((amdgpu_waves_per_eu(4))) void conv_implicit_pair_kernel(const PipeKArgs a)
 {
@@ -537,8 +537,12 @@ __global__ __launch_bounds__(kPipeThreads) __attribute__((amdgpu_waves_per_eu(4)
     const int wave = tid >> 6;
     const int lane = tid & 63;
     const int outs = tk.nimg * tk.rw * a.Wo;
-    int b0, nb;
-    wave_blocks(wave, outs, b0, nb);
+    // blocks two to a wave over as few waves as that takes: a wave reads the
+    // same four filter fragments per tap for one block or two, and LDS reads,
+    // not products, bound this form; the idle waves still load
+    const int busy = min((((outs + 15) >> 4) + 1) >> 1, 8);
+    int b0 = 0, nb = 0;
+    if (wave < busy) wave_blocks_of(wave, busy, outs, b0, nb);
     int qa[4];
     task_bases<MI>(qa, b0, lane, outs, a.Wo, a.IW, tk.rw * a.Wo, tk.SL, a.stride);
     constexpr int MAXB = 2;                          // R * Wo <= 256: at most 2 blocks per wave
