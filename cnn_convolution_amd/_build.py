@@ -28,10 +28,8 @@ SOURCES = [
     os.path.join(CSRC, "kernels", "weight_stage.hip"),
     os.path.join(CSRC, "kernels", "gemm_valu.hip"),
     os.path.join(CSRC, "kernels", "gemm_mfma.hip"),
-    os.path.join(CSRC, "kernels", "gemm_mfma_resident.hip"),
     os.path.join(CSRC, "kernels", "gemm_mfma_dma.hip"),
     os.path.join(CSRC, "kernels", "conv_implicit.hip"),
-    os.path.join(CSRC, "kernels", "conv_implicit_fs.hip"),
     os.path.join(CSRC, "kernels", "conv_implicit_rows.hip"),
     os.path.join(CSRC, "kernels", "conv_implicit_narrow.hip"),
     os.path.join(CSRC, "kernels", "conv_implicit_pipe.hip"),

@@ -8,6 +8,7 @@
 
 #include <cstdint>
 #include <algorithm>
+#include <atomic>
 #include <cstring>
 #include <mutex>
 #include <vector>
@@ -28,7 +29,7 @@ struct Rec {
     int kind;
 };
 std::mutex g_prof_mu;
-bool g_prof_on = false;
+std::atomic<bool> g_prof_on{false};  // read without the mutex by every launch
 std::vector<Rec> g_recs;        // recorded since the last read
 std::vector<hipEvent_t> g_pool;  // reusable events
 
@@ -50,7 +51,7 @@ struct ProfScope {
     hipEvent_t a = nullptr, b = nullptr;
     ProfScope(hipStream_t s_, int kind_) : s(s_), kind(kind_)
     {
-        if (!g_prof_on) return;
+        if (!g_prof_on.load(std::memory_order_relaxed)) return;
         std::lock_guard<std::mutex> lk(g_prof_mu);
         a = pool_get();
         b = pool_get();
@@ -135,7 +136,7 @@ hipError_t launch_gemm(const conv2d_desc_t &d, const conv2d_plan_t &p, const Lay
     ga.bf16 = d.dtype == CONV2D_BF16 ? 1 : 0;
     ga.ablate = p.gemm_ablate;
     if (p.gemm_kernel == 3) return launch_gemm_mfma_dma(ga, s);
-    return p.gemm_kernel == 2 ? launch_gemm_mfma_resident(ga, s) : launch_gemm_mfma(ga, s);
+    return launch_gemm_mfma(ga, s);
 }
 
 ImplicitArgs implicit_args(const conv2d_desc_t &d, const conv2d_implicit_plan_t &p, const void *x,
@@ -168,9 +169,9 @@ ImplicitArgs implicit_args(const conv2d_desc_t &d, const conv2d_implicit_plan_t 
     a.bf16 = d.dtype == CONV2D_BF16 ? 1 : 0;
     a.f32 = d.dtype == CONV2D_F32 ? 1 : 0;
     a.narrow_cp = p.kernel == 3 ? p.stages : 0;
-    // filter-stationary form: workgroups per 64-row filter block; pipelined
-    // row-block form: the persistent workgroups
-    a.fs_groups = p.kernel == 4 ? int(p.tiles) : int(p.tiles / ((d.Cout + 63) / 64));
+    // persistent forms: the pipelined row-block kernel's workgroups, the narrow
+    // kernel's workgroups per 64-row filter block
+    a.groups = p.kernel == 4 ? int(p.tiles) : int(p.tiles / ((d.Cout + 63) / 64));
     a.images = p.kernel == 4 ? p.images : 0;
     return a;
 }
@@ -180,7 +181,8 @@ hipError_t launch_implicit(const conv2d_implicit_plan_t &p, const ImplicitArgs &
     if (p.kernel == 2) return launch_conv_implicit_rows(a, s);
     if (p.kernel == 3) return launch_conv_implicit_narrow(a, s);
     if (p.kernel == 4) return launch_conv_implicit_pipe(a, s);
-    return p.kernel == 1 ? launch_conv_implicit_fs(a, s) : launch_conv_implicit(a, s);
+    if (p.kernel == 0) return launch_conv_implicit(a, s);
+    return hipErrorInvalidValue;                     // no such kernel
 }
 
 // implicit form: (a3) the filter into the window's K order (kw, kh, ci)
@@ -431,7 +433,7 @@ conv2d_status_t im2win_implicit_gemm(const conv2d_desc_t *d, const void *x, cons
 conv2d_status_t conv2d_profile_enable(int32_t on)
 {
     std::lock_guard<std::mutex> lk(g_prof_mu);
-    g_prof_on = on != 0;
+    g_prof_on.store(on != 0, std::memory_order_relaxed);
     return CONV2D_OK;
 }
 

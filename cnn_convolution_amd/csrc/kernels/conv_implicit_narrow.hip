@@ -461,7 +461,7 @@ hipError_t launch_conv_implicit_narrow(const ImplicitArgs &h, hipStream_t s)
         return hipErrorInvalidValue;
     // workgroups: co_blocks x groups, each group walking a contiguous range of
     // the N * row_groups row blocks with its filter block staged once
-    a.groups = h.fs_groups;
+    a.groups = h.groups;
     int ntasks = h.N * a.row_groups;
     const int64_t blocks = int64_t(a.co_blocks) * a.groups;
     if (a.groups < 1 || a.groups > ntasks || blocks > 0x7fffffff) return hipErrorInvalidValue;

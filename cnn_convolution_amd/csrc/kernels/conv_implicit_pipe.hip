@@ -160,9 +160,14 @@ template <int V, bool MI>
 __device__ __forceinline__ ChunkGeom chunk_geom(const PipeKArgs &a, const PipeTask &tk)
 {
     ChunkGeom g;
-    const int r_lo = max(tk.ih0, 0), r_hi = min(tk.ih0 + tk.SL, a.H);
+    // rows [r_lo, r_hi) of the image; both clamped into [0, H], so a task that
+    // lies wholly in the padding below the image (pad > KH) gets the empty run
+    // [H*W, H*W), which is a whole number of V-position units (H*W % V == 0):
+    // no unit is loaded
+    const int r_lo = min(max(tk.ih0, 0), a.H);
+    const int r_hi = max(min(tk.ih0 + tk.SL, a.H), r_lo);
     g.p_lo = r_lo * a.W;
-    g.p_hi = max(r_hi, r_lo) * a.W;
+    g.p_hi = r_hi * a.W;
     g.j_lo = g.p_lo / V;
     g.units1 = 4 * ((g.p_hi + V - 1) / V - g.j_lo);
     g.units = MI ? g.units1 * tk.nimg : g.units1;
@@ -598,7 +603,7 @@ hipError_t launch_conv_implicit_pipe(const ImplicitArgs &h, hipStream_t s)
         (h.Wo - 1) * h.stride + h.KW > h.IW || h.IR != img * ((h.R - 1) * h.stride + h.KH) ||
         (img > 1 && h.R != h.Ho) ||
         int64_t(h.Cin) * h.H * h.W >= (int64_t(1) << 31) ||
-        (!pair && h.fs_groups < 1) || (h.stages != 1 && h.stages != 2) ||
+        (!pair && h.groups < 1) || (h.stages != 1 && h.stages != 2) ||
         !((h.KH == 3 && h.KW == 3) || (h.KH == 1 && h.KW == 1)))
         return hipErrorInvalidValue;
     PipeKArgs a;
@@ -628,7 +633,7 @@ hipError_t launch_conv_implicit_pipe(const ImplicitArgs &h, hipStream_t s)
     a.slot_halves = taps * 64 * kChunkC + a.SLmax * a.IW * kChunkC;
     const size_t lds = size_t(pair ? pair_lds_bytes(taps, a.SLmax, a.IW) : pipe_lds_bytes(taps, a.SLmax, a.IW));
     if (lds > size_t(kImplicitMaxLdsBytes)) return hipErrorInvalidValue;
-    const int groups = pair ? a.ntasks : int(std::min<int64_t>(h.fs_groups, ntasks));
+    const int groups = pair ? a.ntasks : int(std::min<int64_t>(h.groups, ntasks));
     const int hw = h.H * h.W;
     void *args[] = {&a};
     const bool k3 = h.KH == 3;

@@ -65,10 +65,6 @@ struct MfmaGemmArgs {
     int ablate;             // direct-to-LDS kernel: ablation bits (0: as planned)
 };
 hipError_t launch_gemm_mfma(const MfmaGemmArgs &a, hipStream_t s);
-// filter-resident form: a 64-row filter block stays in LDS for the whole K,
-// window fragments go straight to registers; tile_n = columns per workgroup
-// (64, 128 or 256), tile_m = 64
-hipError_t launch_gemm_mfma_resident(const MfmaGemmArgs &a, hipStream_t s);
 // direct-to-LDS form: tile_m x tile_n with wm waves along M, K stages of 64;
 // only for windows whose length krun equals kstage, a multiple of 64
 hipError_t launch_gemm_mfma_dma(const MfmaGemmArgs &a, hipStream_t s);
@@ -88,13 +84,10 @@ struct ImplicitArgs {
     int bf16;
     int f32;                // fp32 x, w (row-block and narrow kernels)
     int narrow_cp;          // narrow kernel: channels per window position (4 or 8)
-    int fs_groups;          // filter-stationary form: workgroups per 64-row filter block
+    int groups;             // persistent forms (narrow, pipelined row-block): workgroups
     int images;             // pipelined row-block form: whole images per task (0 or 1: row tasks)
 };
 hipError_t launch_conv_implicit(const ImplicitArgs &a, hipStream_t s);
-// filter-stationary form (K = KW*KH*Cin of 64, 128, 256 or 576): a 64-row
-// filter block in registers, persistent workgroups over contiguous tiles
-hipError_t launch_conv_implicit_fs(const ImplicitArgs &a, hipStream_t s);
 // row-block form (fp16/bf16: Cin = 64, W % 8 == 0; fp32: Cin % 32 == 0,
 // W % 4 == 0; stride 1, Wo <= 64, 1x1 or 3x3): R whole output rows of one
 // image per workgroup, raw filter and input rows resident in LDS; wst is w

@@ -141,46 +141,13 @@ static void pick_mfma_tile(const conv2d_desc_t &d, int64_t cols, int64_t kgran, 
     p->gemm_wave_m = wm;
 }
 
-// Filter-resident matrix-core form: a 64-row block of the staged filter
-// stays in LDS for the whole K and the window fragments go straight to
-// registers. Opt-in (the block must fit: short filter rows, small
-// Cin*KH*KW). IM2WIN_MFMA_KERNEL=tiled|resident, IM2WIN_MFMA_RESIDENT_N
-// (64, 128 or 256 columns per workgroup) and IM2WIN_MFMA_RESIDENT_PF (4, 8
-// or 16 K steps in flight) override the choice for sweeps.
-static void pick_mfma_resident(const conv2d_desc_t &d, int64_t cols, conv2d_plan_t *p) {
-    (void)d;
-    const bool fits = 64 * (p->K_stage + 8) * 2 <= kResidentMaxLdsBytes;
-    bool use = false;     // measured no faster than the tiled kernel on any layer of the sweep
-    if (const char *k = std::getenv("IM2WIN_MFMA_KERNEL")) {
-        if (std::strcmp(k, "tiled") == 0) use = false;
-        if (std::strcmp(k, "resident") == 0) use = fits;
-    }
-    if (!use) return;
-    int n = ceil_div(d.Cout, 64) * ceil_div(cols, 128) >= 512 ? 128 : 64;
-    if (const char *e = std::getenv("IM2WIN_MFMA_RESIDENT_N")) {
-        const int v = std::atoi(e);
-        if (v == 64 || v == 128 || v == 256) n = v;
-    }
-    int pf = 8;
-    if (const char *e = std::getenv("IM2WIN_MFMA_RESIDENT_PF")) {
-        const int v = std::atoi(e);
-        if (v == 4 || v == 8 || v == 16) pf = v;
-    }
-    p->gemm_kernel = 2;
-    p->gemm_tile_m = 64;
-    p->gemm_tile_n = n;
-    p->gemm_kslice = pf;      // this form: K steps of window fragments in flight per wave
-    p->gemm_ksplit = 1;
-    p->gemm_wave_m = 1;
-}
-
 // Direct-to-LDS matrix-core form: whole 64-element K stages (the window
 // length equals the staged filter row, a multiple of 64). Taken wherever it
 // applies: it measured faster than the tiled kernel on the layers of the
 // sweep. Tile rule from the same sweep: one 64-row block when Cout <= 64 (128
 // columns, or 64 when that leaves fewer tiles than CUs); 64 x 64 for Cout >=
-// 256 with a deep K; else 128 x 64. IM2WIN_MFMA_KERNEL=tiled|resident turns
-// it off; IM2WIN_MFMA_DMA_TILE="MB,NB,WM" overrides the tile for sweeps.
+// 256 with a deep K; else 128 x 64. IM2WIN_MFMA_KERNEL=tiled turns it
+// off; IM2WIN_MFMA_DMA_TILE="MB,NB,WM" overrides the tile for sweeps.
 static const int kDmaTiles[][3] = {
     {64, 128, 1}, {64, 64, 2}, {128, 64, 2}, {128, 128, 2}, {128, 128, 1}, {64, 256, 1},
 };
@@ -194,7 +161,7 @@ static bool dma_tile_known(int m, int n, int wm) {
 static void pick_mfma_dma(const conv2d_desc_t &d, int64_t krun, int64_t cols, conv2d_plan_t *p) {
     if (krun != p->K_stage || p->K_stage % 64 != 0) return;
     if (const char *k = std::getenv("IM2WIN_MFMA_KERNEL"))
-        if (std::strcmp(k, "tiled") == 0 || std::strcmp(k, "resident") == 0) return;
+        if (std::strcmp(k, "tiled") == 0) return;
     int m, n, wm;
     if (d.Cout <= 64) {
         m = 64; wm = 1; n = 128;
@@ -324,7 +291,6 @@ static conv2d_status_t compute_plan(const conv2d_desc_t &d, conv2d_plan_t *p) {
     if (p->path == 1) {
         pick_mfma_tile(d, p->rows_per_chunk * p->Wo, mfma_kgran(d.KW * d.KH * g.Cin_pad), p);
         p->gemm_kernel = 1;
-        pick_mfma_resident(d, p->rows_per_chunk * p->Wo, p);
         pick_mfma_dma(d, d.KW * d.KH * g.Cin_pad, p->rows_per_chunk * p->Wo, p);
         pick_algo(d, p);
     } else {
@@ -347,52 +313,6 @@ static conv2d_status_t compute_plan(const conv2d_desc_t &d, conv2d_plan_t *p) {
 // IM2WIN_IMPLICIT_TILE="MB,NB,WM,R,WB" overrides the choice (for sweeps).
 static const int kImplicitTiles[][3] = {{64, 64, 1}, {64, 128, 1}, {128, 64, 2}, {128, 128, 2}};
 
-// Filter-stationary implicit kernel: K = KW*KH*Cin of 64, 128, 256 or 576
-// (its compiled forms); 64 GEMM columns per tile for K = 576 (the filter
-// block takes 144 registers per lane), 128 otherwise; the loads of the next
-// tile's patch are held in registers (512 row chunks of 8 channels x 8
-// columns when W is a multiple of 8, else 1536 gathered 16-byte vectors); one
-// workgroup per CU,
-// each walking a contiguous range of tiles of one 64-row filter block.
-// Opt-in (IM2WIN_IMPLICIT_KERNEL=stationary): on the measured layers it was
-// no faster than the streamed kernel (with one wave per SIMD, the per-tile
-// address arithmetic and patch packing are not hidden behind other waves).
-static void pick_implicit_fs(const conv2d_desc_t &d, int64_t Ho, int64_t Wo, conv2d_implicit_plan_t *p) {
-    const int64_t K = d.KW * d.KH * d.Cin;
-    if (K != 64 && K != 128 && K != 256 && K != 576) return;
-    const char *e = std::getenv("IM2WIN_IMPLICIT_KERNEL");
-    if (!e || std::strcmp(e, "stationary") != 0) return;
-    const int64_t nb = K == 576 ? 64 : 128;
-    const int64_t nblk = d.Cin / 64;
-    int64_t r, wb;
-    if (Wo >= nb) { r = 1; wb = nb; }
-    else { const int64_t rmax = std::min<int64_t>(Ho, nb / Wo); r = ceil_div(Ho, ceil_div(Ho, rmax)); wb = Wo; }
-    auto fits = [&](int64_t rr, int64_t ww) {
-        const int64_t ir = (rr - 1) * d.stride + d.KH, iw = (ww - 1) * d.stride + d.KW;
-        // held in registers: 16-byte row chunks of 8 channels (W a multiple of
-        // 8), or gathered patch vectors
-        const bool held = d.W % 8 == 0 ? nblk * 8 * ir * ((iw + 7) / 8 + 1) <= 512
-                                       : nblk * ir * iw * 8 <= 1536;
-        return held && implicit_fs_lds_bytes(d.Cin, ir, iw) <= kImplicitMaxLdsBytes;
-    };
-    while (!fits(r, wb) && r > 1) --r;
-    while (!fits(r, wb) && wb > 8) wb = (wb + 1) / 2;
-    if (!fits(r, wb)) return;
-    const int64_t tiles_m = ceil_div(d.Cout, 64);
-    const int64_t col_tiles = d.N * ceil_div(Ho, r) * ceil_div(Wo, wb);
-    const int64_t groups = std::min<int64_t>(col_tiles, std::max<int64_t>(1, 256 / tiles_m));
-    p->kernel = 1;
-    p->tile_m = 64;
-    p->tile_n = int32_t(nb);
-    p->wave_m = 1;
-    p->rows_per_tile = int32_t(r);
-    p->cols_per_tile = int32_t(wb);
-    p->patch_rows = int32_t((r - 1) * d.stride + d.KH);
-    p->patch_cols = int32_t((wb - 1) * d.stride + d.KW);
-    p->lds_bytes = implicit_fs_lds_bytes(d.Cin, p->patch_rows, p->patch_cols);
-    p->tiles = groups * tiles_m;
-}
-
 // Row-block implicit kernel: stride 1, output rows of at most 64 columns, a
 // 1x1 or 3x3 filter; fp16/bf16 with 64 input channels on rows of 8k elements,
 // or any multiple of 64 channels where an image has at least 128 outputs;
@@ -401,7 +321,7 @@ static void pick_implicit_fs(const conv2d_desc_t &d, int64_t Ho, int64_t Wo, con
 // output channels, with the raw filter and the RW + KH - 1 input rows in LDS;
 // no staged filter. RW minimises the rounds of workgroups over the CUs times
 // the busiest SIMD's blocks plus a fixed set-up.
-// Default where it applies; IM2WIN_IMPLICIT_KERNEL=streamed|stationary (or a
+// Default where it applies; IM2WIN_IMPLICIT_KERNEL=streamed (or a
 // tile in IM2WIN_IMPLICIT_TILE) selects the other kernels; IM2WIN_IMPLICIT_ROWS
 // sets RW.
 static void pick_implicit_rows(const conv2d_desc_t &d, int64_t Ho, int64_t Wo, conv2d_implicit_plan_t *p) {
@@ -805,7 +725,6 @@ static conv2d_status_t compute_implicit_plan(const conv2d_desc_t &d, conv2d_impl
     p->lds_bytes = implicit_lds_bytes(best.mb, p->patch_rows, p->patch_cols, ns);
     p->tiles = ceil_div(d.Cout, best.mb) * d.N * ceil_div(Ho, best.r) * ceil_div(Wo, best.wb);
     if (p->tiles > 0x7fffffff) return CONV2D_ERR_INVALID_DESC;
-    pick_implicit_fs(d, Ho, Wo, p);
     pick_implicit_rows(d, Ho, Wo, p);
     // the one-block row kernel stays where it applies (64 channels on rows of
     // 8k elements, measured faster than both pipelined forms); elsewhere the

@@ -23,18 +23,12 @@ constexpr int kValuMt = 16;
 constexpr int kValuNt = 4;
 constexpr int kValuThreads = 256;
 
-// filter-resident matrix-core window-GEMM: LDS bytes one workgroup may hold
-// for its 64 x (K_stage + 8) filter block (two workgroups still fit a CU)
-constexpr int64_t kResidentMaxLdsBytes = 80 * 1024;
-
 // implicit matrix-core convolution: LDS of one workgroup = ns filter stage
 // buffers of mb rows x 128 bytes + a patch of ir x iw positions x 128 bytes
 inline int64_t implicit_lds_bytes(int64_t mb, int64_t ir, int64_t iw, int64_t ns) {
     return (ns * mb + ir * iw) * 128;
 }
 constexpr int64_t kImplicitMaxLdsBytes = 160 * 1024;   // one workgroup per CU
-// filter-stationary implicit form: two patch buffers, all channel blocks
-inline int64_t implicit_fs_lds_bytes(int64_t cin, int64_t ir, int64_t iw) { return 2 * (cin / 64) * ir * iw * 128; }
 constexpr int64_t kImplicitPairLdsBytes = 80 * 1024;   // two workgroups per CU
 // row-block implicit form: the filter block (8 KB per tap) + sl input rows of
 // iw positions x 128 bytes

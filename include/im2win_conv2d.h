@@ -16,13 +16,20 @@
  * M = Cout, N = N*Ho*Wo, K = Cin*KH*KW); the padded output extent of
  * "Unifying Convolutions and GEMM", Sec. 5.
  *
- * How it runs: the input is repacked, one chunk of window rows (n, ho) at a
- * time, into the im2win window tensor held in the caller's workspace; the
- * filter is restaged once per call into the window's K order; a window-GEMM
- * kernel contracts each chunk into y. fp32 inputs run on the vector ALUs,
- * fp16/bf16 inputs on the matrix cores with fp32 accumulation. The chunk size
- * keeps the workspace at most 1/KW of the im2col buffer whenever one window
- * row fits in that budget.
+ * How it runs: conv2d_fwd takes, per layer, one of two forms of the same
+ * method (conv2d_plan_t.algo names which):
+ *   - the implicit form (every measured layer): one kernel builds the window
+ *     rows of each output tile in LDS straight from x (the rows of Eq. (2))
+ *     and contracts them against the filter on the matrix cores with fp32
+ *     accumulation (fp32 inputs on the matrix cores' fp32 products); the
+ *     workspace is at most a staged copy of the filter, often none;
+ *   - the window form: the input is repacked, one chunk of window rows
+ *     (n, ho) at a time, into the im2win window tensor held in the caller's
+ *     workspace, the filter is restaged once per call into the window's K
+ *     order, and a window-GEMM kernel contracts each chunk into y (fp32 on the
+ *     vector ALUs, fp16/bf16 on the matrix cores). The chunk size keeps the
+ *     workspace at most 1/KW of the im2col buffer whenever one window row fits
+ *     in that budget.
  *
  * Layouts: x, w, y are dense, contiguous NCHW: x [N][Cin][H][W] of `dtype`,
  * w [Cout][Cin][KH][KW] of `dtype`, y [N][Cout][Ho][Wo] of float (fp32 for
@@ -56,7 +63,8 @@ extern "C" {
 
 /* Storage type of x and w (y is always fp32). */
 typedef enum {
-    CONV2D_F32 = 0,   /* IEEE binary32; runs on the vector ALUs               */
+    CONV2D_F32 = 0,   /* IEEE binary32; fp32 products on the matrix cores (row-
+                         block and narrow kernels) or the vector ALUs           */
     CONV2D_F16 = 1,   /* IEEE binary16; matrix cores, fp32 accumulation        */
     CONV2D_BF16 = 2   /* bfloat16; matrix cores, fp32 accumulation             */
 } conv2d_dtype_t;
@@ -119,14 +127,12 @@ typedef struct {
     int64_t ws_target_bytes;      /* im2col_bytes / KW                            */
     int32_t meets_ws_target;      /* ws_bytes <= ws_target_bytes                  */
     int32_t gemm_tile_m, gemm_tile_n;  /* output tile of one workgroup (M x N)     */
-    int32_t gemm_kslice;          /* kernel 1: K per LDS stage per wave group;
-                                     kernel 2: K steps of window fragments in flight */
+    int32_t gemm_kslice;          /* K per LDS stage per wave group (kernels 1, 3) */
     int32_t gemm_ksplit;          /* wave groups splitting K inside a workgroup    */
     int32_t gemm_kernel;          /* 0: vector ALU, 1: matrix core via LDS tiles,
-                                     2: matrix core, filter block resident in LDS and
-                                        window fragments straight to registers,
                                      3: matrix core, tiles copied memory -> LDS
-                                        directly (whole 64-element K stages)         */
+                                        directly (whole 64-element K stages);
+                                     (2 is not used)                                */
     int32_t gemm_wave_m;          /* waves along M in a wave group (matrix path)   */
     int32_t algo;                 /* what conv2d_fwd runs: 0 the window tensor in ws
                                      (pack + window-GEMM per chunk), 1 the implicit
@@ -152,7 +158,13 @@ conv2d_status_t conv2d_plan(const conv2d_desc_t *d, conv2d_plan_t *out);
  * below where it measured faster for that layer class.
  * ws: device buffer of at least conv2d_workspace_size(d) bytes, 256-byte
  * aligned (NULL allowed only when that size is 0); its contents on return
- * are unspecified. x, w, y: 16-byte aligned device pointers. */
+ * are unspecified. The staged filter and the window chunk inside it start on
+ * 256-byte boundaries of ws, so every window row and filter row the kernels
+ * copy straight into LDS starts 16-byte aligned whatever the chunk's rows;
+ * PyTorch's device allocations are 512-byte aligned. x, w, y: 16-byte
+ * aligned device pointers. Errors: CONV2D_ERR_HIP when a launch fails (the
+ * runtime refused it, or the kernel's own launch check did); launches of
+ * earlier steps of the same call may then have been enqueued. */
 conv2d_status_t conv2d_fwd(const conv2d_desc_t *d, const void *x, const void *w, float *y,
                            void *ws, void *stream);
 
@@ -209,10 +221,7 @@ typedef struct {
     int32_t patch_rows;           /* input rows held per tile: (rows-1)*stride + KH */
     int32_t patch_cols;           /* input columns held: (cols-1)*stride + KW       */
     int32_t kernel;               /* 0: the filter streamed through LDS per K stage,
-                                     one workgroup per tile; 1 (opt-in): filter-
-                                     stationary, KW*KH*Cin of 64, 128, 256 or 576:
-                                     a 64-row filter block in registers, workgroups
-                                     that each walk a contiguous range of tiles;
+                                     one workgroup per tile; (1 is not used);
                                      2 (default where it applies: Cin = 64,
                                      stride 1, W % 8 == 0, Wo <= 64, 3x3 or 1x1):
                                      row-block, rows_per_tile whole output rows

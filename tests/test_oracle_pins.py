@@ -38,20 +38,20 @@ def _torch_conv(x, w, s, p):
 
 
 def _im2col(x, KH, KW, s, p):
-    """Lowering in the style of the pages' im2col: one row per filter tap, one
-    column per output position; returns [N][Cin*KH*KW][Ho*Wo]."""
+    """Lowering as one gather: entry ((c, kh, kw), (ho, wo)) of image n is
+    x[n, c, ho*s + kh - p, wo*s + kw - p], or zero where that index leaves the
+    image (zero padding). Returns [N][Cin*KH*KW][Ho*Wo]."""
     N, C, H, W = x.shape
-    xp = np.pad(x, ((0, 0), (0, 0), (p, p), (p, p)))
     Ho = (H + 2 * p - KH) // s + 1
     Wo = (W + 2 * p - KW) // s + 1
-    cols = np.empty((N, C * KH * KW, Ho * Wo), dtype=x.dtype)
-    i = 0
-    for c in range(C):
-        for kh in range(KH):
-            for kw in range(KW):
-                cols[:, i] = xp[:, c, kh:kh + s * Ho:s, kw:kw + s * Wo:s].reshape(N, -1)
-                i += 1
-    return cols, Ho, Wo
+    kh, kw, ho, wo = np.meshgrid(np.arange(KH), np.arange(KW), np.arange(Ho), np.arange(Wo),
+                                 indexing="ij")
+    ih = ho * s + kh - p                          # [KH][KW][Ho][Wo] input row of each entry
+    iw = wo * s + kw - p
+    inside = (ih >= 0) & (ih < H) & (iw >= 0) & (iw < W)
+    g = x[:, :, np.clip(ih, 0, H - 1), np.clip(iw, 0, W - 1)]   # [N][C][KH][KW][Ho][Wo]
+    g = np.where(inside, g, np.zeros((), x.dtype))
+    return g.reshape(N, C * KH * KW, Ho * Wo), Ho, Wo
 
 
 def _im2col_conv(x, w, s, p):
