@@ -1,25 +1,30 @@
 #!/usr/bin/env python3
 """Forward-convolution benchmark on one MI355X.
 
-    python bench.py [--gpus 1] [--steps 50] [--warmup 20] [--config resnet3x3] [--dtype f16]
+    python bench.py [--gpus 1] [--steps 50] [--warmup 20]
+    python bench.py --config NAME [--dtype DT]     # one layer, its own line
 
 A step is one conv2d_fwd call in the form the library plans for the layer:
 either the window tensor (filter staging, then for every chunk of window rows
-the im2win pack and the window-GEMM) or the implicit form (filter staging,
-then one kernel that builds the window rows in LDS and contracts them), each
-writing the fp32 output. Where a layer has both forms the other one is timed
-too and reported under "other_form". Inputs are seeded synthetic tensors
-already resident in device memory. The timed region
-is `steps` back-to-back calls on one stream, bracketed by device syncs and
-HIP events; warm-up calls run first and caches stay warm (50 timed calls
-after 20 warm-up ones, the protocol of the fused-WTConv measurements).
+the im2win pack and the window-GEMM) or the implicit form (one kernel that
+builds the window rows in LDS and contracts them, after a small filter
+staging launch where the plan keeps a staged filter), each writing the fp32
+output. Inputs are seeded synthetic tensors already resident in device
+memory. The timed region is `steps` back-to-back calls on one stream,
+bracketed by device syncs and HIP events; warm-up calls run first and caches
+stay warm (50 timed calls after 20 warm-up ones, the protocol of the
+fused-WTConv measurements).
 
-Prints ONE JSON line: TFLOPS (2 * multiply-adds / time, padded taps
-included) of the headline dtype, its fraction of the MI355X peak, the
-roofline of the dominant kernel (per-kernel HIP events around every launch
-in a second timed pass), the other dtype variants of the same layer, a
-parity check of the timed output against the CPU oracle on sampled points,
-and the CPU oracle's own throughput on the host cores as a baseline.
+The default run prints ONE JSON line. Its headline is the ResNet-style 3x3
+layer in fp16 (TFLOPS = 2 * multiply-adds / time, padded taps included, and
+the fraction of the MI355X peak); "layers" holds every layer configuration
+and dtype (tiny, resnet3x3 f32/f16, deep3x3 bf16, stem7x7 f32/f16, mix5x5,
+mix512, mix3x3s2, mix1x1 f16), each with the roofline of its dominant kernel
+(back-to-back launches of that kernel alone between HIP events), the HBM
+traffic from committed counter summaries, workspace bytes against the im2col
+buffer, and a parity check of its timed output against the CPU oracle on
+sampled points. The CPU-baseline leg -- the only part that uses the oracle,
+run after all GPU timing -- times the fp64 oracle on the host cores.
 """
 from __future__ import annotations
 
@@ -48,16 +53,13 @@ def _say(msg):
 
 # sources that decide what the dominant kernel of a call does, per kernel id
 # (0: fp32 vector-ALU window-GEMM, 1: tiled matrix-core window-GEMM,
-# 2: filter-resident matrix-core window-GEMM, 3: direct-to-LDS matrix-core
-# window-GEMM, 4: implicit convolution, window rows built in LDS, 5: the same
-# with the filter held in registers, 6: the row-block implicit kernel, filter
+# 3: direct-to-LDS matrix-core window-GEMM, 4: implicit convolution, window
+# rows built in LDS, filter streamed, 6: the row-block implicit kernel, filter
 # and input rows resident in LDS, 7: the narrow-channel implicit kernel, 8: the
 # pipelined row-block kernel, 32-channel K chunks double-buffered by loader waves)
 GEMM_SOURCES = {
     0: ["cnn_convolution_amd/csrc/kernels/gemm_valu.hip"],
     1: ["cnn_convolution_amd/csrc/kernels/gemm_mfma.hip",
-        "cnn_convolution_amd/csrc/kernels/tile_map.hpp"],
-    2: ["cnn_convolution_amd/csrc/kernels/gemm_mfma_resident.hip",
         "cnn_convolution_amd/csrc/kernels/tile_map.hpp"],
     3: ["cnn_convolution_amd/csrc/kernels/gemm_mfma_dma.hip",
         "cnn_convolution_amd/csrc/kernels/lds_dma.hpp",
@@ -65,8 +67,6 @@ GEMM_SOURCES = {
     4: ["cnn_convolution_amd/csrc/kernels/conv_implicit.hip",
         "cnn_convolution_amd/csrc/kernels/lds_dma.hpp",
         "cnn_convolution_amd/csrc/kernels/tile_map.hpp"],
-    5: ["cnn_convolution_amd/csrc/kernels/conv_implicit_fs.hip",
-        "cnn_convolution_amd/csrc/kernels/lds_dma.hpp"],
     6: ["cnn_convolution_amd/csrc/kernels/conv_implicit_rows.hip",
         "cnn_convolution_amd/csrc/kernels/out_blocks.hpp",
         "cnn_convolution_amd/csrc/kernels/lds_dma.hpp",
@@ -79,8 +79,8 @@ GEMM_SOURCES = {
         "cnn_convolution_amd/csrc/kernels/out_blocks.hpp",
         "cnn_convolution_amd/csrc/kernels/lds_dma.hpp"],
 }
-GEMM_KERNEL_NAMES = {0: "gemm_valu_f32", 1: "gemm_mfma", 2: "gemm_mfma_resident",
-                     3: "gemm_mfma_dma", 4: "conv_implicit", 5: "conv_implicit_fs",
+GEMM_KERNEL_NAMES = {0: "gemm_valu_f32", 1: "gemm_mfma",
+                     3: "gemm_mfma_dma", 4: "conv_implicit",
                      6: "conv_implicit_rows", 7: "conv_implicit_narrow", 8: "conv_implicit_pipe"}
 COPY_BYTES = 256 << 20     # calibration copy for the HBM byte counters
 
@@ -101,7 +101,7 @@ def dominant_key(d, plan):
     import cnn_convolution_amd as conv
     if plan.algo == 1:
         ip = conv.implicit_plan(d)
-        kid = {0: 4, 1: 5, 2: 6, 3: 7, 4: 8}[ip.kernel]
+        kid = {0: 4, 2: 6, 3: 7, 4: 8}[ip.kernel]
         # the pipelined row-block kernel: stages 2 = persistent, 1 = paired form
         form = f"/s{ip.stages}" if ip.kernel == 4 else ""
         return (kid, f"i{ip.kernel}:{ip.tile_m}x{ip.tile_n}/{ip.wave_m}/r{ip.rows_per_tile}/"
@@ -296,13 +296,11 @@ def _time_variant(cfg, dt, steps, warmup, dev):
     conv.conv2d_into(xd, wd, y, wsarg, cfg.stride, cfg.pad)   # y whole again for the parity check
     torch.cuda.synchronize()
 
-    # parity of the timed output on sampled points
-    import oracle
+    # the sampled outputs of the timed call, for the parity check that the
+    # CPU-baseline leg runs (the only place the oracle is used)
     rng = np.random.default_rng(cfg.seed)
-    idx = rng.integers(0, y.numel(), 2000)
+    idx = sample_points(cfg, plan, rng)
     got = y.reshape(-1)[torch.from_numpy(idx).to(dev)].double().cpu().numpy()
-    ref = oracle.conv2d_points(x, w, cfg.stride, cfg.pad, idx)
-    rel = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
 
     flops = plan.flops
     tflops = flops / (ms * 1e-3) / 1e12
@@ -346,21 +344,73 @@ def _time_variant(cfg, dt, steps, warmup, dev):
         "chunk_pack_us": pack_us, "chunk_gemm_us": kern_us if plan.algo == 0 else None,
         "kernel_us": kern_us, "chunk_rows": rows,
         "pct_of_peak": 100.0 * tflops / peak, "peak_tflops": peak,
-        "rel_l2_sampled": rel, "parity_ok": rel <= TOL[dt],
+        "sample_idx": idx, "sample_got": got,
         "ws_bytes": plan.ws_bytes, "im2col_bytes": plan.im2col_bytes,
         "ws_over_im2col": plan.ws_bytes / plan.im2col_bytes, "ws_target": 1.0 / cfg.KW,
         "n_chunks": n_chunks, "kernels": kern, "roofline": roof,
     }
 
 
-def cpu_baseline(cfg, dt, min_seconds=10.0):
-    """The fp64 oracle on the host cores over a bounded sample of the layer:
-    whole images of the same batch, repeated until about min_seconds."""
+def sample_points(cfg, plan, rng, count=2000):
+    """Flat output indices checked against the oracle: random outputs plus the
+    first and last output of every (first/last image, first/last channel)
+    plane's border rows."""
+    ho, wo = plan.Ho, plan.Wo
+    idx = set(rng.integers(0, cfg.N * cfg.Cout * ho * wo, count).tolist())
+    for n in {0, cfg.N - 1}:
+        for co in {0, cfg.Cout - 1}:
+            for h in {0, ho - 1}:
+                for c in {0, wo - 1}:
+                    idx.add(((n * cfg.Cout + co) * ho + h) * wo + c)
+    return np.array(sorted(idx), dtype=np.int64)
+
+
+def host_cpu():
+    """Threads the oracle runs with (OMP_NUM_THREADS, else every core this
+    process may run on), the host's core count and CPU model."""
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count() or 1
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or avail
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return threads, {"host_nproc": os.cpu_count(), "host_affinity": avail, "cpu_model": model,
+                     "omp_num_threads": os.environ.get("OMP_NUM_THREADS")}
+
+
+def cpu_leg(cfg, dt, res, min_seconds):
+    """The CPU-baseline leg, the only part of the benchmark that uses the
+    oracle (after every GPU timing is done):
+    * the fp64 oracle's throughput on the host cores over a bounded sample of
+      the layer (whole images of the same batch, repeated until about
+      min_seconds), reported as a baseline only;
+    * the parity of the timed call: its sampled outputs against the oracle
+      point by point, relative L2 over the sample and the per-output bound
+      |y - ref| <= 2 (K + 1) 2^-24 sum|x w| of any fp32 summation order.
+    Returns (cpu_baseline, parity)."""
     import oracle
-    import workloads
-    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or min(16, os.cpu_count() or 1)
+    threads, host = host_cpu()
     x, w = layer_inputs(cfg, dt)
-    per_img = 2 * cfg.Cout * cfg.out_hw()[0] * cfg.out_hw()[1] * cfg.Cin * cfg.KH * cfg.KW
+    idx, got = res["sample_idx"], res["sample_got"]
+    ref = oracle.conv2d_points(x, w, cfg.stride, cfg.pad, idx, nthreads=threads)
+    mag = oracle.conv2d_points(x.abs(), w.abs(), cfg.stride, cfg.pad, idx, nthreads=threads)
+    K = cfg.Cin * cfg.KH * cfg.KW
+    bound = 2.0 * (K + 1) * 2.0 ** -24 * mag
+    err = np.abs(got - ref)
+    rel = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+    ratio = float(np.max(err / np.where(bound > 0, bound, 1.0)))
+    parity = {"rel_l2_sampled": rel, "max_err_over_bound": ratio, "points": int(idx.size),
+              "parity_ok": bool(rel <= TOL[dt] and np.all(err <= bound))}
+    ho, wo = cfg.out_hw()
+    per_img = 2 * cfg.Cout * ho * wo * cfg.Cin * cfg.KH * cfg.KW
     # size the sample from a one-image probe
     t = time.perf_counter()
     oracle.conv2d(x[:1], w, cfg.stride, cfg.pad, nthreads=threads)
@@ -371,10 +421,29 @@ def cpu_baseline(cfg, dt, min_seconds=10.0):
     for _ in range(reps):
         oracle.conv2d(x[:imgs], w, cfg.stride, cfg.pad, nthreads=threads)
     el = time.perf_counter() - t
-    return {"value": per_img * imgs * reps / el / 1e12, "unit": "TFLOPS", "cores": threads,
+    base = {"value": per_img * imgs * reps / el / 1e12, "unit": "TFLOPS", "cores": threads,
             "kind": "oracle", "seconds": el,
             "sample": f"{imgs} of {cfg.N} images of the {cfg.name} layer, {reps} pass(es), "
-                      f"fp64 direct sum, {dt} inputs"}
+                      f"fp64 direct sum, {dt} inputs", **host}
+    return base, parity
+
+
+def layer_entry(cfg, dt, r):
+    """The per-layer record of the benchmark line."""
+    ho, wo = cfg.out_hw()
+    out = {"workload": f"{cfg.name}: N={cfg.N} Cin={cfg.Cin} H=W={cfg.H} Cout={cfg.Cout} "
+                       f"{cfg.KH}x{cfg.KW} s{cfg.stride} p{cfg.pad}",
+           "dtype": dt, "value": r["value"], "unit": "TFLOPS", "pct_of_peak": r["pct_of_peak"],
+           "peak_tflops": r["peak_tflops"], "ms_per_step": r["ms_per_step"],
+           "ms_per_call_median": r["ms_per_call_median"], "form": r["form"],
+           "flops_per_call": 2 * cfg.N * cfg.Cout * ho * wo * cfg.Cin * cfg.KH * cfg.KW,
+           "roofline": r["roofline"], "kernels": r["kernels"],
+           "ws_bytes": r["ws_bytes"], "im2col_bytes": r["im2col_bytes"],
+           "ws_over_im2col": r["ws_over_im2col"], "ws_target": r["ws_target"]}
+    for k in ("rel_l2_sampled", "max_err_over_bound", "parity_ok", "cpu_oracle_tflops"):
+        if k in r:
+            out[k] = r[k]
+    return out
 
 
 def implicit_applies(cfg, dt):
@@ -399,7 +468,7 @@ def probe(args, dev):
         torch.cuda.synchronize()
         _say(f"probe copy: {args.steps} copies of {COPY_BYTES} bytes")
         return
-    cfg = workloads.get_config(args.config)
+    cfg = workloads.get_config(args.config or HEADLINE[0])
     dt = args.dtype or next((d for d in cfg.dtypes if d != "f32"), cfg.dtypes[0])
     x, w = workloads.make_config_inputs(cfg, dt)
     xd, wd = x.to(dev), w.to(dev)
@@ -503,7 +572,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", default="resnet3x3")
+    ap.add_argument("--config", default=None, help="one layer only (its own line)")
     ap.add_argument("--dtype", default=None, help="headline dtype (default: the layer's "
                     "half-precision variant if it has one)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -544,6 +613,103 @@ def main():
     if args.ablation:
         ablation(args, dev)
         return
+    if args.table1 or args.all_configs or args.config:
+        per_layer_lines(args, dev)
+        return
+    default_line(args, dev)
+
+
+DEFAULT_LAYERS = ("tiny", "resnet3x3", "deep3x3", "stem7x7", "mix5x5", "mix512", "mix3x3s2", "mix1x1")
+HEADLINE = ("resnet3x3", "f16")
+
+
+def other_form(cfg, dt, res, args, dev):
+    """The layer's other form (window <-> implicit) where it has both, or None."""
+    if not implicit_applies(cfg, dt):
+        return None
+    alt = "window" if res["form"] == "implicit" else "implicit"
+    _say(f"bench: {cfg.name} {dt} other form ({alt})")
+    return time_variant(cfg, dt, args.steps, args.warmup, dev, algo=alt)
+
+
+def finish(cfg, dt, res, seconds, args):
+    """CPU leg of one timed variant: parity fields into res, the baseline returned."""
+    if args.no_cpu_baseline:
+        return None
+    base, par = cpu_leg(cfg, dt, res, seconds)
+    res.update(par)
+    res["cpu_oracle_tflops"] = base["value"]
+    return base
+
+
+def clean(res):
+    return {k: v for k, v in res.items() if k not in ("sample_idx", "sample_got")}
+
+
+def head_fields(cfg, dt, h):
+    return {
+        "metric": METRIC, "value": h["value"], "unit": "TFLOPS", "n_gpus": 1,
+        "ms_per_step": h["ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": dt, "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: N={cfg.N} Cin={cfg.Cin} H=W={cfg.H} "
+                               f"Cout={cfg.Cout} {cfg.KH}x{cfg.KW} s{cfg.stride} p{cfg.pad}",
+                   "N": cfg.N, "Cin": cfg.Cin, "H": cfg.H, "W": cfg.W, "Cout": cfg.Cout,
+                   "KH": cfg.KH, "KW": cfg.KW, "stride": cfg.stride, "pad": cfg.pad,
+                   "output": "fp32", "parallelism": "single GPU"},
+        "pct_of_peak": h["pct_of_peak"], "peak_tflops": h["peak_tflops"],
+        "roofline": h["roofline"], "kernels": h["kernels"],
+        "ws_bytes": h["ws_bytes"], "im2col_bytes": h["im2col_bytes"],
+        "ws_over_im2col": h["ws_over_im2col"], "ws_target": h["ws_target"],
+        "rel_l2_sampled": h.get("rel_l2_sampled"), "max_err_over_bound": h.get("max_err_over_bound"),
+        "parity_ok": h.get("parity_ok"),
+        "ms_per_call_median": h["ms_per_call_median"], "ms_per_call_best": h["ms_per_call_best"],
+        "form": h["form"], "kernel_us": h["kernel_us"],
+        "chunk_pack_us": h["chunk_pack_us"], "chunk_gemm_us": h["chunk_gemm_us"],
+        "chunk_rows": h["chunk_rows"], "n_chunks": h["n_chunks"],
+    }
+
+
+def default_line(args, dev):
+    """One JSON line: the headline layer (the ResNet-style 3x3 layer in fp16)
+    plus every layer configuration and dtype under "layers", each with its
+    TFLOPS, roofline of the dominant kernel, HBM traffic where counters were
+    taken, workspace, parity and the oracle's own throughput."""
+    import workloads
+    todo = [(n, dt) for n in DEFAULT_LAYERS for dt in workloads.CONFIGS[n].dtypes]
+    res = {}
+    for name, dt in todo:
+        _say(f"bench: {name} {dt} warmup={args.warmup} steps={args.steps}")
+        res[(name, dt)] = time_variant(workloads.CONFIGS[name], dt, args.steps, args.warmup, dev)
+    hcfg = workloads.CONFIGS[HEADLINE[0]]
+    other = other_form(hcfg, HEADLINE[1], res[HEADLINE], args, dev)
+    # every GPU timing is done: the CPU leg (oracle baseline + parity of the samples)
+    base = None
+    for name, dt in todo:
+        _say(f"bench: cpu leg {name} {dt}")
+        b = finish(workloads.CONFIGS[name], dt, res[(name, dt)],
+                   10.0 if (name, dt) == HEADLINE else 1.5, args)
+        if (name, dt) == HEADLINE:
+            base = b
+    if other is not None:
+        finish(hcfg, HEADLINE[1], other, 0.0, args)
+    h = res[HEADLINE]
+    line = head_fields(hcfg, HEADLINE[1], h)
+    line.update({"steps": args.steps, "warmup": args.warmup})
+    line["other_form"] = clean(other) if other is not None else None
+    line["layers"] = [layer_entry(workloads.CONFIGS[n], dt, res[(n, dt)]) for n, dt in todo]
+    line["all_parity_ok"] = (None if args.no_cpu_baseline
+                             else all(res[k].get("parity_ok") for k in todo))
+    if base is not None:
+        line["cpu_baseline"] = base
+    print(json.dumps(line), flush=True)
+
+
+def per_layer_lines(args, dev):
+    """One JSON line per layer (--config, --all-configs or --table1): the
+    layer's half-precision variant as the headline, its other dtypes under
+    "variants", the other form of each dtype under "other_form"."""
+    import workloads
     names = (list(workloads.TABLE1) if args.table1 else
              sorted(workloads.CONFIGS) if args.all_configs else [args.config])
     for name in names:
@@ -556,44 +722,24 @@ def main():
         for dt in order:
             _say(f"bench: {name} {dt} warmup={args.warmup} steps={args.steps}")
             results[dt] = time_variant(cfg, dt, args.steps, args.warmup, dev)
-        h = results[head]
-        # the other form of each dtype, where the layer has both (for fp32 the
-        # other form is the vector-ALU window form, or the matrix-core implicit one)
-        others = {}
+        others = {dt: other_form(cfg, dt, results[dt], args, dev) for dt in order}
+        base = None
+        first = name == names[0] or args.cpu_baseline_all
         for dt in order:
-            if implicit_applies(cfg, dt):
-                alt = "window" if results[dt]["form"] == "implicit" else "implicit"
-                _say(f"bench: {name} {dt} other form ({alt})")
-                others[dt] = time_variant(cfg, dt, args.steps, args.warmup, dev, algo=alt)
-        other = others.get(head)
+            b = finish(cfg, dt, results[dt], 10.0 if (first and dt == head) else 0.0, args)
+            if dt == head:
+                base = b
+            if others[dt] is not None:
+                finish(cfg, dt, others[dt], 0.0, args)
+        line = head_fields(cfg, head, results[head])
+        line.update({"steps": args.steps, "warmup": args.warmup})
         for dt in order[1:]:
-            if dt in others:
-                results[dt]["other_form"] = others[dt]
-        line = {
-            "metric": METRIC, "value": h["value"], "unit": "TFLOPS", "n_gpus": 1,
-            "steps": args.steps, "warmup": args.warmup, "ms_per_step": h["ms_per_step"],
-            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-            "dtype": head, "data": "synthetic",
-            "config": {"workload": f"{name}: N={cfg.N} Cin={cfg.Cin} H=W={cfg.H} "
-                                   f"Cout={cfg.Cout} {cfg.KH}x{cfg.KW} s{cfg.stride} p{cfg.pad}",
-                       "N": cfg.N, "Cin": cfg.Cin, "H": cfg.H, "W": cfg.W, "Cout": cfg.Cout,
-                       "KH": cfg.KH, "KW": cfg.KW, "stride": cfg.stride, "pad": cfg.pad,
-                       "output": "fp32", "parallelism": "single GPU"},
-            "pct_of_peak": h["pct_of_peak"], "peak_tflops": h["peak_tflops"],
-            "roofline": h["roofline"], "kernels": h["kernels"],
-            "ws_bytes": h["ws_bytes"], "im2col_bytes": h["im2col_bytes"],
-            "ws_over_im2col": h["ws_over_im2col"], "ws_target": h["ws_target"],
-            "rel_l2_sampled": h["rel_l2_sampled"], "parity_ok": h["parity_ok"],
-            "ms_per_call_median": h["ms_per_call_median"], "ms_per_call_best": h["ms_per_call_best"],
-            "form": h["form"], "kernel_us": h["kernel_us"],
-            "chunk_pack_us": h["chunk_pack_us"], "chunk_gemm_us": h["chunk_gemm_us"],
-            "chunk_rows": h["chunk_rows"], "n_chunks": h["n_chunks"],
-            "variants": [{k: v for k, v in results[d].items()} for d in order[1:]],
-            "other_form": other,
-        }
-        if not args.no_cpu_baseline and (name == names[0] or args.cpu_baseline_all):
-            _say("bench: cpu baseline (oracle)")
-            line["cpu_baseline"] = cpu_baseline(cfg, head)
+            if others[dt] is not None:
+                results[dt]["other_form"] = clean(others[dt])
+        line["variants"] = [clean(results[d]) for d in order[1:]]
+        line["other_form"] = clean(others[head]) if others[head] is not None else None
+        if base is not None and first:
+            line["cpu_baseline"] = base
         print(json.dumps(line), flush=True)
 
 
