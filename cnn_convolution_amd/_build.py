@@ -24,6 +24,7 @@ BUILDDIR = os.path.join(PKG, "_build")
 SOURCES = [
     os.path.join(CSRC, "plan.cpp"),
     os.path.join(CSRC, "api.cpp"),
+    os.path.join(CSRC, "noalloc.hip"),
     os.path.join(CSRC, "kernels", "pack.hip"),
     os.path.join(CSRC, "kernels", "weight_stage.hip"),
     os.path.join(CSRC, "kernels", "gemm_valu.hip"),

@@ -19,15 +19,16 @@ KERNEL_WEIGHT_STAGE, KERNEL_PACK, KERNEL_GEMM, KERNEL_IMPLICIT, KERNEL_KINDS = 0
 STATUS = {
     0: "CONV2D_OK", 1: "CONV2D_ERR_INVALID_DESC", 2: "CONV2D_ERR_NULL_POINTER",
     3: "CONV2D_ERR_MISALIGNED", 4: "CONV2D_ERR_UNSUPPORTED", 5: "CONV2D_ERR_WORKSPACE",
-    6: "CONV2D_ERR_HIP", 7: "CONV2D_ERR_RANGE",
+    6: "CONV2D_ERR_HIP", 7: "CONV2D_ERR_RANGE", 8: "CONV2D_ERR_SCRATCH",
 }
+NOALLOC_SCRATCH_BYTES = 32 << 20     # IM2WIN_NOALLOC_SCRATCH_BYTES
 
 # every symbol the header declares
 EXPORTS = [
     "conv2d_workspace_size", "conv2d_plan", "conv2d_fwd", "im2win_pack", "im2win_weight_stage",
     "im2win_window_gemm", "conv2d_status_string", "conv2d_profile_enable", "conv2d_profile_read",
     "conv2d_implicit_plan", "conv2d_implicit_workspace_size", "conv2d_fwd_implicit",
-    "im2win_implicit_gemm",
+    "im2win_implicit_gemm", "conv2d_fwd_noalloc",
 ]
 
 
@@ -126,6 +127,8 @@ def lib() -> ctypes.CDLL:
         L.conv2d_fwd_implicit.argtypes = [dp, vp, vp, vp, vp, vp]
         L.im2win_implicit_gemm.restype = ctypes.c_int
         L.im2win_implicit_gemm.argtypes = [dp, vp, vp, vp, vp]
+        L.conv2d_fwd_noalloc.restype = ctypes.c_int
+        L.conv2d_fwd_noalloc.argtypes = [dp, vp, vp, vp, vp]
         L.conv2d_profile_enable.restype = ctypes.c_int
         L.conv2d_profile_enable.argtypes = [i32]
         L.conv2d_profile_read.restype = ctypes.c_int
@@ -152,6 +155,10 @@ def plan(d: Desc) -> Plan:
 
 def fwd(d: Desc, x: int, w: int, y: int, ws: int, stream: int) -> int:
     return lib().conv2d_fwd(ctypes.byref(d), x, w, y, ws, stream)
+
+
+def fwd_noalloc(d: Desc, x: int, w: int, y: int, stream: int) -> int:
+    return lib().conv2d_fwd_noalloc(ctypes.byref(d), x, w, y, stream)
 
 
 def implicit_plan(d: Desc) -> ImplicitPlan:

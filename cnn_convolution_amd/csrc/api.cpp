@@ -245,6 +245,7 @@ const char *conv2d_status_string(conv2d_status_t s)
     case CONV2D_ERR_WORKSPACE: return "workspace missing";
     case CONV2D_ERR_HIP: return "HIP runtime error";
     case CONV2D_ERR_RANGE: return "row range out of bounds";
+    case CONV2D_ERR_SCRATCH: return "workspace exceeds the static scratch of conv2d_fwd_noalloc";
     }
     return "unknown status";
 }

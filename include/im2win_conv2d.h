@@ -88,7 +88,9 @@ typedef enum {
     CONV2D_ERR_UNSUPPORTED = 4,   /* unknown dtype or layout for this call          */
     CONV2D_ERR_WORKSPACE = 5,     /* ws NULL although a workspace is needed         */
     CONV2D_ERR_HIP = 6,           /* the HIP runtime reported an error on launch    */
-    CONV2D_ERR_RANGE = 7          /* a row range outside [0, N*Ho)                  */
+    CONV2D_ERR_RANGE = 7,         /* a row range outside [0, N*Ho)                  */
+    CONV2D_ERR_SCRATCH = 8        /* conv2d_fwd_noalloc: the planned form needs more
+                                     workspace than IM2WIN_NOALLOC_SCRATCH_BYTES    */
 } conv2d_status_t;
 
 /* Storage orders of the window tensor (Eq. (2) of the im2win paper, with r =
@@ -199,6 +201,22 @@ conv2d_status_t im2win_window_gemm(const conv2d_desc_t *d, const void *win, cons
                                    float *y, int64_t row0, int64_t rows, void *stream);
 
 const char *conv2d_status_string(conv2d_status_t s);
+
+/* ---- allocation-free entry point ----------------------------------------
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc. The same
+ * y = conv2d(x, w) as conv2d_fwd, with the workspace of the planned form taken
+ * from a static device array of IM2WIN_NOALLOC_SCRATCH_BYTES that each GPU the
+ * library runs on holds until the process ends (its address on a device is
+ * looked up on the first call there, with that device current). Calls no
+ * hipMalloc, hipFree or allocating library routine. x, w, y as conv2d_fwd.
+ * Returns CONV2D_ERR_SCRATCH, and launches nothing, when the plan's
+ * workspace (conv2d_workspace_size) exceeds the array. All calls on one GPU
+ * share its array: calls that overlap on one GPU (several streams or host
+ * threads) race on it and must be ordered by the caller. */
+#define IM2WIN_NOALLOC_SCRATCH_BYTES (32u << 20)
+conv2d_status_t conv2d_fwd_noalloc(const conv2d_desc_t *d, const void *x, const void *w, float *y,
+                                   void *stream);
 
 /* ---- implicit (fused) form ---------------------------------------------
  * The same y = conv2d(x, w), with the window rows built in LDS straight

@@ -49,7 +49,7 @@ def test_device_code_is_gfx950_only():
 
 
 def test_status_strings():
-    for code in range(8):
+    for code in range(9):
         s = conv.status_string(code)
         assert s and s != "unknown status"
     assert conv.status_string(99) == "unknown status"
