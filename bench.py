@@ -131,7 +131,7 @@ def recorded_traffic(name, dt, d, plan):
     return None
 
 
-def algorithmic_bytes(cfg, dt, plan):
+def algorithmic_bytes(cfg, dt, plan, ydt="f32"):
     """Per-kernel algorithmic HBM bytes of one call (each tensor moved once).
 
     pack     : reads x, writes the window tensor (N*Ho rows of Cin*W_win*KH)
@@ -144,7 +144,7 @@ def algorithmic_bytes(cfg, dt, plan):
     x = cfg.N * cfg.Cin * cfg.H * cfg.W * es
     w = cfg.Cout * cfg.Cin * cfg.KH * cfg.KW * es
     win = cfg.N * ho * cfg.Cin * plan.W_win * cfg.KH * es
-    y = cfg.N * cfg.Cout * ho * wo * 4
+    y = cfg.N * cfg.Cout * ho * wo * (4 if ydt == "f32" else 2)
     staged = not (cfg.KH == 1 and cfg.KW == 1)
     return {"pack": x + win, "gemm": win + w * plan.n_chunks + y,
             "weight_stage": 2 * w if (plan.wstage_bytes if plan.algo == 0 else staged) else 0,
@@ -171,7 +171,7 @@ def layer_inputs(cfg, dt):
     return x32.to(t).contiguous(), w32.to(t).contiguous()
 
 
-def time_variant(cfg, dt, steps, warmup, dev, algo=None):
+def time_variant(cfg, dt, steps, warmup, dev, algo=None, ydt="f32"):
     """Time conv2d_fwd on one layer and dtype, in the form the planner picks
     (or the one `algo` forces: "window" or "implicit"), and its dominant kernel
     alone; check the timed output against the oracle on sampled points."""
@@ -185,7 +185,7 @@ def time_variant(cfg, dt, steps, warmup, dev, algo=None):
     else:
         os.environ.pop("IM2WIN_ALGO", None)
     try:
-        return _time_variant(cfg, dt, steps, warmup, dev)
+        return _time_variant(cfg, dt, steps, warmup, dev, ydt)
     finally:
         if saved is None:
             os.environ.pop("IM2WIN_ALGO", None)
@@ -193,18 +193,19 @@ def time_variant(cfg, dt, steps, warmup, dev, algo=None):
             os.environ["IM2WIN_ALGO"] = saved
 
 
-def _time_variant(cfg, dt, steps, warmup, dev):
+def _time_variant(cfg, dt, steps, warmup, dev, ydt="f32"):
     import torch
 
     import cnn_convolution_amd as conv
+    import workloads
     from cnn_convolution_amd import _lib
 
     x, w = layer_inputs(cfg, dt)
     xd, wd = x.to(dev), w.to(dev)
-    d = conv.describe(tuple(x.shape), tuple(w.shape), cfg.stride, cfg.pad,
-                      {"f32": conv.F32, "f16": conv.F16, "bf16": conv.BF16}[dt])
+    codes = {"f32": conv.F32, "f16": conv.F16, "bf16": conv.BF16}
+    d = conv.describe(tuple(x.shape), tuple(w.shape), cfg.stride, cfg.pad, codes[dt], codes[ydt])
     plan = conv.plan(d)
-    y = torch.empty((cfg.N, cfg.Cout, plan.Ho, plan.Wo), dtype=torch.float32, device=dev)
+    y = torch.empty((cfg.N, cfg.Cout, plan.Ho, plan.Wo), dtype=workloads.TORCH_DTYPES[ydt], device=dev)
     ws = torch.empty(max(plan.ws_bytes, 1), dtype=torch.uint8, device=dev)
     wsarg = ws if plan.ws_bytes else None
 
@@ -263,7 +264,7 @@ def _time_variant(cfg, dt, steps, warmup, dev):
         torch.cuda.synchronize()
         kern_us = g0.elapsed_time(g1) / steps * 1e3
         dom_flops = plan.flops
-        dom_bytes = algorithmic_bytes(cfg, dt, plan)["implicit"]
+        dom_bytes = algorithmic_bytes(cfg, dt, plan, ydt)["implicit"]
         n_chunks = 1
     else:
         row0 = (plan.n_chunks - 1) * plan.rows_per_chunk
@@ -291,7 +292,8 @@ def _time_variant(cfg, dt, steps, warmup, dev):
         pack_us = p0.elapsed_time(p1) / steps * 1e3
         dom_flops = 2 * rows * plan.Wo * cfg.Cout * cfg.Cin * cfg.KH * cfg.KW
         dom_bytes = (rows * cfg.Cin * plan.W_win * cfg.KH * es
-                     + cfg.Cout * cfg.Cin * cfg.KH * cfg.KW * es + rows * plan.Wo * cfg.Cout * 4)
+                     + cfg.Cout * cfg.Cin * cfg.KH * cfg.KW * es
+                     + rows * plan.Wo * cfg.Cout * (4 if ydt == "f32" else 2))
         n_chunks = plan.n_chunks
     conv.conv2d_into(xd, wd, y, wsarg, cfg.stride, cfg.pad)   # y whole again for the parity check
     torch.cuda.synchronize()
@@ -304,7 +306,7 @@ def _time_variant(cfg, dt, steps, warmup, dev):
 
     flops = plan.flops
     tflops = flops / (ms * 1e-3) / 1e12
-    ab = algorithmic_bytes(cfg, dt, plan)
+    ab = algorithmic_bytes(cfg, dt, plan, ydt)
     kern = {}
     for k in ("weight_stage", "pack", "gemm", "implicit"):
         n = prof[k]["launches"]
@@ -344,7 +346,7 @@ def _time_variant(cfg, dt, steps, warmup, dev):
         "chunk_pack_us": pack_us, "chunk_gemm_us": kern_us if plan.algo == 0 else None,
         "kernel_us": kern_us, "chunk_rows": rows,
         "pct_of_peak": 100.0 * tflops / peak, "peak_tflops": peak,
-        "sample_idx": idx, "sample_got": got,
+        "sample_idx": idx, "sample_got": got, "y_dtype": ydt,
         "ws_bytes": plan.ws_bytes, "im2col_bytes": plan.im2col_bytes,
         "ws_over_im2col": plan.ws_bytes / plan.im2col_bytes, "ws_target": 1.0 / cfg.KW,
         "n_chunks": n_chunks, "kernels": kern, "roofline": roof,
@@ -403,12 +405,14 @@ def cpu_leg(cfg, dt, res, min_seconds):
     ref = oracle.conv2d_points(x, w, cfg.stride, cfg.pad, idx, nthreads=threads)
     mag = oracle.conv2d_points(x.abs(), w.abs(), cfg.stride, cfg.pad, idx, nthreads=threads)
     K = cfg.Cin * cfg.KH * cfg.KW
-    bound = 2.0 * (K + 1) * 2.0 ** -24 * mag
+    u_out = {"f32": 0.0, "f16": 2.0 ** -11, "bf16": 2.0 ** -8}[res.get("y_dtype", "f32")]
+    bound = 2.0 * (K + 1) * 2.0 ** -24 * mag + u_out * np.abs(ref)
     err = np.abs(got - ref)
     rel = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
     ratio = float(np.max(err / np.where(bound > 0, bound, 1.0)))
+    tol = max(TOL[dt], TOL[res.get("y_dtype", "f32")])
     parity = {"rel_l2_sampled": rel, "max_err_over_bound": ratio, "points": int(idx.size),
-              "parity_ok": bool(rel <= TOL[dt] and np.all(err <= bound))}
+              "parity_ok": bool(rel <= tol and np.all(err <= bound))}
     ho, wo = cfg.out_hw()
     per_img = 2 * cfg.Cout * ho * wo * cfg.Cin * cfg.KH * cfg.KW
     # size the sample from a one-image probe
@@ -433,7 +437,8 @@ def layer_entry(cfg, dt, r):
     ho, wo = cfg.out_hw()
     out = {"workload": f"{cfg.name}: N={cfg.N} Cin={cfg.Cin} H=W={cfg.H} Cout={cfg.Cout} "
                        f"{cfg.KH}x{cfg.KW} s{cfg.stride} p{cfg.pad}",
-           "dtype": dt, "value": r["value"], "unit": "TFLOPS", "pct_of_peak": r["pct_of_peak"],
+           "dtype": dt, "y_dtype": r.get("y_dtype", "f32"),
+           "value": r["value"], "unit": "TFLOPS", "pct_of_peak": r["pct_of_peak"],
            "peak_tflops": r["peak_tflops"], "ms_per_step": r["ms_per_step"],
            "ms_per_call_median": r["ms_per_call_median"], "form": r["form"],
            "flops_per_call": 2 * cfg.N * cfg.Cout * ho * wo * cfg.Cin * cfg.KH * cfg.KW,
@@ -472,10 +477,10 @@ def probe(args, dev):
     dt = args.dtype or next((d for d in cfg.dtypes if d != "f32"), cfg.dtypes[0])
     x, w = workloads.make_config_inputs(cfg, dt)
     xd, wd = x.to(dev), w.to(dev)
-    d = conv.describe(tuple(x.shape), tuple(w.shape), cfg.stride, cfg.pad,
-                      {"f32": conv.F32, "f16": conv.F16, "bf16": conv.BF16}[dt])
+    codes = {"f32": conv.F32, "f16": conv.F16, "bf16": conv.BF16}
+    d = conv.describe(tuple(x.shape), tuple(w.shape), cfg.stride, cfg.pad, codes[dt], codes[ydt])
     plan = conv.plan(d)
-    y = torch.empty((cfg.N, cfg.Cout, plan.Ho, plan.Wo), dtype=torch.float32, device=dev)
+    y = torch.empty((cfg.N, cfg.Cout, plan.Ho, plan.Wo), dtype=workloads.TORCH_DTYPES[ydt], device=dev)
     ws = torch.empty(max(plan.ws_bytes, 1), dtype=torch.uint8, device=dev)
     conv.conv2d_into(xd, wd, y, ws if plan.ws_bytes else None, cfg.stride, cfg.pad)
     kid, tile, rows = dominant_key(d, plan)
@@ -621,6 +626,9 @@ def main():
 
 DEFAULT_LAYERS = ("tiny", "resnet3x3", "deep3x3", "stem7x7", "mix5x5", "mix512", "mix3x3s2", "mix1x1")
 HEADLINE = ("resnet3x3", "f16")
+# the layers whose fp32 output is most of their HBM traffic, also with the
+# fp16 output epilogue (y rounded once to fp16 in the kernel that stores it)
+HALF_OUTPUT_LAYERS = (("resnet3x3", "f16", "f16"), ("stem7x7", "f16", "f16"), ("mix1x1", "f16", "f16"))
 
 
 def other_form(cfg, dt, res, args, dev):
@@ -676,28 +684,31 @@ def default_line(args, dev):
     TFLOPS, roofline of the dominant kernel, HBM traffic where counters were
     taken, workspace, parity and the oracle's own throughput."""
     import workloads
-    todo = [(n, dt) for n in DEFAULT_LAYERS for dt in workloads.CONFIGS[n].dtypes]
+    todo = [(n, dt, "f32") for n in DEFAULT_LAYERS for dt in workloads.CONFIGS[n].dtypes]
+    todo += list(HALF_OUTPUT_LAYERS)
     res = {}
-    for name, dt in todo:
-        _say(f"bench: {name} {dt} warmup={args.warmup} steps={args.steps}")
-        res[(name, dt)] = time_variant(workloads.CONFIGS[name], dt, args.steps, args.warmup, dev)
+    for name, dt, ydt in todo:
+        _say(f"bench: {name} {dt} -> y {ydt} warmup={args.warmup} steps={args.steps}")
+        res[(name, dt, ydt)] = time_variant(workloads.CONFIGS[name], dt, args.steps, args.warmup, dev,
+                                            ydt=ydt)
+    head = HEADLINE + ("f32",)
     hcfg = workloads.CONFIGS[HEADLINE[0]]
-    other = other_form(hcfg, HEADLINE[1], res[HEADLINE], args, dev)
+    other = other_form(hcfg, HEADLINE[1], res[head], args, dev)
     # every GPU timing is done: the CPU leg (oracle baseline + parity of the samples)
     base = None
-    for name, dt in todo:
-        _say(f"bench: cpu leg {name} {dt}")
-        b = finish(workloads.CONFIGS[name], dt, res[(name, dt)],
-                   10.0 if (name, dt) == HEADLINE else 1.5, args)
-        if (name, dt) == HEADLINE:
+    for name, dt, ydt in todo:
+        _say(f"bench: cpu leg {name} {dt} -> y {ydt}")
+        b = finish(workloads.CONFIGS[name], dt, res[(name, dt, ydt)],
+                   10.0 if (name, dt, ydt) == head else (1.5 if ydt == "f32" else 0.0), args)
+        if (name, dt, ydt) == head:
             base = b
     if other is not None:
         finish(hcfg, HEADLINE[1], other, 0.0, args)
-    h = res[HEADLINE]
+    h = res[head]
     line = head_fields(hcfg, HEADLINE[1], h)
     line.update({"steps": args.steps, "warmup": args.warmup})
     line["other_form"] = clean(other) if other is not None else None
-    line["layers"] = [layer_entry(workloads.CONFIGS[n], dt, res[(n, dt)]) for n, dt in todo]
+    line["layers"] = [layer_entry(workloads.CONFIGS[n], dt, res[(n, dt, y)]) for n, dt, y in todo]
     line["all_parity_ok"] = (None if args.no_cpu_baseline
                              else all(res[k].get("parity_ok") for k in todo))
     if base is not None:

@@ -1,17 +1,21 @@
 """im2win forward 2-D convolution for MI355X (gfx950).
 
-    y = cnn_convolution_amd.conv2d(x, w, stride=1, pad=0)
+    y = cnn_convolution_amd.conv2d(x, w, stride=1, pad=0,
+                                   bias=None, scale=None, out_dtype=None, layout="nchw")
 
-x [N][Cin][H][W] and w [Cout][Cin][KH][KW] are contiguous CUDA (HIP) tensors
-of float32, float16 or bfloat16 (the same dtype); y is float32. PyTorch
-provides the device memory and the current stream; the convolution itself
-runs in libim2win_conv2d.so (see include/im2win_conv2d.h).
+x [N][Cin][H][W] and w [Cout][Cin][KH][KW] (layout "nhwc": x [N][H][W][Cin],
+w [Cout][KH][KW][Cin], half precision only) are contiguous CUDA (HIP)
+tensors of float32, float16 or bfloat16 (the same dtype); y is float32 unless
+out_dtype says otherwise, y = scale[co] * (conv + bias[co]) when the fp32
+[Cout] tensors scale / bias are given. PyTorch provides the device memory and
+the current stream; the convolution itself runs in libim2win_conv2d.so (see
+include/im2win_conv2d.h).
 """
 from __future__ import annotations
 
 from . import _lib
 from ._lib import (Conv2dError, Desc, Plan, ImplicitPlan, LAYOUT_CL, LAYOUT_ROW,  # noqa: F401
-                   F16, F32, BF16, make_desc, workspace_size, plan, implicit_plan,
+                   F16, F32, BF16, NCHW, NHWC, make_desc, workspace_size, plan, implicit_plan,
                    implicit_workspace_size, profile_enable, profile_read, status_string)
 
 __all__ = ["conv2d", "conv2d_into", "conv2d_implicit", "conv2d_implicit_into", "pack",
@@ -28,12 +32,34 @@ def _dtype_code(t) -> int:
     return codes[t.dtype]
 
 
-def describe(x_shape, w_shape, stride=1, pad=0, dtype=F32) -> Desc:
-    N, Cin, H, W = x_shape
-    Cout, Cin2, KH, KW = w_shape
+_LAYOUTS = {"nchw": NCHW, "nhwc": NHWC}
+
+
+def _layout_code(layout) -> int:
+    if layout in (NCHW, NHWC):
+        return layout
+    if layout not in _LAYOUTS:
+        raise ValueError(f"unknown layout {layout!r}")
+    return _LAYOUTS[layout]
+
+
+def describe(x_shape, w_shape, stride=1, pad=0, dtype=F32, y_dtype=F32, layout=NCHW) -> Desc:
+    """The descriptor of a layer from the shapes of x and w in `layout`."""
+    lay = _layout_code(layout)
+    if lay == NHWC:
+        N, H, W, Cin = x_shape
+        Cout, KH, KW, Cin2 = w_shape
+    else:
+        N, Cin, H, W = x_shape
+        Cout, Cin2, KH, KW = w_shape
     if Cin2 != Cin:
         raise ValueError(f"channel mismatch: x has {Cin}, w has {Cin2}")
-    return make_desc(N, Cin, H, W, Cout, KH, KW, stride, pad, dtype)
+    return make_desc(N, Cin, H, W, Cout, KH, KW, stride, pad, dtype, y_dtype, lay)
+
+
+def out_shape(d: Desc, p) -> tuple:
+    """Shape of y for descriptor d and its plan p."""
+    return (d.N, p.Ho, p.Wo, d.Cout) if d.layout == NHWC else (d.N, d.Cout, p.Ho, p.Wo)
 
 
 def _stream():
@@ -48,26 +74,37 @@ def _check(t, name):
         raise ValueError(f"{name} must be contiguous")
 
 
-def conv2d_into(x, w, y, ws, stride=1, pad=0) -> None:
-    """Enqueue y = conv2d(x, w) on the current stream using caller buffers."""
-    d = describe(tuple(x.shape), tuple(w.shape), stride, pad, _dtype_code(x))
+def conv2d_into(x, w, y, ws, stride=1, pad=0, *, bias=None, scale=None, layout="nchw") -> None:
+    """Enqueue y = conv2d(x, w) on the current stream using caller buffers
+    (y's dtype is the output type; scale / bias: fp32 [Cout] device tensors)."""
+    d = describe(tuple(x.shape), tuple(w.shape), stride, pad, _dtype_code(x), _dtype_code(y), layout)
     if w.dtype != x.dtype:
         raise TypeError("x and w must share a dtype")
-    st = _lib.fwd(d, x.data_ptr(), w.data_ptr(), y.data_ptr(),
-                  ws.data_ptr() if ws is not None and ws.numel() else None, _stream())
+    for t, name in ((scale, "scale"), (bias, "bias")):
+        if t is not None and (t.dtype.itemsize != 4 or not t.is_floating_point() or t.numel() != d.Cout):
+            raise ValueError(f"{name} must be an fp32 tensor of Cout elements")
+    ws_ptr = ws.data_ptr() if ws is not None and ws.numel() else None
+    if bias is None and scale is None:
+        st = _lib.fwd(d, x.data_ptr(), w.data_ptr(), y.data_ptr(), ws_ptr, _stream())
+    else:
+        st = _lib.fwd_ex(d, x.data_ptr(), w.data_ptr(), scale.data_ptr() if scale is not None else None,
+                         bias.data_ptr() if bias is not None else None, y.data_ptr(), ws_ptr, _stream())
     if st != 0:
         raise Conv2dError(st, "conv2d_fwd")
 
 
-def conv2d(x, w, stride: int = 1, pad: int = 0):
+def conv2d(x, w, stride: int = 1, pad: int = 0, *, bias=None, scale=None, out_dtype=None,
+           layout="nchw"):
     import torch
     _check(x, "x")
     _check(w, "w")
-    d = describe(tuple(x.shape), tuple(w.shape), stride, pad, _dtype_code(x))
+    odt = torch.float32 if out_dtype is None else out_dtype
+    d = describe(tuple(x.shape), tuple(w.shape), stride, pad, _dtype_code(x),
+                 _dtype_code(torch.empty(0, dtype=odt)), layout)
     p = plan(d)
-    y = torch.empty((d.N, d.Cout, p.Ho, p.Wo), dtype=torch.float32, device=x.device)
+    y = torch.empty(out_shape(d, p), dtype=odt, device=x.device)
     ws = torch.empty(max(p.ws_bytes, 1), dtype=torch.uint8, device=x.device)
-    conv2d_into(x, w, y, ws if p.ws_bytes else None, stride, pad)
+    conv2d_into(x, w, y, ws if p.ws_bytes else None, stride, pad, bias=bias, scale=scale, layout=layout)
     return y
 
 

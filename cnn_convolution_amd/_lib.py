@@ -13,7 +13,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIBPATH = os.path.join(PKG, "lib", "libim2win_conv2d.so")
 
 F32, F16, BF16 = 0, 1, 2
-LAYOUT_ROW, LAYOUT_CL = 0, 1
+NCHW, NHWC = 0, 1                    # conv2d_layout_t: memory layout of x, w and y
+LAYOUT_ROW, LAYOUT_CL = 0, 1         # im2win_layout_t: storage order of the window tensor
 KERNEL_WEIGHT_STAGE, KERNEL_PACK, KERNEL_GEMM, KERNEL_IMPLICIT, KERNEL_KINDS = 0, 1, 2, 3, 4
 
 STATUS = {
@@ -28,14 +29,15 @@ EXPORTS = [
     "conv2d_workspace_size", "conv2d_plan", "conv2d_fwd", "im2win_pack", "im2win_weight_stage",
     "im2win_window_gemm", "conv2d_status_string", "conv2d_profile_enable", "conv2d_profile_read",
     "conv2d_implicit_plan", "conv2d_implicit_workspace_size", "conv2d_fwd_implicit",
-    "im2win_implicit_gemm", "conv2d_fwd_noalloc",
+    "im2win_implicit_gemm", "conv2d_fwd_noalloc", "conv2d_fwd_ex",
 ]
 
 
 class Desc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in
                 ("N", "Cin", "H", "W", "Cout", "KH", "KW", "stride", "pad")] + \
-               [("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+               [("dtype", ctypes.c_int32), ("y_dtype", ctypes.c_int32), ("layout", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
 
 _PLAN_FIELDS = [
@@ -111,6 +113,8 @@ def lib() -> ctypes.CDLL:
         L.conv2d_plan.argtypes = [dp, ctypes.POINTER(Plan)]
         L.conv2d_fwd.restype = ctypes.c_int
         L.conv2d_fwd.argtypes = [dp, vp, vp, vp, vp, vp]
+        L.conv2d_fwd_ex.restype = ctypes.c_int
+        L.conv2d_fwd_ex.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp]
         L.im2win_pack.restype = ctypes.c_int
         L.im2win_pack.argtypes = [dp, i32, vp, vp, i64, i64, vp]
         L.im2win_weight_stage.restype = ctypes.c_int
@@ -137,8 +141,8 @@ def lib() -> ctypes.CDLL:
     return _lib
 
 
-def make_desc(N, Cin, H, W, Cout, KH, KW, stride, pad, dtype) -> Desc:
-    return Desc(N, Cin, H, W, Cout, KH, KW, stride, pad, dtype, 0)
+def make_desc(N, Cin, H, W, Cout, KH, KW, stride, pad, dtype, y_dtype=F32, layout=NCHW) -> Desc:
+    return Desc(N, Cin, H, W, Cout, KH, KW, stride, pad, dtype, y_dtype, layout, 0)
 
 
 def workspace_size(d: Desc) -> int:
@@ -155,6 +159,10 @@ def plan(d: Desc) -> Plan:
 
 def fwd(d: Desc, x: int, w: int, y: int, ws: int, stream: int) -> int:
     return lib().conv2d_fwd(ctypes.byref(d), x, w, y, ws, stream)
+
+
+def fwd_ex(d: Desc, x: int, w: int, scale: int, bias: int, y: int, ws: int, stream: int) -> int:
+    return lib().conv2d_fwd_ex(ctypes.byref(d), x, w, scale, bias, y, ws, stream)
 
 
 def fwd_noalloc(d: Desc, x: int, w: int, y: int, stream: int) -> int:

@@ -66,6 +66,22 @@ struct ProfScope {
     }
 };
 
+// y and its epilogue (scale and bias may be null) for the kernels
+OutSpec make_out(const conv2d_desc_t &d, int64_t Ho, int64_t Wo, void *y, const float *scale,
+                 const float *bias)
+{
+    OutSpec o{};
+    o.y = y;
+    o.scale = scale;
+    o.bias = bias;
+    o.type = d.y_dtype;
+    o.nhwc = d.layout == CONV2D_NHWC ? 1 : 0;
+    o.plain = (o.type == CONV2D_F32 && !o.nhwc && !scale && !bias) ? 1 : 0;
+    o.Cout = int(d.Cout);
+    o.plane = Ho * Wo;
+    return o;
+}
+
 PackArgs pack_args(const conv2d_desc_t &d, const conv2d_plan_t &p, int32_t layout,
                    const LayoutGeom &g, const void *x, void *out, int64_t row0, int64_t rows)
 {
@@ -87,19 +103,20 @@ PackArgs pack_args(const conv2d_desc_t &d, const conv2d_plan_t &p, int32_t layou
     a.row0 = int(row0);
     a.rows = int(rows);
     a.esize = int(elem_size(d.dtype));
+    a.nhwc = d.layout == CONV2D_NHWC ? 1 : 0;
     (void)layout;
     return a;
 }
 
 hipError_t launch_gemm(const conv2d_desc_t &d, const conv2d_plan_t &p, const LayoutGeom &g,
-                       const void *win, const void *wst, float *y, int64_t row0, int64_t rows,
+                       const void *win, const void *wst, const OutSpec &out, int64_t row0, int64_t rows,
                        hipStream_t s)
 {
     if (p.path == 0) {
         ValuGemmArgs ga{};
         ga.win = static_cast<const float *>(win);
         ga.wst = static_cast<const float *>(wst);
-        ga.y = y;
+        ga.out = out;
         ga.rows = int(rows);
         ga.row0 = int(row0);
         ga.Cin = int(d.Cin);
@@ -118,7 +135,7 @@ hipError_t launch_gemm(const conv2d_desc_t &d, const conv2d_plan_t &p, const Lay
     MfmaGemmArgs ga{};
     ga.win = win;
     ga.wst = wst;
-    ga.y = y;
+    ga.out = out;
     ga.rows = int(rows);
     ga.row0 = int(row0);
     ga.row_elems = int(g.row_elems);
@@ -140,12 +157,12 @@ hipError_t launch_gemm(const conv2d_desc_t &d, const conv2d_plan_t &p, const Lay
 }
 
 ImplicitArgs implicit_args(const conv2d_desc_t &d, const conv2d_implicit_plan_t &p, const void *x,
-                           const void *wst, float *y)
+                           const void *wst, const OutSpec &out)
 {
     ImplicitArgs a{};
     a.x = x;
     a.wst = wst;
-    a.y = y;
+    a.out = out;
     a.N = int(d.N);
     a.Cin = int(d.Cin);
     a.H = int(d.H);
@@ -189,7 +206,7 @@ hipError_t launch_implicit(const conv2d_implicit_plan_t &p, const ImplicitArgs &
 // unless a 1x1 filter already is, then (a2, a4, a5) in one kernel: window
 // rows built in LDS, contracted, fp32 y written. Arguments checked by the caller.
 conv2d_status_t run_implicit(const conv2d_desc_t &d, const conv2d_implicit_plan_t &p, const void *x,
-                             const void *w, float *y, void *ws, hipStream_t s)
+                             const void *w, const OutSpec &out, void *ws, hipStream_t s)
 {
     const void *wst = w;
     if (p.ws_bytes > 0) {
@@ -212,9 +229,15 @@ conv2d_status_t run_implicit(const conv2d_desc_t &d, const conv2d_implicit_plan_
         wst = ws;
     }
     ProfScope ps(s, CONV2D_KERNEL_IMPLICIT);
-    return launch_implicit(p, implicit_args(d, p, x, wst, y), s) == hipSuccess ? CONV2D_OK
-                                                                               : CONV2D_ERR_HIP;
+    return launch_implicit(p, implicit_args(d, p, x, wst, out), s) == hipSuccess ? CONV2D_OK
+                                                                                 : CONV2D_ERR_HIP;
 }
+
+bool aligned_or_null(const void *p, uintptr_t a) { return !p || aligned(p, a); }
+
+// conv2d_fwd and conv2d_fwd_ex: validate -> plan -> the planned form
+conv2d_status_t fwd_impl(const conv2d_desc_t *d, const void *x, const void *w, const float *scale,
+                         const float *bias, void *y, void *ws, void *stream);
 
 }  // namespace
 
@@ -250,8 +273,24 @@ const char *conv2d_status_string(conv2d_status_t s)
     return "unknown status";
 }
 
-conv2d_status_t conv2d_fwd(const conv2d_desc_t *d, const void *x, const void *w, float *y,
+conv2d_status_t conv2d_fwd(const conv2d_desc_t *d, const void *x, const void *w, void *y,
                            void *ws, void *stream)
+{
+    return fwd_impl(d, x, w, nullptr, nullptr, y, ws, stream);
+}
+
+conv2d_status_t conv2d_fwd_ex(const conv2d_desc_t *d, const void *x, const void *w, const float *scale,
+                              const float *bias, void *y, void *ws, void *stream)
+{
+    return fwd_impl(d, x, w, scale, bias, y, ws, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+conv2d_status_t fwd_impl(const conv2d_desc_t *d, const void *x, const void *w, const float *scale,
+                         const float *bias, void *y, void *ws, void *stream)
 {
     if (!d) return CONV2D_ERR_NULL_POINTER;
     conv2d_plan_t p;
@@ -261,12 +300,14 @@ conv2d_status_t conv2d_fwd(const conv2d_desc_t *d, const void *x, const void *w,
     if (p.ws_bytes > 0 && !ws) return CONV2D_ERR_WORKSPACE;
     if (!aligned(x, 16) || !aligned(w, 16) || !aligned(y, 16)) return CONV2D_ERR_MISALIGNED;
     if (ws && !aligned(ws, 256)) return CONV2D_ERR_MISALIGNED;
+    if (!aligned_or_null(scale, 4) || !aligned_or_null(bias, 4)) return CONV2D_ERR_MISALIGNED;
+    const OutSpec out = make_out(*d, p.Ho, p.Wo, y, scale, bias);
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (p.algo == 1) {
         conv2d_implicit_plan_t ip;
         if (make_implicit_plan(*d, &ip) != CONV2D_OK) return CONV2D_ERR_UNSUPPORTED;
-        return run_implicit(*d, ip, x, w, y, ws, s);
+        return run_implicit(*d, ip, x, w, out, ws, s);
     }
     char *wsb = static_cast<char *>(ws);
     const LayoutGeom g = layout_geom(*d, p.layout);
@@ -290,6 +331,7 @@ conv2d_status_t conv2d_fwd(const conv2d_desc_t *d, const void *x, const void *w,
         sa.rows = int(sg.rows);
         sa.row_len = int(sg.row_len);
         sa.esize = es;
+        sa.ohwi = d->layout == CONV2D_NHWC ? 1 : 0;
         wst = wsb;
     }
     void *win = wsb + p.win_offset_bytes;
@@ -315,12 +357,16 @@ conv2d_status_t conv2d_fwd(const conv2d_desc_t *d, const void *x, const void *w,
         // (a4, a5) window-GEMM of the chunk, fp32 result written into y
         {
             ProfScope ps(s, CONV2D_KERNEL_GEMM);
-            e = launch_gemm(*d, p, g, win, wst, y, row0, rows, s);
+            e = launch_gemm(*d, p, g, win, wst, out, row0, rows, s);
         }
         if (e != hipSuccess) return CONV2D_ERR_HIP;
     }
     return CONV2D_OK;
 }
+
+}  // namespace
+
+extern "C" {
 
 conv2d_status_t im2win_pack(const conv2d_desc_t *d, int32_t layout, const void *x, void *out,
                             int64_t row0, int64_t rows, void *stream)
@@ -331,6 +377,7 @@ conv2d_status_t im2win_pack(const conv2d_desc_t *d, int32_t layout, const void *
     if (st != CONV2D_OK) return st;
     if (layout != IM2WIN_LAYOUT_ROW && layout != IM2WIN_LAYOUT_CL) return CONV2D_ERR_UNSUPPORTED;
     if (layout == IM2WIN_LAYOUT_CL && d->dtype == CONV2D_F32) return CONV2D_ERR_UNSUPPORTED;
+    if (layout == IM2WIN_LAYOUT_ROW && d->layout == CONV2D_NHWC) return CONV2D_ERR_UNSUPPORTED;
     if (row0 < 0 || rows < 1 || row0 + rows > p.rows_total) return CONV2D_ERR_RANGE;
     if (!x || !out) return CONV2D_ERR_NULL_POINTER;
     if (!aligned(x, 16) || !aligned(out, 16)) return CONV2D_ERR_MISALIGNED;
@@ -350,6 +397,7 @@ conv2d_status_t im2win_weight_stage(const conv2d_desc_t *d, int32_t layout, cons
     const conv2d_status_t st = make_plan(*d, &p);
     if (st != CONV2D_OK) return st;
     if (layout != IM2WIN_LAYOUT_ROW && layout != IM2WIN_LAYOUT_CL) return CONV2D_ERR_UNSUPPORTED;
+    if (layout == IM2WIN_LAYOUT_ROW && d->layout == CONV2D_NHWC) return CONV2D_ERR_UNSUPPORTED;
     if (!w || !out) return CONV2D_ERR_NULL_POINTER;
     if (!aligned(w, 16) || !aligned(out, 16)) return CONV2D_ERR_MISALIGNED;
     const LayoutGeom g = layout_geom(*d, layout);
@@ -365,13 +413,14 @@ conv2d_status_t im2win_weight_stage(const conv2d_desc_t *d, int32_t layout, cons
     sa.rows = int(sg.rows);
     sa.row_len = int(sg.row_len);
     sa.esize = int(elem_size(d->dtype));
+    sa.ohwi = d->layout == CONV2D_NHWC ? 1 : 0;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const hipError_t e = layout == IM2WIN_LAYOUT_ROW ? launch_stage_row(sa, s) : launch_stage_cl(sa, s);
     return e == hipSuccess ? CONV2D_OK : CONV2D_ERR_HIP;
 }
 
 conv2d_status_t im2win_window_gemm(const conv2d_desc_t *d, const void *win, const void *wst,
-                                   float *y, int64_t row0, int64_t rows, void *stream)
+                                   void *y, int64_t row0, int64_t rows, void *stream)
 {
     if (!d) return CONV2D_ERR_NULL_POINTER;
     conv2d_plan_t p;
@@ -384,7 +433,8 @@ conv2d_status_t im2win_window_gemm(const conv2d_desc_t *d, const void *win, cons
     if (rows * g.row_elems > kMaxElems) return CONV2D_ERR_INVALID_DESC;
     hipStream_t s = static_cast<hipStream_t>(stream);
     ProfScope ps(s, CONV2D_KERNEL_GEMM);
-    const hipError_t e = launch_gemm(*d, p, g, win, wst, y, row0, rows, s);
+    const hipError_t e = launch_gemm(*d, p, g, win, wst, make_out(*d, p.Ho, p.Wo, y, nullptr, nullptr), row0,
+                                     rows, s);
     return e == hipSuccess ? CONV2D_OK : CONV2D_ERR_HIP;
 }
 
@@ -403,7 +453,7 @@ size_t conv2d_implicit_workspace_size(const conv2d_desc_t *d)
 }
 
 conv2d_status_t conv2d_fwd_implicit(const conv2d_desc_t *d, const void *x, const void *w,
-                                    float *y, void *ws, void *stream)
+                                    void *y, void *ws, void *stream)
 {
     if (!d) return CONV2D_ERR_NULL_POINTER;
     conv2d_implicit_plan_t p;
@@ -413,11 +463,12 @@ conv2d_status_t conv2d_fwd_implicit(const conv2d_desc_t *d, const void *x, const
     if (p.ws_bytes > 0 && !ws) return CONV2D_ERR_WORKSPACE;
     if (!aligned(x, 16) || !aligned(w, 16) || !aligned(y, 16)) return CONV2D_ERR_MISALIGNED;
     if (ws && !aligned(ws, 256)) return CONV2D_ERR_MISALIGNED;
-    return run_implicit(*d, p, x, w, y, ws, static_cast<hipStream_t>(stream));
+    return run_implicit(*d, p, x, w, make_out(*d, p.Ho, p.Wo, y, nullptr, nullptr), ws,
+                        static_cast<hipStream_t>(stream));
 }
 
 conv2d_status_t im2win_implicit_gemm(const conv2d_desc_t *d, const void *x, const void *wst,
-                                     float *y, void *stream)
+                                     void *y, void *stream)
 {
     if (!d) return CONV2D_ERR_NULL_POINTER;
     conv2d_implicit_plan_t p;
@@ -427,8 +478,10 @@ conv2d_status_t im2win_implicit_gemm(const conv2d_desc_t *d, const void *x, cons
     if (!aligned(x, 16) || !aligned(wst, 16) || !aligned(y, 16)) return CONV2D_ERR_MISALIGNED;
     hipStream_t s = static_cast<hipStream_t>(stream);
     ProfScope ps(s, CONV2D_KERNEL_IMPLICIT);
-    return launch_implicit(p, implicit_args(*d, p, x, wst, y), s) == hipSuccess ? CONV2D_OK
-                                                                                : CONV2D_ERR_HIP;
+    return launch_implicit(p, implicit_args(*d, p, x, wst, make_out(*d, p.Ho, p.Wo, y, nullptr, nullptr)), s) ==
+                   hipSuccess
+               ? CONV2D_OK
+               : CONV2D_ERR_HIP;
 }
 
 conv2d_status_t conv2d_profile_enable(int32_t on)

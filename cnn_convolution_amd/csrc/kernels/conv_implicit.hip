@@ -32,6 +32,7 @@
 #include <cstdint>
 
 #include "../launch.hpp"
+#include "epilogue.hpp"
 #include "lds_dma.hpp"
 #include "tile_map.hpp"
 
@@ -44,7 +45,7 @@ constexpr int kPatchBatch = 4;   // patch vectors per thread whose loads are in 
 struct ImplicitKArgs {
     const uint16_t *x;
     const uint16_t *wst;
-    float *y;
+    OutSpec out;            // y and its epilogue
     int Cin, H, W, Cout, KH, KW, stride, pad, Ho, Wo;
     int kstage;
     int R, WB, IR, IW;
@@ -228,20 +229,23 @@ __global__ __launch_bounds__(256) void conv_implicit_kernel(const ImplicitKArgs 
 
     // epilogue: lane holds D[4*(lane/16) + v][lane%16] of every 16x16 block
     const int64_t plane = int64_t(a.Ho) * a.Wo;
-    float *const yimg = a.y + int64_t(n) * a.Cout * plane;
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
         if (!cok[j]) continue;
         const int c = wn * (NB / WN) + j * 16 + (lane & 15);
         const int i = c / a.WB;
         const int wl = c - i * a.WB;
-        float *yb = yimg + int64_t(ho0 + i) * a.Wo + wo0 + wl;
+        const int64_t p = int64_t(ho0 + i) * a.Wo + wo0 + wl;
 #pragma unroll
         for (int i2 = 0; i2 < FM; ++i2) {
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const int co = m0 + wm * (MB / WM) + i2 * 16 + (lane >> 4) * 4 + v;
-                if (co < a.Cout) yb[int64_t(co) * plane] = acc[i2][j][v];
+                if (co >= a.Cout) continue;
+                if (a.out.plain)
+                    static_cast<float *>(a.out.y)[(int64_t(n) * a.Cout + co) * plane + p] = acc[i2][j][v];
+                else
+                    out_store(a.out, n, co, p, acc[i2][j][v]);
             }
         }
     }
@@ -253,7 +257,7 @@ hipError_t launch_implicit_tile(const ImplicitArgs &h, hipStream_t s)
     ImplicitKArgs a{};
     a.x = static_cast<const uint16_t *>(h.x);
     a.wst = static_cast<const uint16_t *>(h.wst);
-    a.y = h.y;
+    a.out = h.out;
     a.Cin = h.Cin;
     a.H = h.H;
     a.W = h.W;

@@ -45,7 +45,7 @@ constexpr int kNarrowThreads = 512;
 struct NarrowKArgs {
     const void *x;
     const void *w;
-    float *y;
+    OutSpec out;            // y and its epilogue
     int Cin, H, W, Cout, KH, KW, stride, pad, Ho, Wo;
     int K, Kp;              // window run KW*KH*CP and its padded length
     int Wwin;               // (Wo - 1) * stride + KW
@@ -265,12 +265,12 @@ __global__ __launch_bounds__(kNarrowThreads) void conv_implicit_narrow_kernel(co
         else if (nb == 2) contract(std::integral_constant<int, 2>{});
         else if (nb == 1) contract(std::integral_constant<int, 1>{});
         if ((a.Wo & 3) == 0) {
-            if (nb > 0) store_blocks(acc, nb, b0, lane, a.y, n, a.Cout, cb, a.Ho, a.Wo, ho0, outs);
+            if (nb > 0) store_blocks(acc, nb, b0, lane, a.out, n, a.Cout, cb, a.Ho, a.Wo, ho0, outs);
         } else {
             __syncthreads();                         // the window rows are dead: their LDS is store scratch
             if (nb > 0)
                 store_blocks_lds(acc, nb, b0, lane, reinterpret_cast<float *>(win) + wave * kStoreScratchFloats,
-                                 a.y, n, a.Cout, cb, a.Ho, a.Wo, ho0, outs);
+                                 a.out, n, a.Cout, cb, a.Ho, a.Wo, ho0, outs);
         }
     };
     if constexpr (!PIPE) {
@@ -373,11 +373,11 @@ __global__ __launch_bounds__(kNarrowThreads) void conv_implicit_narrow_f32_kerne
                 }
         }
         if ((a.Wo & 3) == 0) {
-            if (nb > 0) store_blocks(acc, nb, b0, lane, a.y, n, a.Cout, cb, a.Ho, a.Wo, ho0, outs);
+            if (nb > 0) store_blocks(acc, nb, b0, lane, a.out, n, a.Cout, cb, a.Ho, a.Wo, ho0, outs);
         } else {
             __syncthreads();
             if (nb > 0)
-                store_blocks_lds(acc, nb, b0, lane, win + wave * kStoreScratchFloats, a.y, n, a.Cout, cb, a.Ho,
+                store_blocks_lds(acc, nb, b0, lane, win + wave * kStoreScratchFloats, a.out, n, a.Cout, cb, a.Ho,
                                  a.Wo, ho0, outs);
         }
     };
@@ -429,7 +429,7 @@ hipError_t launch_conv_implicit_narrow(const ImplicitArgs &h, hipStream_t s)
     NarrowKArgs a{};
     a.x = h.x;
     a.w = h.wst;
-    a.y = h.y;
+    a.out = h.out;
     a.Cin = h.Cin;
     a.H = h.H;
     a.W = h.W;

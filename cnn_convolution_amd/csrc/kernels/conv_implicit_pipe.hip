@@ -52,7 +52,7 @@ constexpr int kUnitsHeld = 2;     // patch units per loader lane held in registe
 struct PipeKArgs {
     const uint16_t *x;
     const uint16_t *w;
-    float *y;
+    OutSpec out;            // y and its epilogue
     int Cin, H, W, Cout, pad, Ho, Wo;
     int RW;             // output rows per task
     int row_groups;     // ceil(Ho / RW)
@@ -283,13 +283,13 @@ __device__ __forceinline__ void task_bases(int *qa, int b0, int lane, int outs, 
 // row, at its image's plane.
 template <int MAXB>
 __device__ __forceinline__ void store_blocks_images(const floatx4_t (*acc)[4], int nb, int b0, int lane,
-                                                   float *scratch, float *y, int n, int Cout, int cb,
+                                                   float *scratch, const OutSpec &o, int n, int Cout, int cb,
                                                    int plane, int outs)
 {
     const int nout = min(nb * 16, outs - b0 * 16);
     const int m = b0 * 16 + lane;
     const int im = m / plane;
-    float *const yb = y + (int64_t(n + im) * Cout + cb * 64) * plane + (m - im * plane);
+    const int p = m - im * plane;
     float *const srow = scratch + (lane & 15) * kStoreRow + 4 * (lane >> 4);
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
@@ -300,7 +300,12 @@ __device__ __forceinline__ void store_blocks_images(const floatx4_t (*acc)[4], i
         for (int r = 0; r < 16; ++r) {
             const int co = cb * 64 + c * 16 + r;
             const float v = scratch[r * kStoreRow + lane];
-            if (co < Cout && lane < nout) yb[int64_t(c * 16 + r) * plane] = v;
+            if (co < Cout && lane < nout) {
+                if (o.plain)
+                    static_cast<float *>(o.y)[(int64_t(n + im) * Cout + co) * plane + p] = v;
+                else
+                    out_store(o, n + im, co, p, v);
+            }
         }
     }
 }
@@ -501,12 +506,12 @@ __global__ __launch_bounds__(kPipeThreads) void conv_implicit_pipe_kernel(const 
             if (blk == nch - 1) {
                 if (nb > 0) {
                     if (MI)
-                        store_blocks_images<4>(acc, nb, b0, lane, scratch + wave * kStoreScratchFloats, a.y,
+                        store_blocks_images<4>(acc, nb, b0, lane, scratch + wave * kStoreScratchFloats, a.out,
                                                tk.n, a.Cout, tk.cb, a.Ho * a.Wo, outs);
                     else if ((a.Wo & 3) == 0)
-                        store_blocks(acc, nb, b0, lane, a.y, tk.n, a.Cout, tk.cb, a.Ho, a.Wo, tk.ho0, outs);
+                        store_blocks(acc, nb, b0, lane, a.out, tk.n, a.Cout, tk.cb, a.Ho, a.Wo, tk.ho0, outs);
                     else
-                        store_blocks_lds(acc, nb, b0, lane, scratch + wave * kStoreScratchFloats, a.y, tk.n,
+                        store_blocks_lds(acc, nb, b0, lane, scratch + wave * kStoreScratchFloats, a.out, tk.n,
                                          a.Cout, tk.cb, a.Ho, a.Wo, tk.ho0, outs);
                 }
 #pragma unroll
@@ -576,17 +581,17 @@ __global__ __launch_bounds__(kPipeThreads) __attribute__((amdgpu_waves_per_eu(4)
         contract_blocks<KH, KW, BF16, false, MAXB>(acc, nb, qa, fl, a.IW, lane);
     }
     if ((a.Wo & 3) == 0 && !MI) {
-        if (nb > 0) store_blocks<MAXB>(acc, nb, b0, lane, a.y, tk.n, a.Cout, tk.cb, a.Ho, a.Wo, tk.ho0, outs);
+        if (nb > 0) store_blocks<MAXB>(acc, nb, b0, lane, a.out, tk.n, a.Cout, tk.cb, a.Ho, a.Wo, tk.ho0, outs);
     } else if (MI) {
         __syncthreads();                             // the chunk is dead: LDS is store scratch
         if (nb > 0)
             store_blocks_images<MAXB>(acc, nb, b0, lane, reinterpret_cast<float *>(lds) + wave * kStoreScratchFloats,
-                                      a.y, tk.n, a.Cout, tk.cb, a.Ho * a.Wo, outs);
+                                      a.out, tk.n, a.Cout, tk.cb, a.Ho * a.Wo, outs);
     } else {
         __syncthreads();                             // the chunk is dead: LDS is store scratch
         if (nb > 0)
             store_blocks_lds<MAXB>(acc, nb, b0, lane, reinterpret_cast<float *>(lds) + wave * kStoreScratchFloats,
-                                   a.y, tk.n, a.Cout, tk.cb, a.Ho, a.Wo, tk.ho0, outs);
+                                   a.out, tk.n, a.Cout, tk.cb, a.Ho, a.Wo, tk.ho0, outs);
     }
 }
 
@@ -609,7 +614,7 @@ hipError_t launch_conv_implicit_pipe(const ImplicitArgs &h, hipStream_t s)
     PipeKArgs a;
     a.x = static_cast<const uint16_t *>(h.x);
     a.w = static_cast<const uint16_t *>(h.wst);
-    a.y = h.y;
+    a.out = h.out;
     a.Cin = h.Cin;
     a.H = h.H;
     a.W = h.W;

@@ -45,7 +45,7 @@ constexpr int kRowsThreads = 512;   // eight waves: one output row each
 struct RowsKArgs {
     const uint16_t *x;
     const uint16_t *w;
-    float *y;
+    OutSpec out;            // y and its epilogue
     int Cin, H, W, Cout, pad, Ho, Wo;
     int RW;                 // output rows per workgroup
     int row_groups;         // ceil(Ho / RW)
@@ -223,12 +223,12 @@ __global__ __launch_bounds__(kRowsThreads) void conv_implicit_rows_kernel(const 
     else if (nb == 2) contract(std::integral_constant<int, 2>{});
     else if (nb == 1) contract(std::integral_constant<int, 1>{});
     if ((a.Wo & 3) == 0) {
-        if (nb > 0) store_blocks(acc, nb, b0, lane, a.y, n, a.Cout, cb, a.Ho, a.Wo, ho0, outs);
+        if (nb > 0) store_blocks(acc, nb, b0, lane, a.out, n, a.Cout, cb, a.Ho, a.Wo, ho0, outs);
     } else {
         __syncthreads();                             // patch and filter are dead: LDS is store scratch
         if (nb > 0)
             store_blocks_lds(acc, nb, b0, lane, reinterpret_cast<float *>(lds) + wave * kStoreScratchFloats,
-                             a.y, n, a.Cout, cb, a.Ho, a.Wo, ho0, outs);
+                             a.out, n, a.Cout, cb, a.Ho, a.Wo, ho0, outs);
     }
 }
 
@@ -469,12 +469,12 @@ __global__ __launch_bounds__(kRowsThreads) void conv_implicit_rows_multi_kernel(
         else if (nb == 1) contract(std::integral_constant<int, 1>{});
     }
     if ((a.Wo & 3) == 0) {
-        if (nb > 0) store_blocks(acc, nb, b0, lane, a.y, n, a.Cout, cb, a.Ho, a.Wo, ho0, outs);
+        if (nb > 0) store_blocks(acc, nb, b0, lane, a.out, n, a.Cout, cb, a.Ho, a.Wo, ho0, outs);
     } else {
         __syncthreads();                             // patch and filter are dead: LDS is store scratch
         if (nb > 0)
             store_blocks_lds(acc, nb, b0, lane, reinterpret_cast<float *>(lds) + wave * kStoreScratchFloats,
-                             a.y, n, a.Cout, cb, a.Ho, a.Wo, ho0, outs);
+                             a.out, n, a.Cout, cb, a.Ho, a.Wo, ho0, outs);
     }
 }
 
@@ -492,7 +492,7 @@ __global__ __launch_bounds__(kRowsThreads) void conv_implicit_rows_multi_kernel(
 struct RowsF32KArgs {
     const float *x;
     const float *w;
-    float *y;
+    OutSpec out;            // y and its epilogue
     int Cin, H, W, Cout, pad, Ho, Wo;
     int RW, row_groups, co_blocks, IW;
 };
@@ -677,11 +677,11 @@ __global__ __launch_bounds__(kRowsThreads) void conv_implicit_rows_f32_kernel(co
         }
     }
     if ((a.Wo & 3) == 0) {
-        if (nb > 0) store_blocks(acc, nb, b0, lane, a.y, n, a.Cout, cb, a.Ho, a.Wo, ho0, outs);
+        if (nb > 0) store_blocks(acc, nb, b0, lane, a.out, n, a.Cout, cb, a.Ho, a.Wo, ho0, outs);
     } else {
         __syncthreads();                             // patch and filter are dead: LDS is store scratch
         if (nb > 0)
-            store_blocks_lds(acc, nb, b0, lane, ldsf + wave * kStoreScratchFloats, a.y, n, a.Cout, cb, a.Ho,
+            store_blocks_lds(acc, nb, b0, lane, ldsf + wave * kStoreScratchFloats, a.out, n, a.Cout, cb, a.Ho,
                              a.Wo, ho0, outs);
     }
 }
@@ -692,7 +692,7 @@ hipError_t launch_rows_f32(const ImplicitArgs &h, hipStream_t s)
     RowsF32KArgs a{};
     a.x = static_cast<const float *>(h.x);
     a.w = static_cast<const float *>(h.wst);
-    a.y = h.y;
+    a.out = h.out;
     a.Cin = h.Cin;
     a.H = h.H;
     a.W = h.W;
@@ -723,7 +723,7 @@ hipError_t launch_rows(const ImplicitArgs &h, hipStream_t s)
     RowsKArgs a{};
     a.x = static_cast<const uint16_t *>(h.x);
     a.w = static_cast<const uint16_t *>(h.wst);
-    a.y = h.y;
+    a.out = h.out;
     a.Cin = h.Cin;
     a.H = h.H;
     a.W = h.W;

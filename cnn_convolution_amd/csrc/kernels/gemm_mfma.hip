@@ -24,6 +24,7 @@
 #include <type_traits>
 
 #include "../launch.hpp"
+#include "epilogue.hpp"
 #include "tile_map.hpp"
 
 namespace im2win {
@@ -47,7 +48,7 @@ __device__ __forceinline__ floatx4 mfma16(const uint4 &a, const uint4 &b, const 
 
 template <int MB, int NB, int KB, int KS, int WM, int WN, bool BF16>
 __global__ __launch_bounds__(256 * KS) void gemm_mfma_kernel(
-    const uint16_t *__restrict__ win, const uint16_t *__restrict__ wst, float *__restrict__ y,
+    const uint16_t *__restrict__ win, const uint16_t *__restrict__ wst, const OutSpec o,
     int rows, int row0, int row_elems, int col_step, int krun, int kstage, int Ho, int Wo,
     int Cout, int tiles_m)
 {
@@ -251,14 +252,21 @@ __global__ __launch_bounds__(256 * KS) void gemm_mfma_kernel(
         const int r = row0 + rl;
         const int img = r / Ho;
         const int ho = r - img * Ho;
-        float *yb = y + int64_t(img) * Cout * plane + int64_t(ho) * Wo + wo;
+        const int64_t p = int64_t(ho) * Wo + wo;
+        if (o.plain) {
+            float *yb = static_cast<float *>(o.y) + int64_t(img) * Cout * plane + p;
 #pragma unroll
-        for (int i = 0; i < FM; ++i) {
+            for (int i = 0; i < FM; ++i) {
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int co = m0 + wm * (MB / WM) + i * 16 + (lane >> 4) * 4 + v;
-                if (co < Cout) yb[int64_t(co) * plane] = acc[i][j][v];
+                for (int v = 0; v < 4; ++v) {
+                    const int co = m0 + wm * (MB / WM) + i * 16 + (lane >> 4) * 4 + v;
+                    if (co < Cout) yb[int64_t(co) * plane] = acc[i][j][v];
+                }
             }
+        } else {
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+                out_store_cols4(o, img, m0 + wm * (MB / WM) + i * 16 + (lane >> 4) * 4, p, acc[i][j]);
         }
     }
 }
@@ -275,11 +283,11 @@ hipError_t launch_tile(const MfmaGemmArgs &a, hipStream_t s)
     const auto *wst = static_cast<const uint16_t *>(a.wst);
     if (a.bf16)
         hipLaunchKernelGGL((gemm_mfma_kernel<MB, NB, KB, KS, WM, WN, true>), grid, dim3(256 * KS),
-                           0, s, win, wst, a.y, a.rows, a.row0, a.row_elems, a.col_step, a.krun,
+                           0, s, win, wst, a.out, a.rows, a.row0, a.row_elems, a.col_step, a.krun,
                            a.kstage, a.Ho, a.Wo, a.Cout, tiles_m);
     else
         hipLaunchKernelGGL((gemm_mfma_kernel<MB, NB, KB, KS, WM, WN, false>), grid, dim3(256 * KS),
-                           0, s, win, wst, a.y, a.rows, a.row0, a.row_elems, a.col_step, a.krun,
+                           0, s, win, wst, a.out, a.rows, a.row0, a.row_elems, a.col_step, a.krun,
                            a.kstage, a.Ho, a.Wo, a.Cout, tiles_m);
     return hipGetLastError();
 }

@@ -24,6 +24,7 @@
 #include <cstdint>
 
 #include "../launch.hpp"
+#include "epilogue.hpp"
 #include "lds_dma.hpp"
 #include "tile_map.hpp"
 
@@ -45,7 +46,7 @@ constexpr int kAblateBuffers = 4;
 
 template <int MB, int NB, int WM, bool BF16, int ABL>
 __global__ __launch_bounds__(256) void gemm_mfma_dma_kernel(
-    const uint16_t *__restrict__ win, const uint16_t *__restrict__ wst, float *__restrict__ y,
+    const uint16_t *__restrict__ win, const uint16_t *__restrict__ wst, const OutSpec o,
     int rows, int row0, int row_elems, int col_step, int kstage, int Ho, int Wo, int Cout,
     int tiles_m)
 {
@@ -234,14 +235,21 @@ __global__ __launch_bounds__(256) void gemm_mfma_dma_kernel(
         const int r = row0 + rl;
         const int img = r / Ho;
         const int ho = r - img * Ho;
-        float *yb = y + int64_t(img) * Cout * plane + int64_t(ho) * Wo + wo;
+        const int64_t p = int64_t(ho) * Wo + wo;
+        if (o.plain) {
+            float *yb = static_cast<float *>(o.y) + int64_t(img) * Cout * plane + p;
 #pragma unroll
-        for (int i = 0; i < FM; ++i) {
+            for (int i = 0; i < FM; ++i) {
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int co = m0 + wm * (MB / WM) + i * 16 + (lane >> 4) * 4 + v;
-                if (co < Cout) yb[int64_t(co) * plane] = acc[i][j][v];
+                for (int v = 0; v < 4; ++v) {
+                    const int co = m0 + wm * (MB / WM) + i * 16 + (lane >> 4) * 4 + v;
+                    if (co < Cout) yb[int64_t(co) * plane] = acc[i][j][v];
+                }
             }
+        } else {
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+                out_store_cols4(o, img, m0 + wm * (MB / WM) + i * 16 + (lane >> 4) * 4, p, acc[i][j]);
         }
     }
 }
@@ -257,11 +265,11 @@ hipError_t launch_dma_variant(const MfmaGemmArgs &a, hipStream_t s)
     const auto *wst = static_cast<const uint16_t *>(a.wst);
     if (a.bf16)
         hipLaunchKernelGGL((gemm_mfma_dma_kernel<MB, NB, WM, true, ABL>), grid, dim3(256), 0, s, win, wst,
-                           a.y, a.rows, a.row0, a.row_elems, a.col_step, a.kstage, a.Ho, a.Wo,
+                           a.out, a.rows, a.row0, a.row_elems, a.col_step, a.kstage, a.Ho, a.Wo,
                            a.Cout, tiles_m);
     else
         hipLaunchKernelGGL((gemm_mfma_dma_kernel<MB, NB, WM, false, ABL>), grid, dim3(256), 0, s, win,
-                           wst, a.y, a.rows, a.row0, a.row_elems, a.col_step, a.kstage, a.Ho, a.Wo,
+                           wst, a.out, a.rows, a.row0, a.row_elems, a.col_step, a.kstage, a.Ho, a.Wo,
                            a.Cout, tiles_m);
     return hipGetLastError();
 }

@@ -23,6 +23,7 @@
 #include <cstdint>
 
 #include "../launch.hpp"
+#include "epilogue.hpp"
 #include "tile_map.hpp"
 
 namespace im2win {
@@ -101,7 +102,7 @@ __device__ __forceinline__ void valu_reduce(float (&acc)[MT][NT], float *red, in
 }
 
 template <int NT>
-__device__ __forceinline__ void valu_store(const float (&acc)[MT][NT], float *__restrict__ y, int cb,
+__device__ __forceinline__ void valu_store(const float (&acc)[MT][NT], const OutSpec &o, int cb,
                                            int rl, int row0, int wo0, int nvalid, int Ho, int Wo,
                                            int Cout)
 {
@@ -109,19 +110,26 @@ __device__ __forceinline__ void valu_store(const float (&acc)[MT][NT], float *__
     const int n = r / Ho;
     const int ho = r - n * Ho;
     const bool vec_ok = (Wo % 4) == 0;
+    const int64_t p = int64_t(ho) * Wo + wo0;
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
         const int co = cb * MT + m;
-        if (co < Cout)
-            store_cols<NT>(y + ((int64_t(n) * Cout + co) * Ho + ho) * Wo + wo0, acc[m], nvalid,
+        if (co >= Cout) continue;
+        if (o.plain) {
+            store_cols<NT>(static_cast<float *>(o.y) + (int64_t(n) * Cout + co) * o.plane + p, acc[m], nvalid,
                            vec_ok);
+        } else {
+#pragma unroll
+            for (int j = 0; j < NT; ++j)
+                if (j < nvalid) out_store(o, n, co, p + j, acc[m][j]);
+        }
     }
 }
 
 // Shapes known at compile time: KH, KW, S, NT.
 template <int KH, int KW, int S, int NT>
 __global__ __launch_bounds__(256) void gemm_valu_kernel(
-    const float *__restrict__ win, const float *__restrict__ wst, float *__restrict__ y, int rows,
+    const float *__restrict__ win, const float *__restrict__ wst, const OutSpec o, int rows,
     int row0, int Cin, int pos_pad, int row_elems, int Ho, int Wo, int Cout, int slots,
     int waves_m, int tiles_m, int ks)
 {
@@ -186,13 +194,13 @@ __global__ __launch_bounds__(256) void gemm_valu_kernel(
     }
     if (ks > 1) valu_reduce<NT>(acc, red, wave, lane, ks);
     if (mp.ksi != 0 || nvalid <= 0) return;
-    valu_store<NT>(acc, y, mp.cb, rl, row0, wo0, nvalid, Ho, Wo, Cout);
+    valu_store<NT>(acc, o, mp.cb, rl, row0, wo0, nvalid, Ho, Wo, Cout);
 }
 
 // Any shape: taps loaded one element at a time (used for shapes without a
 // compiled specialisation; same work split, NT = 4).
 __global__ __launch_bounds__(256) void gemm_valu_generic_kernel(
-    const float *__restrict__ win, const float *__restrict__ wst, float *__restrict__ y, int rows,
+    const float *__restrict__ win, const float *__restrict__ wst, const OutSpec o, int rows,
     int row0, int Cin, int pos_pad, int row_elems, int KH, int KW, int S, int Ho, int Wo, int Cout,
     int slots, int waves_m, int tiles_m, int ks)
 {
@@ -235,7 +243,7 @@ __global__ __launch_bounds__(256) void gemm_valu_generic_kernel(
     }
     if (ks > 1) valu_reduce<NT>(acc, red, wave, lane, ks);
     if (mp.ksi != 0 || nvalid <= 0) return;
-    valu_store<NT>(acc, y, mp.cb, rl, row0, wo0, nvalid, Ho, Wo, Cout);
+    valu_store<NT>(acc, o, mp.cb, rl, row0, wo0, nvalid, Ho, Wo, Cout);
 }
 
 struct ValuGrid {
@@ -264,7 +272,7 @@ hipError_t launch_spec(const ValuGemmArgs &a, hipStream_t s)
 {
     const ValuGrid g = valu_grid(a, NT);
     hipLaunchKernelGGL((gemm_valu_kernel<KH, KW, S, NT>), dim3(g.blocks), dim3(256), 0, s, a.win,
-                       a.wst, a.y, a.rows, a.row0, a.Cin, a.pos_pad, a.row_elems, a.Ho, a.Wo, a.Cout,
+                       a.wst, a.out, a.rows, a.row0, a.Cin, a.pos_pad, a.row_elems, a.Ho, a.Wo, a.Cout,
                        g.slots, g.waves_m, g.tiles_m, g.ks);
     return hipGetLastError();
 }
@@ -272,7 +280,7 @@ hipError_t launch_spec(const ValuGemmArgs &a, hipStream_t s)
 hipError_t launch_generic(const ValuGemmArgs &a, hipStream_t s)
 {
     const ValuGrid g = valu_grid(a, 4);
-    hipLaunchKernelGGL(gemm_valu_generic_kernel, dim3(g.blocks), dim3(256), 0, s, a.win, a.wst, a.y,
+    hipLaunchKernelGGL(gemm_valu_generic_kernel, dim3(g.blocks), dim3(256), 0, s, a.win, a.wst, a.out,
                        a.rows, a.row0, a.Cin, a.pos_pad, a.row_elems, a.KH, a.KW, a.stride, a.Ho,
                        a.Wo, a.Cout, g.slots, g.waves_m, g.tiles_m, g.ks);
     return hipGetLastError();

@@ -9,6 +9,7 @@
 
 #include <cstdint>
 
+#include "epilogue.hpp"
 #include "lds_dma.hpp"
 
 namespace im2win {
@@ -46,29 +47,52 @@ __device__ __forceinline__ void block_bases(int *qa, int b0, int lane, int outs,
 
 // Lane l holds D[4*(l/16) + v][l % 16] of each 16 x 16 block: 4 consecutive
 // outputs m of output channel co = block column l % 16, which are 4
-// consecutive floats of the plane (one 16-byte store when Wo % 4 == 0).
-// acc holds MAXB blocks, nb <= MAXB of them in use.
+// consecutive elements of the plane (one 16-byte fp32 or 8-byte half store
+// when Wo % 4 == 0 and y is NCHW). acc holds MAXB blocks, nb <= MAXB of them
+// in use. Outputs through the epilogue of o (y type, scale, bias, layout).
 template <int MAXB = 4>
 __device__ __forceinline__ void store_blocks(const floatx4_t (*acc)[4], int nb, int b0, int lane,
-                                             float *y, int n, int Cout, int cb, int Ho, int Wo,
+                                             const OutSpec &o, int n, int Cout, int cb, int Ho, int Wo,
                                              int ho0, int outs)
 {
     const int64_t plane = int64_t(Ho) * Wo;
+    if (o.plain) {
+        float *const y = static_cast<float *>(o.y);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int co = cb * 64 + c * 16 + (lane & 15);
+            if (co >= Cout) continue;
+            float *yb = y + (int64_t(n) * Cout + co) * plane + int64_t(ho0) * Wo;
+#pragma unroll
+            for (int s = 0; s < MAXB; ++s) {
+                if (s >= nb) break;
+                const int m = (b0 + s) * 16 + (lane >> 4) * 4;
+                if ((Wo & 3) == 0) {
+                    if (m < outs) *reinterpret_cast<floatx4_t *>(yb + m) = acc[s][c];
+                } else {
+#pragma unroll
+                    for (int v = 0; v < 4; ++v)
+                        if (m + v < outs) yb[m + v] = acc[s][c][v];
+                }
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
         const int co = cb * 64 + c * 16 + (lane & 15);
         if (co >= Cout) continue;
-        float *yb = y + (int64_t(n) * Cout + co) * plane + int64_t(ho0) * Wo;
 #pragma unroll
         for (int s = 0; s < MAXB; ++s) {
             if (s >= nb) break;
             const int m = (b0 + s) * 16 + (lane >> 4) * 4;
-            if ((Wo & 3) == 0) {
-                if (m < outs) *reinterpret_cast<floatx4_t *>(yb + m) = acc[s][c];
+            const int64_t p = int64_t(ho0) * Wo + m;
+            if ((Wo & 3) == 0 && !o.nhwc) {
+                if (m < outs) out_store4(o, out_offset(o, n, co, p), co, acc[s][c]);
             } else {
 #pragma unroll
                 for (int v = 0; v < 4; ++v)
-                    if (m + v < outs) yb[m + v] = acc[s][c][v];
+                    if (m + v < outs) out_store(o, n, co, p + v, acc[s][c][v]);
             }
         }
     }
@@ -90,12 +114,12 @@ constexpr int kStoreScratchFloats = 16 * kStoreRow;
 // complete in order, so no barrier is needed between the 4 blocks.
 template <int MAXB = 4>
 __device__ __forceinline__ void store_blocks_lds(const floatx4_t (*acc)[4], int nb, int b0, int lane,
-                                                 float *scratch, float *y, int n, int Cout, int cb,
+                                                 float *scratch, const OutSpec &o, int n, int Cout, int cb,
                                                  int Ho, int Wo, int ho0, int outs)
 {
     const int64_t plane = int64_t(Ho) * Wo;
     const int nout = min(nb * 16, outs - b0 * 16);   // this wave's outputs
-    float *const yb = y + (int64_t(n) * Cout + cb * 64) * plane + int64_t(ho0) * Wo + b0 * 16;
+    const int64_t p0 = int64_t(ho0) * Wo + b0 * 16;   // their first position in the plane
     float *const srow = scratch + (lane & 15) * kStoreRow + 4 * (lane >> 4);
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
@@ -106,7 +130,12 @@ __device__ __forceinline__ void store_blocks_lds(const floatx4_t (*acc)[4], int 
         for (int r = 0; r < 16; ++r) {
             const int co = cb * 64 + c * 16 + r;
             const float v = scratch[r * kStoreRow + lane];
-            if (co < Cout && lane < nout) yb[int64_t(c * 16 + r) * plane + lane] = v;
+            if (co < Cout && lane < nout) {
+                if (o.plain)
+                    static_cast<float *>(o.y)[(int64_t(n) * Cout + co) * plane + p0 + lane] = v;
+                else
+                    out_store(o, n, co, p0 + lane, v);
+            }
         }
     }
 }

@@ -10,6 +10,7 @@
 // the result is bit-identical to the definition. Both are HBM-bound.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
@@ -380,6 +381,62 @@ __global__ __launch_bounds__(256) void pack_cl_staged_kernel(
     }
 }
 
+// Channels-last window rows from NHWC x: element (pos = w*KH + kh, ci) of
+// window row r = n*Ho + ho is x[n][ho*stride + kh - pad][w - pad][ci], zero
+// outside the image and for the padding channels ci >= Cin; every element of
+// the row's row_elems, the spare tail included, is written. One 16-byte
+// output vector per thread, consecutive threads on consecutive vectors of a
+// row: with Cin % 8 == 0 it is 8 channels of one input position, one 16-byte
+// load (the channels of a position are contiguous in NHWC); else 2-byte
+// gathers.
+__global__ __launch_bounds__(256) void pack_cl_nhwc_kernel(const uint16_t *__restrict__ x,
+                                                           uint16_t *__restrict__ out, int Cin, int H, int W,
+                                                           int KH, int stride, int pad, int Ho, int Wwin,
+                                                           int Cin_pad, int row_elems, int row0, int rows)
+{
+    const int vpr = row_elems >> 3;
+    const int npos = Wwin * KH;
+    const int64_t total = int64_t(rows) * vpr;
+    for (int64_t t = int64_t(blockIdx.x) * 256 + threadIdx.x; t < total; t += int64_t(gridDim.x) * 256) {
+        const int rl = int(t / vpr);
+        const int e0 = int(t - int64_t(rl) * vpr) * 8;
+        const int r = row0 + rl;
+        const int n = r / Ho;
+        const int ho = r - n * Ho;
+        uint4 o{0u, 0u, 0u, 0u};
+        if (Cin % 8 == 0) {                             // Cin_pad == Cin
+            const int pos = e0 / Cin;
+            if (pos < npos) {
+                const int c0 = e0 - pos * Cin;
+                const int wc = pos / KH;
+                const int kh = pos - wc * KH;
+                const int ih = ho * stride + kh - pad;
+                const int iw = wc - pad;
+                if (unsigned(ih) < unsigned(H) && unsigned(iw) < unsigned(W))
+                    o = *reinterpret_cast<const uint4 *>(x + ((int64_t(n) * H + ih) * W + iw) * Cin + c0);
+            }
+        } else {
+            uint32_t v[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int k = e0 + e;
+                const int pos = k / Cin_pad;
+                const int ci = k - pos * Cin_pad;
+                if (pos < npos && ci < Cin) {
+                    const int wc = pos / KH;
+                    const int kh = pos - wc * KH;
+                    const int ih = ho * stride + kh - pad;
+                    const int iw = wc - pad;
+                    if (unsigned(ih) < unsigned(H) && unsigned(iw) < unsigned(W))
+                        v[e >> 1] |= uint32_t(x[((int64_t(n) * H + ih) * W + iw) * Cin + ci]) << (16 * (e & 1));
+                }
+            }
+            o = uint4{v[0], v[1], v[2], v[3]};
+        }
+        *reinterpret_cast<uint4 *>(out + int64_t(rl) * row_elems + e0) = o;
+    }
+}
+
 }  // namespace
 
 // staging workgroups a pack launch carries: about 4 filter elements per
@@ -437,6 +494,16 @@ constexpr int kStagedLdsBytes = 63 * 1024;   // plus 1 KB of spill slots: within
 
 hipError_t launch_pack_cl(const PackArgs &a, hipStream_t s, const StageArgs *fold, bool *folded)
 {
+    if (a.nhwc) {
+        if (folded) *folded = false;
+        if (a.esize != 2 || a.row_elems % 8 != 0 || a.Cin_pad % 4 != 0) return hipErrorInvalidValue;
+        const int64_t vecs = int64_t(a.rows) * (a.row_elems / 8);
+        const int64_t blocks = std::min<int64_t>((vecs + 255) / 256, 1 << 18);
+        hipLaunchKernelGGL(pack_cl_nhwc_kernel, dim3(unsigned(blocks)), dim3(256), 0, s,
+                           static_cast<const uint16_t *>(a.x), static_cast<uint16_t *>(a.out), a.Cin, a.H,
+                           a.W, a.KH, a.stride, a.pad, a.Ho, a.Wwin, a.Cin_pad, a.row_elems, a.row0, a.rows);
+        return hipGetLastError();
+    }
     if (folded) *folded = false;
     if (a.esize != 2) return hipErrorInvalidValue;
     const auto *x = static_cast<const uint16_t *>(a.x);

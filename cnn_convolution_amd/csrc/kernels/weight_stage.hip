@@ -47,6 +47,30 @@ __global__ __launch_bounds__(256) void stage_cl_vec8_kernel(const uint16_t *__re
                   gridDim.x * blockDim.x);
 }
 
+// NHWC filters (w [Cout][KH][KW][Cin]) into the channels-last K order:
+// out[co][(kw*KH + kh)*Cin_pad + ci] = w[co][kh][kw][ci]; every element of
+// the rows x row_len staged filter is written (zero past Cout, Cin and K).
+__global__ __launch_bounds__(256) void stage_cl_ohwi_kernel(const uint16_t *__restrict__ w,
+                                                            uint16_t *__restrict__ out, int Cout, int Cin,
+                                                            int KH, int KW, int Cin_pad, int rows, int row_len)
+{
+    const int krun = KW * KH * Cin_pad;
+    const unsigned total = unsigned(rows) * unsigned(row_len);
+    for (unsigned e = blockIdx.x * blockDim.x + threadIdx.x; e < total; e += gridDim.x * blockDim.x) {
+        const int co = int(e / unsigned(row_len));
+        const int k = int(e) - co * row_len;
+        uint16_t v = 0;
+        if (co < Cout && k < krun) {
+            const int pos = k / Cin_pad;
+            const int ci = k - pos * Cin_pad;
+            const int kw = pos / KH;
+            const int kh = pos - kw * KH;
+            if (ci < Cin) v = w[((co * KH + kh) * KW + kw) * Cin + ci];
+        }
+        out[e] = v;
+    }
+}
+
 unsigned grid_for(int64_t total)
 {
     int64_t b = (total + 255) / 256;
@@ -74,6 +98,13 @@ hipError_t launch_stage_row(const StageArgs &a, hipStream_t s)
 
 hipError_t launch_stage_cl(const StageArgs &a, hipStream_t s)
 {
+    if (a.ohwi) {
+        if (a.esize != 2) return hipErrorInvalidValue;
+        hipLaunchKernelGGL(stage_cl_ohwi_kernel, dim3(grid_for(int64_t(a.rows) * a.row_len)), dim3(256), 0, s,
+                           static_cast<const uint16_t *>(a.w), static_cast<uint16_t *>(a.out), a.Cout, a.Cin,
+                           a.KH, a.KW, a.Cin_pad, a.rows, a.row_len);
+        return hipGetLastError();
+    }
     if (a.esize == 2 && a.Cin_pad % 8 == 0 && a.row_len % 8 == 0) {
         // one 16-byte output vector per thread
         hipLaunchKernelGGL(stage_cl_vec8_kernel, dim3(grid_for(int64_t(a.Cout) * (a.row_len / 8))), dim3(256),

@@ -11,6 +11,21 @@
 
 namespace im2win {
 
+// Output of every convolution kernel: y = scale[co] * (conv + bias[co]) (each
+// factor optional), rounded once to the storage type of y, at its NCHW or
+// NHWC offset. `plain` marks fp32 NCHW y with neither factor, the kernels'
+// own fp32 store path.
+struct OutSpec {
+    void *y;
+    const float *scale;     // [Cout] or nullptr (a factor of 1)
+    const float *bias;      // [Cout] or nullptr (no bias)
+    int type;               // 0 fp32, 1 fp16, 2 bf16
+    int nhwc;               // 1: y [N][Ho][Wo][Cout]; 0: y [N][Cout][Ho][Wo]
+    int plain;              // type 0, NCHW, no scale, no bias
+    int Cout;
+    int64_t plane;          // Ho * Wo
+};
+
 struct PackArgs {
     const void *x;          // NCHW input
     void *out;              // window rows [rows][row_elems]
@@ -18,6 +33,7 @@ struct PackArgs {
     int Cin_pad, pos_pad, row_elems;
     int row0, rows;         // window rows r in [row0, row0 + rows)
     int esize;              // 2 or 4 bytes
+    int nhwc;               // x is [N][H][W][Cin] (channels-last window layout only)
 };
 struct StageArgs;
 // A pack launch can carry the filter staging along, as extra workgroups
@@ -34,6 +50,7 @@ struct StageArgs {
     int Cout, Cin, KH, KW;
     int Cin_pad, rows, row_len;  // staged geometry
     int esize;
+    int ohwi;               // w is [Cout][KH][KW][Cin] (channels-last order only)
 };
 hipError_t launch_stage_row(const StageArgs &a, hipStream_t s);
 hipError_t launch_stage_cl(const StageArgs &a, hipStream_t s);
@@ -41,7 +58,7 @@ hipError_t launch_stage_cl(const StageArgs &a, hipStream_t s);
 struct ValuGemmArgs {
     const float *win;       // window chunk [rows][Cin][pos_pad]
     const float *wst;       // staged filter [Cout_stage/16][Cin][KH][KW][16]
-    float *y;               // [N][Cout][Ho][Wo]
+    OutSpec out;            // y and its epilogue
     int rows, row0, Cin, pos_pad, row_elems;
     int KH, KW, stride;
     int Ho, Wo, Cout, Cout_stage;
@@ -52,7 +69,7 @@ hipError_t launch_gemm_valu_f32(const ValuGemmArgs &a, hipStream_t s);
 struct MfmaGemmArgs {
     const void *win;        // window chunk [rows][row_elems] (channels-last)
     const void *wst;        // staged filter [Cout][K_stage]
-    float *y;
+    OutSpec out;            // y and its epilogue
     int rows, row0, row_elems;
     int col_step;           // stride*KH*Cin_pad: window start step between columns
     int krun;               // KW*KH*Cin_pad: window length
@@ -75,7 +92,7 @@ hipError_t launch_gemm_mfma_dma(const MfmaGemmArgs &a, hipStream_t s);
 struct ImplicitArgs {
     const void *x;          // NCHW input
     const void *wst;        // staged filter [Cout][kstage], K order (kw, kh, ci)
-    float *y;
+    OutSpec out;            // y and its epilogue
     int N, Cin, H, W, Cout, KH, KW, stride, pad, Ho, Wo;
     int kstage;             // KW*KH*Cin
     int R, WB, IR, IW;
@@ -98,7 +115,7 @@ hipError_t launch_conv_implicit_rows(const ImplicitArgs &a, hipStream_t s);
 // filter in LDS; wst is w itself
 hipError_t launch_conv_implicit_narrow(const ImplicitArgs &a, hipStream_t s);
 // pipelined row-block form (fp16/bf16, Cin % 32 == 0, stride 1, R * Wo <=
-// 256, 1x1 or 3x3): fs_groups persistent workgroups over tasks of R whole
+// 256, 1x1 or 3x3): `groups` persistent workgroups over tasks of R whole
 // output rows x 64 output channels, 32-channel K chunks double-buffered in
 // LDS by four loader waves while four waves contract; wst is w itself
 hipError_t launch_conv_implicit_pipe(const ImplicitArgs &a, hipStream_t s);

@@ -45,7 +45,7 @@ conv2d_status_t scratch_on_current_device(void **out)
 }  // namespace
 
 extern "C" conv2d_status_t conv2d_fwd_noalloc(const conv2d_desc_t *d, const void *x, const void *w,
-                                               float *y, void *stream)
+                                               void *y, void *stream)
 {
     if (!d) return CONV2D_ERR_NULL_POINTER;
     conv2d_plan_t p;

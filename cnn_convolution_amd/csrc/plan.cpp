@@ -17,6 +17,11 @@ namespace im2win {
 conv2d_status_t check_desc(const conv2d_desc_t &d) {
     if (d.dtype != CONV2D_F32 && d.dtype != CONV2D_F16 && d.dtype != CONV2D_BF16)
         return CONV2D_ERR_UNSUPPORTED;
+    if (d.y_dtype != CONV2D_F32 && d.y_dtype != CONV2D_F16 && d.y_dtype != CONV2D_BF16)
+        return CONV2D_ERR_UNSUPPORTED;
+    if (d.layout != CONV2D_NCHW && d.layout != CONV2D_NHWC) return CONV2D_ERR_UNSUPPORTED;
+    // NHWC runs the channels-last window form only, which is half precision
+    if (d.layout == CONV2D_NHWC && d.dtype == CONV2D_F32) return CONV2D_ERR_UNSUPPORTED;
     if (d.reserved != 0) return CONV2D_ERR_INVALID_DESC;
     if (d.N < 1 || d.Cin < 1 || d.H < 1 || d.W < 1 || d.Cout < 1 || d.KH < 1 || d.KW < 1 ||
         d.stride < 1 || d.pad < 0)
@@ -639,6 +644,8 @@ static conv2d_status_t compute_implicit_plan(const conv2d_desc_t &d, conv2d_impl
     p->Wo = Wo;
     p->K_stage = d.KW * d.KH * d.Cin;
     p->flops = 2 * d.N * d.Cout * Ho * Wo * d.Cin * d.KH * d.KW;
+    // the implicit kernels load NCHW planes; NHWC takes the window form
+    if (d.layout == CONV2D_NHWC) return CONV2D_ERR_UNSUPPORTED;
     if (d.Cin <= 8) {
         // few input channels: the narrow-channel kernel, any dtype
         pick_implicit_narrow(d, Ho, Wo, p);

@@ -8,8 +8,9 @@
  *                                       * w[co][ci][kh][kw]
  *
  * with xp = x zero-padded by `pad` on all four sides: a cross-correlation (no
- * kernel flip), one stride and one padding for both axes, no bias, dilation
- * or groups. Sources: "Enabling Memory-efficient Im2win Convolution with
+ * kernel flip), one stride and one padding for both axes, no dilation or
+ * groups. conv2d_fwd_ex adds the epilogue y = scale[co] * (conv + bias[co]).
+ * Sources: "Enabling Memory-efficient Im2win Convolution with
  * Multi-precision Support on GPU CUDA and Tensor Cores", Sec. III-A Eq. (1)
  * (the sum), Sec. III-B Eq. (2) (the window tensor), Sec. III-C Eq. (3) and
  * Sec. III-D with Algorithm 1 (the window contraction as a GEMM with
@@ -31,9 +32,12 @@
  *     workspace at most 1/KW of the im2col buffer whenever one window row fits
  *     in that budget.
  *
- * Layouts: x, w, y are dense, contiguous NCHW: x [N][Cin][H][W] of `dtype`,
- * w [Cout][Cin][KH][KW] of `dtype`, y [N][Cout][Ho][Wo] of float (fp32 for
- * every input dtype).
+ * Layouts (conv2d_desc_t.layout): dense and contiguous,
+ *   CONV2D_NCHW (default): x [N][Cin][H][W], w [Cout][Cin][KH][KW], y [N][Cout][Ho][Wo];
+ *   CONV2D_NHWC          : x [N][H][W][Cin], w [Cout][KH][KW][Cin], y [N][Ho][Wo][Cout]
+ *                          (fp16/bf16 inputs only; channels innermost, the input
+ *                          layout of the tensor-core design of Sec. III-D).
+ * x and w are of `dtype`; y of `y_dtype` (fp32 by default, whatever `dtype`).
  *
  * Pointers: x, w, y, ws and the pack/stage outputs are DEVICE pointers the
  * caller allocates and owns. The library allocates no device memory and
@@ -61,7 +65,7 @@
 extern "C" {
 #endif
 
-/* Storage type of x and w (y is always fp32). */
+/* Storage type of x and w (conv2d_desc_t.dtype) and of y (y_dtype). */
 typedef enum {
     CONV2D_F32 = 0,   /* IEEE binary32; fp32 products on the matrix cores (row-
                          block and narrow kernels) or the vector ALUs           */
@@ -69,12 +73,19 @@ typedef enum {
     CONV2D_BF16 = 2   /* bfloat16; matrix cores, fp32 accumulation             */
 } conv2d_dtype_t;
 
-/* The layer. All sizes in elements. */
+/* Memory layout of x, w and y. */
+typedef enum { CONV2D_NCHW = 0, CONV2D_NHWC = 1 } conv2d_layout_t;
+
+/* The layer. All sizes in elements. A zero-initialised tail (y_dtype, layout,
+ * reserved) is the plain convolution: fp32 NCHW output. */
 typedef struct {
     int64_t N, Cin, H, W;     /* input batch, channels, height, width          */
     int64_t Cout, KH, KW;     /* filters, filter height, filter width          */
     int64_t stride, pad;      /* one stride and one zero padding for both axes */
-    int32_t dtype;            /* a conv2d_dtype_t                              */
+    int32_t dtype;            /* a conv2d_dtype_t: storage type of x and w     */
+    int32_t y_dtype;          /* a conv2d_dtype_t: storage type of y; the fp32
+                                 result is rounded once, to nearest even       */
+    int32_t layout;           /* a conv2d_layout_t (NHWC: fp16/bf16 only)      */
     int32_t reserved;         /* must be 0                                     */
 } conv2d_desc_t;
 
@@ -85,7 +96,8 @@ typedef enum {
     CONV2D_ERR_NULL_POINTER = 2,  /* a required pointer is NULL                     */
     CONV2D_ERR_MISALIGNED = 3,    /* x, w, y or an output not 16-byte aligned;
                                      ws not 256-byte aligned                        */
-    CONV2D_ERR_UNSUPPORTED = 4,   /* unknown dtype or layout for this call          */
+    CONV2D_ERR_UNSUPPORTED = 4,   /* unknown dtype, y_dtype or layout; NHWC with fp32
+                                     inputs; a form that does not take the layer     */
     CONV2D_ERR_WORKSPACE = 5,     /* ws NULL although a workspace is needed         */
     CONV2D_ERR_HIP = 6,           /* the HIP runtime reported an error on launch    */
     CONV2D_ERR_RANGE = 7,         /* a row range outside [0, N*Ho)                  */
@@ -167,15 +179,29 @@ conv2d_status_t conv2d_plan(const conv2d_desc_t *d, conv2d_plan_t *out);
  * aligned device pointers. Errors: CONV2D_ERR_HIP when a launch fails (the
  * runtime refused it, or the kernel's own launch check did); launches of
  * earlier steps of the same call may then have been enqueued. */
-conv2d_status_t conv2d_fwd(const conv2d_desc_t *d, const void *x, const void *w, float *y,
+conv2d_status_t conv2d_fwd(const conv2d_desc_t *d, const void *x, const void *w, void *y,
                            void *ws, void *stream);
+
+/* y = scale[co] * (conv2d(x, w) + bias[co]), the same call with the
+ * epilogue of a convolution layer: a per-output-channel bias (the bias
+ * argument of the convolution of "Unifying Convolutions and GEMM", Sec. 5)
+ * and a per-output-channel scale folded into the output pass (the scale
+ * folding of "Fast and Memory-Efficient Wavelet Convolutions via I/O-Aware
+ * Reformulation": s * (X * W + b) = X * (s W) + s b, so the scale needs no
+ * pass of its own). Both are applied to the fp32 accumulator in the kernel
+ * that stores y, before the single rounding to y_dtype. scale, bias: fp32
+ * [Cout] device arrays, 4-byte aligned, or NULL (scale 1, bias 0); owned by
+ * the caller. Other arguments and errors as conv2d_fwd. */
+conv2d_status_t conv2d_fwd_ex(const conv2d_desc_t *d, const void *x, const void *w, const float *scale,
+                              const float *bias, void *y, void *ws, void *stream);
 
 /* Row (a2) on its own: write window rows [row0, row0 + rows) of the window
  * tensor of x (Eq. (2) of the im2win paper, zero padding included) in the
  * given layout to `out`, with the row length, Cin_pad and pos_pad that
  * conv2d_plan reports for that layout. A pure copy: every value is bit-equal
  * to an element of x or zero. out must hold rows * row_elems elements of
- * dtype and be 16-byte aligned. */
+ * dtype and be 16-byte aligned. x in the descriptor's layout (NHWC: the
+ * channels-last window layout only). */
 conv2d_status_t im2win_pack(const conv2d_desc_t *d, int32_t layout, const void *x, void *out,
                             int64_t row0, int64_t rows, void *stream);
 
@@ -183,7 +209,7 @@ conv2d_status_t im2win_pack(const conv2d_desc_t *d, int32_t layout, const void *
  *   ROW: out[cb][ci][kh][kw][j] = w[cb*16 + j][ci][kh][kw], j < 16, Cout padded
  *        to a multiple of 16 with zeros (fp32 path);
  *   CL : out[co][(kw*KH + kh)*Cin_pad + ci] = w[co][ci][kh][kw], rows padded to
- *        Cout_stage and to K_stage with zeros.
+ *        Cout_stage and to K_stage with zeros (w[co][kh][kw][ci] for NHWC).
  * out holds Cout_stage * K_stage elements of dtype and is 16-byte aligned. */
 conv2d_status_t im2win_weight_stage(const conv2d_desc_t *d, int32_t layout, const void *w,
                                     void *out, void *stream);
@@ -194,11 +220,12 @@ conv2d_status_t im2win_weight_stage(const conv2d_desc_t *d, int32_t layout, cons
  * layout conv2d_plan reports for d (as im2win_pack writes them, row length
  * row_elems); `wst` holds the staged filter of that layout (as
  * im2win_weight_stage writes it; for a 1x1 filter whose plan has
- * wstage_bytes == 0, w itself). fp32 accumulation, fp32 output.
+ * wstage_bytes == 0, w itself). fp32 accumulation; y of the descriptor's
+ * y_dtype and layout, no bias or scale.
  * ("Enabling Memory-efficient Im2win Convolution ...", Sec. III-C Eq. (3),
  * Sec. III-D Algorithm 1.) Device pointers, 16-byte aligned. */
 conv2d_status_t im2win_window_gemm(const conv2d_desc_t *d, const void *win, const void *wst,
-                                   float *y, int64_t row0, int64_t rows, void *stream);
+                                   void *y, int64_t row0, int64_t rows, void *stream);
 
 const char *conv2d_status_string(conv2d_status_t s);
 
@@ -215,7 +242,7 @@ const char *conv2d_status_string(conv2d_status_t s);
  * share its array: calls that overlap on one GPU (several streams or host
  * threads) race on it and must be ordered by the caller. */
 #define IM2WIN_NOALLOC_SCRATCH_BYTES (32u << 20)
-conv2d_status_t conv2d_fwd_noalloc(const conv2d_desc_t *d, const void *x, const void *w, float *y,
+conv2d_status_t conv2d_fwd_noalloc(const conv2d_desc_t *d, const void *x, const void *w, void *y,
                                    void *stream);
 
 /* ---- implicit (fused) form ---------------------------------------------
@@ -273,9 +300,10 @@ typedef struct {
 } conv2d_implicit_plan_t;
 
 /* Fill *out for *d. CONV2D_ERR_UNSUPPORTED when the implicit form does not
- * take the layer (fp32 outside the row-block kernel's layers, Cin past 8 and
- * not a multiple of 64 outside the pipelined row-block kernel's layers, or no
- * tile whose patch fits in LDS); other errors as conv2d_plan. Host only. */
+ * take the layer (NHWC, fp32 outside the row-block and narrow kernels' layers,
+ * Cin past 8 and not a multiple of 64 outside the pipelined row-block
+ * kernel's layers, or no tile whose patch fits in LDS); other errors as
+ * conv2d_plan. Host only. */
 conv2d_status_t conv2d_implicit_plan(const conv2d_desc_t *d, conv2d_implicit_plan_t *out);
 
 /* Bytes of workspace conv2d_fwd_implicit needs (0 if d is invalid or not
@@ -287,16 +315,17 @@ size_t conv2d_implicit_workspace_size(const conv2d_desc_t *d);
  * bytes (NULL allowed when that is 0). Returns CONV2D_ERR_UNSUPPORTED, and
  * launches nothing, for a layer conv2d_implicit_plan does not take. */
 conv2d_status_t conv2d_fwd_implicit(const conv2d_desc_t *d, const void *x, const void *w,
-                                    float *y, void *ws, void *stream);
+                                    void *y, void *ws, void *stream);
 
 /* Rows (a2, a4, a5) of the implicit form on their own: the implicit kernel
  * with a filter already staged in the window's K order (as
  * im2win_weight_stage writes it for IM2WIN_LAYOUT_CL), or w itself where the
  * plan keeps no staged filter (conv2d_implicit_workspace_size(d) == 0: a 1x1
  * filter, or the row-block kernels, which reorder w in LDS on their own),
- * writing all of y. Device pointers, 16-byte aligned. */
+ * writing all of y (y_dtype of the descriptor, no bias or scale). Device
+ * pointers, 16-byte aligned. */
 conv2d_status_t im2win_implicit_gemm(const conv2d_desc_t *d, const void *x, const void *wst,
-                                     float *y, void *stream);
+                                     void *y, void *stream);
 
 /* ---- measurement hook --------------------------------------------------
  * While enabled, conv2d_fwd and conv2d_fwd_implicit record a HIP event pair

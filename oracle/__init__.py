@@ -6,6 +6,8 @@ this package imports nothing from it.
 
 * ``conv2d`` / ``conv2d_points``: the direct sum in float64 (plain C, OpenMP),
   see ``conv2d_oracle.c`` for the definition and its sources.
+* ``conv2d_ex`` / ``conv2d_points_ex``: the same sum with the layer epilogue
+  y = scale[co] * (sum + bias[co]) and the NHWC layout, in float64.
 * ``im2win`` / ``window_conv``: a numpy model of the im2win transform and of
   the convolution read off the window tensor (``im2win_model.py``).
 """
@@ -117,3 +119,70 @@ def conv2d(x, w, stride=1, pad=0, nthreads=0):
 
 def conv2d_points(x, w, stride, pad, idx, nthreads=0):
     return default().conv2d_points(x, w, stride, pad, idx, nthreads)
+
+
+def _vec64(v, n):
+    if v is None:
+        return None
+    v = np.asarray(v.detach().cpu().double().numpy() if hasattr(v, "detach") else v, np.float64)
+    if v.shape != (n,):
+        raise ValueError(f"expected {n} per-channel values, got shape {v.shape}")
+    return v
+
+
+def _nchw(x, w, layout):
+    """x, w of `layout` as NCHW / OIHW float64 arrays (a transpose, no arithmetic)."""
+    x = Oracle._f64(x)
+    w = Oracle._f64(w)
+    if layout == "nhwc":                 # x [N][H][W][C], w [Cout][KH][KW][Cin]
+        x = np.ascontiguousarray(x.transpose(0, 3, 1, 2))
+        w = np.ascontiguousarray(w.transpose(0, 3, 1, 2))
+    elif layout != "nchw":
+        raise ValueError(f"unknown layout {layout!r}")
+    return x, w
+
+
+def conv2d_ex(x, w, stride=1, pad=0, bias=None, scale=None, layout="nchw", nthreads=0):
+    """y = scale[co] * (conv2d(x, w) + bias[co]) in float64, x, w and y in
+    `layout` ("nchw", or "nhwc": x [N][H][W][Cin], w [Cout][KH][KW][Cin],
+    y [N][Ho][Wo][Cout]).
+
+    The bias is the per-output-channel bias of the convolution call of
+    "Unifying Convolutions and GEMM" (Sec. 5); the scale is the learned
+    per-channel scale of "Fast and Memory-Efficient Wavelet Convolutions via
+    I/O-Aware Reformulation" (scale folding), which multiplies the
+    convolution and its bias alike (s * (X * W + b) = X * (s W) + s b).
+    The NHWC layout is the input layout of the tensor-core design of
+    "Enabling Memory-efficient Im2win Convolution ...", Sec. III-D. Either
+    factor may be None."""
+    x, w = _nchw(x, w, layout)
+    y = conv2d(x, w, stride, pad, nthreads)
+    b = _vec64(bias, w.shape[0])
+    s = _vec64(scale, w.shape[0])
+    if b is not None:
+        y = y + b[None, :, None, None]
+    if s is not None:
+        y = y * s[None, :, None, None]
+    return np.ascontiguousarray(y.transpose(0, 2, 3, 1)) if layout == "nhwc" else y
+
+
+def conv2d_points_ex(x, w, stride, pad, idx, bias=None, scale=None, layout="nchw", nthreads=0):
+    """conv2d_ex at the flat output indices idx of y in `layout` only."""
+    x, w = _nchw(x, w, layout)
+    N, _, H, W = x.shape
+    Cout, _, KH, KW = w.shape
+    Ho, Wo = out_extent(H, KH, stride, pad), out_extent(W, KW, stride, pad)
+    idx = np.asarray(idx, np.int64)
+    if layout == "nhwc":                 # flat NHWC index -> flat NCHW index of the same output
+        n, ho, wo, co = np.unravel_index(idx, (N, Ho, Wo, Cout))
+    else:
+        n, co, ho, wo = np.unravel_index(idx, (N, Cout, Ho, Wo))
+    y = conv2d_points(x, w, stride, pad, np.ravel_multi_index((n, co, ho, wo), (N, Cout, Ho, Wo)),
+                      nthreads)
+    b = _vec64(bias, Cout)
+    s = _vec64(scale, Cout)
+    if b is not None:
+        y = y + b[co]
+    if s is not None:
+        y = y * s[co]
+    return y

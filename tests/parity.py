@@ -17,6 +17,10 @@ Every floating-point comparison applies two bounds:
   core that truncates instead of rounding. A single wrong output (a dropped
   block, a wrong border row or channel) breaks it even where the global
   relative L2 would still pass.
+
+With the layer epilogue y = s * (sum + b) the magnitude is |s| (sum|x w| +
+|b|) and K + 1 becomes K + 3 (the bias add and the scale multiply each round
+once more in fp32).
 """
 from __future__ import annotations
 
@@ -49,24 +53,34 @@ def _host(y):
     return np.asarray(y, np.float64)
 
 
-def check(got, x, w, stride, pad, dt, *, ref=None, idx=None, out_dt="f32", what=""):
-    """Assert both bounds for y = conv2d(x, w) (all outputs, or the flat output
-    indices ``idx``). ``got`` holds the compared outputs: the whole y, or y
-    flattened and already indexed by ``idx``. Returns (rel_l2, max ratio of
-    error to the per-output bound)."""
+def check(got, x, w, stride, pad, dt, *, ref=None, idx=None, out_dt="f32", what="",
+          bias=None, scale=None, layout="nchw"):
+    """Assert both bounds for y = scale * (conv2d(x, w) + bias) in `layout`
+    (all outputs, or the flat output indices ``idx``). ``got`` holds the
+    compared outputs: the whole y, or y flattened and already indexed by
+    ``idx``. Returns (rel_l2, max ratio of error to the per-output bound)."""
     g = _host(got).reshape(-1)
-    if idx is None:
+    epi = bias is not None or scale is not None or layout != "nchw"
+    ab = None if bias is None else _abs(bias)
+    asc = None if scale is None else _abs(scale)
+    if not epi and idx is None:
         r = oracle.conv2d(x, w, stride, pad) if ref is None else ref
         mag = oracle.conv2d(_abs(x), _abs(w), stride, pad)
-    else:
+    elif not epi:
         r = oracle.conv2d_points(x, w, stride, pad, idx) if ref is None else ref
         mag = oracle.conv2d_points(_abs(x), _abs(w), stride, pad, idx)
+    elif idx is None:
+        r = oracle.conv2d_ex(x, w, stride, pad, bias, scale, layout) if ref is None else ref
+        mag = oracle.conv2d_ex(_abs(x), _abs(w), stride, pad, ab, asc, layout)
+    else:
+        r = oracle.conv2d_points_ex(x, w, stride, pad, idx, bias, scale, layout) if ref is None else ref
+        mag = oracle.conv2d_points_ex(_abs(x), _abs(w), stride, pad, idx, ab, asc, layout)
     r = np.asarray(r, np.float64).reshape(-1)
     mag = np.asarray(mag, np.float64).reshape(-1)
     assert g.shape == r.shape, f"{what}: {g.shape} outputs compared with {r.shape}"
     assert np.isfinite(g).all(), f"{what}: non-finite outputs"
-    K = int(w.shape[1] * w.shape[2] * w.shape[3])
-    bound = 2.0 * (K + 1) * U32 * mag + U_OUT[out_dt] * np.abs(r)
+    K = int(np.prod(w.shape[1:]))
+    bound = 2.0 * (K + (3 if epi else 1)) * U32 * mag + U_OUT[out_dt] * np.abs(r)
     err = np.abs(g - r)
     bad = np.flatnonzero(err > bound)
     ratio = float(np.max(err / np.where(bound > 0, bound, 1.0))) if err.size else 0.0

@@ -272,3 +272,79 @@ def test_half_precision_inputs_widen_exactly(orc):
     y = orc.conv2d(x, w, 1, 1)
     ref = _torch_conv(x.double().numpy(), w.double().numpy(), 1, 1)
     np.testing.assert_allclose(y, ref, rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------- layer epilogue and NHWC
+
+def _epi_case(seed, N=2, Cin=5, H=9, W=8, Cout=6, KH=3, KW=2, s=2, p=1):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((N, Cin, H, W))
+    w = rng.standard_normal((Cout, Cin, KH, KW))
+    b = rng.standard_normal(Cout)
+    sc = rng.uniform(0.25, 4.0, Cout) * rng.choice([-1.0, 1.0], Cout)
+    return x, w, b, sc, s, p
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_bias_matches_library_conv(seed):
+    """The bias of the convolution call of "Unifying Convolutions and GEMM"
+    (Sec. 5): a library convolution with its bias argument, in float64."""
+    x, w, b, _, s, p = _epi_case(seed)
+    got = oracle.conv2d_ex(x, w, s, p, bias=b)
+    want = F.conv2d(torch.from_numpy(x), torch.from_numpy(w), torch.from_numpy(b), stride=s, padding=p).numpy()
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_scale_folding_identity(seed):
+    """The scale folding of "Fast and Memory-Efficient Wavelet Convolutions via
+    I/O-Aware Reformulation": s * (X * W + b) equals X * (s W) + s b, the
+    convolution with the scale folded into the filter and the bias."""
+    x, w, b, sc, s, p = _epi_case(seed)
+    got = oracle.conv2d_ex(x, w, s, p, bias=b, scale=sc)
+    folded = oracle.conv2d(x, w * sc[:, None, None, None], s, p) + (sc * b)[None, :, None, None]
+    np.testing.assert_allclose(got, folded, rtol=1e-12, atol=1e-12)
+    # the other reading (scale the sum, then add the unscaled bias) is a
+    # different operator and must not pass
+    wrong = oracle.conv2d(x, w, s, p) * sc[None, :, None, None] + b[None, :, None, None]
+    assert np.max(np.abs(wrong - got)) > 1e-3
+
+
+def test_epilogue_exact_on_integers():
+    """Integer inputs and bias, power-of-two scales: every step is exact."""
+    rng = np.random.default_rng(9)
+    x = rng.integers(-3, 4, (2, 4, 7, 6)).astype(np.float64)
+    w = rng.integers(-3, 4, (5, 4, 3, 3)).astype(np.float64)
+    b = rng.integers(-9, 10, 5).astype(np.float64)
+    sc = np.array([0.5, 2.0, -1.0, 4.0, 0.25])
+    got = oracle.conv2d_ex(x, w, 1, 1, bias=b, scale=sc)
+    want = (F.conv2d(torch.from_numpy(x), torch.from_numpy(w), torch.from_numpy(b), padding=1).numpy()
+            * sc[None, :, None, None])
+    assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_nhwc_layout_matches_library_conv(seed):
+    """x [N][H][W][Cin], w [Cout][KH][KW][Cin], y [N][Ho][Wo][Cout]: a library
+    convolution on the channels-first views, and the NCHW oracle transposed
+    (the same sum, so bit-equal)."""
+    x, w, b, sc, s, p = _epi_case(seed + 20)
+    xh = np.ascontiguousarray(x.transpose(0, 2, 3, 1))
+    wh = np.ascontiguousarray(w.transpose(0, 2, 3, 1))
+    got = oracle.conv2d_ex(xh, wh, s, p, bias=b, scale=sc, layout="nhwc")
+    lib = F.conv2d(torch.from_numpy(xh).permute(0, 3, 1, 2), torch.from_numpy(wh).permute(0, 3, 1, 2),
+                   torch.from_numpy(b), stride=s, padding=p).permute(0, 2, 3, 1).numpy() * sc
+    np.testing.assert_allclose(got, lib, rtol=1e-12, atol=1e-12)
+    assert np.array_equal(got, oracle.conv2d_ex(x, w, s, p, bias=b, scale=sc).transpose(0, 2, 3, 1))
+
+
+@pytest.mark.parametrize("layout", ["nchw", "nhwc"])
+def test_points_ex_index_the_whole_output(layout):
+    x, w, b, sc, s, p = _epi_case(31)
+    if layout == "nhwc":
+        x = np.ascontiguousarray(x.transpose(0, 2, 3, 1))
+        w = np.ascontiguousarray(w.transpose(0, 2, 3, 1))
+    full = oracle.conv2d_ex(x, w, s, p, bias=b, scale=sc, layout=layout).reshape(-1)
+    idx = np.array([0, 1, 7, full.size // 2, full.size - 2, full.size - 1], np.int64)
+    got = oracle.conv2d_points_ex(x, w, s, p, idx, bias=b, scale=sc, layout=layout)
+    np.testing.assert_allclose(got, full[idx], rtol=1e-13, atol=1e-13)

@@ -63,3 +63,23 @@ def test_sampled_outputs_and_fp16_output_rounding():
     check(y.half(), x, w, s, p, "f16", out_dt="f16")
     with pytest.raises(AssertionError):
         check(y.half(), x, w, s, p, "f16")          # but not inside the fp32-output bound
+
+
+def test_epilogue_and_nhwc_bounds():
+    """A library convolution with bias, scaled, in NHWC and rounded to bf16
+    passes with those arguments; the result without the bias does not."""
+    shape = (2, 16, 10, 10, 24, 3, 3, 1, 1)
+    N, Cin, H, W, Cout, KH, KW, s, p = shape
+    x, w = workloads.make_inputs(N, Cin, H, W, Cout, KH, KW, seed=7, dtype="bf16")
+    b = torch.linspace(-1, 1, Cout)
+    sc = torch.linspace(0.5, 2, Cout)
+    y = torch.nn.functional.conv2d(x.float(), w.float(), b, stride=s, padding=p) * sc[None, :, None, None]
+    xh, wh = x.permute(0, 2, 3, 1).contiguous(), w.permute(0, 2, 3, 1).contiguous()
+    yh = y.permute(0, 2, 3, 1).contiguous().bfloat16()
+    check(yh, xh, wh, s, p, "bf16", out_dt="bf16", bias=b, scale=sc, layout="nhwc")
+    idx = np.array([0, 3, 100, yh.numel() - 1], dtype=np.int64)
+    check(yh.reshape(-1)[idx], xh, wh, s, p, "bf16", idx=idx, out_dt="bf16", bias=b, scale=sc,
+          layout="nhwc")
+    y0 = (torch.nn.functional.conv2d(x.float(), w.float(), stride=s, padding=p) * sc[None, :, None, None])
+    with pytest.raises(AssertionError):
+        check(y0.permute(0, 2, 3, 1).contiguous(), xh, wh, s, p, "bf16", bias=b, scale=sc, layout="nhwc")
