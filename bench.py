@@ -475,6 +475,7 @@ def probe(args, dev):
         return
     cfg = workloads.get_config(args.config or HEADLINE[0])
     dt = args.dtype or next((d for d in cfg.dtypes if d != "f32"), cfg.dtypes[0])
+    ydt = args.ydtype
     x, w = workloads.make_config_inputs(cfg, dt)
     xd, wd = x.to(dev), w.to(dev)
     codes = {"f32": conv.F32, "f16": conv.F16, "bf16": conv.BF16}
@@ -580,6 +581,8 @@ def main():
     ap.add_argument("--config", default=None, help="one layer only (its own line)")
     ap.add_argument("--dtype", default=None, help="headline dtype (default: the layer's "
                     "half-precision variant if it has one)")
+    ap.add_argument("--ydtype", default="f32", choices=["f32", "f16", "bf16"],
+                    help="with --probe: the storage type of y")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-baseline-all", action="store_true",
                     help="with --all-configs: time the oracle on every layer, not only the first")

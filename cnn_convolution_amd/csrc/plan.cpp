@@ -163,6 +163,30 @@ static bool dma_tile_known(int m, int n, int wm) {
     return false;
 }
 
+// Which of the page's three optimisations the direct-to-LDS window-GEMM
+// keeps for a launch, chosen per layer from measurements as the page's
+// Table II does ("Enabling Memory-efficient Im2win Convolution ...", Sec.
+// IV-B; the ablation of Sec. IV-E). On MI355X the direct-to-LDS copies and the
+// serpentine tile order never lost (turning the order off gained at most
+// 4.5%, within run-to-run spread), so both stay. Three stage buffers lose
+// where their LDS (3 x (MB + NB) x 128 bytes per workgroup) is what makes the
+// launch take more rounds of workgroups over the CUs than one buffer would,
+// and K is either a single 64-element stage (nothing to overlap) or long (at
+// least 16 stages, where the extra resident workgroups hide the loads
+// instead): measured 1.22x on the 64 -> 256 1x1 layer and 1.13x on Table I's
+// cv11, equal on cv10, and a loss of 13% on cv9 (9 stages), where they stay.
+// Returns the ablation bits of the plan (bit 2: one stage buffer).
+static int dma_variant(int m, int n, int64_t cols, int64_t stages, int64_t cout) {
+    const int64_t tiles = ceil_div(cout, m) * ceil_div(cols, n);
+    auto per_cu = [&](int64_t bufs) {
+        const int64_t lds = bufs * (m + n) * 64 * 2;
+        return std::max<int64_t>(1, std::min<int64_t>(8, (160 * 1024) / lds));
+    };
+    const int64_t rounds3 = ceil_div(tiles, 256 * per_cu(3));
+    const int64_t rounds1 = ceil_div(tiles, 256 * per_cu(1));
+    return (rounds1 < rounds3 && (stages == 1 || stages >= 16)) ? 4 : 0;
+}
+
 static void pick_mfma_dma(const conv2d_desc_t &d, int64_t krun, int64_t cols, conv2d_plan_t *p) {
     if (krun != p->K_stage || p->K_stage % 64 != 0) return;
     if (const char *k = std::getenv("IM2WIN_MFMA_KERNEL"))
@@ -188,6 +212,7 @@ static void pick_mfma_dma(const conv2d_desc_t &d, int64_t krun, int64_t cols, co
     p->gemm_kslice = 64;
     p->gemm_ksplit = 1;
     p->gemm_wave_m = wm;
+    p->gemm_ablate = dma_variant(m, n, cols, p->K_stage / 64, d.Cout);
     // IM2WIN_ABLATE: a comma list of "serpentine", "dma", "buffers", each
     // turning one of the page's optimisations off in this kernel (the
     // ablation of "Enabling Memory-efficient Im2win Convolution ...",

@@ -82,3 +82,27 @@ def test_dominant_kernel_follows_the_plan(monkeypatch):
 def test_traffic_is_null_without_a_summary():
     d, p = _plan("mix512", "f16")
     assert bench.recorded_traffic("mix512", "f16", d, p) is None
+
+
+def test_bench_functions_reference_only_defined_names():
+    """Every free name a function of bench.py reads is a module-level name or a
+    builtin (catches a variable used outside the function that defines it,
+    which only a GPU run would otherwise reach)."""
+    import builtins
+    import os
+    import symtable
+    path = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "bench.py")
+    top = symtable.symtable(open(path).read(), path, "exec")
+    module_names = {s.get_name() for s in top.get_symbols() if s.is_assigned() or s.is_imported()}
+    bad = []
+
+    def walk(t):
+        for ch in t.get_children():
+            if ch.get_type() == "function":
+                for s in ch.get_symbols():
+                    if (s.is_global() and s.is_referenced() and s.get_name() not in module_names
+                            and not hasattr(builtins, s.get_name())):
+                        bad.append((ch.get_name(), s.get_name()))
+            walk(ch)
+    walk(top)
+    assert not bad, bad

@@ -617,3 +617,22 @@ def test_plans_are_cached_per_descriptor_and_override(monkeypatch):
         q = conv.plan(conv.make_desc(n, 16, 8, 8, 8, 3, 3, 1, 1, conv.F32))
         assert q.rows_total == n * 8
     assert conv.implicit_plan(d).as_dict() == first
+
+
+# the variant of the direct-to-LDS window-GEMM the planner keeps per layer
+# (as Table II of the im2win paper picks per layer), against the fastest
+# measured variant of the ablation on MI355X: one stage buffer (bit 2) for the
+# 1x1 layer and Table I's cv10 / cv11, all three optimisations elsewhere
+_ABLATION_CHOICE = {"resnet3x3": 0, "deep3x3": 0, "mix5x5": 0, "mix512": 0, "mix3x3s2": 0, "mix1x1": 4,
+                    "cv9": 0, "cv10": 4, "cv11": 4, "cv12": 0}
+
+
+@pytest.mark.parametrize("name", sorted(_ABLATION_CHOICE))
+def test_planner_picks_the_measured_ablation_variant(name, monkeypatch):
+    monkeypatch.setenv("IM2WIN_ALGO", "window")
+    cfg = workloads.get_config(name)
+    dt = conv.BF16 if name == "deep3x3" else conv.F16
+    p = conv.plan(conv.make_desc(*cfg.desc().values(), dt))
+    assert p.gemm_kernel == 3 and p.gemm_ablate == _ABLATION_CHOICE[name]
+    monkeypatch.setenv("IM2WIN_ABLATE", "serpentine")          # the override still wins
+    assert conv.plan(conv.make_desc(*cfg.desc().values(), dt)).gemm_ablate == 1
