@@ -58,26 +58,33 @@ def _say(msg):
 # and input rows resident in LDS, 7: the narrow-channel implicit kernel, 8: the
 # pipelined row-block kernel, 32-channel K chunks double-buffered by loader waves)
 GEMM_SOURCES = {
-    0: ["cnn_convolution_amd/csrc/kernels/gemm_valu.hip"],
+    0: ["cnn_convolution_amd/csrc/kernels/gemm_valu.hip",
+        "cnn_convolution_amd/csrc/kernels/epilogue.hpp"],
     1: ["cnn_convolution_amd/csrc/kernels/gemm_mfma.hip",
-        "cnn_convolution_amd/csrc/kernels/tile_map.hpp"],
+        "cnn_convolution_amd/csrc/kernels/tile_map.hpp",
+        "cnn_convolution_amd/csrc/kernels/epilogue.hpp"],
     3: ["cnn_convolution_amd/csrc/kernels/gemm_mfma_dma.hip",
         "cnn_convolution_amd/csrc/kernels/lds_dma.hpp",
-        "cnn_convolution_amd/csrc/kernels/tile_map.hpp"],
+        "cnn_convolution_amd/csrc/kernels/tile_map.hpp",
+        "cnn_convolution_amd/csrc/kernels/epilogue.hpp"],
     4: ["cnn_convolution_amd/csrc/kernels/conv_implicit.hip",
         "cnn_convolution_amd/csrc/kernels/lds_dma.hpp",
-        "cnn_convolution_amd/csrc/kernels/tile_map.hpp"],
+        "cnn_convolution_amd/csrc/kernels/tile_map.hpp",
+        "cnn_convolution_amd/csrc/kernels/epilogue.hpp"],
     6: ["cnn_convolution_amd/csrc/kernels/conv_implicit_rows.hip",
         "cnn_convolution_amd/csrc/kernels/out_blocks.hpp",
         "cnn_convolution_amd/csrc/kernels/lds_dma.hpp",
-        "cnn_convolution_amd/csrc/kernels/tile_map.hpp"],
+        "cnn_convolution_amd/csrc/kernels/tile_map.hpp",
+        "cnn_convolution_amd/csrc/kernels/epilogue.hpp"],
     7: ["cnn_convolution_amd/csrc/kernels/conv_implicit_narrow.hip",
         "cnn_convolution_amd/csrc/kernels/out_blocks.hpp",
         "cnn_convolution_amd/csrc/kernels/lds_dma.hpp",
-        "cnn_convolution_amd/csrc/kernels/tile_map.hpp"],
+        "cnn_convolution_amd/csrc/kernels/tile_map.hpp",
+        "cnn_convolution_amd/csrc/kernels/epilogue.hpp"],
     8: ["cnn_convolution_amd/csrc/kernels/conv_implicit_pipe.hip",
         "cnn_convolution_amd/csrc/kernels/out_blocks.hpp",
-        "cnn_convolution_amd/csrc/kernels/lds_dma.hpp"],
+        "cnn_convolution_amd/csrc/kernels/lds_dma.hpp",
+        "cnn_convolution_amd/csrc/kernels/epilogue.hpp"],
 }
 GEMM_KERNEL_NAMES = {0: "gemm_valu_f32", 1: "gemm_mfma",
                      3: "gemm_mfma_dma", 4: "conv_implicit",
@@ -111,12 +118,13 @@ def dominant_key(d, plan):
             f"{plan.gemm_kslice}/{plan.gemm_ksplit}/{plan.gemm_wave_m}", rows)
 
 
-def recorded_traffic(name, dt, d, plan):
+def recorded_traffic(name, dt, d, plan, ydt="f32"):
     """HBM bytes per launch of the dominant kernel from the committed counter
-    summary (profiles/<layer>_<dtype>_gemm_counters.md), or None when there is
-    none or the kernel sources, tile or launch size differ from what the
-    counters measured."""
-    path = os.path.join(ROOT, "profiles", f"{name}_{dt}_gemm_counters.md")
+    summary (profiles/<layer>_<dtype>[_y<output type>]_gemm_counters.md), or
+    None when there is none or the kernel sources, tile or launch size differ
+    from what the counters measured."""
+    ysuf = "" if ydt == "f32" else f"_y{ydt}"
+    path = os.path.join(ROOT, "profiles", f"{name}_{dt}{ysuf}_gemm_counters.md")
     if not os.path.exists(path):
         return None
     kid, tile, rows = dominant_key(d, plan)
@@ -331,7 +339,7 @@ def _time_variant(cfg, dt, steps, warmup, dev, ydt="f32"):
     roof["frac"] = roof["achieved"] / roof["peak"]
     # HBM bytes per launch from FETCH_SIZE + WRITE_SIZE counters scaled by a copy
     # of known size (committed summary); null once the kernel has changed
-    roof["traffic"] = recorded_traffic(cfg.name, dt, d, plan)
+    roof["traffic"] = recorded_traffic(cfg.name, dt, d, plan, ydt)
     roof["kernel"] = GEMM_KERNEL_NAMES[kid]
     roof["tile"] = tile
     roof["alg_bytes_per_launch"] = dom_bytes

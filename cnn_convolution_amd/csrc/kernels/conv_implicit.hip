@@ -229,26 +229,30 @@ __global__ __launch_bounds__(256) void conv_implicit_kernel(const ImplicitKArgs 
 
     // epilogue: lane holds D[4*(lane/16) + v][lane%16] of every 16x16 block
     const int64_t plane = int64_t(a.Ho) * a.Wo;
+    with_ytype(a.out, [&](auto tc) {
+        constexpr int T = decltype(tc)::value;
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-        if (!cok[j]) continue;
-        const int c = wn * (NB / WN) + j * 16 + (lane & 15);
-        const int i = c / a.WB;
-        const int wl = c - i * a.WB;
-        const int64_t p = int64_t(ho0 + i) * a.Wo + wo0 + wl;
+        for (int j = 0; j < FN; ++j) {
+            if (!cok[j]) continue;
+            const int c = wn * (NB / WN) + j * 16 + (lane & 15);
+            const int i = c / a.WB;
+            const int wl = c - i * a.WB;
+            const int64_t p = int64_t(ho0 + i) * a.Wo + wo0 + wl;
 #pragma unroll
-        for (int i2 = 0; i2 < FM; ++i2) {
+            for (int i2 = 0; i2 < FM; ++i2) {
+                const int co0 = m0 + wm * (MB / WM) + i2 * 16 + (lane >> 4) * 4;
+                if (a.out.plain) {
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int co = m0 + wm * (MB / WM) + i2 * 16 + (lane >> 4) * 4 + v;
-                if (co >= a.Cout) continue;
-                if (a.out.plain)
-                    static_cast<float *>(a.out.y)[(int64_t(n) * a.Cout + co) * plane + p] = acc[i2][j][v];
-                else
-                    out_store(a.out, n, co, p, acc[i2][j][v]);
+                    for (int v = 0; v < 4; ++v)
+                        if (co0 + v < a.Cout)
+                            static_cast<float *>(a.out.y)[(int64_t(n) * a.Cout + co0 + v) * plane + p] =
+                                acc[i2][j][v];
+                } else {
+                    out_store_cols4<T>(a.out, n, co0, p, acc[i2][j]);
+                }
             }
         }
-    }
+    });
 }
 
 template <int MB, int NB, int WM, int NS>

@@ -291,23 +291,26 @@ __device__ __forceinline__ void store_blocks_images(const floatx4_t (*acc)[4], i
     const int im = m / plane;
     const int p = m - im * plane;
     float *const srow = scratch + (lane & 15) * kStoreRow + 4 * (lane >> 4);
+    with_ytype(o, [&](auto tc) {
+        constexpr int T = decltype(tc)::value;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
+        for (int c = 0; c < 4; ++c) {
 #pragma unroll
-        for (int s = 0; s < MAXB; ++s)
-            if (s < nb) *reinterpret_cast<floatx4_t *>(srow + s * 16) = acc[s][c];
+            for (int s = 0; s < MAXB; ++s)
+                if (s < nb) *reinterpret_cast<floatx4_t *>(srow + s * 16) = acc[s][c];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int co = cb * 64 + c * 16 + r;
-            const float v = scratch[r * kStoreRow + lane];
-            if (co < Cout && lane < nout) {
-                if (o.plain)
-                    static_cast<float *>(o.y)[(int64_t(n + im) * Cout + co) * plane + p] = v;
-                else
-                    out_store(o, n + im, co, p, v);
+            for (int r = 0; r < 16; ++r) {
+                const int co = cb * 64 + c * 16 + r;
+                const float v = scratch[r * kStoreRow + lane];
+                if (co < Cout && lane < nout) {
+                    if (o.plain)
+                        static_cast<float *>(o.y)[(int64_t(n + im) * Cout + co) * plane + p] = v;
+                    else
+                        out_store<T>(o, n + im, co, p, v);
+                }
             }
         }
-    }
+    });
 }
 
 // zero the padding columns (positions < pad and >= pad + W) of rows 0 .. SL-1
@@ -508,7 +511,7 @@ __global__ __launch_bounds__(kPipeThreads) void conv_implicit_pipe_kernel(const 
                     if (MI)
                         store_blocks_images<4>(acc, nb, b0, lane, scratch + wave * kStoreScratchFloats, a.out,
                                                tk.n, a.Cout, tk.cb, a.Ho * a.Wo, outs);
-                    else if ((a.Wo & 3) == 0)
+                    else if ((a.Wo & 3) == 0 && a.out.type == 0)
                         store_blocks(acc, nb, b0, lane, a.out, tk.n, a.Cout, tk.cb, a.Ho, a.Wo, tk.ho0, outs);
                     else
                         store_blocks_lds(acc, nb, b0, lane, scratch + wave * kStoreScratchFloats, a.out, tk.n,
@@ -580,7 +583,7 @@ __global__ __launch_bounds__(kPipeThreads) __attribute__((amdgpu_waves_per_eu(4)
         __syncthreads();
         contract_blocks<KH, KW, BF16, false, MAXB>(acc, nb, qa, fl, a.IW, lane);
     }
-    if ((a.Wo & 3) == 0 && !MI) {
+    if ((a.Wo & 3) == 0 && a.out.type == 0 && !MI) {
         if (nb > 0) store_blocks<MAXB>(acc, nb, b0, lane, a.out, tk.n, a.Cout, tk.cb, a.Ho, a.Wo, tk.ho0, outs);
     } else if (MI) {
         __syncthreads();                             // the chunk is dead: LDS is store scratch

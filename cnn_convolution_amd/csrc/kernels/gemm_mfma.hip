@@ -264,9 +264,12 @@ __global__ __launch_bounds__(256 * KS) void gemm_mfma_kernel(
                 }
             }
         } else {
+            with_ytype(o, [&](auto tc) {
+                constexpr int T = decltype(tc)::value;
 #pragma unroll
-            for (int i = 0; i < FM; ++i)
-                out_store_cols4(o, img, m0 + wm * (MB / WM) + i * 16 + (lane >> 4) * 4, p, acc[i][j]);
+                for (int i = 0; i < FM; ++i)
+                    out_store_cols4<T>(o, img, m0 + wm * (MB / WM) + i * 16 + (lane >> 4) * 4, p, acc[i][j]);
+            });
         }
     }
 }

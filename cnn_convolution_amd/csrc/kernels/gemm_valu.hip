@@ -119,9 +119,13 @@ __device__ __forceinline__ void valu_store(const float (&acc)[MT][NT], const Out
             store_cols<NT>(static_cast<float *>(o.y) + (int64_t(n) * Cout + co) * o.plane + p, acc[m], nvalid,
                            vec_ok);
         } else {
+            with_ytype(o, [&](auto tc) {
+                constexpr int T = decltype(tc)::value;
+                const ChanEpi e = chan_epi(o, co);
 #pragma unroll
-            for (int j = 0; j < NT; ++j)
-                if (j < nvalid) out_store(o, n, co, p + j, acc[m][j]);
+                for (int j = 0; j < NT; ++j)
+                    if (j < nvalid) put1<T>(o.y, out_offset(o, n, co, p + j), epi_apply(e, acc[m][j]));
+            });
         }
     }
 }

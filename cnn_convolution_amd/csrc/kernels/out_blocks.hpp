@@ -78,24 +78,30 @@ __device__ __forceinline__ void store_blocks(const floatx4_t (*acc)[4], int nb, 
         }
         return;
     }
+    with_ytype(o, [&](auto tc) {
+        constexpr int T = decltype(tc)::value;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        const int co = cb * 64 + c * 16 + (lane & 15);
-        if (co >= Cout) continue;
+        for (int c = 0; c < 4; ++c) {
+            const int co = cb * 64 + c * 16 + (lane & 15);
+            if (co >= Cout) continue;
+            const ChanEpi e = chan_epi(o, co);
 #pragma unroll
-        for (int s = 0; s < MAXB; ++s) {
-            if (s >= nb) break;
-            const int m = (b0 + s) * 16 + (lane >> 4) * 4;
-            const int64_t p = int64_t(ho0) * Wo + m;
-            if ((Wo & 3) == 0 && !o.nhwc) {
-                if (m < outs) out_store4(o, out_offset(o, n, co, p), co, acc[s][c]);
-            } else {
+            for (int s = 0; s < MAXB; ++s) {
+                if (s >= nb) break;
+                const int m = (b0 + s) * 16 + (lane >> 4) * 4;
+                const int64_t p = int64_t(ho0) * Wo + m;
+                if ((Wo & 3) == 0 && !o.nhwc) {
+                    if (m < outs)
+                        put4<T>(o.y, out_offset(o, n, co, p), epi_apply(e, acc[s][c][0]), epi_apply(e, acc[s][c][1]),
+                                epi_apply(e, acc[s][c][2]), epi_apply(e, acc[s][c][3]));
+                } else {
 #pragma unroll
-                for (int v = 0; v < 4; ++v)
-                    if (m + v < outs) out_store(o, n, co, p + v, acc[s][c][v]);
+                    for (int v = 0; v < 4; ++v)
+                        if (m + v < outs) put1<T>(o.y, out_offset(o, n, co, p + v), epi_apply(e, acc[s][c][v]));
+                }
             }
         }
-    }
+    });
 }
 
 // Per-wave LDS scratch of store_blocks_lds: 16 rows (output channels) of 64
@@ -121,23 +127,48 @@ __device__ __forceinline__ void store_blocks_lds(const floatx4_t (*acc)[4], int 
     const int nout = min(nb * 16, outs - b0 * 16);   // this wave's outputs
     const int64_t p0 = int64_t(ho0) * Wo + b0 * 16;   // their first position in the plane
     float *const srow = scratch + (lane & 15) * kStoreRow + 4 * (lane >> 4);
+    with_ytype(o, [&](auto tc) {
+        constexpr int T = decltype(tc)::value;
+        // NCHW y with whole 4-output groups: lane (row group lane / 16, column
+        // quad lane % 16) reads 4 consecutive outputs of a channel row and
+        // stores them as one vector (16 bytes fp32, 8 bytes half), so that each
+        // store instruction writes 4 channels x 64 consecutive outputs (whole
+        // 128-byte lines) instead of one channel row of 4-byte pieces
+        // (measured: deep 3x3 layer 29 -> 27 us, the 1x1 layer 47 -> 45 us)
+        const bool quads = !o.nhwc && (p0 & 3) == 0 && (nout & 3) == 0;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
+        for (int c = 0; c < 4; ++c) {
 #pragma unroll
-        for (int s = 0; s < MAXB; ++s)
-            if (s < nb) *reinterpret_cast<floatx4_t *>(srow + s * 16) = acc[s][c];
+            for (int s = 0; s < MAXB; ++s)
+                if (s < nb) *reinterpret_cast<floatx4_t *>(srow + s * 16) = acc[s][c];
+            if (quads) {
+                const int col = 4 * (lane & 15);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int co = cb * 64 + c * 16 + r;
-            const float v = scratch[r * kStoreRow + lane];
-            if (co < Cout && lane < nout) {
-                if (o.plain)
-                    static_cast<float *>(o.y)[(int64_t(n) * Cout + co) * plane + p0 + lane] = v;
-                else
-                    out_store(o, n, co, p0 + lane, v);
+                for (int j = 0; j < 4; ++j) {
+                    const int r = (lane >> 4) + 4 * j;
+                    const int co = cb * 64 + c * 16 + r;
+                    if (co < Cout && col < nout) {
+                        const floatx4_t v = *reinterpret_cast<const floatx4_t *>(scratch + r * kStoreRow + col);
+                        const ChanEpi e = chan_epi(o, co);
+                        put4<T>(o.y, (int64_t(n) * Cout + co) * plane + p0 + col, epi_apply(e, v[0]),
+                                epi_apply(e, v[1]), epi_apply(e, v[2]), epi_apply(e, v[3]));
+                    }
+                }
+                continue;
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int co = cb * 64 + c * 16 + r;
+                const float v = scratch[r * kStoreRow + lane];
+                if (co < Cout && lane < nout) {
+                    if (o.plain)
+                        static_cast<float *>(o.y)[(int64_t(n) * Cout + co) * plane + p0 + lane] = v;
+                    else
+                        out_store<T>(o, n, co, p0 + lane, v);
+                }
             }
         }
-    }
+    });
 }
 
 }  // namespace im2win
