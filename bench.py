@@ -153,9 +153,11 @@ def algorithmic_bytes(cfg, dt, plan, ydt="f32"):
     w = cfg.Cout * cfg.Cin * cfg.KH * cfg.KW * es
     win = cfg.N * ho * cfg.Cin * plan.W_win * cfg.KH * es
     y = cfg.N * cfg.Cout * ho * wo * (4 if ydt == "f32" else 2)
-    staged = not (cfg.KH == 1 and cfg.KW == 1)
+    # a staging launch runs only where the plan keeps a staged filter (the
+    # window form's, or the implicit form's workspace)
+    staged = plan.wstage_bytes > 0 if plan.algo == 0 else plan.ws_bytes > 0
     return {"pack": x + win, "gemm": win + w * plan.n_chunks + y,
-            "weight_stage": 2 * w if (plan.wstage_bytes if plan.algo == 0 else staged) else 0,
+            "weight_stage": 2 * w if staged else 0,
             "implicit": x + w + y}
 
 

@@ -202,9 +202,12 @@ hipError_t launch_implicit(const conv2d_implicit_plan_t &p, const ImplicitArgs &
     return hipErrorInvalidValue;                     // no such kernel
 }
 
-// implicit form: (a3) the filter into the window's K order (kw, kh, ci)
-// unless a 1x1 filter already is, then (a2, a4, a5) in one kernel: window
-// rows built in LDS, contracted, fp32 y written. Arguments checked by the caller.
+// implicit form: (a3) the filter into the window's K order (kw, kh, ci) by a
+// staging launch where the plan keeps a staged filter (the streamed kernel,
+// and the narrow one on launches of more than one workgroup per CU; the
+// others reorder w in LDS themselves), then (a2, a4, a5) in one kernel:
+// window rows built in LDS, contracted, y written. Arguments checked by the
+// caller.
 conv2d_status_t run_implicit(const conv2d_desc_t &d, const conv2d_implicit_plan_t &p, const void *x,
                              const void *w, const OutSpec &out, void *ws, hipStream_t s)
 {

@@ -9,16 +9,21 @@
 // (Wo - 1) * s + KW and filter row kh, the CP (4 or 8, zero-padded) channels
 // of input position (ho * s - pad + kh, w - pad). The window of output
 // column wo is then ONE contiguous run of K = KW * KH * CP elements starting
-// at wo * s * KH * CP, contracted against the filter staged in the same K
-// order (kw, kh, ci) (Sec. III-C Eq. (3), Sec. III-D) — the contraction of the
+// at wo * s * KH * CP, contracted against the filter held in LDS in the same
+// K order (kw, kh, ci) (Sec. III-C Eq. (3), Sec. III-D) — the contraction of the
 // window form with the window rows in LDS instead of HBM.
 //
 // A workgroup of eight waves owns a block of 64 output channels and walks a
 // contiguous range of row blocks (R output rows of one image, R * Wo <= 512).
-// It stages its filter block into LDS once (64 rows of Kp elements, Kp = K
-// rounded up to the MFMA K step, zero past K, as the channels-last filter
-// staging writes it into the workspace; each LDS row 16 bytes longer than Kp
-// so that the 16 rows a fragment read touches fall in different bank groups).
+// It puts its filter block into LDS once: 64 rows of Kp elements in the
+// window's K order, Kp = K rounded up to the MFMA K step, zero at padded
+// channels and past K, each LDS row 16 bytes longer than Kp so that the 16
+// rows a fragment read touches fall in different bank groups. Launches of at
+// most one workgroup per CU gather it straight from w as stored
+// (w[co][ci][kh][kw]: no staging launch, no workspace); larger launches read
+// it from the filter staged in that order in the workspace ([Cout][Kp], as
+// the channels-last staging writes it), since each of their workgroups would
+// otherwise pay for the scattered 2- or 4-byte gathers again.
 // Per row block it builds the R window rows (zero outside the image; the
 // gathers of the next row block are in flight while this one is contracted
 // and stored), and after a barrier each wave contracts its 16-output blocks
@@ -54,11 +59,67 @@ struct NarrowKArgs {
     int groups;             // workgroups per 64-channel block (gridDim.x / co_blocks)
 };
 
-// The filter block: the staged rows [Cout][Kp] (16-byte vectors; rows past
-// Cout read row Cout-1, never stored) into LDS rows of FS elements, FB
-// vectors per thread in flight at a time.
-template <int FB, typename T>
-__device__ __forceinline__ void load_filter(const NarrowKArgs &a, const T *wst, T *fl, int FS, int cb, int tid)
+// One 16-byte vector of the filter block, gathered from w as stored: vector
+// v is row r = v / (Kp / VE) (output channel cb*64 + r; rows past Cout read
+// row Cout-1 and are never stored) and K elements k0 .. k0+VE-1, k0 = (v mod
+// (Kp / VE)) * VE. Element k is channel ci = k mod CP of window position
+// k / CP = kw * KH + kh, i.e. w[co][ci][kh][kw], or zero for ci >= Cin or
+// k >= K. A vector covers VE / CP whole positions (VE >= CP) or part of one
+// (fp32 with CP = 8), so one division by KH per vector.
+template <int CP, typename T>
+__device__ __forceinline__ uint4 gather_filter_vec(const NarrowKArgs &a, const T *w, int cb, int v)
+{
+    constexpr int VE = 16 / sizeof(T);
+    const int fv_row = a.Kp / VE;
+    const int r = v / fv_row;
+    const int k0 = (v - r * fv_row) * VE;
+    const int co = min(cb * 64 + r, a.Cout - 1);
+    const T *wr = w + int64_t(co) * a.Cin * a.KH * a.KW;
+    const int pos0 = k0 / CP;
+    int kw = pos0 / a.KH;
+    int kh = pos0 - kw * a.KH;
+    T o[VE];
+#pragma unroll
+    for (int e = 0; e < VE; ++e) {
+        int ci;
+        if constexpr (VE >= CP) {
+            if (e > 0 && e % CP == 0 && ++kh == a.KH) {   // next window position
+                kh = 0;
+                ++kw;
+            }
+            ci = e % CP;
+        } else {
+            ci = k0 % CP + e;
+        }
+        const bool in = ci < a.Cin && k0 + e < a.K;
+        const T val = wr[in ? (ci * a.KH + kh) * a.KW + kw : 0];   // every load in bounds
+        o[e] = in ? val : T(0);
+    }
+    uint4 q;
+    __builtin_memcpy(&q, o, 16);
+    return q;
+}
+
+// Vector v of the filter block: gathered from w as stored (GATHER), or read
+// from the staged rows [Cout][Kp] in the workspace.
+template <int CP, bool GATHER, typename T>
+__device__ __forceinline__ uint4 filter_vec(const NarrowKArgs &a, const T *w, int cb, int v)
+{
+    if constexpr (GATHER) {
+        return gather_filter_vec<CP>(a, w, cb, v);
+    } else {
+        constexpr int VE = 16 / sizeof(T);
+        const int fv_row = a.Kp / VE;
+        const int r = v / fv_row;
+        const int row = min(cb * 64 + r, a.Cout - 1);
+        return *reinterpret_cast<const uint4 *>(w + int64_t(row) * a.Kp + (v - r * fv_row) * VE);
+    }
+}
+
+// The filter block into LDS rows of FS elements, FB vectors per thread in
+// flight at a time.
+template <int CP, bool GATHER, int FB, typename T>
+__device__ __forceinline__ void load_filter(const NarrowKArgs &a, const T *w, T *fl, int FS, int cb, int tid)
 {
     constexpr int V = 16 / sizeof(T);
     const int fv_row = a.Kp / V;
@@ -66,12 +127,8 @@ __device__ __forceinline__ void load_filter(const NarrowKArgs &a, const T *wst, 
     for (int f0 = 0; f0 < fvec; f0 += FB * kNarrowThreads) {
         uint4 fv[FB];
 #pragma unroll
-        for (int j = 0; j < FB; ++j) {
-            const int v = min(f0 + tid + j * kNarrowThreads, fvec - 1);
-            const int r = v / fv_row;
-            const int row = min(cb * 64 + r, a.Cout - 1);
-            fv[j] = *reinterpret_cast<const uint4 *>(wst + int64_t(row) * a.Kp + (v - r * fv_row) * V);
-        }
+        for (int j = 0; j < FB; ++j)
+            fv[j] = filter_vec<CP, GATHER>(a, w, cb, min(f0 + tid + j * kNarrowThreads, fvec - 1));
 #pragma unroll
         for (int j = 0; j < FB; ++j) {
             const int v = f0 + tid + j * kNarrowThreads;
@@ -164,8 +221,8 @@ __device__ __forceinline__ void put_window(const NarrowKArgs &a, T *win, int rw,
 // One row block per workgroup: the filter block's vectors (FB per thread) and
 // the window units (UB per thread) of a round all in flight together, then
 // written; normally a single round.
-template <int CP, int FB, int UB, typename T>
-__device__ __forceinline__ void load_block(const NarrowKArgs &a, const T *ximg, const T *wst, T *fl, T *win,
+template <int CP, bool GATHER, int FB, int UB, typename T>
+__device__ __forceinline__ void load_block(const NarrowKArgs &a, const T *ximg, const T *w, T *fl, T *win,
                                            int FS, int cb, int ho0, int rw, int tid)
 {
     constexpr int V = 16 / sizeof(T);
@@ -175,12 +232,8 @@ __device__ __forceinline__ void load_block(const NarrowKArgs &a, const T *ximg, 
     for (int f0 = 0, u0 = 0; f0 < fvec || u0 < units; f0 += FB * kNarrowThreads, u0 += UB * kNarrowThreads) {
         uint4 fv[FB];
 #pragma unroll
-        for (int j = 0; j < FB; ++j) {
-            const int v = min(f0 + tid + j * kNarrowThreads, fvec - 1);
-            const int r = v / fv_row;
-            const int row = min(cb * 64 + r, a.Cout - 1);
-            fv[j] = *reinterpret_cast<const uint4 *>(wst + int64_t(row) * a.Kp + (v - r * fv_row) * V);
-        }
+        for (int j = 0; j < FB; ++j)
+            fv[j] = filter_vec<CP, GATHER>(a, w, cb, min(f0 + tid + j * kNarrowThreads, fvec - 1));
         WinRegs<CP, UB, T> wr;
         if (u0 < units) fetch_window(a, ximg, ho0, rw, u0, tid, wr);
 #pragma unroll
@@ -204,7 +257,7 @@ __device__ __forceinline__ void task_rows(const NarrowKArgs &a, int t, int &n, i
 }
 
 // ---- fp16 / bf16 -------------------------------------------------------------
-template <int CP, bool BF16, bool PIPE>
+template <int CP, bool BF16, bool PIPE, bool GATHER>
 __global__ __launch_bounds__(kNarrowThreads) void conv_implicit_narrow_kernel(const NarrowKArgs a, int ntasks)
 {
     extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
@@ -219,7 +272,7 @@ __global__ __launch_bounds__(kNarrowThreads) void conv_implicit_narrow_kernel(co
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
     const int lane = tid & 63;
-    const uint16_t *const wst = static_cast<const uint16_t *>(a.w);   // staged [Cout][Kp]
+    const uint16_t *const wsrc = static_cast<const uint16_t *>(a.w);  // w, or the staged rows
     constexpr int UB = CP == 4 ? 16 : 8;
     constexpr int UBR = UB * kNarrowThreads;         // window units per round
     const uint16_t *const x = static_cast<const uint16_t *>(a.x);
@@ -277,7 +330,7 @@ __global__ __launch_bounds__(kNarrowThreads) void conv_implicit_narrow_kernel(co
         // one row block: filter and window loads in one round trip
         int n, ho0, rw;
         task_rows(a, t_begin, n, ho0, rw);
-        load_block<CP, 4, UB>(a, x + n * img, wst, fl, win, FS, cb, ho0, rw, tid);
+        load_block<CP, GATHER, 4, UB>(a, x + n * img, wsrc, fl, win, FS, cb, ho0, rw, tid);
         __syncthreads();
         run_block(n, ho0, rw);
     } else {
@@ -290,7 +343,7 @@ __global__ __launch_bounds__(kNarrowThreads) void conv_implicit_narrow_kernel(co
             task_rows(a, t_begin, n, ho0, rw);
             fetch_window(a, x + n * img, ho0, rw, 0, tid, nxt);
         }
-        load_filter<4>(a, wst, fl, FS, cb, tid);
+        load_filter<CP, GATHER, 4>(a, wsrc, fl, FS, cb, tid);
         for (int t = t_begin; t < t_end; ++t) {
             int n, ho0, rw;
             task_rows(a, t, n, ho0, rw);
@@ -315,7 +368,7 @@ __global__ __launch_bounds__(kNarrowThreads) void conv_implicit_narrow_kernel(co
 // ---- fp32: v_mfma_f32_16x16x4_f32; K in slices of 16 elements, lane group
 // g = lane / 16 holding elements 4g .. 4g + 3 of a slice as one vector and
 // feeding element j to K step j (window runs and filter alike) -------------
-template <int CP, bool PIPE>
+template <int CP, bool PIPE, bool GATHER>
 __global__ __launch_bounds__(kNarrowThreads) void conv_implicit_narrow_f32_kernel(const NarrowKArgs a, int ntasks)
 {
     extern __shared__ __attribute__((aligned(16))) float ldsf[];
@@ -330,7 +383,7 @@ __global__ __launch_bounds__(kNarrowThreads) void conv_implicit_narrow_f32_kerne
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
     const int lane = tid & 63;
-    const float *const wst = static_cast<const float *>(a.w);         // staged [Cout][Kp]
+    const float *const wsrc = static_cast<const float *>(a.w);        // w, or the staged rows
     constexpr int UB = CP == 4 ? 16 : 8;
     constexpr int UBR = UB * kNarrowThreads;         // window units per round
     const float *const x = static_cast<const float *>(a.x);
@@ -385,7 +438,7 @@ __global__ __launch_bounds__(kNarrowThreads) void conv_implicit_narrow_f32_kerne
         // one row block: filter and window loads in one round trip
         int n, ho0, rw;
         task_rows(a, t_begin, n, ho0, rw);
-        load_block<CP, 4, UB>(a, x + n * img, wst, fl, win, FS, cb, ho0, rw, tid);
+        load_block<CP, GATHER, 4, UB>(a, x + n * img, wsrc, fl, win, FS, cb, ho0, rw, tid);
         __syncthreads();
         run_block(n, ho0, rw);
     } else {
@@ -398,7 +451,7 @@ __global__ __launch_bounds__(kNarrowThreads) void conv_implicit_narrow_f32_kerne
             task_rows(a, t_begin, n, ho0, rw);
             fetch_window(a, x + n * img, ho0, rw, 0, tid, nxt);
         }
-        load_filter<4>(a, wst, fl, FS, cb, tid);
+        load_filter<CP, GATHER, 4>(a, wsrc, fl, FS, cb, tid);
         for (int t = t_begin; t < t_end; ++t) {
             int n, ho0, rw;
             task_rows(a, t, n, ho0, rw);
@@ -428,7 +481,7 @@ hipError_t launch_conv_implicit_narrow(const ImplicitArgs &h, hipStream_t s)
     const int kstep = h.f32 ? 16 : 32;
     NarrowKArgs a{};
     a.x = h.x;
-    a.w = h.wst;
+    a.w = h.wst;                                     // w as stored, or the staged rows
     a.out = h.out;
     a.Cin = h.Cin;
     a.H = h.H;
@@ -460,7 +513,7 @@ hipError_t launch_conv_implicit_narrow(const ImplicitArgs &h, hipStream_t s)
         implicit_narrow_lds_bytes(es, a.Kp, a.Lp, h.R) > kImplicitMaxLdsBytes)
         return hipErrorInvalidValue;
     // workgroups: co_blocks x groups, each group walking a contiguous range of
-    // the N * row_groups row blocks with its filter block staged once
+    // the N * row_groups row blocks with its filter block gathered once
     a.groups = h.groups;
     int ntasks = h.N * a.row_groups;
     const int64_t blocks = int64_t(a.co_blocks) * a.groups;
@@ -469,18 +522,25 @@ hipError_t launch_conv_implicit_narrow(const ImplicitArgs &h, hipStream_t s)
     // one row block per workgroup, or persistent workgroups that prefetch the
     // next row block's gathers (more registers: one workgroup per CU)
     const bool pipe = a.groups < ntasks;
+    // the filter gathered from w (the plan then keeps no staged filter), or
+    // read from the staged rows
+    const bool gather = narrow_gathers_filter(blocks);
     const void *kern;
-#define IM2WIN_NARROW_PICK(P)                                                                                      \
-    if (h.f32) kern = cp == 4 ? reinterpret_cast<const void *>(conv_implicit_narrow_f32_kernel<4, P>)              \
-                              : reinterpret_cast<const void *>(conv_implicit_narrow_f32_kernel<8, P>);             \
-    else if (h.bf16) kern = cp == 4 ? reinterpret_cast<const void *>(conv_implicit_narrow_kernel<4, true, P>)      \
-                                    : reinterpret_cast<const void *>(conv_implicit_narrow_kernel<8, true, P>);     \
-    else kern = cp == 4 ? reinterpret_cast<const void *>(conv_implicit_narrow_kernel<4, false, P>)                 \
-                        : reinterpret_cast<const void *>(conv_implicit_narrow_kernel<8, false, P>);
+#define IM2WIN_NARROW_PICK(P, G)                                                                                   \
+    if (h.f32) kern = cp == 4 ? reinterpret_cast<const void *>(conv_implicit_narrow_f32_kernel<4, P, G>)           \
+                              : reinterpret_cast<const void *>(conv_implicit_narrow_f32_kernel<8, P, G>);          \
+    else if (h.bf16) kern = cp == 4 ? reinterpret_cast<const void *>(conv_implicit_narrow_kernel<4, true, P, G>)   \
+                                    : reinterpret_cast<const void *>(conv_implicit_narrow_kernel<8, true, P, G>);  \
+    else kern = cp == 4 ? reinterpret_cast<const void *>(conv_implicit_narrow_kernel<4, false, P, G>)              \
+                        : reinterpret_cast<const void *>(conv_implicit_narrow_kernel<8, false, P, G>);
+    // persistent launches have at most 256 workgroups: always the gathered filter
+    if (pipe && !gather) return hipErrorInvalidValue;
     if (pipe) {
-        IM2WIN_NARROW_PICK(true)
+        IM2WIN_NARROW_PICK(true, true)
+    } else if (gather) {
+        IM2WIN_NARROW_PICK(false, true)
     } else {
-        IM2WIN_NARROW_PICK(false)
+        IM2WIN_NARROW_PICK(false, false)
     }
 #undef IM2WIN_NARROW_PICK
     if (lds > 64 * 1024) {

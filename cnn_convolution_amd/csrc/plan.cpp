@@ -599,10 +599,11 @@ static void pick_implicit_pipelined(const conv2d_desc_t &d, int64_t Ho, int64_t 
 // takes R output rows of one image (R * Wo <= 512) and 64 output channels,
 // with its R channels-last window rows (CP = 4 channels per position, or 8
 // where 4 would leave a window start off a 16-byte boundary) and the filter in
-// the window's K order in LDS, read from the filter staged in the workspace.
+// the window's K order in LDS, gathered from w as stored, or (launches of more
+// than one workgroup per CU) read from the filter staged in the workspace.
 // Default where it applies; IM2WIN_IMPLICIT_KERNEL names another kernel to
 // leave it; IM2WIN_IMPLICIT_ROWS sets R. The plan's `stages` field carries CP
-// and `K_stage` the staged row length Kp.
+// and `K_stage` the filter's LDS row length Kp.
 static void pick_implicit_narrow(const conv2d_desc_t &d, int64_t Ho, int64_t Wo, conv2d_implicit_plan_t *p) {
     if (d.Cin > 8 || Wo > 512 || Wo < 1 || Ho < 1) return;
     if (const char *e = std::getenv("IM2WIN_IMPLICIT_KERNEL"))
@@ -652,11 +653,12 @@ static void pick_implicit_narrow(const conv2d_desc_t &d, int64_t Ho, int64_t Wo,
     const bool persistent = f32 || 64 * Kp * es > 48 * 1024;
     const int64_t groups = persistent ? std::min(row_blocks, std::max<int64_t>(1, 256 / co_blocks)) : row_blocks;
     p->tiles = co_blocks * groups;
-    // the filter staged into the workspace by the channels-last staging:
-    // [Cout][Kp], CP channels per position (the half-precision layout's
-    // Cin_pad and row length)
+    // the filter block in LDS rows of Kp elements: gathered from w as stored
+    // by launches of at most one workgroup per CU (no workspace), else read
+    // from the filter staged into the workspace by the channels-last staging,
+    // [Cout][Kp] with CP channels per position
     p->K_stage = Kp;
-    p->ws_bytes = round_up(d.Cout * Kp * es, 256);
+    p->ws_bytes = narrow_gathers_filter(p->tiles) ? 0 : round_up(d.Cout * Kp * es, 256);
 }
 
 static conv2d_status_t compute_implicit_plan(const conv2d_desc_t &d, conv2d_implicit_plan_t *p) {

@@ -51,6 +51,11 @@ inline int64_t pair_lds_bytes(int64_t taps, int64_t sl, int64_t iw) {
 // narrow-channel implicit form: the filter block (64 rows of kp elements + 16
 // bytes) + r window rows of lp elements, es bytes per element (the window rows'
 // space holds at least the store scratch)
+// The narrow-channel kernel gathers its filter block from w as stored when
+// its launch has at most one workgroup per CU (each gather is paid once per
+// workgroup); larger launches read the filter staged in the workspace.
+inline bool narrow_gathers_filter(int64_t workgroups) { return workgroups <= 256; }
+
 inline int64_t implicit_narrow_lds_bytes(int64_t es, int64_t kp, int64_t lp, int64_t r) {
     return 64 * (kp + 16 / es) * es + std::max<int64_t>(r * lp * es, kImplicitStoreScratchBytes);
 }

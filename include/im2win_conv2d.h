@@ -273,7 +273,10 @@ typedef struct {
                                      of one image per workgroup with w as stored
                                      and the input rows resident in LDS, no
                                      staged filter (ws_bytes 0); 3: narrow-channel
-                                     (Cin <= 8); 4 (default for the other 3x3 and
+                                     (Cin <= 8), the filter block gathered from w
+                                     as stored into LDS when tiles <= 256
+                                     (ws_bytes 0), else read from the staged
+                                     filter; 4 (default for the other 3x3 and
                                      1x1 layers of stride 1 or 2 with Cin % 32 ==
                                      0 and Wo <= 256): pipelined row-block, tasks of
                                      rows_per_tile whole output rows (or of
@@ -293,9 +296,12 @@ typedef struct {
     int64_t lds_bytes;            /* LDS per workgroup                              */
     int64_t tiles;                /* workgroups of the launch                       */
     int64_t Ho, Wo;
-    int64_t K_stage;              /* staged filter row: KW*KH*Cin                   */
-    int64_t ws_bytes;             /* the staged filter; 0 for a 1x1 filter and for
-                                     kernels 2 and 4                                */
+    int64_t K_stage;              /* staged filter row: KW*KH*Cin (kernel 3: the
+                                     filter's LDS row, KW*KH*CP rounded up to the
+                                     matrix-core K step)                            */
+    int64_t ws_bytes;             /* the staged filter of kernel 0 (0 for a 1x1
+                                     filter) and of kernel 3 when tiles > 256; 0
+                                     for kernels 2 and 4                            */
     int64_t flops;                /* 2*N*Cout*Ho*Wo*Cin*KH*KW                        */
 } conv2d_implicit_plan_t;
 
@@ -307,7 +313,8 @@ typedef struct {
 conv2d_status_t conv2d_implicit_plan(const conv2d_desc_t *d, conv2d_implicit_plan_t *out);
 
 /* Bytes of workspace conv2d_fwd_implicit needs (0 if d is invalid or not
- * supported, or for a 1x1 filter). */
+ * supported, for a 1x1 filter, for the row-block and pipelined kernels, and
+ * for the narrow-channel kernel on launches of at most 256 workgroups). */
 size_t conv2d_implicit_workspace_size(const conv2d_desc_t *d);
 
 /* y = conv2d(x, w) by the implicit form. Arguments, alignment, ownership and
@@ -321,7 +328,8 @@ conv2d_status_t conv2d_fwd_implicit(const conv2d_desc_t *d, const void *x, const
  * with a filter already staged in the window's K order (as
  * im2win_weight_stage writes it for IM2WIN_LAYOUT_CL), or w itself where the
  * plan keeps no staged filter (conv2d_implicit_workspace_size(d) == 0: a 1x1
- * filter, or the row-block kernels, which reorder w in LDS on their own),
+ * filter, or the row-block, pipelined and small narrow-channel launches, which
+ * reorder w in LDS on their own),
  * writing all of y (y_dtype of the descriptor, no bias or scale). Device
  * pointers, 16-byte aligned. */
 conv2d_status_t im2win_implicit_gemm(const conv2d_desc_t *d, const void *x, const void *wst,

@@ -387,6 +387,7 @@ NARROW_SHAPES = [
     (1, 3, 4, 4, 2, 3, 3, 1, 5),         # padding wider than the filter: zero border
     (2, 2, 5, 4, 6, 5, 4, 1, 0),         # dense-as-conv: one output per image
     (1, 3, 6, 600, 12, 3, 3, 2, 1),      # 300 outputs per row: one row per workgroup
+    (9, 3, 130, 128, 40, 3, 3, 1, 1),    # more than 256 one-block workgroups in half precision: staged filter
 ]
 
 
@@ -399,7 +400,8 @@ def test_narrow_kernel_matches_oracle(shape, dt, rows, monkeypatch):
         monkeypatch.setenv("IM2WIN_IMPLICIT_ROWS", str(rows))
     d = conv.make_desc(*shape, CODE[dt])
     pl = conv.implicit_plan(d)
-    assert pl.kernel == 3 and pl.ws_bytes > 0 and conv.plan(d).algo == 1
+    # the filter gathered from w by launches of at most 256 workgroups, else staged
+    assert pl.kernel == 3 and (pl.ws_bytes == 0) == (pl.tiles <= 256) and conv.plan(d).algo == 1
     _say(f"implicit-narrow {dt} {shape} rows/block={pl.rows_per_tile} cp={pl.stages} workgroups={pl.tiles}")
     x, w = workloads.make_inputs(N, Cin, H, W, Cout, KH, KW, seed=31, dtype=dt, w_dist="normal")
     got = run_implicit(x, w, s, p)
@@ -427,7 +429,7 @@ def test_narrow_kernel_leaves_memory_past_y_untouched(dt):
     assert pl.kernel == 3
     n_out = N * Cout * pl.Ho * pl.Wo
     buf = torch.full((n_out + 4096,), 12345.0, dtype=torch.float32, device=DEV)
-    ws = torch.empty(pl.ws_bytes, dtype=torch.uint8, device=DEV)
+    ws = torch.empty(pl.ws_bytes, dtype=torch.uint8, device=DEV) if pl.ws_bytes else None
     conv.conv2d_implicit_into(x.to(DEV), w.to(DEV), buf, ws, s, p)
     torch.cuda.synchronize()
     host = buf.cpu().numpy()
