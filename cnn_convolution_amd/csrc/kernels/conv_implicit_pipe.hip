@@ -471,7 +471,10 @@ __global__ __launch_bounds__(kPipeThreads) void conv_implicit_pipe_kernel(const 
                 load_patch_unit<V, MI>(a, tk, blk, cg, u, raw);
                 put_patch_unit<V, MI>(patch, a, tk, cg, u, raw);
             }
-            zero_rows<MI>(patch, a, tk, lt, kLoaderThreads);
+            // rows outside the image: zero in each slot once per task (the
+            // task's first two chunks, one per slot); the loads of its later
+            // chunks write only rows inside the image
+            if (blk < 2) zero_rows<MI>(patch, a, tk, lt, kLoaderThreads);
         };
         if (total > 0) {
             fetch(0);
@@ -579,7 +582,9 @@ __global__ __launch_bounds__(kPipeThreads) __attribute__((amdgpu_waves_per_eu(4)
             load_patch_unit<V, MI>(a, tk, blk, cg, u, raw);
             put_patch_unit<V, MI>(patch, a, tk, cg, u, raw);
         }
-        zero_rows<MI>(patch, a, tk, tid, kPipeThreads);
+        // rows outside the image: zeroed once (the chunks' loads write only
+        // rows inside it)
+        if (blk == 0) zero_rows<MI>(patch, a, tk, tid, kPipeThreads);
         __syncthreads();
         contract_blocks<KH, KW, BF16, false, MAXB>(acc, nb, qa, fl, a.IW, lane);
     }
