@@ -485,7 +485,9 @@ def implicit_applies(cfg, dt):
 
 
 def probe(args, dev):
-    """Kernel launches for the counter passes, nothing else timed or printed on stdout."""
+    """Kernel launches for the counter passes, nothing else timed or printed on
+    stdout: warm-up calls of the layer (at least WARMUP_MIN_S), then `steps`
+    launches of its dominant kernel alone."""
     import torch
 
     import cnn_convolution_amd as conv
@@ -508,7 +510,15 @@ def probe(args, dev):
     plan = conv.plan(d)
     y = torch.empty((cfg.N, cfg.Cout, plan.Ho, plan.Wo), dtype=workloads.TORCH_DTYPES[ydt], device=dev)
     ws = torch.empty(max(plan.ws_bytes, 1), dtype=torch.uint8, device=dev)
-    conv.conv2d_into(xd, wd, y, ws if plan.ws_bytes else None, cfg.stride, cfg.pad)
+    # warm-up calls as in the timed runs (the clocks' ramp from idle); a
+    # profile of the probe keeps only the last `steps` launches of the kernel
+    n_warm = 0
+    tw = time.perf_counter()
+    while time.perf_counter() - tw < WARMUP_MIN_S:
+        for _ in range(10):
+            conv.conv2d_into(xd, wd, y, ws if plan.ws_bytes else None, cfg.stride, cfg.pad)
+        n_warm += 10
+        torch.cuda.synchronize()
     kid, tile, rows = dominant_key(d, plan)
     if plan.algo == 1:
         ip = conv.implicit_plan(d)
@@ -526,7 +536,8 @@ def probe(args, dev):
             conv.window_gemm(win, wst, y, d, row0, rows)
     torch.cuda.synchronize()
     _say(f"probe gemm: {cfg.name} {dt} rows={rows} tile={tile} "
-         f"kernel={GEMM_KERNEL_NAMES[kid]} sha={gemm_source_sha(kid)} launches={args.steps}")
+         f"kernel={GEMM_KERNEL_NAMES[kid]} sha={gemm_source_sha(kid)} launches={args.steps} "
+         f"after {n_warm} warm-up calls")
 
 
 ABLATIONS = [("none", ""), ("serpentine", "serpentine"), ("dma", "dma"), ("buffers", "buffers"),

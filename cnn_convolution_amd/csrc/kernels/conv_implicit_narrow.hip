@@ -318,7 +318,7 @@ __global__ __launch_bounds__(kNarrowThreads) void conv_implicit_narrow_kernel(co
         else if (nb == 2) contract(std::integral_constant<int, 2>{});
         else if (nb == 1) contract(std::integral_constant<int, 1>{});
         if ((a.Wo & 3) == 0 && a.out.type == 0) {
-            if (nb > 0) store_blocks(acc, nb, b0, lane, a.out, n, a.Cout, cb, a.Ho, a.Wo, ho0, outs);
+            if (nb > 0) store_blocks<4, true>(acc, nb, b0, lane, a.out, n, a.Cout, cb, a.Ho, a.Wo, ho0, outs);
         } else {
             __syncthreads();                         // the window rows are dead: their LDS is store scratch
             if (nb > 0)
@@ -426,7 +426,7 @@ __global__ __launch_bounds__(kNarrowThreads) void conv_implicit_narrow_f32_kerne
                 }
         }
         if ((a.Wo & 3) == 0 && a.out.type == 0) {
-            if (nb > 0) store_blocks(acc, nb, b0, lane, a.out, n, a.Cout, cb, a.Ho, a.Wo, ho0, outs);
+            if (nb > 0) store_blocks<4, true>(acc, nb, b0, lane, a.out, n, a.Cout, cb, a.Ho, a.Wo, ho0, outs);
         } else {
             __syncthreads();
             if (nb > 0)

@@ -226,7 +226,7 @@ __global__ __launch_bounds__(kRowsThreads) void conv_implicit_rows_kernel(const 
     // LDS-staged whole-line stores there: 14.5 vs 16.5 us on the ResNet layer);
     // the 1x1 form, half-precision y and rows of other widths go through LDS
     if ((a.Wo & 3) == 0 && a.out.type == 0 && TAPS > 1) {
-        if (nb > 0) store_blocks(acc, nb, b0, lane, a.out, n, a.Cout, cb, a.Ho, a.Wo, ho0, outs);
+        if (nb > 0) store_blocks<4, true>(acc, nb, b0, lane, a.out, n, a.Cout, cb, a.Ho, a.Wo, ho0, outs);
     } else {
         __syncthreads();                             // patch and filter are dead: LDS is store scratch
         if (nb > 0)
@@ -680,7 +680,7 @@ __global__ __launch_bounds__(kRowsThreads) void conv_implicit_rows_f32_kernel(co
         }
     }
     if ((a.Wo & 3) == 0 && a.out.type == 0) {
-        if (nb > 0) store_blocks(acc, nb, b0, lane, a.out, n, a.Cout, cb, a.Ho, a.Wo, ho0, outs);
+        if (nb > 0) store_blocks<4, true>(acc, nb, b0, lane, a.out, n, a.Cout, cb, a.Ho, a.Wo, ho0, outs);
     } else {
         __syncthreads();                             // patch and filter are dead: LDS is store scratch
         if (nb > 0)

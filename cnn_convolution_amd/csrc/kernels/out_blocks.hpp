@@ -45,12 +45,37 @@ __device__ __forceinline__ void block_bases(int *qa, int b0, int lane, int outs,
     }
 }
 
+// THROUGH: output lines (128 bytes) that one workgroup writes whole are
+// stored at device scope (sc1). Each XCD's L2 keeps ordinary stores dirty
+// until the kernel ends and then writes them all back, a tail the whole chip
+// waits for; device-scope stores go through to memory as they are issued, in
+// the shadow of the other waves' work. A line shared with a neighbouring
+// workgroup keeps the ordinary store: written through in pieces from two
+// XCDs it costs more than the tail. Measured on the ResNet 3x3 layer (fp16 x,
+// fp32 y): 14.1 us with ordinary stores; 12.1 us with 8-row blocks, whose
+// plane segments are whole lines, written through; 13.85 us with 7-row
+// blocks written through regardless of lines. The same stores from the
+// LDS-staged path measured slower (deep 3x3 layer 25.2 -> 27.0 us, the 1x1
+// layer 42.0 -> 46.5 us), so only the direct stores of the row-block and
+// narrow-channel kernels take it.
+__device__ __forceinline__ void store16_through(void *p, const floatx4_t &v)
+{
+    asm volatile("global_store_dwordx4 %0, %1, off sc1" ::"v"(p), "v"(v) : "memory");
+}
+
+// Whether the 128-byte line holding byte address p lies inside [lo, hi).
+__device__ __forceinline__ bool whole_line(const void *p, uintptr_t lo, uintptr_t hi)
+{
+    const uintptr_t l = reinterpret_cast<uintptr_t>(p) & ~uintptr_t(127);
+    return l >= lo && l + 128 <= hi;
+}
+
 // Lane l holds D[4*(l/16) + v][l % 16] of each 16 x 16 block: 4 consecutive
 // outputs m of output channel co = block column l % 16, which are 4
 // consecutive elements of the plane (one 16-byte fp32 or 8-byte half store
 // when Wo % 4 == 0 and y is NCHW). acc holds MAXB blocks, nb <= MAXB of them
 // in use. Outputs through the epilogue of o (y type, scale, bias, layout).
-template <int MAXB = 4>
+template <int MAXB = 4, bool THROUGH = false>
 __device__ __forceinline__ void store_blocks(const floatx4_t (*acc)[4], int nb, int b0, int lane,
                                              const OutSpec &o, int n, int Cout, int cb, int Ho, int Wo,
                                              int ho0, int outs)
@@ -63,12 +88,20 @@ __device__ __forceinline__ void store_blocks(const floatx4_t (*acc)[4], int nb, 
             const int co = cb * 64 + c * 16 + (lane & 15);
             if (co >= Cout) continue;
             float *yb = y + (int64_t(n) * Cout + co) * plane + int64_t(ho0) * Wo;
+            // this workgroup's segment of the channel's plane
+            const uintptr_t lo = reinterpret_cast<uintptr_t>(yb);
+            const uintptr_t hi = reinterpret_cast<uintptr_t>(yb + outs);
 #pragma unroll
             for (int s = 0; s < MAXB; ++s) {
                 if (s >= nb) break;
                 const int m = (b0 + s) * 16 + (lane >> 4) * 4;
                 if ((Wo & 3) == 0) {
-                    if (m < outs) *reinterpret_cast<floatx4_t *>(yb + m) = acc[s][c];
+                    if (m < outs) {
+                        if (THROUGH && whole_line(yb + m, lo, hi))
+                            store16_through(yb + m, acc[s][c]);
+                        else
+                            *reinterpret_cast<floatx4_t *>(yb + m) = acc[s][c];
+                    }
                 } else {
 #pragma unroll
                     for (int v = 0; v < 4; ++v)

@@ -410,7 +410,12 @@ def test_row_block_plan_geometry(monkeypatch):
     # the other kernels stay reachable
     monkeypatch.delenv("IM2WIN_IMPLICIT_KERNEL")
     d = conv.make_desc(32, 64, 56, 56, 64, 3, 3, 1, 1, conv.F16)
-    assert conv.implicit_plan(d).kernel == 2 and conv.implicit_plan(d).rows_per_tile == 7
+    # 8 rows: 8 * 56 fp32 outputs are whole 128-byte lines, written through (7 rows by the count alone)
+    assert conv.implicit_plan(d).kernel == 2 and conv.implicit_plan(d).rows_per_tile == 8
+    d32 = conv.make_desc(32, 64, 56, 56, 64, 3, 3, 1, 1, conv.F32)
+    assert conv.implicit_plan(d32).rows_per_tile == 7
+    d16 = conv.make_desc(32, 64, 56, 56, 64, 3, 3, 1, 1, conv.F16, conv.F16)
+    assert conv.implicit_plan(d16).rows_per_tile == 7          # half y: the LDS-staged stores
     monkeypatch.setenv("IM2WIN_IMPLICIT_KERNEL", "streamed")
     assert conv.implicit_plan(d).kernel == 0 and conv.implicit_plan(d).ws_bytes > 0
     monkeypatch.setenv("IM2WIN_IMPLICIT_KERNEL", "rows")
