@@ -154,44 +154,88 @@ struct WinRegs {
     bool in[UB];
 };
 
-template <int CP, int UB, typename T>
+// Unit u = (i * KH + kh) * Wwin + wc as its digits, and a step of
+// kNarrowThreads units as digits (di, dkh, dwc) of the same radices, so that
+// a thread walks its units with adds and compares instead of two divisions
+// each (STEP; measured on the fp16 stem, one row block per workgroup: 50.1
+// -> 41.8 us). The persistent form, whose registers are already spilling
+// with the next block's gathers held, keeps the divisions (stepping there
+// measured 142 -> 154 us on the fp32 stem).
+struct UnitPos {
+    int i, kh, wc;
+};
+
+__device__ __forceinline__ UnitPos unit_pos(const NarrowKArgs &a, int u)
+{
+    const int upr = a.KH * a.Wwin;
+    UnitPos p;
+    p.i = u / upr;
+    const int q = u - p.i * upr;
+    p.kh = q / a.Wwin;
+    p.wc = q - p.kh * a.Wwin;
+    return p;
+}
+
+__device__ __forceinline__ void unit_next(const NarrowKArgs &a, UnitPos &p, const UnitPos &d)
+{
+    p.wc += d.wc;
+    p.kh += d.kh;
+    p.i += d.i;
+    if (p.wc >= a.Wwin) {
+        p.wc -= a.Wwin;
+        ++p.kh;
+    }
+    if (p.kh >= a.KH) {
+        p.kh -= a.KH;
+        ++p.i;
+    }
+}
+
+template <bool STEP, int CP, int UB, typename T>
 __device__ __forceinline__ void fetch_window(const NarrowKArgs &a, const T *ximg, int ho0, int rw, int u0,
                                              int tid, WinRegs<CP, UB, T> &r)
 {
-    const int upr = a.KH * a.Wwin;
-    const int units = rw * upr;
+    const int units = rw * a.KH * a.Wwin;
     const int HW = a.H * a.W;
+    const UnitPos d = unit_pos(a, kNarrowThreads);
+    UnitPos p = unit_pos(a, u0 + tid);
 #pragma unroll
     for (int j = 0; j < UB; ++j) {
-        const int u = min(u0 + tid + j * kNarrowThreads, units - 1);
-        const int i = u / upr;
-        const int q = u - i * upr;
-        const int kh = q / a.Wwin;
-        const int wc = q - kh * a.Wwin;
-        const int ih = (ho0 + i) * a.stride - a.pad + kh;
-        const int iw = wc - a.pad;
-        r.in[j] = unsigned(ih) < unsigned(a.H) && unsigned(iw) < unsigned(a.W);
+        if constexpr (STEP) {
+            if (j > 0) unit_next(a, p, d);
+        } else {
+            p = unit_pos(a, min(u0 + tid + j * kNarrowThreads, units - 1));
+        }
+        const int ih = (ho0 + p.i) * a.stride - a.pad + p.kh;
+        const int iw = p.wc - a.pad;
+        // (without STEP the unit is clamped to the last one; put_window skips
+        // units past the end in both forms)
+        r.in[j] = (!STEP || u0 + tid + j * kNarrowThreads < units) && unsigned(ih) < unsigned(a.H) &&
+                  unsigned(iw) < unsigned(a.W);
         const int src = r.in[j] ? ih * a.W + iw : 0;
 #pragma unroll
         for (int c = 0; c < CP; ++c) r.v[j][c] = ximg[min(c, a.Cin - 1) * HW + src];
     }
 }
 
-template <int CP, int UB, typename T>
+template <bool STEP, int CP, int UB, typename T>
 __device__ __forceinline__ void put_window(const NarrowKArgs &a, T *win, int rw, int u0, int tid,
                                            const WinRegs<CP, UB, T> &r)
 {
     constexpr int V = 16 / sizeof(T);
-    const int upr = a.KH * a.Wwin;
-    const int units = rw * upr;
+    const int units = rw * a.KH * a.Wwin;
+    const UnitPos d = unit_pos(a, kNarrowThreads);
+    UnitPos p = unit_pos(a, u0 + tid);
 #pragma unroll
     for (int j = 0; j < UB; ++j) {
         const int u = u0 + tid + j * kNarrowThreads;
         if (u >= units) break;
-        const int i = u / upr;
-        const int q = u - i * upr;
-        const int kh = q / a.Wwin;
-        const int wc = q - kh * a.Wwin;
+        if constexpr (STEP) {
+            if (j > 0) unit_next(a, p, d);
+        } else {
+            p = unit_pos(a, u);
+        }
+        const int i = p.i, kh = p.kh, wc = p.wc;
         T o[CP];
 #pragma unroll
         for (int c = 0; c < CP; ++c) o[c] = (r.in[j] && c < a.Cin) ? r.v[j][c] : T(0);
@@ -235,7 +279,7 @@ __device__ __forceinline__ void load_block(const NarrowKArgs &a, const T *ximg, 
         for (int j = 0; j < FB; ++j)
             fv[j] = filter_vec<CP, GATHER>(a, w, cb, min(f0 + tid + j * kNarrowThreads, fvec - 1));
         WinRegs<CP, UB, T> wr;
-        if (u0 < units) fetch_window(a, ximg, ho0, rw, u0, tid, wr);
+        if (u0 < units) fetch_window<true>(a, ximg, ho0, rw, u0, tid, wr);
 #pragma unroll
         for (int j = 0; j < FB; ++j) {
             const int v = f0 + tid + j * kNarrowThreads;
@@ -244,7 +288,7 @@ __device__ __forceinline__ void load_block(const NarrowKArgs &a, const T *ximg, 
                 *reinterpret_cast<uint4 *>(fl + r * FS + (v - r * fv_row) * V) = fv[j];
             }
         }
-        if (u0 < units) put_window(a, win, rw, u0, tid, wr);
+        if (u0 < units) put_window<true>(a, win, rw, u0, tid, wr);
     }
 }
 
@@ -341,23 +385,23 @@ __global__ __launch_bounds__(kNarrowThreads) void conv_implicit_narrow_kernel(co
         {
             int n, ho0, rw;
             task_rows(a, t_begin, n, ho0, rw);
-            fetch_window(a, x + n * img, ho0, rw, 0, tid, nxt);
+            fetch_window<false>(a, x + n * img, ho0, rw, 0, tid, nxt);
         }
         load_filter<CP, GATHER, 4>(a, wsrc, fl, FS, cb, tid);
         for (int t = t_begin; t < t_end; ++t) {
             int n, ho0, rw;
             task_rows(a, t, n, ho0, rw);
             if (t != t_begin) __syncthreads();       // the previous block's window rows (scratch) are dead
-            put_window(a, win, rw, 0, tid, nxt);
+            put_window<false>(a, win, rw, 0, tid, nxt);
             for (int u0 = UBR; u0 < rw * a.KH * a.Wwin; u0 += UBR) {
                 WinRegs<CP, UB, uint16_t> more;
-                fetch_window(a, x + n * img, ho0, rw, u0, tid, more);
-                put_window(a, win, rw, u0, tid, more);
+                fetch_window<false>(a, x + n * img, ho0, rw, u0, tid, more);
+                put_window<false>(a, win, rw, u0, tid, more);
             }
             if (t + 1 < t_end) {
                 int n1, h1, r1;
                 task_rows(a, t + 1, n1, h1, r1);
-                fetch_window(a, x + n1 * img, h1, r1, 0, tid, nxt);
+                fetch_window<false>(a, x + n1 * img, h1, r1, 0, tid, nxt);
             }
             __syncthreads();
             run_block(n, ho0, rw);
@@ -449,23 +493,23 @@ __global__ __launch_bounds__(kNarrowThreads) void conv_implicit_narrow_f32_kerne
         {
             int n, ho0, rw;
             task_rows(a, t_begin, n, ho0, rw);
-            fetch_window(a, x + n * img, ho0, rw, 0, tid, nxt);
+            fetch_window<false>(a, x + n * img, ho0, rw, 0, tid, nxt);
         }
         load_filter<CP, GATHER, 4>(a, wsrc, fl, FS, cb, tid);
         for (int t = t_begin; t < t_end; ++t) {
             int n, ho0, rw;
             task_rows(a, t, n, ho0, rw);
             if (t != t_begin) __syncthreads();       // the previous block's window rows (scratch) are dead
-            put_window(a, win, rw, 0, tid, nxt);
+            put_window<false>(a, win, rw, 0, tid, nxt);
             for (int u0 = UBR; u0 < rw * a.KH * a.Wwin; u0 += UBR) {
                 WinRegs<CP, UB, float> more;
-                fetch_window(a, x + n * img, ho0, rw, u0, tid, more);
-                put_window(a, win, rw, u0, tid, more);
+                fetch_window<false>(a, x + n * img, ho0, rw, u0, tid, more);
+                put_window<false>(a, win, rw, u0, tid, more);
             }
             if (t + 1 < t_end) {
                 int n1, h1, r1;
                 task_rows(a, t + 1, n1, h1, r1);
-                fetch_window(a, x + n1 * img, h1, r1, 0, tid, nxt);
+                fetch_window<false>(a, x + n1 * img, h1, r1, 0, tid, nxt);
             }
             __syncthreads();
             run_block(n, ho0, rw);
