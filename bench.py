@@ -62,7 +62,8 @@ def _say(msg):
 # 3: direct-to-LDS matrix-core window-GEMM, 4: implicit convolution, window
 # rows built in LDS, filter streamed, 6: the row-block implicit kernel, filter
 # and input rows resident in LDS, 7: the narrow-channel implicit kernel, 8: the
-# pipelined row-block kernel, 32-channel K chunks double-buffered by loader waves)
+# pipelined row-block kernel, 32-channel K chunks double-buffered by loader
+# waves, 9: the split-K row-block kernel, input channels split over the waves)
 GEMM_SOURCES = {
     0: ["cnn_convolution_amd/csrc/kernels/gemm_valu.hip",
         "cnn_convolution_amd/csrc/kernels/epilogue.hpp"],
@@ -88,13 +89,19 @@ GEMM_SOURCES = {
         "cnn_convolution_amd/csrc/kernels/tile_map.hpp",
         "cnn_convolution_amd/csrc/kernels/epilogue.hpp"],
     8: ["cnn_convolution_amd/csrc/kernels/conv_implicit_pipe.hip",
+        "cnn_convolution_amd/csrc/kernels/pipe_patch.hpp",
         "cnn_convolution_amd/csrc/kernels/out_blocks.hpp",
+        "cnn_convolution_amd/csrc/kernels/lds_dma.hpp",
+        "cnn_convolution_amd/csrc/kernels/epilogue.hpp"],
+    9: ["cnn_convolution_amd/csrc/kernels/conv_implicit_ksplit.hip",
+        "cnn_convolution_amd/csrc/kernels/pipe_patch.hpp",
         "cnn_convolution_amd/csrc/kernels/lds_dma.hpp",
         "cnn_convolution_amd/csrc/kernels/epilogue.hpp"],
 }
 GEMM_KERNEL_NAMES = {0: "gemm_valu_f32", 1: "gemm_mfma",
                      3: "gemm_mfma_dma", 4: "conv_implicit",
-                     6: "conv_implicit_rows", 7: "conv_implicit_narrow", 8: "conv_implicit_pipe"}
+                     6: "conv_implicit_rows", 7: "conv_implicit_narrow", 8: "conv_implicit_pipe",
+                     9: "conv_implicit_ksplit"}
 COPY_BYTES = 256 << 20     # calibration copy for the HBM byte counters
 
 
@@ -114,7 +121,7 @@ def dominant_key(d, plan):
     import cnn_convolution_amd as conv
     if plan.algo == 1:
         ip = conv.implicit_plan(d)
-        kid = {0: 4, 2: 6, 3: 7, 4: 8}[ip.kernel]
+        kid = {0: 4, 2: 6, 3: 7, 4: 8, 5: 9}[ip.kernel]
         # the pipelined row-block kernel: stages 2 = persistent, 1 = paired form
         form = f"/s{ip.stages}" if ip.kernel == 4 else ""
         return (kid, f"i{ip.kernel}:{ip.tile_m}x{ip.tile_n}/{ip.wave_m}/r{ip.rows_per_tile}/"

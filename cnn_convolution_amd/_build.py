@@ -34,6 +34,7 @@ SOURCES = [
     os.path.join(CSRC, "kernels", "conv_implicit_rows.hip"),
     os.path.join(CSRC, "kernels", "conv_implicit_narrow.hip"),
     os.path.join(CSRC, "kernels", "conv_implicit_pipe.hip"),
+    os.path.join(CSRC, "kernels", "conv_implicit_ksplit.hip"),
 ]
 
 ARCH = "gfx950"

@@ -189,7 +189,7 @@ ImplicitArgs implicit_args(const conv2d_desc_t &d, const conv2d_implicit_plan_t 
     // persistent forms: the pipelined row-block kernel's workgroups, the narrow
     // kernel's workgroups per 64-row filter block
     a.groups = p.kernel == 4 ? int(p.tiles) : int(p.tiles / ((d.Cout + 63) / 64));
-    a.images = p.kernel == 4 ? p.images : 0;
+    a.images = p.kernel == 4 || p.kernel == 5 ? p.images : 0;
     return a;
 }
 
@@ -198,6 +198,7 @@ hipError_t launch_implicit(const conv2d_implicit_plan_t &p, const ImplicitArgs &
     if (p.kernel == 2) return launch_conv_implicit_rows(a, s);
     if (p.kernel == 3) return launch_conv_implicit_narrow(a, s);
     if (p.kernel == 4) return launch_conv_implicit_pipe(a, s);
+    if (p.kernel == 5) return launch_conv_implicit_ksplit(a, s);
     if (p.kernel == 0) return launch_conv_implicit(a, s);
     return hipErrorInvalidValue;                     // no such kernel
 }
@@ -212,7 +213,13 @@ conv2d_status_t run_implicit(const conv2d_desc_t &d, const conv2d_implicit_plan_
                              const void *w, const OutSpec &out, void *ws, hipStream_t s)
 {
     const void *wst = w;
-    if (p.ws_bytes > 0) {
+    if (p.kernel == 5) {
+        // the split-K kernel reads the filter in its fragment order
+        ProfScope ps(s, CONV2D_KERNEL_WEIGHT_STAGE);
+        if (launch_ksplit_stage(w, ws, int(d.Cout), int(d.Cin), int(d.KH * d.KW), s) != hipSuccess)
+            return CONV2D_ERR_HIP;
+        wst = ws;
+    } else if (p.ws_bytes > 0) {
         const LayoutGeom g = layout_geom(d, IM2WIN_LAYOUT_CL);
         const StageGeom sg = stage_geom(d, IM2WIN_LAYOUT_CL, p.tile_m);
         StageArgs sa{};

@@ -119,5 +119,14 @@ hipError_t launch_conv_implicit_narrow(const ImplicitArgs &a, hipStream_t s);
 // output rows x 64 output channels, 32-channel K chunks double-buffered in
 // LDS by four loader waves while four waves contract; wst is w itself
 hipError_t launch_conv_implicit_pipe(const ImplicitArgs &a, hipStream_t s);
+// split-K row-block form (fp16/bf16, Cin % 128 == 0, stride 1 or 2, 3x3, 5x5
+// or 1x1, images * R * Wo <= 208): one task of R whole output rows (or of
+// `images` whole images) x 64 output channels per workgroup, the four waves
+// splitting the input channels; wst is the filter in fragment order
+// (launch_ksplit_stage)
+hipError_t launch_conv_implicit_ksplit(const ImplicitArgs &a, hipStream_t s);
+// w [Cout][Cin][taps] (fp16/bf16) -> wf in the split-K kernel's fragment
+// order, ksplit_stage_bytes(Cout, Cin, taps) bytes (Cin % 32 == 0)
+hipError_t launch_ksplit_stage(const void *w, void *wf, int Cout, int Cin, int taps, hipStream_t s);
 
 }  // namespace im2win

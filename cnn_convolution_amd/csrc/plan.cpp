@@ -616,6 +616,84 @@ static void pick_implicit_pipelined(const conv2d_desc_t &d, int64_t Ho, int64_t 
     pick_implicit_pipe(d, Ho, Wo, p, true);
 }
 
+// Split-K row-block implicit kernel: fp16/bf16, Cin % 128 == 0, stride 1 or
+// 2, 3x3, 5x5 or 1x1, one task per workgroup of RW whole output rows (or of
+// several whole images) x 64 output channels, at most 224 outputs (14
+// blocks of 16), four K groups of two waves splitting the input channels,
+// each wave half of the task's blocks. The task shape minimises the rounds
+// of workgroups over the CUs times the blocks each wave contracts (4 or 7 as
+// compiled), ties to the larger task (each filter fragment read by fewer
+// workgroups). Default for 5x5 filters (measured on the 28x28 5x5 layer:
+// 46.7 us per kernel + 5.3 us filter staging against 59.3 us for the
+// streamed kernel); on the 3x3 layers the staging launch cancels its gain
+// over the pipelined kernels (deep 3x3: 22.6 + 3.1 against 25.3 us), so
+// there it is taken when IM2WIN_IMPLICIT_KERNEL=ksplit. IM2WIN_IMPLICIT_ROWS
+// sets RW and IM2WIN_IMPLICIT_IMAGES the images per task.
+static void pick_implicit_ksplit(const conv2d_desc_t &d, int64_t Ho, int64_t Wo, conv2d_implicit_plan_t *p,
+                                 bool dflt) {
+    if (d.dtype == CONV2D_F32 || d.Cin % (32 * kKsplitGroups) != 0 || d.stride > 2 || Wo < 1 || Ho < 1) return;
+    if (!((d.KH == 3 && d.KW == 3) || (d.KH == 1 && d.KW == 1) || (d.KH == 5 && d.KW == 5))) return;
+    if (d.Cin * d.H * d.W >= (int64_t(1) << 31)) return;
+    if (const char *e = std::getenv("IM2WIN_IMPLICIT_KERNEL")) {
+        if (std::strcmp(e, "ksplit") != 0) return;
+    } else if (!dflt || std::getenv("IM2WIN_IMPLICIT_TILE")) {
+        return;
+    }
+    const int64_t s = d.stride, iw = d.W + 2 * d.pad;
+    const int64_t co_blocks = ceil_div(d.Cout, 64);
+    const int64_t sl1 = (Ho - 1) * s + d.KH;             // rows of one whole image
+    int64_t best_rw = 0, best_img = 0;
+    double best_cost = 0.0;
+    auto consider = [&](int64_t rw, int64_t img) {
+        const int64_t outs = img * rw * Wo;
+        if (outs > kKsplitMaxOuts) return;
+        const int64_t sl = img * ((rw - 1) * s + d.KH);
+        const int64_t nbw = ksplit_nbw(outs);
+        if (ksplit_lds_bytes(sl, iw, d.Cin, nbw) > kImplicitMaxLdsBytes) return;
+        const int64_t tasks = img > 1 ? co_blocks * ceil_div(d.N, img) : co_blocks * d.N * ceil_div(Ho, rw);
+        const double cost = double(ceil_div(tasks, 256)) * double(nbw);
+        if (best_rw == 0 || cost < best_cost || (cost == best_cost && outs > best_img * best_rw * Wo)) {
+            best_rw = rw;
+            best_img = img;
+            best_cost = cost;
+        }
+    };
+    for (int64_t rw = 1; rw <= Ho; ++rw) consider(ceil_div(Ho, ceil_div(Ho, rw)), 1);
+    for (int64_t img = 2; img <= d.N && img * Ho * Wo <= kKsplitMaxOuts; ++img) consider(Ho, img);
+    (void)sl1;
+    if (const char *e = std::getenv("IM2WIN_IMPLICIT_IMAGES")) {
+        const int64_t v = std::atoi(e);
+        if (v >= 2 && v <= d.N && v * Ho * Wo <= kKsplitMaxOuts &&
+            ksplit_lds_bytes(v * sl1, iw, d.Cin, ksplit_nbw(v * Ho * Wo)) <= kImplicitMaxLdsBytes) {
+            best_img = v;
+            best_rw = Ho;
+        }
+    }
+    if (const char *e = std::getenv("IM2WIN_IMPLICIT_ROWS")) {
+        const int64_t v = std::min<int64_t>(std::atoi(e), Ho);
+        if (v >= 1 && v * Wo <= kKsplitMaxOuts &&
+            ksplit_lds_bytes((v - 1) * s + d.KH, iw, d.Cin, ksplit_nbw(v * Wo)) <= kImplicitMaxLdsBytes) {
+            best_rw = v;
+            best_img = 1;
+        }
+    }
+    if (best_rw == 0) return;
+    const int64_t outs = best_img * best_rw * Wo;
+    p->kernel = 5;
+    p->tile_m = 64;
+    p->tile_n = int32_t(ksplit_nbw(outs) * 16);
+    p->wave_m = int32_t(kKsplitGroups);
+    p->rows_per_tile = int32_t(best_rw);
+    p->cols_per_tile = int32_t(Wo);
+    p->patch_rows = int32_t(best_img * ((best_rw - 1) * s + d.KH));
+    p->patch_cols = int32_t(iw);
+    p->stages = 0;
+    p->images = int32_t(best_img);
+    p->lds_bytes = ksplit_lds_bytes(p->patch_rows, iw, d.Cin, ksplit_nbw(outs));
+    p->tiles = best_img > 1 ? co_blocks * ceil_div(d.N, best_img) : co_blocks * d.N * ceil_div(Ho, best_rw);
+    p->ws_bytes = round_up(ksplit_stage_bytes(d.Cout, d.Cin, d.KH * d.KW), 256);
+}
+
 // Narrow-channel implicit kernel: Cin <= 8 (the RGB stem and its kind), any
 // filter and stride, Wo <= 512, fp16/bf16/fp32. A workgroup of eight waves
 // takes R output rows of one image (R * Wo <= 512) and 64 output channels,
@@ -787,6 +865,7 @@ static conv2d_status_t compute_implicit_plan(const conv2d_desc_t &d, conv2d_impl
     // pipelined forms take the 3x3 and 1x1 layers of stride 1 or 2
     const bool one_block = p->kernel == 2 && d.Cin == 64 && d.W % 8 == 0;
     pick_implicit_pipelined(d, Ho, Wo, p, !one_block);
+    pick_implicit_ksplit(d, Ho, Wo, p, d.KH * d.KW >= 25);
     return CONV2D_OK;
 }
 

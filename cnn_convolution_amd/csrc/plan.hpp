@@ -48,6 +48,23 @@ inline int64_t pipe_lds_bytes(int64_t taps, int64_t sl, int64_t iw) {
 inline int64_t pair_lds_bytes(int64_t taps, int64_t sl, int64_t iw) {
     return std::max<int64_t>(taps * 4096 + sl * iw * 64, kImplicitStoreScratchBytes);
 }
+// split-K row-block implicit form: four K groups (two waves each), each with
+// two LDS slots (one when it has a single chunk) of sl input rows of iw
+// positions x 64 bytes; after the contraction the same LDS holds the partial
+// sums that the groups exchange, two rounds of 12 KB per 16-output block of a
+// wave (nbw blocks)
+constexpr int64_t kKsplitGroups = 4;
+constexpr int64_t kKsplitMaxOuts = 14 * 16;    // two waves of at most 7 blocks
+inline int64_t ksplit_lds_bytes(int64_t sl, int64_t iw, int64_t cin, int64_t nbw) {
+    const int64_t spw = cin / (32 * kKsplitGroups) > 1 ? 2 : 1;
+    return std::max<int64_t>(kKsplitGroups * spw * sl * iw * 64, 12 * nbw * 1024);
+}
+// blocks per wave as compiled: 4 (tasks of at most 128 outputs) or 7
+inline int64_t ksplit_nbw(int64_t outs) { return outs <= 8 * 16 ? 4 : 7; }
+// the filter staged in fragment order: 64-row output-channel blocks x Cin x taps
+inline int64_t ksplit_stage_bytes(int64_t cout, int64_t cin, int64_t taps) {
+    return ((cout + 63) / 64) * 64 * cin * taps * 2;
+}
 // narrow-channel implicit form: the filter block (64 rows of kp elements + 16
 // bytes) + r window rows of lp elements, es bytes per element (the window rows'
 // space holds at least the store scratch)
