@@ -14,7 +14,7 @@ include/im2win_conv2d.h).
 from __future__ import annotations
 
 from . import _lib
-from ._lib import (Conv2dError, Desc, Plan, ImplicitPlan, LAYOUT_CL, LAYOUT_ROW,  # noqa: F401
+from ._lib import (Conv2dError, Desc, Plan, ImplicitPlan, LAYOUT_CL, LAYOUT_FRAG, LAYOUT_ROW,  # noqa: F401
                    F16, F32, BF16, NCHW, NHWC, make_desc, workspace_size, plan, implicit_plan,
                    implicit_workspace_size, profile_enable, profile_read, status_string)
 
@@ -180,6 +180,8 @@ def weight_stage(w, stride: int, pad: int, x_hw, layout: int):
     p = plan(d)
     if layout == LAYOUT_ROW:
         rows, row_len = -(-Cout // 16) * 16, Cin * KH * KW
+    elif layout == LAYOUT_FRAG:
+        rows, row_len = -(-Cout // 64) * 64, Cin * KH * KW
     else:
         rows, row_len = Cout, p.K_stage if p.layout == LAYOUT_CL else None
         if row_len is None:

@@ -15,6 +15,7 @@ LIBPATH = os.path.join(PKG, "lib", "libim2win_conv2d.so")
 F32, F16, BF16 = 0, 1, 2
 NCHW, NHWC = 0, 1                    # conv2d_layout_t: memory layout of x, w and y
 LAYOUT_ROW, LAYOUT_CL = 0, 1         # im2win_layout_t: storage order of the window tensor
+LAYOUT_FRAG = 2                      # im2win_layout_t: the split-K kernel's staged filter order
 KERNEL_WEIGHT_STAGE, KERNEL_PACK, KERNEL_GEMM, KERNEL_IMPLICIT, KERNEL_KINDS = 0, 1, 2, 3, 4
 
 STATUS = {

@@ -406,10 +406,21 @@ conv2d_status_t im2win_weight_stage(const conv2d_desc_t *d, int32_t layout, cons
     conv2d_plan_t p;
     const conv2d_status_t st = make_plan(*d, &p);
     if (st != CONV2D_OK) return st;
-    if (layout != IM2WIN_LAYOUT_ROW && layout != IM2WIN_LAYOUT_CL) return CONV2D_ERR_UNSUPPORTED;
+    if (layout != IM2WIN_LAYOUT_ROW && layout != IM2WIN_LAYOUT_CL && layout != IM2WIN_LAYOUT_FRAG)
+        return CONV2D_ERR_UNSUPPORTED;
     if (layout == IM2WIN_LAYOUT_ROW && d->layout == CONV2D_NHWC) return CONV2D_ERR_UNSUPPORTED;
+    const int64_t taps = d->KH * d->KW;
+    if (layout == IM2WIN_LAYOUT_FRAG &&
+        (d->dtype == CONV2D_F32 || d->layout == CONV2D_NHWC || d->Cin % 32 != 0 ||
+         !(taps == 1 || (d->KH == 3 && d->KW == 3) || (d->KH == 5 && d->KW == 5))))
+        return CONV2D_ERR_UNSUPPORTED;
     if (!w || !out) return CONV2D_ERR_NULL_POINTER;
     if (!aligned(w, 16) || !aligned(out, 16)) return CONV2D_ERR_MISALIGNED;
+    if (layout == IM2WIN_LAYOUT_FRAG)
+        return launch_ksplit_stage(w, out, int(d->Cout), int(d->Cin), int(taps), static_cast<hipStream_t>(stream)) ==
+                       hipSuccess
+                   ? CONV2D_OK
+                   : CONV2D_ERR_HIP;
     const LayoutGeom g = layout_geom(*d, layout);
     const StageGeom sg = stage_geom(*d, layout, p.gemm_tile_m);
     StageArgs sa{};

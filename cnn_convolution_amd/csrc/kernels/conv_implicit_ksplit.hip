@@ -47,11 +47,13 @@ constexpr int kKsGroups = int(kKsplitGroups);   // K groups
 constexpr int kKsThreads = 512;                  // 8 waves: K group x output half
 
 // patch units a lane holds in registers between a chunk's global loads and
-// its LDS writes (32 registers for any vector width)
-template <int V>
+// its LDS writes (32 registers for any vector width); none for filters of
+// more than 9 taps, whose longer contraction keeps more registers live (the
+// units then go straight from memory to LDS at the end of a chunk)
+template <int V, int TAPS>
 constexpr int ks_units_held()
 {
-    return V == 8 ? 1 : V == 4 ? 2 : 4;
+    return TAPS > 9 ? 0 : V == 8 ? 1 : V == 4 ? 2 : 4;
 }
 
 // Staged filter, fragment order: fragment (cb, blk, t, c4) is 64 lanes x 8
@@ -106,7 +108,9 @@ __global__ __launch_bounds__(256) void ks_stage_kernel(const uint16_t *__restric
 // patch position q are the 16 bytes at (g * NP + q) * 16, NP positions per
 // granule plane. Sixteen lanes that read one granule at consecutive
 // positions hit consecutive 16-byte slots (no bank conflict), and a tap's
-// window is the same address plus one uniform offset.
+// window is the same address plus one uniform offset. NP is 1 modulo 8, so
+// that the four granules of one position fall in different bank groups when
+// the loads write them.
 template <int V, bool MI>
 __device__ __forceinline__ void ks_put_unit(uint16_t *patch, int NP, const PipeKArgs &a, const PipeTask &tk,
                                             const ChunkGeom &cg, int u, const PlaneVec<V> *raw)
@@ -115,15 +119,17 @@ __device__ __forceinline__ void ks_put_unit(uint16_t *patch, int NP, const PipeK
     const int g = u1 & 3;
     const int p0 = (cg.j_lo + (u1 >> 2)) * V;
     const int row0 = im * tk.SL - tk.ih0;            // patch row of input row 0 of this image
-    int r = p0 / a.W;
-    int col = p0 - r * a.W;
     uint16_t *const gp = patch + g * NP * 8;
+    {
+        int r = p0 / a.W;
+        int col = p0 - r * a.W;
 #pragma unroll
-    for (int v = 0; v < V; ++v) {
-        const int p = p0 + v;
-        if (p >= cg.p_lo && p < cg.p_hi)
-            *reinterpret_cast<uint4 *>(gp + ((row0 + r) * a.IW + a.pad + col) * 8) = position_of<V>(raw, v);
-        if (++col == a.W) { col = 0; ++r; }
+        for (int v = 0; v < V; ++v) {
+            const int p = p0 + v;
+            if (p >= cg.p_lo && p < cg.p_hi)
+                *reinterpret_cast<uint4 *>(gp + ((row0 + r) * a.IW + a.pad + col) * 8) = position_of<V>(raw, v);
+            if (++col == a.W) { col = 0; ++r; }
+        }
     }
 }
 
@@ -157,7 +163,7 @@ __global__ __launch_bounds__(kKsThreads) __attribute__((amdgpu_waves_per_eu(2, 2
     const PipeKArgs a)
 {
     constexpr int TAPS = KH * KW;
-    constexpr int UH = ks_units_held<V>();
+    constexpr int UH = ks_units_held<V, TAPS>();
     extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
@@ -173,7 +179,7 @@ __global__ __launch_bounds__(kKsThreads) __attribute__((amdgpu_waves_per_eu(2, 2
     uint16_t *const slot0 = lds + spw * kg * a.slot_halves;
     uint16_t *const slot1 = slot0 + (spw - 1) * a.slot_halves;
 
-    PlaneVec<V> raw[UH][8];
+    PlaneVec<V> raw[UH > 0 ? UH : 1][8];
     auto fetch = [&](int j) {
         const int blk = kg + kKsGroups * j;
 #pragma unroll
@@ -390,7 +396,7 @@ hipError_t launch_conv_implicit_ksplit(const ImplicitArgs &h, hipStream_t s)
     if (ntasks > 0x7fffffff) return hipErrorInvalidValue;
     a.ntasks = int(ntasks);
     a.SLmax = h.IR;
-    a.slot_halves = h.IR * h.IW * kChunkC;
+    a.slot_halves = int(ksplit_plane(h.IR, h.IW)) * 4 * 8;
     const int64_t lds = ksplit_lds_bytes(h.IR, h.IW, h.Cin, nbw);
     if (lds > kImplicitMaxLdsBytes) return hipErrorInvalidValue;
     const int hw = h.H * h.W;

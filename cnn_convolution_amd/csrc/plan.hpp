@@ -55,9 +55,11 @@ inline int64_t pair_lds_bytes(int64_t taps, int64_t sl, int64_t iw) {
 // wave (nbw blocks)
 constexpr int64_t kKsplitGroups = 4;
 constexpr int64_t kKsplitMaxOuts = 14 * 16;    // two waves of at most 7 blocks
+// positions per granule plane of a slot: sl * iw rounded up to 1 modulo 8
+inline int64_t ksplit_plane(int64_t sl, int64_t iw) { return ((sl * iw + 6) / 8) * 8 + 1; }
 inline int64_t ksplit_lds_bytes(int64_t sl, int64_t iw, int64_t cin, int64_t nbw) {
     const int64_t spw = cin / (32 * kKsplitGroups) > 1 ? 2 : 1;
-    return std::max<int64_t>(kKsplitGroups * spw * sl * iw * 64, 12 * nbw * 1024);
+    return std::max<int64_t>(kKsplitGroups * spw * ksplit_plane(sl, iw) * 64, 12 * nbw * 1024);
 }
 // blocks per wave as compiled: 4 (tasks of at most 128 outputs) or 7
 inline int64_t ksplit_nbw(int64_t outs) { return outs <= 8 * 16 ? 4 : 7; }

@@ -114,7 +114,10 @@ typedef enum {
  *   CL  : T[r][pos][ci]   channels innermost; the window of column wo is ONE
  *         contiguous run of KW*KH*Cin_pad elements. Used by the fp16/bf16
  *         path. Cin is zero-padded to Cin_pad (see conv2d_plan_t). */
-typedef enum { IM2WIN_LAYOUT_ROW = 0, IM2WIN_LAYOUT_CL = 1 } im2win_layout_t;
+typedef enum { IM2WIN_LAYOUT_ROW = 0, IM2WIN_LAYOUT_CL = 1, IM2WIN_LAYOUT_FRAG = 2 } im2win_layout_t;
+/* IM2WIN_LAYOUT_FRAG names no window tensor: it is the order of the staged
+ * filter of the split-K implicit kernel (conv2d_implicit_plan_t.kernel 5),
+ * for im2win_weight_stage only (see there). */
 
 /* What conv2d_fwd will do for a descriptor (host-side only, no GPU needed). */
 typedef struct {
@@ -206,11 +209,21 @@ conv2d_status_t im2win_pack(const conv2d_desc_t *d, int32_t layout, const void *
                             int64_t row0, int64_t rows, void *stream);
 
 /* Row (a3) on its own: restage w into the K order of the window of `layout`:
- *   ROW: out[cb][ci][kh][kw][j] = w[cb*16 + j][ci][kh][kw], j < 16, Cout padded
- *        to a multiple of 16 with zeros (fp32 path);
- *   CL : out[co][(kw*KH + kh)*Cin_pad + ci] = w[co][ci][kh][kw], rows padded to
- *        Cout_stage and to K_stage with zeros (w[co][kh][kw][ci] for NHWC).
- * out holds Cout_stage * K_stage elements of dtype and is 16-byte aligned. */
+ *   ROW : out[cb][ci][kh][kw][j] = w[cb*16 + j][ci][kh][kw], j < 16, Cout padded
+ *         to a multiple of 16 with zeros (fp32 path);
+ *   CL  : out[co][(kw*KH + kh)*Cin_pad + ci] = w[co][ci][kh][kw], rows padded to
+ *         Cout_stage and to K_stage with zeros (w[co][kh][kw][ci] for NHWC).
+ *         out holds Cout_stage * K_stage elements of dtype;
+ *   FRAG: the matrix-core fragment order of the split-K implicit kernel
+ *         (fp16/bf16, NCHW, Cin % 32 == 0, 1x1, 3x3 or 5x5 filters): with
+ *         taps t = kh*KW + kw, fragment (cb, blk, t, c4) is 64 lanes x 8
+ *         elements, lane l holding w[cb*64 + c4*16 + (l % 16)][blk*32 +
+ *         (l / 16)*8 + e][t], e < 8 (zero past Cout), fragments in the order
+ *         ((cb*Cin/32 + blk)*taps + t)*4 + c4; out holds ceil(Cout/64)*64 *
+ *         Cin * taps elements (conv2d_implicit_workspace_size(d) bytes when
+ *         the plan's kernel is 5).
+ * out is 16-byte aligned. CONV2D_ERR_UNSUPPORTED for a layout the layer does
+ * not take. */
 conv2d_status_t im2win_weight_stage(const conv2d_desc_t *d, int32_t layout, const void *w,
                                     void *out, void *stream);
 
@@ -282,14 +295,23 @@ typedef struct {
                                      rows_per_tile whole output rows (or of
                                      `images` whole images) x 64 output channels
                                      over 32-channel K chunks double-buffered in
-                                     LDS, w as stored (ws_bytes 0)                  */
+                                     LDS, w as stored (ws_bytes 0); 5 (default
+                                     for 5x5 filters with Cin % 128 == 0, else
+                                     by name): split-K row-block, tasks of
+                                     rows_per_tile whole output rows (or of
+                                     `images` whole images, at most 224
+                                     outputs) x 64 output channels, four K
+                                     groups of two waves splitting the input
+                                     channels, the filter staged in the
+                                     workspace in fragment order
+                                     (IM2WIN_LAYOUT_FRAG)                           */
     int32_t stages;               /* kernel 0: filter K stages in flight + 1 (LDS
                                      stage buffers); kernel 3: channels per window
                                      position; kernel 4: 2 = persistent workgroups
                                      (tiles of them) with loading and computing
                                      waves, 1 = one task per workgroup (tiles
-                                     tasks), two workgroups per CU                 */
-    int32_t images;               /* kernel 4: whole images per task when > 1 (then
+                                     tasks), two workgroups per CU; 0 otherwise    */
+    int32_t images;               /* kernels 4, 5: whole images per task when > 1 (then
                                      rows_per_tile = Ho and patch_rows = images *
                                      (Ho + KH - 1)); 1 otherwise, 0 for the other
                                      kernels                                        */
@@ -300,8 +322,9 @@ typedef struct {
                                      filter's LDS row, KW*KH*CP rounded up to the
                                      matrix-core K step)                            */
     int64_t ws_bytes;             /* the staged filter of kernel 0 (0 for a 1x1
-                                     filter) and of kernel 3 when tiles > 256; 0
-                                     for kernels 2 and 4                            */
+                                     filter), of kernel 3 when tiles > 256 and of
+                                     kernel 5 (fragment order); 0 for kernels 2
+                                     and 4                                          */
     int64_t flops;                /* 2*N*Cout*Ho*Wo*Cin*KH*KW                        */
 } conv2d_implicit_plan_t;
 
@@ -326,10 +349,12 @@ conv2d_status_t conv2d_fwd_implicit(const conv2d_desc_t *d, const void *x, const
 
 /* Rows (a2, a4, a5) of the implicit form on their own: the implicit kernel
  * with a filter already staged in the window's K order (as
- * im2win_weight_stage writes it for IM2WIN_LAYOUT_CL), or w itself where the
- * plan keeps no staged filter (conv2d_implicit_workspace_size(d) == 0: a 1x1
- * filter, or the row-block, pipelined and small narrow-channel launches, which
- * reorder w in LDS on their own),
+ * im2win_weight_stage writes it for IM2WIN_LAYOUT_CL; for IM2WIN_LAYOUT_FRAG
+ * when the plan's kernel is 5, so that a caller whose filter does not change
+ * stages it once), or w itself where the plan keeps no staged filter
+ * (conv2d_implicit_workspace_size(d) == 0: a 1x1 filter outside kernel 5, or
+ * the row-block, pipelined and small narrow-channel launches, which reorder w
+ * in LDS on their own),
  * writing all of y (y_dtype of the descriptor, no bias or scale). Device
  * pointers, 16-byte aligned. */
 conv2d_status_t im2win_implicit_gemm(const conv2d_desc_t *d, const void *x, const void *wst,

@@ -185,3 +185,27 @@ def test_ksplit_full_size_sampled(name, monkeypatch):
     idx = _sample_indices(cfg.N, cfg.Cout, ho, wo, rng)
     assert np.isfinite(yf[idx]).all()
     check(yf[idx], x, w, cfg.stride, cfg.pad, dt, idx=idx, what=f"{name} {dt}")
+
+
+def test_ksplit_kernel_alone_with_filter_staged_once(monkeypatch):
+    """A filter staged once in fragment order (im2win_weight_stage,
+    IM2WIN_LAYOUT_FRAG) serves two calls of the kernel alone
+    (im2win_implicit_gemm), equal bit for bit to conv2d_fwd's output."""
+    monkeypatch.setenv("IM2WIN_IMPLICIT_KERNEL", "ksplit")
+    N, Cin, H, W, Cout, KH, KW, s, p = 2, 256, 14, 14, 72, 3, 3, 1, 1
+    x, w = workloads.make_inputs(N, Cin, H, W, Cout, KH, KW, seed=47, dtype="bf16")
+    xd, wd = x.to(DEV), w.to(DEV)
+    d = conv.describe(tuple(x.shape), tuple(w.shape), s, p, conv.BF16)
+    pl = conv.implicit_plan(d)
+    assert pl.kernel == 5
+    wst, geo = conv.weight_stage(wd, s, p, (H, W), conv.LAYOUT_FRAG)
+    assert wst.numel() * 2 == conv.implicit_workspace_size(d) == geo["rows"] * geo["row_len"] * 2
+    ys = []
+    for _ in range(2):
+        y = torch.empty((N, Cout, pl.Ho, pl.Wo), dtype=torch.float32, device=DEV)
+        conv.implicit_gemm(xd, wst, y, d)
+        ys.append(y)
+    ref = conv.conv2d_implicit(xd, wd, stride=s, pad=p)
+    torch.cuda.synchronize()
+    assert torch.equal(ys[0], ref) and torch.equal(ys[1], ref)
+    check(ys[0], x, w, s, p, "bf16")

@@ -145,7 +145,10 @@ def test_pointer_checks_before_launch(monkeypatch):
     assert _lib.pack(d, 1, 16, 16, 0, 1, None) == 4         # channels-last is half precision
     assert _lib.pack(d, 2, 16, 16, 0, 1, None) == 4
     assert _lib.weight_stage(d, 3, 16, 16, None) == 4
+    assert _lib.weight_stage(d, conv.LAYOUT_FRAG, 16, 16, None) == 4   # fragment order: fp16/bf16 only
     assert _lib.pack(d, 0, None, 16, 0, 1, None) == 2
+    for shape in [(1, 48, 8, 8, 16, 3, 3, 1, 1), (1, 64, 8, 8, 16, 7, 7, 1, 3)]:   # Cin % 32, filter
+        assert _lib.weight_stage(conv.make_desc(*shape, conv.F16), conv.LAYOUT_FRAG, 16, 16, None) == 4
 
 
 def _gpu_visible():
@@ -176,6 +179,10 @@ def test_launch_failure_reports_hip_status(algo, dt, monkeypatch):
     assert _lib.pack(d, conv.LAYOUT_CL, X, WS, 0, 3, None) == 6
     assert _lib.weight_stage(d, conv.LAYOUT_CL, W_, WS, None) == 6
     assert _lib.window_gemm(d, WS, W_, Y, 0, 3, None) == 6
+    d = conv.make_desc(2, 128, 12, 12, 64, 5, 5, 1, 2, conv.F16)     # the split-K kernel: staging, then the kernel
+    assert conv.implicit_plan(d).kernel == 5
+    assert _lib.fwd_implicit(d, X, W_, Y, WS, None) == 6
+    assert _lib.weight_stage(d, conv.LAYOUT_FRAG, W_, WS, None) == 6
 
 
 def _compiled_mfma_tiles():
@@ -644,3 +651,32 @@ def test_planner_picks_the_measured_ablation_variant(name, monkeypatch):
     assert p.gemm_kernel == 3 and p.gemm_ablate == _ABLATION_CHOICE[name]
     monkeypatch.setenv("IM2WIN_ABLATE", "serpentine")          # the override still wins
     assert conv.plan(conv.make_desc(*cfg.desc().values(), dt)).gemm_ablate == 1
+
+
+def test_ksplit_plan_geometry(monkeypatch):
+    """The split-K kernel (5): planned by default for 5x5 filters with Cin a
+    multiple of 128, by name elsewhere; tasks of at most 224 outputs, whole
+    images stacked for small images, the fragment-ordered filter as workspace
+    and LDS within one CU."""
+    from cnn_convolution_amd import _lib as L
+    five = conv.implicit_plan(conv.make_desc(64, 128, 28, 28, 128, 5, 5, 1, 2, conv.F16))
+    assert five.kernel == 5 and five.rows_per_tile == 7 and five.images == 1
+    assert five.tiles == 2 * 64 * 4 and five.ws_bytes == 128 * 128 * 25 * 2
+    assert five.lds_bytes <= 160 * 1024 and five.wave_m == 4
+    assert conv.plan(conv.make_desc(64, 128, 28, 28, 128, 5, 5, 1, 2, conv.F16)).ws_bytes == five.ws_bytes
+    for shape in [(64, 256, 14, 14, 256, 3, 3, 1, 1), (64, 512, 7, 7, 512, 3, 3, 1, 1),
+                  (2, 64, 28, 28, 64, 5, 5, 1, 2)]:          # 3x3 layers, and Cin % 128 != 0
+        assert conv.implicit_plan(conv.make_desc(*shape, conv.F16)).kernel != 5, shape
+    monkeypatch.setenv("IM2WIN_IMPLICIT_KERNEL", "ksplit")
+    deep = conv.implicit_plan(conv.make_desc(64, 256, 14, 14, 256, 3, 3, 1, 1, conv.BF16))
+    assert (deep.kernel, deep.rows_per_tile, deep.images, deep.tiles) == (5, 14, 1, 256)
+    assert deep.ws_bytes == 256 * 256 * 9 * 2 and deep.patch_rows == 16 and deep.patch_cols == 16
+    m512 = conv.implicit_plan(conv.make_desc(64, 512, 7, 7, 512, 3, 3, 1, 1, conv.F16))
+    assert (m512.kernel, m512.images, m512.rows_per_tile, m512.tiles) == (5, 2, 7, 8 * 32)
+    assert m512.patch_rows == 2 * 9 and m512.lds_bytes <= 160 * 1024
+    odd = conv.implicit_plan(conv.make_desc(3, 128, 9, 9, 70, 3, 3, 1, 1, conv.F16))
+    assert odd.kernel == 5 and odd.ws_bytes == 128 * 128 * 9 * 2       # Cout padded to 128
+    for p in (five, deep, m512, odd):
+        assert p.images * p.rows_per_tile * p.Wo <= 224
+    assert conv.implicit_plan(conv.make_desc(2, 64, 9, 9, 64, 3, 3, 1, 1, conv.F16)).kernel != 5
+    assert L.LAYOUT_FRAG == 2

@@ -83,3 +83,47 @@ def test_unclamped_row_range_read_past_the_plane(monkeypatch):
     N, Cin, H, W = shape[:4]
     bad = [(pl_, pos, V) for pl_, pos, V in _reads(shape, pl, clamp=False) if pos + V > H * W]
     assert bad and max(pl_ for pl_, _, _ in bad) == N * Cin - 1
+
+
+KS_SHAPES = [
+    # N, Cin, H, W, Cout, KH, KW, stride, pad (Cin a multiple of 128)
+    (8, 128, 8, 4, 64, 1, 1, 1, 2),      # 1x1 pad 2: row tasks below the image
+    (2, 128, 6, 6, 72, 3, 3, 1, 4),      # 3x3 pad 4
+    (1, 256, 5, 7, 40, 3, 3, 1, 4),      # odd planes
+    (3, 128, 7, 6, 64, 1, 1, 2, 3),      # stride 2
+    (2, 384, 9, 10, 64, 3, 3, 2, 4),     # stride 2, three chunks per K group
+    (64, 256, 14, 14, 256, 3, 3, 1, 1),  # the deep 3x3 layer
+    (64, 512, 7, 7, 512, 3, 3, 1, 1),    # the 512-channel 7x7 layer (two images per task)
+    (4, 128, 28, 28, 128, 5, 5, 1, 2),   # the 5x5 layer's images
+]
+
+
+@pytest.mark.parametrize("rows", [None, 1, 2])
+@pytest.mark.parametrize("shape", KS_SHAPES, ids=[str(s) for s in KS_SHAPES])
+def test_ksplit_kernel_reads_and_patch_writes_stay_in_bounds(shape, rows, monkeypatch):
+    """The split-K kernel loads its patches with the same task and chunk
+    geometry: every read stays inside its own plane of x, and every position
+    the loads write (row0 + r) * IW + pad + col lies inside the task's patch
+    of images * SL rows of IW positions."""
+    monkeypatch.setenv("IM2WIN_IMPLICIT_KERNEL", "ksplit")
+    if rows is not None:
+        monkeypatch.setenv("IM2WIN_IMPLICIT_ROWS", str(rows))
+    pl = conv.implicit_plan(conv.make_desc(*shape, conv.F16))
+    assert pl.kernel == 5
+    N, Cin, H, W, Cout, KH, KW, s, p = shape
+    n = 0
+    for plane, pos, V in _reads(shape, pl):
+        assert 0 <= plane < N * Cin and 0 <= pos and pos + V <= H * W, (plane, pos, V)
+        n += 1
+    assert n > 0
+    # patch positions written: rows of the image inside the task, shifted by the task's first row
+    Ho, R, img = pl.Ho, pl.rows_per_tile, max(pl.images, 1)
+    IW = W + 2 * p
+    for ho0 in range(0, Ho, R):
+        rw = min(R, Ho - ho0)
+        ih0, SL = ho0 * s - p, (rw - 1) * s + KH
+        assert img * SL <= pl.patch_rows and pl.patch_cols == IW
+        for ih in range(max(ih0, 0), min(ih0 + SL, H)):
+            for col in range(W):
+                q = (ih - ih0) * IW + p + col
+                assert 0 <= q < SL * IW
