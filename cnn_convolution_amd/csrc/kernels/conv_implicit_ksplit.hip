@@ -174,8 +174,13 @@ __global__ __launch_bounds__(kKsThreads) __attribute__((amdgpu_waves_per_eu(2, 2
     const ChunkGeom cg = chunk_geom<V, MI>(a, tk);
     const int nch = a.Cin / kChunkC;
     const int steps = nch / kKsGroups;
-    const int spw = steps > 1 ? 2 : 1;             // LDS slots per K group
+    const int spw = steps > 1 ? a.slots : 1;       // LDS slots per K group
     const int NP = a.slot_halves / 32;             // positions per granule plane
+    // this wave's 64 output channels: the task's (co_split 1) or its half of
+    // the task's 128 (co_split 2); the filter is read from the last block
+    // that exists where the half lies past Cout (nothing of it is stored)
+    const int cbw = a.co_split == 2 ? tk.cb * 2 + half : tk.cb;
+    const int cba = min(cbw, (a.Cout - 1) >> 6);
     uint16_t *const slot0 = lds + spw * kg * a.slot_halves;
     uint16_t *const slot1 = slot0 + (spw - 1) * a.slot_halves;
 
@@ -213,8 +218,9 @@ __global__ __launch_bounds__(kKsThreads) __attribute__((amdgpu_waves_per_eu(2, 2
     const int outs = tk.nimg * tk.rw * a.Wo;
     const int opi = tk.rw * a.Wo;
     const int nbt = (outs + 15) >> 4;
-    const int b0 = half ? (nbt + 1) >> 1 : 0;
-    const int nbs = half ? nbt - b0 : (nbt + 1) >> 1;
+    const bool split_out = a.co_split == 1;
+    const int b0 = split_out && half ? (nbt + 1) >> 1 : 0;
+    const int nbs = !split_out ? nbt : half ? nbt - b0 : (nbt + 1) >> 1;
     const int gr = lane >> 4;
     int bb[NBW];
 #pragma unroll
@@ -229,7 +235,7 @@ __global__ __launch_bounds__(kKsThreads) __attribute__((amdgpu_waves_per_eu(2, 2
     // for this iteration, fa1 for the next, loaded during this one
     auto load_a = [&](int it, uint4 *f) {
         const int j = it / TAPS, t = it - j * TAPS;
-        const uint4 *p = ks_frag(a.w, nch, TAPS, tk.cb, kg + kKsGroups * j, t) + lane;
+        const uint4 *p = ks_frag(a.w, nch, TAPS, cba, kg + kKsGroups * j, t) + lane;
 #pragma unroll
         for (int c4 = 0; c4 < 4; ++c4) f[c4] = p[c4 * 64];
     };
@@ -271,7 +277,9 @@ __global__ __launch_bounds__(kKsThreads) __attribute__((amdgpu_waves_per_eu(2, 2
         if (t + 1 == TAPS) {
             if (j + 1 < steps) {
                 // the other slot was last read in the previous chunk, which
-                // every wave finished before the last barrier
+                // every wave finished before the last barrier; with one slot,
+                // every wave first finishes reading this chunk
+                if (spw == 1) stage_barrier();
                 put(j + 1, (j & 1) ? slot0 : slot1);
                 stage_barrier();
             }
@@ -318,7 +326,7 @@ __global__ __launch_bounds__(kKsThreads) __attribute__((amdgpu_waves_per_eu(2, 2
     // lane l holds outputs m0 .. m0+3 (m0 = 16 (b0 + s) + 4 (l >> 4)) of
     // output channel co: consecutive elements of one plane unless they cross
     // an image (several images per task) or the task's end
-    const int co = tk.cb * 64 + kg * 16 + (lane & 15);
+    const int co = cbw * 64 + kg * 16 + (lane & 15);
     if (co >= a.Cout) return;
     const OutSpec &o = a.out;
     const int64_t plane = o.plane;
@@ -366,9 +374,13 @@ hipError_t launch_conv_implicit_ksplit(const ImplicitArgs &h, hipStream_t s)
 {
     const int img = std::max(h.images, 1);
     const int64_t outs = int64_t(img) * h.R * h.Wo;
-    const int nbw = int(ksplit_nbw(outs));
+    // tile_m 128: the two waves of a K group split 128 output channels, each
+    // over all of the task's blocks
+    const int cos = h.tile_m == 128 ? 2 : 1;
+    const int nbw = int(ksplit_nbw(outs, cos));
+    const int slots = h.stages == 1 ? 1 : 2;
     if (h.f32 || h.Cin % (kChunkC * kKsGroups) != 0 || h.stride < 1 || h.stride > 2 || h.W < 1 || h.H < 1 ||
-        h.Wo < 1 || h.Ho < 1 || h.R < 1 || outs > kKsplitMaxOuts || h.IW != h.W + 2 * h.pad ||
+        h.Wo < 1 || h.Ho < 1 || h.R < 1 || outs > kKsplitMaxOuts / cos || h.IW != h.W + 2 * h.pad ||
         (h.Wo - 1) * h.stride + h.KW > h.IW || h.IR != img * ((h.R - 1) * h.stride + h.KH) ||
         (img > 1 && h.R != h.Ho) || int64_t(h.Cin) * h.H * h.W >= (int64_t(1) << 31) ||
         !((h.KH == 3 && h.KW == 3) || (h.KH == 1 && h.KW == 1) || (h.KH == 5 && h.KW == 5)))
@@ -386,7 +398,9 @@ hipError_t launch_conv_implicit_ksplit(const ImplicitArgs &h, hipStream_t s)
     a.Wo = h.Wo;
     a.RW = h.R;
     a.row_groups = (h.Ho + h.R - 1) / h.R;
-    a.co_blocks = (h.Cout + 63) / 64;
+    a.co_blocks = (h.Cout + 64 * cos - 1) / (64 * cos);
+    a.co_split = cos;
+    a.slots = slots;
     a.IW = h.IW;
     a.N = h.N;
     a.IMG = img;
@@ -397,7 +411,7 @@ hipError_t launch_conv_implicit_ksplit(const ImplicitArgs &h, hipStream_t s)
     a.ntasks = int(ntasks);
     a.SLmax = h.IR;
     a.slot_halves = int(ksplit_plane(h.IR, h.IW)) * 4 * 8;
-    const int64_t lds = ksplit_lds_bytes(h.IR, h.IW, h.Cin, nbw);
+    const int64_t lds = ksplit_lds_bytes(h.IR, h.IW, h.Cin, nbw, slots);
     if (lds > kImplicitMaxLdsBytes) return hipErrorInvalidValue;
     const int hw = h.H * h.W;
     void *args[] = {&a};

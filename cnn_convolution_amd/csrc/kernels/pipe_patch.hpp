@@ -40,6 +40,10 @@ struct PipeKArgs {
     int IMG;            // 1: tasks of RW output rows of one image; > 1: tasks of
                         // IMG whole images (RW = Ho), their patches stacked
     int stride;
+    int slots;          // split-K kernel: LDS slots per K group (1 or 2)
+    int co_split;       // split-K kernel: 1, the two waves of a K group take
+                        // halves of the task's outputs; 2, one 64-channel half
+                        // each of a task of 128 output channels
 };
 
 // LDS slot of 16-byte granule g (0..3) of 64-byte row q. A 16-byte LDS read

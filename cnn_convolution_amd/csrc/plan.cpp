@@ -623,17 +623,25 @@ static void pick_implicit_pipelined(const conv2d_desc_t &d, int64_t Ho, int64_t 
 
 // Split-K row-block implicit kernel: fp16/bf16, Cin % 128 == 0, stride 1 or
 // 2, 3x3, 5x5 or 1x1, one task per workgroup of RW whole output rows (or of
-// several whole images) x 64 output channels, at most 224 outputs (14
-// blocks of 16), four K groups of two waves splitting the input channels,
-// each wave half of the task's blocks. The task shape minimises the rounds
-// of workgroups over the CUs times the blocks each wave contracts (4 or 7 as
-// compiled), ties to the larger task (each filter fragment read by fewer
-// workgroups). Default for 5x5 filters (measured on the 28x28 5x5 layer:
-// 46.7 us per kernel + 5.3 us filter staging against 59.3 us for the
-// streamed kernel); on the 3x3 layers the staging launch cancels its gain
-// over the pipelined kernels (deep 3x3: 22.6 + 3.1 against 25.3 us), so
-// there it is taken when IM2WIN_IMPLICIT_KERNEL=ksplit. IM2WIN_IMPLICIT_ROWS
-// sets RW and IM2WIN_IMPLICIT_IMAGES the images per task.
+// several whole images), four K groups of two waves splitting the input
+// channels. The two waves of a group either split the task's 16-output
+// blocks (tasks of at most 224 outputs x 64 output channels) or, where
+// patches are large (stride 2), split 128 output channels over tasks of at
+// most 112 outputs (co_split 2, tile_m 128), so each wave keeps a tile of up
+// to 7 blocks. The task shape, split and LDS slots per K group (two, or one
+// where two do not fit) minimise the rounds of workgroups over the CUs times
+// a wave's blocks plus a fixed cost per tap (3 blocks' worth), 15% more for
+// one slot; ties go to the larger task (each filter fragment read by fewer
+// workgroups), then to the split of the task's outputs. Default for 5x5
+// filters (measured on the 28x28 5x5 layer: 46.7 us per kernel + 5.3 us
+// filter staging against 59.3 us for the streamed kernel) and for stride 2
+// (the 28x28 -> 14x14 layer, 512 output channels: 58.1 us + 3.3 us, tasks of
+// 7 rows x 128 output channels with one slot, against 78.4 us for the paired
+// pipelined kernel); on the stride-1 3x3 layers the staging launch cancels
+// its gain over the pipelined kernels (deep 3x3: 22.6 + 3.1 against 25.3
+// us), so there it is taken when IM2WIN_IMPLICIT_KERNEL=ksplit. IM2WIN_IMPLICIT_ROWS
+// sets RW, IM2WIN_IMPLICIT_IMAGES the images per task, IM2WIN_KSPLIT_CO=1|2
+// the split and IM2WIN_KSPLIT_SLOTS=1|2 the slots.
 static void pick_implicit_ksplit(const conv2d_desc_t &d, int64_t Ho, int64_t Wo, conv2d_implicit_plan_t *p,
                                  bool dflt) {
     if (d.dtype == CONV2D_F32 || d.Cin % (32 * kKsplitGroups) != 0 || d.stride > 2 || Wo < 1 || Ho < 1) return;
@@ -644,58 +652,73 @@ static void pick_implicit_ksplit(const conv2d_desc_t &d, int64_t Ho, int64_t Wo,
     } else if (!dflt || std::getenv("IM2WIN_IMPLICIT_TILE")) {
         return;
     }
+    int64_t force_co = 0, force_slots = 0;
+    if (const char *e = std::getenv("IM2WIN_KSPLIT_CO")) force_co = std::atoi(e);
+    if (const char *e = std::getenv("IM2WIN_KSPLIT_SLOTS")) force_slots = std::atoi(e);
     const int64_t s = d.stride, iw = d.W + 2 * d.pad;
-    const int64_t co_blocks = ceil_div(d.Cout, 64);
-    const int64_t sl1 = (Ho - 1) * s + d.KH;             // rows of one whole image
-    int64_t best_rw = 0, best_img = 0;
-    double best_cost = 0.0;
-    auto consider = [&](int64_t rw, int64_t img) {
+    struct Pick { int64_t rw, img, cos, slots; double cost; };
+    Pick best{0, 0, 0, 0, 0.0};
+    auto fits = [&](int64_t rw, int64_t img, int64_t cos, int64_t slots) {
         const int64_t outs = img * rw * Wo;
-        if (outs > kKsplitMaxOuts) return;
+        if (outs > kKsplitMaxOuts / cos || (cos == 2 && d.Cout <= 64)) return false;
         const int64_t sl = img * ((rw - 1) * s + d.KH);
-        const int64_t nbw = ksplit_nbw(outs);
-        if (ksplit_lds_bytes(sl, iw, d.Cin, nbw) > kImplicitMaxLdsBytes) return;
-        const int64_t tasks = img > 1 ? co_blocks * ceil_div(d.N, img) : co_blocks * d.N * ceil_div(Ho, rw);
-        const double cost = double(ceil_div(tasks, 256)) * double(nbw);
-        if (best_rw == 0 || cost < best_cost || (cost == best_cost && outs > best_img * best_rw * Wo)) {
-            best_rw = rw;
-            best_img = img;
-            best_cost = cost;
+        return ksplit_lds_bytes(sl, iw, d.Cin, ksplit_nbw(outs, cos), slots) <= kImplicitMaxLdsBytes;
+    };
+    auto consider = [&](int64_t rw, int64_t img) {
+        for (int64_t cos = 1; cos <= 2; ++cos) {
+            if (force_co && cos != force_co) continue;
+            for (int64_t slots = 2; slots >= 1; --slots) {
+                if ((force_slots && slots != force_slots) || !fits(rw, img, cos, slots)) continue;
+                const int64_t outs = img * rw * Wo;
+                const int64_t nbt = ceil_div(outs, 16);
+                const int64_t per_wave = cos == 2 ? nbt : ceil_div(nbt, 2);
+                const int64_t co_blocks = ceil_div(d.Cout, 64 * cos);
+                const int64_t tasks = img > 1 ? co_blocks * ceil_div(d.N, img) : co_blocks * d.N * ceil_div(Ho, rw);
+                const double cost = double(ceil_div(tasks, 256)) * double(per_wave + 3) * (slots == 1 ? 1.15 : 1.0);
+                const int64_t bouts = best.img * best.rw * Wo;
+                const bool tie = best.rw != 0 && cost == best.cost;
+                if (best.rw == 0 || cost < best.cost ||
+                    (tie && (cos < best.cos || (cos == best.cos && outs > bouts))))
+                    best = Pick{rw, img, cos, slots, cost};
+                break;                             // two slots where they fit
+            }
         }
     };
     for (int64_t rw = 1; rw <= Ho; ++rw) consider(ceil_div(Ho, ceil_div(Ho, rw)), 1);
     for (int64_t img = 2; img <= d.N && img * Ho * Wo <= kKsplitMaxOuts; ++img) consider(Ho, img);
-    (void)sl1;
     if (const char *e = std::getenv("IM2WIN_IMPLICIT_IMAGES")) {
         const int64_t v = std::atoi(e);
-        if (v >= 2 && v <= d.N && v * Ho * Wo <= kKsplitMaxOuts &&
-            ksplit_lds_bytes(v * sl1, iw, d.Cin, ksplit_nbw(v * Ho * Wo)) <= kImplicitMaxLdsBytes) {
-            best_img = v;
-            best_rw = Ho;
+        if (v >= 2 && v <= d.N) {
+            const Pick keep = best;
+            best = Pick{0, 0, 0, 0, 0.0};
+            consider(Ho, v);
+            if (best.rw == 0) best = keep;
         }
     }
     if (const char *e = std::getenv("IM2WIN_IMPLICIT_ROWS")) {
         const int64_t v = std::min<int64_t>(std::atoi(e), Ho);
-        if (v >= 1 && v * Wo <= kKsplitMaxOuts &&
-            ksplit_lds_bytes((v - 1) * s + d.KH, iw, d.Cin, ksplit_nbw(v * Wo)) <= kImplicitMaxLdsBytes) {
-            best_rw = v;
-            best_img = 1;
+        if (v >= 1) {
+            const Pick keep = best;
+            best = Pick{0, 0, 0, 0, 0.0};
+            consider(v, 1);
+            if (best.rw == 0) best = keep;
         }
     }
-    if (best_rw == 0) return;
-    const int64_t outs = best_img * best_rw * Wo;
+    if (best.rw == 0) return;
+    const int64_t outs = best.img * best.rw * Wo;
+    const int64_t co_blocks = ceil_div(d.Cout, 64 * best.cos);
     p->kernel = 5;
-    p->tile_m = 64;
-    p->tile_n = int32_t(ksplit_nbw(outs) * 16);
+    p->tile_m = int32_t(64 * best.cos);
+    p->tile_n = int32_t(ksplit_nbw(outs, best.cos) * 16);
     p->wave_m = int32_t(kKsplitGroups);
-    p->rows_per_tile = int32_t(best_rw);
+    p->rows_per_tile = int32_t(best.rw);
     p->cols_per_tile = int32_t(Wo);
-    p->patch_rows = int32_t(best_img * ((best_rw - 1) * s + d.KH));
+    p->patch_rows = int32_t(best.img * ((best.rw - 1) * s + d.KH));
     p->patch_cols = int32_t(iw);
-    p->stages = 0;
-    p->images = int32_t(best_img);
-    p->lds_bytes = ksplit_lds_bytes(p->patch_rows, iw, d.Cin, ksplit_nbw(outs));
-    p->tiles = best_img > 1 ? co_blocks * ceil_div(d.N, best_img) : co_blocks * d.N * ceil_div(Ho, best_rw);
+    p->stages = int32_t(best.slots);
+    p->images = int32_t(best.img);
+    p->lds_bytes = ksplit_lds_bytes(p->patch_rows, iw, d.Cin, ksplit_nbw(outs, best.cos), best.slots);
+    p->tiles = best.img > 1 ? co_blocks * ceil_div(d.N, best.img) : co_blocks * d.N * ceil_div(Ho, best.rw);
     p->ws_bytes = round_up(ksplit_stage_bytes(d.Cout, d.Cin, d.KH * d.KW), 256);
 }
 
@@ -870,7 +893,7 @@ static conv2d_status_t compute_implicit_plan(const conv2d_desc_t &d, conv2d_impl
     // pipelined forms take the 3x3 and 1x1 layers of stride 1 or 2
     const bool one_block = p->kernel == 2 && d.Cin == 64 && d.W % 8 == 0;
     pick_implicit_pipelined(d, Ho, Wo, p, !one_block);
-    pick_implicit_ksplit(d, Ho, Wo, p, d.KH * d.KW >= 25);
+    pick_implicit_ksplit(d, Ho, Wo, p, d.KH * d.KW >= 25 || d.stride == 2);
     return CONV2D_OK;
 }
 

@@ -57,12 +57,16 @@ constexpr int64_t kKsplitGroups = 4;
 constexpr int64_t kKsplitMaxOuts = 14 * 16;    // two waves of at most 7 blocks
 // positions per granule plane of a slot: sl * iw rounded up to 1 modulo 8
 inline int64_t ksplit_plane(int64_t sl, int64_t iw) { return ((sl * iw + 6) / 8) * 8 + 1; }
-inline int64_t ksplit_lds_bytes(int64_t sl, int64_t iw, int64_t cin, int64_t nbw) {
-    const int64_t spw = cin / (32 * kKsplitGroups) > 1 ? 2 : 1;
+inline int64_t ksplit_lds_bytes(int64_t sl, int64_t iw, int64_t cin, int64_t nbw, int64_t slots = 2) {
+    const int64_t spw = cin / (32 * kKsplitGroups) > 1 ? slots : 1;
     return std::max<int64_t>(kKsplitGroups * spw * ksplit_plane(sl, iw) * 64, 12 * nbw * 1024);
 }
-// blocks per wave as compiled: 4 (tasks of at most 128 outputs) or 7
-inline int64_t ksplit_nbw(int64_t outs) { return outs <= 8 * 16 ? 4 : 7; }
+// blocks per wave as compiled, 4 or 7: the two waves of a K group split a
+// task of at most 128 (or 224) outputs (co_split 1), or each takes all of a
+// task of at most 64 (or 112) outputs (co_split 2)
+inline int64_t ksplit_nbw(int64_t outs, int64_t co_split = 1) {
+    return outs <= (co_split == 2 ? 4 : 8) * 16 ? 4 : 7;
+}
 // the filter staged in fragment order: 64-row output-channel blocks x Cin x taps
 inline int64_t ksplit_stage_bytes(int64_t cout, int64_t cin, int64_t taps) {
     return ((cout + 63) / 64) * 64 * cin * taps * 2;

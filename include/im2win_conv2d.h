@@ -296,13 +296,16 @@ typedef struct {
                                      `images` whole images) x 64 output channels
                                      over 32-channel K chunks double-buffered in
                                      LDS, w as stored (ws_bytes 0); 5 (default
-                                     for 5x5 filters with Cin % 128 == 0, else
-                                     by name): split-K row-block, tasks of
-                                     rows_per_tile whole output rows (or of
-                                     `images` whole images, at most 224
-                                     outputs) x 64 output channels, four K
-                                     groups of two waves splitting the input
-                                     channels, the filter staged in the
+                                     for 5x5 filters and stride 2 with Cin %
+                                     128 == 0, else by name): split-K
+                                     row-block, tasks of rows_per_tile whole
+                                     output rows (or of `images` whole images)
+                                     x tile_m output channels, four K groups of
+                                     two waves splitting the input channels
+                                     (tile_m 64: the two waves split the task's
+                                     outputs, at most 224; tile_m 128: they
+                                     take 64 channels each, at most 112
+                                     outputs), the filter staged in the
                                      workspace in fragment order
                                      (IM2WIN_LAYOUT_FRAG)                           */
     int32_t stages;               /* kernel 0: filter K stages in flight + 1 (LDS
@@ -310,7 +313,9 @@ typedef struct {
                                      position; kernel 4: 2 = persistent workgroups
                                      (tiles of them) with loading and computing
                                      waves, 1 = one task per workgroup (tiles
-                                     tasks), two workgroups per CU; 0 otherwise    */
+                                     tasks), two workgroups per CU; kernel 5: LDS
+                                     slots per K group (2, or 1 where two do not
+                                     fit); 0 otherwise                              */
     int32_t images;               /* kernels 4, 5: whole images per task when > 1 (then
                                      rows_per_tile = Ho and patch_rows = images *
                                      (Ho + KH - 1)); 1 otherwise, 0 for the other

@@ -75,6 +75,47 @@ def test_ksplit_kernel_matches_oracle(shape, dt, rw, monkeypatch):
     check(got, x, w, s, p, dt)
 
 
+# the two waves of a K group on 64 output channels each (tasks of 128 output
+# channels, at most 112 outputs), and one LDS slot per K group (the chunk
+# written after every wave has read the previous one)
+KS_MODE_SHAPES = [
+    (2, 256, 14, 14, 200, 3, 3, 1, 1),   # Cout past one 128-block: the last half lies past Cout
+    (2, 256, 28, 28, 130, 3, 3, 2, 1),   # stride 2 (the planned split there), Cout ragged
+    (1, 384, 9, 13, 72, 3, 3, 1, 0),     # three chunks per K group, odd planes
+    (3, 128, 12, 20, 256, 1, 1, 2, 0),   # 1x1 stride 2
+    (2, 128, 12, 12, 192, 5, 5, 1, 2),   # 5x5
+]
+KS_MODE_CASES = [(s, dt, co, sl) for dt in ("f16", "bf16") for s in KS_MODE_SHAPES
+                 for co, sl in ((2, None), (2, 1), (1, 1))]
+
+
+@pytest.mark.parametrize("shape,dt,co,slots", KS_MODE_CASES,
+                         ids=[f"{dt}-{s}-co{co}-s{sl}" for s, dt, co, sl in KS_MODE_CASES])
+@pytest.mark.parametrize("rw", [None, 2])
+def test_ksplit_kernel_channel_split_and_one_slot(shape, dt, co, slots, rw, monkeypatch):
+    N, Cin, H, W, Cout, KH, KW, s, p = shape
+    monkeypatch.setenv("IM2WIN_IMPLICIT_KERNEL", "ksplit")
+    monkeypatch.setenv("IM2WIN_KSPLIT_CO", str(co))
+    if slots is not None:
+        monkeypatch.setenv("IM2WIN_KSPLIT_SLOTS", str(slots))
+    if rw is not None:
+        monkeypatch.setenv("IM2WIN_IMPLICIT_ROWS", str(rw))
+    pl = conv.implicit_plan(conv.make_desc(*shape, CODE[dt]))
+    assert pl.kernel == 5 and pl.tile_m == 64 * co
+    if slots is not None:
+        assert pl.stages == slots
+    _say(f"implicit-ksplit {dt} {shape} co_split={co} slots={pl.stages} rows/task={pl.rows_per_tile} "
+         f"workgroups={pl.tiles} lds={pl.lds_bytes}")
+    x, w = workloads.make_inputs(N, Cin, H, W, Cout, KH, KW, seed=48, dtype=dt)
+    got = run_conv(x, w, s, p)
+    check(got, x, w, s, p, dt)
+    if dt == "f16" and rw is None:
+        xi, wi = workloads.make_inputs(N, Cin, H, W, Cout, KH, KW, seed=49, dtype="f16",
+                                       x_dist="int3", w_dist="int3")
+        got = run_conv(xi, wi, s, p)
+        assert np.array_equal(got.numpy().astype(np.float64), oracle.conv2d(xi, wi, s, p))
+
+
 @pytest.mark.parametrize("shape", KS_SHAPES[:8], ids=[str(s) for s in KS_SHAPES[:8]])
 def test_ksplit_kernel_integer_inputs_exact(shape, monkeypatch):
     N, Cin, H, W, Cout, KH, KW, s, p = shape
@@ -105,9 +146,9 @@ def test_ksplit_kernel_whole_image_tasks(shape, dt, images, monkeypatch):
     pl = conv.implicit_plan(conv.make_desc(*shape, CODE[dt]))
     assert pl.kernel == 5
     sl = images * ((pl.Ho - 1) * s + KH)
-    slots = 4 * (2 if Cin // 128 > 1 else 1)
-    nbw = 7 if images * pl.Ho * pl.Wo <= 112 else 13
-    fits = max(slots * sl * (W + 2 * p) * 64, 12 * nbw * 1024) <= 160 * 1024
+    nbw = 4 if images * pl.Ho * pl.Wo <= 128 else 7
+    plane = ((sl * (W + 2 * p) + 6) // 8) * 8 + 1          # positions per granule plane, 1 mod 8
+    fits = max(4 * plane * 64, 12 * nbw * 1024) <= 160 * 1024    # one LDS slot per K group at least
     if images * pl.Ho * pl.Wo <= 208 and images <= N and fits:
         assert pl.images == images and pl.rows_per_tile == pl.Ho and pl.patch_rows == sl
     else:

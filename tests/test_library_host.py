@@ -464,8 +464,11 @@ def test_pipelined_plan_geometry(monkeypatch):
                 assert pl.kernel == 2, (N, Cin, H, W, Cout, KH, KW, s, p)
                 continue
             if pl.kernel != 4:
-                # only where a pipelined form does not apply, or its LDS does not fit
-                assert not pipelined or pl.lds_bytes == 0 or form, (N, Cin, H, W, Cout, KH, KW, s, p)
+                # only where a pipelined form does not apply, or its LDS does not
+                # fit, or (by default) the split-K kernel takes the layer: stride
+                # 2 with Cin a multiple of 128
+                splitk = form is None and s == 2 and Cin % 128 == 0 and pl.kernel == 5
+                assert not pipelined or pl.lds_bytes == 0 or form or splitk, (N, Cin, H, W, Cout, KH, KW, s, p)
                 continue
             assert pipelined
             seen[pl.stages] += 1
@@ -665,11 +668,17 @@ def test_ksplit_plan_geometry(monkeypatch):
     assert five.lds_bytes <= 160 * 1024 and five.wave_m == 4
     assert conv.plan(conv.make_desc(64, 128, 28, 28, 128, 5, 5, 1, 2, conv.F16)).ws_bytes == five.ws_bytes
     for shape in [(64, 256, 14, 14, 256, 3, 3, 1, 1), (64, 512, 7, 7, 512, 3, 3, 1, 1),
-                  (2, 64, 28, 28, 64, 5, 5, 1, 2)]:          # 3x3 layers, and Cin % 128 != 0
+                  (2, 64, 28, 28, 64, 5, 5, 1, 2)]:          # stride-1 3x3 layers, and Cin % 128 != 0
         assert conv.implicit_plan(conv.make_desc(*shape, conv.F16)).kernel != 5, shape
+    # stride 2: 7-row tasks of 128 output channels (the two waves of a K group
+    # on 64 channels each), one LDS slot per K group (two do not fit)
+    s2 = conv.implicit_plan(conv.make_desc(64, 256, 28, 28, 512, 3, 3, 2, 1, conv.F16))
+    assert (s2.kernel, s2.tile_m, s2.stages, s2.rows_per_tile, s2.images) == (5, 128, 1, 7, 1)
+    assert s2.tiles == 4 * 64 * 2 and s2.lds_bytes <= 160 * 1024
     monkeypatch.setenv("IM2WIN_IMPLICIT_KERNEL", "ksplit")
     deep = conv.implicit_plan(conv.make_desc(64, 256, 14, 14, 256, 3, 3, 1, 1, conv.BF16))
     assert (deep.kernel, deep.rows_per_tile, deep.images, deep.tiles) == (5, 14, 1, 256)
+    assert (deep.tile_m, deep.stages) == (64, 2)
     assert deep.ws_bytes == 256 * 256 * 9 * 2 and deep.patch_rows == 16 and deep.patch_cols == 16
     m512 = conv.implicit_plan(conv.make_desc(64, 512, 7, 7, 512, 3, 3, 1, 1, conv.F16))
     assert (m512.kernel, m512.images, m512.rows_per_tile, m512.tiles) == (5, 2, 7, 8 * 32)
