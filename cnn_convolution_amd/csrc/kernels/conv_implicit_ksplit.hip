@@ -64,44 +64,58 @@ __device__ __forceinline__ const uint4 *ks_frag(const uint16_t *wf, int nch, int
     return reinterpret_cast<const uint4 *>(wf) + ((int64_t(cb) * nch + blk) * taps + t) * (4 * 64);
 }
 
-// one thread per (output channel, 8 input channels): the 8 x TAPS halves of
-// w[co][ci0 .. ci0+7][taps] as stored (one contiguous run) into the lane slot
-// of each tap's fragment
+// One workgroup per (cb, blk, c4): the 16 output channels cb*64 + c4*16 ..
+// +15 each hold their 32 input channels blk*32 .. +31 over all taps as one
+// contiguous run of 64*TAPS bytes of w. The workgroup copies the 16 runs into
+// LDS with 16-byte loads (consecutive lanes on consecutive bytes of a run),
+// then writes the TAPS fragments (cb, blk, t, c4), each 1 KB contiguous, one
+// 16-byte lane slot per thread: lane l's 8 halves are channels (l >> 4)*8 ..
+// +7 of output channel l & 15 at tap t, gathered from LDS 2 bytes at a time.
+// Output channels past Cout are written as zeros.
+constexpr int kStageThreads = 256;
 template <int TAPS>
-__global__ __launch_bounds__(256) void ks_stage_kernel(const uint16_t *__restrict__ w, uint4 *__restrict__ wf,
-                                                      int Cout, int Cin, int64_t threads)
+__global__ __launch_bounds__(kStageThreads) void ks_stage_kernel(const uint16_t *__restrict__ w,
+                                                                uint4 *__restrict__ wf, int Cout, int Cin)
 {
-    const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
-    if (i >= threads) return;
+    constexpr int RUN = kChunkC * TAPS;              // halves of one output channel's run
+    constexpr int RUNV = RUN / 8;                    // 16-byte vectors of a run (4 * TAPS)
+    __shared__ uint4 runs[16 * RUNV];
     const int nch = Cin / kChunkC;
-    const int lane = int(i & 63), c4 = int((i >> 6) & 3);
-    const int64_t r = i >> 8;
-    const int blk = int(r % nch);
-    const int cb = int(r / nch);
-    const int co = cb * 64 + c4 * 16 + (lane & 15);
-    const int ci0 = blk * kChunkC + (lane >> 4) * 8;
-    uint32_t h[8 * TAPS];
-    if (co < Cout) {
-        const uint4 *src = reinterpret_cast<const uint4 *>(w + (int64_t(co) * Cin + ci0) * TAPS);
+    const int c4 = blockIdx.x & 3;
+    const int r = blockIdx.x >> 2;
+    const int blk = r % nch;
+    const int cb = r / nch;
+    const int co0 = cb * 64 + c4 * 16;
+    // every load of the thread in flight before the first LDS write
+    constexpr int PER = (16 * RUNV + kStageThreads - 1) / kStageThreads;
+    uint4 v4[PER];
 #pragma unroll
-        for (int k = 0; k < TAPS; ++k) {
-            const uint4 v = src[k];
-            h[8 * k + 0] = v.x & 0xffffu; h[8 * k + 1] = v.x >> 16;
-            h[8 * k + 2] = v.y & 0xffffu; h[8 * k + 3] = v.y >> 16;
-            h[8 * k + 4] = v.z & 0xffffu; h[8 * k + 5] = v.z >> 16;
-            h[8 * k + 6] = v.w & 0xffffu; h[8 * k + 7] = v.w >> 16;
-        }
-    } else {
-#pragma unroll
-        for (int k = 0; k < 8 * TAPS; ++k) h[k] = 0u;
+    for (int j = 0; j < PER; ++j) {
+        const int v = threadIdx.x + j * kStageThreads;
+        const int col = v / RUNV;                    // output channel of the block
+        const int k = v - col * RUNV;
+        const int co = co0 + col;
+        v4[j] = v < 16 * RUNV && co < Cout
+                    ? reinterpret_cast<const uint4 *>(w + (int64_t(co) * Cin + blk * kChunkC) * TAPS)[k]
+                    : uint4{0u, 0u, 0u, 0u};
     }
-    // element (channel e, tap t) is half e * TAPS + t of the run
-    uint4 *dst = wf + ((int64_t(cb) * nch + blk) * TAPS * 4 + c4) * 64 + lane;
 #pragma unroll
-    for (int t = 0; t < TAPS; ++t)
-        dst[int64_t(t) * 4 * 64] = uint4{h[t] | (h[TAPS + t] << 16), h[2 * TAPS + t] | (h[3 * TAPS + t] << 16),
-                                         h[4 * TAPS + t] | (h[5 * TAPS + t] << 16),
-                                         h[6 * TAPS + t] | (h[7 * TAPS + t] << 16)};
+    for (int j = 0; j < PER; ++j) {
+        const int v = threadIdx.x + j * kStageThreads;
+        if (v < 16 * RUNV) runs[v] = v4[j];
+    }
+    __syncthreads();
+    const uint16_t *h = reinterpret_cast<const uint16_t *>(runs);
+    uint4 *const dst = wf + ((int64_t(cb) * nch + blk) * TAPS * 4 + c4) * 64;
+    for (int o = threadIdx.x; o < TAPS * 64; o += kStageThreads) {
+        const int t = o >> 6, lane = o & 63;
+        // channel e of the lane's 8 at tap t: half ((lane >> 4)*8 + e)*TAPS + t of run lane & 15
+        const uint16_t *src = h + (lane & 15) * RUN + ((lane >> 4) * 8) * TAPS + t;
+        uint32_t d[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) d[e] = uint32_t(src[(2 * e) * TAPS]) | (uint32_t(src[(2 * e + 1) * TAPS]) << 16);
+        dst[int64_t(t) * 4 * 64 + lane] = uint4{d[0], d[1], d[2], d[3]};
+    }
 }
 
 // The slots hold a patch granule-major: the 8 channels of granule g (0..3) at
@@ -362,12 +376,14 @@ __global__ __launch_bounds__(kKsThreads) __attribute__((amdgpu_waves_per_eu(2, 2
 hipError_t launch_ksplit_stage(const void *w, void *wf, int Cout, int Cin, int taps, hipStream_t s)
 {
     if (Cin % kChunkC != 0 || Cout < 1 || !(taps == 1 || taps == 9 || taps == 25)) return hipErrorInvalidValue;
-    const int64_t threads = ksplit_stage_bytes(Cout, Cin, taps) / (16 * taps);
-    void *args[] = {&w, &wf, &Cout, &Cin, const_cast<int64_t *>(&threads)};
+    // one workgroup per 1 KB x taps fragment group (cb, blk, c4)
+    const int64_t groups = ksplit_stage_bytes(Cout, Cin, taps) / (1024 * int64_t(taps));
+    if (groups > 0x7fffffff) return hipErrorInvalidValue;
+    void *args[] = {&w, &wf, &Cout, &Cin};
     const void *k = taps == 9    ? reinterpret_cast<const void *>(ks_stage_kernel<9>)
                     : taps == 25 ? reinterpret_cast<const void *>(ks_stage_kernel<25>)
                                  : reinterpret_cast<const void *>(ks_stage_kernel<1>);
-    return hipLaunchKernel(k, dim3(unsigned((threads + 255) / 256)), dim3(256), args, 0, s);
+    return hipLaunchKernel(k, dim3(unsigned(groups)), dim3(kStageThreads), args, 0, s);
 }
 
 hipError_t launch_conv_implicit_ksplit(const ImplicitArgs &h, hipStream_t s)

@@ -250,3 +250,34 @@ def test_ksplit_kernel_alone_with_filter_staged_once(monkeypatch):
     torch.cuda.synchronize()
     assert torch.equal(ys[0], ref) and torch.equal(ys[1], ref)
     check(ys[0], x, w, s, p, "bf16")
+
+
+FRAG_SHAPES = [
+    # Cout, Cin, taps: rows past Cout, one and several chunks and blocks
+    (72, 64, 9),
+    (40, 128, 25),
+    (130, 96, 1),
+    (512, 512, 9),
+]
+
+
+@pytest.mark.parametrize("shape", FRAG_SHAPES, ids=[str(s) for s in FRAG_SHAPES])
+def test_fragment_order_staging_layout(shape):
+    """The staged filter holds, for fragment (cb, blk, t, c4) and lane l, the
+    8 halves w[cb*64 + c4*16 + l % 16][blk*32 + (l // 16)*8 + e][t], e = 0..7,
+    and zeros for output channels past Cout: byte for byte against the same
+    layout built with numpy indexing."""
+    Cout, Cin, taps = shape
+    k = {1: 1, 9: 3, 25: 5}[taps]
+    g = torch.Generator().manual_seed(Cout * 1000 + Cin + taps)
+    w = torch.randint(-30000, 30000, (Cout, Cin, k, k), generator=g, dtype=torch.int16).view(torch.float16)
+    wst, geo = conv.weight_stage(w.to(DEV), 1, k // 2, (8, 8), conv.LAYOUT_FRAG)
+    torch.cuda.synchronize()
+    got = wst.cpu().view(torch.int16).numpy().reshape(-1)
+    cbs, nch = (Cout + 63) // 64, Cin // 32
+    wn = np.zeros((cbs * 64, Cin, taps), np.int16)
+    wn[:Cout] = w.view(torch.int16).numpy().reshape(Cout, Cin, taps)
+    # [cb][c4][col][blk][grp][e][t] -> [cb][blk][t][c4][grp][col][e]
+    exp = wn.reshape(cbs, 4, 16, nch, 4, 8, taps).transpose(0, 3, 6, 1, 4, 2, 5).reshape(-1)
+    assert got.shape == exp.shape
+    assert np.array_equal(got, exp)
