@@ -57,6 +57,7 @@ struct NarrowKArgs {
     int L, Lp;              // window row elements W_win*KH*CP, and per row in LDS (with slack)
     int R, row_groups, co_blocks;
     int groups;             // workgroups per 64-channel block (gridDim.x / co_blocks)
+    int rowvec;             // fp16/bf16, CP 4, W % 4 == 0: window rows from whole input rows
 };
 
 // One 16-byte vector of the filter block, gathered from w as stored: vector
@@ -292,6 +293,134 @@ __device__ __forceinline__ void load_block(const NarrowKArgs &a, const T *ximg, 
     }
 }
 
+// Window rows from whole input rows (fp16/bf16, CP = 4, W % 4 == 0, x 8-byte
+// aligned): unit (input row r of the block, 4-column group g) reads the 4
+// columns 4g .. 4g+3 of each channel (one 8-byte load per channel,
+// consecutive lanes on consecutive groups), turns them in registers into 4
+// positions of 4 channels, and writes each position into every window row
+// (i, kh) that interleaves this input row (kh = r - i * stride), so that an
+// input element is read once per row block rather than once per window row
+// holding it (7x7 stride 2, 4 output rows: 13 input rows against 28 window
+// row segments), with a quarter of the load instructions. The window's
+// padding columns (wc < pad, wc >= pad + W) are zeroed apart.
+constexpr int kRowVecUnits = 2;                      // units per thread per round
+
+struct RowRegs {
+    uint2 v[kRowVecUnits][4];
+};
+
+__device__ __forceinline__ void fetch_rows(const NarrowKArgs &a, const uint16_t *ximg, int ho0, int rw, int u0,
+                                           int tid, RowRegs &q)
+{
+    const int G4 = a.W >> 2;
+    const int units = ((rw - 1) * a.stride + a.KH) * G4;
+    const int HW = a.H * a.W;
+#pragma unroll
+    for (int j = 0; j < kRowVecUnits; ++j) {
+        const int u = min(u0 + tid + j * kNarrowThreads, units - 1);
+        const int r = u / G4;
+        const int g = u - r * G4;
+        const int ih = ho0 * a.stride - a.pad + r;
+        const int src = (unsigned(ih) < unsigned(a.H) ? ih * a.W : 0) + 4 * g;   // every load in bounds
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            q.v[j][c] = *reinterpret_cast<const uint2 *>(ximg + min(c, a.Cin - 1) * HW + src);
+    }
+}
+
+__device__ __forceinline__ void put_rows(const NarrowKArgs &a, uint16_t *win, int ho0, int rw, int u0, int tid,
+                                         const RowRegs &q)
+{
+    const int G4 = a.W >> 2;
+    const int units = ((rw - 1) * a.stride + a.KH) * G4;
+#pragma unroll
+    for (int j = 0; j < kRowVecUnits; ++j) {
+        const int u = u0 + tid + j * kNarrowThreads;
+        if (u >= units) break;
+        const int r = u / G4;
+        const int g = u - r * G4;
+        const int ih = ho0 * a.stride - a.pad + r;
+        const bool in = unsigned(ih) < unsigned(a.H);
+        uint2 v[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) v[c] = (in && c < a.Cin) ? q.v[j][c] : uint2{0u, 0u};
+        // position p (column 4g + p): channel c's half p of its 4 columns
+        uint2 pos[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const uint32_t sel = (p & 1) ? 0x07060302u : 0x05040100u;
+            const uint32_t d0 = p < 2 ? v[0].x : v[0].y, d1 = p < 2 ? v[1].x : v[1].y;
+            const uint32_t d2 = p < 2 ? v[2].x : v[2].y, d3 = p < 2 ? v[3].x : v[3].y;
+            pos[p] = uint2{__builtin_amdgcn_perm(d1, d0, sel), __builtin_amdgcn_perm(d3, d2, sel)};
+        }
+        // window rows i with 0 <= r - i * stride < KH
+        const int num = r - a.KH + 1;
+        const int i_lo = num > 0 ? (num + a.stride - 1) / a.stride : 0;
+        const int i_hi = min(rw - 1, r / a.stride);
+        for (int i = i_lo; i <= i_hi; ++i) {
+            const int kh = r - i * a.stride;
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const int wc = 4 * g + p + a.pad;
+                if (wc < a.Wwin) *reinterpret_cast<uint2 *>(win + i * a.Lp + (wc * a.KH + kh) * 4) = pos[p];
+            }
+        }
+    }
+}
+
+// zero the padding columns of the rw window rows, and the slack after each
+__device__ __forceinline__ void zero_row_pads(const NarrowKArgs &a, uint16_t *win, int rw, int tid)
+{
+    const int right = max(0, a.Wwin - a.pad - a.W);
+    const int npad = a.pad + right;
+    const int n = rw * a.KH * npad;
+    for (int v = tid; v < n; v += kNarrowThreads) {
+        const int ik = v / npad;
+        const int col = v - ik * npad;
+        const int i = ik / a.KH;
+        const int kh = ik - i * a.KH;
+        const int wc = col < a.pad ? col : a.pad + a.W + (col - a.pad);
+        *reinterpret_cast<uint2 *>(win + i * a.Lp + (wc * a.KH + kh) * 4) = uint2{0u, 0u};
+    }
+    const int slack = a.Lp - a.L;
+    for (int v = tid; v < rw * slack; v += kNarrowThreads) {
+        const int i = v / slack;
+        win[i * a.Lp + a.L + (v - i * slack)] = 0;
+    }
+}
+
+// One row block per workgroup from whole input rows: the filter block's
+// vectors and a round of row units in flight together, then written.
+template <bool GATHER, int FB>
+__device__ __forceinline__ void load_block_rows(const NarrowKArgs &a, const uint16_t *ximg, const uint16_t *w,
+                                                uint16_t *fl, uint16_t *win, int FS, int cb, int ho0, int rw,
+                                                int tid)
+{
+    constexpr int V = 8;
+    const int fv_row = a.Kp / V;
+    const int fvec = 64 * fv_row;
+    const int units = ((rw - 1) * a.stride + a.KH) * (a.W >> 2);
+    constexpr int UR = kRowVecUnits * kNarrowThreads;
+    for (int f0 = 0, u0 = 0; f0 < fvec || u0 < units; f0 += FB * kNarrowThreads, u0 += UR) {
+        uint4 fv[FB];
+#pragma unroll
+        for (int j = 0; j < FB; ++j)
+            fv[j] = filter_vec<4, GATHER>(a, w, cb, min(f0 + tid + j * kNarrowThreads, fvec - 1));
+        RowRegs q;
+        if (u0 < units) fetch_rows(a, ximg, ho0, rw, u0, tid, q);
+#pragma unroll
+        for (int j = 0; j < FB; ++j) {
+            const int v = f0 + tid + j * kNarrowThreads;
+            if (v < fvec) {
+                const int r = v / fv_row;
+                *reinterpret_cast<uint4 *>(fl + r * FS + (v - r * fv_row) * V) = fv[j];
+            }
+        }
+        if (u0 < units) put_rows(a, win, ho0, rw, u0, tid, q);
+    }
+    zero_row_pads(a, win, rw, tid);
+}
+
 // this workgroup's row blocks [t_begin, t_end): image and first output row
 __device__ __forceinline__ void task_rows(const NarrowKArgs &a, int t, int &n, int &ho0, int &rw)
 {
@@ -374,7 +503,10 @@ __global__ __launch_bounds__(kNarrowThreads) void conv_implicit_narrow_kernel(co
         // one row block: filter and window loads in one round trip
         int n, ho0, rw;
         task_rows(a, t_begin, n, ho0, rw);
-        load_block<CP, GATHER, 4, UB>(a, x + n * img, wsrc, fl, win, FS, cb, ho0, rw, tid);
+        if (CP == 4 && a.rowvec)
+            load_block_rows<GATHER, 4>(a, x + n * img, wsrc, fl, win, FS, cb, ho0, rw, tid);
+        else
+            load_block<CP, GATHER, 4, UB>(a, x + n * img, wsrc, fl, win, FS, cb, ho0, rw, tid);
         __syncthreads();
         run_block(n, ho0, rw);
     } else {
@@ -546,6 +678,7 @@ hipError_t launch_conv_implicit_narrow(const ImplicitArgs &h, hipStream_t s)
     a.R = h.R;
     a.row_groups = (h.Ho + h.R - 1) / h.R;
     a.co_blocks = (h.Cout + 63) / 64;
+    a.rowvec = !h.f32 && cp == 4 && h.W % 4 == 0 && (reinterpret_cast<uintptr_t>(h.x) & 7) == 0;
     // the kernel's assumptions: CP channels hold Cin, every window start is a
     // whole 16-byte vector, the outputs of a block fit 32 MFMA blocks, and
     // element offsets of the image fit 32 bits

@@ -437,6 +437,37 @@ def test_narrow_kernel_leaves_memory_past_y_untouched(dt):
     check(host[:n_out], x, w, s, p, dt)
 
 
+# half precision with 4 channels per position on rows of 4k elements: window
+# rows written from whole input rows (each input row into every window row
+# that interleaves it), padding columns zeroed apart
+NARROW_ROWVEC = [
+    (2, 3, 28, 32, 64, 7, 7, 2, 3),      # the stem's geometry: 3 zero columns left, 2 right
+    (1, 4, 12, 16, 24, 5, 5, 2, 0),      # four real channels; input column 15 in no window
+    (2, 2, 9, 8, 16, 3, 3, 2, 2),        # two channels, rows above and below the image
+    (3, 1, 10, 12, 8, 1, 1, 2, 0),       # 1x1 stride 2: every other input row unused
+    (1, 3, 9, 1000, 8, 9, 9, 2, 0),      # 9 x 250 row units: three rounds per thread
+    (20, 3, 64, 64, 64, 7, 7, 2, 3),     # more than 256 workgroups: the staged filter
+]
+
+
+@pytest.mark.parametrize("shape", NARROW_ROWVEC, ids=[str(s) for s in NARROW_ROWVEC])
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+@pytest.mark.parametrize("rows", [None, 2, 3])
+def test_narrow_kernel_from_whole_input_rows(shape, dt, rows, monkeypatch):
+    N, Cin, H, W, Cout, KH, KW, s, p = shape
+    if rows is not None:
+        monkeypatch.setenv("IM2WIN_IMPLICIT_ROWS", str(rows))
+    pl = conv.implicit_plan(conv.make_desc(*shape, CODE[dt]))
+    assert pl.kernel == 3 and pl.stages == 4 and W % 4 == 0
+    _say(f"implicit-narrow rows {dt} {shape} rows/block={pl.rows_per_tile} workgroups={pl.tiles}")
+    x, w = workloads.make_inputs(N, Cin, H, W, Cout, KH, KW, seed=35, dtype=dt, w_dist="normal")
+    got = run_implicit(x, w, s, p)
+    ref = oracle.conv2d(x, w, s, p)
+    check(got, x, w, s, p, dt, ref=ref)
+    xi, wi = workloads.make_inputs(N, Cin, H, W, Cout, KH, KW, seed=36, dtype=dt, x_dist="int3", w_dist="int3")
+    assert np.array_equal(run_implicit(xi, wi, s, p).numpy().astype(np.float64), oracle.conv2d(xi, wi, s, p))
+
+
 # the narrow kernel's two launch forms and its multi-round window loads:
 # persistent workgroups (fp32, or filter blocks over 48 KB) walking several
 # row blocks with the next block's gathers prefetched, and window rows whose
