@@ -591,8 +591,13 @@ __global__ __launch_bounds__(kNarrowThreads) void conv_implicit_narrow_f32_kerne
                 if (s < nb) af[s] = *reinterpret_cast<const floatx4_t *>(win + abase[s] + sl * 16);
 #pragma unroll
             for (int c = 0; c < 4; ++c) bf[c] = *reinterpret_cast<const floatx4_t *>(fl + bbase + c * 16 * FS + sl * 16);
+            // with CP = 4 a K step j takes channel j of every position (each
+            // lane group's 4 elements are one position): the steps of the
+            // zero-padded channels j >= Cin would only add 0 * 0, so they are
+            // not issued (the 3-channel stem: a quarter of the products)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < 4; ++j) {
+                if (CP == 4 && j >= a.Cin) break;
 #pragma unroll
                 for (int s = 0; s < 4; ++s) {
                     if (s >= nb) break;
@@ -600,6 +605,7 @@ __global__ __launch_bounds__(kNarrowThreads) void conv_implicit_narrow_f32_kerne
                     for (int c = 0; c < 4; ++c)
                         acc[s][c] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[s][j], bf[c][j], acc[s][c], 0, 0, 0);
                 }
+            }
         }
         if ((a.Wo & 3) == 0 && a.out.type == 0) {
             if (nb > 0) store_blocks<4, true>(acc, nb, b0, lane, a.out, n, a.Cout, cb, a.Ho, a.Wo, ho0, outs);
