@@ -645,9 +645,9 @@ def main():
 
     if args.gpus != 1:
         print(json.dumps({"metric": METRIC, "value": None, "n_gpus": args.gpus,
-                          "error": "this build runs on one GPU only; a per-GPU share of a "
+                          "error": "this benchmark runs on one GPU only; a per-GPU share of a "
                                    "sharded layer is the same kernel at N/G images"}))
-        _say("bench.py: only --gpus 1 is supported (single-GPU build)")
+        _say("bench.py: only --gpus 1 is supported (one GPU per process, no collectives)")
         sys.exit(2)
 
     import torch
