@@ -49,11 +49,14 @@ constexpr int kKsThreads = 512;                  // 8 waves: K group x output ha
 // patch units a lane holds in registers between a chunk's global loads and
 // its LDS writes (32 registers for any vector width); none for filters of
 // more than 9 taps, whose longer contraction keeps more registers live (the
-// units then go straight from memory to LDS at the end of a chunk)
-template <int V, int TAPS>
+// units then go straight from memory to LDS at the end of a chunk), nor for
+// the 3x3 form with 8-position vectors and 7 blocks per wave, whose registers
+// spilled with them (14 registers; the 28x28 stride-2 layer 57.7 -> 54.6 us
+// without)
+template <int V, int TAPS, int NBW>
 constexpr int ks_units_held()
 {
-    return TAPS > 9 ? 0 : V == 8 ? 1 : V == 4 ? 2 : 4;
+    return TAPS > 9 || (TAPS == 9 && V == 8 && NBW == 7) ? 0 : V == 8 ? 1 : V == 4 ? 2 : 4;
 }
 
 // Staged filter, fragment order: fragment (cb, blk, t, c4) is 64 lanes x 8
@@ -177,7 +180,7 @@ __global__ __launch_bounds__(kKsThreads) __attribute__((amdgpu_waves_per_eu(2, 2
     const PipeKArgs a)
 {
     constexpr int TAPS = KH * KW;
-    constexpr int UH = ks_units_held<V, TAPS>();
+    constexpr int UH = ks_units_held<V, TAPS, NBW>();
     extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
