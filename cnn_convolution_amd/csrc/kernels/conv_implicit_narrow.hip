@@ -57,8 +57,14 @@ struct NarrowKArgs {
     int L, Lp;              // window row elements W_win*KH*CP, and per row in LDS (with slack)
     int R, row_groups, co_blocks;
     int groups;             // workgroups per 64-channel block (gridDim.x / co_blocks)
-    int rowvec;             // fp16/bf16, CP 4, W % 4 == 0: window rows from whole input rows
+    int rowvec;             // CP 4, W % 4 == 0, x aligned: the ROWS kernels (window rows from whole input rows)
 };
+
+// dword p (0..3) of a 16-byte vector
+__device__ __forceinline__ uint32_t dword_at(const uint4 &v, int p)
+{
+    return p == 0 ? v.x : p == 1 ? v.y : p == 2 ? v.z : v.w;
+}
 
 // One 16-byte vector of the filter block, gathered from w as stored: vector
 // v is row r = v / (Kp / VE) (output channel cb*64 + r; rows past Cout read
@@ -293,27 +299,38 @@ __device__ __forceinline__ void load_block(const NarrowKArgs &a, const T *ximg, 
     }
 }
 
-// Window rows from whole input rows (fp16/bf16, CP = 4, W % 4 == 0, x 8-byte
-// aligned): unit (input row r of the block, 4-column group g) reads the 4
-// columns 4g .. 4g+3 of each channel (one 8-byte load per channel,
-// consecutive lanes on consecutive groups), turns them in registers into 4
-// positions of 4 channels, and writes each position into every window row
-// (i, kh) that interleaves this input row (kh = r - i * stride), so that an
-// input element is read once per row block rather than once per window row
-// holding it (7x7 stride 2, 4 output rows: 13 input rows against 28 window
-// row segments), with a quarter of the load instructions. The window's
-// padding columns (wc < pad, wc >= pad + W) are zeroed apart.
+// Window rows from whole input rows (CP = 4, W % 4 == 0, x aligned to 4
+// elements): unit (input row r of the block, 4-column group g) reads the 4
+// columns 4g .. 4g+3 of each channel (one 8-byte load in half precision,
+// 16-byte in fp32; consecutive lanes on consecutive groups), turns them in
+// registers into 4 positions of 4 channels, and writes each position into
+// every window row (i, kh) that interleaves this input row (kh = r - i *
+// stride), so that an input element is read once per row block rather than
+// once per window row holding it (7x7 stride 2, 4 output rows: 13 input rows
+// against 28 window row segments), with a quarter of the load instructions
+// and of the registers a prefetched round holds. The window's padding columns
+// (wc < pad, wc >= pad + W) are zeroed apart.
 constexpr int kRowVecUnits = 2;                      // units per thread per round
 
+template <typename T>
 struct RowRegs {
-    uint2 v[kRowVecUnits][4];
+    using Q = std::conditional_t<sizeof(T) == 2, uint2, uint4>;   // 4 columns of one channel
+    Q v[kRowVecUnits][4];
 };
 
-__device__ __forceinline__ void fetch_rows(const NarrowKArgs &a, const uint16_t *ximg, int ho0, int rw, int u0,
-                                           int tid, RowRegs &q)
+template <typename T>
+__device__ __forceinline__ int row_units(const NarrowKArgs &a, int rw)
 {
+    return ((rw - 1) * a.stride + a.KH) * (a.W >> 2);
+}
+
+template <typename T>
+__device__ __forceinline__ void fetch_rows(const NarrowKArgs &a, const T *ximg, int ho0, int rw, int u0, int tid,
+                                           RowRegs<T> &q)
+{
+    using Q = typename RowRegs<T>::Q;
     const int G4 = a.W >> 2;
-    const int units = ((rw - 1) * a.stride + a.KH) * G4;
+    const int units = row_units<T>(a, rw);
     const int HW = a.H * a.W;
 #pragma unroll
     for (int j = 0; j < kRowVecUnits; ++j) {
@@ -323,16 +340,17 @@ __device__ __forceinline__ void fetch_rows(const NarrowKArgs &a, const uint16_t 
         const int ih = ho0 * a.stride - a.pad + r;
         const int src = (unsigned(ih) < unsigned(a.H) ? ih * a.W : 0) + 4 * g;   // every load in bounds
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
-            q.v[j][c] = *reinterpret_cast<const uint2 *>(ximg + min(c, a.Cin - 1) * HW + src);
+        for (int c = 0; c < 4; ++c) q.v[j][c] = *reinterpret_cast<const Q *>(ximg + min(c, a.Cin - 1) * HW + src);
     }
 }
 
-__device__ __forceinline__ void put_rows(const NarrowKArgs &a, uint16_t *win, int ho0, int rw, int u0, int tid,
-                                         const RowRegs &q)
+template <typename T>
+__device__ __forceinline__ void put_rows(const NarrowKArgs &a, T *win, int ho0, int rw, int u0, int tid,
+                                         const RowRegs<T> &q)
 {
+    using Q = typename RowRegs<T>::Q;
     const int G4 = a.W >> 2;
-    const int units = ((rw - 1) * a.stride + a.KH) * G4;
+    const int units = row_units<T>(a, rw);
 #pragma unroll
     for (int j = 0; j < kRowVecUnits; ++j) {
         const int u = u0 + tid + j * kNarrowThreads;
@@ -341,17 +359,21 @@ __device__ __forceinline__ void put_rows(const NarrowKArgs &a, uint16_t *win, in
         const int g = u - r * G4;
         const int ih = ho0 * a.stride - a.pad + r;
         const bool in = unsigned(ih) < unsigned(a.H);
-        uint2 v[4];
+        Q v[4];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) v[c] = (in && c < a.Cin) ? q.v[j][c] : uint2{0u, 0u};
-        // position p (column 4g + p): channel c's half p of its 4 columns
-        uint2 pos[4];
+        for (int c = 0; c < 4; ++c) v[c] = (in && c < a.Cin) ? q.v[j][c] : Q{};
+        // position p (column 4g + p): element p of each channel's 4 columns
+        Q pos[4];
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-            const uint32_t sel = (p & 1) ? 0x07060302u : 0x05040100u;
-            const uint32_t d0 = p < 2 ? v[0].x : v[0].y, d1 = p < 2 ? v[1].x : v[1].y;
-            const uint32_t d2 = p < 2 ? v[2].x : v[2].y, d3 = p < 2 ? v[3].x : v[3].y;
-            pos[p] = uint2{__builtin_amdgcn_perm(d1, d0, sel), __builtin_amdgcn_perm(d3, d2, sel)};
+            if constexpr (sizeof(T) == 2) {
+                const uint32_t sel = (p & 1) ? 0x07060302u : 0x05040100u;
+                const uint32_t d0 = p < 2 ? v[0].x : v[0].y, d1 = p < 2 ? v[1].x : v[1].y;
+                const uint32_t d2 = p < 2 ? v[2].x : v[2].y, d3 = p < 2 ? v[3].x : v[3].y;
+                pos[p] = Q{__builtin_amdgcn_perm(d1, d0, sel), __builtin_amdgcn_perm(d3, d2, sel)};
+            } else {
+                pos[p] = Q{dword_at(v[0], p), dword_at(v[1], p), dword_at(v[2], p), dword_at(v[3], p)};
+            }
         }
         // window rows i with 0 <= r - i * stride < KH
         const int num = r - a.KH + 1;
@@ -362,15 +384,17 @@ __device__ __forceinline__ void put_rows(const NarrowKArgs &a, uint16_t *win, in
 #pragma unroll
             for (int p = 0; p < 4; ++p) {
                 const int wc = 4 * g + p + a.pad;
-                if (wc < a.Wwin) *reinterpret_cast<uint2 *>(win + i * a.Lp + (wc * a.KH + kh) * 4) = pos[p];
+                if (wc < a.Wwin) *reinterpret_cast<Q *>(win + i * a.Lp + (wc * a.KH + kh) * 4) = pos[p];
             }
         }
     }
 }
 
 // zero the padding columns of the rw window rows, and the slack after each
-__device__ __forceinline__ void zero_row_pads(const NarrowKArgs &a, uint16_t *win, int rw, int tid)
+template <typename T>
+__device__ __forceinline__ void zero_row_pads(const NarrowKArgs &a, T *win, int rw, int tid)
 {
+    using Q = typename RowRegs<T>::Q;
     const int right = max(0, a.Wwin - a.pad - a.W);
     const int npad = a.pad + right;
     const int n = rw * a.KH * npad;
@@ -380,33 +404,43 @@ __device__ __forceinline__ void zero_row_pads(const NarrowKArgs &a, uint16_t *wi
         const int i = ik / a.KH;
         const int kh = ik - i * a.KH;
         const int wc = col < a.pad ? col : a.pad + a.W + (col - a.pad);
-        *reinterpret_cast<uint2 *>(win + i * a.Lp + (wc * a.KH + kh) * 4) = uint2{0u, 0u};
+        *reinterpret_cast<Q *>(win + i * a.Lp + (wc * a.KH + kh) * 4) = Q{};
     }
     const int slack = a.Lp - a.L;
     for (int v = tid; v < rw * slack; v += kNarrowThreads) {
         const int i = v / slack;
-        win[i * a.Lp + a.L + (v - i * slack)] = 0;
+        win[i * a.Lp + a.L + (v - i * slack)] = T(0);
+    }
+}
+
+// every row-unit round of a row block after the first, fetched and written
+template <typename T>
+__device__ __forceinline__ void rows_rest(const NarrowKArgs &a, const T *ximg, T *win, int ho0, int rw, int tid)
+{
+    for (int u0 = kRowVecUnits * kNarrowThreads; u0 < row_units<T>(a, rw); u0 += kRowVecUnits * kNarrowThreads) {
+        RowRegs<T> more;
+        fetch_rows(a, ximg, ho0, rw, u0, tid, more);
+        put_rows(a, win, ho0, rw, u0, tid, more);
     }
 }
 
 // One row block per workgroup from whole input rows: the filter block's
 // vectors and a round of row units in flight together, then written.
-template <bool GATHER, int FB>
-__device__ __forceinline__ void load_block_rows(const NarrowKArgs &a, const uint16_t *ximg, const uint16_t *w,
-                                                uint16_t *fl, uint16_t *win, int FS, int cb, int ho0, int rw,
-                                                int tid)
+template <bool GATHER, int FB, typename T>
+__device__ __forceinline__ void load_block_rows(const NarrowKArgs &a, const T *ximg, const T *w, T *fl, T *win,
+                                                int FS, int cb, int ho0, int rw, int tid)
 {
-    constexpr int V = 8;
+    constexpr int V = 16 / sizeof(T);
     const int fv_row = a.Kp / V;
     const int fvec = 64 * fv_row;
-    const int units = ((rw - 1) * a.stride + a.KH) * (a.W >> 2);
+    const int units = row_units<T>(a, rw);
     constexpr int UR = kRowVecUnits * kNarrowThreads;
     for (int f0 = 0, u0 = 0; f0 < fvec || u0 < units; f0 += FB * kNarrowThreads, u0 += UR) {
         uint4 fv[FB];
 #pragma unroll
         for (int j = 0; j < FB; ++j)
             fv[j] = filter_vec<4, GATHER>(a, w, cb, min(f0 + tid + j * kNarrowThreads, fvec - 1));
-        RowRegs q;
+        RowRegs<T> q;
         if (u0 < units) fetch_rows(a, ximg, ho0, rw, u0, tid, q);
 #pragma unroll
         for (int j = 0; j < FB; ++j) {
@@ -430,7 +464,8 @@ __device__ __forceinline__ void task_rows(const NarrowKArgs &a, int t, int &n, i
 }
 
 // ---- fp16 / bf16 -------------------------------------------------------------
-template <int CP, bool BF16, bool PIPE, bool GATHER>
+// ROWS (CP = 4 only): window rows from whole input rows (load_block_rows)
+template <int CP, bool BF16, bool PIPE, bool GATHER, bool ROWS>
 __global__ __launch_bounds__(kNarrowThreads) void conv_implicit_narrow_kernel(const NarrowKArgs a, int ntasks)
 {
     extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
@@ -451,7 +486,7 @@ __global__ __launch_bounds__(kNarrowThreads) void conv_implicit_narrow_kernel(co
     const uint16_t *const x = static_cast<const uint16_t *>(a.x);
     const int64_t img = int64_t(a.Cin) * a.H * a.W;
     // contraction and stores of one row block, after its window rows are in LDS
-    auto run_block = [&](int n, int ho0, int rw) {
+    auto run_block = [&](int n, int ho0, int rw) __attribute__((always_inline)) {
         const int outs = rw * a.Wo;
         int b0, nb;
         wave_blocks(wave, outs, b0, nb);
@@ -503,7 +538,7 @@ __global__ __launch_bounds__(kNarrowThreads) void conv_implicit_narrow_kernel(co
         // one row block: filter and window loads in one round trip
         int n, ho0, rw;
         task_rows(a, t_begin, n, ho0, rw);
-        if (CP == 4 && a.rowvec)
+        if constexpr (ROWS)
             load_block_rows<GATHER, 4>(a, x + n * img, wsrc, fl, win, FS, cb, ho0, rw, tid);
         else
             load_block<CP, GATHER, 4, UB>(a, x + n * img, wsrc, fl, win, FS, cb, ho0, rw, tid);
@@ -544,7 +579,7 @@ __global__ __launch_bounds__(kNarrowThreads) void conv_implicit_narrow_kernel(co
 // ---- fp32: v_mfma_f32_16x16x4_f32; K in slices of 16 elements, lane group
 // g = lane / 16 holding elements 4g .. 4g + 3 of a slice as one vector and
 // feeding element j to K step j (window runs and filter alike) -------------
-template <int CP, bool PIPE, bool GATHER>
+template <int CP, bool PIPE, bool GATHER, bool ROWS>
 __global__ __launch_bounds__(kNarrowThreads) void conv_implicit_narrow_f32_kernel(const NarrowKArgs a, int ntasks)
 {
     extern __shared__ __attribute__((aligned(16))) float ldsf[];
@@ -565,7 +600,7 @@ __global__ __launch_bounds__(kNarrowThreads) void conv_implicit_narrow_f32_kerne
     const float *const x = static_cast<const float *>(a.x);
     const int64_t img = int64_t(a.Cin) * a.H * a.W;
     // contraction and stores of one row block, after its window rows are in LDS
-    auto run_block = [&](int n, int ho0, int rw) {
+    auto run_block = [&](int n, int ho0, int rw) __attribute__((always_inline)) {
         const int outs = rw * a.Wo;
         int b0, nb;
         wave_blocks(wave, outs, b0, nb);
@@ -620,9 +655,38 @@ __global__ __launch_bounds__(kNarrowThreads) void conv_implicit_narrow_f32_kerne
         // one row block: filter and window loads in one round trip
         int n, ho0, rw;
         task_rows(a, t_begin, n, ho0, rw);
-        load_block<CP, GATHER, 4, UB>(a, x + n * img, wsrc, fl, win, FS, cb, ho0, rw, tid);
+        if constexpr (ROWS)
+            load_block_rows<GATHER, 4>(a, x + n * img, wsrc, fl, win, FS, cb, ho0, rw, tid);
+        else
+            load_block<CP, GATHER, 4, UB>(a, x + n * img, wsrc, fl, win, FS, cb, ho0, rw, tid);
         __syncthreads();
         run_block(n, ho0, rw);
+    } else if constexpr (ROWS) {
+        // persistent, window rows from whole input rows: the first round of
+        // each row block's row units in flight during the previous block's
+        // contraction
+        RowRegs<float> nxt;
+        {
+            int n, ho0, rw;
+            task_rows(a, t_begin, n, ho0, rw);
+            fetch_rows(a, x + n * img, ho0, rw, 0, tid, nxt);
+        }
+        load_filter<CP, GATHER, 4>(a, wsrc, fl, FS, cb, tid);
+        for (int t = t_begin; t < t_end; ++t) {
+            int n, ho0, rw;
+            task_rows(a, t, n, ho0, rw);
+            if (t != t_begin) __syncthreads();       // the previous block's window rows (scratch) are dead
+            put_rows(a, win, ho0, rw, 0, tid, nxt);
+            rows_rest(a, x + n * img, win, ho0, rw, tid);
+            zero_row_pads(a, win, rw, tid);
+            if (t + 1 < t_end) {
+                int n1, h1, r1;
+                task_rows(a, t + 1, n1, h1, r1);
+                fetch_rows(a, x + n1 * img, h1, r1, 0, tid, nxt);
+            }
+            __syncthreads();
+            run_block(n, ho0, rw);
+        }
     } else {
         // persistent: the filter once; the first round of each row block's
         // gathers in flight during the previous block's contraction (the
@@ -684,7 +748,9 @@ hipError_t launch_conv_implicit_narrow(const ImplicitArgs &h, hipStream_t s)
     a.R = h.R;
     a.row_groups = (h.Ho + h.R - 1) / h.R;
     a.co_blocks = (h.Cout + 63) / 64;
-    a.rowvec = !h.f32 && cp == 4 && h.W % 4 == 0 && (reinterpret_cast<uintptr_t>(h.x) & 7) == 0;
+    // window rows from whole input rows: 4 channels per position, rows of 4k
+    // elements, x aligned to 4 elements
+    a.rowvec = cp == 4 && h.W % 4 == 0 && (reinterpret_cast<uintptr_t>(h.x) & (h.f32 ? 15 : 7)) == 0;
     // the kernel's assumptions: CP channels hold Cin, every window start is a
     // whole 16-byte vector, the outputs of a block fit 32 MFMA blocks, and
     // element offsets of the image fit 32 bits
@@ -710,12 +776,18 @@ hipError_t launch_conv_implicit_narrow(const ImplicitArgs &h, hipStream_t s)
     const bool gather = narrow_gathers_filter(blocks);
     const void *kern;
 #define IM2WIN_NARROW_PICK(P, G)                                                                                   \
-    if (h.f32) kern = cp == 4 ? reinterpret_cast<const void *>(conv_implicit_narrow_f32_kernel<4, P, G>)           \
-                              : reinterpret_cast<const void *>(conv_implicit_narrow_f32_kernel<8, P, G>);          \
-    else if (h.bf16) kern = cp == 4 ? reinterpret_cast<const void *>(conv_implicit_narrow_kernel<4, true, P, G>)   \
-                                    : reinterpret_cast<const void *>(conv_implicit_narrow_kernel<8, true, P, G>);  \
-    else kern = cp == 4 ? reinterpret_cast<const void *>(conv_implicit_narrow_kernel<4, false, P, G>)              \
-                        : reinterpret_cast<const void *>(conv_implicit_narrow_kernel<8, false, P, G>);
+    if (h.f32)                                                                                                     \
+        kern = cp == 8   ? reinterpret_cast<const void *>(conv_implicit_narrow_f32_kernel<8, P, G, false>)         \
+               : a.rowvec ? reinterpret_cast<const void *>(conv_implicit_narrow_f32_kernel<4, P, G, true>)         \
+                          : reinterpret_cast<const void *>(conv_implicit_narrow_f32_kernel<4, P, G, false>);       \
+    else if (h.bf16)                                                                                               \
+        kern = cp == 8   ? reinterpret_cast<const void *>(conv_implicit_narrow_kernel<8, true, P, G, false>)       \
+               : a.rowvec ? reinterpret_cast<const void *>(conv_implicit_narrow_kernel<4, true, P, G, true>)       \
+                          : reinterpret_cast<const void *>(conv_implicit_narrow_kernel<4, true, P, G, false>);     \
+    else                                                                                                           \
+        kern = cp == 8   ? reinterpret_cast<const void *>(conv_implicit_narrow_kernel<8, false, P, G, false>)      \
+               : a.rowvec ? reinterpret_cast<const void *>(conv_implicit_narrow_kernel<4, false, P, G, true>)      \
+                          : reinterpret_cast<const void *>(conv_implicit_narrow_kernel<4, false, P, G, false>);
     // persistent launches have at most 256 workgroups: always the gathered filter
     if (pipe && !gather) return hipErrorInvalidValue;
     if (pipe) {

@@ -58,9 +58,23 @@ __device__ __forceinline__ void block_bases(int *qa, int b0, int lane, int outs,
 // LDS-staged path measured slower (deep 3x3 layer 25.2 -> 27.0 us, the 1x1
 // layer 42.0 -> 46.5 us), so only the direct stores of the row-block and
 // narrow-channel kernels take it.
-__device__ __forceinline__ void store16_through(void *p, const floatx4_t &v)
+//
+// The store is a buffer store with the sc1 cache policy from a wave-uniform
+// base, written with the compiler's builtin rather than as inline asm, so
+// that the compiler keeps the wait rules around it: a store of more than 8
+// bytes reads its data registers after it issues (a vector-ALU write to them
+// needs a wait state), and the data comes straight from matrix-core
+// accumulators (a vector-memory read of them needs wait states after the
+// product). An earlier inline-asm form kept neither, and now and then
+// stored whatever the next instruction had put into the data registers.
+constexpr int kCachePolicySc1 = 16;                  // buffer-store cache policy: sc1
+constexpr int kBufferWord3 = 0x00020000;             // raw-buffer descriptor word 3 on gfx9
+
+__device__ __forceinline__ void store16_through(void *base, uint32_t off, const floatx4_t &v)
 {
-    asm volatile("global_store_dwordx4 %0, %1, off sc1" ::"v"(p), "v"(v) : "memory");
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(base, 0, -1, kBufferWord3);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, int(off), 0, kCachePolicySc1);
 }
 
 // Whether the 128-byte line holding byte address p lies inside [lo, hi).
@@ -83,11 +97,16 @@ __device__ __forceinline__ void store_blocks(const floatx4_t (*acc)[4], int nb, 
     const int64_t plane = int64_t(Ho) * Wo;
     if (o.plain) {
         float *const y = static_cast<float *>(o.y);
+        // the write-through stores address the workgroup's 64 channel planes
+        // from one wave-uniform base with 32-bit byte offsets
+        float *const yw = y + (int64_t(n) * Cout + cb * 64) * plane + int64_t(ho0) * Wo;
+        const bool through = THROUGH && 64 * plane * 4 < (int64_t(1) << 32);
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const int co = cb * 64 + c * 16 + (lane & 15);
             if (co >= Cout) continue;
             float *yb = y + (int64_t(n) * Cout + co) * plane + int64_t(ho0) * Wo;
+            const int64_t cbase = int64_t(c * 16 + (lane & 15)) * plane;   // yb - yw, in floats
             // this workgroup's segment of the channel's plane
             const uintptr_t lo = reinterpret_cast<uintptr_t>(yb);
             const uintptr_t hi = reinterpret_cast<uintptr_t>(yb + outs);
@@ -97,8 +116,8 @@ __device__ __forceinline__ void store_blocks(const floatx4_t (*acc)[4], int nb, 
                 const int m = (b0 + s) * 16 + (lane >> 4) * 4;
                 if ((Wo & 3) == 0) {
                     if (m < outs) {
-                        if (THROUGH && whole_line(yb + m, lo, hi))
-                            store16_through(yb + m, acc[s][c]);
+                        if (through && whole_line(yb + m, lo, hi))
+                            store16_through(yw, uint32_t((cbase + m) * 4), acc[s][c]);
                         else
                             *reinterpret_cast<floatx4_t *>(yb + m) = acc[s][c];
                     }

@@ -437,21 +437,26 @@ def test_narrow_kernel_leaves_memory_past_y_untouched(dt):
     check(host[:n_out], x, w, s, p, dt)
 
 
-# half precision with 4 channels per position on rows of 4k elements: window
-# rows written from whole input rows (each input row into every window row
-# that interleaves it), padding columns zeroed apart
+# 4 channels per position on rows of 4k elements: window rows written from
+# whole input rows (each input row into every window row that interleaves
+# it), padding columns zeroed apart; in fp32 also in the persistent form
 NARROW_ROWVEC = [
     (2, 3, 28, 32, 64, 7, 7, 2, 3),      # the stem's geometry: 3 zero columns left, 2 right
     (1, 4, 12, 16, 24, 5, 5, 2, 0),      # four real channels; input column 15 in no window
     (2, 2, 9, 8, 16, 3, 3, 2, 2),        # two channels, rows above and below the image
     (3, 1, 10, 12, 8, 1, 1, 2, 0),       # 1x1 stride 2: every other input row unused
     (1, 3, 9, 1000, 8, 9, 9, 2, 0),      # 9 x 250 row units: three rounds per thread
-    (20, 3, 64, 64, 64, 7, 7, 2, 3),     # more than 256 workgroups: the staged filter
+    (20, 3, 64, 64, 64, 7, 7, 2, 3),     # more than 256 workgroups: the staged filter (half), persistent (fp32)
+    (1, 3, 600, 600, 8, 7, 7, 2, 0),     # 297 row blocks of two unit rounds each: persistent in fp32
 ]
 
 
-@pytest.mark.parametrize("shape", NARROW_ROWVEC, ids=[str(s) for s in NARROW_ROWVEC])
-@pytest.mark.parametrize("dt", ["f16", "bf16"])
+# (the 9x9 filter's 999-column window rows do not fit LDS in fp32)
+ROWVEC_CASES = [(s, dt) for s in NARROW_ROWVEC for dt in ("f16", "bf16", "f32")
+                if not (dt == "f32" and s[3] == 1000)]
+
+
+@pytest.mark.parametrize("shape,dt", ROWVEC_CASES, ids=[f"{d}-{s}" for s, d in ROWVEC_CASES])
 @pytest.mark.parametrize("rows", [None, 2, 3])
 def test_narrow_kernel_from_whole_input_rows(shape, dt, rows, monkeypatch):
     N, Cin, H, W, Cout, KH, KW, s, p = shape
