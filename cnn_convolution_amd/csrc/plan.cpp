@@ -656,8 +656,13 @@ static void pick_implicit_ksplit(const conv2d_desc_t &d, int64_t Ho, int64_t Wo,
     if (const char *e = std::getenv("IM2WIN_KSPLIT_CO")) force_co = std::atoi(e);
     if (const char *e = std::getenv("IM2WIN_KSPLIT_SLOTS")) force_slots = std::atoi(e);
     const int64_t s = d.stride, iw = d.W + 2 * d.pad;
-    struct Pick { int64_t rw, img, cos, slots; double cost; };
-    Pick best{0, 0, 0, 0, 0.0};
+    // padded: the products a choice issues, in 16-output x 64-channel block
+    // steps over all tasks (ties of the round count go to the fewest: the
+    // 28x28 5x5 layer's 4-row x 128-channel tasks issue 6272, its 7-row x
+    // 64-channel ones 6656 and measured 52.5 -> 47.7 us; the 14x14 deep
+    // layer's whole images x 64 channels issue 3328 against 3584)
+    struct Pick { int64_t rw, img, cos, slots; double cost; int64_t padded; };
+    Pick best{0, 0, 0, 0, 0.0, 0};
     auto fits = [&](int64_t rw, int64_t img, int64_t cos, int64_t slots) {
         const int64_t outs = img * rw * Wo;
         if (outs > kKsplitMaxOuts / cos || (cos == 2 && d.Cout <= 64)) return false;
@@ -675,11 +680,13 @@ static void pick_implicit_ksplit(const conv2d_desc_t &d, int64_t Ho, int64_t Wo,
                 const int64_t co_blocks = ceil_div(d.Cout, 64 * cos);
                 const int64_t tasks = img > 1 ? co_blocks * ceil_div(d.N, img) : co_blocks * d.N * ceil_div(Ho, rw);
                 const double cost = double(ceil_div(tasks, 256)) * double(per_wave + 3) * (slots == 1 ? 1.15 : 1.0);
+                const int64_t padded = tasks * nbt * cos;
                 const int64_t bouts = best.img * best.rw * Wo;
                 const bool tie = best.rw != 0 && cost == best.cost;
                 if (best.rw == 0 || cost < best.cost ||
-                    (tie && (cos < best.cos || (cos == best.cos && outs > bouts))))
-                    best = Pick{rw, img, cos, slots, cost};
+                    (tie && (padded < best.padded ||
+                             (padded == best.padded && (cos < best.cos || (cos == best.cos && outs > bouts))))))
+                    best = Pick{rw, img, cos, slots, cost, padded};
                 break;                             // two slots where they fit
             }
         }
@@ -690,7 +697,7 @@ static void pick_implicit_ksplit(const conv2d_desc_t &d, int64_t Ho, int64_t Wo,
         const int64_t v = std::atoi(e);
         if (v >= 2 && v <= d.N) {
             const Pick keep = best;
-            best = Pick{0, 0, 0, 0, 0.0};
+            best = Pick{0, 0, 0, 0, 0.0, 0};
             consider(Ho, v);
             if (best.rw == 0) best = keep;
         }
@@ -699,7 +706,7 @@ static void pick_implicit_ksplit(const conv2d_desc_t &d, int64_t Ho, int64_t Wo,
         const int64_t v = std::min<int64_t>(std::atoi(e), Ho);
         if (v >= 1) {
             const Pick keep = best;
-            best = Pick{0, 0, 0, 0, 0.0};
+            best = Pick{0, 0, 0, 0, 0.0, 0};
             consider(v, 1);
             if (best.rw == 0) best = keep;
         }
