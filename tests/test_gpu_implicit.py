@@ -671,3 +671,31 @@ def test_pipelined_kernel_stride_two(shape, dt, form, images, monkeypatch):
                                        x_dist="int3", w_dist="int3")
         got = run_implicit(xi, wi, s, p)
         assert np.array_equal(got.numpy().astype(np.float64), oracle.conv2d(xi, wi, s, p))
+
+
+# the write-through stores of the row-block and narrow kernels: repeated
+# launches give the same bits as the first and match the oracle (a store
+# form that skipped the wait rule around its data registers wrote another
+# instruction's values for a few outputs, different ones each run)
+REPEAT_CASES = [
+    ((9, 3, 130, 128, 40, 3, 3, 1, 1), "f32", None),   # persistent narrow kernel, fp32
+    ((2, 3, 66, 64, 64, 7, 7, 2, 3), "f16", None),      # narrow kernel, whole input rows
+    ((4, 64, 32, 56, 64, 3, 3, 1, 1), "f16", 8),        # row-block kernel, 8 rows: every line whole
+    ((2, 64, 16, 32, 96, 3, 3, 1, 1), "f32", 4),        # fp32 row-block kernel
+]
+
+
+@pytest.mark.parametrize("shape,dt,rows", REPEAT_CASES, ids=[f"{d}-{s}" for s, d, _ in REPEAT_CASES])
+def test_write_through_stores_repeat_exactly(shape, dt, rows, monkeypatch):
+    if rows is not None:
+        monkeypatch.setenv("IM2WIN_IMPLICIT_ROWS", str(rows))
+    N, Cin, H, W, Cout, KH, KW, s, p = shape
+    x, w = workloads.make_inputs(N, Cin, H, W, Cout, KH, KW, seed=37, dtype=dt, w_dist="normal")
+    xd, wd = x.to(DEV), w.to(DEV)
+    runs = []
+    for _ in range(5):
+        runs.append(conv.conv2d_implicit(xd, wd, stride=s, pad=p))
+    torch.cuda.synchronize()
+    for y in runs[1:]:
+        assert torch.equal(y, runs[0])
+    check(runs[0].cpu(), x, w, s, p, dt, ref=oracle.conv2d(x, w, s, p))
